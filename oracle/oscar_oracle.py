@@ -1,0 +1,474 @@
+"""CPU oracle for the rotated-INT2 KV cache and its mixed-precision decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline
+leg may import this module.  The HIP library never calls it and it never calls the library;
+the two share no code.  Everything here is plain numpy, written to be checked by eye against
+the method's description, not to be fast.
+
+What it follows.  The OSCAR pages (project card "FutureMLS-Lab/OSCAR", section "How it works";
+the write-up "OSCAR: Cut LLM Inference Costs 8x with 2-bit KV Cache Quantization", sections
+"Practical Summary" and "How OSCAR Works"; and the OSCAR paper's "Abstract") fix the shape of
+the method:
+
+  * every cached K/V row is multiplied by a fixed orthogonal rotation, clipped with fixed
+    thresholds, and quantised to 2 bits (4 levels);
+  * a few initial "sink" tokens and a recent window of tokens are kept in BF16, the rest of
+    the cache in INT2, inside a paged KV cache;
+  * decode attention reads that mixed cache in one fused softmax.
+
+Every number and bit-level choice the pages leave open is taken from the workload
+definitions and the readings listed in the design notes: per-token groups of 32 channels,
+asymmetric (min/scale) levels with fp16 scale and zero, clip ratio applied to each group's
+min and max, 16-token pages, q rotated by the key rotation and the output rotated back by
+the transpose of the value rotation.
+
+Precision.  Rotations and attention are fp64.  The quantiser parameters are an fp32 formula
+(numpy float32 scalars and arrays: IEEE single, round to nearest even, never fused), then
+rounded to fp16 with round to nearest even, because the encoded bytes must be reproduced bit
+for bit.  bf16 rounding is round to nearest even.
+
+Parity pins: every function here is checked in the CPU tests against closed forms,
+invariants, special cases and brute force (orthogonality, rotation invariance of attention,
+level membership, exhaustive code enumeration, hand-derived record bytes, partition
+invariance of the split merge).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+D = 128          # head dimension
+PAGE = 16        # tokens per page
+GROUP = 32       # channels per quantisation group
+NGROUPS = D // GROUP
+LEVELS = 4       # 2-bit codes
+RECORD = 1536    # bytes of one (page, KV head) INT2 record
+K_CODES, V_CODES, K_META, V_META = 0, 512, 1024, 1280
+
+
+# ----------------------------------------------------------------------------------------
+# Rounding helpers (own implementations; the input generator has its own copies).
+# ----------------------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 to bf16 with round-to-nearest-even; returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    u = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------
+# Rotation of cache rows and of the query.
+# ----------------------------------------------------------------------------------------
+
+def rotate_rows(x_bits: np.ndarray, rot32: np.ndarray) -> np.ndarray:
+    """y = x . R for bf16 rows x (row-vector convention), result rounded to fp32.
+
+    The sum over the 128 input channels is accumulated in fp64 in ascending channel order
+    starting from +0.0, then rounded once to fp32 (nearest even).  Each product of a bf16
+    value and an fp32 value is exact in fp64, so the order of the additions is the only
+    rounding choice, and it is fixed here.
+
+    x_bits: uint16 [N][128] bf16 bit patterns.  rot32: float32 [128][128].
+    Returns float32 [N][128].
+    """
+    x = bf16_bits_to_f64(x_bits)
+    r = np.asarray(rot32, dtype=np.float32).astype(np.float64)
+    acc = np.zeros((x.shape[0], D), dtype=np.float64)
+    for i in range(D):
+        acc = acc + x[:, i:i + 1] * r[i:i + 1, :]
+    return acc.astype(np.float32)
+
+
+def rotate_query(q_bits: np.ndarray, rot_k32: np.ndarray, group: int) -> np.ndarray:
+    """q' = q . R_K(h) in fp64 for each query head; query head j reads KV head j // group.
+
+    q_bits: uint16 [Hq][128]; rot_k32: float32 [Hkv][128][128].  Returns fp64 [Hq][128].
+    """
+    q = bf16_bits_to_f64(q_bits)
+    out = np.empty_like(q)
+    for j in range(q.shape[0]):
+        out[j] = q[j] @ np.asarray(rot_k32[j // group], dtype=np.float32).astype(np.float64)
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Quantiser: per-token groups of 32 rotated channels, clipped min/max, 4 affine levels.
+# ----------------------------------------------------------------------------------------
+
+def group_params(y: np.ndarray, clip: float):
+    """fp16 scale and zero of every 32-channel group of every rotated row.
+
+    For each group: mx = max, mn = min of the fp32 values; the clip ratio c (as fp32) scales
+    both ends, mx_c = c*mx and mn_c = c*mn in fp32; the step is s = (mx_c - mn_c) / 3 in fp32
+    (3 = number of steps between 4 levels); the stored scale is fp16(s) and the stored zero
+    is fp16(mn_c), both rounded to nearest even.
+
+    y: float32 [N][128].  Returns (s16, z16) float16 [N][4].
+    """
+    y = np.asarray(y, dtype=np.float32)
+    c = np.float32(clip)
+    g = y.reshape(y.shape[0], NGROUPS, GROUP)
+    mx = g.max(axis=2)
+    mn = g.min(axis=2)
+    mx_c = (c * mx).astype(np.float32)
+    mn_c = (c * mn).astype(np.float32)
+    width = (mx_c - mn_c).astype(np.float32)
+    s32 = (width / np.float32(LEVELS - 1)).astype(np.float32)
+    return s32.astype(np.float16), mn_c.astype(np.float16)
+
+
+def group_codes(y: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """2-bit code of every channel: round((y - z) / s) to nearest even, clamped to [0, 3].
+
+    The quotient uses the stored fp16 scale and zero (widened to fp32) in fp32 arithmetic, so
+    the codes agree with what dequantisation reconstructs.  A group whose stored scale is 0
+    gets all codes 0.
+
+    Returns uint8 [N][128].
+    """
+    y = np.asarray(y, dtype=np.float32).reshape(-1, NGROUPS, GROUP)
+    s = s16.astype(np.float32)[:, :, None]
+    z = z16.astype(np.float32)[:, :, None]
+    diff = (y - z).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (diff / np.where(s == 0, np.float32(1), s)).astype(np.float32)
+    code = np.clip(np.rint(t), 0, LEVELS - 1)
+    code = np.where(s == 0, 0, code)
+    return code.astype(np.uint8).reshape(-1, D)
+
+
+def dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """Reconstructed values s*code + z in fp64 (exact). codes [N][128], s16/z16 [N][4]."""
+    c = codes.astype(np.float64).reshape(-1, NGROUPS, GROUP)
+    v = s16.astype(np.float64)[:, :, None] * c + z16.astype(np.float64)[:, :, None]
+    return v.reshape(-1, D)
+
+
+def quantize_rows(x_bits: np.ndarray, rot32: np.ndarray, clip: float):
+    """Rotate, clip and quantise rows: returns (y fp32, codes u8, s16, z16)."""
+    y = rotate_rows(x_bits, rot32)
+    s16, z16 = group_params(y, clip)
+    return y, group_codes(y, s16, z16), s16, z16
+
+
+# ----------------------------------------------------------------------------------------
+# Byte layout of one (page, KV head) INT2 record (1536 bytes).
+#
+#   [   0,  512)  K codes.  Channel c of page slot r: 16-channel word d = c // 16, stored as the
+#                 dword at 8*(16*(d % 4) + r) + 4*(d // 4); inside the dword, byte (c % 16)//4,
+#                 bits 2*(c % 4) .. +1.
+#   [ 512, 1024)  V codes.  Channel c of slot r: lane chunk L = 16*(r // 4) + (c % 16) at
+#                 512 + 8*L; dword (r % 4) // 2 of the chunk, 16-bit half r % 2 of the dword;
+#                 inside the half, bits 2*(c // 16) .. +1.
+#   [1024, 1280)  K scale/zero.  Group g of slot r: fp16 scale then fp16 zero at 1024 + 64*g + 4*r.
+#   [1280, 1536)  V scale/zero, same arrangement at 1280 + 64*g + 4*r.
+#
+# All multi-byte fields are little-endian.
+# ----------------------------------------------------------------------------------------
+
+def k_code_location(r, c):
+    """(byte offset in the record, bit offset in that byte) of K channel c of slot r.
+
+    Works elementwise on integers or integer arrays."""
+    d = c // 16
+    byte = K_CODES + 8 * (16 * (d % 4) + r) + 4 * (d // 4) + (c % 16) // 4
+    return byte, 2 * (c % 4)
+
+
+def v_code_location(r, c):
+    """(byte offset, bit offset) of V channel c of slot r; elementwise on arrays."""
+    lane = 16 * (r // 4) + (c % 16)
+    nb = c // 16
+    byte = V_CODES + 8 * lane + 4 * ((r % 4) // 2) + 2 * (r % 2) + nb // 4
+    return byte, 2 * (nb % 4)
+
+
+def meta_location(kind: str, r, g):
+    """Byte offset of the (fp16 scale, fp16 zero) pair of group g of slot r."""
+    return (K_META if kind == "k" else V_META) + 64 * g + 4 * r
+
+
+_CH = np.arange(D)
+_GR = np.arange(NGROUPS)
+
+
+def _put_codes(flat, base, r, codes, loc):
+    byte, bit = loc(r[:, None], _CH[None, :])
+    idx = (base[:, None] + byte).ravel()
+    bit = np.broadcast_to(bit, codes.shape).ravel().astype(np.uint8)
+    np.bitwise_and.at(flat, idx, (~(np.uint8(3) << bit)).astype(np.uint8))
+    np.bitwise_or.at(flat, idx, (codes.astype(np.uint8).ravel() << bit).astype(np.uint8))
+
+
+def _get_codes(flat, base, r, loc):
+    byte, bit = loc(r[:, None], _CH[None, :])
+    return ((flat[base[:, None] + byte] >> np.broadcast_to(bit, byte.shape).astype(np.uint8)) & 3
+            ).astype(np.uint8)
+
+
+def _put_meta(flat, base, r, kind, s16, z16):
+    off = base[:, None] + meta_location(kind, r[:, None], _GR[None, :])
+    for field, vals in ((0, s16), (2, z16)):
+        u = np.asarray(vals, dtype=np.float16).view(np.uint16)
+        flat[off + field] = (u & 0xFF).astype(np.uint8)
+        flat[off + field + 1] = (u >> 8).astype(np.uint8)
+
+
+def _get_meta(flat, base, r, kind):
+    off = base[:, None] + meta_location(kind, r[:, None], _GR[None, :])
+    out = []
+    for field in (0, 2):
+        u = flat[off + field].astype(np.uint16) | (flat[off + field + 1].astype(np.uint16) << 8)
+        out.append(u.view(np.float16))
+    return out[0], out[1]
+
+
+def write_slots(flat, base, r, kcodes, ks16, kz16, vcodes, vs16, vz16) -> None:
+    """Store n tokens' K and V encodings (in place) into a flat byte pool.
+
+    base: int [n] byte offset of each token's record; r: int [n] page slot of each token;
+    codes [n][128]; scales/zeros [n][4].  Only the bits belonging to each token's slot change.
+    """
+    base = np.asarray(base, dtype=np.int64)
+    r = np.asarray(r, dtype=np.int64)
+    _put_codes(flat, base, r, kcodes, k_code_location)
+    _put_codes(flat, base, r, vcodes, v_code_location)
+    _put_meta(flat, base, r, "k", ks16, kz16)
+    _put_meta(flat, base, r, "v", vs16, vz16)
+
+
+def read_slots(flat, base, r):
+    """Decode n tokens: (kcodes, ks16, kz16, vcodes, vs16, vz16), codes [n][128], meta [n][4]."""
+    base = np.asarray(base, dtype=np.int64)
+    r = np.asarray(r, dtype=np.int64)
+    kc = _get_codes(flat, base, r, k_code_location)
+    vc = _get_codes(flat, base, r, v_code_location)
+    ks, kz = _get_meta(flat, base, r, "k")
+    vs, vz = _get_meta(flat, base, r, "v")
+    return kc, ks, kz, vc, vs, vz
+
+
+def write_slot(record: np.ndarray, r: int, kcodes, ks16, kz16, vcodes, vs16, vz16) -> None:
+    """Single-token form of write_slots on one 1536-byte record."""
+    write_slots(record, [0], [r], np.asarray(kcodes)[None], np.asarray(ks16)[None],
+                np.asarray(kz16)[None], np.asarray(vcodes)[None], np.asarray(vs16)[None],
+                np.asarray(vz16)[None])
+
+
+def read_slot(record: np.ndarray, r: int):
+    """Single-token form of read_slots on one record."""
+    return tuple(a[0] for a in read_slots(record, [0], [r]))
+
+
+# ----------------------------------------------------------------------------------------
+# Cache model: paged INT2 records + dense BF16 sink/window store.
+# ----------------------------------------------------------------------------------------
+
+def sink_window_index(pos: int, num_sink: int, window: int, new_len: int):
+    """Row of the BF16 store that position `pos` goes to when the sequence length becomes
+    new_len, or None.  Sinks are positions [0, S) at rows [0, S); a window position
+    p >= S with p >= new_len - W goes to row S + (p mod W) (a ring)."""
+    if pos < num_sink:
+        return pos
+    if window > 0 and pos >= new_len - window:
+        return num_sink + pos % window
+    return None
+
+
+class Cache:
+    """Oracle model of the cache a sequence batch writes.
+
+    pages:   uint8 [num_pages][Hkv][1536]  INT2 records.
+    sinkwin: uint16 [num_slots][Hkv][S+W][2][128] bf16 bits of the rotated K (index 0) and
+             V (index 1) rows of sink and window positions.
+    """
+
+    def __init__(self, num_pages, num_kv_heads, num_slots, num_sink, window, fill=0):
+        self.pages = np.full((num_pages, num_kv_heads, RECORD), fill, dtype=np.uint8)
+        self.sinkwin = np.full((num_slots, num_kv_heads, num_sink + window, 2, D),
+                               fill | (fill << 8), dtype=np.uint16)
+        self.num_sink = num_sink
+        self.window = window
+        self.hkv = num_kv_heads
+
+    def _bases(self, table_row, h, positions):
+        pages = np.asarray(table_row)[np.asarray(positions) // PAGE].astype(np.int64)
+        return (pages * self.hkv + h) * RECORD, np.asarray(positions) % PAGE
+
+    def append(self, table_row, slot, start_pos, k_bits, v_bits, rot_k32, rot_v32, clip_k, clip_v):
+        """Append n new tokens of one sequence at positions start_pos .. start_pos+n-1.
+
+        k_bits, v_bits: uint16 [n][Hkv][128] unrotated bf16 rows.  Every new position gets its
+        INT2 encoding in its page record; sink positions and the last W positions of the new
+        length also get bf16(y) in the BF16 store.
+        """
+        n = k_bits.shape[0]
+        new_len = start_pos + n
+        positions = np.arange(start_pos, new_len)
+        flat = self.pages.reshape(-1)
+        for h in range(self.hkv):
+            yk, kc, ks, kz = quantize_rows(k_bits[:, h], rot_k32[h], clip_k)
+            yv, vc, vs, vz = quantize_rows(v_bits[:, h], rot_v32[h], clip_v)
+            base, r = self._bases(table_row, h, positions)
+            write_slots(flat, base, r, kc, ks, kz, vc, vs, vz)
+            kb = f32_to_bf16_bits(yk)
+            vb = f32_to_bf16_bits(yv)
+            for i, pos in enumerate(positions):
+                row = sink_window_index(int(pos), self.num_sink, self.window, new_len)
+                if row is not None:
+                    self.sinkwin[slot, h, row, 0] = kb[i]
+                    self.sinkwin[slot, h, row, 1] = vb[i]
+
+    def read_sequence(self, table_row, slot, h, length):
+        """Keys and values of positions [0, length) of one KV head, in the rotated frame, fp64.
+
+        Positions [0, min(L, S)) and the last min(W, L - n_sink) positions come from the BF16
+        store; the rest is dequantised from the INT2 records.  Returns (k, v) fp64 [L][128]
+        and a bool [L] mask marking the INT2 positions.
+        """
+        S, W = self.num_sink, self.window
+        n_sink = min(length, S)
+        n_win = min(W, length - n_sink)
+        k = np.empty((length, D))
+        v = np.empty((length, D))
+        is_int2 = np.zeros(length, dtype=bool)
+        for p in range(length):
+            if p < n_sink:
+                row = p
+            elif p >= length - n_win:
+                row = S + p % W
+            else:
+                row = None
+            if row is not None:
+                k[p] = bf16_bits_to_f64(self.sinkwin[slot, h, row, 0])
+                v[p] = bf16_bits_to_f64(self.sinkwin[slot, h, row, 1])
+            else:
+                is_int2[p] = True
+        idx = np.nonzero(is_int2)[0]
+        if idx.size:
+            kc, ks, kz, vc, vs, vz = self.decode_positions(table_row, h, idx)
+            k[idx] = dequant(kc, ks, kz)
+            v[idx] = dequant(vc, vs, vz)
+        return k, v, is_int2
+
+    def decode_positions(self, table_row, h, positions):
+        base, r = self._bases(table_row, h, positions)
+        return read_slots(self.pages.reshape(-1), base, r)
+
+
+# ----------------------------------------------------------------------------------------
+# Attention.
+# ----------------------------------------------------------------------------------------
+
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
+    """Single-query softmax attention in fp64: returns (o [128], lse, weights [L]).
+
+    z_p = sm * (q . k_p); a = softmax(z); o = sum_p a_p v_p; lse = max z + ln sum exp(z - max z).
+    """
+    z = float(np.float32(sm_scale)) * (k @ q)
+    zmax = z.max()
+    e = np.exp(z - zmax)
+    den = e.sum()
+    a = e / den
+    return a @ v, zmax + np.log(den), a
+
+
+def decode_attention(cache: Cache, table, slots, seq_lens, q_bits, rot_k32, rot_v32, sm_scale,
+                     batches=None, heads=None):
+    """Decode attention over the mixed cache, rotated frame inside, original frame out.
+
+    q' = q . R_K(h); keys/values are the stored rotated rows (BF16 sinks/window, dequantised
+    INT2 bulk); o = softmax(sm q'.k) v in the rotated frame; out = o . R_V(h)^T.
+
+    Returns out fp64 [B][Hq][128] and lse fp64 [B][Hq] (NaN where not computed).
+    """
+    B, Hq = q_bits.shape[0], q_bits.shape[1]
+    G = Hq // cache.hkv
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    batches = range(B) if batches is None else batches
+    for b in batches:
+        L = int(seq_lens[b])
+        qr = rotate_query(q_bits[b], rot_k32, G)
+        kv_heads = range(cache.hkv) if heads is None else sorted({j // G for j in heads})
+        for h in kv_heads:
+            k, v, _ = cache.read_sequence(table[b], slots[b], h, L)
+            rv = np.asarray(rot_v32[h], dtype=np.float32).astype(np.float64)
+            for j in range(h * G, (h + 1) * G):
+                if heads is not None and j not in heads:
+                    continue
+                o, l, _ = softmax_attention(qr[j], k, v, sm_scale)
+                out[b, j] = o @ rv.T
+                lse[b, j] = l
+    return out, lse
+
+
+def merge_partials(m2: np.ndarray, l: np.ndarray, o: np.ndarray):
+    """Merge split partials of one query row.
+
+    Each split s carries m_s (its running max of the logits, in log2 units, i.e. logit*log2 e),
+    l_s = sum of 2^(logit*log2e - m_s) and o_s = sum of 2^(...) v (unnormalised).  Splits with
+    l_s == 0 are empty.  The merge is the exact softmax over the union:
+        M = max_s m_s,  l = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) o_s / l,
+        lse = M ln 2 + ln l   (natural log of the sum of exp of the logits).
+    m2, l: [S]; o: [S][128].  Returns (o fp64 [128], lse).
+    """
+    m2 = np.asarray(m2, np.float64)
+    l = np.asarray(l, np.float64)
+    o = np.asarray(o, np.float64)
+    live = l > 0
+    M = m2[live].max()
+    w = np.where(live, np.exp2(np.where(live, m2, M) - M), 0.0)
+    lt = (w * l).sum()
+    ot = (w[:, None] * o).sum(axis=0) / lt
+    return ot, M * np.log(2.0) + np.log(lt)
+
+
+# ----------------------------------------------------------------------------------------
+# BF16 paged baseline (no rotation, no quantisation).
+#
+# Page layout per (page, KV head), 8192 bytes: K as [16 tokens][128] bf16, then V transposed
+# as [128 channels][16 tokens] bf16.
+# ----------------------------------------------------------------------------------------
+
+BF16_PAGE_ELEMS = 2 * PAGE * D
+
+
+def bf16_write_token(page: np.ndarray, r: int, k_bits_row, v_bits_row) -> None:
+    """page: uint16 [4096]; store token slot r's K row and V column."""
+    page[r * D:(r + 1) * D] = k_bits_row
+    page[PAGE * D + np.arange(D) * PAGE + r] = v_bits_row
+
+
+def bf16_read_page(page: np.ndarray):
+    k = page[:PAGE * D].reshape(PAGE, D)
+    v = page[PAGE * D:].reshape(D, PAGE).T
+    return k, v
+
+
+def bf16_decode_attention(pages, table, seq_lens, q_bits, sm_scale, num_kv_heads):
+    """Plain softmax attention over the unrotated bf16 pages. Returns out fp64 [B][Hq][128], lse."""
+    B, Hq = q_bits.shape[0], q_bits.shape[1]
+    G = Hq // num_kv_heads
+    out = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(num_kv_heads):
+            ks = np.empty((L, D))
+            vs = np.empty((L, D))
+            for p0 in range(0, L, PAGE):
+                kp, vp = bf16_read_page(pages[int(table[b][p0 // PAGE]), h])
+                n = min(PAGE, L - p0)
+                ks[p0:p0 + n] = bf16_bits_to_f64(kp[:n])
+                vs[p0:p0 + n] = bf16_bits_to_f64(vp[:n])
+            for j in range(h * G, (h + 1) * G):
+                o, l, _ = softmax_attention(bf16_bits_to_f64(q_bits[b, j]), ks, vs, sm_scale)
+                out[b, j] = o
+                lse[b, j] = l
+    return out, lse
