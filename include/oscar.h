@@ -1,0 +1,216 @@
+/*
+ * oscar.h - C ABI of the rotated INT2 KV cache and its mixed-precision paged decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method: every cached key/value row is multiplied by a fixed, offline-derived orthogonal
+ * rotation, clipped with fixed thresholds and stored in 2 bits per element inside a paged KV
+ * cache, while a few initial "sink" tokens and a recent window of tokens stay in BF16; decode
+ * attention reads the three parts in one fused softmax.  Sources: OSCAR project card
+ * "FutureMLS-Lab/OSCAR" (agentlenshq.com), section "How it works"; OSCAR paper
+ * (thelatestinai.com/papers/2605.17757), "Abstract"; write-up "OSCAR: Cut LLM Inference Costs
+ * 8x with 2-bit KV Cache Quantization" (strixaai.com), sections "Practical Summary" and
+ * "How OSCAR Works".
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers (memory on the GPU that is current when the call is
+ *     made), except `lay`, which is a host pointer read during the call only.
+ *   - The caller owns all memory.  The library never allocates, frees or keeps a pointer past
+ *     the call.  It keeps no state between calls.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the default stream)
+ *     and returns without synchronising.  Calls on one stream run in order; calls that write
+ *     the same cache from two streams at once race.
+ *   - Host-visible arguments are checked before anything is launched; on a non-zero return
+ *     nothing was launched.  OSCAR_ERR_HIP reports a launch failure (hipGetLastError).
+ *   - Values that live in device memory (lengths, positions, block-table entries, slot ids)
+ *     are not checked by the host.  The kernels skip any page id outside [0, num_pages), any
+ *     logical page outside the block-table row and any slot outside [0, num_slots) instead of
+ *     touching memory outside the caller's buffers; results for such inputs are unspecified.
+ *   - Inputs must be finite, and every rotated value must stay below 65504 in magnitude so the
+ *     fp16 scales and zeros stay finite.
+ *   - Pointers to pages, stores, q, k_new, v_new and workspace must be 16-byte aligned.
+ *
+ * Fixed geometry: head_dim 128, page_size 16 tokens, quantisation group 32 channels.
+ *
+ * INT2 page record (one per physical page and KV head, 1536 bytes, all fields little-endian):
+ *   [   0,  512) K codes.  Channel c of page slot r (token r of the page) belongs to 16-channel
+ *                word d = c/16, stored as the dword at 8*(16*(d%4) + r) + 4*(d/4); inside the
+ *                dword, byte (c%16)/4, bits 2*(c%4)..+1.
+ *   [ 512, 1024) V codes.  Channel c of slot r: chunk L = 16*(r/4) + c%16 at 512 + 8*L;
+ *                dword (r%4)/2 of the chunk, 16-bit half r%2; bits 2*(c/16)..+1 of the half.
+ *   [1024, 1280) K scale/zero: group g of slot r at 1024 + 64*g + 4*r, fp16 scale then fp16 zero.
+ *   [1280, 1536) V scale/zero, same arrangement at 1280 + 64*g + 4*r.
+ *   A code q in group g decodes to scale_g * q + zero_g, in the rotated frame.
+ *   Pool: uint8 [num_pages][num_kv_heads][1536].
+ *
+ * BF16 sink/window store: uint16 (bf16 bits) [num_slots][num_kv_heads][S+W][2][128], rotated
+ *   K (index 0) and V (index 1).  Sink position p < S lives in row p; a window position p >= S
+ *   lives in row S + (p mod W).
+ *
+ * Block table: int32 [batch][max_pages_per_seq]; entry [b][i] is the physical page holding
+ *   positions 16*i .. 16*i+15 of sequence b.  Unused entries should be -1.
+ */
+#ifndef OSCAR_H_
+#define OSCAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad ratio, ... */
+  OSCAR_ERR_UNSUPPORTED = 2,        /* geometry other than 128 / 16 / 32, too many heads */
+  OSCAR_ERR_WORKSPACE_TOO_SMALL = 3,
+  OSCAR_ERR_HIP = 4                 /* a kernel launch failed */
+};
+
+typedef struct oscar_layout {
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* must be 128 */
+  int32_t page_size;          /* must be 16 */
+  int32_t group_size;         /* must be 32 */
+  int32_t num_sink;           /* S >= 0 */
+  int32_t window;             /* W >= 0; S + W <= 1024 */
+  int32_t num_pages;          /* physical pages in the pool */
+  int32_t max_pages_per_seq;  /* block-table row stride */
+  int32_t num_slots;          /* sequences the BF16 sink/window store can hold */
+} oscar_layout;
+
+/* Human-readable name of a status code (static storage). */
+const char* oscar_status_string(int32_t status);
+
+/*
+ * Rotate, clip, quantise and append new K/V rows to the cache.
+ * (OSCAR project card, "How it works": fixed per-layer rotations and clipping thresholds, INT2
+ *  bulk with BF16 sinks and recent window; OSCAR paper, "Abstract": INT2 kernel compatible
+ *  with a paged KV cache.)
+ *
+ * For sequence b, rows new_offsets[b] .. new_offsets[b+1]-1 of k_new / v_new are its new
+ * tokens, at positions start_pos[b], start_pos[b]+1, ...  For every new row x of KV head h:
+ *   y = x . R (R = rot_k[h] or rot_v[h]; row-vector convention), computed as an fp64 sum over
+ *       the 128 input channels in ascending order, rounded once to fp32;
+ *   for each 32-channel group of y: mx, mn = max, min; mx_c = clip*mx, mn_c = clip*mn (fp32);
+ *       scale = fp16(fp32(mx_c - mn_c) / 3), zero = fp16(mn_c) (round to nearest even);
+ *   code = clamp(rint((y - zero) / scale), 0, 3) in fp32 (0 when scale == 0).
+ * Every new position's codes and scales go to its page record; a position p with p < S, or
+ * p >= start_pos[b] + n_new - W, also gets bf16(y) in the sink/window store row of slot
+ * slot_ids[b] (slot b when slot_ids is NULL).
+ *
+ *   lay          host; geometry and pool sizes.
+ *   pages        uint8 [num_pages][Hkv][1536], written.
+ *   sinkwin      uint16 [num_slots][Hkv][S+W][2][128], written (may be NULL when S + W == 0).
+ *   block_table  int32 [batch][max_pages_per_seq].
+ *   slot_ids     int32 [batch] or NULL.
+ *   batch        number of sequences (>= 0; 0 launches nothing).
+ *   total_new    rows in k_new / v_new (== new_offsets[batch]; >= 0).
+ *   k_new, v_new bf16 bits [total_new][Hkv][128], unrotated (after RoPE).
+ *   new_offsets  int32 [batch+1], non-decreasing, new_offsets[0] == 0.
+ *   start_pos    int32 [batch].
+ *   rot_k, rot_v fp32 [Hkv][128][128], row-major.
+ *   clip_k, clip_v  clip ratios, 0 < clip <= 1.
+ * Two new rows of one call must not share a (page, slot).
+ */
+int32_t oscar_rotate_quantize_append(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+    void* stream);
+
+/*
+ * Bytes of workspace oscar_decode_attention / oscar_bf16_decode_attention need for `batch`
+ * sequences of `num_q_heads` query heads split at most `max_splits` ways.  Returns 0 for
+ * invalid arguments.
+ */
+size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits);
+
+/*
+ * Mixed-precision paged decode attention, first stage: per (sequence, KV head, split) partial
+ * softmax results, written to `workspace`.  oscar_combine finishes the step.
+ * (OSCAR project card, "How it works": BF16 sink + recent window + INT2 bulk under fused
+ *  mixed-precision flash attention; OSCAR paper, "Abstract": paged INT2 attention kernel.)
+ *
+ * For sequence b of length L = seq_lens[b] (positions 0..L-1, including the token being
+ * decoded) and query head j of KV head h = j / (num_q_heads / Hkv):
+ *   q' = q[b][j] . rot_k[h];
+ *   positions [0, min(L,S)) and the last min(W, L - min(L,S)) positions are read from the
+ *   BF16 store; the others are decoded from their INT2 records;
+ *   logits z_p = sm_scale * (q' . k_p), and the partials hold, per split, the max of
+ *   z_p*log2(e), the sum of 2^(z_p*log2(e) - max), and the matching unnormalised weighted sum
+ *   of the rotated values.
+ * The INT2 positions are split into runs of split_pages pages (split s covers logical pages
+ * [s*split_pages, (s+1)*split_pages), the last split everything after); the BF16 positions
+ * form one more split.
+ *
+ *   q            bf16 bits [batch][num_q_heads][128] (after RoPE, unrotated).
+ *   seq_lens     int32 [batch], >= 1.
+ *   rot_k        fp32 [Hkv][128][128].
+ *   sm_scale     softmax scale, usually 1/sqrt(128).
+ *   split_pages  pages per split, >= 1.
+ *   max_splits   INT2 splits per sequence, >= 1.
+ *   workspace    device buffer of at least oscar_decode_workspace_bytes(batch, num_q_heads,
+ *                max_splits) bytes; contents on entry do not matter.
+ * num_q_heads must be a multiple of Hkv with num_q_heads / Hkv in {1, 2, 4, 8}.
+ */
+int32_t oscar_decode_attention(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k, float sm_scale,
+    int32_t split_pages, int32_t max_splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second stage: merge the splits of every (sequence, query head) in ascending split order,
+ * normalise, and rotate back with the transpose of the value rotation:
+ *   M = max_s m_s, l = sum_s 2^(m_s - M) l_s, o' = sum_s 2^(m_s - M) o'_s / l,
+ *   out = o' . rot_v[h]^T,  lse = M*ln(2) + ln(l)  (natural-log sum of exp of the logits).
+ * (OSCAR paper, "Abstract": attention stays exact under the fixed orthogonal rotation.)
+ *
+ *   workspace  as written by oscar_decode_attention / oscar_bf16_decode_attention with the
+ *              same batch, num_q_heads and max_splits.
+ *   rot_v      fp32 [Hkv][128][128], or NULL for no rotation (BF16 baseline).
+ *   out        fp32 [batch][num_q_heads][128], written.
+ *   lse        fp32 [batch][num_q_heads] or NULL.
+ * A row with no positions gets out = 0 and lse = -inf.
+ */
+int32_t oscar_combine(
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_splits,
+    const void* workspace, size_t workspace_bytes, const float* rot_v,
+    float* out, float* lse, void* stream);
+
+/*
+ * BF16 paged baseline in the same library: no rotation, no quantisation.  The pages' memory,
+ * throughput and latency claims are all stated against a BF16 KV cache (write-up, "Practical
+ * Summary"; OSCAR paper, "Abstract").
+ *
+ * BF16 page (one per physical page and KV head, 8192 bytes): K as bf16 [16 tokens][128],
+ * then V transposed as bf16 [128 channels][16 tokens].  Pool: uint16 [num_pages][Hkv][4096].
+ * Only num_kv_heads, head_dim, page_size, num_pages and max_pages_per_seq of `lay` are used.
+ */
+int32_t oscar_bf16_append(
+    const oscar_layout* lay, uint16_t* pages, const int32_t* block_table,
+    int32_t batch, int32_t total_new, const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos, void* stream);
+
+/*
+ * BF16 baseline decode, first stage: same split scheme and workspace format as
+ * oscar_decode_attention over all positions [0, L) of the BF16 pages (q unrotated); finish
+ * with oscar_combine(..., rot_v = NULL, ...).
+ */
+int32_t oscar_bf16_decode_attention(
+    const oscar_layout* lay, const uint16_t* pages, const int32_t* block_table,
+    int32_t batch, int32_t num_q_heads, const uint16_t* q, const int32_t* seq_lens,
+    float sm_scale, int32_t split_pages, int32_t max_splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H_ */

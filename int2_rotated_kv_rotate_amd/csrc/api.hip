@@ -1,0 +1,167 @@
+// C ABI entry points: validate host-visible arguments, then enqueue the kernels on the caller's
+// stream.  No allocation, no synchronisation, no state.
+#include "../../include/oscar.h"
+#include "oscar_internal.h"
+
+using namespace oscar;
+
+namespace {
+
+int32_t check_layout(const oscar_layout* lay) {
+  if (lay == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->head_dim != kHeadDim || lay->page_size != kPage || lay->group_size != kGroup)
+    return OSCAR_ERR_UNSUPPORTED;
+  if (lay->num_kv_heads < 1 || lay->num_kv_heads > 65535) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink < 0 || lay->window < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > kMaxSinkWindow) return OSCAR_ERR_UNSUPPORTED;
+  if (lay->num_pages < 0 || lay->max_pages_per_seq < 1 || lay->num_slots < 0)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  return OSCAR_OK;
+}
+
+CacheGeom geom(const oscar_layout* lay) {
+  return CacheGeom{lay->num_kv_heads, lay->num_sink, lay->window,
+                   lay->num_pages, lay->max_pages_per_seq, lay->num_slots};
+}
+
+int32_t check_heads(int32_t hq, int32_t hkv) {
+  if (hq < 1 || hq % hkv != 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  const int G = hq / hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return OSCAR_ERR_UNSUPPORTED;
+  return OSCAR_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? OSCAR_OK : OSCAR_ERR_HIP; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_status_string(int32_t status) {
+  switch (status) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case OSCAR_ERR_UNSUPPORTED: return "unsupported geometry";
+    case OSCAR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case OSCAR_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int32_t oscar_rotate_quantize_append(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+    void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || total_new == 0) return OSCAR_OK;
+  if (!pages || !block_table || !k_new || !v_new || !new_offsets || !start_pos || !rot_k || !rot_v)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rot_k) ||
+      !aligned16(rot_v) || (sinkwin && !aligned16(sinkwin)))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_append(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                  total_new, k_new, v_new, new_offsets, start_pos, rot_k, rot_v,
+                                  clip_k, clip_v, (hipStream_t)stream));
+}
+
+size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits) {
+  if (batch < 0 || num_q_heads < 1 || max_splits < 1) return 0;
+  return workspace_bytes(batch, num_q_heads, max_splits);
+}
+
+int32_t oscar_decode_attention(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k, float sm_scale,
+    int32_t split_pages, int32_t max_splits,
+    void* workspace, size_t workspace_bytes_given, void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || split_pages < 1 || max_splits < 1 || max_splits > 65535)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return OSCAR_OK;
+  if (!pages || !block_table || !q || !seq_lens || !rot_k || !workspace)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(q) || !aligned16(workspace) || !aligned16(rot_k) ||
+      (sinkwin && !aligned16(sinkwin)))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
+  return hip_status(launch_decode(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                  num_q_heads, q, seq_lens, rot_k, sm_scale, split_pages, ws,
+                                  (hipStream_t)stream));
+}
+
+int32_t oscar_combine(
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_splits,
+    const void* workspace, size_t workspace_bytes_given, const float* rot_v,
+    float* out, float* lse, void* stream) {
+  if (batch < 0 || num_kv_heads < 1 || max_splits < 1 || max_splits > 65535)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  int32_t st = check_heads(num_q_heads, num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  if (batch == 0) return OSCAR_OK;
+  if (!workspace || !out) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace) || (rot_v && !aligned16(rot_v))) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws = make_workspace(const_cast<void*>(workspace), batch, num_q_heads, max_splits);
+  return hip_status(launch_combine(batch, num_q_heads, num_kv_heads, ws, rot_v, out, lse,
+                                   (hipStream_t)stream));
+}
+
+int32_t oscar_bf16_append(
+    const oscar_layout* lay, uint16_t* pages, const int32_t* block_table,
+    int32_t batch, int32_t total_new, const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos, void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || total_new == 0) return OSCAR_OK;
+  if (!pages || !block_table || !k_new || !v_new || !new_offsets || !start_pos)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new)) return OSCAR_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_bf16_append(geom(lay), pages, block_table, batch, total_new, k_new,
+                                       v_new, new_offsets, start_pos, (hipStream_t)stream));
+}
+
+int32_t oscar_bf16_decode_attention(
+    const oscar_layout* lay, const uint16_t* pages, const int32_t* block_table,
+    int32_t batch, int32_t num_q_heads, const uint16_t* q, const int32_t* seq_lens,
+    float sm_scale, int32_t split_pages, int32_t max_splits,
+    void* workspace, size_t workspace_bytes_given, void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || split_pages < 1 || max_splits < 1 || max_splits > 65535)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return OSCAR_OK;
+  if (!pages || !block_table || !q || !seq_lens || !workspace) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(q) || !aligned16(workspace)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
+  return hip_status(launch_bf16_decode(geom(lay), pages, block_table, batch, num_q_heads, q,
+                                       seq_lens, sm_scale, split_pages, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

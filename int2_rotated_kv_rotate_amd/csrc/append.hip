@@ -1,0 +1,212 @@
+// Rotate-clip-quantize-append: new K/V rows -> fixed orthogonal rotation -> per-token groups of
+// 32 channels clipped and quantised to 2 bits -> paged INT2 records (+ BF16 sink/window rows).
+//
+// Method: OSCAR project card "FutureMLS-Lab/OSCAR", section "How it works" (fixed per-layer
+// rotations and clipping thresholds, INT2 bulk, BF16 sink and recent window); OSCAR paper,
+// "Abstract" (rotation + clipping computed offline and applied as fixed parameters; INT2 cache
+// kept compatible with paged serving).  The bit-level rules (fp64 ascending accumulation of the
+// rotation, fp32 scale formula, fp16 scale/zero, round-half-even codes) are this library's
+// definition of the encoding and are reproduced bit for bit by the CPU oracle.
+//
+// This translation unit is built with -ffp-contract=off: the quantiser is an fp32 formula that
+// must not be fused.
+//
+// One workgroup = 16 consecutive new rows of one (KV head, K|V).  The 64 KiB rotation matrix is
+// staged in LDS once per workgroup; each thread accumulates 2 rows x 4 output channels in fp64.
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+constexpr int kRows = 16;
+constexpr int kThreads = 256;
+
+// Keeps the compiler from fusing an fp32 result into a following conversion (it would
+// otherwise turn fp16(c * mn) into one single-rounding mixed-precision FMA).
+__device__ __forceinline__ float materialize(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+struct RowInfo {
+  long long rec;     // byte offset of the row's page record in the pool, -1 = skip
+  int slot_in_page;  // 0..15
+  long long sw;      // element offset of the row's bf16 K/V row in the store, -1 = none
+};
+
+__global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
+    CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
+    int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ new_offsets, const int32_t* __restrict__ start_pos,
+    const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
+    float clip_v) {
+#pragma clang fp contract(off)
+  __shared__ float4 s_rot[kHeadDim * kHeadDim / 4];   // R[i][j], row-major, 64 KiB
+  __shared__ float s_x[kRows][kHeadDim];              // input rows (bf16 widened)
+  __shared__ float s_y[kRows][kHeadDim + 1];          // rotated rows (fp32)
+  __shared__ uint8_t s_code[kRows][kHeadDim];
+  __shared__ RowInfo s_info[kRows];
+
+  const int t = threadIdx.x;
+  const int row0 = blockIdx.x * kRows;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const float* rot = (is_v ? rot_v : rot_k) + (size_t)h * kHeadDim * kHeadDim;
+  const uint16_t* src = is_v ? v_new : k_new;
+  const float clip = is_v ? clip_v : clip_k;
+  const int nrows = min(kRows, total_new - row0);
+
+  // Stage R (fp32) and the rows.
+  const float4* rot4 = reinterpret_cast<const float4*>(rot);
+  for (int i = t; i < kHeadDim * kHeadDim / 4; i += kThreads) s_rot[i] = rot4[i];
+  for (int i = t; i < kRows * kHeadDim; i += kThreads) {
+    int r = i / kHeadDim, c = i % kHeadDim;
+    s_x[r][c] = r < nrows ? bf16_to_f32(src[((size_t)(row0 + r) * g.hkv + h) * kHeadDim + c]) : 0.f;
+  }
+  if (t < kRows) {
+    RowInfo info{-1, 0, -1};
+    if (t < nrows) {
+      int n = row0 + t;
+      int b = row_to_seq(new_offsets, batch, n);
+      int first = new_offsets[b];
+      int nnew = new_offsets[b + 1] - first;
+      int pos = start_pos[b] + (n - first);
+      int new_len = start_pos[b] + nnew;
+      int lp = pos / kPage;
+      if (pos >= 0 && lp < g.max_pages) {
+        int page = block_table[(size_t)b * g.max_pages + lp];
+        if (page >= 0 && page < g.num_pages) {
+          info.rec = ((long long)page * g.hkv + h) * kRecord;
+          info.slot_in_page = pos % kPage;
+        }
+      }
+      int slot = slot_ids ? slot_ids[b] : b;
+      int row = -1;
+      if (pos >= 0 && pos < g.num_sink) row = pos;
+      else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
+        row = g.num_sink + pos % g.window;
+      if (row >= 0 && sinkwin != nullptr && slot >= 0 && slot < g.num_slots)
+        info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
+                  (is_v ? kHeadDim : 0);
+    }
+    s_info[t] = info;
+  }
+  __syncthreads();
+
+  // y = x . R: thread -> rows {2*rp, 2*rp+1}, channels 4*jq .. 4*jq+3; fp64, i ascending.
+  {
+    const int rp = t / 32, jq = t % 32;
+    const int r0 = 2 * rp, r1 = 2 * rp + 1;
+    double a0[4] = {0.0, 0.0, 0.0, 0.0}, a1[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int i = 0; i < kHeadDim; ++i) {
+      const double x0 = (double)s_x[r0][i];
+      const double x1 = (double)s_x[r1][i];
+      const float4 rv = s_rot[i * (kHeadDim / 4) + jq];
+      const double rr[4] = {(double)rv.x, (double)rv.y, (double)rv.z, (double)rv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a0[k] = __fma_rn(x0, rr[k], a0[k]);   // product exact in fp64: same as mul then add
+        a1[k] = __fma_rn(x1, rr[k], a1[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s_y[r0][4 * jq + k] = (float)a0[k];
+      s_y[r1][4 * jq + k] = (float)a1[k];
+    }
+  }
+  __syncthreads();
+
+  // Group parameters and codes: threads 0..63 -> (row, group).
+  if (t < kRows * kGroups) {
+    const int r = t / kGroups, gi = t % kGroups;
+    const RowInfo info = s_info[r];
+    if (r < nrows) {
+      float mx = s_y[r][gi * kGroup], mn = mx;
+      for (int c = 1; c < kGroup; ++c) {
+        float v = s_y[r][gi * kGroup + c];
+        mx = fmaxf(mx, v);
+        mn = fminf(mn, v);
+      }
+      mx = mx + 0.0f;  // a signed-zero extreme becomes +0
+      mn = mn + 0.0f;
+      const float mx_c = clip * mx;
+      const float mn_c = clip * mn;
+      const float width = mx_c - mn_c;
+      const float s32 = width / 3.0f;
+      const _Float16 s16 = (_Float16)materialize(s32);
+      const _Float16 z16 = (_Float16)materialize(mn_c);
+      const float s = (float)s16, z = (float)z16;
+      for (int c = 0; c < kGroup; ++c) {
+        int code = 0;
+        if (s != 0.0f) {
+          float q = (s_y[r][gi * kGroup + c] - z) / s;
+          q = __builtin_rintf(q);
+          q = fminf(fmaxf(q, 0.0f), 3.0f);
+          code = (int)q;
+        }
+        s_code[r][gi * kGroup + c] = (uint8_t)code;
+      }
+      if (info.rec >= 0) {
+        uint32_t meta = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+        *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kVMeta : kKMeta) + 64 * gi +
+                                     4 * info.slot_in_page) = meta;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Pack codes into the record.
+  if (!is_v) {
+    // K: row r, 16-channel word d -> dword at 8*(16*(d%4) + slot) + 4*(d/4).
+    if (t < kRows * 8) {
+      const int r = t / 8, d = t % 8;
+      const RowInfo info = s_info[r];
+      if (r < nrows && info.rec >= 0) {
+        uint32_t w = 0;
+        for (int c = 0; c < 16; ++c)
+          w |= (uint32_t)s_code[r][16 * d + c] << (8 * (c / 4) + 2 * (c % 4));
+        *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes +
+                                     8 * (16 * (d % 4) + info.slot_in_page) + 4 * (d / 4)) = w;
+      }
+    }
+  } else {
+    // V: row r, channel residue c16 -> 16-bit half (slot%2) of dword (slot%4)/2 of chunk
+    // 16*(slot/4) + c16; channel c16 + 16*nb at bits 2*nb of the half.
+    const int r = t / 16, c16 = t % 16;
+    const RowInfo info = s_info[r];
+    if (r < nrows && info.rec >= 0) {
+      uint32_t hw = 0;
+      for (int nb = 0; nb < 8; ++nb) hw |= (uint32_t)s_code[r][c16 + 16 * nb] << (2 * nb);
+      const int sl = info.slot_in_page;
+      *reinterpret_cast<uint16_t*>(pages + info.rec + kVCodes + 8 * (16 * (sl / 4) + c16) +
+                                   4 * ((sl % 4) / 2) + 2 * (sl % 2)) = (uint16_t)hw;
+    }
+  }
+
+  // BF16 sink/window rows.
+  for (int i = t; i < kRows * kHeadDim; i += kThreads) {
+    const int r = i / kHeadDim, c = i % kHeadDim;
+    if (r < nrows && s_info[r].sw >= 0) sinkwin[s_info[r].sw + c] = f32_to_bf16_rne(s_y[r][c]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                         const int32_t* block_table, const int32_t* slot_ids, int batch,
+                         int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* new_offsets, const int32_t* start_pos,
+                         const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+                         hipStream_t stream) {
+  if (batch == 0 || total_new == 0) return hipSuccess;
+  dim3 grid((total_new + kRows - 1) / kRows, g.hkv, 2);
+  hipLaunchKernelGGL(rotate_quantize_append_kernel, grid, dim3(kThreads), 0, stream, g, pages,
+                     sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
+                     start_pos, rot_k, rot_v, clip_k, clip_v);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -1,0 +1,115 @@
+// Internal definitions shared by the HIP translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kGroup = 32;
+constexpr int kGroups = kHeadDim / kGroup;
+constexpr int kRecord = 1536;                 // bytes per (page, KV head) INT2 record
+constexpr int kKCodes = 0, kVCodes = 512, kKMeta = 1024, kVMeta = 1280;
+constexpr int kBf16PageElems = 2 * kPage * kHeadDim;  // 4096 bf16 per (page, KV head)
+constexpr int kMaxSinkWindow = 1024;
+
+// Workspace layout (all offsets in bytes from the workspace base).
+//   Q region:  per (b, j) a 1024-byte block
+//     [  0, 512) float q'[128]           rotated query (fp32)
+//     [512, 640) int8  hi[128]           q' ~= qsc * (hi + lo/254), stored in MFMA slot order
+//     [640, 768) int8  lo[128]
+//     [768, 772) float qsc
+//     [772, 788) float qsum[4]           sum of q' over each 32-channel group
+//   O region:  float o'[B][Hq][nslots][128]   unnormalised partial outputs (rotated frame)
+//   ML region: float2 (m, l)[B][Hq][nslots]  m in log2 units, l = sum of 2^(z*log2e - m)
+constexpr int kQBlock = 1024;
+constexpr int kQHiOff = 512, kQLoOff = 640, kQScOff = 768, kQSumOff = 772;
+
+struct Workspace {
+  char* base;
+  int nslots;  // max_splits + 1 (the last slot holds the BF16 sink/window split)
+  size_t q_bytes, o_bytes, ml_bytes;
+  __host__ __device__ char* qblock(int b, int hq, int j) const {
+    return base + ((size_t)b * hq + j) * kQBlock;
+  }
+  __host__ __device__ float* o(int b, int hq, int j, int s) const {
+    return (float*)(base + q_bytes) + (((size_t)b * hq + j) * nslots + s) * kHeadDim;
+  }
+  __host__ __device__ float2* ml(int b, int hq, int j, int s) const {
+    return (float2*)(base + q_bytes + o_bytes) + ((size_t)b * hq + j) * nslots + s;
+  }
+};
+
+inline Workspace make_workspace(void* base, int batch, int hq, int max_splits) {
+  Workspace w;
+  w.base = (char*)base;
+  w.nslots = max_splits + 1;
+  w.q_bytes = (size_t)batch * hq * kQBlock;
+  w.o_bytes = (size_t)batch * hq * w.nslots * kHeadDim * sizeof(float);
+  w.ml_bytes = (size_t)batch * hq * w.nslots * sizeof(float2);
+  return w;
+}
+
+inline size_t workspace_bytes(int batch, int hq, int max_splits) {
+  Workspace w = make_workspace(nullptr, batch, hq, max_splits);
+  return w.q_bytes + w.o_bytes + w.ml_bytes;
+}
+
+struct CacheGeom {
+  int hkv, num_sink, window, num_pages, max_pages, num_slots;
+};
+
+// Host launchers (each defined next to its kernel).
+hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                         const int32_t* block_table, const int32_t* slot_ids, int batch,
+                         int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* new_offsets, const int32_t* start_pos,
+                         const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+                         hipStream_t stream);
+
+hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
+                         const int32_t* block_table, const int32_t* slot_ids, int batch,
+                         int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
+                         float sm_scale, int split_pages, const Workspace& ws,
+                         hipStream_t stream);
+
+hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
+                          float* out, float* lse, hipStream_t stream);
+
+hipError_t launch_bf16_append(const CacheGeom& g, uint16_t* pages, const int32_t* block_table,
+                              int batch, int total_new, const uint16_t* k_new,
+                              const uint16_t* v_new, const int32_t* new_offsets,
+                              const int32_t* start_pos, hipStream_t stream);
+
+hipError_t launch_bf16_decode(const CacheGeom& g, const uint16_t* pages,
+                              const int32_t* block_table, int batch, int hq, const uint16_t* q,
+                              const int32_t* seq_lens, float sm_scale, int split_pages,
+                              const Workspace& ws, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------- device
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Sequence index of flattened row n, given prefix offsets off[0..batch] (binary search).
+__device__ __forceinline__ int row_to_seq(const int32_t* off, int batch, int n) {
+  int lo = 0, hi = batch;  // find largest b with off[b] <= n
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (off[mid] <= n) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace oscar

@@ -1,0 +1,158 @@
+"""Device-side driver for the library: caches in HBM, seeded inputs, one decode step.
+
+Plumbing only (torch for device memory and streams); every step of the method runs in the
+HIP library through ``ops``.  Used by the tests, the smoke check and the benchmark.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import ops
+from . import workload as W
+
+SM_SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
+
+
+@dataclasses.dataclass
+class Problem:
+    """Host-side description of one decode step on a workload (numpy arrays)."""
+    w: W.Workload
+    lens: np.ndarray            # int64 [B], context length including the decoded token
+    table: np.ndarray           # int32 [B][max_pages]
+    num_pages: int
+    rot_k: np.ndarray           # float32 [Hkv][128][128]
+    rot_v: np.ndarray
+    q: np.ndarray               # uint16 bf16 bits [B][Hq][128]
+
+    @property
+    def batch(self):
+        return self.w.batch
+
+
+def make_problem(w: W.Workload, lens: Optional[Sequence[int]] = None, extra_pages: int = 3,
+                 rot_k: Optional[np.ndarray] = None, rot_v: Optional[np.ndarray] = None) -> Problem:
+    lens = W.seq_lengths(w) if lens is None else np.asarray(lens, dtype=np.int64)
+    table, num_pages = W.block_table(w, lens, extra_pages=extra_pages)
+    rk = (W.rotations(w, "k") if rot_k is None else rot_k).astype(np.float32)
+    rv = (W.rotations(w, "v") if rot_v is None else rot_v).astype(np.float32)
+    return Problem(w, lens, table, num_pages, rk, rv, W.queries(w))
+
+
+def as_i16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+
+
+class GpuCache:
+    """INT2 page pool + BF16 sink/window store + block table on the GPU."""
+
+    def __init__(self, p: Problem, device="cuda", fill: Optional[int] = None):
+        w = p.w
+        self.p = p
+        self.device = device
+        self.layout = ops.make_layout(w.num_kv_heads, w.num_sink, w.window, p.num_pages,
+                                      p.table.shape[1], w.batch)
+        self.pages = torch.empty((p.num_pages, w.num_kv_heads, ops.RECORD_BYTES), dtype=torch.uint8,
+                                 device=device)
+        self.sinkwin = torch.empty((w.batch, w.num_kv_heads, max(w.num_sink + w.window, 1), 2, 128),
+                                   dtype=torch.int16, device=device)
+        if fill is not None:
+            self.pages.fill_(fill)
+            v16 = fill | (fill << 8)
+            self.sinkwin.fill_(v16 - 65536 if v16 >= 32768 else v16)
+        self.table = torch.from_numpy(p.table).to(device)
+        self.slots = torch.arange(w.batch, dtype=torch.int32, device=device)
+        self.rot_k = torch.from_numpy(p.rot_k).to(device)
+        self.rot_v = torch.from_numpy(p.rot_v).to(device)
+
+    def append(self, k_rows: Sequence[np.ndarray], v_rows: Sequence[np.ndarray],
+               start: Sequence[int]):
+        """Append rows for every sequence b (bf16 bits [n_b][Hkv][128], n_b may be 0) at
+        positions start[b], start[b]+1, ...  Lists are indexed by sequence."""
+        counts = np.array([r.shape[0] for r in k_rows], dtype=np.int64)
+        if counts.sum() == 0:
+            return
+        offs = np.zeros(len(k_rows) + 1, dtype=np.int32)
+        offs[1:] = np.cumsum(counts)
+        k = as_i16(np.concatenate(k_rows)).to(self.device)
+        v = as_i16(np.concatenate(v_rows)).to(self.device)
+        ops.rotate_quantize_append(
+            self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
+            torch.from_numpy(offs).to(self.device),
+            torch.from_numpy(np.asarray(start, dtype=np.int32)).to(self.device),
+            self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip)
+
+    def fill_context(self, chunk_tokens: int = 1 << 20):
+        """Append positions [0, L_b - 1) of every sequence (everything but the decoded token),
+        in chunks of whole sequences.  Returns the per-sequence last rows (k, v) [1][Hkv][128]."""
+        w = self.p.w
+        hkv = w.num_kv_heads
+        empty = np.zeros((0, hkv, 128), dtype=np.uint16)
+        needle = W.needle_site(w, self.p.lens)
+        last_k, last_v = [], []
+        pend_k = [empty] * w.batch
+        pend_v = [empty] * w.batch
+        pend_n = 0
+        for b in range(w.batch):
+            L = int(self.p.lens[b])
+            kb, vb = W.sequence_kv(w, b, L, needle=needle, q_bits=self.p.q)
+            last_k.append(kb[L - 1:L])
+            last_v.append(vb[L - 1:L])
+            pend_k[b] = kb[:L - 1]
+            pend_v[b] = vb[:L - 1]
+            pend_n += L - 1
+            if pend_n >= chunk_tokens or b == w.batch - 1:
+                self.append(pend_k, pend_v, [0] * w.batch)
+                torch.cuda.synchronize()
+                pend_k = [empty] * w.batch
+                pend_v = [empty] * w.batch
+                pend_n = 0
+        return last_k, last_v
+
+
+class DecodeStep:
+    """Buffers and launches of one decode step: append the new token, attend, combine."""
+
+    def __init__(self, cache: GpuCache, split_pages: int = 128, max_splits: Optional[int] = None):
+        p = cache.p
+        self.cache = cache
+        self.split_pages = split_pages
+        pages_max = int((p.lens.max() + 15) // 16)
+        self.max_splits = max_splits or max(1, (pages_max + split_pages - 1) // split_pages)
+        dev = cache.device
+        self.ws = torch.empty(ops.decode_workspace_bytes(p.batch, p.w.num_q_heads, self.max_splits),
+                              dtype=torch.uint8, device=dev)
+        self.q = as_i16(p.q).to(dev)
+        self.seq_lens = torch.from_numpy(p.lens.astype(np.int32)).to(dev)
+        self.out = torch.empty((p.batch, p.w.num_q_heads, 128), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((p.batch, p.w.num_q_heads), dtype=torch.float32, device=dev)
+        self.new_off = torch.arange(p.batch + 1, dtype=torch.int32, device=dev)
+        self.start = torch.from_numpy((p.lens - 1).astype(np.int32)).to(dev)
+        self.k_last = None
+        self.v_last = None
+
+    def set_new_token(self, last_k, last_v):
+        self.k_last = as_i16(np.concatenate(last_k)).to(self.cache.device)
+        self.v_last = as_i16(np.concatenate(last_v)).to(self.cache.device)
+
+    def append_new(self, stream=None):
+        c = self.cache
+        ops.rotate_quantize_append(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.k_last,
+                                   self.v_last, self.new_off, self.start, c.rot_k, c.rot_v,
+                                   c.p.w.clip, c.p.w.clip, stream)
+
+    def attend(self, stream=None):
+        c = self.cache
+        p = c.p
+        ops.decode_attention(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.q, self.seq_lens,
+                             c.rot_k, SM_SCALE, self.split_pages, self.max_splits, self.ws, stream)
+        ops.combine(p.batch, p.w.num_q_heads, p.w.num_kv_heads, self.max_splits, self.ws, c.rot_v,
+                    self.out, self.lse, stream)
+
+    def run(self, stream=None):
+        self.append_new(stream)
+        self.attend(stream)

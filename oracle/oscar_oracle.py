@@ -103,7 +103,8 @@ def rotate_query(q_bits: np.ndarray, rot_k32: np.ndarray, group: int) -> np.ndar
 def group_params(y: np.ndarray, clip: float):
     """fp16 scale and zero of every 32-channel group of every rotated row.
 
-    For each group: mx = max, mn = min of the fp32 values; the clip ratio c (as fp32) scales
+    For each group: mx = max, mn = min of the fp32 values (a -0.0 extreme counts as +0.0);
+    the clip ratio c (as fp32) scales
     both ends, mx_c = c*mx and mn_c = c*mn in fp32; the step is s = (mx_c - mn_c) / 3 in fp32
     (3 = number of steps between 4 levels); the stored scale is fp16(s) and the stored zero
     is fp16(mn_c), both rounded to nearest even.
@@ -113,8 +114,10 @@ def group_params(y: np.ndarray, clip: float):
     y = np.asarray(y, dtype=np.float32)
     c = np.float32(clip)
     g = y.reshape(y.shape[0], NGROUPS, GROUP)
-    mx = g.max(axis=2)
-    mn = g.min(axis=2)
+    # signed zeros: an extreme equal to -0.0 is taken as +0.0 (x + 0 in fp32), so the stored
+    # zero's sign bit never depends on the order of a group's +0/-0 entries
+    mx = (g.max(axis=2) + np.float32(0)).astype(np.float32)
+    mn = (g.min(axis=2) + np.float32(0)).astype(np.float32)
     mx_c = (c * mx).astype(np.float32)
     mn_c = (c * mn).astype(np.float32)
     width = (mx_c - mn_c).astype(np.float32)

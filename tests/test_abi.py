@@ -1,0 +1,116 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects invalid host-visible arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from int2_rotated_kv_rotate_amd import ops
+    return ops.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    from int2_rotated_kv_rotate_amd import ops
+    assert _declared_functions() == sorted(ops.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.oscar_status_string(code)
+    assert lib.oscar_status_string(99) == b"unknown status"
+
+
+def test_workspace_size(lib):
+    from int2_rotated_kv_rotate_amd import ops
+    assert ops.decode_workspace_bytes(64, 32, 12) == 64 * 32 * 1024 + 64 * 32 * 13 * (512 + 8)
+    assert lib.oscar_decode_workspace_bytes(-1, 32, 12) == 0
+    assert lib.oscar_decode_workspace_bytes(1, 32, 0) == 0
+
+
+def _layout(**kw):
+    from int2_rotated_kv_rotate_amd import ops
+    d = dict(num_kv_heads=8, num_sink=4, window=128, num_pages=100, max_pages_per_seq=10,
+             num_slots=2)
+    d.update(kw)
+    return ops.make_layout(**d)
+
+
+FAKE = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+
+
+def _append(lib, lay, **kw):
+    a = dict(pages=FAKE, sinkwin=FAKE, bt=FAKE, slots=None, batch=1, total=1, k=FAKE, v=FAKE,
+             off=FAKE, start=FAKE, rk=FAKE, rv=FAKE, ck=0.95, cv=0.95)
+    a.update(kw)
+    return lib.oscar_rotate_quantize_append(
+        ctypes.byref(lay) if lay is not None else None, a["pages"], a["sinkwin"], a["bt"],
+        a["slots"], a["batch"], a["total"], a["k"], a["v"], a["off"], a["start"], a["rk"],
+        a["rv"], a["ck"], a["cv"], None)
+
+
+def test_append_validation(lib):
+    assert _append(lib, None) == 1
+    assert _append(lib, _layout(head_dim=64)) == 2
+    assert _append(lib, _layout(page_size=32)) == 2
+    assert _append(lib, _layout(group_size=64)) == 2
+    assert _append(lib, _layout(num_sink=600, window=600)) == 2
+    assert _append(lib, _layout(window=-1)) == 1
+    assert _append(lib, _layout(), ck=0.0) == 1
+    assert _append(lib, _layout(), cv=1.5) == 1
+    assert _append(lib, _layout(), pages=None) == 1
+    assert _append(lib, _layout(), sinkwin=None) == 1
+    assert _append(lib, _layout(), k=ctypes.c_void_p(18)) == 1   # misaligned
+    assert _append(lib, _layout(), batch=-1) == 1
+    assert _append(lib, _layout(), batch=0) == 0                 # nothing to do, no launch
+    assert _append(lib, _layout(), total=0) == 0
+
+
+def _decode(lib, lay, **kw):
+    a = dict(pages=FAKE, sinkwin=FAKE, bt=FAKE, slots=None, batch=1, hq=32, q=FAKE, lens=FAKE,
+             rk=FAKE, sm=0.088, sp=128, ms=4, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.oscar_decode_attention(
+        ctypes.byref(lay), a["pages"], a["sinkwin"], a["bt"], a["slots"], a["batch"], a["hq"],
+        a["q"], a["lens"], a["rk"], a["sm"], a["sp"], a["ms"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, _layout(), hq=30) == 1          # not a multiple of Hkv
+    assert _decode(lib, _layout(), hq=24) == 2          # group 3 unsupported
+    assert _decode(lib, _layout(), hq=128) == 2         # group 16 unsupported
+    assert _decode(lib, _layout(), sp=0) == 1
+    assert _decode(lib, _layout(), ms=0) == 1
+    assert _decode(lib, _layout(), sm=float("nan")) == 1
+    assert _decode(lib, _layout(), wsb=100) == 3
+    assert _decode(lib, _layout(), q=None) == 1
+    assert _decode(lib, _layout(head_dim=256)) == 2
+    assert _decode(lib, _layout(), batch=0) == 0
+
+
+def test_combine_and_bf16_validation(lib):
+    assert lib.oscar_combine(1, 32, 8, 4, FAKE, 100, None, FAKE, None, None) == 3
+    assert lib.oscar_combine(1, 32, 8, 4, None, 1 << 30, None, FAKE, None, None) == 1
+    assert lib.oscar_combine(1, 33, 8, 4, FAKE, 1 << 30, None, FAKE, None, None) == 1
+    assert lib.oscar_combine(0, 32, 8, 4, FAKE, 1 << 30, None, FAKE, None, None) == 0
+    lay = _layout()
+    assert lib.oscar_bf16_append(ctypes.byref(lay), None, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.oscar_bf16_decode_attention(ctypes.byref(lay), FAKE, FAKE, 1, 32, FAKE, FAKE, 0.1,
+                                           128, 4, FAKE, 10, None) == 3

@@ -193,6 +193,17 @@ def test_constant_group_has_zero_scale():
     assert np.all(O.dequant(codes, s16, z16) == float(np.float16(np.float32(0.95) * np.float32(1.5))))
 
 
+def test_signed_zero_extreme_gives_positive_zero():
+    y = np.zeros((2, 128), np.float32)
+    y[0, :32] = np.abs(np.linspace(0, 3, 32, dtype=np.float32))
+    y[0, 5] = -0.0                     # min is a signed zero
+    y[1, :32] = -np.abs(np.linspace(0, 3, 32, dtype=np.float32))
+    y[1, 7] = -0.0                     # max is a signed zero
+    s16, z16 = O.group_params(y, 0.95)
+    assert z16[0, 0].view(np.uint16) == 0x0000
+    assert s16[1, 0] > 0 and np.float16(z16[1, 0]) < 0
+
+
 def test_exhaustive_bf16_sweep_between_anchors():
     """R = I; anchor a group's max and min, sweep every bf16 value between them."""
     lo, hi = -3.0, 5.0
