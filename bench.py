@@ -1,0 +1,244 @@
+"""Benchmark: one decode step of the rotated-INT2 mixed-precision paged attention on one GPU.
+
+A step is one pass of the whole hot path over the batch: rotate-quantize-append of each
+sequence's new token, decode attention (q rotation, INT2 page splits, BF16 sink + window) and
+the split combine with R_V^T.  Default workload: Qwen3-8B-shaped layer, batch 64, 32 query /
+8 KV heads, head_dim 128, context lengths uniform in [16384, 32768], sink 4 + window 128 in
+BF16, INT2 bulk, 16-token pages, all inputs synthetic and already resident in HBM.
+
+Prints ONE JSON line.  Extra fields: effective GB/s of the step, the decode-attention roofline
+(bytes from the method's byte model / the launch's HIP-event duration), the prefill append of
+2048 tokens per sequence, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+INT2_TOKEN_HEAD_BYTES = 96      # 32 B K codes + 32 B V codes + 16 B K meta + 16 B V meta
+BF16_TOKEN_HEAD_BYTES = 512     # bf16 K + V rows
+METRIC = "decode attn tokens/s + effective HBM GB/s (% of peak), Qwen3-8B shape B=64 ctx=32k"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def byte_model(w, lens):
+    """Algorithmic HBM bytes of one decode step, split by part."""
+    lens = np.asarray(lens, dtype=np.int64)
+    n_sink = np.minimum(lens, w.num_sink)
+    n_win = np.minimum(w.window, lens - n_sink)
+    n_int2 = lens - n_sink - n_win
+    hkv, hq, B = w.num_kv_heads, w.num_q_heads, w.batch
+    int2 = int(hkv * INT2_TOKEN_HEAD_BYTES * n_int2.sum())
+    bf16 = int(hkv * BF16_TOKEN_HEAD_BYTES * (n_sink + n_win).sum())
+    q = B * hq * 128 * 2
+    table = 4 * int(((lens + 15) // 16).sum())
+    out = B * hq * 128 * 4
+    # append of one token per sequence: bf16 K,V in; one INT2 slot + one bf16 window row out
+    append = B * hkv * (2 * 128 * 2 + INT2_TOKEN_HEAD_BYTES + BF16_TOKEN_HEAD_BYTES)
+    rot = 2 * hkv * 128 * 128 * 4
+    return dict(int2=int2, bf16=bf16, q=q, table=table, out=out, append=append, rot=rot,
+                decode_attention=int2 + bf16 + q + table,
+                step=int2 + bf16 + q + table + out + append + rot)
+
+
+def cpu_baseline(p, target_s: float):
+    """The CPU oracle as it stands, on a bounded sample: sequence 0, KV heads 0..n-1 (all G
+    query heads of each), oracle cache built untimed, then timed: the append of the decoded
+    token plus decode attention.  Scaled to the batch: tokens/s = 1 / (t_per_head * Hkv)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import oscar_oracle as O
+    from int2_rotated_kv_rotate_amd import workload as W
+    import math
+
+    w = p.w
+    L = int(p.lens[0])
+    G = w.group
+    kb, vb = W.sequence_kv(w, 0, L)
+    sm = float(np.float32(1.0 / math.sqrt(128.0)))
+    per_head = []
+    with threadpool_limits(limits=1):
+        for h in range(w.num_kv_heads):
+            cache = O.Cache(p.num_pages, 1, 1, w.num_sink, w.window)
+            tbl = p.table[0]
+            cache.append(tbl, 0, 0, kb[:L - 1, h:h + 1], vb[:L - 1, h:h + 1],
+                         p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
+            t0 = time.perf_counter()
+            cache.append(tbl, 0, L - 1, kb[L - 1:, h:h + 1], vb[L - 1:, h:h + 1],
+                         p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
+            O.decode_attention(cache, p.table[:1], np.zeros(1, np.int64), p.lens[:1],
+                               p.q[:1, h * G:(h + 1) * G], p.rot_k[h:h + 1], p.rot_v[h:h + 1], sm)
+            per_head.append(time.perf_counter() - t0)
+            if sum(per_head) >= target_s:
+                break
+    t_head = float(np.mean(per_head))
+    return {"value": 1.0 / (t_head * w.num_kv_heads), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"sequence 0 (L={L}), {len(per_head)} of {w.num_kv_heads} KV heads x "
+                       f"{G} query heads: decode-token append + decode attention, "
+                       f"{sum(per_head):.1f} s total, scaled to all KV heads; one BLAS thread"),
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_b64")
+    ap.add_argument("--split-pages", type=int, default=128)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int2_rotated_kv_rotate_amd import harness as H
+    from int2_rotated_kv_rotate_amd import ops
+    from int2_rotated_kv_rotate_amd import workload as W
+
+    ops.load_library()
+    w = W.WORKLOADS[args.workload]
+    p = H.make_problem(w)
+    bm = byte_model(w, p.lens)
+    log(f"workload {w.name}: B={w.batch} lens mean {p.lens.mean():.0f} "
+        f"[{p.lens.min()}, {p.lens.max()}], pool {p.num_pages} pages "
+        f"({p.num_pages * w.num_kv_heads * 1536 / 1e9:.2f} GB)")
+
+    t0 = time.time()
+    cache = H.GpuCache(p)
+    tail = w.prefill_new if not args.no_prefill else 0
+    if tail:
+        last_k, last_v, tail_k, tail_v = cache.fill_context(keep_tail=tail)
+    else:
+        last_k, last_v = cache.fill_context()
+    torch.cuda.synchronize()
+    log(f"cache filled in {time.time() - t0:.1f} s")
+
+    step = H.DecodeStep(cache, split_pages=args.split_pages)
+    step.set_new_token(last_k, last_v)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step.append_new()
+        ev[k][0].record(stream)
+        step.decode_only()
+        ev[k][1].record(stream)
+        step.combine_only()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    attn_avg = float(attn_ms.mean())
+    log(f"step {ms_step:.4f} ms; decode attention avg {attn_avg:.4f} ms "
+        f"(p10 {np.percentile(attn_ms, 10):.4f}, p90 {np.percentile(attn_ms, 90):.4f})")
+
+    tokens_per_s = w.batch / (ms_step / 1e3)
+    step_gbps = bm["step"] / (ms_step / 1e3) / 1e9
+    attn_gbps = bm["decode_attention"] / (attn_avg / 1e3) / 1e9
+
+    prefill = None
+    if tail:
+        offs = np.zeros(w.batch + 1, dtype=np.int32)
+        offs[1:] = np.cumsum([t.shape[0] for t in tail_k])
+        kt = H.as_i16(np.concatenate(tail_k)).cuda()
+        vt = H.as_i16(np.concatenate(tail_v)).cuda()
+        offs_d = torch.from_numpy(offs).cuda()
+        start_d = torch.from_numpy((p.lens - 1 - tail).astype(np.int32)).cuda()
+
+        def do_prefill():
+            ops.rotate_quantize_append(cache.layout, cache.pages, cache.sinkwin, cache.table,
+                                       cache.slots, kt, vt, offs_d, start_d, cache.rot_k,
+                                       cache.rot_v, w.clip, w.clip)
+        do_prefill()
+        torch.cuda.synchronize()
+        reps = 3
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            do_prefill()
+        b.record(stream)
+        torch.cuda.synchronize()
+        pf_ms = a.elapsed_time(b) / reps
+        n_new = int(offs[-1])
+        pf_bytes = n_new * w.num_kv_heads * (2 * 256 + INT2_TOKEN_HEAD_BYTES) + \
+            w.batch * w.num_kv_heads * w.window * BF16_TOKEN_HEAD_BYTES + bm["rot"]
+        prefill = {"tokens": n_new, "ms": round(pf_ms, 4),
+                   "tokens_per_s": round(n_new / (pf_ms / 1e3), 1),
+                   "effective_gbps": round(pf_bytes / (pf_ms / 1e3) / 1e9, 1),
+                   "rotation": "fp64 VALU (exact order)"}
+        log(f"prefill append {n_new} tokens: {pf_ms:.3f} ms")
+        step.run()  # restore the window rows the prefill re-append rewrote
+        torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device copy done")
+
+    cpu = None
+    if not args.no_cpu:
+        t0 = time.time()
+        cpu = cpu_baseline(p, args.cpu_seconds)
+        log(f"cpu oracle baseline: {cpu['value']:.4f} tokens/s ({time.time() - t0:.1f} s)")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2-kv/int8+bf16-mfma/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": 128,
+                   "ctx": f"U[{w.ctx_min},{w.ctx}]" if w.ctx_min else w.ctx,
+                   "mean_ctx": float(p.lens.mean()), "sink": w.num_sink, "window": w.window,
+                   "page": 16, "split_pages": args.split_pages},
+        "effective_gbps": round(step_gbps, 1),
+        "pct_of_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "oscar_decode_attention (q prep + INT2 splits + "
+                     "BF16 window)", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+                     "bytes_per_launch": bm["decode_attention"], "launch_ms": round(attn_avg, 5),
+                     "traffic": None},
+        "bytes": bm,
+        "prefill_append": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

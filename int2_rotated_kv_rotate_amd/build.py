@@ -22,7 +22,8 @@ SOURCES = {
     "api.hip": [],
     # the quantiser is an fp32 formula reproduced bit for bit: never contract it into FMAs
     "append.hip": ["-ffp-contract=off"],
-    "decode.hip": [],
+    # MFMA accumulators in VGPRs: the rescale path then needs no AGPR round trips
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "combine.hip": [],
     "bf16_baseline.hip": [],
 }

@@ -253,7 +253,178 @@ __global__ __launch_bounds__(64) void window_kernel(CacheGeom g, const uint16_t*
 
 // ------------------------------------------------------------------------ INT2 page splits
 
+// Lane-uniform helpers.
+__device__ __forceinline__ float dpp_add_xor1(float x) {  // x + x[lane ^ 1] within quads
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_add_xor2(float x) {  // x + x[lane ^ 2] within quads
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+// max over lanes l, l^16, l^32, l^48 (the four 16-lane rows), without LDS.
+__device__ __forceinline__ float rowmax4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rowsum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// (x & mask) | magic.  With mask in an SGPR and magic in a VGPR (see int2_decode_kernel) the
+// compiler selects one v_and_or_b32; with both as literals it needs two instructions.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  return (x & mask) | magic;
+}
+
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+struct PageRegs {
+  uint2 kc;  // K code dwords of this lane (words kq and 4 + kq of token c16)
+  uint2 vc;  // V code chunk of this lane (4 tokens x 8 channel blocks)
+  uint4 km;  // K (scale, zero) of tokens 4*kq .. 4*kq+3, this lane's group
+  uint4 vm;  // V (scale, zero), same tokens and group
+};
+
+constexpr int kTile = 1;  // pages per online-softmax step
+
+template <int NCB>
+struct SplitState {
+  v4f acc[NCB][8];   // P.V accumulators: rows (query head 4*cb + kq, group i), cols 16*nb + c16
+  float mrun[NCB];   // running max (log2 units) of this lane's query head
+  float lsum[NCB];   // sum of p over this lane's tokens
+  float zsum[NCB];   // sum of p * (zero_v - 4 * scale_v) over this lane's tokens
+};
+
+template <int NCB>
+struct QOperands {
+  v4i hi[NCB][2], lo[NCB][2];
+  float qsum_s[NCB];  // (sum of q' over the lane's group) * 254 / qsc
+  float cscale[NCB];  // qsc / 254 * sm_scale * log2(e)
+};
+
+// One tile of kTile pages: logits on the int8 MFMA, online softmax, P.V on the bf16 MFMA.
+// MASKED: some tokens of the tile are outside the INT2 range [lo, hi) (or on a skipped page);
+// their bytes may be stale, so every use is a select, never a multiply.
+template <int NCB, bool MASKED>
+__device__ __forceinline__ void int2_tile(const PageRegs (&d)[kTile], int pg, int lo, int hi,
+                                          uint32_t live_pages, const QOperands<NCB>& qo,
+                                          SplitState<NCB>& st, int kq, uint32_t vmask,
+                                          uint32_t magic) {
+  float lg[kTile][NCB][4];
+  float tmax[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) tmax[cb] = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kTile; ++u) {
+    const uint32_t w0 = d[u].kc.x, w1 = d[u].kc.y;
+    const v4i ka0 = (v4i){(int)(w0 & 0x03030303u), (int)((w0 >> 2) & 0x03030303u),
+                          (int)((w0 >> 4) & 0x03030303u), (int)((w0 >> 6) & 0x03030303u)};
+    const v4i ka1 = (v4i){(int)(w1 & 0x03030303u), (int)((w1 >> 2) & 0x03030303u),
+                          (int)((w1 >> 4) & 0x03030303u), (int)((w1 >> 6) & 0x03030303u)};
+    const uint32_t kmw[4] = {d[u].km.x, d[u].km.y, d[u].km.z, d[u].km.w};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
+      dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka0, qo.hi[cb][0], dh, 0, 0, 0);
+      dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1, qo.hi[cb][1], dh, 0, 0, 0);
+      dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka0, qo.lo[cb][0], dl, 0, 0, 0);
+      dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1, qo.lo[cb][1], dl, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dint = __mul24(dh[i], 254) + dl[i];
+        float part = fmaf(f16lo(kmw[i]), (float)dint, f16hi(kmw[i]) * qo.qsum_s[cb]);
+        part = dpp_add_xor1(part);
+        part = dpp_add_xor2(part);
+        float l2 = part * qo.cscale[cb];
+        if (MASKED) {
+          const int pos = (pg + u) * kPage + 4 * kq + i;
+          const bool live = ((live_pages >> u) & 1u) && pos >= lo && pos < hi;
+          l2 = live ? l2 : -INFINITY;
+        }
+        lg[u][cb][i] = l2;
+        tmax[cb] = fmaxf(tmax[cb], l2);
+      }
+    }
+  }
+
+  // Online softmax: exact running max per query head, lazy rescale of the accumulators.
+  bool need = false;
+  float mnew[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    mnew[cb] = fmaxf(st.mrun[cb], rowmax4(tmax[cb]));
+    need |= mnew[cb] > st.mrun[cb];
+  }
+  if (__any(need)) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const float alpha = __builtin_amdgcn_exp2f(st.mrun[cb] - mnew[cb]);
+      // accumulator rows belong to query head 4*cb + kq: its alpha sits in lane 4*kq
+      const float arow = __shfl(alpha, 4 * kq);
+      st.lsum[cb] *= alpha;
+      st.zsum[cb] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) st.acc[cb][nb] *= arow;
+      st.mrun[cb] = mnew[cb];
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < kTile; ++u) {
+    // V codes -> bf16 (1 + code/4); pair nb of dword x holds codes at bits 2nb and 16 + 2nb.
+    v4s vb[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint32_t x0 = d[u].vc.x, x1 = d[u].vc.y;
+      const uint32_t y0 = nb <= 2 ? (x0 << (5 - 2 * nb)) : (x0 >> (2 * nb - 5));
+      const uint32_t y1 = nb <= 2 ? (x1 << (5 - 2 * nb)) : (x1 >> (2 * nb - 5));
+      const uint32_t p0 = and_or(y0, vmask, magic), p1 = and_or(y1, vmask, magic);
+      vb[nb] = __builtin_bit_cast(v4s, make_uint2(p0, p1));
+    }
+    const uint32_t vmw[4] = {d[u].vm.x, d[u].vm.y, d[u].vm.z, d[u].vm.w};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(lg[u][cb][i] - st.mrun[cb]);
+        const float sv = f16lo(vmw[i]), zv = f16hi(vmw[i]);
+        const float zz = fmaf(-4.0f, sv, zv);
+        if (MASKED) {
+          const bool live = lg[u][cb][i] != -INFINITY;
+          st.lsum[cb] += p;  // p == 0 exactly for masked tokens
+          st.zsum[cb] = live ? fmaf(p, zz, st.zsum[cb]) : st.zsum[cb];
+          w[i] = live ? p * sv : 0.f;
+        } else {
+          st.lsum[cb] += p;
+          st.zsum[cb] = fmaf(p, zz, st.zsum[cb]);
+          w[i] = p * sv;
+        }
+      }
+      uint32_t h01, h23, l01, l23;
+      split_bf16(w, h01, h23, l01, l23);
+      const v4s ahi = __builtin_bit_cast(v4s, make_uint2(h01, h23));
+      const v4s alo = __builtin_bit_cast(v4s, make_uint2(l01, l23));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        st.acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nb], st.acc[cb][nb], 0, 0, 0);
+        st.acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nb], st.acc[cb][nb], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // NCB = number of 16-wide column blocks of (query head, group) pairs = ceil(G / 4).
+// grid (max_splits, Hkv, batch), block 64: one wavefront per (split, KV head, sequence).
 template <int NCB>
 __global__ __launch_bounds__(64) void int2_decode_kernel(
     CacheGeom g, const uint8_t* __restrict__ pages, const int32_t* __restrict__ block_table,
@@ -262,171 +433,125 @@ __global__ __launch_bounds__(64) void int2_decode_kernel(
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int max_splits = ws.nslots - 1;
   const int G = hq / g.hkv;
-  const int L = seq_lens[b];
+  const int L = max(seq_lens[b], 0);
   const float sm_log2 = sm_scale * kLog2e;
-
   const int kq = lane >> 4, c16 = lane & 15;
   const int grp = c16 & 3;  // quantisation group of this lane's (query head, group) column
 
   // INT2 positions [lo, hi) and this split's logical pages [pg0, pg1).
-  const int n_sink = min(max(L, 0), g.num_sink);
-  const int n_win = min(g.window, max(L, 0) - n_sink);
-  const int lo = n_sink, hi = max(L, 0) - n_win;
+  const int n_sink = min(L, g.num_sink);
+  const int n_win = min(g.window, L - n_sink);
+  const int lo = n_sink, hi = L - n_win;
   int pg0 = split * split_pages;
   int pg1 = (split == max_splits - 1) ? 0x7fffffff : pg0 + split_pages;
   pg0 = max(pg0, lo / kPage);
   pg1 = min(min(pg1, (hi + kPage - 1) / kPage), g.max_pages);
   if (hi <= lo) pg1 = pg0;
 
-  // Per-lane query operands and constants for each column block.
-  v4i qhi[NCB][2], qlo[NCB][2];
-  float qsum_s[NCB], cscale[NCB];
-  bool jvalid[NCB];
+  QOperands<NCB> qo;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int j = 4 * cb + (c16 >> 2);
-    jvalid[cb] = j < G;
-    const int jj = jvalid[cb] ? j : 0;
-    const char* blk = ws.qblock(b, hq, h * G + jj);
+    const bool jvalid = j < G;
+    const char* blk = ws.qblock(b, hq, h * G + (jvalid ? j : 0));
     const float qsc = *reinterpret_cast<const float*>(blk + kQScOff);
     const float qs = reinterpret_cast<const float*>(blk + kQSumOff)[grp];
-    qsum_s[cb] = qsc > 0.f ? qs * 254.0f / qsc : 0.f;
-    cscale[cb] = qsc / 254.0f * sm_log2;
+    qo.qsum_s[cb] = qsc > 0.f ? qs * 254.0f / qsc : 0.f;
+    // strictly positive so that a masked -inf logit never becomes 0 * inf
+    qo.cscale[cb] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int d = 4 * m + kq;  // 16-channel word of this lane's K quarter
-      const bool use = jvalid[cb] && (d >> 1) == grp;
+      const bool use = jvalid && (d >> 1) == grp;
       const v4i zh = *reinterpret_cast<const v4i*>(blk + kQHiOff + 16 * d);
       const v4i zl = *reinterpret_cast<const v4i*>(blk + kQLoOff + 16 * d);
       const v4i zero = {0, 0, 0, 0};
-      qhi[cb][m] = use ? zh : zero;
-      qlo[cb][m] = use ? zl : zero;
+      qo.hi[cb][m] = use ? zh : zero;
+      qo.lo[cb][m] = use ? zl : zero;
     }
   }
 
-  v4f acc[NCB][8];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[cb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float mrun[NCB], lsum[NCB], zsum[NCB];
+  SplitState<NCB> st;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    mrun[cb] = kNegBig;
-    lsum[cb] = 0.f;
-    zsum[cb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st.acc[cb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+    st.mrun[cb] = kNegBig;
+    st.lsum[cb] = 0.f;
+    st.zsum[cb] = 0.f;
   }
+  // Opaque copies of the two V-code constants: mask in an SGPR, magic in a VGPR, so every
+  // (x & mask) | magic is one instruction.  The empty asm statements emit nothing.
+  uint32_t vmask = 0x00600060u, magic = 0x3F803F80u;
+  asm volatile("" : "+s"(vmask));
+  asm volatile("" : "+v"(magic));
 
+  // Page ids of the split, 64 per lane register, fetched lane-parallel and read back per page
+  // with v_readlane (no scalar-load latency inside the loop).
   const int32_t* bt = block_table + (size_t)b * g.max_pages;
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const int page = bt[pg];
-    if (page < 0 || page >= g.num_pages) continue;
-    const uint8_t* rec = pages + ((size_t)page * g.hkv + h) * kRecord;
-    const uint2 kc = reinterpret_cast<const uint2*>(rec + kKCodes)[lane];
-    const uint2 vc = reinterpret_cast<const uint2*>(rec + kVCodes)[lane];
-    const uint4 km = *reinterpret_cast<const uint4*>(rec + kKMeta + 64 * grp + 16 * kq);
-    const uint4 vm = *reinterpret_cast<const uint4*>(rec + kVMeta + 64 * grp + 16 * kq);
+  int id_base = pg0;
+  int ids = (pg0 + lane < pg1) ? bt[pg0 + lane] : -1;
 
-    // K codes -> int8 operands (slot 4*i + b of word d holds channel 16*d + 4*b + i).
-    v4i ka[2];
-    {
-      const uint32_t w0 = kc.x, w1 = kc.y;
-      ka[0] = (v4i){(int)(w0 & 0x03030303u), (int)((w0 >> 2) & 0x03030303u),
-                    (int)((w0 >> 4) & 0x03030303u), (int)((w0 >> 6) & 0x03030303u)};
-      ka[1] = (v4i){(int)(w1 & 0x03030303u), (int)((w1 >> 2) & 0x03030303u),
-                    (int)((w1 >> 4) & 0x03030303u), (int)((w1 >> 6) & 0x03030303u)};
+  auto page_id = [&](int pg) -> int {  // uniform
+    if (pg >= pg1) return -1;
+    if (pg - id_base >= 64) {
+      id_base = pg;
+      ids = (pg + lane < pg1) ? bt[pg + lane] : -1;
     }
-    const uint32_t kmw[4] = {km.x, km.y, km.z, km.w};
-    const uint32_t vmw[4] = {vm.x, vm.y, vm.z, vm.w};
-
-    float lg[NCB][4];
+    return __builtin_amdgcn_readlane(ids, pg - id_base);
+  };
+  auto load_tile = [&](int pgt, PageRegs (&d)[kTile], uint32_t& live) {
+    live = 0;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
-      dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[0], qhi[cb][0], dh, 0, 0, 0);
-      dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qhi[cb][1], dh, 0, 0, 0);
-      dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[0], qlo[cb][0], dl, 0, 0, 0);
-      dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qlo[cb][1], dl, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dint = 254 * dh[i] + dl[i];
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(kmw[i] & 0xFFFF));
-        const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(kmw[i] >> 16));
-        float part = fmaf(s, (float)dint, z * qsum_s[cb]);
-        part += dpp_quad_xor1(part);
-        part += dpp_quad_xor2(part);
-        const int pos = pg * kPage + 4 * kq + i;
-        lg[cb][i] = (pos >= lo && pos < hi) ? part * cscale[cb] : -INFINITY;
+    for (int u = 0; u < kTile; ++u) {
+      const int page = page_id(pgt + u);
+      if (page >= 0 && page < g.num_pages) {
+        const uint8_t* rec = pages + ((size_t)page * g.hkv + h) * kRecord;
+        d[u].kc = reinterpret_cast<const uint2*>(rec + kKCodes)[lane];
+        d[u].vc = reinterpret_cast<const uint2*>(rec + kVCodes)[lane];
+        d[u].km = *reinterpret_cast<const uint4*>(rec + kKMeta + 64 * grp + 16 * kq);
+        d[u].vm = *reinterpret_cast<const uint4*>(rec + kVMeta + 64 * grp + 16 * kq);
+        live |= 1u << u;
+      } else {
+        d[u].kc = make_uint2(0, 0);
+        d[u].vc = make_uint2(0, 0);
+        d[u].km = make_uint4(0, 0, 0, 0);
+        d[u].vm = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  auto run_tile = [&](int pgt, const PageRegs (&d)[kTile], uint32_t live) {
+    const bool interior = live == (1u << kTile) - 1 && pgt * kPage >= lo &&
+                          (pgt + kTile) * kPage <= hi;
+    if (interior)
+      int2_tile<NCB, false>(d, pgt, lo, hi, live, qo, st, kq, vmask, magic);
+    else
+      int2_tile<NCB, true>(d, pgt, lo, hi, live, qo, st, kq, vmask, magic);
+  };
 
-    // Online softmax update (exact running max).
-    bool need = false;
-    float mnew[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      float tm = fmaxf(fmaxf(lg[cb][0], lg[cb][1]), fmaxf(lg[cb][2], lg[cb][3]));
-      tm = max_across_rows(tm);
-      mnew[cb] = fmaxf(mrun[cb], tm);
-      need |= mnew[cb] > mrun[cb];
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const float alpha = __builtin_amdgcn_exp2f(mrun[cb] - mnew[cb]);
-        // rows of acc[cb] belong to query head 4*cb + kq: fetch that head's alpha
-        const float arow = __shfl(alpha, 4 * kq);
-        lsum[cb] *= alpha;
-        zsum[cb] *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[cb][nb] *= arow;
-        mrun[cb] = mnew[cb];
-      }
-    }
-
-    // Vcodes -> bf16 operands (1 + code/4), shared by all column blocks.
-    v4s vb[8];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const uint32_t p0 = vcode_pair(vc.x, nb), p1 = vcode_pair(vc.y, nb);
-      vb[nb] = (v4s){(short)(p0 & 0xFFFF), (short)(p0 >> 16), (short)(p1 & 0xFFFF),
-                     (short)(p1 >> 16)};
-    }
-
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      float w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // masked slots (outside the INT2 range) may hold stale bytes: select, never multiply
-        const bool live = lg[cb][i] != -INFINITY;
-        const float p = live ? __builtin_amdgcn_exp2f(lg[cb][i] - mrun[cb]) : 0.f;
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(vmw[i] & 0xFFFF));
-        const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(vmw[i] >> 16));
-        lsum[cb] += p;
-        zsum[cb] = live ? fmaf(p, fmaf(-4.0f, s, z), zsum[cb]) : zsum[cb];
-        w[i] = live ? p * s : 0.f;
-      }
-      uint32_t h01, h23, l01, l23;
-      split_bf16(w, h01, h23, l01, l23);
-      const v4s ahi = (v4s){(short)(h01 & 0xFFFF), (short)(h01 >> 16), (short)(h23 & 0xFFFF),
-                            (short)(h23 >> 16)};
-      const v4s alo = (v4s){(short)(l01 & 0xFFFF), (short)(l01 >> 16), (short)(l23 & 0xFFFF),
-                            (short)(l23 >> 16)};
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nb], acc[cb][nb], 0, 0, 0);
-        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nb], acc[cb][nb], 0, 0, 0);
-      }
-    }
+  // Two register buffers: the next tile's loads are in flight while the current one computes.
+  PageRegs bufA[kTile], bufB[kTile];
+  uint32_t liveA = 0, liveB = 0;
+  int pg = pg0;
+  if (pg < pg1) load_tile(pg, bufA, liveA);
+  while (pg < pg1) {
+    const int nxt = pg + kTile;
+    if (nxt < pg1) load_tile(nxt, bufB, liveB);
+    run_tile(pg, bufA, liveA);
+    pg = nxt;
+    if (pg >= pg1) break;
+    const int nxt2 = pg + kTile;
+    if (nxt2 < pg1) load_tile(nxt2, bufA, liveA);
+    run_tile(pg, bufB, liveB);
+    pg = nxt2;
   }
 
   // Finish: reduce l and the zero-point term over the four token quarters, assemble
   // o'[j][c] = 4 * acc[row (j, g(c))][c] + Z[j][g(c)], write the split's partials.
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const float lt = sum_across_rows(lsum[cb]);
-    const float zt = sum_across_rows(zsum[cb]);
+    const float lt = rowsum4(st.lsum[cb]);
+    const float zt = rowsum4(st.zsum[cb]);
     const int j = 4 * cb + kq;  // query head of the accumulator rows this lane holds
     float zrow[4];
 #pragma unroll
@@ -436,11 +561,11 @@ __global__ __launch_bounds__(64) void int2_decode_kernel(
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         const int gsel = nb >> 1;
-        o[16 * nb + c16] = 4.0f * acc[cb][nb][gsel] + zrow[gsel];
+        o[16 * nb + c16] = 4.0f * st.acc[cb][nb][gsel] + zrow[gsel];
       }
     }
     const float lrow = __shfl(lt, 4 * kq);
-    const float mrow = __shfl(mrun[cb], 4 * kq);
+    const float mrow = __shfl(st.mrun[cb], 4 * kq);
     if (c16 == 0 && j < G) *ws.ml(b, hq, h * G + j, split) = make_float2(mrow, lrow);
   }
 }

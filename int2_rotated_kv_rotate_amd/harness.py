@@ -7,6 +7,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional, Sequence
 
 import numpy as np
@@ -86,31 +88,47 @@ class GpuCache:
             torch.from_numpy(np.asarray(start, dtype=np.int32)).to(self.device),
             self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip)
 
-    def fill_context(self, chunk_tokens: int = 1 << 20):
+    def fill_context(self, chunk_tokens: int = 1 << 20, keep_tail: int = 0):
         """Append positions [0, L_b - 1) of every sequence (everything but the decoded token),
-        in chunks of whole sequences.  Returns the per-sequence last rows (k, v) [1][Hkv][128]."""
+        in chunks of whole sequences.  Returns the per-sequence last rows (k, v) [1][Hkv][128];
+        with keep_tail > 0 also the rows of positions [L_b - 1 - keep_tail, L_b - 1)."""
         w = self.p.w
         hkv = w.num_kv_heads
         empty = np.zeros((0, hkv, 128), dtype=np.uint16)
         needle = W.needle_site(w, self.p.lens)
-        last_k, last_v = [], []
+        offsets, outliers = W.key_offsets(w), W.outlier_channels(w)
+        last_k, last_v, tail_k, tail_v = [], [], [], []
         pend_k = [empty] * w.batch
         pend_v = [empty] * w.batch
         pend_n = 0
-        for b in range(w.batch):
-            L = int(self.p.lens[b])
-            kb, vb = W.sequence_kv(w, b, L, needle=needle, q_bits=self.p.q)
-            last_k.append(kb[L - 1:L])
-            last_v.append(vb[L - 1:L])
-            pend_k[b] = kb[:L - 1]
-            pend_v[b] = vb[:L - 1]
-            pend_n += L - 1
-            if pend_n >= chunk_tokens or b == w.batch - 1:
-                self.append(pend_k, pend_v, [0] * w.batch)
-                torch.cuda.synchronize()
-                pend_k = [empty] * w.batch
-                pend_v = [empty] * w.batch
-                pend_n = 0
+
+        def gen(b):
+            return W.sequence_kv(w, b, int(self.p.lens[b]), offsets=offsets, outliers=outliers,
+                                 needle=needle, q_bits=self.p.q)
+
+        workers = max(1, min(16, os.cpu_count() or 1))
+        with ThreadPoolExecutor(workers) as ex:
+            for g0 in range(0, w.batch, 2 * workers):
+                group = list(range(g0, min(w.batch, g0 + 2 * workers)))
+                for b, (kb, vb) in zip(group, ex.map(gen, group)):
+                    L = int(self.p.lens[b])
+                    last_k.append(kb[L - 1:L])
+                    last_v.append(vb[L - 1:L])
+                    if keep_tail:
+                        t0 = max(0, L - 1 - keep_tail)
+                        tail_k.append(kb[t0:L - 1].copy())
+                        tail_v.append(vb[t0:L - 1].copy())
+                    pend_k[b] = kb[:L - 1]
+                    pend_v[b] = vb[:L - 1]
+                    pend_n += L - 1
+                    if pend_n >= chunk_tokens or b == w.batch - 1:
+                        self.append(pend_k, pend_v, [0] * w.batch)
+                        torch.cuda.synchronize()
+                        pend_k = [empty] * w.batch
+                        pend_v = [empty] * w.batch
+                        pend_n = 0
+        if keep_tail:
+            return last_k, last_v, tail_k, tail_v
         return last_k, last_v
 
 
@@ -145,13 +163,20 @@ class DecodeStep:
                                    self.v_last, self.new_off, self.start, c.rot_k, c.rot_v,
                                    c.p.w.clip, c.p.w.clip, stream)
 
-    def attend(self, stream=None):
+    def decode_only(self, stream=None):
         c = self.cache
-        p = c.p
         ops.decode_attention(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.q, self.seq_lens,
                              c.rot_k, SM_SCALE, self.split_pages, self.max_splits, self.ws, stream)
+
+    def combine_only(self, stream=None):
+        c = self.cache
+        p = c.p
         ops.combine(p.batch, p.w.num_q_heads, p.w.num_kv_heads, self.max_splits, self.ws, c.rot_v,
                     self.out, self.lse, stream)
+
+    def attend(self, stream=None):
+        self.decode_only(stream)
+        self.combine_only(stream)
 
     def run(self, stream=None):
         self.append_new(stream)

@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liboscar_hip.so")
+LIB_PATH = os.environ.get("OSCAR_LIBRARY", os.path.join(_PKG, "liboscar_hip.so"))
 
 HEAD_DIM, PAGE_SIZE, GROUP_SIZE, RECORD_BYTES = 128, 16, 32, 1536
 BF16_PAGE_ELEMS = 2 * PAGE_SIZE * HEAD_DIM
