@@ -37,8 +37,8 @@
  *                dword, byte (c%16)/4, bits 2*(c%4)..+1.
  *   [ 512, 1024) V codes.  Channel c of slot r: chunk L = 16*(r/4) + c%16 at 512 + 8*L;
  *                dword (r%4)/2 of the chunk, 16-bit half r%2; bits 2*(c/16)..+1 of the half.
- *   [1024, 1280) K scale/zero: group g of slot r at 1024 + 64*g + 4*r, fp16 scale then fp16 zero.
- *   [1280, 1536) V scale/zero, same arrangement at 1280 + 64*g + 4*r.
+ *   [1024, 1280) K scale/zero: group g of slot r at 1024 + 16*r + 4*g, fp16 scale then fp16 zero.
+ *   [1280, 1536) V scale/zero, same arrangement at 1280 + 16*r + 4*g.
  *   A code q in group g decodes to scale_g * q + zero_g, in the rotated frame.
  *   Pool: uint8 [num_pages][num_kv_heads][1536].
  *
@@ -73,7 +73,7 @@ typedef struct oscar_layout {
   int32_t page_size;          /* must be 16 */
   int32_t group_size;         /* must be 32 */
   int32_t num_sink;           /* S >= 0 */
-  int32_t window;             /* W >= 0; S + W <= 1024 */
+  int32_t window;             /* W >= 0; S + W <= 256 */
   int32_t num_pages;          /* physical pages in the pool */
   int32_t max_pages_per_seq;  /* block-table row stride */
   int32_t num_slots;          /* sequences the BF16 sink/window store can hold */
@@ -152,7 +152,8 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *   rot_k        fp32 [Hkv][128][128].
  *   sm_scale     softmax scale, usually 1/sqrt(128).
  *   split_pages  pages per split, >= 1.
- *   max_splits   INT2 splits per sequence, >= 1.
+ *   max_splits   INT2 splits per sequence, >= 1, with 8 * (num_q_heads / Hkv) * (max_splits + 1)
+ *                <= 49152 (else OSCAR_ERR_UNSUPPORTED).
  *   workspace    device buffer of at least oscar_decode_workspace_bytes(batch, num_q_heads,
  *                max_splits) bytes; contents on entry do not matter.
  * num_q_heads must be a multiple of Hkv with num_q_heads / Hkv in {1, 2, 4, 8}.

@@ -23,7 +23,8 @@ SOURCES = {
     # the quantiser is an fp32 formula reproduced bit for bit: never contract it into FMAs
     "append.hip": ["-ffp-contract=off"],
     # MFMA accumulators in VGPRs: the rescale path then needs no AGPR round trips
-    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # no NaN inputs by contract: lets max/min fuse with DPP row operations (no canonicalize)
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "combine.hip": [],
     "bf16_baseline.hip": [],
 }

@@ -31,6 +31,14 @@ int32_t check_heads(int32_t hq, int32_t hkv) {
   return OSCAR_OK;
 }
 
+// The combine keeps (m, l) of every split of a KV head's G query heads in 48 KiB of LDS.
+int32_t check_splits(int32_t hq, int32_t hkv, int32_t max_splits) {
+  if (max_splits < 1) return OSCAR_ERR_INVALID_ARGUMENT;
+  if ((size_t)2 * (hq / hkv) * ((size_t)max_splits + 1) * sizeof(float) > 48 * 1024)
+    return OSCAR_ERR_UNSUPPORTED;
+  return OSCAR_OK;
+}
+
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? OSCAR_OK : OSCAR_ERR_HIP; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -93,6 +101,8 @@ int32_t oscar_decode_attention(
     return OSCAR_ERR_INVALID_ARGUMENT;
   st = check_heads(num_q_heads, lay->num_kv_heads);
   if (st != OSCAR_OK) return st;
+  st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
+  if (st != OSCAR_OK) return st;
   if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0) return OSCAR_OK;
   if (!pages || !block_table || !q || !seq_lens || !rot_k || !workspace)
@@ -116,6 +126,8 @@ int32_t oscar_combine(
   if (batch < 0 || num_kv_heads < 1 || max_splits < 1 || max_splits > 65535)
     return OSCAR_ERR_INVALID_ARGUMENT;
   int32_t st = check_heads(num_q_heads, num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_splits(num_q_heads, num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
   if (batch == 0) return OSCAR_OK;
   if (!workspace || !out) return OSCAR_ERR_INVALID_ARGUMENT;
@@ -152,6 +164,8 @@ int32_t oscar_bf16_decode_attention(
   if (batch < 0 || split_pages < 1 || max_splits < 1 || max_splits > 65535)
     return OSCAR_ERR_INVALID_ARGUMENT;
   st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
   if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0) return OSCAR_OK;

@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
       if (info.rec >= 0) {
         uint32_t meta = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
                         ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
-        *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kVMeta : kKMeta) + 64 * gi +
-                                     4 * info.slot_in_page) = meta;
+        *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kVMeta : kKMeta) +
+                                     16 * info.slot_in_page + 4 * gi) = meta;
       }
     }
   }

@@ -3,70 +3,88 @@
 // rotation (o = o' . R_V^T, exact for orthogonal R_V; OSCAR paper, "Abstract": fixed rotations
 // keep attention aligned with what it consumes).
 //
-// grid (Hkv, batch), block 128 (thread = output channel).  One workgroup serves the G query heads
-// of a KV head, so each row of R_V is read once per workgroup.
+// One workgroup serves the G query heads of a KV head; every thread issues all of its global
+// loads (its R_V row and its channel of every split) before the first use.
 #include "oscar_internal.h"
 
 namespace oscar {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kRStride = kHeadDim + 4;  // floats per LDS row of R_V (16-byte aligned, skewed banks)
 
-__global__ __launch_bounds__(128) void combine_kernel(int hq, int hkv, Workspace ws,
-                                                     const float* __restrict__ rot_v,
-                                                     float* __restrict__ out,
-                                                     float* __restrict__ lse) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+// grid (Hkv, batch), block 128 * G: thread (j, c) = (query head of the group, channel).
+__global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspace ws,
+                                                      const float* __restrict__ rot_v,
+                                                      float* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  const int h = blockIdx.x, b = blockIdx.y;
   const int G = hq / hkv;
+  const int j = threadIdx.x >> 7, c = threadIdx.x & 127;
+  const int ns = ws.nslots;
+  const int jq = h * G + j;
+  extern __shared__ float s_w[];        // [G][ns] merge weights 2^(m_s - M), 0 for empty
   __shared__ float s_o[8][kHeadDim];
-  float inv_l[8];
-  for (int j = 0; j < G; ++j) {
-    const int jq = h * G + j;
-    float M = -INFINITY;
-    for (int s = 0; s < ws.nslots; ++s) {
-      const float2 ml = *ws.ml(b, hq, jq, s);
-      if (ml.y > 0.f) M = fmaxf(M, ml.x);
-    }
-    float l = 0.f, o = 0.f;
-    for (int s = 0; s < ws.nslots; ++s) {
-      const float2 ml = *ws.ml(b, hq, jq, s);
-      if (ml.y > 0.f) {
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        l = fmaf(w, ml.y, l);
-        o = fmaf(w, ws.o(b, hq, jq, s)[c], o);
-      }
-    }
-    s_o[j][c] = l > 0.f ? o / l : 0.f;
-    inv_l[j & 7] = l;
-    if (c == 0 && lse != nullptr)
-      lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
+  __shared__ float s_inv[8];
+  __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
+
+  // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of every split.
+  if (rot_v != nullptr) {
+    const float4* R = reinterpret_cast<const float4*>(rot_v + (size_t)h * kHeadDim * kHeadDim);
+    for (int e = threadIdx.x; e < kHeadDim * kHeadDim / 4; e += blockDim.x)
+      s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = R[e];
+  }
+  const float* o = ws.o(b, hq, jq, 0) + c;
+  constexpr int kBatch = 16;
+  float ov[kBatch];
+#pragma unroll
+  for (int s = 0; s < kBatch; ++s) ov[s] = s < ns ? o[(size_t)s * kHeadDim] : 0.f;
+
+  // Merge weights of head j (threads c < ns of each head load one split's (m, l)).
+  for (int s = c; s < ns; s += 128) {
+    const float2 ml = *ws.ml(b, hq, jq, s);
+    s_w[j * ns + s] = ml.y > 0.f ? ml.x : -INFINITY;
+    s_w[G * ns + j * ns + s] = ml.y;
   }
   __syncthreads();
-  (void)inv_l;
-  float* orow = out + ((size_t)b * hq + h * G) * kHeadDim;
+  if (c == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_w[j * ns + s]);
+    float l = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ls = s_w[G * ns + j * ns + s];
+      const float w = ls > 0.f ? __builtin_amdgcn_exp2f(s_w[j * ns + s] - M) : 0.f;
+      s_w[j * ns + s] = w;
+      l = fmaf(w, ls, l);
+    }
+    s_inv[j] = l > 0.f ? 1.0f / l : 0.f;
+    if (lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
+  }
+  __syncthreads();
+  // o'[j][c] = sum_s w_s o'_s[c] / l, splits in ascending order.
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < kBatch; ++s)
+    if (s < ns) acc = fmaf(s_w[j * ns + s], ov[s], acc);
+  for (int s = kBatch; s < ns; ++s) acc = fmaf(s_w[j * ns + s], o[(size_t)s * kHeadDim], acc);
+  s_o[j][c] = acc * s_inv[j];
+  __syncthreads();
+  float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
   if (rot_v == nullptr) {
-    for (int j = 0; j < G; ++j) orow[j * kHeadDim + c] = s_o[j][c];
+    orow[c] = s_o[j][c];
     return;
   }
   // out[j][c] = sum_k o'[j][k] * R_V[h][c][k]
-  const float4* R = reinterpret_cast<const float4*>(rot_v + ((size_t)h * kHeadDim + c) * kHeadDim);
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  float acc2 = 0.f;
+#pragma unroll 8
   for (int k4 = 0; k4 < kHeadDim / 4; ++k4) {
-    const float4 r = R[k4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < G) {
-        acc[j] = fmaf(s_o[j][4 * k4 + 0], r.x, acc[j]);
-        acc[j] = fmaf(s_o[j][4 * k4 + 1], r.y, acc[j]);
-        acc[j] = fmaf(s_o[j][4 * k4 + 2], r.z, acc[j]);
-        acc[j] = fmaf(s_o[j][4 * k4 + 3], r.w, acc[j]);
-      }
+    const float4 r = s_r[c][k4];
+    acc2 = fmaf(s_o[j][4 * k4 + 0], r.x, acc2);
+    acc2 = fmaf(s_o[j][4 * k4 + 1], r.y, acc2);
+    acc2 = fmaf(s_o[j][4 * k4 + 2], r.z, acc2);
+    acc2 = fmaf(s_o[j][4 * k4 + 3], r.w, acc2);
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < G) orow[j * kHeadDim + c] = acc[j];
+  orow[c] = acc2;
 }
 
 }  // namespace
@@ -74,8 +92,10 @@ __global__ __launch_bounds__(128) void combine_kernel(int hq, int hkv, Workspace
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(hkv, batch), dim3(128), 0, stream, hq, hkv, ws, rot_v,
-                     out, lse);
+  const size_t lds = (size_t)2 * (hq / hkv) * ws.nslots * sizeof(float);
+  if (lds > 48 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(hkv, batch), dim3(128 * (hq / hkv)), lds, stream, hq, hkv,
+                     ws, rot_v, out, lse);
   return hipGetLastError();
 }
 

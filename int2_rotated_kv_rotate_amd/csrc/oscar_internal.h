@@ -14,7 +14,7 @@ constexpr int kGroups = kHeadDim / kGroup;
 constexpr int kRecord = 1536;                 // bytes per (page, KV head) INT2 record
 constexpr int kKCodes = 0, kVCodes = 512, kKMeta = 1024, kVMeta = 1280;
 constexpr int kBf16PageElems = 2 * kPage * kHeadDim;  // 4096 bf16 per (page, KV head)
-constexpr int kMaxSinkWindow = 1024;
+constexpr int kMaxSinkWindow = 256;   // S + W
 
 // Workspace layout (all offsets in bytes from the workspace base).
 //   Q region:  per (b, j) a 1024-byte block

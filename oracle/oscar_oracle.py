@@ -168,8 +168,8 @@ def quantize_rows(x_bits: np.ndarray, rot32: np.ndarray, clip: float):
 #   [ 512, 1024)  V codes.  Channel c of slot r: lane chunk L = 16*(r // 4) + (c % 16) at
 #                 512 + 8*L; dword (r % 4) // 2 of the chunk, 16-bit half r % 2 of the dword;
 #                 inside the half, bits 2*(c // 16) .. +1.
-#   [1024, 1280)  K scale/zero.  Group g of slot r: fp16 scale then fp16 zero at 1024 + 64*g + 4*r.
-#   [1280, 1536)  V scale/zero, same arrangement at 1280 + 64*g + 4*r.
+#   [1024, 1280)  K scale/zero.  Group g of slot r: fp16 scale then fp16 zero at 1024 + 16*r + 4*g.
+#   [1280, 1536)  V scale/zero, same arrangement at 1280 + 16*r + 4*g.
 #
 # All multi-byte fields are little-endian.
 # ----------------------------------------------------------------------------------------
@@ -193,7 +193,7 @@ def v_code_location(r, c):
 
 def meta_location(kind: str, r, g):
     """Byte offset of the (fp16 scale, fp16 zero) pair of group g of slot r."""
-    return (K_META if kind == "k" else V_META) + 64 * g + 4 * r
+    return (K_META if kind == "k" else V_META) + 16 * r + 4 * g
 
 
 _CH = np.arange(D)

@@ -71,7 +71,7 @@ def test_append_validation(lib):
     assert _append(lib, _layout(head_dim=64)) == 2
     assert _append(lib, _layout(page_size=32)) == 2
     assert _append(lib, _layout(group_size=64)) == 2
-    assert _append(lib, _layout(num_sink=600, window=600)) == 2
+    assert _append(lib, _layout(num_sink=100, window=157)) == 2
     assert _append(lib, _layout(window=-1)) == 1
     assert _append(lib, _layout(), ck=0.0) == 1
     assert _append(lib, _layout(), cv=1.5) == 1
