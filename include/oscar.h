@@ -143,19 +143,27 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *   logits z_p = sm_scale * (q' . k_p), and the partials hold, per split, the max of
  *   z_p*log2(e), the sum of 2^(z_p*log2(e) - max), and the matching unnormalised weighted sum
  *   of the rotated values.
- * The INT2 positions are split into runs of split_pages pages (split s covers logical pages
- * [s*split_pages, (s+1)*split_pages), the last split everything after); the BF16 positions
- * form one more split.
+ * Work split: the INT2 pages of all (sequence, KV head) pairs, laid end to end in (sequence,
+ * head) order, are cut into equal runs of C pages, one per worker wavefront, so every worker
+ * streams the same number of pages however the lengths are mixed.  A run yields one partial
+ * for each pair it touches; a pair's partials fill its slots 0, 1, ... in page order.  C is the
+ * smallest run length that needs at most num_workers runs and gives no pair more than
+ * max_splits partials.  The BF16 positions of each pair form one more partial.
  *
  *   q            bf16 bits [batch][num_q_heads][128] (after RoPE, unrotated).
  *   seq_lens     int32 [batch], >= 1.
  *   rot_k        fp32 [Hkv][128][128].
  *   sm_scale     softmax scale, usually 1/sqrt(128).
- *   split_pages  pages per split, >= 1.
- *   max_splits   INT2 splits per sequence, >= 1, with 8 * (num_q_heads / Hkv) * (max_splits + 1)
- *                <= 49152 (else OSCAR_ERR_UNSUPPORTED).
+ *   num_workers  worker wavefronts, 0 for one per resident wavefront slot of the device
+ *                (the fastest choice); at most 2^20.
+ *   max_splits   INT2 partials per (sequence, KV head), >= 1, with
+ *                8 * (num_q_heads / Hkv) * (max_splits + 1) <= 49152 (else
+ *                OSCAR_ERR_UNSUPPORTED).  Too small a value lengthens the runs.
  *   workspace    device buffer of at least oscar_decode_workspace_bytes(batch, num_q_heads,
  *                max_splits) bytes; contents on entry do not matter.
+ * batch * Hkv * max_pages_per_seq must be below 2^31 (else OSCAR_ERR_UNSUPPORTED).
+ * A block-table entry outside [0, num_pages) for a position below seq_lens[b] is a caller error:
+ * page 0 is read in its place (memory stays in bounds; the result is unspecified).
  * num_q_heads must be a multiple of Hkv with num_q_heads / Hkv in {1, 2, 4, 8}.
  */
 int32_t oscar_decode_attention(
@@ -163,7 +171,7 @@ int32_t oscar_decode_attention(
     const int32_t* block_table, const int32_t* slot_ids,
     int32_t batch, int32_t num_q_heads,
     const uint16_t* q, const int32_t* seq_lens, const float* rot_k, float sm_scale,
-    int32_t split_pages, int32_t max_splits,
+    int32_t num_workers, int32_t max_splits,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -200,9 +208,10 @@ int32_t oscar_bf16_append(
     const int32_t* new_offsets, const int32_t* start_pos, void* stream);
 
 /*
- * BF16 baseline decode, first stage: same split scheme and workspace format as
- * oscar_decode_attention over all positions [0, L) of the BF16 pages (q unrotated); finish
- * with oscar_combine(..., rot_v = NULL, ...).
+ * BF16 baseline decode, first stage: the same workspace format as oscar_decode_attention
+ * over all positions [0, L) of the BF16 pages (q unrotated), split per sequence into runs of
+ * split_pages logical pages (split s covers pages [s*split_pages, (s+1)*split_pages), the last
+ * split everything after); finish with oscar_combine(..., rot_v = NULL, ...).
  */
 int32_t oscar_bf16_decode_attention(
     const oscar_layout* lay, const uint16_t* pages, const int32_t* block_table,

@@ -39,6 +39,8 @@ int32_t check_splits(int32_t hq, int32_t hkv, int32_t max_splits) {
   return OSCAR_OK;
 }
 
+constexpr int32_t kMaxWorkers = 1 << 20;
+
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? OSCAR_OK : OSCAR_ERR_HIP; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -93,12 +95,16 @@ int32_t oscar_decode_attention(
     const int32_t* block_table, const int32_t* slot_ids,
     int32_t batch, int32_t num_q_heads,
     const uint16_t* q, const int32_t* seq_lens, const float* rot_k, float sm_scale,
-    int32_t split_pages, int32_t max_splits,
+    int32_t num_workers, int32_t max_splits,
     void* workspace, size_t workspace_bytes_given, void* stream) {
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
-  if (batch < 0 || split_pages < 1 || max_splits < 1 || max_splits > 65535)
+  if (batch < 0 || num_workers < 0 || num_workers > kMaxWorkers || max_splits < 1 ||
+      max_splits > 65535)
     return OSCAR_ERR_INVALID_ARGUMENT;
+  // page counts of the work plan are int32
+  if ((long long)batch * lay->num_kv_heads * lay->max_pages_per_seq > 0x7FFFFFFFLL)
+    return OSCAR_ERR_UNSUPPORTED;
   st = check_heads(num_q_heads, lay->num_kv_heads);
   if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
@@ -115,7 +121,7 @@ int32_t oscar_decode_attention(
     return OSCAR_ERR_WORKSPACE_TOO_SMALL;
   Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
   return hip_status(launch_decode(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
-                                  num_q_heads, q, seq_lens, rot_k, sm_scale, split_pages, ws,
+                                  num_q_heads, q, seq_lens, rot_k, sm_scale, num_workers, ws,
                                   (hipStream_t)stream));
 }
 

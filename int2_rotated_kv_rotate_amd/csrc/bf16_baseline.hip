@@ -164,11 +164,13 @@ __global__ __launch_bounds__(64) void bf16_decode_kernel(
   if (kq == 0 && c16 < G) *ws.ml(b, hq, h * G + c16, split) = make_float2(mrun, lt);
 }
 
-// The BF16 baseline has no sink/window split: mark the last slot empty.
-__global__ void empty_slot_kernel(int hq, Workspace ws) {
+// The BF16 baseline has no sink/window split: mark the last slot empty, and every split slot
+// of every (sequence, KV head) as written (each split writes its slot, empty or not).
+__global__ void empty_slot_kernel(int hq, int hkv, Workspace ws) {
   const int b = blockIdx.x;
   for (int j = threadIdx.x; j < hq; j += blockDim.x)
     *ws.ml(b, hq, j, ws.nslots - 1) = make_float2(kNegBig, 0.f);
+  for (int h = threadIdx.x; h < hkv; h += blockDim.x) ws.nvalid()[b * hkv + h] = ws.nslots - 1;
 }
 
 }  // namespace
@@ -190,7 +192,7 @@ hipError_t launch_bf16_decode(const CacheGeom& g, const uint16_t* pages,
   if (batch == 0) return hipSuccess;
   hipLaunchKernelGGL(bf16_decode_kernel, dim3(ws.nslots - 1, g.hkv, batch), dim3(64), 0, stream,
                      g, pages, block_table, hq, q, seq_lens, sm_scale, split_pages, ws);
-  hipLaunchKernelGGL(empty_slot_kernel, dim3(batch), dim3(64), 0, stream, hq, ws);
+  hipLaunchKernelGGL(empty_slot_kernel, dim3(batch), dim3(64), 0, stream, hq, g.hkv, ws);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   const int j = threadIdx.x >> 7, c = threadIdx.x & 127;
   const int ns = ws.nslots;
   const int jq = h * G + j;
-  extern __shared__ float s_w[];        // [G][ns] merge weights 2^(m_s - M), 0 for empty
+  extern __shared__ float s_w[];        // [2][G][ns]: merge weights 2^(m - M) (0 for empty), l
   __shared__ float s_o[8][kHeadDim];
   __shared__ float s_inv[8];
   __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
@@ -34,39 +34,50 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
     for (int e = threadIdx.x; e < kHeadDim * kHeadDim / 4; e += blockDim.x)
       s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = R[e];
   }
+  // INT2 partials in slots [0, nvalid), the BF16 sink/window partial in the last slot; the
+  // merge runs over n = nvalid + 1 entries, entry e < nvalid being slot e.
+  const int nv = min(max(ws.nvalid()[b * hkv + h], 0), ns - 1);
+  const int n = nv + 1;
+  auto slot_of = [&](int e) { return e < nv ? e : ns - 1; };
   const float* o = ws.o(b, hq, jq, 0) + c;
   constexpr int kBatch = 16;
   float ov[kBatch];
 #pragma unroll
-  for (int s = 0; s < kBatch; ++s) ov[s] = s < ns ? o[(size_t)s * kHeadDim] : 0.f;
+  for (int e = 0; e < kBatch; ++e) ov[e] = e < n ? o[(size_t)slot_of(e) * kHeadDim] : 0.f;
 
-  // Merge weights of head j (threads c < ns of each head load one split's (m, l)).
-  for (int s = c; s < ns; s += 128) {
-    const float2 ml = *ws.ml(b, hq, jq, s);
-    s_w[j * ns + s] = ml.y > 0.f ? ml.x : -INFINITY;
-    s_w[G * ns + j * ns + s] = ml.y;
+  // Merge weights of head j (threads c < n of each head load one entry's (m, l)).
+  for (int e = c; e < n; e += 128) {
+    const float2 ml = *ws.ml(b, hq, jq, slot_of(e));
+    s_w[j * ns + e] = ml.y > 0.f ? ml.x : -INFINITY;
+    s_w[G * ns + j * ns + e] = ml.y;
   }
   __syncthreads();
   if (c == 0) {
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_w[j * ns + s]);
+    for (int e = 0; e < n; ++e) M = fmaxf(M, s_w[j * ns + e]);
     float l = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ls = s_w[G * ns + j * ns + s];
-      const float w = ls > 0.f ? __builtin_amdgcn_exp2f(s_w[j * ns + s] - M) : 0.f;
-      s_w[j * ns + s] = w;
+    for (int e = 0; e < n; ++e) {
+      const float ls = s_w[G * ns + j * ns + e];
+      const float w = ls > 0.f ? __builtin_amdgcn_exp2f(s_w[j * ns + e] - M) : 0.f;
+      s_w[j * ns + e] = w;
       l = fmaf(w, ls, l);
     }
     s_inv[j] = l > 0.f ? 1.0f / l : 0.f;
     if (lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
   }
   __syncthreads();
-  // o'[j][c] = sum_s w_s o'_s[c] / l, splits in ascending order.
+  // o'[j][c] = sum_e w_e o'_e[c] / l in entry order; an empty entry (w = 0) is skipped, so its
+  // partial output is never read into the sum.
   float acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < kBatch; ++s)
-    if (s < ns) acc = fmaf(s_w[j * ns + s], ov[s], acc);
-  for (int s = kBatch; s < ns; ++s) acc = fmaf(s_w[j * ns + s], o[(size_t)s * kHeadDim], acc);
+  for (int e = 0; e < kBatch; ++e) {
+    const float w = s_w[j * ns + e];
+    if (e < n && w > 0.f) acc = fmaf(w, ov[e], acc);
+  }
+  for (int e = kBatch; e < n; ++e) {
+    const float w = s_w[j * ns + e];
+    if (w > 0.f) acc = fmaf(w, o[(size_t)slot_of(e) * kHeadDim], acc);
+  }
   s_o[j][c] = acc * s_inv[j];
   __syncthreads();
   float* orow = out + ((size_t)b * hq + jq) * kHeadDim;

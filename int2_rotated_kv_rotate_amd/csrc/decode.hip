@@ -7,20 +7,25 @@
 // orthogonal R_K, and the rotated output is rotated back with R_V^T by the combine kernel.
 //
 // Kernels
-//   prep_window_kernel per (KV head, sequence): q' = q . R_K for the G query heads of the group
-//                      plus an integer form of q' for the int8 matrix cores, and attention
-//                      over the BF16 sink + window positions (the last split).
-//   int2_decode_kernel per (split, KV head, sequence), one wavefront: walks the split's pages
-//                      through the block table.  Per page it reads one 1536-byte record with
-//                      four coalesced vector loads per lane, computes the G x 16 logits on the
-//                      int8 MFMA (codes are exact int8, q' is two int8 pieces), runs the online
-//                      softmax, and accumulates P.V on the bf16 MFMA (codes exact as bf16
-//                      1 + code/4, weights p*scale as two bf16 pieces).
+//   prep_q_kernel      per (KV head, sequence): q' = q . R_K for the G query heads of the group
+//                      plus an integer form of q' for the int8 matrix cores; one extra
+//                      workgroup writes the work plan of the INT2 workers.
+//   int2_decode_kernel persistent INT2 workers, one wavefront each: a worker walks an equal
+//                      share of all pages of all (sequence, KV head) pairs through the block
+//                      tables.  Per page it copies one 1536-byte record into an LDS ring with
+//                      direct-to-LDS loads, computes the G x 16 logits on the int8 MFMA (codes
+//                      are exact int8, q' is two int8 pieces), runs the softmax against a
+//                      reference max, and accumulates P.V on the bf16 MFMA (codes exact as
+//                      bf16 1 + code/16 or 1 + code/4, weights p*scale as two bf16 pieces).
+//                      Extra workgroups at the end of the grid attend over each pair's BF16
+//                      sink + window positions.
 //
 // MFMA operand layouts (16x16 tiles, wave64): an A operand row m lives in lane m + 16*k4 and a
 // B operand column n in lane n + 16*k4, with k4 selecting a quarter of the K dimension; the
 // 16x16 result puts rows 4*(lane/16) + i of column lane%16 in accumulator register i.  The K
 // axis is permuted consistently on both operands, which leaves the product unchanged.
+#include <atomic>
+
 #include "oscar_internal.h"
 
 namespace oscar {
@@ -75,52 +80,108 @@ __device__ __forceinline__ void split_bf16(const float w[4], uint32_t& h01, uint
   l23 = pack_bf16(w[2] - __uint_as_float(h23 << 16), w[3] - __uint_as_float(h23 & 0xFFFF0000u));
 }
 
-// ---------------------------------------------------------------- q rotation + BF16 window
+// ------------------------------------------------------------------------ q rotation + plan
 
-// One workgroup (256 threads) per (KV head, sequence):
-//  1. q' = q . R_K for the G query heads of the group (fp32), written to the workspace with its
-//     int8 form for the matrix cores: q' ~= qsc * (hi + lo / 254), hi/lo in [-127, 127], stored
-//     in MFMA slot order, plus the sum of q' over each 32-channel group;
-//  2. attention over the BF16 positions [0, n_sink) and [L - n_win, L) (sinks + recent window,
-//     rotated frame), written as the last split's partials (m in log2 units, l, o').
-// Every global load is issued before its first use: R_K as 16 independent float4 loads per
-// thread (partial sums over 16 input rows, reduced through LDS), each token's K row straight
-// into the registers of the thread that scores it, and the V rows bulk-copied into LDS, so
-// each phase pays about one memory latency.
+// One workgroup (256 threads) per (KV head, sequence): q' = q . R_K for the G query heads of
+// the group (fp32), written to the workspace with its int8 form for the matrix cores:
+// q' ~= qsc * (hi + lo / 254), hi/lo in [-127, 127], stored in MFMA slot order, plus the
+// per-group sums of the encoded values.  Every global load is issued before its first use:
+// R_K as 16 independent float4 loads per thread (partial sums over 16 input rows, reduced
+// through LDS).  One more workgroup, (0, batch), builds the work plan of the INT2 kernel.
 constexpr int kPrepThreads = 256;
 
-struct PrepPhase1 {
-  float4 part[8][8][kHeadDim / 4];  // [input block][head][channel quad] partial q'
-};
-struct PrepPhase2 {
-  float p[kMaxSinkWindow][8];       // logits, then probabilities
-  float o[2][8][kHeadDim];          // P.V halves
-};
+// Work plan for int2_decode_kernel, built by one workgroup (kPrepThreads threads).  The INT2
+// pages of every (sequence, KV head) pair, laid end to end in (sequence, head) order, are cut
+// into runs of C pages, one run per worker; C is the smallest length that needs at most
+// `workers` runs and leaves no pair more than max_splits runs.
+__device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_lens, int workers,
+                           const Workspace& ws) {
+  __shared__ int s_scan[kPrepThreads];
+  __shared__ int s_max[kPrepThreads];
+  const int t = threadIdx.x, B = ws.batch, max_splits = ws.nslots - 1;
+  auto int2_pages = [&](int b, int& first) -> int {  // INT2 pages of sequence b, first page
+    const int L = max(seq_lens[b], 0);
+    const int n_sink = min(L, g.num_sink);
+    const int lo = n_sink, hi = L - min(g.window, L - n_sink);
+    first = lo / kPage;
+    if (hi <= lo) return 0;
+    return max(min((hi + kPage - 1) / kPage, g.max_pages) - first, 0);
+  };
+  // pass 1: total pages and the largest pair
+  int tot = 0, pmax = 0;
+  for (int b = t; b < B; b += kPrepThreads) {
+    int first;
+    const int P = int2_pages(b, first);
+    tot += P * g.hkv;
+    pmax = max(pmax, P);
+  }
+  s_scan[t] = tot;
+  s_max[t] = pmax;
+  __syncthreads();
+  for (int o = kPrepThreads / 2; o > 0; o >>= 1) {
+    if (t < o) {
+      s_scan[t] += s_scan[t + o];
+      s_max[t] = max(s_max[t], s_max[t + o]);
+    }
+    __syncthreads();
+  }
+  const int total = s_scan[0];
+  pmax = s_max[0];
+  __syncthreads();
+  long long C = max(1LL, ((long long)total + workers - 1) / workers);
+  if (max_splits > 1) C = max(C, ((long long)pmax + max_splits - 2) / (max_splits - 1));
+  else C = max(C, (long long)total);
+  // pass 2: prefix sums in chunks of kPrepThreads sequences
+  int32_t* pstart = ws.pstart();
+  int32_t* npg = ws.npg();
+  int32_t* pglo = ws.pglo();
+  int32_t* nvalid = ws.nvalid();
+  int carry = 0;
+  for (int base = 0; base < B; base += kPrepThreads) {
+    const int b = base + t;
+    int first = 0;
+    const int P = b < B ? int2_pages(b, first) : 0;
+    const int x = P * g.hkv;
+    s_scan[t] = x;
+    __syncthreads();
+    for (int o = 1; o < kPrepThreads; o <<= 1) {  // inclusive scan
+      const int y = t >= o ? s_scan[t - o] : 0;
+      __syncthreads();
+      s_scan[t] += y;
+      __syncthreads();
+    }
+    if (b < B) {
+      const int start = carry + s_scan[t] - x;
+      pstart[b] = start;
+      npg[b] = P;
+      pglo[b] = first;
+      for (int h = 0; h < g.hkv; ++h) {
+        const long long s0 = (long long)start + (long long)h * P;
+        nvalid[b * g.hkv + h] = P == 0 ? 0 : (int)((s0 + P - 1) / C - s0 / C + 1);
+      }
+    }
+    carry += s_scan[kPrepThreads - 1];
+    __syncthreads();
+  }
+  if (t == 0) {
+    ws.plan()[0] = total;
+    ws.plan()[1] = (int)C;
+  }
+}
 
-__global__ __launch_bounds__(kPrepThreads) void prep_window_kernel(
-    CacheGeom g, const uint16_t* __restrict__ q, const float* __restrict__ rot_k,
-    const uint16_t* __restrict__ sinkwin, const int32_t* __restrict__ slot_ids, int hq,
-    const int32_t* __restrict__ seq_lens, float sm_scale, Workspace ws) {
+__global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
+    CacheGeom g, const uint16_t* __restrict__ q, const float* __restrict__ rot_k, int hq,
+    const int32_t* __restrict__ seq_lens, int workers, Workspace ws) {
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  if (b == ws.batch) {  // the extra row of workgroups: (0, batch) builds the plan
+    if (h == 0) build_plan(g, seq_lens, workers, ws);
+    return;
+  }
   const int lane = t & 63, wv = t >> 6;
   const int G = hq / g.hkv;
-  extern __shared__ uint32_t s_v[];                    // [n][64] window V rows (bf16 pairs)
   __shared__ float s_q[8][kHeadDim];                   // q (bf16 widened)
   __shared__ float s_qr[8][kHeadDim];                  // q' = q . R_K
-  __shared__ union { PrepPhase1 a; PrepPhase2 c; } s_u;
-  __shared__ float s_red[4][8];
-
-  const int L = max(seq_lens[b], 0);
-  const int slot = slot_ids ? slot_ids[b] : b;
-  const int n_sink = min(L, g.num_sink);
-  const int n_win = min(g.window, L - n_sink);
-  const bool live = sinkwin != nullptr && slot >= 0 && slot < g.num_slots && n_sink + n_win > 0;
-  const int n = live ? n_sink + n_win : 0;
-  const size_t base = ((size_t)slot * g.hkv + h) * (size_t)(g.num_sink + g.window);
-  auto row_of = [&](int i) {  // window token index -> store row
-    const int p = i < n_sink ? i : L - n_win + (i - n_sink);
-    return p < g.num_sink ? p : g.num_sink + p % g.window;
-  };
+  __shared__ float4 s_part[8][8][kHeadDim / 4];        // [input block][head][channel quad]
 
   // Issue the R_K loads: thread -> channel quad c4 = t % 32, input block ib = t / 32 (16 rows).
   const int c4 = t & 31, ib = t >> 5;
@@ -128,24 +189,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_window_kernel(
   float4 r[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) r[k] = R4[(16 * ib + k) * (kHeadDim / 4) + c4];
-  // This thread's window token: its K row into registers.
-  uint4 kk[16];
-  if (t < n) {
-    const uint4* krow = reinterpret_cast<const uint4*>(sinkwin + (base + row_of(t)) * 2 * kHeadDim);
-#pragma unroll
-    for (int c8 = 0; c8 < 16; ++c8) kk[c8] = krow[c8];
-  }
-  // V rows into LDS.
-  for (int e = t; e < n * (kHeadDim / 8); e += kPrepThreads) {
-    const int i = e >> 4, w = e & 15;
-    reinterpret_cast<uint4*>(s_v)[e] =
-        reinterpret_cast<const uint4*>(sinkwin + (base + row_of(i)) * 2 * kHeadDim + kHeadDim)[w];
-  }
   for (int i = t; i < G * kHeadDim; i += kPrepThreads)
     s_q[i / kHeadDim][i % kHeadDim] = bf16_to_f32(q[((size_t)b * hq + h * G) * kHeadDim + i]);
   __syncthreads();
 
-  // 1. q' partial sums over this thread's 16 input rows, then reduce the 8 blocks in order.
+  // q' partial sums over this thread's 16 input rows, then reduce the 8 blocks in order.
   {
     float4 acc[8];
 #pragma unroll
@@ -165,14 +213,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_window_kernel(
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < G) s_u.a.part[ib][j][c4] = acc[j];
+      if (j < G) s_part[ib][j][c4] = acc[j];
   }
   __syncthreads();
   for (int e = t; e < G * kHeadDim; e += kPrepThreads) {
     const int j = e / kHeadDim, c = e % kHeadDim;
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s += reinterpret_cast<const float*>(&s_u.a.part[k][j][0])[c];
+    for (int k = 0; k < 8; ++k) s += reinterpret_cast<const float*>(&s_part[k][j][0])[c];
     s_qr[j][c] = s;
   }
   __syncthreads();
@@ -182,10 +230,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_window_kernel(
     const float v0 = s_qr[j][2 * lane], v1 = s_qr[j][2 * lane + 1];
     float a = fmaxf(fabsf(v0), fabsf(v1));
     for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-    float s = v0 + v1;  // 16 lanes = one 32-channel group
-    for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     const float qsc = a / 127.0f;
     char* blk = ws.qblock(b, hq, h * G + j);
+    int esum = 0;  // sum of the encoded values 254*hi + lo over this lane's two channels
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int c = 2 * lane + e;
@@ -195,101 +242,19 @@ __global__ __launch_bounds__(kPrepThreads) void prep_window_kernel(
         hi = max(-127, min(127, (int)__builtin_rintf(v / qsc)));
         lo = max(-127, min(127, (int)__builtin_rintf((v - (float)hi * qsc) * 254.0f / qsc)));
       }
+      esum += 254 * hi + lo;
       // slot order inside each 16-channel word: slot 4*i + b holds channel 4*b + i
       const int pos = 16 * (c / 16) + 4 * (c % 4) + (c % 16) / 4;
       blk[kQHiOff + pos] = (char)hi;
       blk[kQLoOff + pos] = (char)lo;
     }
+    // The zero-point term of a logit uses these sums of the encoded q' (exact integers), so
+    // that a key's code and zero parts see the same query: z*sum(q') and s*q'.codes then
+    // carry one encoding error that cancels as in q'.k, instead of two that do not.
+    for (int o = 8; o >= 1; o >>= 1) esum += __shfl_xor(esum, o);  // 16 lanes = 32 channels
     reinterpret_cast<float2*>(blk)[lane] = make_float2(v0, v1);
     if (lane == 0) *reinterpret_cast<float*>(blk + kQScOff) = qsc;
-    if ((lane & 15) == 0) reinterpret_cast<float*>(blk + kQSumOff)[lane >> 4] = s;
-  }
-
-  // 2. Window logits: thread t scores token t from its K row in registers.
-  const float sm_log2 = sm_scale * kLog2e;
-  float lg[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) lg[j] = -INFINITY;
-  if (t < n) {
-    float dot[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dot[j] = 0.f;
-#pragma unroll
-    for (int c8 = 0; c8 < 16; ++c8) {
-      const uint32_t w[4] = {kk[c8].x, kk[c8].y, kk[c8].z, kk[c8].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float k0 = __uint_as_float(w[e] << 16), k1 = __uint_as_float(w[e] & 0xFFFF0000u);
-        const int c = 8 * c8 + 2 * e;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < G) dot[j] = fmaf(s_qr[j][c + 1], k1, fmaf(s_qr[j][c], k0, dot[j]));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < G) lg[j] = dot[j] * sm_log2;
-  }
-  float m[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float x = lg[j];
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    if (lane == 0) s_red[wv][j] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    m[j] = fmaxf(fmaxf(s_red[0][j], s_red[1][j]), fmaxf(s_red[2][j], s_red[3][j]));
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = t < n && j < G ? __builtin_amdgcn_exp2f(lg[j] - m[j]) : 0.f;
-    if (t < n) s_u.c.p[t][j] = p;
-    float x = p;
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    if (lane == 0) s_red[wv][j] = x;
-  }
-  __syncthreads();
-  // P.V: thread -> channel pair cp, token quarter tq.
-  {
-    const int cp = t & 63, tq = t >> 6;
-    float o0[8], o1[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o0[j] = o1[j] = 0.f;
-    for (int i = tq; i < n; i += 4) {
-      const uint32_t vv = s_v[i * (kHeadDim / 2) + cp];
-      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xFFFF0000u);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < G) {
-          o0[j] = fmaf(s_u.c.p[i][j], v0, o0[j]);
-          o1[j] = fmaf(s_u.c.p[i][j], v1, o1[j]);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < G && tq >= 2) {
-        s_u.c.o[tq - 2][j][2 * cp] = o0[j];
-        s_u.c.o[tq - 2][j][2 * cp + 1] = o1[j];
-      }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < G && tq < 2) {
-        s_u.c.o[tq][j][2 * cp] += o0[j];
-        s_u.c.o[tq][j][2 * cp + 1] += o1[j];
-      }
-    __syncthreads();
-  }
-  const int out_slot = ws.nslots - 1;
-  for (int i = t; i < G * kHeadDim; i += kPrepThreads) {
-    const int j = i / kHeadDim, c = i % kHeadDim;
-    ws.o(b, hq, h * G + j, out_slot)[c] = s_u.c.o[0][j][c] + s_u.c.o[1][j][c];
-  }
-  if (t < G) {
-    const float l = s_red[0][t] + s_red[1][t] + s_red[2][t] + s_red[3][t];
-    *ws.ml(b, hq, h * G + t, out_slot) = n > 0 ? make_float2(m[t], l) : make_float2(kNegBig, 0.f);
+    if ((lane & 15) == 0) reinterpret_cast<float*>(blk + kQSumOff)[lane >> 4] = (float)esum;
   }
 }
 
@@ -353,8 +318,8 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 // track them (it would otherwise wait for every outstanding direct-to-LDS load before any LDS
 // access).  Loads the compiler does issue are only ever waited on more strictly as a result.
 
-constexpr int kRing = 4;            // LDS slots per wave: 1 being computed + 3 in flight
-constexpr int kAhead = kRing - 1;
+constexpr int kRing = 4;            // LDS slots per wave (a power of two)
+constexpr int kAhead = kRing - 1;   // pages in flight while one is computed
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -388,12 +353,14 @@ template <int N>
 __device__ __forceinline__ void wait_pages() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * N) : "memory");
 }
-__device__ __forceinline__ void wait_pages_rt(int n) {  // n in [0, kAhead]
-  switch (n) {
-    case 0: wait_pages<0>(); break;
-    case 1: wait_pages<1>(); break;
-    case 2: wait_pages<2>(); break;
-    default: wait_pages<3>(); break;
+// Runtime count n in [0, N]: waits for the largest template count not above n.
+template <int N>
+__device__ __forceinline__ void wait_pages_rt(int n) {
+  if constexpr (N == 0) {
+    wait_pages<0>();
+  } else {
+    if (n >= N) wait_pages<N>();
+    else wait_pages_rt<N - 1>(n);
   }
 }
 
@@ -423,46 +390,61 @@ __device__ __forceinline__ PageRegs read_slot(uint32_t slot, int lane, int t) {
 template <int NCB>
 struct SplitState {
   v4f acc[NCB][8];     // P.V accumulators
-  float mref[NCB];     // reference max (log2 units) of this lane's head; p = 2^(z - mref)
-  float mtrue[NCB];    // exact running max of this lane's head
+  float mref[NCB];     // reference (log2 units) of this lane's head; p = 2^(z - mref)
+  float mlane[NCB];    // running max of this lane's unscaled logits
   float lsum[NCB];     // sum of p over this lane's token positions
-  float zsum[NCB][4];  // sum of p * (zero_v - 4 * scale_v) per group
+  float zp[NCB][4];    // sum of p * zero_v per group
+  v4f wsum[NCB];       // sum of the bf16 weights W = p * scale_v per group (rows 4r + g)
 };
 
 template <int NCB>
 struct QOperands {
   v4i hi[NCB][2], lo[NCB][2];   // A operands (masked q' pieces), channel halves m = 0, 1
-  float qs[NCB][4];             // (sum of q' over group g) * 254 / qsc for this lane's head
+  float qs[NCB][4];             // sum over group g of the encoded q' (254*hi + lo), this lane's head
   float cscale[NCB];            // qsc / 254 * sm_scale * log2(e), > 0
 };
 
-// Per-wave LDS tile for the W transpose: [cb][hi/lo][row (j,g)][token] bf16.
+// Per-wave LDS tile for the W transpose: [cb][hi/lo][row (j,g)][token] bf16.  Rows are padded
+// to 20 entries (40 bytes): the 16-lane groups of one write land on distinct banks and every
+// 4-token A operand read stays 8-byte aligned.
+constexpr int kTileRow = kPage + 4;
 template <int NCB>
 struct WTile {
-  uint16_t w[NCB][2][16][kPage];
+  uint16_t w[NCB][2][16][kTileRow];
 };
 
-// A split keeps the first live page's max as its reference: later logits may exceed it, and
+// A run keeps the first page's max as its reference: later logits may exceed it, and
 // p = 2^(z - mref) > 1 is fine in fp32/bf16 as long as z - mref stays below this margin.
-// Beyond it the split is recomputed once with its exact max (never in the loop: no rescale).
+// Beyond it the run is recomputed once with its exact max (never in the loop: no rescale).
 constexpr float kRefMargin = 64.0f;
 
-// One page.  `live` says whether this lane's token is an INT2 position of a valid page; a dead
-// token's slot may hold stale bytes, so its logit is replaced by -inf and its V scale/zero by 0
-// (selects, never arithmetic on the stale values), which makes all its contributions exactly 0.
-template <int NCB>
+// V code words -> B operands.  Column blocks nb = 2q and 2q + 1 (the two halves of group q)
+// come from one shifted copy of each code word: block 2q's codes sit at bits 3-4 (and 19-20),
+// read as bf16 1 + code/16, block 2q + 1's at bits 5-6 (and 21-22), read as 1 + code/4.
+constexpr float kVScale[2] = {16.0f, 4.0f};  // code = scale * (bf16 value - 1), even / odd nb
+
+// One page.  MASKED: tokens outside [lo, hi) (sink or window positions, or past the end) may
+// hold stale bytes, so their logits are replaced by -inf and their V scale/zero by 0 (selects,
+// never arithmetic on the stale values), which makes all their contributions exactly 0.
+// FIRST: the page sets the run's reference max (unless a fixed reference is given).
+template <int NCB, bool MASKED, bool FIRST>
 __device__ __forceinline__ void int2_page(const PageRegs& d, bool live, const QOperands<NCB>& qo,
                                           SplitState<NCB>& st, WTile<NCB>& tile, int t, int r,
-                                          uint32_t vmask, uint32_t magic, bool fixed_ref) {
+                                          uint32_t mask_e, uint32_t mask_o, uint32_t magic,
+                                          v4s ones, bool fixed_ref) {
   const v4i ka0 = (v4i){(int)(d.kc.x & 0x03030303u), (int)((d.kc.x >> 2) & 0x03030303u),
                         (int)((d.kc.x >> 4) & 0x03030303u), (int)((d.kc.x >> 6) & 0x03030303u)};
   const v4i ka1 = (v4i){(int)(d.kc.y & 0x03030303u), (int)((d.kc.y >> 2) & 0x03030303u),
                         (int)((d.kc.y >> 4) & 0x03030303u), (int)((d.kc.y >> 6) & 0x03030303u)};
   const uint32_t kmw[4] = {d.km.x, d.km.y, d.km.z, d.km.w};
-  const uint32_t vmw[4] = {live ? d.vm.x : 0u, live ? d.vm.y : 0u, live ? d.vm.z : 0u,
-                           live ? d.vm.w : 0u};
+  uint32_t vmw[4] = {d.vm.x, d.vm.y, d.vm.z, d.vm.w};
+  if (MASKED) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vmw[g] = live ? vmw[g] : 0u;
+  }
 
-  float lg[NCB];
+  // logits in units of cscale: sum_g s_g * (q'.codes)_g + z_g * (sum of q' over g)
+  float a[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
@@ -470,49 +452,48 @@ __device__ __forceinline__ void int2_page(const PageRegs& d, bool live, const QO
     dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[cb][1], ka1, dh, 0, 0, 0);
     dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[cb][0], ka0, dl, 0, 0, 0);
     dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[cb][1], ka1, dl, 0, 0, 0);
-    float a = 0.f;
+    float x = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dint = __mul24(dh[g], 254) + dl[g];
-      a = fmaf(f16lo(kmw[g]), (float)dint, a);
-      a = fmaf(f16hi(kmw[g]), qo.qs[cb][g], a);
+      x = fmaf(f16lo(kmw[g]), (float)dint, x);
+      x = fmaf(f16hi(kmw[g]), qo.qs[cb][g], x);
     }
-    lg[cb] = live ? a * qo.cscale[cb] : -INFINITY;
-    // reference / exact max of the head (one 16-lane row); no accumulator is ever rescaled
-    const float pm = row_max16(lg[cb]);
-    st.mtrue[cb] = fmaxf(st.mtrue[cb], pm);
-    if (!fixed_ref && st.mref[cb] == kNegBig) st.mref[cb] = fmaxf(pm, kNegBig);
+    if (MASKED) x = live ? x : -INFINITY;
+    a[cb] = x;
+    st.mlane[cb] = fmaxf(st.mlane[cb], x);
+    if (FIRST && !fixed_ref) st.mref[cb] = fmaxf(row_max16(x) * qo.cscale[cb], kNegBig);
   }
 
-  // V codes -> bf16 (1 + code/4); pair nb of dword x holds codes at bits 2nb and 16 + 2nb.
   v4s vb[8];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const uint32_t y0 = nb <= 2 ? (d.vc.x << (5 - 2 * nb)) : (d.vc.x >> (2 * nb - 5));
-    const uint32_t y1 = nb <= 2 ? (d.vc.y << (5 - 2 * nb)) : (d.vc.y >> (2 * nb - 5));
-    vb[nb] = __builtin_bit_cast(v4s, make_uint2(and_or(y0, vmask, magic), and_or(y1, vmask, magic)));
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t y0 = q == 0 ? (d.vc.x << 3) : (d.vc.x >> (4 * q - 3));
+    const uint32_t y1 = q == 0 ? (d.vc.y << 3) : (d.vc.y >> (4 * q - 3));
+    vb[2 * q] = __builtin_bit_cast(v4s, make_uint2(and_or(y0, mask_e, magic), and_or(y1, mask_e, magic)));
+    vb[2 * q + 1] = __builtin_bit_cast(v4s, make_uint2(and_or(y0, mask_o, magic), and_or(y1, mask_o, magic)));
   }
 
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    // p = 0 for masked tokens and until the split has a reference (exp2(-inf) = 0)
-    const float p = __builtin_amdgcn_exp2f(lg[cb] - st.mref[cb]);
+    // p = 0 for masked tokens (exp2(-inf) = 0)
+    const float p = __builtin_amdgcn_exp2f(fmaf(a[cb], qo.cscale[cb], -st.mref[cb]));
     st.lsum[cb] += p;
-    float w[4];
+    float w[4], lo[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float sv = f16lo(vmw[g]), zv = f16hi(vmw[g]);
-      st.zsum[cb][g] = fmaf(p, fmaf(-4.0f, sv, zv), st.zsum[cb][g]);
-      w[g] = fmaf(p, sv, 0.0f);
+      w[g] = fmaf(p, sv, 0.0f);  // one v_fma_mix_f32 from the fp16 scale
+      st.zp[cb][g] = fmaf(p, zv, st.zp[cb][g]);
+      // w ~= hi + lo: hi = w truncated to bf16, lo = bf16(w - hi) rounded to nearest even;
+      // relative error <= 2^-17, unbiased
+      lo[g] = w[g] - __uint_as_float(__float_as_uint(w[g]) & 0xFFFF0000u);
     }
-    uint32_t h01, h23, l01, l23;
-    split_bf16(w, h01, h23, l01, l23);
+    const uint32_t l01 = pack_bf16(lo[0], lo[1]), l23 = pack_bf16(lo[2], lo[3]);
     // transpose: this lane's (head r, token t, groups 0..3) -> rows 4r + g, column t
     const int row = 4 * r;
-    tile.w[cb][0][row + 0][t] = (uint16_t)h01;
-    tile.w[cb][0][row + 1][t] = (uint16_t)(h01 >> 16);
-    tile.w[cb][0][row + 2][t] = (uint16_t)h23;
-    tile.w[cb][0][row + 3][t] = (uint16_t)(h23 >> 16);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) tile.w[cb][0][row + g][t] = (uint16_t)(__float_as_uint(w[g]) >> 16);
     tile.w[cb][1][row + 0][t] = (uint16_t)l01;
     tile.w[cb][1][row + 1][t] = (uint16_t)(l01 >> 16);
     tile.w[cb][1][row + 2][t] = (uint16_t)l23;
@@ -525,145 +506,403 @@ __device__ __forceinline__ void int2_page(const PageRegs& d, bool live, const QO
       st.acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nb], st.acc[cb][nb], 0, 0, 0);
       st.acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nb], st.acc[cb][nb], 0, 0, 0);
     }
+    // the same weights against a column of ones: the exact bf16 weight sums that the code
+    // accumulators carry in their "1 +" part
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, ones, st.wsum[cb], 0, 0, 0);
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, ones, st.wsum[cb], 0, 0, 0);
+  }
+}
+
+// Worker waves per workgroup: each wave is an independent worker with its own LDS ring and
+// tile; two per workgroup lets a CU hold more than 16 workers.
+constexpr int kWaves = 2;
+
+// Shared memory of one workgroup of int2_decode_kernel: the page rings and W tiles of its
+// INT2 workers, or the scratch of the BF16 window role.
+template <int NCB>
+constexpr size_t kSmemBytes = (size_t)kWaves * kRing * kRecord + (size_t)kWaves * sizeof(WTile<NCB>);
+
+// BF16 sink + window positions of one (sequence, KV head), computed by the kWaves waves of one
+// workgroup: logits on the bf16 MFMA (q' as a hi/lo bf16 pair, K rows exact), softmax in fp32,
+// P.V on the VALU with one channel pair per lane.  Written as the pair's last partial slot.
+template <int NCB>
+__device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* __restrict__ sinkwin,
+                                            const int32_t* __restrict__ slot_ids, int hq,
+                                            const int32_t* __restrict__ seq_lens, float sm_log2,
+                                            const Workspace& ws, int b, int h, uint8_t* smem) {
+  constexpr int kJ = 4 * NCB;  // head rows kept (G <= kJ)
+  static_assert((kMaxSinkWindow * kJ + 2 * kJ + kJ * kHeadDim) * sizeof(float) <= kSmemBytes<NCB>,
+                "window scratch exceeds the workgroup's shared memory");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = hq / g.hkv;
+  const int L = max(seq_lens[b], 0);
+  const int slot = slot_ids ? slot_ids[b] : b;
+  const int n_sink = min(L, g.num_sink);
+  const int n_win = min(g.window, L - n_sink);
+  const bool live = sinkwin != nullptr && slot >= 0 && slot < g.num_slots && n_sink + n_win > 0;
+  const int n = live ? n_sink + n_win : 0;
+  float* s_p = reinterpret_cast<float*>(smem);   // [kMaxSinkWindow][kJ] logits, then p
+  float* s_red = s_p + kMaxSinkWindow * kJ;      // [kJ] max, then [kJ] sum
+  float* s_o = s_red + 2 * kJ;                   // [kJ][128] P.V of the second wave
+  const size_t base = ((size_t)slot * g.hkv + h) * (size_t)(g.num_sink + g.window);
+  auto row_ptr = [&](int i) -> const uint16_t* {  // K row of window index i; the V row follows
+    const int p = i < n_sink ? i : L - n_win + (i - n_sink);
+    const int row = p < g.num_sink ? p : g.num_sink + p % g.window;
+    return sinkwin + (base + row) * 2 * kHeadDim;
+  };
+
+  // Logits: S[j][token] = q'[j] . K[token], 16 tokens per tile.  A row m = lane % 16 is head m
+  // (0 beyond G) holding channels 32*kq + 4*s .. +3 at step s (kq = lane / 16); the B column of
+  // the same lane is token m of the tile with the same channels, read straight from its row.
+  const int m = lane & 15, kq = lane >> 4;
+  v4s qhi[8], qlo[8];
+  {
+    const float* qrow = reinterpret_cast<const float*>(ws.qblock(b, hq, h * G + (m < G ? m : 0)));
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float4 v = *reinterpret_cast<const float4*>(qrow + 32 * kq + 4 * s);
+      if (m >= G) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t h01, h23, l01, l23;
+      split_bf16(w, h01, h23, l01, l23);
+      qhi[s] = __builtin_bit_cast(v4s, make_uint2(h01, h23));
+      qlo[s] = __builtin_bit_cast(v4s, make_uint2(l01, l23));
+    }
+  }
+  const int ntiles = (n + kPage - 1) / kPage;
+  for (int tl = wave; tl < ntiles; tl += kWaves) {
+    const int i = tl * kPage + m;
+    uint4 kr[4] = {};
+    if (i < n) {
+      const uint4* kp = reinterpret_cast<const uint4*>(row_ptr(i) + 32 * kq);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kr[u] = kp[u];
+    }
+    v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint4& u = kr[s >> 1];
+      const v4s kb = __builtin_bit_cast(v4s, (s & 1) ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y));
+      d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qhi[s], kb, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qlo[s], kb, d, 0, 0, 0);
+    }
+    // D: this lane holds token i (column lane % 16) for heads 4*kq + e
+    if (i < n) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * kq + e < kJ) s_p[i * kJ + 4 * kq + e] = d[e] * sm_log2;
+    }
+  }
+  __syncthreads();
+
+  // Softmax per head over the n tokens: 16 threads per head.
+  if (tid < kJ * 16) {
+    const int j = tid >> 4, q = tid & 15;
+    float mx = -INFINITY;
+    for (int i = q; i < n; i += 16) mx = fmaxf(mx, s_p[i * kJ + j]);
+    for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.f;
+    for (int i = q; i < n; i += 16) {
+      const float p = __builtin_amdgcn_exp2f(s_p[i * kJ + j] - mx);
+      s_p[i * kJ + j] = p;
+      sum += p;
+    }
+    for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if (q == 0) {
+      s_red[j] = mx;
+      s_red[kJ + j] = sum;
+    }
+  }
+  __syncthreads();
+
+  // P.V: lane -> channels 2*lane, 2*lane + 1; wave w takes tokens w, w + kWaves, ...
+  float acc[kJ][2];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) acc[j][0] = acc[j][1] = 0.f;
+  constexpr int kBatch = 8;
+  for (int i0 = wave; i0 < n; i0 += kWaves * kBatch) {
+    uint32_t vv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + kWaves * u;
+      vv[u] = i < n ? reinterpret_cast<const uint32_t*>(row_ptr(i) + kHeadDim)[lane] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + kWaves * u;
+      if (i < n) {
+        const float v0 = __uint_as_float(vv[u] << 16), v1 = __uint_as_float(vv[u] & 0xFFFF0000u);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const float p = s_p[i * kJ + j];
+          acc[j][0] = fmaf(p, v0, acc[j][0]);
+          acc[j][1] = fmaf(p, v1, acc[j][1]);
+        }
+      }
+    }
+  }
+  if (wave == 1) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      s_o[j * kHeadDim + 2 * lane] = acc[j][0];
+      s_o[j * kHeadDim + 2 * lane + 1] = acc[j][1];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int out_slot = ws.nslots - 1;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (j < G) {
+        float* o = ws.o(b, hq, h * G + j, out_slot);
+        o[2 * lane] = acc[j][0] + s_o[j * kHeadDim + 2 * lane];
+        o[2 * lane + 1] = acc[j][1] + s_o[j * kHeadDim + 2 * lane + 1];
+      }
+    if (lane < G)
+      *ws.ml(b, hq, h * G + lane, out_slot) =
+          n > 0 ? make_float2(s_red[lane], s_red[kJ + lane]) : make_float2(kNegBig, 0.f);
   }
 }
 
 // NCB = number of 16-row blocks of (query head, group) pairs = ceil(G / 4).
-// grid (max_splits, Hkv, batch), block 64: one wavefront per (split, KV head, sequence).
+// Workgroups [0, worker_groups) are INT2 workers, kWaves per workgroup.  Persistent part:
+// worker w (one wavefront) takes run w of C pages of the concatenation of all (sequence, KV
+// head) pairs' INT2 pages (the plan in the workspace, built by prep_q_kernel), and writes one
+// partial for each pair its run touches, into that pair's slot w - (first run of the pair).
+// Every worker therefore streams about the same number of pages.  The workgroups after them
+// compute the BF16 sink + window partial of one pair each; they are dispatched last and so
+// mostly run in the tail of the INT2 workers.
 template <int NCB>
-__global__ __launch_bounds__(64) void int2_decode_kernel(
-    CacheGeom g, const uint8_t* __restrict__ pages, const int32_t* __restrict__ block_table,
-    int hq, const int32_t* __restrict__ seq_lens, float sm_scale, int split_pages, Workspace ws) {
-  const int lane = threadIdx.x;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int max_splits = ws.nslots - 1;
-  const int G = hq / g.hkv;
-  const int L = max(seq_lens[b], 0);
-  const float sm_log2 = sm_scale * kLog2e;
+__global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
+    CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ plan, float sm_scale,
+    int worker_groups, Workspace ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes<NCB>];
+  if ((int)blockIdx.x >= worker_groups) {
+    const int pair = blockIdx.x - worker_groups;
+    window_pair<NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
+                     pair % g.hkv, smem);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
+  const int worker = blockIdx.x * kWaves + wave;
   const int t = lane & 15, r = lane >> 4;
-  __shared__ WTile<NCB> tile;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kRecord];
-  const uint32_t ring0 = lds_offset(&ring[0][0]);
+  WTile<NCB>& tile = *reinterpret_cast<WTile<NCB>*>(smem + (size_t)kWaves * kRing * kRecord +
+                                                    wave * sizeof(WTile<NCB>));
+  const uint32_t ring0 = lds_offset(smem + (size_t)wave * kRing * kRecord);
 
-  // INT2 positions [lo, hi) and this split's logical pages [pg0, pg1).
-  const int n_sink = min(L, g.num_sink);
-  const int n_win = min(g.window, L - n_sink);
-  const int lo = n_sink, hi = L - n_win;
-  int pg0 = split * split_pages;
-  int pg1 = (split == max_splits - 1) ? 0x7fffffff : pg0 + split_pages;
-  pg0 = max(pg0, lo / kPage);
-  pg1 = min(min(pg1, (hi + kPage - 1) / kPage), g.max_pages);
-  if (hi <= lo || g.num_pages < 1) pg1 = pg0;
-
-  QOperands<NCB> qo;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    // A-operand row of this lane: head 4*cb + t/4, group t%4
-    const int ja = 4 * cb + (t >> 2), ga = t & 3;
-    const char* blka = ws.qblock(b, hq, h * G + (ja < G ? ja : 0));
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int dw = 4 * m + r;  // 16-channel word of this lane's K quarter
-      const bool use = ja < G && (dw >> 1) == ga;
-      const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * dw);
-      const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * dw);
-      const v4i zero = {0, 0, 0, 0};
-      qo.hi[cb][m] = use ? zh : zero;
-      qo.lo[cb][m] = use ? zl : zero;
+  const int total = plan[0], C = plan[1];
+  if ((long long)worker * C >= total) return;
+  // Equal-work waves on one SIMD would otherwise finish in dispatch order (the issue arbiter
+  // prefers older waves) and leave the SIMD short of waves at the end; a wave lowers its
+  // priority as it passes each quarter of its run, which lets the younger ones catch up.
+  __builtin_amdgcn_s_setprio(3);
+  const int band_len = max(C / 4, 1);
+  int band_left = band_len, band = 0;
+  const int run0 = worker * C;
+  const int run1 = (int)min((long long)total, (long long)run0 + C);
+  const int B = ws.batch;
+  const int max_splits = ws.nslots - 1;
+  const int32_t* pstart = plan + kPlanHeader;
+  const int32_t* npg = pstart + B;
+  const int32_t* pglo = npg + B;
+  // sequence of the run's first page: the last b with pstart[b] <= run0 (it has pages)
+  int b = 0;
+  {
+    int hi_b = B;
+    while (hi_b - b > 1) {
+      const int mid = (b + hi_b) >> 1;
+      if (pstart[mid] <= run0) b = mid; else hi_b = mid;
     }
-    // D rows of this lane: head 4*cb + r
-    const int jd = 4 * cb + r;
-    const char* blkd = ws.qblock(b, hq, h * G + (jd < G ? jd : 0));
-    const float qsc = jd < G ? *reinterpret_cast<const float*>(blkd + kQScOff) : 0.f;
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg)
-      qo.qs[cb][gg] = qsc > 0.f ? reinterpret_cast<const float*>(blkd + kQSumOff)[gg] * 254.0f / qsc : 0.f;
-    // strictly positive so that a masked -inf logit never becomes 0 * inf
-    qo.cscale[cb] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
   }
+  const int G = hq / g.hkv;
+  const float sm_log2 = sm_scale * kLog2e;
+  const size_t rec_stride = (size_t)g.hkv * kRecord;  // bytes between pages of one head
 
-  // Opaque copies of the two V-code constants: mask in an SGPR, magic in a VGPR, so every
+  // Opaque copies of the V-code constants: masks in SGPRs, magic in a VGPR, so every
   // (x & mask) | magic is one instruction.  The empty asm statements emit nothing.
-  uint32_t vmask = 0x00600060u, magic = 0x3F803F80u;
-  asm volatile("" : "+s"(vmask));
+  uint32_t mask_e = 0x00180018u, mask_o = 0x00600060u, magic = 0x3F803F80u;
+  asm volatile("" : "+s"(mask_e));
+  asm volatile("" : "+s"(mask_o));
   asm volatile("" : "+v"(magic));
+  const v4s ones = __builtin_bit_cast(v4s, make_uint2(0x3F803F80u, 0x3F803F80u));  // bf16 1.0
 
-  const int32_t* bt = block_table + (size_t)b * g.max_pages;
-  const uint8_t* pages_h = pages + (size_t)h * kRecord;      // record of (page 0, head h)
-  const size_t rec_stride = (size_t)g.hkv * kRecord;         // bytes between pages
-  SplitState<NCB> st;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    st.mref[cb] = kNegBig;
-    st.mtrue[cb] = kNegBig;
-  }
-#pragma nounroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool fixed_ref = pass > 0;
+  int pos = run0;
+  while (true) {
+    const int P = npg[b];
+    const int rel = pos - pstart[b];
+    const int h = rel / P;
+    const int pair0 = pstart[b] + h * P;
+    const int seg_end = min(run1, pair0 + P);
+    const int slot = worker - pair0 / C;
+    const int pgA = pglo[b] + (pos - pair0), pgB = pgA + (seg_end - pos);
+
+    const int L = max(seq_lens[b], 0);
+    const int n_sink = min(L, g.num_sink);
+    const int lo = n_sink, hi = L - min(g.window, L - n_sink);
+
+    QOperands<NCB> qo;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
+      // A-operand row of this lane: head 4*cb + t/4, group t%4
+      const int ja = 4 * cb + (t >> 2), ga = t & 3;
+      const char* blka = ws.qblock(b, hq, h * G + (ja < G ? ja : 0));
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) st.acc[cb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
-      st.lsum[cb] = 0.f;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) st.zsum[cb][gg] = 0.f;
-    }
-
-    // Page ids come from uniform (scalar) loads, fetched one iteration before they are used;
-    // scalar loads are counted by lgkmcnt, so waiting for one never drains the page ring.
-    auto load_id = [&](int pg) -> int { return pg < pg1 ? bt[pg] : -1; };
-    // Every page in [pg0, pg1) issues exactly one record copy (a skipped page copies page 0 of
-    // the pool and is masked), so the per-page wait counts are exact.
-    uint32_t live_bits = 0;  // bit (pg % 32): page id valid
-    auto issue = [&](int pg, int page) {
-      const bool ok = page >= 0 && page < g.num_pages;
-      const uint8_t* rec = pages_h + (size_t)(ok ? page : 0) * rec_stride;
-      dma_record(rec, ring0 + (uint32_t)(pg & (kRing - 1)) * kRecord, lane);
-      live_bits = ok ? (live_bits | (1u << (pg & 31))) : (live_bits & ~(1u << (pg & 31)));
-    };
-
-    for (int k = 0; k < kAhead; ++k)
-      if (pg0 + k < pg1) issue(pg0 + k, load_id(pg0 + k));
-    int id_next = load_id(pg0 + kAhead);
-    for (int pg = pg0; pg < pg1; ++pg) {
-      if (pg + kAhead < pg1) {
-        issue(pg + kAhead, id_next);
-        id_next = load_id(pg + kAhead + 1);
-        wait_pages<kAhead>();
-      } else {
-        wait_pages_rt(pg1 - 1 - pg);
+      for (int m = 0; m < 2; ++m) {
+        const int dw = 4 * m + r;  // 16-channel word of this lane's K quarter
+        const bool use = ja < G && (dw >> 1) == ga;
+        const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * dw);
+        const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * dw);
+        const v4i zero = {0, 0, 0, 0};
+        qo.hi[cb][m] = use ? zh : zero;
+        qo.lo[cb][m] = use ? zl : zero;
       }
-      const PageRegs d = read_slot(ring0 + (uint32_t)(pg & (kRing - 1)) * kRecord, lane, t);
-      const int pos = pg * kPage + t;
-      const bool live = ((live_bits >> (pg & 31)) & 1u) && pos >= lo && pos < hi;
-      int2_page<NCB>(d, live, qo, st, tile, t, r, vmask, magic, fixed_ref);
+      // D rows of this lane: head 4*cb + r
+      const int jd = 4 * cb + r;
+      const char* blkd = ws.qblock(b, hq, h * G + (jd < G ? jd : 0));
+      const float qsc = jd < G ? *reinterpret_cast<const float*>(blkd + kQScOff) : 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        qo.qs[cb][gg] = jd < G ? reinterpret_cast<const float*>(blkd + kQSumOff)[gg] : 0.f;
+      // strictly positive so that a masked -inf logit never becomes 0 * inf
+      qo.cscale[cb] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
     }
 
-    // A logit beyond the reference margin: recompute once with the exact max (rare path).
-    bool redo = false;
+    const int32_t* bt = block_table + (size_t)b * g.max_pages;
+    const uint8_t* pages_h = pages + (size_t)h * kRecord;  // record of (page 0, head h)
+    SplitState<NCB> st;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) redo |= st.mtrue[cb] > st.mref[cb] + kRefMargin;
-    if (pass > 0 || !__any(redo)) break;
+    for (int cb = 0; cb < NCB; ++cb) st.mref[cb] = kNegBig;
+#pragma nounroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool fixed_ref = pass > 0;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) st.mref[cb] = st.mtrue[cb];
-  }
+      for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) st.acc[cb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+        st.lsum[cb] = 0.f;
+        st.mlane[cb] = -INFINITY;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) st.zp[cb][gg] = 0.f;
+        st.wsum[cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+      }
 
-  // Finish: l and the zero-point terms reduced over the row's 16 tokens; the accumulator row
-  // of a lane (head 4*cb + r) matches its own row, so no exchange is needed.
+      // Page ids come from uniform (scalar) loads, fetched one page before they are used;
+      // scalar loads are counted by lgkmcnt, so waiting for one never drains the page ring.
+      // Each page issues exactly one record copy, so the per-page wait counts are exact.  An
+      // id outside the pool reads page 0 instead (memory safety; the caller's table is wrong).
+      auto load_id = [&](int pg) -> int { return pg < pgB ? bt[pg] : 0; };
+      auto issue = [&](int pg, int page) {
+        const bool ok = page >= 0 && page < g.num_pages;
+        dma_record(pages_h + (size_t)(ok ? page : 0) * rec_stride,
+                   ring0 + (uint32_t)(pg & (kRing - 1)) * kRecord, lane);
+      };
+      for (int k = 0; k < kAhead; ++k)
+        if (pgA + k < pgB) issue(pgA + k, load_id(pgA + k));
+      int id_next = load_id(pgA + kAhead);
+      auto fetch = [&](int pg) -> PageRegs {
+        if (--band_left == 0) {
+          band_left = band_len;
+          ++band;
+          if (band == 1) __builtin_amdgcn_s_setprio(2);
+          else if (band == 2) __builtin_amdgcn_s_setprio(1);
+          else if (band == 3) __builtin_amdgcn_s_setprio(0);
+        }
+        if (pg + kAhead < pgB) {
+          issue(pg + kAhead, id_next);
+          id_next = load_id(pg + kAhead + 1);
+          wait_pages<kAhead>();
+        } else {
+          wait_pages_rt<kAhead>(pgB - 1 - pg);
+        }
+        return read_slot(ring0 + (uint32_t)(pg & (kRing - 1)) * kRecord, lane, t);
+      };
+      auto live_at = [&](int pg) { const int p = pg * kPage + t; return p >= lo && p < hi; };
+
+      // first page (it may hold sink positions), interior pages (all INT2), last page (it may
+      // hold window positions or the end of the sequence)
+      {
+        const PageRegs d = fetch(pgA);
+        int2_page<NCB, true, true>(d, live_at(pgA), qo, st, tile, t, r, mask_e, mask_o, magic, ones,
+                                   fixed_ref);
+      }
+      for (int pg = pgA + 1; pg < pgB - 1; ++pg) {
+        const PageRegs d = fetch(pg);
+        int2_page<NCB, false, false>(d, true, qo, st, tile, t, r, mask_e, mask_o, magic, ones,
+                                     fixed_ref);
+      }
+      if (pgB - 1 > pgA) {
+        const PageRegs d = fetch(pgB - 1);
+        int2_page<NCB, true, false>(d, live_at(pgB - 1), qo, st, tile, t, r, mask_e, mask_o, magic,
+                                    ones, fixed_ref);
+      }
+
+      // A logit beyond the reference margin: recompute once with the exact max (rare path).
+      bool redo = false;
+      float mexact[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const float lt = row_sum16(st.lsum[cb]);
-    float zt[4];
+      for (int cb = 0; cb < NCB; ++cb) {
+        mexact[cb] = row_max16(st.mlane[cb]) * qo.cscale[cb];
+        redo |= mexact[cb] > st.mref[cb] + kRefMargin;
+      }
+      if (pass > 0 || !__any(redo)) break;
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) zt[gg] = row_sum16(st.zsum[cb][gg]);
-    const int j = 4 * cb + r;
-    if (j < G) {
-      float* o = ws.o(b, hq, h * G + j, split);
+      for (int cb = 0; cb < NCB; ++cb) st.mref[cb] = mexact[cb];
+    }
+
+    // Finish: l and the per-group sums reduced over the row's 16 tokens; the accumulator row
+    // of a lane (head 4*cb + r) matches its own row, so no exchange is needed.
+    //   o'[c] = sum_t p_t (s_t code_t(c) + z_t) = f (acc - sum_t W_t) + sum_t p_t z_t
+    // with f = 16 or 4 for the block's code scale and W_t the bf16 weight pair.
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[16 * nb + t] = 4.0f * st.acc[cb][nb][nb >> 1] + zt[nb >> 1];
-      if (t == 0) *ws.ml(b, hq, h * G + j, split) = make_float2(st.mref[cb], lt);
+    for (int cb = 0; cb < NCB; ++cb) {
+      const float lt = row_sum16(st.lsum[cb]);
+      float zt[4], wt[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        zt[gg] = row_sum16(st.zp[cb][gg]);
+        wt[gg] = st.wsum[cb][gg];
+      }
+      const int j = 4 * cb + r;
+      if (j < G && (unsigned)slot < (unsigned)max_splits) {
+        float* o = ws.o(b, hq, h * G + j, slot);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int gg = nb >> 1;
+          o[16 * nb + t] = fmaf(kVScale[nb & 1], st.acc[cb][nb][gg] - wt[gg], zt[gg]);
+        }
+        if (t == 0) *ws.ml(b, hq, h * G + j, slot) = make_float2(st.mref[cb], lt);
+      }
+    }
+
+    pos = seg_end;
+    if (pos >= run1) break;
+    if (h == g.hkv - 1) {
+      do { ++b; } while (b < B - 1 && npg[b] == 0);
     }
   }
+}
+
+// Resident worker waves of int2_decode_kernel<NCB> on the current device (cached per device).
+template <int NCB>
+int resident_workers() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)int2_decode_kernel<NCB>,
+                                                   64 * kWaves, 0) != hipSuccess)
+    per_cu = 0;
+  n = max(cus, 1) * max(per_cu, 1) * kWaves;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace
@@ -671,21 +910,25 @@ __global__ __launch_bounds__(64) void int2_decode_kernel(
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
-                         float sm_scale, int split_pages, const Workspace& ws,
+                         float sm_scale, int num_workers, const Workspace& ws,
                          hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  // dynamic LDS: the window rows of one (sequence, KV head)
-  const size_t win_lds = (size_t)(g.num_sink + g.window) * kHeadDim * sizeof(uint16_t);
-  hipLaunchKernelGGL(prep_window_kernel, dim3(g.hkv, batch), dim3(kPrepThreads), win_lds, stream,
-                     g, q, rot_k, sinkwin, slot_ids, hq, seq_lens, sm_scale, ws);
   const int G = hq / g.hkv;
-  dim3 grid(ws.nslots - 1, g.hkv, batch);
+  const int workers = num_workers > 0 ? num_workers
+                                      : (G <= 4 ? resident_workers<1>() : resident_workers<2>());
+  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv, batch + 1), dim3(kPrepThreads), 0, stream, g, q,
+                     rot_k, hq, seq_lens, workers, ws);
+  const int worker_groups = (workers + kWaves - 1) / kWaves;
+  const dim3 grid(worker_groups + batch * g.hkv);
+  const int32_t* plan = ws.plan();
   if (G <= 4)
-    hipLaunchKernelGGL(int2_decode_kernel<1>, grid, dim3(64), 0, stream, g, pages, block_table,
-                       hq, seq_lens, sm_scale, split_pages, ws);
+    hipLaunchKernelGGL(int2_decode_kernel<1>, grid, dim3(64 * kWaves), 0, stream, g, pages,
+                       sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
+                       worker_groups, ws);
   else
-    hipLaunchKernelGGL(int2_decode_kernel<2>, grid, dim3(64), 0, stream, g, pages, block_table,
-                       hq, seq_lens, sm_scale, split_pages, ws);
+    hipLaunchKernelGGL(int2_decode_kernel<2>, grid, dim3(64 * kWaves), 0, stream, g, pages,
+                       sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
+                       worker_groups, ws);
   return hipGetLastError();
 }
 

@@ -22,16 +22,25 @@ constexpr int kMaxSinkWindow = 256;   // S + W
 //     [512, 640) int8  hi[128]           q' ~= qsc * (hi + lo/254), stored in MFMA slot order
 //     [640, 768) int8  lo[128]
 //     [768, 772) float qsc
-//     [772, 788) float qsum[4]           sum of q' over each 32-channel group
+//     [772, 788) float qsum[4]           sum of 254*hi + lo over each 32-channel group (exact)
 //   O region:  float o'[B][Hq][nslots][128]   unnormalised partial outputs (rotated frame)
 //   ML region: float2 (m, l)[B][Hq][nslots]  m in log2 units, l = sum of 2^(z*log2e - m)
+//   Plan region (int32):
+//     [0] total INT2 pages over all (sequence, KV head) pairs, [1] pages per worker run,
+//     [2], [3] unused; then pstart[B] (first run index of sequence b's pairs: pair (b, h) owns
+//     pages pstart[b] + h*npg[b] .. + npg[b] of the concatenation), npg[B] (INT2 pages per
+//     KV head of sequence b), pglo[B] (first logical INT2 page of sequence b), and
+//     nvalid[B][Hkv] (partial slots 0 .. nvalid-1 of the pair hold INT2 partials).
+//   Slot nslots - 1 of every (b, j) holds the BF16 sink/window partial.
 constexpr int kQBlock = 1024;
 constexpr int kQHiOff = 512, kQLoOff = 640, kQScOff = 768, kQSumOff = 772;
+constexpr int kPlanHeader = 4;
 
 struct Workspace {
   char* base;
+  int batch;
   int nslots;  // max_splits + 1 (the last slot holds the BF16 sink/window split)
-  size_t q_bytes, o_bytes, ml_bytes;
+  size_t q_bytes, o_bytes, ml_bytes, plan_bytes;
   __host__ __device__ char* qblock(int b, int hq, int j) const {
     return base + ((size_t)b * hq + j) * kQBlock;
   }
@@ -41,21 +50,31 @@ struct Workspace {
   __host__ __device__ float2* ml(int b, int hq, int j, int s) const {
     return (float2*)(base + q_bytes + o_bytes) + ((size_t)b * hq + j) * nslots + s;
   }
+  __host__ __device__ int32_t* plan() const {
+    return (int32_t*)(base + q_bytes + o_bytes + ml_bytes);
+  }
+  __host__ __device__ int32_t* pstart() const { return plan() + kPlanHeader; }
+  __host__ __device__ int32_t* npg() const { return pstart() + batch; }
+  __host__ __device__ int32_t* pglo() const { return npg() + batch; }
+  __host__ __device__ int32_t* nvalid() const { return pglo() + batch; }
 };
 
+// The plan sizes nvalid for Hq (>= Hkv) pairs per sequence so that its size needs no Hkv.
 inline Workspace make_workspace(void* base, int batch, int hq, int max_splits) {
   Workspace w;
   w.base = (char*)base;
+  w.batch = batch;
   w.nslots = max_splits + 1;
   w.q_bytes = (size_t)batch * hq * kQBlock;
   w.o_bytes = (size_t)batch * hq * w.nslots * kHeadDim * sizeof(float);
   w.ml_bytes = (size_t)batch * hq * w.nslots * sizeof(float2);
+  w.plan_bytes = ((size_t)(kPlanHeader + 3 * batch + batch * hq) * sizeof(int32_t) + 255) & ~(size_t)255;
   return w;
 }
 
 inline size_t workspace_bytes(int batch, int hq, int max_splits) {
   Workspace w = make_workspace(nullptr, batch, hq, max_splits);
-  return w.q_bytes + w.o_bytes + w.ml_bytes;
+  return w.q_bytes + w.o_bytes + w.ml_bytes + w.plan_bytes;
 }
 
 struct CacheGeom {
@@ -73,7 +92,7 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
-                         float sm_scale, int split_pages, const Workspace& ws,
+                         float sm_scale, int num_workers, const Workspace& ws,
                          hipStream_t stream);
 
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,

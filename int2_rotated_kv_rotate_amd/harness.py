@@ -132,15 +132,21 @@ class GpuCache:
         return last_k, last_v
 
 
+# Partial slots per (sequence, KV head): enough that the run length is set by the worker count
+# for the contexts used here (a pair of P pages needs about P / run + 1 slots).
+DEFAULT_MAX_SPLITS = 64
+
+
 class DecodeStep:
     """Buffers and launches of one decode step: append the new token, attend, combine."""
 
-    def __init__(self, cache: GpuCache, split_pages: int = 128, max_splits: Optional[int] = None):
+    def __init__(self, cache: GpuCache, num_workers: int = 0, max_splits: int = DEFAULT_MAX_SPLITS):
+        """num_workers 0: one worker per resident wavefront slot; max_splits bounds the INT2
+        partials per (sequence, KV head) (a small value lengthens the workers' runs)."""
         p = cache.p
         self.cache = cache
-        self.split_pages = split_pages
-        pages_max = int((p.lens.max() + 15) // 16)
-        self.max_splits = max_splits or max(1, (pages_max + split_pages - 1) // split_pages)
+        self.num_workers = num_workers
+        self.max_splits = max_splits
         dev = cache.device
         self.ws = torch.empty(ops.decode_workspace_bytes(p.batch, p.w.num_q_heads, self.max_splits),
                               dtype=torch.uint8, device=dev)
@@ -166,7 +172,7 @@ class DecodeStep:
     def decode_only(self, stream=None):
         c = self.cache
         ops.decode_attention(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.q, self.seq_lens,
-                             c.rot_k, SM_SCALE, self.split_pages, self.max_splits, self.ws, stream)
+                             c.rot_k, SM_SCALE, self.num_workers, self.max_splits, self.ws, stream)
 
     def combine_only(self, stream=None):
         c = self.cache

@@ -135,15 +135,16 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, max_splits: int) -> int
 
 
 def decode_attention(lay: Layout, pages, sinkwin, block_table, slot_ids, q, seq_lens, rot_k,
-                     sm_scale: float, split_pages: int, max_splits: int, workspace,
+                     sm_scale: float, num_workers: int, max_splits: int, workspace,
                      stream=None) -> None:
+    """num_workers: worker wavefronts (0 = one per resident slot of the device)."""
     lib = load_library()
     batch, hq = q.shape[0], q.shape[1]
     _check("oscar_decode_attention", lib.oscar_decode_attention(
         ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
         _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
         batch, hq, _ptr(q, torch.int16, "q"), _ptr(seq_lens, torch.int32, "seq_lens"),
-        _ptr(rot_k, torch.float32, "rot_k"), float(sm_scale), split_pages, max_splits,
+        _ptr(rot_k, torch.float32, "rot_k"), float(sm_scale), num_workers, max_splits,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 

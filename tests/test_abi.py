@@ -40,7 +40,10 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     from int2_rotated_kv_rotate_amd import ops
-    assert ops.decode_workspace_bytes(64, 32, 12) == 64 * 32 * 1024 + 64 * 32 * 13 * (512 + 8)
+    # Q blocks, partial outputs and (m, l) per slot, then the work plan (4 header words,
+    # three words per sequence, one per (sequence, head)) rounded up to 256 bytes
+    plan = (4 * (4 + 3 * 64 + 64 * 32) + 255) // 256 * 256
+    assert ops.decode_workspace_bytes(64, 32, 12) == 64 * 32 * 1024 + 64 * 32 * 13 * (512 + 8) + plan
     assert lib.oscar_decode_workspace_bytes(-1, 32, 12) == 0
     assert lib.oscar_decode_workspace_bytes(1, 32, 0) == 0
 
@@ -85,18 +88,20 @@ def test_append_validation(lib):
 
 def _decode(lib, lay, **kw):
     a = dict(pages=FAKE, sinkwin=FAKE, bt=FAKE, slots=None, batch=1, hq=32, q=FAKE, lens=FAKE,
-             rk=FAKE, sm=0.088, sp=128, ms=4, ws=FAKE, wsb=1 << 30)
+             rk=FAKE, sm=0.088, nw=0, ms=4, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.oscar_decode_attention(
         ctypes.byref(lay), a["pages"], a["sinkwin"], a["bt"], a["slots"], a["batch"], a["hq"],
-        a["q"], a["lens"], a["rk"], a["sm"], a["sp"], a["ms"], a["ws"], a["wsb"], None)
+        a["q"], a["lens"], a["rk"], a["sm"], a["nw"], a["ms"], a["ws"], a["wsb"], None)
 
 
 def test_decode_validation(lib):
     assert _decode(lib, _layout(), hq=30) == 1          # not a multiple of Hkv
     assert _decode(lib, _layout(), hq=24) == 2          # group 3 unsupported
     assert _decode(lib, _layout(), hq=128) == 2         # group 16 unsupported
-    assert _decode(lib, _layout(), sp=0) == 1
+    assert _decode(lib, _layout(), nw=-1) == 1
+    assert _decode(lib, _layout(), nw=(1 << 20) + 1) == 1
+    assert _decode(lib, _layout(max_pages_per_seq=1 << 20), batch=1 << 10) == 2  # plan > int32
     assert _decode(lib, _layout(), ms=0) == 1
     assert _decode(lib, _layout(), sm=float("nan")) == 1
     assert _decode(lib, _layout(), wsb=100) == 3

@@ -5,8 +5,10 @@
   placement, untouched bytes).
 * Decode: out (fp32, rotated back) within 2e-3 normwise per (sequence, query head) row:
   max_c |gpu - oracle| / max_c |oracle|; lse within 2e-3.
-Sizes span several pages and splits, ragged lengths and partial pages; edge cases cover a
-context entirely in BF16, a single token, and a split budget smaller than the context.
+Sizes span several pages and worker runs, ragged lengths and partial pages; worker counts go
+from one worker for the whole batch (runs crossing many (sequence, head) pairs) to more
+workers than pages; edge cases cover a context entirely in BF16, a single token, and a
+partial-slot budget small enough to lengthen the runs.
 """
 import math
 import sys
@@ -42,10 +44,10 @@ def oracle_cache(p: H.Problem):
     return cache
 
 
-def run_gpu(p: H.Problem, split_pages, max_splits=None):
+def run_gpu(p: H.Problem, num_workers=0, max_splits=H.DEFAULT_MAX_SPLITS):
     cache = H.GpuCache(p, fill=SENTINEL)
     last_k, last_v = cache.fill_context()
-    step = H.DecodeStep(cache, split_pages=split_pages, max_splits=max_splits)
+    step = H.DecodeStep(cache, num_workers=num_workers, max_splits=max_splits)
     step.set_new_token(last_k, last_v)
     step.run()
     torch.cuda.synchronize()
@@ -59,27 +61,29 @@ def row_errors(gpu, ref):
 
 
 CASES = {
-    # name: (workload, overrides, split_pages, max_splits)
-    "tiny": (W.WORKLOADS["tiny"], {}, 8, None),
-    "q4b_ragged": (W.WORKLOADS["qwen3_4b"], dict(batch=2, ctx=1500, ctx_min=700), 16, None),
-    "q32b_g8": (W.WORKLOADS["qwen3_32b"], dict(batch=2, ctx=1000), 32, None),
-    "q8b_many_splits": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=5, ctx=900, ctx_min=100), 4, None),
-    "q8b_few_splits": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=1200, ctx_min=600), 4, 3),
-    "all_bf16": (W.WORKLOADS["tiny"], dict(ctx=60), 8, None),
-    "one_token": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=1), 8, None),
-    "just_past_window": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=4 + 128 + 1), 1, None),
-    "page_multiple": (W.WORKLOADS["qwen3_4b"], dict(batch=2, ctx=16 * 20), 3, None),
+    # name: (workload, overrides, num_workers (0 = one per resident slot), max_splits)
+    "tiny": (W.WORKLOADS["tiny"], {}, 0, 64),
+    "q4b_ragged": (W.WORKLOADS["qwen3_4b"], dict(batch=2, ctx=1500, ctx_min=700), 7, 64),
+    "q32b_g8": (W.WORKLOADS["qwen3_32b"], dict(batch=2, ctx=1000), 3, 64),
+    "q8b_more_workers_than_pages": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=5, ctx=900, ctx_min=100), 5000, 64),
+    "q8b_few_slots": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=1200, ctx_min=600), 0, 3),
+    "q8b_one_slot": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=700, ctx_min=300), 0, 1),
+    "all_bf16": (W.WORKLOADS["tiny"], dict(ctx=60), 0, 64),
+    "one_token": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=1), 0, 64),
+    "just_past_window": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=4 + 128 + 1), 1, 64),
+    "page_multiple": (W.WORKLOADS["qwen3_4b"], dict(batch=2, ctx=16 * 20), 5, 64),
+    "one_worker_many_pairs": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=4, ctx=500, ctx_min=140), 1, 64),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_append_and_decode_parity(name):
-    base, over, split_pages, max_splits = CASES[name]
+    base, over, num_workers, max_splits = CASES[name]
     w = W.scaled(base, name=name, **over) if over else base
     p = H.make_problem(w)
     _log(f"[parity] {name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
-         f"lens={p.lens.tolist()} split_pages={split_pages} max_splits={max_splits}")
-    cache, step = run_gpu(p, split_pages, max_splits)
+         f"lens={p.lens.tolist()} num_workers={num_workers} max_splits={max_splits}")
+    cache, step = run_gpu(p, num_workers, max_splits)
     oc = oracle_cache(p)
 
     pages = cache.pages.cpu().numpy()
@@ -101,16 +105,18 @@ def test_append_and_decode_parity(name):
 
 
 def test_split_size_and_permutation_invariance():
-    """Different split sizes agree to 1e-4; a permuted block table gives identical bits.
+    """Different worker counts agree to 1e-4; a permuted block table gives identical bits.
 
-    Split sizes change where the running max restarts and the fp32 accumulation order, so
-    results differ by rounding only.  The P.V accumulator carries the codes as 1 + code/4, a
+    Worker counts change where runs start (and with them the reference max and the fp32
+    accumulation order), so results differ by rounding only.  The P.V accumulator carries the codes as 1 + code/4, a
     bias about 3.7x the signal that is removed after accumulation, and the normwise metric
     divides by max|o|, which is small for diffuse attention: ~1e-5 here, bounded by 1e-4."""
     w = W.scaled(W.WORKLOADS["qwen3_4b"], batch=2, ctx=1300, ctx_min=900, name="inv")
     p = H.make_problem(w)
     _, s1 = run_gpu(p, 4)
     _, s2 = run_gpu(p, 33)
+    _, s0 = run_gpu(p, 0)
+    assert row_errors(s0.out.cpu().numpy(), s2.out.cpu().numpy().astype(np.float64)).max() <= 1e-4
     a, b = s1.out.cpu().numpy(), s2.out.cpu().numpy()
     assert row_errors(a, b.astype(np.float64)).max() <= 1e-4
     # same physical content, different page ids
@@ -140,14 +146,25 @@ def test_distinct_k_and_v_rotations_are_not_conflated():
 
 
 def test_combine_with_synthetic_partials():
-    """oscar_combine on seeded partials (not produced by the library) vs the oracle merge."""
+    """oscar_combine on seeded partials (not produced by the library) vs the oracle merge.
+
+    Each (sequence, KV head) pair declares how many INT2 slots it filled (the plan's nvalid);
+    slots past that hold NaN outputs and large (m, l) and must not be read."""
     B, hq, hkv, max_splits = 3, 8, 2, 5
     nslots = max_splits + 1
+    G = hq // hkv
     valid = np.ones((B, nslots), bool)
     valid[0, 2] = False
     valid[1, 1:] = False
     valid[2, :] = False                      # a row with no positions at all
     m, l, o = W.synthetic_partials(42, B, hq, nslots, valid)
+    nvalid = np.array([[5, 3], [2, 0], [4, 5]], np.int32)       # [B][hkv]
+    for b in range(B):
+        for j in range(hq):
+            stale = np.arange(nvalid[b, j // G], max_splits)
+            o[b, j, stale] = np.nan
+            m[b, j, stale] = 1e30
+            l[b, j, stale] = 7.0
     rot_v = W.rotations(W.scaled(W.WORKLOADS["qwen3_4b"], name="rv"), "v")[:hkv].astype(np.float32)
     nbytes = ops.decode_workspace_bytes(B, hq, max_splits)
     ws = np.zeros(nbytes, np.uint8)
@@ -156,19 +173,22 @@ def test_combine_with_synthetic_partials():
     ws[qb:qb + ob] = o.astype(np.float32).reshape(-1).view(np.uint8)
     ml = np.stack([m, l], axis=-1).astype(np.float32)
     ws[qb + ob:qb + ob + ml.nbytes] = ml.reshape(-1).view(np.uint8)
+    # plan region: 4 header words, pstart/npg/pglo [B] each, then nvalid [B][hkv]
+    nv_off = qb + ob + ml.nbytes + 4 * (4 + 3 * B)
+    ws[nv_off:nv_off + nvalid.nbytes] = nvalid.reshape(-1).view(np.uint8)
     dws = torch.from_numpy(ws).cuda()
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
     ops.combine(B, hq, hkv, max_splits, dws, torch.from_numpy(rot_v).cuda(), out, lse)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    G = hq // hkv
     for b in range(B):
         for j in range(hq):
-            if not valid[b].any():
+            used = list(range(nvalid[b, j // G])) + [nslots - 1]
+            if not valid[b, used].any():
                 assert np.all(out[b, j] == 0) and lse[b, j] == -np.inf
                 continue
-            o_ref, lse_ref = O.merge_partials(m[b, j], l[b, j], o[b, j])
+            o_ref, lse_ref = O.merge_partials(m[b, j, used], l[b, j, used], o[b, j, used])
             o_ref = o_ref @ rot_v[j // G].astype(np.float64).T
             assert np.abs(out[b, j] - o_ref).max() <= 1e-5 * max(1, np.abs(o_ref).max())
             assert abs(lse[b, j] - lse_ref) <= 1e-5 * max(1, abs(lse_ref))
