@@ -34,6 +34,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
@@ -104,7 +105,7 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
     const int n_sink = min(L, g.num_sink);
     const int lo = n_sink, hi = L - min(g.window, L - n_sink);
     first = lo / kPage;
-    if (hi <= lo) return 0;
+    if (hi <= lo || g.num_pages < 1) return 0;
     return max(min((hi + kPage - 1) / kPage, g.max_pages) - first, 0);
   };
   // pass 1: total pages and the largest pair
@@ -309,82 +310,97 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 }
 
 
-// ---- page ring in LDS, filled by direct-to-LDS loads -------------------------------------
+// ---- page-pair ring in LDS, filled by direct-to-LDS loads --------------------------------
 //
-// Each page record (1536 B) is copied into a per-wave LDS slot by two global_load_lds_dwordx4
-// (64 lanes, then 32 lanes, 16 B each), several pages ahead of the page being computed, so that the memory
-// latency is covered without holding the data in VGPRs.  These loads and the reads of a slot
-// are issued as inline assembly with an explicit vmcnt wait per page: the compiler does not
-// track them (it would otherwise wait for every outstanding direct-to-LDS load before any LDS
-// access).  Loads the compiler does issue are only ever waited on more strictly as a result.
+// Pages are processed in pairs.  A pair's two records (1536 B each) are copied into a per-wave
+// LDS pair slot of 3072 B by four global_load_lds_dwordx4 (16 B per lane): record A bytes
+// [0, 1024) to [0, 1024), record B bytes [0, 1024) to [1024, 2048), and the two 512-byte tails
+// to [2048, 2560) (lanes 0..31) and [2560, 3072) (lanes 32..63).  The next pair is in flight
+// while one is computed, so the memory latency is covered without holding data in VGPRs.
+// These loads and the reads of a slot are inline assembly with an explicit vmcnt wait per
+// pair: the compiler does not track them (it would otherwise wait for every outstanding
+// direct-to-LDS load before any LDS access).  Loads the compiler does issue are only ever
+// waited on more strictly as a result.
 
-constexpr int kRing = 4;            // LDS slots per wave (a power of two)
-constexpr int kAhead = kRing - 1;   // pages in flight while one is computed
+constexpr int kPairBytes = 3 * 1024;
+constexpr int kPairSlots = 2;  // the pair being computed + the next one in flight
+constexpr int kRingBytes = kPairSlots * kPairBytes;
+constexpr int kPairHeadB = 1024, kPairTailA = 2048, kPairTailB = 2560;
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Copy the 1536-byte record at `rec` into the LDS slot at byte offset `slot`: lane l moves 16
-// bytes to slot + 16 l (bytes [0, 1024) with all lanes, then [1024, 1536) with lanes 0..31).
-__device__ __forceinline__ void dma_record(const uint8_t* rec, uint32_t slot, int lane) {
-  const uint8_t* a0 = rec + 16 * lane;
+// Copy records recA and recB (uniform addresses) into the pair slot at LDS byte offset ps.
+// Lane l's 16 bytes land at M0 + 16 l.  voff = 16 l reads the heads; the tails are copied by
+// two half-wave loads (exec restricted inside the statement and restored before it ends) with
+// per-lane offsets vta = 1024 + 16 l (lanes 0..31: A bytes [1024, 1536)) and vtb = 512 + 16 l
+// (lanes 32..63: B bytes [1024, 1536)).  No immediate offsets are used.
+__device__ __forceinline__ void dma_pair(const uint8_t* recA, const uint8_t* recB, uint32_t ps,
+                                         uint32_t voff, uint32_t vta, uint32_t vtb) {
+  uint64_t saved;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %[ps]\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(a0), "s"(slot)
+      "global_load_lds_dwordx4 %[v], %[a]\n\t"
+      "s_add_u32 m0, %[ps], 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v], %[b]\n\t"
+      "s_add_u32 m0, %[ps], 0x800\n\t"
+      "s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b32 exec_hi, 0\n\t"
+      "global_load_lds_dwordx4 %[ta], %[a]\n\t"
+      "s_mov_b64 exec, %[sv]\n\t"
+      "s_mov_b32 exec_lo, 0\n\t"
+      "global_load_lds_dwordx4 %[tb], %[b]\n\t"
+      "s_mov_b64 exec, %[sv]"
+      : [sv] "=&s"(saved)
+      : [ps] "s"(ps), [v] "v"(voff), [ta] "v"(vta), [tb] "v"(vtb), [a] "s"(recA), [b] "s"(recB)
       : "memory", "m0");
-  if (lane < 32) {
-    const uint8_t* a1 = rec + 1024 + 16 * lane;
-    asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(a1), "s"(slot + 1024u)
-        : "memory", "m0");
-  }
 }
 
-// Wait until at most 2*N direct-to-LDS page loads (N pages) are still outstanding.
+// Wait until at most N pairs' copies (4 loads each) are still outstanding.
 template <int N>
-__device__ __forceinline__ void wait_pages() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * N) : "memory");
-}
-// Runtime count n in [0, N]: waits for the largest template count not above n.
-template <int N>
-__device__ __forceinline__ void wait_pages_rt(int n) {
-  if constexpr (N == 0) {
-    wait_pages<0>();
-  } else {
-    if (n >= N) wait_pages<N>();
-    else wait_pages_rt<N - 1>(n);
-  }
+__device__ __forceinline__ void wait_pairs() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * N) : "memory");
 }
 
-struct PageRegs {
-  uint2 kc;  // K code words r and 4 + r of token t
-  uint2 vc;  // V code chunk of this lane (channel residue t, tokens 4r .. 4r+3, 8 blocks)
-  uint4 km;  // K (scale, zero) of token t, groups 0..3
-  uint4 vm;  // V (scale, zero) of token t, groups 0..3
+// This lane's K operands of page X of a pair: K code words r and 4 + r of token t, and the K
+// (scale, zero) of token t for groups 0..3.
+struct PageK {
+  uint2 kc;
+  uint4 km;
+};
+// V scale/zero of token t (page A, page B) and this lane's V code words for P.V: page kq / 2,
+// token quads 2 (kq % 2) and 2 (kq % 2) + 1 of channel residue t (8 tokens of one channel).
+struct PairV {
+  uint4 vmA, vmB;
+  uint4 vs;
 };
 
-// Read this lane's part of the record in LDS slot `slot`.
-__device__ __forceinline__ PageRegs read_slot(uint32_t slot, int lane, int t) {
-  PageRegs d;
-  const uint32_t a8 = slot + 8 * lane, a16 = slot + 16 * t;
+// K parts of both pages of the pair slot at LDS offset ps.  a8 = 8 * lane, a16 = 16 * t.
+__device__ __forceinline__ void read_pair_k(uint32_t ps, uint32_t a8, uint32_t a16, PageK& A,
+                                            PageK& B) {
   asm volatile(
       "ds_read_b64 %0, %4\n\t"
-      "ds_read_b64 %1, %4 offset:512\n\t"
-      "ds_read_b128 %2, %5 offset:1024\n\t"
-      "ds_read_b128 %3, %5 offset:1280\n\t"
+      "ds_read_b64 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %5 offset:2048\n\t"
+      "ds_read_b128 %3, %5 offset:2560\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(d.kc), "=&v"(d.vc), "=&v"(d.km), "=&v"(d.vm)
-      : "v"(a8), "v"(a16)
+      : "=&v"(A.kc), "=&v"(B.kc), "=&v"(A.km), "=&v"(B.km)
+      : "v"(ps + a8), "v"(ps + a16)
       : "memory");
-  return d;
+}
+// V parts.  av = this lane's V code offset within a pair slot.
+__device__ __forceinline__ void read_pair_v(uint32_t ps, uint32_t a16, uint32_t av, PairV& V) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:2304\n\t"
+      "ds_read_b128 %1, %3 offset:2816\n\t"
+      "ds_read2_b64 %2, %4 offset1:16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(V.vmA), "=&v"(V.vmB), "=&v"(V.vs)
+      : "v"(ps + a16), "v"(ps + av)
+      : "memory");
 }
 
 template <int NCB>
@@ -404,10 +420,10 @@ struct QOperands {
   float cscale[NCB];            // qsc / 254 * sm_scale * log2(e), > 0
 };
 
-// Per-wave LDS tile for the W transpose: [cb][hi/lo][row (j,g)][token] bf16.  Rows are padded
-// to 20 entries (40 bytes): the 16-lane groups of one write land on distinct banks and every
-// 4-token A operand read stays 8-byte aligned.
-constexpr int kTileRow = kPage + 4;
+// Per-wave LDS tile for the W transpose: [cb][hi/lo][row (j,g)][token of the pair] bf16, page A
+// tokens in columns 0..15, page B in 16..31.  Rows hold 36 entries (72 bytes): the 16-lane
+// groups of one write land on distinct banks and the 8-token A operand reads are 8-byte aligned.
+constexpr int kTileRow = 36;
 template <int NCB>
 struct WTile {
   uint16_t w[NCB][2][16][kTileRow];
@@ -423,28 +439,17 @@ constexpr float kRefMargin = 64.0f;
 // read as bf16 1 + code/16, block 2q + 1's at bits 5-6 (and 21-22), read as 1 + code/4.
 constexpr float kVScale[2] = {16.0f, 4.0f};  // code = scale * (bf16 value - 1), even / odd nb
 
-// One page.  MASKED: tokens outside [lo, hi) (sink or window positions, or past the end) may
-// hold stale bytes, so their logits are replaced by -inf and their V scale/zero by 0 (selects,
-// never arithmetic on the stale values), which makes all their contributions exactly 0.
-// FIRST: the page sets the run's reference max (unless a fixed reference is given).
-template <int NCB, bool MASKED, bool FIRST>
-__device__ __forceinline__ void int2_page(const PageRegs& d, bool live, const QOperands<NCB>& qo,
-                                          SplitState<NCB>& st, WTile<NCB>& tile, int t, int r,
-                                          uint32_t mask_e, uint32_t mask_o, uint32_t magic,
-                                          v4s ones, bool fixed_ref) {
+// Logits of one page in units of cscale: sum_g s_g * (q'.codes)_g + z_g * (sum of q' over g).
+// MASKED: tokens outside [lo, hi) may hold stale bytes and get -inf (a select, never arithmetic
+// on the stale values).
+template <int NCB, bool MASKED>
+__device__ __forceinline__ void page_logits(const PageK& d, bool live, const QOperands<NCB>& qo,
+                                            float a[NCB]) {
   const v4i ka0 = (v4i){(int)(d.kc.x & 0x03030303u), (int)((d.kc.x >> 2) & 0x03030303u),
                         (int)((d.kc.x >> 4) & 0x03030303u), (int)((d.kc.x >> 6) & 0x03030303u)};
   const v4i ka1 = (v4i){(int)(d.kc.y & 0x03030303u), (int)((d.kc.y >> 2) & 0x03030303u),
                         (int)((d.kc.y >> 4) & 0x03030303u), (int)((d.kc.y >> 6) & 0x03030303u)};
   const uint32_t kmw[4] = {d.km.x, d.km.y, d.km.z, d.km.w};
-  uint32_t vmw[4] = {d.vm.x, d.vm.y, d.vm.z, d.vm.w};
-  if (MASKED) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) vmw[g] = live ? vmw[g] : 0u;
-  }
-
-  // logits in units of cscale: sum_g s_g * (q'.codes)_g + z_g * (sum of q' over g)
-  float a[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
@@ -461,22 +466,24 @@ __device__ __forceinline__ void int2_page(const PageRegs& d, bool live, const QO
     }
     if (MASKED) x = live ? x : -INFINITY;
     a[cb] = x;
-    st.mlane[cb] = fmaxf(st.mlane[cb], x);
-    if (FIRST && !fixed_ref) st.mref[cb] = fmaxf(row_max16(x) * qo.cscale[cb], kNegBig);
   }
+}
 
-  v4s vb[8];
+// Softmax weights of one page and their transpose into the W tile (columns col0 + t):
+// p = 2^(a * cscale - mref), W = p * scale_v as a bf16 pair (hi = W truncated, lo = the rest
+// rounded to nearest even; relative error <= 2^-17, unbiased).  A dead token has p = 0 and its
+// V scale/zero replaced by 0.
+template <int NCB, bool MASKED>
+__device__ __forceinline__ void page_weights(const float a[NCB], uint4 vm, bool live,
+                                             const QOperands<NCB>& qo, SplitState<NCB>& st,
+                                             WTile<NCB>& tile, int t, int r, int col0) {
+  uint32_t vmw[4] = {vm.x, vm.y, vm.z, vm.w};
+  if (MASKED) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t y0 = q == 0 ? (d.vc.x << 3) : (d.vc.x >> (4 * q - 3));
-    const uint32_t y1 = q == 0 ? (d.vc.y << 3) : (d.vc.y >> (4 * q - 3));
-    vb[2 * q] = __builtin_bit_cast(v4s, make_uint2(and_or(y0, mask_e, magic), and_or(y1, mask_e, magic)));
-    vb[2 * q + 1] = __builtin_bit_cast(v4s, make_uint2(and_or(y0, mask_o, magic), and_or(y1, mask_o, magic)));
+    for (int g = 0; g < 4; ++g) vmw[g] = live ? vmw[g] : 0u;
   }
-
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    // p = 0 for masked tokens (exp2(-inf) = 0)
     const float p = __builtin_amdgcn_exp2f(fmaf(a[cb], qo.cscale[cb], -st.mref[cb]));
     st.lsum[cb] += p;
     float w[4], lo[4];
@@ -485,32 +492,82 @@ __device__ __forceinline__ void int2_page(const PageRegs& d, bool live, const QO
       const float sv = f16lo(vmw[g]), zv = f16hi(vmw[g]);
       w[g] = fmaf(p, sv, 0.0f);  // one v_fma_mix_f32 from the fp16 scale
       st.zp[cb][g] = fmaf(p, zv, st.zp[cb][g]);
-      // w ~= hi + lo: hi = w truncated to bf16, lo = bf16(w - hi) rounded to nearest even;
-      // relative error <= 2^-17, unbiased
       lo[g] = w[g] - __uint_as_float(__float_as_uint(w[g]) & 0xFFFF0000u);
     }
     const uint32_t l01 = pack_bf16(lo[0], lo[1]), l23 = pack_bf16(lo[2], lo[3]);
-    // transpose: this lane's (head r, token t, groups 0..3) -> rows 4r + g, column t
-    const int row = 4 * r;
+    // transpose: this lane's (head r, token t, groups 0..3) -> rows 4r + g, column col0 + t
+    const int row = 4 * r, col = col0 + t;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) tile.w[cb][0][row + g][t] = (uint16_t)(__float_as_uint(w[g]) >> 16);
-    tile.w[cb][1][row + 0][t] = (uint16_t)l01;
-    tile.w[cb][1][row + 1][t] = (uint16_t)(l01 >> 16);
-    tile.w[cb][1][row + 2][t] = (uint16_t)l23;
-    tile.w[cb][1][row + 3][t] = (uint16_t)(l23 >> 16);
-    // A operands: row (j,g) = l % 16 (= t as an index), tokens 4r .. 4r+3
-    const v4s ahi = *reinterpret_cast<const v4s*>(&tile.w[cb][0][t][4 * r]);
-    const v4s alo = *reinterpret_cast<const v4s*>(&tile.w[cb][1][t][4 * r]);
+    for (int g = 0; g < 4; ++g) tile.w[cb][0][row + g][col] = (uint16_t)(__float_as_uint(w[g]) >> 16);
+    tile.w[cb][1][row + 0][col] = (uint16_t)l01;
+    tile.w[cb][1][row + 1][col] = (uint16_t)(l01 >> 16);
+    tile.w[cb][1][row + 2][col] = (uint16_t)l23;
+    tile.w[cb][1][row + 3][col] = (uint16_t)(l23 >> 16);
+  }
+}
+
+// One pair of pages.  MASKED: either page may hold positions outside [lo, hi) (liveA/liveB per
+// lane token).  FIRST: page A sets the run's reference max (unless a fixed reference is given).
+// after_reads() runs once the pair's LDS reads have completed (the page-id prefetch goes there,
+// so that waiting for those reads never waits for it).
+template <int NCB, bool MASKED, bool FIRST, class AfterReads>
+__device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16, uint32_t av,
+                                          bool liveA, bool liveB, const QOperands<NCB>& qo,
+                                          SplitState<NCB>& st, WTile<NCB>& tile, int t, int r,
+                                          uint32_t mask_e, uint32_t mask_o, uint32_t magic,
+                                          v8bf ones, bool fixed_ref, AfterReads&& after_reads) {
+  PageK kA, kB;
+  read_pair_k(ps, a8, a16, kA, kB);
+  float aA[NCB], aB[NCB];
+  page_logits<NCB, MASKED>(kA, liveA, qo, aA);
+  page_logits<NCB, MASKED>(kB, liveB, qo, aB);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      st.acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nb], st.acc[cb][nb], 0, 0, 0);
-      st.acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nb], st.acc[cb][nb], 0, 0, 0);
+  for (int cb = 0; cb < NCB; ++cb) {
+    st.mlane[cb] = fmaxf(st.mlane[cb], fmaxf(aA[cb], aB[cb]));
+    if (FIRST && !fixed_ref) st.mref[cb] = fmaxf(row_max16(aA[cb]) * qo.cscale[cb], kNegBig);
+  }
+  PairV V;
+  read_pair_v(ps, a16, av, V);
+  after_reads();
+  page_weights<NCB, MASKED>(aA, V.vmA, liveA, qo, st, tile, t, r, 0);
+  page_weights<NCB, MASKED>(aB, V.vmB, liveB, qo, st, tile, t, r, kPage);
+
+  const uint32_t vsw[4] = {V.vs.x, V.vs.y, V.vs.z, V.vs.w};
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    // A operands: row (j,g) = l % 16 (= t as an index), tokens 8r .. 8r+7 of the pair
+    // (rows are 8-byte aligned only: two 8-byte reads each)
+    const uint2* ph = reinterpret_cast<const uint2*>(&tile.w[cb][0][t][8 * r]);
+    const uint2* pl = reinterpret_cast<const uint2*>(&tile.w[cb][1][t][8 * r]);
+    const uint2 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
+    const v8bf ahi = __builtin_bit_cast(v8bf, make_uint4(h0.x, h0.y, h1.x, h1.y));
+    const v8bf alo = __builtin_bit_cast(v8bf, make_uint4(l0.x, l0.y, l1.x, l1.y));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = q == 0 ? (vsw[i] << 3) : (vsw[i] >> (4 * q - 3));
+      const v8bf ve = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_e, magic), and_or(y[1], mask_e, magic),
+                                                          and_or(y[2], mask_e, magic), and_or(y[3], mask_e, magic)));
+      const v8bf vo = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_o, magic), and_or(y[1], mask_o, magic),
+                                                          and_or(y[2], mask_o, magic), and_or(y[3], mask_o, magic)));
+      st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, ve, st.acc[cb][2 * q], 0, 0, 0);
+      st.acc[cb][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vo, st.acc[cb][2 * q + 1], 0, 0, 0);
+      st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ve, st.acc[cb][2 * q], 0, 0, 0);
+      st.acc[cb][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vo, st.acc[cb][2 * q + 1], 0, 0, 0);
     }
     // the same weights against a column of ones: the exact bf16 weight sums that the code
     // accumulators carry in their "1 +" part
-    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, ones, st.wsum[cb], 0, 0, 0);
-    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, ones, st.wsum[cb], 0, 0, 0);
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, ones, st.wsum[cb], 0, 0, 0);
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ones, st.wsum[cb], 0, 0, 0);
   }
+}
+
+// Priority of a worker wave after `band` quarters of its run (3 at the start, 0 in the last).
+__device__ __forceinline__ void lower_priority(int band) {
+  if (band == 1) __builtin_amdgcn_s_setprio(2);
+  else if (band == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // Worker waves per workgroup: each wave is an independent worker with its own LDS ring and
@@ -520,7 +577,7 @@ constexpr int kWaves = 2;
 // Shared memory of one workgroup of int2_decode_kernel: the page rings and W tiles of its
 // INT2 workers, or the scratch of the BF16 window role.
 template <int NCB>
-constexpr size_t kSmemBytes = (size_t)kWaves * kRing * kRecord + (size_t)kWaves * sizeof(WTile<NCB>);
+constexpr size_t kSmemBytes = (size_t)kWaves * kRingBytes + (size_t)kWaves * sizeof(WTile<NCB>);
 
 // BF16 sink + window positions of one (sequence, KV head), computed by the kWaves waves of one
 // workgroup: logits on the bf16 MFMA (q' as a hi/lo bf16 pair, K rows exact), softmax in fp32,
@@ -690,9 +747,13 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
   const int worker = blockIdx.x * kWaves + wave;
   const int t = lane & 15, r = lane >> 4;
-  WTile<NCB>& tile = *reinterpret_cast<WTile<NCB>*>(smem + (size_t)kWaves * kRing * kRecord +
+  WTile<NCB>& tile = *reinterpret_cast<WTile<NCB>*>(smem + (size_t)kWaves * kRingBytes +
                                                     wave * sizeof(WTile<NCB>));
-  const uint32_t ring0 = lds_offset(smem + (size_t)wave * kRing * kRecord);
+  const uint32_t ring0 = lds_offset(smem + (size_t)wave * kRingBytes);
+  // per-lane LDS offsets inside a pair slot (see read_pair_k / read_pair_v) and copy offset
+  const uint32_t a8 = 8 * lane, a16 = 16 * t, voff = 16 * lane;
+  const uint32_t vta = voff + 1024, vtb = voff + 512;  // tail copy offsets (see dma_pair)
+  const uint32_t av = kPairHeadB * (r >> 1) + 512 + 256 * (r & 1) + 8 * t;
 
   const int total = plan[0], C = plan[1];
   if ((long long)worker * C >= total) return;
@@ -721,6 +782,7 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   const int G = hq / g.hkv;
   const float sm_log2 = sm_scale * kLog2e;
   const size_t rec_stride = (size_t)g.hkv * kRecord;  // bytes between pages of one head
+  const uint32_t last_page = (uint32_t)(g.num_pages - 1);
 
   // Opaque copies of the V-code constants: masks in SGPRs, magic in a VGPR, so every
   // (x & mask) | magic is one instruction.  The empty asm statements emit nothing.
@@ -728,7 +790,8 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   asm volatile("" : "+s"(mask_e));
   asm volatile("" : "+s"(mask_o));
   asm volatile("" : "+v"(magic));
-  const v4s ones = __builtin_bit_cast(v4s, make_uint2(0x3F803F80u, 0x3F803F80u));  // bf16 1.0
+  const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                        0x3F803F80u));  // bf16 1.0
 
   int pos = run0;
   while (true) {
@@ -794,50 +857,68 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
       // scalar loads are counted by lgkmcnt, so waiting for one never drains the page ring.
       // Each page issues exactly one record copy, so the per-page wait counts are exact.  An
       // id outside the pool reads page 0 instead (memory safety; the caller's table is wrong).
-      auto load_id = [&](int pg) -> int { return pg < pgB ? bt[pg] : 0; };
-      auto issue = [&](int pg, int page) {
-        const bool ok = page >= 0 && page < g.num_pages;
-        dma_record(pages_h + (size_t)(ok ? page : 0) * rec_stride,
-                   ring0 + (uint32_t)(pg & (kRing - 1)) * kRecord, lane);
+      // Pages in pairs [pgA + 2k, pgA + 2k + 1); a second page at or beyond pgB is a dummy
+      // (it copies the segment's last page again and is masked).  An id outside the pool reads
+      // the pool's last page instead (memory safety; the caller's table is wrong).  Page ids
+      // come from uniform (scalar) loads, fetched one pair before they are used.
+      const int npairs = (pgB - pgA + 1) >> 1;
+      auto pslot = [&](int k) { return ring0 + (uint32_t)(k & 1) * kPairBytes; };
+      int nidA = bt[pgA], nidB = bt[min(pgA + 1, pgB - 1)];  // ids of the next pair to issue
+      int pfA = 0, pfB = 0;                                 // prefetched ids of the one after
+      auto rec_of = [&](int id) {
+        return pages_h + (size_t)min((uint32_t)id, last_page) * rec_stride;
       };
-      for (int k = 0; k < kAhead; ++k)
-        if (pgA + k < pgB) issue(pgA + k, load_id(pgA + k));
-      int id_next = load_id(pgA + kAhead);
-      auto fetch = [&](int pg) -> PageRegs {
-        if (--band_left == 0) {
-          band_left = band_len;
-          ++band;
-          if (band == 1) __builtin_amdgcn_s_setprio(2);
-          else if (band == 2) __builtin_amdgcn_s_setprio(1);
-          else if (band == 3) __builtin_amdgcn_s_setprio(0);
-        }
-        if (pg + kAhead < pgB) {
-          issue(pg + kAhead, id_next);
-          id_next = load_id(pg + kAhead + 1);
-          wait_pages<kAhead>();
-        } else {
-          wait_pages_rt<kAhead>(pgB - 1 - pg);
-        }
-        return read_slot(ring0 + (uint32_t)(pg & (kRing - 1)) * kRecord, lane, t);
+      auto issue = [&](int k) {  // issue pair k (its ids are in nidA / nidB)
+        dma_pair(rec_of(nidA), rec_of(nidB), pslot(k), voff, vta, vtb);
       };
-      auto live_at = [&](int pg) { const int p = pg * kPage + t; return p >= lo && p < hi; };
+      auto prefetch = [&](int k) {  // ids of pair k
+        const int pg = pgA + 2 * k;
+        pfA = bt[min(pg, pgB - 1)];
+        pfB = bt[min(pg + 1, pgB - 1)];
+      };
+      auto band_tick = [&]() {
+        band_left -= 2;
+        if (__builtin_expect(band_left <= 0, 0)) {
+          band_left += band_len;
+          lower_priority(++band);
+        }
+      };
+      auto live_at = [&](int q) {
+        const int p = q * kPage + t;
+        return q < pgB && p >= lo && p < hi;
+      };
 
-      // first page (it may hold sink positions), interior pages (all INT2), last page (it may
-      // hold window positions or the end of the sequence)
-      {
-        const PageRegs d = fetch(pgA);
-        int2_page<NCB, true, true>(d, live_at(pgA), qo, st, tile, t, r, mask_e, mask_o, magic, ones,
-                                   fixed_ref);
+      issue(0);
+      if (npairs > 1) {  // pair 1 is issued before pair 0 is waited for
+        prefetch(1);
+        nidA = pfA;
+        nidB = pfB;
+        issue(1);
+        prefetch(2);
+        wait_pairs<1>();
+      } else {
+        wait_pairs<0>();
       }
-      for (int pg = pgA + 1; pg < pgB - 1; ++pg) {
-        const PageRegs d = fetch(pg);
-        int2_page<NCB, false, false>(d, true, qo, st, tile, t, r, mask_e, mask_o, magic, ones,
-                                     fixed_ref);
+      // first pair (page A may hold sink positions; both pages may hold window positions or
+      // the end when it is also the last pair)
+      int2_pair<NCB, true, true>(pslot(0), a8, a16, av, live_at(pgA), live_at(pgA + 1), qo, st,
+                                 tile, t, r, mask_e, mask_o, magic, ones, fixed_ref, [] {});
+      int k = 1;
+      for (; k < npairs - 1; ++k) {  // interior pairs: every position is INT2
+        band_tick();
+        nidA = pfA;
+        nidB = pfB;
+        issue(k + 1);
+        wait_pairs<1>();
+        int2_pair<NCB, false, false>(pslot(k), a8, a16, av, true, true, qo, st, tile, t, r,
+                                     mask_e, mask_o, magic, ones, fixed_ref,
+                                     [&] { prefetch(k + 2); });
       }
-      if (pgB - 1 > pgA) {
-        const PageRegs d = fetch(pgB - 1);
-        int2_page<NCB, true, false>(d, live_at(pgB - 1), qo, st, tile, t, r, mask_e, mask_o, magic,
-                                    ones, fixed_ref);
+      if (k == npairs - 1) {  // last pair (k >= 1)
+        wait_pairs<0>();
+        const int pg = pgA + 2 * k;
+        int2_pair<NCB, true, false>(pslot(k), a8, a16, av, live_at(pg), live_at(pg + 1), qo, st,
+                                    tile, t, r, mask_e, mask_o, magic, ones, fixed_ref, [] {});
       }
 
       // A logit beyond the reference margin: recompute once with the exact max (rare path).
