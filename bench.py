@@ -26,6 +26,38 @@ BF16_TOKEN_HEAD_BYTES = 512     # bf16 K + V rows
 METRIC = "decode attn tokens/s + effective HBM GB/s (% of peak), Qwen3-8B shape B=64 ctx=32k"
 
 
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "int2_decode_qwen3_8b_b64_hbm_traffic.md")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None when
+    that summary is for another workload or the decode kernels have changed since (their
+    sources no longer hash to the recorded value)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        if fields.get("workload") != workload:
+            return None
+        root = os.path.dirname(os.path.abspath(__file__))
+        h = hashlib.sha256()
+        for src in fields["kernel_sources"].split():
+            h.update(open(os.path.join(root, src), "rb").read())
+        if h.hexdigest() != fields["kernel_sources_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -254,7 +286,7 @@ def main():
                      "BF16 window)", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": bm["decode_attention"], "launch_ms": round(attn_avg, 5),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
         "bytes": bm,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
