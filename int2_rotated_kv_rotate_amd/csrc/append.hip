@@ -57,9 +57,17 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
   const float clip = is_v ? clip_v : clip_k;
   const int nrows = min(kRows, total_new - row0);
 
-  // Stage R (fp32) and the rows.
+  // Stage R (fp32) and the rows: all 16 loads of a thread are issued before the first LDS
+  // store, so staging costs one memory latency.
   const float4* rot4 = reinterpret_cast<const float4*>(rot);
-  for (int i = t; i < kHeadDim * kHeadDim / 4; i += kThreads) s_rot[i] = rot4[i];
+  {
+    constexpr int kPer = kHeadDim * kHeadDim / 4 / kThreads;  // 16
+    float4 rr[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) rr[k] = rot4[t + kThreads * k];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) s_rot[t + kThreads * k] = rr[k];
+  }
   for (int i = t; i < kRows * kHeadDim; i += kThreads) {
     int r = i / kHeadDim, c = i % kHeadDim;
     s_x[r][c] = r < nrows ? bf16_to_f32(src[((size_t)(row0 + r) * g.hkv + h) * kHeadDim + c]) : 0.f;
@@ -118,42 +126,48 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
   }
   __syncthreads();
 
-  // Group parameters and codes: threads 0..63 -> (row, group).
-  if (t < kRows * kGroups) {
-    const int r = t / kGroups, gi = t % kGroups;
+  // Group parameters and codes: thread -> (row, group, quarter of the group's 32 channels).
+  {
+    const int r = t >> 4, gi = (t >> 2) & 3, sub = t & 3;
+    const int c0 = gi * kGroup + 8 * sub;
+    float mx = s_y[r][c0], mn = mx;
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+      const float v = s_y[r][c0 + c];
+      mx = fmaxf(mx, v);
+      mn = fminf(mn, v);
+    }
+    // the four quarters of the group are adjacent lanes
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mn = fminf(mn, __shfl_xor(mn, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mn = fminf(mn, __shfl_xor(mn, 2));
+    mx = mx + 0.0f;  // a signed-zero extreme becomes +0
+    mn = mn + 0.0f;
+    const float mx_c = clip * mx;
+    const float mn_c = clip * mn;
+    const float width = mx_c - mn_c;
+    const float s32 = width / 3.0f;
+    const _Float16 s16 = (_Float16)materialize(s32);
+    const _Float16 z16 = (_Float16)materialize(mn_c);
+    const float sc = (float)s16, z = (float)z16;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      int code = 0;
+      if (sc != 0.0f) {
+        float q = (s_y[r][c0 + c] - z) / sc;
+        q = __builtin_rintf(q);
+        q = fminf(fmaxf(q, 0.0f), 3.0f);
+        code = (int)q;
+      }
+      s_code[r][c0 + c] = (uint8_t)code;
+    }
     const RowInfo info = s_info[r];
-    if (r < nrows) {
-      float mx = s_y[r][gi * kGroup], mn = mx;
-      for (int c = 1; c < kGroup; ++c) {
-        float v = s_y[r][gi * kGroup + c];
-        mx = fmaxf(mx, v);
-        mn = fminf(mn, v);
-      }
-      mx = mx + 0.0f;  // a signed-zero extreme becomes +0
-      mn = mn + 0.0f;
-      const float mx_c = clip * mx;
-      const float mn_c = clip * mn;
-      const float width = mx_c - mn_c;
-      const float s32 = width / 3.0f;
-      const _Float16 s16 = (_Float16)materialize(s32);
-      const _Float16 z16 = (_Float16)materialize(mn_c);
-      const float s = (float)s16, z = (float)z16;
-      for (int c = 0; c < kGroup; ++c) {
-        int code = 0;
-        if (s != 0.0f) {
-          float q = (s_y[r][gi * kGroup + c] - z) / s;
-          q = __builtin_rintf(q);
-          q = fminf(fmaxf(q, 0.0f), 3.0f);
-          code = (int)q;
-        }
-        s_code[r][gi * kGroup + c] = (uint8_t)code;
-      }
-      if (info.rec >= 0) {
-        uint32_t meta = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
-        *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kVMeta : kKMeta) +
-                                     16 * info.slot_in_page + 4 * gi) = meta;
-      }
+    if (sub == 0 && r < nrows && info.rec >= 0) {
+      uint32_t meta = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+      *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kVMeta : kKMeta) +
+                                   16 * info.slot_in_page + 4 * gi) = meta;
     }
   }
   __syncthreads();

@@ -29,10 +29,21 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
 
   // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of every split.
+  // Loads are issued 4 at a time before their LDS stores (4096 quads = a multiple of
+  // 4 * blockDim.x for every group size), so staging costs 1 to 8 memory latencies.
   if (rot_v != nullptr) {
     const float4* R = reinterpret_cast<const float4*>(rot_v + (size_t)h * kHeadDim * kHeadDim);
-    for (int e = threadIdx.x; e < kHeadDim * kHeadDim / 4; e += blockDim.x)
-      s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = R[e];
+    constexpr int kQuads = kHeadDim * kHeadDim / 4, kChunk = 4;
+    for (int e0 = threadIdx.x; e0 < kQuads; e0 += kChunk * blockDim.x) {
+      float4 rr[kChunk];
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) rr[k] = R[e0 + k * blockDim.x];
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const int e = e0 + k * blockDim.x;
+        s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = rr[k];
+      }
+    }
   }
   // INT2 partials in slots [0, nvalid), the BF16 sink/window partial in the last slot; the
   // merge runs over n = nvalid + 1 entries, entry e < nvalid being slot e.
