@@ -100,6 +100,7 @@ def cpu_baseline(p, target_s: float):
     sm = float(np.float32(1.0 / math.sqrt(128.0)))
     heads = list(range(min(2, w.num_kv_heads)))
     per_step = []
+    ref = {}
     with threadpool_limits(limits=1):
         caches = {}
         for h in heads:
@@ -112,18 +113,115 @@ def cpu_baseline(p, target_s: float):
                 t0 = time.perf_counter()
                 caches[h].append(p.table[0], 0, L - 1, kb[L - 1:, h:h + 1], vb[L - 1:, h:h + 1],
                                  p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
-                O.decode_attention(caches[h], p.table[:1], np.zeros(1, np.int64), p.lens[:1],
-                                   p.q[:1, h * G:(h + 1) * G], p.rot_k[h:h + 1],
-                                   p.rot_v[h:h + 1], sm)
+                ref[h] = O.decode_attention(caches[h], p.table[:1], np.zeros(1, np.int64),
+                                            p.lens[:1], p.q[:1, h * G:(h + 1) * G],
+                                            p.rot_k[h:h + 1], p.rot_v[h:h + 1], sm)
                 per_step.append(time.perf_counter() - t0)
     t_head = float(np.mean(per_step))
-    return {"value": 1.0 / (t_head * w.num_kv_heads), "unit": "tokens/s", "cores": 1,
+    return ref, {"value": 1.0 / (t_head * w.num_kv_heads), "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
             "sample": (f"sequence 0 (L={L}), KV heads {heads} x {G} query heads: "
                        f"{len(per_step)} timed single-head decode steps (append of the new "
                        f"token + decode attention), {sum(per_step):.1f} s in total, scaled to "
                        f"all {w.num_kv_heads} KV heads of one decode step; one BLAS thread"),
             "host_cpus": os.cpu_count()}
+
+
+def time_scrubbed(fn, n: int, scrub):
+    """Median (and p10, p90) of n launches of fn, each timed with an event pair on the current
+    stream, with the whole last-level cache overwritten before each launch (scrub)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(n):
+        scrub.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts = np.array(ts)
+    return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+
+def int2_vs_bf16(n_iter: int):
+    """Attention (decode launch + combine) of the INT2 path against the BF16 paged baseline of
+    the same library, with a 1 GiB cache scrub before every timed launch:
+      * Qwen3-32B layer shape, context 32768: INT2 at batch 16 vs BF16 at batch 2 (about 1/8
+        of the batch) and batch 3 (the equal-memory batch for 3 bits per element);
+      * Qwen3-4B layer shape, batch 1, context 32768: latency of each."""
+    import torch
+    from int2_rotated_kv_rotate_amd import harness as H
+    from int2_rotated_kv_rotate_amd import workload as W
+
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    res = {}
+
+    def attn_bytes(w, p, bf16):
+        """Algorithmic bytes of one attention launch + combine (KV read, q, table, out)."""
+        lens = np.asarray(p.lens, np.int64)
+        hkv, hq, B = w.num_kv_heads, w.num_q_heads, w.batch
+        if bf16:
+            kv = hkv * BF16_TOKEN_HEAD_BYTES * int(lens.sum())
+        else:
+            n_sink = np.minimum(lens, w.num_sink)
+            n_win = np.minimum(w.window, lens - n_sink)
+            kv = hkv * (INT2_TOKEN_HEAD_BYTES * int((lens - n_sink - n_win).sum()) +
+                        BF16_TOKEN_HEAD_BYTES * int((n_sink + n_win).sum()))
+        return kv + B * hq * 128 * (2 + 4) + 4 * int(((lens + 15) // 16).sum())
+
+    def int2_case(w):
+        p = H.make_problem(w)
+        cache = H.GpuCache(p)
+        lk, lv = cache.fill_context()
+        step = H.DecodeStep(cache)
+        step.set_new_token(lk, lv)
+        step.run()
+        torch.cuda.synchronize()
+        ms = time_scrubbed(step.attend, n_iter, scrub)
+        pool = p.num_pages * w.num_kv_heads * 1536
+        del step, cache
+        return p, ms, pool
+
+    def bf16_case(w):
+        p = H.make_problem(w)
+        bc = H.Bf16Cache(p)
+        bc.attend()
+        torch.cuda.synchronize()
+        ms = time_scrubbed(bc.attend, n_iter, scrub)
+        pool = p.num_pages * w.num_kv_heads * 8192
+        del bc
+        return p, ms, pool
+
+    def gbps(w, p, ms, bf16):
+        return round(attn_bytes(w, p, bf16) / (ms * 1e-3) / 1e9, 1)
+
+    w32 = W.WORKLOADS["qwen3_32b"]
+    p, (ms, p10, p90), pool = int2_case(w32)
+    r32 = {"int2": {"batch": w32.batch, "ms": round(ms, 4), "tokens_per_s": round(w32.batch / ms * 1e3, 1),
+                    "pool_bytes": pool, "effective_gbps": gbps(w32, p, ms, False)}}
+    for bb in w32.bf16_batches:
+        wb = W.scaled(w32, batch=bb, name=f"qwen3_32b_bf16_b{bb}")
+        pb, (msb, _, _), poolb = bf16_case(wb)
+        r32[f"bf16_b{bb}"] = {"batch": bb, "ms": round(msb, 4),
+                              "tokens_per_s": round(bb / msb * 1e3, 1), "pool_bytes": poolb,
+                              "effective_gbps": gbps(wb, pb, msb, True)}
+        r32[f"throughput_ratio_vs_bf16_b{bb}"] = round((w32.batch / ms) / (bb / msb), 3)
+    res["qwen3_32b_ctx32k"] = r32
+    log(f"qwen3_32b: INT2 B={w32.batch} {ms:.4f} ms; " + ", ".join(
+        f"BF16 B={r32[k]['batch']} {r32[k]['ms']:.4f} ms" for k in r32 if k.startswith("bf16")))
+
+    w4 = W.WORKLOADS["qwen3_4b"]
+    p4, (ms_i, _, _), _ = int2_case(w4)
+    _, (ms_b, _, _), _ = bf16_case(w4)
+    res["qwen3_4b_b1_ctx32k"] = {"int2_ms": round(ms_i, 4), "bf16_ms": round(ms_b, 4),
+                                 "latency_ratio": round(ms_b / ms_i, 3),
+                                 "int2_effective_gbps": gbps(w4, p4, ms_i, False),
+                                 "bf16_effective_gbps": gbps(w4, p4, ms_b, True)}
+    log(f"qwen3_4b B=1: INT2 {ms_i:.4f} ms, BF16 {ms_b:.4f} ms")
+    del scrub
+    return res
 
 
 def main():
@@ -139,6 +237,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the INT2 vs BF16 comparisons at the Qwen3-32B and batch-1 shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -256,10 +356,27 @@ def main():
         log("copy calibration: 1 GiB device copy done")
 
     cpu = None
+    parity = None
     if not args.no_cpu:
         t0 = time.time()
-        cpu = cpu_baseline(p, args.cpu_seconds)
+        ref, cpu = cpu_baseline(p, args.cpu_seconds)
         log(f"cpu oracle baseline: {cpu['value']:.4f} tokens/s ({time.time() - t0:.1f} s)")
+        # the oracle's outputs of the same cache state against the GPU's last decode step
+        G = w.group
+        out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
+        errs, dl = [], []
+        for h, (o_ref, l_ref) in ref.items():
+            o_gpu = out[0, h * G:(h + 1) * G].astype(np.float64)
+            errs.append(np.abs(o_gpu - o_ref[0]).max(axis=-1) / np.abs(o_ref[0]).max(axis=-1))
+            dl.append(np.abs(lse[0, h * G:(h + 1) * G] - l_ref[0]))
+        parity = {"rows": int(sum(e.size for e in errs)), "sequence": 0,
+                  "kv_heads": sorted(ref), "max_row_rel_err": float(np.max(errs)),
+                  "max_abs_dlse": float(np.max(dl)), "tolerance": 2e-3}
+        log(f"parity sample: {parity}")
+
+    compare = None
+    if not args.no_compare:
+        compare = int2_vs_bf16(20)
 
     line = {
         "metric": METRIC,
@@ -290,6 +407,8 @@ def main():
         "bytes": bm,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "int2_vs_bf16": compare,
     }
     print(json.dumps(line), flush=True)
 

@@ -187,3 +187,46 @@ class DecodeStep:
     def run(self, stream=None):
         self.append_new(stream)
         self.attend(stream)
+
+
+class Bf16Cache:
+    """Device buffers of the BF16 paged baseline for a Problem (no rotation, no quantisation):
+    pages int16 [num_pages][Hkv][4096] (bf16 K [16][128] then V^T [128][16]) filled with every
+    sequence's whole context, plus a decode workspace split every `split_pages` pages."""
+
+    def __init__(self, p: Problem, device="cuda", split_pages: Optional[int] = None):
+        w = p.w
+        self.p = p
+        self.device = device
+        hkv = w.num_kv_heads
+        self.layout = ops.make_layout(hkv, 0, 0, p.num_pages, p.table.shape[1], w.batch)
+        self.pages = torch.zeros((p.num_pages, hkv, ops.BF16_PAGE_ELEMS), dtype=torch.int16,
+                                 device=device)
+        self.table = torch.from_numpy(p.table).to(device)
+        offsets, outliers = W.key_offsets(w), W.outlier_channels(w)
+        for b in range(w.batch):
+            L = int(p.lens[b])
+            kb, vb = W.sequence_kv(w, b, L, offsets=offsets, outliers=outliers)
+            ops.bf16_append(self.layout, self.pages, self.table[b:b + 1],
+                            as_i16(kb).to(device), as_i16(vb).to(device),
+                            torch.tensor([0, L], dtype=torch.int32, device=device),
+                            torch.zeros(1, dtype=torch.int32, device=device))
+        torch.cuda.synchronize()
+        pages_max = int((p.lens.max() + 15) // 16)
+        if split_pages is None:  # about 4096 (split, KV head, sequence) waves
+            split_pages = max(1, -(-pages_max * w.batch * hkv // 4096))
+        self.split_pages = split_pages
+        self.max_splits = max(1, -(-pages_max // split_pages))
+        self.ws = torch.empty(ops.decode_workspace_bytes(w.batch, w.num_q_heads, self.max_splits),
+                              dtype=torch.uint8, device=device)
+        self.q = as_i16(p.q).to(device)
+        self.seq_lens = torch.from_numpy(p.lens.astype(np.int32)).to(device)
+        self.out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=device)
+        self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=device)
+
+    def attend(self, stream=None):
+        w = self.p.w
+        ops.bf16_decode_attention(self.layout, self.pages, self.table, self.q, self.seq_lens,
+                                  SM_SCALE, self.split_pages, self.max_splits, self.ws, stream)
+        ops.combine(w.batch, w.num_q_heads, w.num_kv_heads, self.max_splits, self.ws, None,
+                    self.out, self.lse, stream)
