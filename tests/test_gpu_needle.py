@@ -1,0 +1,78 @@
+"""Planted-needle check at 128K context (batch 1, 32 query / 8 KV heads, sink 4 + window 128).
+
+One seeded key row in the middle of the context (position L/2, a seeded KV head h* and query
+head j* of its group) is set to bf16(8 q_j* / |q_j*|) before it is appended.  Its attention
+weight is w = exp(z - lse), where z is the needle's logit from its stored codes (the oracle's,
+which the GPU's page records must equal byte for byte) and lse is the log-sum-exp of all the
+head's logits: the GPU's lse (from oscar_combine) must give the oracle's weight to 2e-3
+relative.  (Among 131K positions with ×15 outlier key channels the needle's weight is small,
+about 1e-5 here; the check is the agreement, not its size.)  The output rows of the needle's
+KV head must also match the oracle to 2e-3.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oscar_oracle as O
+from int2_rotated_kv_rotate_amd import harness as H
+from int2_rotated_kv_rotate_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+SENTINEL = 0xA5
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def test_needle_weight_128k():
+    w = W.WORKLOADS["long_128k"]
+    p = H.make_problem(w)
+    b, pos, h, j = W.needle_site(w, p.lens)
+    L = int(p.lens[b])
+    G = w.group
+    _log(f"[needle] L={L} position {pos} KV head {h} query head {j}")
+
+    cache = H.GpuCache(p, fill=SENTINEL)
+    last_k, last_v = cache.fill_context()
+    step = H.DecodeStep(cache)
+    step.set_new_token(last_k, last_v)
+    step.run()
+    torch.cuda.synchronize()
+
+    kb, vb = W.sequence_kv(w, b, L, offsets=W.key_offsets(w), outliers=W.outlier_channels(w),
+                           needle=(b, pos, h, j), q_bits=p.q)
+    oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window, fill=SENTINEL)
+    args = (p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
+    oc.append(p.table[b], b, 0, kb[:L - 1, h:h + 1], vb[:L - 1, h:h + 1], *args)
+    oc.append(p.table[b], b, L - 1, kb[L - 1:, h:h + 1], vb[L - 1:, h:h + 1], *args)
+
+    pages_b = p.table[b, :math.ceil(L / 16)]
+    idx = torch.from_numpy(pages_b.astype(np.int64)).to(cache.pages.device)
+    assert np.array_equal(cache.pages[idx, h].cpu().numpy(), oc.pages[pages_b, 0])
+
+    ref, ref_lse = O.decode_attention(oc, p.table[b:b + 1], np.array([b]), p.lens[b:b + 1],
+                                      p.q[b:b + 1, h * G:(h + 1) * G], p.rot_k[h:h + 1],
+                                      p.rot_v[h:h + 1], H.SM_SCALE)
+    # the needle's logit from its stored (dequantised) key in the rotated frame
+    k_all, _, _ = oc.read_sequence(p.table[b], b, 0, L)
+    qr = O.rotate_query(p.q[b], p.rot_k, G)[j]
+    z = H.SM_SCALE * float(k_all[pos] @ qr)
+    lse_gpu = float(step.lse[b, j].item())
+    lse_ref = float(ref_lse[0, j - h * G])
+    w_ref = math.exp(z - lse_ref)
+    w_gpu = math.exp(z - lse_gpu)
+    _log(f"[needle] logit {z:.4f}, lse oracle {lse_ref:.4f} gpu {lse_gpu:.4f}; weight oracle "
+         f"{w_ref:.4e} gpu {w_gpu:.4e} (rel {abs(w_gpu / w_ref - 1):.2e})")
+    assert w_ref > 0.0
+    assert abs(w_gpu / w_ref - 1.0) <= TOL
+
+    out = step.out[b, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+    rel = np.abs(out - ref[0]).max(axis=-1) / np.abs(ref[0]).max(axis=-1)
+    _log(f"[needle] KV head {h}: max row rel err {rel.max():.3e}")
+    assert rel.max() <= TOL
