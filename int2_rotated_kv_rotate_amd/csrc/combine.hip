@@ -28,7 +28,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   __shared__ float s_inv[8];
   __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
 
-  // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of every split.
+  // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of the slots.
   // Loads are issued 4 at a time before their LDS stores (4096 quads = a multiple of
   // 4 * blockDim.x for every group size), so staging costs 1 to 8 memory latencies.
   if (rot_v != nullptr) {
@@ -45,50 +45,56 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
       }
     }
   }
-  // INT2 partials in slots [0, nvalid), the BF16 sink/window partial in the last slot; the
-  // merge runs over n = nvalid + 1 entries, entry e < nvalid being slot e.
-  const int nv = min(max(ws.nvalid()[b * hkv + h], 0), ns - 1);
-  const int n = nv + 1;
-  auto slot_of = [&](int e) { return e < nv ? e : ns - 1; };
+  // INT2 partials in slots [0, nvalid), the BF16 sink/window partial in the last slot.  All
+  // loads are issued before nvalid is known (slots past it hold stale but readable values that
+  // never enter the sums), so the kernel pays one memory latency, not two.
+  const int nv_raw = ws.nvalid()[b * hkv + h];
   const float* o = ws.o(b, hq, jq, 0) + c;
   constexpr int kBatch = 16;
   float ov[kBatch];
 #pragma unroll
-  for (int e = 0; e < kBatch; ++e) ov[e] = e < n ? o[(size_t)slot_of(e) * kHeadDim] : 0.f;
-
-  // Merge weights of head j (threads c < n of each head load one entry's (m, l)).
-  for (int e = c; e < n; e += 128) {
-    const float2 ml = *ws.ml(b, hq, jq, slot_of(e));
-    s_w[j * ns + e] = ml.y > 0.f ? ml.x : -INFINITY;
+  for (int e = 0; e < kBatch; ++e) ov[e] = e < ns - 1 ? o[(size_t)e * kHeadDim] : 0.f;
+  const float ow = o[(size_t)(ns - 1) * kHeadDim];
+  for (int e = c; e < ns; e += 128) {  // raw (m, l) of every slot of head j
+    const float2 ml = *ws.ml(b, hq, jq, e);
+    s_w[j * ns + e] = ml.x;
     s_w[G * ns + j * ns + e] = ml.y;
   }
   __syncthreads();
-  if (c == 0) {
+  const int nv = min(max(nv_raw, 0), ns - 1);
+  if (c == 0) {  // weights of the entries: INT2 slots 0 .. nv-1, then the window slot
+    float* wm = s_w + j * ns;
+    const float* wl = s_w + G * ns + j * ns;
     float M = -INFINITY;
-    for (int e = 0; e < n; ++e) M = fmaxf(M, s_w[j * ns + e]);
+    for (int e = 0; e < nv; ++e)
+      if (wl[e] > 0.f) M = fmaxf(M, wm[e]);
+    if (wl[ns - 1] > 0.f) M = fmaxf(M, wm[ns - 1]);
     float l = 0.f;
-    for (int e = 0; e < n; ++e) {
-      const float ls = s_w[G * ns + j * ns + e];
-      const float w = ls > 0.f ? __builtin_amdgcn_exp2f(s_w[j * ns + e] - M) : 0.f;
-      s_w[j * ns + e] = w;
-      l = fmaf(w, ls, l);
+    for (int e = 0; e < nv; ++e) {
+      const float w = wl[e] > 0.f ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
+      wm[e] = w;
+      l = fmaf(w, wl[e], l);
     }
+    const float wwin = wl[ns - 1] > 0.f ? __builtin_amdgcn_exp2f(wm[ns - 1] - M) : 0.f;
+    wm[ns - 1] = wwin;
+    l = fmaf(wwin, wl[ns - 1], l);
     s_inv[j] = l > 0.f ? 1.0f / l : 0.f;
     if (lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
   }
   __syncthreads();
-  // o'[j][c] = sum_e w_e o'_e[c] / l in entry order; an empty entry (w = 0) is skipped, so its
-  // partial output is never read into the sum.
+  // o'[j][c] = sum_e w_e o'_e[c] / l over the INT2 slots in order, then the window slot; an
+  // empty entry (w = 0) is skipped, so its partial output is never read into the sum.
+  const float* wj = s_w + j * ns;
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < kBatch; ++e) {
-    const float w = s_w[j * ns + e];
-    if (e < n && w > 0.f) acc = fmaf(w, ov[e], acc);
+    if (e < nv && wj[e] > 0.f) acc = fmaf(wj[e], ov[e], acc);
   }
-  for (int e = kBatch; e < n; ++e) {
-    const float w = s_w[j * ns + e];
-    if (w > 0.f) acc = fmaf(w, o[(size_t)slot_of(e) * kHeadDim], acc);
+  for (int e = kBatch; e < nv; ++e) {
+    const float w = wj[e];
+    if (w > 0.f) acc = fmaf(w, o[(size_t)e * kHeadDim], acc);
   }
+  if (wj[ns - 1] > 0.f) acc = fmaf(wj[ns - 1], ow, acc);
   s_o[j][c] = acc * s_inv[j];
   __syncthreads();
   float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
