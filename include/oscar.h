@@ -122,6 +122,31 @@ int32_t oscar_rotate_quantize_append(
     const float* rot_k, const float* rot_v, float clip_k, float clip_v,
     void* stream);
 
+/* Kernel choices for oscar_rotate_quantize_append_method. */
+enum {
+  OSCAR_APPEND_AUTO = 0,    /* the matrix cores from 256 new rows, else the vector ALUs */
+  OSCAR_APPEND_VECTOR = 1,  /* the rotation in fp64 on the vector ALUs, as defined above */
+  OSCAR_APPEND_MATRIX = 2   /* the rotation on the bf16 matrix cores (R split exactly into three
+                               bf16 pieces), each rotated value's error bounded; every scale,
+                               zero, code and BF16 copy the bound cannot certify is recomputed
+                               as defined above */
+};
+
+/*
+ * oscar_rotate_quantize_append with the kernel chosen by `method` (one of OSCAR_APPEND_*;
+ * anything else is OSCAR_ERR_INVALID_ARGUMENT).  Every method writes the same bytes; they differ
+ * in speed only (the matrix cores win for prefill-sized appends, the vector ALUs for a few
+ * rows).  oscar_rotate_quantize_append is this call with OSCAR_APPEND_AUTO.
+ */
+int32_t oscar_rotate_quantize_append_method(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+    int32_t method, void* stream);
+
 /*
  * Bytes of workspace oscar_decode_attention / oscar_bf16_decode_attention need for `batch`
  * sequences of `num_q_heads` query heads split at most `max_splits` ways.  Returns 0 for

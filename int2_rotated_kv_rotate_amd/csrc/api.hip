@@ -60,17 +60,19 @@ const char* oscar_status_string(int32_t status) {
   }
 }
 
-int32_t oscar_rotate_quantize_append(
+int32_t oscar_rotate_quantize_append_method(
     const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
     const int32_t* block_table, const int32_t* slot_ids,
     int32_t batch, int32_t total_new,
     const uint16_t* k_new, const uint16_t* v_new,
     const int32_t* new_offsets, const int32_t* start_pos,
     const float* rot_k, const float* rot_v, float clip_k, float clip_v,
-    void* stream) {
+    int32_t method, void* stream) {
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (method != OSCAR_APPEND_AUTO && method != OSCAR_APPEND_VECTOR && method != OSCAR_APPEND_MATRIX)
+    return OSCAR_ERR_INVALID_ARGUMENT;
   if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
     return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0 || total_new == 0) return OSCAR_OK;
@@ -80,9 +82,24 @@ int32_t oscar_rotate_quantize_append(
   if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rot_k) ||
       !aligned16(rot_v) || (sinkwin && !aligned16(sinkwin)))
     return OSCAR_ERR_INVALID_ARGUMENT;
+  static_assert(OSCAR_APPEND_AUTO == kAppendAuto && OSCAR_APPEND_VECTOR == kAppendVector &&
+                OSCAR_APPEND_MATRIX == kAppendMatrix, "append method numbering");
   return hip_status(launch_append(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
                                   total_new, k_new, v_new, new_offsets, start_pos, rot_k, rot_v,
-                                  clip_k, clip_v, (hipStream_t)stream));
+                                  clip_k, clip_v, method, (hipStream_t)stream));
+}
+
+int32_t oscar_rotate_quantize_append(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+    void* stream) {
+  return oscar_rotate_quantize_append_method(lay, pages, sinkwin, block_table, slot_ids, batch,
+                                             total_new, k_new, v_new, new_offsets, start_pos, rot_k,
+                                             rot_v, clip_k, clip_v, OSCAR_APPEND_AUTO, stream);
 }
 
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits) {

@@ -82,12 +82,16 @@ struct CacheGeom {
 };
 
 // Host launchers (each defined next to its kernel).
+// Append kernels (same bytes; speed differs): fp64 on the vector ALUs, or the matrix cores with
+// certification and exact recomputation.  Auto takes the matrix cores from kMatrixAppendRows rows.
+constexpr int kAppendAuto = 0, kAppendVector = 1, kAppendMatrix = 2;
+constexpr int kMatrixAppendRows = 256;
 hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int total_new, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* new_offsets, const int32_t* start_pos,
                          const float* rot_k, const float* rot_v, float clip_k, float clip_v,
-                         hipStream_t stream);
+                         int method, hipStream_t stream);
 
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,

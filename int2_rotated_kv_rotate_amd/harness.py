@@ -72,7 +72,7 @@ class GpuCache:
         self.rot_v = torch.from_numpy(p.rot_v).to(device)
 
     def append(self, k_rows: Sequence[np.ndarray], v_rows: Sequence[np.ndarray],
-               start: Sequence[int]):
+               start: Sequence[int], method: int = ops.APPEND_AUTO):
         """Append rows for every sequence b (bf16 bits [n_b][Hkv][128], n_b may be 0) at
         positions start[b], start[b]+1, ...  Lists are indexed by sequence."""
         counts = np.array([r.shape[0] for r in k_rows], dtype=np.int64)
@@ -86,7 +86,7 @@ class GpuCache:
             self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
             torch.from_numpy(offs).to(self.device),
             torch.from_numpy(np.asarray(start, dtype=np.int32)).to(self.device),
-            self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip)
+            self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip, method=method)
 
     def fill_context(self, chunk_tokens: int = 1 << 20, keep_tail: int = 0):
         """Append positions [0, L_b - 1) of every sequence (everything but the decoded token),

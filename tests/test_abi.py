@@ -86,6 +86,23 @@ def test_append_validation(lib):
     assert _append(lib, _layout(), total=0) == 0
 
 
+def test_append_method_validation(lib):
+    lay = _layout()
+
+    def call(method, **kw):
+        a = dict(pages=FAKE, batch=1)
+        a.update(kw)
+        return lib.oscar_rotate_quantize_append_method(
+            ctypes.byref(lay), a["pages"], FAKE, FAKE, None, a["batch"], 1, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, 0.95, 0.95, method, None)
+
+    assert call(3) == 1
+    assert call(-1) == 1
+    for m in (0, 1, 2):
+        assert call(m, pages=None) == 1       # every method validates before launching
+        assert call(m, batch=0) == 0          # nothing to do
+
+
 def _decode(lib, lay, **kw):
     a = dict(pages=FAKE, sinkwin=FAKE, bt=FAKE, slots=None, batch=1, hq=32, q=FAKE, lens=FAKE,
              rk=FAKE, sm=0.088, nw=0, ms=4, ws=FAKE, wsb=1 << 30)
