@@ -265,26 +265,30 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
 // slice that is at most 7u sum|terms| of dropped bits (u = 2^-24) and, since the small pieces
 // come first, about 4.1u sum|terms| of rounding; the two levels of fp32 additions and the
 // defined value's own rounding to fp32 add 3u.  So |y_mc - y| <= 14.1 u sum_i |x_i R_ij| <=
-// 14.1 u ||x|| ||R_.j||.  The kernel uses E = 64 u ||x|| ||R_.j|| (the fp32 norms scaled up by
-// 1.01 and 1.001) plus 2^-100 for flushed subnormals.
+// 14.1 u ||x|| ||R_.j||.  The kernel takes E = 64 u ||x|| ||R_.j|| plus 2^-100 for flushed
+// subnormals, computed 5% high so that y -+ E rounded to nearest still encloses [y - E, y + E].
 //
 // Certification (each output is a monotone function of the values it reads):
 //   * s16, z16 of a group: equal at the ends of the extremes' intervals [m - E, m + E], else
-//     every channel that can be the extreme (within 2E of it) is recomputed as defined, after
+//     every channel that can hold the group's extreme (within 2E of it) is recomputed, after
 //     which the extremes are the defined ones;
-//   * a code: code_of equal at y - E and y + E, else y is recomputed;
-//   * a BF16 copy (sink/window row): bf16 equal at y - E and y + E, else y is recomputed.
-// Recomputed values are the defined ones (fp64, ascending, one rounding) and certify exactly,
-// so every written byte equals the fp64 kernel's.
+//   * a code: with t = (y - z) * (1/s) (fp32), the defined t lies within
+//     mt = (E + (|y| + |z| + E) 2^-23) / s * 1.01 + 2^-19 of it (E, the rounding of y - z, the
+//     rounding of the defined division, of 1/s and of the product, for |t| < 4); the code is
+//     clamp(rint(t), 0, 3) when no boundary 1/2, 3/2, 5/2 lies within mt of t, else recomputed;
+//   * a BF16 copy (sink/window row): certified when bf16(y - E) == bf16(y + E), else recomputed.
+//
+// Recomputation reads R (fp32) from LDS, where the workgroup stages it once; four lanes share a
+// value and the midpoint argument below keeps the result the defined one.
 constexpr int kPTile = 64;
 constexpr int kPThreads = 512;
 constexpr int kXStride = kHeadDim + 8;   // bf16 per LDS row of x: 16-byte rows, skewed banks
 constexpr int kYStride = kHeadDim + 4;   // floats per LDS row of y
 constexpr int kExact = 0x80;             // s_code mark: s_y holds the defined value
-constexpr float kErrUnits = 64.0f;
-constexpr float kErrAbs = 0x1p-100f;
+constexpr float kErrScale = 64.0f * 0x1p-24f * 1.05f;
+constexpr float kErrAbs = 0x1p-100f * 1.05f;
 
-// The next fp32 value above / below a finite x (outward rounding of interval ends).
+// The next fp32 value above / below a finite x.
 __device__ __forceinline__ float up(float x) {
   if (x == 0.0f) return __uint_as_float(1u);
   const uint32_t b = __float_as_uint(x);
@@ -292,25 +296,84 @@ __device__ __forceinline__ float up(float x) {
 }
 __device__ __forceinline__ float down(float x) { return -up(-x); }
 
-// The defined rotated value of (row r, channel c): fp64 sum over i ascending, rounded to fp32.
-__device__ float defined_y(const uint16_t* xrow, const float* __restrict__ rot, int c) {
-  double acc = 0.0;
-  for (int i0 = 0; i0 < kHeadDim; i0 += 8) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + i0);
-    float rv[8];
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+constexpr int kRStride = kHeadDim + 1;   // floats per LDS row of R: column reads spread banks
+constexpr int kListCap = kPTile * kHeadDim;
+
+// Recompute the listed (row, channel) values as defined, four lanes per value: lane q sums the
+// products of inputs 32q .. 32q+31 in fp64, and the four partial sums are combined.  That sum
+// differs from the defined ascending one by at most 2 * 127 * 2^-53 sum|terms| <= 2^-45 ||x||
+// ||R_.c||; unless it lies that close to a midpoint between fp32 values both round to the same
+// fp32 value, and the rare value that close is summed again in ascending order.  `pass2` also
+// recodes the values (the defined formula); otherwise they are marked exact.
+// Called by all threads of the workgroup.
+__device__ void recompute_listed(const uint16_t* __restrict__ list, int n,
+                                 const float (*s_rot)[kRStride], const uint16_t (*s_x)[kXStride],
+                                 const float* s_nrm, const float* s_cng, float (*s_y)[kYStride],
+                                 uint8_t (*s_code)[kHeadDim], const float2 (*s_sz)[kGroups],
+                                 bool pass2) {
+  const int t = threadIdx.x, q = t & 3;
+  for (int k0 = 0; k0 < n; k0 += kPThreads / 4) {
+    const int k = k0 + (t >> 2);
+    const bool act = k < n;
+    const int it = act ? list[k] : 0;
+    const int r = it / kHeadDim, c = it % kHeadDim;
+    double part = 0.0;
+    if (act) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rv[e] = rot[(i0 + e) * kHeadDim + c];
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      for (int j = 0; j < 4; ++j) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(&s_x[r][32 * q + 8 * j]);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float xf = __uint_as_float(e & 1 ? xw[e / 2] & 0xFFFF0000u : xw[e / 2] << 16);
-      acc = __fma_rn((double)xf, (double)rv[e], acc);
+        for (int e = 0; e < 8; ++e) {
+          const float x = e & 1 ? bf16_hi(xw[e / 2]) : bf16_lo(xw[e / 2]);
+          part = __fma_rn((double)x, (double)s_rot[32 * q + 8 * j + e][c], part);
+        }
+      }
+    }
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    if (act && q == 0) {
+      float f = (float)part + 0.0f;   // the defined sum is never -0
+      const double tol = (double)s_nrm[r] * (double)s_cng[c / kGroup] * 0x1p-44;
+      const double m_lo = ((double)f + (double)down(f)) * 0.5;
+      const double m_hi = ((double)f + (double)up(f)) * 0.5;
+      if (fabs(part - m_lo) <= tol || fabs(part - m_hi) <= tol) {
+        double acc = 0.0;
+        for (int i = 0; i < kHeadDim; ++i)
+          acc = __fma_rn((double)bf16_to_f32(s_x[r][i]), (double)s_rot[i][c], acc);
+        f = (float)acc;
+      }
+      s_y[r][c] = f;
+      const float2 sz = s_sz[r][c / kGroup];
+      s_code[r][c] = pass2 ? (uint8_t)code_of(f, sz.x, sz.y) : (uint8_t)kExact;
     }
   }
-  return (float)acc;
 }
 
-__global__ __launch_bounds__(kPThreads, 4) void rotate_quantize_prefill_kernel(
+// Sequence of flattened new row n: the largest b < batch with off[b] <= n, searched upward
+// from `seq` (a sequence of an earlier row), galloping then bisecting; bounded loops.
+__device__ int advance_seq(const int32_t* __restrict__ off, int batch, int seq, int n) {
+  int lo = seq, hi;
+  int step = 1;
+  for (int i = 0; i < 32; ++i) {
+    hi = lo + step;
+    if (hi >= batch) { hi = batch; break; }
+    if (off[hi] > n) break;
+    lo = hi;
+    step <<= 1;
+  }
+  for (int i = 0; i < 32 && hi - lo > 1; ++i) {
+    const int mid = lo + (hi - lo) / 2;
+    if (off[mid] <= n) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
     int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -318,16 +381,17 @@ __global__ __launch_bounds__(kPThreads, 4) void rotate_quantize_prefill_kernel(
     const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
     float clip_v) {
 #pragma clang fp contract(off)
+  __shared__ float s_rot[kHeadDim][kRStride];  // R (fp32), for the A operands and recomputation
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kPTile][kXStride];
   __shared__ __attribute__((aligned(16))) float s_y[kPTile][kYStride];
   __shared__ __attribute__((aligned(16))) uint8_t s_code[kPTile][kHeadDim];
+  __shared__ float2 s_sz[kPTile][kGroups];     // (scale, zero) of each group, fp32
+  __shared__ uint16_t s_list[kListCap];        // (row, channel) to recompute: 128 r + c
   __shared__ RowInfo s_info[kPTile];
-  __shared__ float s_err[kPTile];          // 64 u ||x|| (x 1.01) per row
-  __shared__ float s_cn[kHeadDim];         // ||R_.j|| per output channel (rounded up)
-  __shared__ float s_cng[kGroups];         // the largest of them per group
-  __shared__ float2 s_sz[kPTile][kGroups]; // (scale, zero) as fp32
-  __shared__ int s_n[2];                   // lengths of the two recompute lists
-  __shared__ uint16_t s_list[kPTile * kHeadDim];  // (row, channel) to recompute: 128 r + c
+  __shared__ float s_err[kPTile];              // 64 u ||x|| per row, 5% high
+  __shared__ float s_nrm[kPTile];              // ||x|| per row (rounded up)
+  __shared__ float s_cng[kGroups];             // the largest ||R_.j|| of each group (rounded up)
+  __shared__ int s_n[2];                       // list lengths of the two passes
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -338,84 +402,120 @@ __global__ __launch_bounds__(kPThreads, 4) void rotate_quantize_prefill_kernel(
   const float clip = is_v ? clip_v : clip_k;
   const int m = lane & 15, kq = lane >> 4;
 
-  // A operands: lane (m, kq), slice s holds R[32s + 8kq + e][16w + m], e = 0..7, as 3 pieces.
-  v8bf ra[4][3];
+  // Stage R: all 8 float4 loads of a thread first, then the (unaligned-row) LDS stores.
   {
-    float ss = 0.f;
+    constexpr int kPer = kHeadDim * kHeadDim / 4 / kPThreads;  // 8
+    const float4* rot4 = reinterpret_cast<const float4*>(rot);
+    float4 rr[kPer];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float rv[8];
+    for (int k = 0; k < kPer; ++k) rr[k] = rot4[t + kPThreads * k];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rv[e] = rot[(32 * s + 8 * kq + e) * kHeadDim + 16 * wave + m];
-      uint16_t pc[3][8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float r0 = rv[e];
-        ss = fmaf(r0, r0, ss);
-        pc[0][e] = f32_to_bf16_rne(r0);
-        const float r1 = r0 - bf16_to_f32(pc[0][e]);
-        pc[1][e] = f32_to_bf16_rne(r1);
-        const float r2 = r1 - bf16_to_f32(pc[1][e]);
-        pc[2][e] = f32_to_bf16_rne(r2);
-      }
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        uint4 w;
-        w.x = pc[q][0] | ((uint32_t)pc[q][1] << 16);
-        w.y = pc[q][2] | ((uint32_t)pc[q][3] << 16);
-        w.z = pc[q][4] | ((uint32_t)pc[q][5] << 16);
-        w.w = pc[q][6] | ((uint32_t)pc[q][7] << 16);
-        ra[s][q] = __builtin_bit_cast(v8bf, w);
-      }
+    for (int k = 0; k < kPer; ++k) {
+      const int e = 4 * (t + kPThreads * k), i = e / kHeadDim, j = e % kHeadDim;
+      s_rot[i][j] = rr[k].x;
+      s_rot[i][j + 1] = rr[k].y;
+      s_rot[i][j + 2] = rr[k].z;
+      s_rot[i][j + 3] = rr[k].w;
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    if (kq == 0) s_cn[16 * wave + m] = __builtin_sqrtf(ss) * 1.001f;
   }
   __syncthreads();
-  if (t < kGroups) {
-    float cm = s_cn[kGroup * t];
-    for (int c = 1; c < kGroup; ++c) cm = fmaxf(cm, s_cn[kGroup * t + c]);
-    s_cng[t] = cm;
+  if (t < kHeadDim) {  // column norms (squared), parked in s_y before its first use
+    float ss = 0.f;
+    for (int i = 0; i < kHeadDim; ++i) ss = fmaf(s_rot[i][t], s_rot[i][t], ss);
+    s_y[0][t] = ss;
+  }
+  __syncthreads();
+  if (t < kGroups) {   // the largest per group, rounded up
+    float cm = 0.f;
+    for (int c = kGroup * t; c < kGroup * (t + 1); ++c) cm = fmaxf(cm, s_y[0][c]);
+    s_cng[t] = __builtin_sqrtf(cm) * 1.001f;
+  }
+  __syncthreads();
+
+  // A operands: lane (m, kq), slice s holds R[32s + 8kq + e][16w + m], e = 0..7, as 3 pieces.
+  v8bf ra[4][3];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint16_t pc[3][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r0 = s_rot[32 * s + 8 * kq + e][16 * wave + m];
+      pc[0][e] = f32_to_bf16_rne(r0);
+      const float r1 = r0 - bf16_to_f32(pc[0][e]);
+      pc[1][e] = f32_to_bf16_rne(r1);
+      pc[2][e] = f32_to_bf16_rne(r1 - bf16_to_f32(pc[1][e]));
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      uint4 w;
+      w.x = pc[q][0] | ((uint32_t)pc[q][1] << 16);
+      w.y = pc[q][2] | ((uint32_t)pc[q][3] << 16);
+      w.z = pc[q][4] | ((uint32_t)pc[q][5] << 16);
+      w.w = pc[q][6] | ((uint32_t)pc[q][7] << 16);
+      ra[s][q] = __builtin_bit_cast(v8bf, w);
+    }
   }
 
   const int ntiles = (total_new + kPTile - 1) / kPTile;
+  const bool has_store = sinkwin != nullptr;
+
+  // Software pipeline over the tiles: while tile k is processed, its successor's input rows are
+  // in flight into registers, and threads t < 64 look up the successor's row placements in
+  // stages (one dependent load per stage, each consumed a phase later).
+  auto load_rows = [&](int tl, uint4& a0, uint4& a1) {
+    const int r = t >> 3, q = t & 7, n = tl * kPTile + r;
+    a0 = uint4{0, 0, 0, 0};
+    a1 = uint4{0, 0, 0, 0};
+    if (tl < ntiles && n < total_new) {
+      const uint4* rp = reinterpret_cast<const uint4*>(src + ((size_t)n * g.hkv + h) * kHeadDim);
+      a0 = rp[q];
+      a1 = rp[q + 8];
+    }
+  };
+  uint4 u0, u1;
+  load_rows(blockIdx.x, u0, u1);
+  int seq = 0;                         // sequence of this thread's row (t < 64)
+  RowInfo info_next{-1, 0, -1};
+  if (t < kPTile && blockIdx.x < ntiles && (int)blockIdx.x * kPTile + t < total_new) {
+    seq = row_to_seq(new_offsets, batch, blockIdx.x * kPTile + t);
+    info_next = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store,
+                         blockIdx.x * kPTile + t, h, is_v);
+  }
+
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int row0 = tile * kPTile;
     const int nrows = min(kPTile, total_new - row0);
+    const int nt = tile + gridDim.x;   // the successor tile
+    const int n_next = nt * kPTile + t;
+    const bool look = t < kPTile && nt < ntiles && n_next < total_new;
 
     // Input rows into LDS (8 threads per row, 2 x 16 bytes each), their norms, placements.
     {
       const int r = t >> 3, q = t & 7;
-      uint4 u0 = {0, 0, 0, 0}, u1 = {0, 0, 0, 0};
-      if (r < nrows) {
-        const uint4* rp = reinterpret_cast<const uint4*>(src + ((size_t)(row0 + r) * g.hkv + h) * kHeadDim);
-        u0 = rp[q];
-        u1 = rp[q + 8];
-      }
       *reinterpret_cast<uint4*>(&s_x[r][8 * q]) = u0;
       *reinterpret_cast<uint4*>(&s_x[r][8 * q + 64]) = u1;
       const uint32_t xw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-      float ss = 0.f;
+      double ss = 0.0;   // fp64: no underflow for rows of subnormal values
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a = __uint_as_float(xw[k] << 16), b = __uint_as_float(xw[k] & 0xFFFF0000u);
-        ss = fmaf(a, a, ss);
-        ss = fmaf(b, b, ss);
+        ss = __fma_rn((double)bf16_lo(xw[k]), (double)bf16_lo(xw[k]), ss);
+        ss = __fma_rn((double)bf16_hi(xw[k]), (double)bf16_hi(xw[k]), ss);
       }
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
-      if (q == 0) s_err[r] = kErrUnits * 0x1p-24f * 1.01f * __builtin_sqrtf(ss);
-      if (t < kPTile) {
-        RowInfo info{-1, 0, -1};
-        if (t < nrows)
-          info = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos,
-                          sinkwin != nullptr, row0 + t, h, is_v);
-        s_info[t] = info;
+      if (q == 0) {
+        const float nrm = (float)__builtin_sqrt(ss) * (1.0f + 0x1p-20f);
+        s_nrm[r] = nrm;
+        s_err[r] = kErrScale * nrm;
       }
+      if (t < kPTile) s_info[t] = info_next;
       if (t == 0) s_n[0] = s_n[1] = 0;
     }
+    load_rows(nt, u0, u1);
+    // placement stage 1: is the successor's row still in the same sequence?
+    int off_up = 0;
+    if (look && seq + 1 < batch) off_up = new_offsets[seq + 1];
     __syncthreads();
 
     // y on the matrix cores: channels 16w .. 16w+15 of the tile's 64 rows.
@@ -440,12 +540,22 @@ __global__ __launch_bounds__(kPThreads, 4) void rotate_quantize_prefill_kernel(
     }
     __syncthreads();
 
+    // placement stage 2: the successor row's sequence, then its per-sequence values
+    int first = 0, next_first = 0, sp = 0, slot = 0;
+    if (look) {
+      if (seq + 1 < batch && off_up <= n_next) seq = advance_seq(new_offsets, batch, seq + 1, n_next);
+      first = new_offsets[seq];
+      next_first = new_offsets[seq + 1];
+      sp = start_pos[seq];
+      slot = slot_ids ? slot_ids[seq] : seq;
+    }
+
     // Thread -> (row r, group gi, half of the group's 32 channels) for the group passes.
     const int r = t >> 3, gi = (t >> 1) & 3, half = t & 1;
     const int c0 = gi * kGroup + 16 * half;
     const float er = s_err[r];
 
-    // Pass 1: certify each group's scale and zero; if they are not certain, queue every channel
+    // Pass 1: certify each group's scale and zero; if they are not certain, flag every channel
     // that can hold the group's maximum or minimum.
     {
       float yv[16];
@@ -462,108 +572,152 @@ __global__ __launch_bounds__(kPThreads, 4) void rotate_quantize_prefill_kernel(
       }
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mn = fminf(mn, __shfl_xor(mn, 1));
-      const float cmax = s_cng[gi];
-      const float E = up(er * cmax + kErrAbs);
+      const float E = er * s_cng[gi] + kErrAbs;
       _Float16 s_hi, z_hi, s_lo, z_lo;
-      group_params(up(mx + E), down(mn - E), clip, s_hi, z_lo);
-      group_params(down(mx - E), up(mn + E), clip, s_lo, z_hi);
+      group_params(mx + E, mn - E, clip, s_hi, z_lo);
+      group_params(mx - E, mn + E, clip, s_lo, z_hi);
       const bool sure = __builtin_bit_cast(uint16_t, s_hi) == __builtin_bit_cast(uint16_t, s_lo) &&
                         __builtin_bit_cast(uint16_t, z_hi) == __builtin_bit_cast(uint16_t, z_lo);
       *reinterpret_cast<uint4*>(&s_code[r][c0]) = uint4{0, 0, 0, 0};
       if (!sure && r < nrows) {
-        const float top = down(mx - 2.0f * E), bot = up(mn + 2.0f * E);
+        const float top = mx - 2.0f * E, bot = mn + 2.0f * E;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
           if (yv[c] >= top || yv[c] <= bot) s_list[atomicAdd(&s_n[0], 1)] = (uint16_t)(kHeadDim * r + c0 + c);
       }
     }
     __syncthreads();
-    {
-      const int n = s_n[0];
-      for (int k = t; k < n; k += kPThreads) {
-        const int it = s_list[k], rr = it / kHeadDim, c = it % kHeadDim;
-        s_y[rr][c] = defined_y(&s_x[rr][0], rot, c);
-        s_code[rr][c] = kExact;
-      }
-    }
+    recompute_listed(s_list, s_n[0], s_rot, s_x, s_nrm, s_cng, s_y, s_code, s_sz, false);
     __syncthreads();
 
-    // Pass 2: the group's scale and zero (now the defined ones), then every code and BF16 copy,
-    // queueing the values the bound cannot certify.
+    // placement stage 3: page of the successor row
+    int pos = 0, page = -1;
+    if (look) {
+      pos = sp + (n_next - first);
+      const int lp = pos / kPage;
+      if (pos >= 0 && lp < g.max_pages) page = block_table[(size_t)seq * g.max_pages + lp];
+    }
+
+    // Pass 2: the group's scale and zero (now the defined ones), every code and BF16 copy; flag
+    // what the bound cannot certify (E taken for the group's largest column norm).
     {
-      float yv[16];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0 + 4 * k]);
-        yv[4 * k] = a.x; yv[4 * k + 1] = a.y; yv[4 * k + 2] = a.z; yv[4 * k + 3] = a.w;
+      float mx, mn;
+      {
+        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0]);
+        mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+        mn = fminf(fminf(a.x, a.y), fminf(a.z, a.w));
       }
-      const uint4 mk = *reinterpret_cast<const uint4*>(&s_code[r][c0]);
-      const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
-      float mx = yv[0], mn = yv[0];
 #pragma unroll
-      for (int c = 1; c < 16; ++c) {
-        mx = fmaxf(mx, yv[c]);
-        mn = fminf(mn, yv[c]);
+      for (int k = 1; k < 4; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0 + 4 * k]);
+        mx = fmaxf(mx, fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)));
+        mn = fminf(mn, fminf(fminf(a.x, a.y), fminf(a.z, a.w)));
       }
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mn = fminf(mn, __shfl_xor(mn, 1));
       _Float16 s16, z16;
       group_params(mx, mn, clip, s16, z16);
       const float sc = (float)s16, z = (float)z16;
+      const float inv = sc != 0.0f ? 1.0f / sc : 0.0f;
       const RowInfo info = s_info[r];
       if (half == 0) {
         s_sz[r][gi] = make_float2(sc, z);
         if (r < nrows && info.rec >= 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
       }
       const bool bf = info.sw >= 0;
+      const float Eg = er * s_cng[gi] + kErrAbs;
+      const uint4 mk = *reinterpret_cast<const uint4*>(&s_code[r][c0]);
+      const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
       uint32_t cw[4] = {0, 0, 0, 0};
+      unsigned flagged = 0;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const float y = yv[c];
-        int code;
-        bool ok = true;
-        if (((mw[c / 4] >> (8 * (c % 4))) & 0xFF) == kExact) {
-          code = code_of(y, sc, z);
-        } else {
-          const float E = up(er * s_cn[c0 + c] + kErrAbs);
-          const float ylo = down(y - E), yhi = up(y + E);
-          code = code_of(ylo, sc, z);
-          ok = code == code_of(yhi, sc, z);
-          if (bf) ok = ok && f32_to_bf16_rne(ylo) == f32_to_bf16_rne(yhi);
+      for (int k = 0; k < 4; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0 + 4 * k]);
+        const float yk[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = yk[i];
+          const float E = ((mw[k] >> (8 * i)) & 0xFF) == kExact ? 0.0f : Eg;
+          // t within mt of the defined t (see above); the code is certain when no boundary
+          // k + 1/2 lies within mt of t
+          const float tq = (y - z) * inv;
+          const float mt = (E + (fabsf(y) + fabsf(z) + E) * 0x1p-23f) * inv * 1.01f + 0x1p-19f;
+          const float dist = fminf(fminf(fabsf(tq - 0.5f), fabsf(tq - 1.5f)), fabsf(tq - 2.5f));
+          bool ok = dist > mt;
+          if (bf) ok = ok && f32_to_bf16_rne(y - E) == f32_to_bf16_rne(y + E);
+          const int code = (int)fminf(fmaxf(__builtin_rintf(tq), 0.0f), 3.0f);
+          cw[k] |= (uint32_t)code << (8 * i);
+          flagged |= (ok ? 0u : 1u) << (4 * k + i);
         }
-        cw[c / 4] |= (uint32_t)code << (8 * (c % 4));
-        if (!ok && r < nrows) s_list[atomicAdd(&s_n[1], 1)] = (uint16_t)(kHeadDim * r + c0 + c);
       }
       *reinterpret_cast<uint4*>(&s_code[r][c0]) = uint4{cw[0], cw[1], cw[2], cw[3]};
+      if (r < nrows)
+        while (flagged) {
+          const int c = __builtin_ctz(flagged);
+          flagged &= flagged - 1u;
+          s_list[atomicAdd(&s_n[1], 1)] = (uint16_t)(kHeadDim * r + c0 + c);
+        }
     }
     __syncthreads();
-    {
-      const int n = s_n[1];
-      for (int k = t; k < n; k += kPThreads) {
-        const int it = s_list[k], rr = it / kHeadDim, c = it % kHeadDim;
-        const float y = defined_y(&s_x[rr][0], rot, c);
-        const float2 sz = s_sz[rr][c / kGroup];
-        s_y[rr][c] = y;
-        s_code[rr][c] = (uint8_t)code_of(y, sz.x, sz.y);
-      }
-    }
+    recompute_listed(s_list, s_n[1], s_rot, s_x, s_nrm, s_cng, s_y, s_code, s_sz, true);
     __syncthreads();
 
-    // Pack the codes into the records; BF16 copies of sink/window rows.
-    if (!is_v) {
-      const int d = t & 7;
-      const RowInfo info = s_info[r];
-      if (r < nrows && info.rec >= 0) store_k_word(pages, info, s_code[r], d);
+    // placement stage 4: the successor row's record and sink/window row
+    if (look) {
+      RowInfo info{-1, 0, -1};
+      if (pos >= 0 && page >= 0 && page < g.num_pages && pos / kPage < g.max_pages) {
+        info.rec = ((long long)page * g.hkv + h) * kRecord;
+        info.slot_in_page = pos % kPage;
+      }
+      const int new_len = sp + (next_first - first);
+      int row = -1;
+      if (pos >= 0 && pos < g.num_sink) row = pos;
+      else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
+        row = g.num_sink + pos % g.window;
+      if (row >= 0 && has_store && slot >= 0 && slot < g.num_slots)
+        info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
+                  (is_v ? kHeadDim : 0);
+      info_next = info;
     } else {
+      info_next = RowInfo{-1, 0, -1};
+    }
+
+    // Pack the codes into the records; BF16 copies of sink/window rows.
+    {
+      const int q = t & 7;
+      const RowInfo info = s_info[r];
+      if (r < nrows && info.rec >= 0 && !is_v) {
+        const uint4 cv = *reinterpret_cast<const uint4*>(&s_code[r][16 * q]);
+        const uint32_t cwd[4] = {cv.x, cv.y, cv.z, cv.w};
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t b = cwd[k];  // four codes, one per byte
+          const uint32_t packed = (b & 3u) | ((b >> 6) & 0xCu) | ((b >> 12) & 0x30u) | ((b >> 18) & 0xC0u);
+          w |= packed << (8 * k);
+        }
+        *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes +
+                                     8 * (16 * (q % 4) + info.slot_in_page) + 4 * (q / 4)) = w;
+      }
+      if (r < nrows && info.sw >= 0) {
+        uint32_t o[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 a = *reinterpret_cast<const float4*>(&s_y[r][16 * q + 4 * k]);
+          o[2 * k] = f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
+          o[2 * k + 1] = f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(sinkwin + info.sw + 16 * q);
+        dst[0] = uint4{o[0], o[1], o[2], o[3]};
+        dst[1] = uint4{o[4], o[5], o[6], o[7]};
+      }
+    }
+    if (is_v) {
       for (int e = t; e < kPTile * 16; e += kPThreads) {
         const int rr = e >> 4, c16 = e & 15;
         const RowInfo info = s_info[rr];
         if (rr < nrows && info.rec >= 0) store_v_half(pages, info, s_code[rr], c16);
       }
-    }
-    for (int e = t; e < kPTile * kHeadDim; e += kPThreads) {
-      const int rr = e / kHeadDim, c = e % kHeadDim;
-      if (rr < nrows && s_info[rr].sw >= 0) sinkwin[s_info[rr].sw + c] = f32_to_bf16_rne(s_y[rr][c]);
     }
     __syncthreads();
   }
@@ -585,9 +739,10 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    // two resident workgroups per CU over the 2 * Hkv (KV head, K|V) pairs
+    // one resident workgroup per CU (R and the tile take most of the LDS) over the 2 * Hkv
+    // (KV head, K|V) pairs
     const int tiles = (total_new + kPTile - 1) / kPTile;
-    const int per_pair = max(1, min(tiles, (2 * cus + 2 * g.hkv - 1) / (2 * g.hkv)));
+    const int per_pair = max(1, min(tiles, (cus + 2 * g.hkv - 1) / (2 * g.hkv)));
     hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_pair, g.hkv, 2), dim3(kPThreads), 0,
                        stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
                        v_new, new_offsets, start_pos, rot_k, rot_v, clip_k, clip_v);

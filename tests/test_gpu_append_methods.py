@@ -13,6 +13,7 @@ Cases:
   * special rows with a seeded orthogonal rotation: rows along a column of R (every other
     rotated value is tiny next to ||x||, so scales, zeros, codes and BF16 copies are uncertain
     and recomputed), zero rows, subnormal rows, a huge dynamic range within a row;
+  * groups with max == -min (a code threshold exactly at zero), one-signed and constant groups;
   * the full prefill shape: 64 sequences x 2048 new tokens at the end of 16K-32K contexts
     (GPU against GPU: 2.1 million rows are beyond the oracle's seconds).
 """
@@ -141,6 +142,31 @@ def test_special_rows():
     ks = [_special_rows(rng, p.rot_k, int(L)) for L in p.lens]
     vs = [_special_rows(rng, p.rot_v, int(L)) for L in p.lens]
     _check("special_rows", p, ks, vs, [0] * w.batch)
+
+
+def test_symmetric_groups():
+    """Identity rotation, rows whose every 32-channel group has max == -min (so a code threshold
+    sits exactly at zero, where fp32 values are densest), plus rows whose groups are one-signed
+    or constant."""
+    w = W.scaled(W.WORKLOADS["qwen3_4b"], name="append_symmetric", batch=2, ctx=520, ctx_min=400)
+    eye = np.broadcast_to(np.eye(128), (w.num_kv_heads, 128, 128)).copy()
+    p = H.make_problem(w, rot_k=eye, rot_v=eye)
+    rng = np.random.default_rng(13)
+
+    def rows(n):
+        x = rng.uniform(-1.0, 1.0, size=(n, w.num_kv_heads, 4, 32)).astype(np.float32)
+        a = np.float32(2.0) ** rng.integers(-8, 8, size=(n, w.num_kv_heads, 4, 1)).astype(np.float32)
+        x *= a
+        kind = rng.integers(0, 4, size=(n, w.num_kv_heads, 4))
+        x[..., 0] = np.where(kind < 2, a[..., 0], x[..., 0])      # max = a, min = -a
+        x[..., 1] = np.where(kind < 2, -a[..., 0], x[..., 1])
+        x = np.where((kind == 2)[..., None], np.abs(x), x)        # one-signed group
+        x = np.where((kind == 3)[..., None], a, x)                # constant group
+        return W.to_bf16_bits(x.reshape(n, w.num_kv_heads, 128))
+
+    ks = [rows(int(L)) for L in p.lens]
+    vs = [rows(int(L)) for L in p.lens]
+    _check("symmetric_groups", p, ks, vs, [0] * w.batch)
 
 
 def test_chunked_appends_with_window_rows():
