@@ -25,9 +25,6 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 16;
-constexpr int kThreads = 256;
-
 // Keeps the compiler from fusing an fp32 result into a following conversion (it would
 // otherwise turn fp16(c * mn) into one single-rounding mixed-precision FMA).
 __device__ __forceinline__ float materialize(float x) {
@@ -130,9 +127,14 @@ __device__ __forceinline__ void store_v_half(uint8_t* pages, const RowInfo& info
 
 // ------------------------------------------------------------------ exact fp64 (few rows)
 //
-// One workgroup = 16 consecutive new rows of one (KV head, K|V).  The 64 KiB rotation matrix is
-// staged in LDS once per workgroup; each thread accumulates 2 rows x 4 output channels in fp64.
+// One workgroup = ROWS consecutive new rows of one (KV head, K|V).  The 64 KiB rotation matrix
+// is staged in LDS once per workgroup.  ROWS = 16: each thread accumulates 2 rows x 4 output
+// channels in fp64; ROWS = 4 (small appends, e.g. one decoded token per sequence, so that the
+// launch spreads over more CUs): each thread accumulates 1 row x 2 channels.
 
+constexpr int kThreads = 256;
+
+template <int ROWS>
 __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
     CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
@@ -141,20 +143,21 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
     const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
     float clip_v) {
 #pragma clang fp contract(off)
+  static_assert(ROWS == 4 || ROWS == 16, "row blocking");
   __shared__ float4 s_rot[kHeadDim * kHeadDim / 4];   // R[i][j], row-major, 64 KiB
-  __shared__ float s_x[kRows][kHeadDim];              // input rows (bf16 widened)
-  __shared__ float s_y[kRows][kHeadDim + 1];          // rotated rows (fp32)
-  __shared__ uint8_t s_code[kRows][kHeadDim];
-  __shared__ RowInfo s_info[kRows];
+  __shared__ float s_x[ROWS][kHeadDim];               // input rows (bf16 widened)
+  __shared__ float s_y[ROWS][kHeadDim + 1];           // rotated rows (fp32)
+  __shared__ uint8_t s_code[ROWS][kHeadDim];
+  __shared__ RowInfo s_info[ROWS];
 
   const int t = threadIdx.x;
-  const int row0 = blockIdx.x * kRows;
+  const int row0 = blockIdx.x * ROWS;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
   const float* rot = (is_v ? rot_v : rot_k) + (size_t)h * kHeadDim * kHeadDim;
   const uint16_t* src = is_v ? v_new : k_new;
   const float clip = is_v ? clip_v : clip_k;
-  const int nrows = min(kRows, total_new - row0);
+  const int nrows = min(ROWS, total_new - row0);
 
   // Stage R (fp32) and the rows: all 16 loads of a thread are issued before the first LDS
   // store, so staging costs one memory latency.
@@ -167,11 +170,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
 #pragma unroll
     for (int k = 0; k < kPer; ++k) s_rot[t + kThreads * k] = rr[k];
   }
-  for (int i = t; i < kRows * kHeadDim; i += kThreads) {
+  for (int i = t; i < ROWS * kHeadDim; i += kThreads) {
     int r = i / kHeadDim, c = i % kHeadDim;
     s_x[r][c] = r < nrows ? bf16_to_f32(src[((size_t)(row0 + r) * g.hkv + h) * kHeadDim + c]) : 0.f;
   }
-  if (t < kRows) {
+  if (t < ROWS) {
     RowInfo info{-1, 0, -1};
     if (t < nrows)
       info = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, sinkwin != nullptr,
@@ -180,8 +183,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
   }
   __syncthreads();
 
-  // y = x . R: thread -> rows {2*rp, 2*rp+1}, channels 4*jq .. 4*jq+3; fp64, i ascending.
-  {
+  // y = x . R in fp64, i ascending (products are exact in fp64: fma == mul then add).
+  if constexpr (ROWS == 16) {
+    // thread -> rows {2*rp, 2*rp+1}, channels 4*jq .. 4*jq+3
     const int rp = t / 32, jq = t % 32;
     const int r0 = 2 * rp, r1 = 2 * rp + 1;
     double a0[4] = {0.0, 0.0, 0.0, 0.0}, a1[4] = {0.0, 0.0, 0.0, 0.0};
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
       const double rr[4] = {(double)rv.x, (double)rv.y, (double)rv.z, (double)rv.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        a0[k] = __fma_rn(x0, rr[k], a0[k]);   // product exact in fp64: same as mul then add
+        a0[k] = __fma_rn(x0, rr[k], a0[k]);
         a1[k] = __fma_rn(x1, rr[k], a1[k]);
       }
     }
@@ -201,30 +205,46 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
       s_y[r0][4 * jq + k] = (float)a0[k];
       s_y[r1][4 * jq + k] = (float)a1[k];
     }
+  } else {
+    // thread -> row t / 64, channels 2*jp, 2*jp + 1
+    const int rr = t / 64, jp = t % 64;
+    const float2* rot2 = reinterpret_cast<const float2*>(s_rot);
+    double a[2] = {0.0, 0.0};
+#pragma unroll 8
+    for (int i = 0; i < kHeadDim; ++i) {
+      const double x = (double)s_x[rr][i];
+      const float2 rv = rot2[i * (kHeadDim / 2) + jp];
+      a[0] = __fma_rn(x, (double)rv.x, a[0]);
+      a[1] = __fma_rn(x, (double)rv.y, a[1]);
+    }
+    s_y[rr][2 * jp] = (float)a[0];
+    s_y[rr][2 * jp + 1] = (float)a[1];
   }
   __syncthreads();
 
-  // Group parameters and codes: thread -> (row, group, quarter of the group's 32 channels).
+  // Group parameters and codes: SUB threads per (row, group), adjacent lanes.
   {
-    const int r = t >> 4, gi = (t >> 2) & 3, sub = t & 3;
-    const int c0 = gi * kGroup + 8 * sub;
+    constexpr int kSub = kThreads / (ROWS * kGroups);   // 4 (ROWS = 16) or 16 (ROWS = 4)
+    constexpr int kPerSub = kGroup / kSub;               // 8 or 2 channels each
+    const int r = t / (kSub * kGroups), gi = (t / kSub) % kGroups, sub = t % kSub;
+    const int c0 = gi * kGroup + kPerSub * sub;
     float mx = s_y[r][c0], mn = mx;
 #pragma unroll
-    for (int c = 1; c < 8; ++c) {
+    for (int c = 1; c < kPerSub; ++c) {
       const float v = s_y[r][c0 + c];
       mx = fmaxf(mx, v);
       mn = fminf(mn, v);
     }
-    // the four quarters of the group are adjacent lanes
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mn = fminf(mn, __shfl_xor(mn, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    mn = fminf(mn, __shfl_xor(mn, 2));
+#pragma unroll
+    for (int o = 1; o < kSub; o <<= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+      mn = fminf(mn, __shfl_xor(mn, o));
+    }
     _Float16 s16, z16;
     group_params(mx, mn, clip, s16, z16);
     const float sc = (float)s16, z = (float)z16;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_code[r][c0 + c] = (uint8_t)code_of(s_y[r][c0 + c], sc, z);
+    for (int c = 0; c < kPerSub; ++c) s_code[r][c0 + c] = (uint8_t)code_of(s_y[r][c0 + c], sc, z);
     const RowInfo info = s_info[r];
     if (sub == 0 && r < nrows && info.rec >= 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
   }
@@ -232,19 +252,19 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
 
   // Pack codes into the record.
   if (!is_v) {
-    if (t < kRows * 8) {
+    if (t < ROWS * 8) {
       const int r = t / 8, d = t % 8;
       const RowInfo info = s_info[r];
       if (r < nrows && info.rec >= 0) store_k_word(pages, info, s_code[r], d);
     }
-  } else {
+  } else if (t < ROWS * 16) {
     const int r = t / 16, c16 = t % 16;
     const RowInfo info = s_info[r];
     if (r < nrows && info.rec >= 0) store_v_half(pages, info, s_code[r], c16);
   }
 
   // BF16 sink/window rows.
-  for (int i = t; i < kRows * kHeadDim; i += kThreads) {
+  for (int i = t; i < ROWS * kHeadDim; i += kThreads) {
     const int r = i / kHeadDim, c = i % kHeadDim;
     if (r < nrows && s_info[r].sw >= 0) sinkwin[s_info[r].sw + c] = f32_to_bf16_rne(s_y[r][c]);
   }
@@ -748,10 +768,18 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                        v_new, new_offsets, start_pos, rot_k, rot_v, clip_k, clip_v);
     return hipGetLastError();
   }
-  dim3 grid((total_new + kRows - 1) / kRows, g.hkv, 2);
-  hipLaunchKernelGGL(rotate_quantize_append_kernel, grid, dim3(kThreads), 0, stream, g, pages,
-                     sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
-                     start_pos, rot_k, rot_v, clip_k, clip_v);
+  // few rows: 4 per workgroup, so that the launch covers more CUs
+  if (total_new <= 64 * 16) {
+    dim3 grid((total_new + 3) / 4, g.hkv, 2);
+    hipLaunchKernelGGL(rotate_quantize_append_kernel<4>, grid, dim3(kThreads), 0, stream, g, pages,
+                       sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
+                       start_pos, rot_k, rot_v, clip_k, clip_v);
+  } else {
+    dim3 grid((total_new + 15) / 16, g.hkv, 2);
+    hipLaunchKernelGGL(rotate_quantize_append_kernel<16>, grid, dim3(kThreads), 0, stream, g, pages,
+                       sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
+                       start_pos, rot_k, rot_v, clip_k, clip_v);
+  }
   return hipGetLastError();
 }
 

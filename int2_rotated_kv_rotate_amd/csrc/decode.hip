@@ -770,13 +770,20 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   const int32_t* pstart = plan + kPlanHeader;
   const int32_t* npg = pstart + B;
   const int32_t* pglo = npg + B;
-  // sequence of the run's first page: the last b with pstart[b] <= run0 (it has pages)
+  // sequence of the run's first page: the last b with pstart[b] <= run0 (it has pages).  The
+  // wave probes 64 evenly spaced entries per round (pstart is non-decreasing, so the lanes that
+  // pass form a prefix): one round for up to 64 sequences, two for up to 4096.
   int b = 0;
   {
-    int hi_b = B;
-    while (hi_b - b > 1) {
-      const int mid = (b + hi_b) >> 1;
-      if (pstart[mid] <= run0) b = mid; else hi_b = mid;
+    int len = B;   // the answer lies in [b, b + len); pstart[b] <= run0
+    while (len > 1) {
+      const int step = (len + 63) / 64;
+      const bool probe = lane * step < len;
+      const int v = pstart[probe ? b + lane * step : b];   // every index inside [b, b + len)
+      const bool ok = probe && v <= run0;
+      const int last = 63 - __clzll(__ballot(ok));   // lane 0 always passes
+      b += last * step;
+      len = min(step, len - last * step);
     }
   }
   const int G = hq / g.hkv;

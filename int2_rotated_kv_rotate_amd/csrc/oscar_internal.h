@@ -127,7 +127,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // Sequence index of flattened row n, given prefix offsets off[0..batch] (binary search).
 __device__ __forceinline__ int row_to_seq(const int32_t* off, int batch, int n) {
-  int lo = 0, hi = batch;  // find largest b with off[b] <= n
+  // find the largest b < batch with off[b] <= n.  First guess b = n (one new row per sequence,
+  // as in decode): two independent loads settle it; otherwise bisect.
+  const int g = min(n, batch - 1);
+  const int og = off[g], og1 = off[g + 1];
+  if (og <= n && (g == batch - 1 || og1 > n)) return g;
+  int lo = 0, hi = batch;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
     if (off[mid] <= n) lo = mid; else hi = mid;
