@@ -129,12 +129,14 @@ def cpu_baseline(p, target_s: float):
 
 def time_scrubbed(fn, n: int, scrub):
     """Median (and p10, p90) of n launches of fn, each timed with an event pair on the current
-    stream, with the whole last-level cache overwritten before each launch (scrub)."""
+    stream, with the whole last-level cache evicted before each launch by reading the 1 GiB
+    scrub buffer (a read leaves clean lines: no write-backs land in the timed launch)."""
     import torch
     stream = torch.cuda.current_stream()
     ts = []
+    sink = torch.empty((), dtype=scrub.dtype, device=scrub.device)
     for _ in range(n):
-        scrub.zero_()
+        torch.sum(scrub, dim=None, out=sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         fn()
@@ -155,7 +157,7 @@ def int2_vs_bf16(n_iter: int):
     from int2_rotated_kv_rotate_amd import harness as H
     from int2_rotated_kv_rotate_amd import workload as W
 
-    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
     res = {}
 
     def attn_bytes(w, p, bf16):

@@ -93,62 +93,86 @@ __global__ __launch_bounds__(64) void bf16_decode_kernel(
   for (int nb = 0; nb < 8; ++nb) acc[nb] = (v4f){0.f, 0.f, 0.f, 0.f};
   float mrun = kNegBig, lsum = 0.f;
   const int32_t* bt = block_table + (size_t)b * g.max_pages;
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const int page = bt[pg];
-    if (page < 0 || page >= g.num_pages) continue;
-    const uint16_t* base = pages + ((size_t)page * g.hkv + h) * kBf16PageElems;
+  // Software pipeline: page pg is computed while page pg + 1's K and V are in flight and page
+  // pg + 2's id is being fetched.  An id outside the pool skips its page.
+  auto valid_id = [&](int id) { return id >= 0 && id < g.num_pages; };
+  auto fetch = [&](int id, uint4 (&kk)[4], uint2 (&vv)[8]) {
+    const uint16_t* base = pages + ((size_t)id * g.hkv + h) * kBf16PageElems;
     const uint4* krow = reinterpret_cast<const uint4*>(base + c16 * kHeadDim + 32 * kq);
-    const uint4 k0 = krow[0], k1 = krow[1], k2 = krow[2], k3 = krow[3];
-    const uint32_t kw[16] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w,
-                             k2.x, k2.y, k2.z, k2.w, k3.x, k3.y, k3.z, k3.w};
-    v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const v4s ka = (v4s){(short)(kw[2 * kc] & 0xFFFF), (short)(kw[2 * kc] >> 16),
-                           (short)(kw[2 * kc + 1] & 0xFFFF), (short)(kw[2 * kc + 1] >> 16)};
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qb[kc], s, 0, 0, 0);
-    }
-    float lg[4];
-    float tm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pos = pg * kPage + 4 * kq + i;
-      lg[i] = pos < L ? s[i] * sm_log2 : -INFINITY;
-      tm = fmaxf(tm, lg[i]);
-    }
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
-    const float mnew = fmaxf(mrun, tm);
-    if (__any(mnew > mrun)) {
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      lsum *= alpha;
-      // accumulator rows are query heads 4*kq + i: fetch their alphas from lanes 4*kq + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * kq + i);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[nb][i] *= ai;
-      }
-      mrun = mnew;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = lg[i] != -INFINITY ? __builtin_amdgcn_exp2f(lg[i] - mrun) : 0.f;
-      lsum += p[i];
-    }
-    uint32_t h01, h23, l01, l23;
-    split_bf16(p, h01, h23, l01, l23);
-    const v4s ahi = (v4s){(short)(h01 & 0xFFFF), (short)(h01 >> 16), (short)(h23 & 0xFFFF), (short)(h23 >> 16)};
-    const v4s alo = (v4s){(short)(l01 & 0xFFFF), (short)(l01 >> 16), (short)(l23 & 0xFFFF), (short)(l23 >> 16)};
+    for (int k = 0; k < 4; ++k) kk[k] = krow[k];
     const uint16_t* vt = base + kPage * kHeadDim;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const uint2 vv = *reinterpret_cast<const uint2*>(vt + (16 * nb + c16) * kPage + 4 * kq);
-      const v4s vb = (v4s){(short)(vv.x & 0xFFFF), (short)(vv.x >> 16), (short)(vv.y & 0xFFFF), (short)(vv.y >> 16)};
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb, acc[nb], 0, 0, 0);
+    for (int nb = 0; nb < 8; ++nb)
+      vv[nb] = *reinterpret_cast<const uint2*>(vt + (16 * nb + c16) * kPage + 4 * kq);
+  };
+  uint4 kc[4] = {};
+  uint2 vc[8] = {};
+  int id_cur = pg0 < pg1 ? bt[pg0] : -1;
+  int id_next = pg0 + 1 < pg1 ? bt[pg0 + 1] : -1;
+  if (valid_id(id_cur)) fetch(id_cur, kc, vc);
+  for (int pg = pg0; pg < pg1; ++pg) {
+    uint4 kn[4] = {};
+    uint2 vn[8] = {};
+    if (pg + 1 < pg1 && valid_id(id_next)) fetch(id_next, kn, vn);
+    const int id_after = pg + 2 < pg1 ? bt[pg + 2] : -1;
+    if (valid_id(id_cur)) {
+      const uint32_t kw[16] = {kc[0].x, kc[0].y, kc[0].z, kc[0].w, kc[1].x, kc[1].y, kc[1].z, kc[1].w,
+                               kc[2].x, kc[2].y, kc[2].z, kc[2].w, kc[3].x, kc[3].y, kc[3].z, kc[3].w};
+      v4f s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc8 = 0; kc8 < 8; ++kc8) {
+        const v4s ka = (v4s){(short)(kw[2 * kc8] & 0xFFFF), (short)(kw[2 * kc8] >> 16),
+                             (short)(kw[2 * kc8 + 1] & 0xFFFF), (short)(kw[2 * kc8 + 1] >> 16)};
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qb[kc8], s, 0, 0, 0);
+      }
+      float lg[4];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = pg * kPage + 4 * kq + i;
+        lg[i] = pos < L ? s[i] * sm_log2 : -INFINITY;
+        tm = fmaxf(tm, lg[i]);
+      }
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mnew = fmaxf(mrun, tm);
+      if (__any(mnew > mrun)) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        lsum *= alpha;
+        // accumulator rows are query heads 4*kq + i: fetch their alphas from lanes 4*kq + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * kq + i);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) acc[nb][i] *= ai;
+        }
+        mrun = mnew;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = lg[i] != -INFINITY ? __builtin_amdgcn_exp2f(lg[i] - mrun) : 0.f;
+        lsum += p[i];
+      }
+      uint32_t h01, h23, l01, l23;
+      split_bf16(p, h01, h23, l01, l23);
+      const v4s ahi = (v4s){(short)(h01 & 0xFFFF), (short)(h01 >> 16), (short)(h23 & 0xFFFF), (short)(h23 >> 16)};
+      const v4s alo = (v4s){(short)(l01 & 0xFFFF), (short)(l01 >> 16), (short)(l23 & 0xFFFF), (short)(l23 >> 16)};
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const uint2 vv = vc[nb];
+        const v4s vb = (v4s){(short)(vv.x & 0xFFFF), (short)(vv.x >> 16), (short)(vv.y & 0xFFFF), (short)(vv.y >> 16)};
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb, acc[nb], 0, 0, 0);
+      }
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kc[k] = kn[k];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) vc[nb] = vn[nb];
+    id_cur = pg + 1 < pg1 ? id_next : -1;
+    id_next = id_after;
   }
   // l per query head j = c16 (sum over token quarters); rows of acc are heads 4*kq + i.
   const float lt = lsum + __shfl_xor(lsum, 16) + __shfl_xor(lsum, 32) + __shfl_xor(lsum, 48);

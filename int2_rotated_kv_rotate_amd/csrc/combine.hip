@@ -25,7 +25,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   const int jq = h * G + j;
   extern __shared__ float s_w[];        // [2][G][ns]: merge weights 2^(m - M) (0 for empty), l
   __shared__ float s_o[8][kHeadDim];
-  __shared__ float s_inv[8];
+  __shared__ float s_red[8][4];         // per head: max, then l, of each of its two waves
   __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
 
   // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of the slots.
@@ -62,40 +62,51 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   }
   __syncthreads();
   const int nv = min(max(nv_raw, 0), ns - 1);
-  if (c == 0) {  // weights of the entries: INT2 slots 0 .. nv-1, then the window slot
-    float* wm = s_w + j * ns;
-    const float* wl = s_w + G * ns + j * ns;
-    float M = -INFINITY;
-    for (int e = 0; e < nv; ++e)
-      if (wl[e] > 0.f) M = fmaxf(M, wm[e]);
-    if (wl[ns - 1] > 0.f) M = fmaxf(M, wm[ns - 1]);
-    float l = 0.f;
-    for (int e = 0; e < nv; ++e) {
-      const float w = wl[e] > 0.f ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
-      wm[e] = w;
-      l = fmaf(w, wl[e], l);
-    }
-    const float wwin = wl[ns - 1] > 0.f ? __builtin_amdgcn_exp2f(wm[ns - 1] - M) : 0.f;
-    wm[ns - 1] = wwin;
-    l = fmaf(wwin, wl[ns - 1], l);
-    s_inv[j] = l > 0.f ? 1.0f / l : 0.f;
-    if (lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
-  }
+  // Merge weights, computed by the head's 128 threads (entry e by thread e % 128): the INT2
+  // slots 0 .. nv-1 and the window slot; M and l reduced in a fixed order.
+  float* wm = s_w + j * ns;
+  const float* wl = s_w + G * ns + j * ns;
+  float mloc = -INFINITY;
+  for (int e = c; e < ns; e += 128)
+    if ((e < nv || e == ns - 1) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2));
+  if ((c & 63) == 0) s_red[j][c >> 6] = mloc;
   __syncthreads();
+  const float M = fmaxf(s_red[j][0], s_red[j][1]);
+  float lloc = 0.f;
+  for (int e = c; e < ns; e += 128) {
+    const bool use = (e < nv || e == ns - 1) && wl[e] > 0.f;
+    const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
+    wm[e] = w;
+    lloc = fmaf(w, wl[e], lloc);
+  }
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2);
+  if ((c & 63) == 0) s_red[j][2 + (c >> 6)] = lloc;
+  __syncthreads();
+  const float l = s_red[j][2] + s_red[j][3];
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (c == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
   // o'[j][c] = sum_e w_e o'_e[c] / l over the INT2 slots in order, then the window slot; an
-  // empty entry (w = 0) is skipped, so its partial output is never read into the sum.
-  const float* wj = s_w + j * ns;
+  // empty entry (w = 0) is skipped, so its partial output is never read into the sum.  Slots
+  // past the first 16 are loaded 16 at a time.
+  const float* wj = wm;
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < kBatch; ++e) {
     if (e < nv && wj[e] > 0.f) acc = fmaf(wj[e], ov[e], acc);
   }
-  for (int e = kBatch; e < nv; ++e) {
-    const float w = wj[e];
-    if (w > 0.f) acc = fmaf(w, o[(size_t)e * kHeadDim], acc);
+  for (int e0 = kBatch; e0 < nv; e0 += kBatch) {
+    float ob[kBatch];
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) ob[e] = e0 + e < nv ? o[(size_t)(e0 + e) * kHeadDim] : 0.f;
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const float w = e0 + e < nv ? wj[e0 + e] : 0.f;
+      if (w > 0.f) acc = fmaf(w, ob[e], acc);
+    }
   }
   if (wj[ns - 1] > 0.f) acc = fmaf(wj[ns - 1], ow, acc);
-  s_o[j][c] = acc * s_inv[j];
+  s_o[j][c] = acc * inv;
   __syncthreads();
   float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
   if (rot_v == nullptr) {

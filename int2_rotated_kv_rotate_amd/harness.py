@@ -213,8 +213,8 @@ class Bf16Cache:
                             torch.zeros(1, dtype=torch.int32, device=device))
         torch.cuda.synchronize()
         pages_max = int((p.lens.max() + 15) // 16)
-        if split_pages is None:  # about 4096 (split, KV head, sequence) waves
-            split_pages = max(1, -(-pages_max * w.batch * hkv // 4096))
+        if split_pages is None:  # about 1024 (split, KV head, sequence) waves: one per SIMD
+            split_pages = max(1, -(-pages_max * w.batch * hkv // 1024))
         self.split_pages = split_pages
         self.max_splits = max(1, -(-pages_max // split_pages))
         self.ws = torch.empty(ops.decode_workspace_bytes(w.batch, w.num_q_heads, self.max_splits),
