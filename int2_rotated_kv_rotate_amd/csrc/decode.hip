@@ -335,18 +335,22 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // Lane l's 16 bytes land at M0 + 16 l.  voff = 16 l reads the heads; the tails are copied by
 // two half-wave loads (exec restricted inside the statement and restored before it ends) with
 // per-lane offsets vta = 1024 + 16 l (lanes 0..31: A bytes [1024, 1536)) and vtb = 512 + 16 l
-// (lanes 32..63: B bytes [1024, 1536)).  No immediate offsets are used.
+// (lanes 32..63: B bytes [1024, 1536)).  No immediate offsets are used.  The three M0 values
+// are computed outside the statement, which contains no instruction that writes SCC: the
+// compiler may keep a condition live in SCC across it.
 __device__ __forceinline__ void dma_pair(const uint8_t* recA, const uint8_t* recB, uint32_t ps,
                                          uint32_t voff, uint32_t vta, uint32_t vtb) {
   uint64_t saved;
+  const uint32_t ps1 = __builtin_amdgcn_readfirstlane(ps + 0x400u);
+  const uint32_t ps2 = __builtin_amdgcn_readfirstlane(ps + 0x800u);
   asm volatile(
       "s_mov_b32 m0, %[ps]\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %[v], %[a]\n\t"
-      "s_add_u32 m0, %[ps], 0x400\n\t"
+      "s_mov_b32 m0, %[ps1]\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %[v], %[b]\n\t"
-      "s_add_u32 m0, %[ps], 0x800\n\t"
+      "s_mov_b32 m0, %[ps2]\n\t"
       "s_mov_b64 %[sv], exec\n\t"
       "s_mov_b32 exec_hi, 0\n\t"
       "global_load_lds_dwordx4 %[ta], %[a]\n\t"
@@ -355,7 +359,8 @@ __device__ __forceinline__ void dma_pair(const uint8_t* recA, const uint8_t* rec
       "global_load_lds_dwordx4 %[tb], %[b]\n\t"
       "s_mov_b64 exec, %[sv]"
       : [sv] "=&s"(saved)
-      : [ps] "s"(ps), [v] "v"(voff), [ta] "v"(vta), [tb] "v"(vtb), [a] "s"(recA), [b] "s"(recB)
+      : [ps] "s"(ps), [ps1] "s"(ps1), [ps2] "s"(ps2), [v] "v"(voff), [ta] "v"(vta),
+        [tb] "v"(vtb), [a] "s"(recA), [b] "s"(recB)
       : "memory", "m0");
 }
 
