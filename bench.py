@@ -124,7 +124,8 @@ def cpu_baseline(p, target_s: float):
                        f"{len(per_step)} timed single-head decode steps (append of the new "
                        f"token + decode attention), {sum(per_step):.1f} s in total, scaled to "
                        f"all {w.num_kv_heads} KV heads of one decode step; one BLAS thread"),
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads": 1}
 
 
 def time_scrubbed(fn, n: int, scrub):
@@ -152,7 +153,8 @@ def int2_vs_bf16(n_iter: int):
     the same library, with a 1 GiB cache scrub before every timed launch:
       * Qwen3-32B layer shape, context 32768: INT2 at batch 16 vs BF16 at batch 2 (about 1/8
         of the batch) and batch 3 (the equal-memory batch for 3 bits per element);
-      * Qwen3-4B layer shape, batch 1, context 32768: latency of each."""
+      * Qwen3-4B layer shape, batch 1, context 32768: latency of each;
+      * long-context layer (32 query / 8 KV heads), batch 1, context 131072: latency of each."""
     import torch
     from int2_rotated_kv_rotate_amd import harness as H
     from int2_rotated_kv_rotate_amd import workload as W
@@ -198,6 +200,16 @@ def int2_vs_bf16(n_iter: int):
 
     def gbps(w, p, ms, bf16):
         return round(attn_bytes(w, p, bf16) / (ms * 1e-3) / 1e9, 1)
+
+    # Long context, batch 1 (131072 positions, the needle workload's cache): INT2 latency
+    wl = W.WORKLOADS["long_128k"]
+    pl, (msl, _, _), _ = int2_case(wl)
+    _, (msl_b, _, _), _ = bf16_case(wl)
+    res["long_128k_b1"] = {"int2_ms": round(msl, 4), "bf16_ms": round(msl_b, 4),
+                           "latency_ratio": round(msl_b / msl, 3),
+                           "int2_effective_gbps": gbps(wl, pl, msl, False),
+                           "bf16_effective_gbps": gbps(wl, pl, msl_b, True)}
+    log(f"long_128k B=1: INT2 {msl:.4f} ms, BF16 {msl_b:.4f} ms")
 
     w32 = W.WORKLOADS["qwen3_32b"]
     p, (ms, p10, p90), pool = int2_case(w32)
@@ -325,6 +337,24 @@ def main():
     log(f"step {ms_step:.4f} ms; decode attention avg {attn_avg:.4f} ms "
         f"(p10 {np.percentile(attn_ms, 10):.4f}, p90 {np.percentile(attn_ms, 90):.4f})")
 
+    # The same step with the last-level cache evicted (a 1 GiB read) before each one.
+    scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    ms_scrub, _, _ = time_scrubbed(step.run, max(5, args.steps // 2), scrub)
+    # Achievable device-copy bandwidth in the same run: 1 GiB copied (2 GiB moved).
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ca.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    cb.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) / (ca.elapsed_time(cb) / 5 / 1e3) / 1e9
+    del scrub, csrc, cdst
+    log(f"step with cache scrub {ms_scrub:.4f} ms; device copy {copy_gbps:.0f} GB/s")
+
     tokens_per_s = w.batch / (ms_step / 1e3)
     step_gbps = bm["step"] / (ms_step / 1e3) / 1e9
     attn_gbps = bm["decode_attention"] / (attn_avg / 1e3) / 1e9
@@ -409,11 +439,14 @@ def main():
                    "max_splits": args.max_splits},
         "effective_gbps": round(step_gbps, 1),
         "pct_of_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
+        "ms_per_step_cache_scrubbed": round(ms_scrub, 5),
+        "copy_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "oscar_decode_attention (q prep + INT2 runs + "
                      "BF16 window)", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": bm["decode_attention"], "launch_ms": round(attn_avg, 5),
-                     "traffic": measured_traffic(w.name)},
+                     "traffic": measured_traffic(w.name),
+                     "frac_of_copy": round(attn_gbps / copy_gbps, 4)},
         "bytes": bm,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
