@@ -246,8 +246,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_b64")
     ap.add_argument("--workers", type=int, default=0,
                     help="INT2 worker wavefronts (0: one per resident slot of the device)")
-    ap.add_argument("--max-splits", type=int, default=64,
-                    help="INT2 partial slots per (sequence, KV head)")
+    ap.add_argument("--max-splits", type=int, default=None,
+                    help="INT2 partial slots per (sequence, KV head) (default: by batch size)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -436,7 +436,7 @@ def main():
                    "ctx": f"U[{w.ctx_min},{w.ctx}]" if w.ctx_min else w.ctx,
                    "mean_ctx": float(p.lens.mean()), "sink": w.num_sink, "window": w.window,
                    "page": 16, "workers": args.workers or "auto",
-                   "max_splits": args.max_splits},
+                   "max_splits": step.max_splits},
         "effective_gbps": round(step_gbps, 1),
         "pct_of_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
         "ms_per_step_cache_scrubbed": round(ms_scrub, 5),

@@ -126,11 +126,155 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   orow[c] = acc2;
 }
 
+// Small-grid form: grid (Hq, batch), block 512, one workgroup per query head, for launches
+// where one workgroup per KV head would leave most of the chip idle and each head has many
+// splits.  Thread t = (slot lane sg = t / 32 of 16, channel quad c4 = t % 32): slot lane sg
+// sums slots sg, sg + 16, ... in ascending order with 16-byte loads, eight slots in flight; the
+// 16 lanes' partial sums are added in lane order.  For R_V^T, thread t computes half (kh = t % 2)
+// of output channel t / 2 (only threads < 256) from its R_V row, loaded first.
+constexpr int kHeadThreads = 512, kSlotLanes = kHeadThreads / 32;
+
+__global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int hkv, Workspace ws,
+                                                                  const float* __restrict__ rot_v,
+                                                                  float* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  const int jq = blockIdx.x, b = blockIdx.y, h = jq / (hq / hkv);
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int ns = ws.nslots;
+  extern __shared__ float s_w[];  // [2][ns]: m of each slot (then its merge weight), l
+  __shared__ float4 s_part[kSlotLanes][32];
+  __shared__ float s_o[kHeadDim];
+  __shared__ float s_red[2][kHeadThreads / 64];
+
+  const int c_out = t >> 1, kh = t & 1;
+  float4 r[16];
+  if (rot_v != nullptr && t < 2 * kHeadDim) {
+    const float4* R = reinterpret_cast<const float4*>(
+        rot_v + ((size_t)h * kHeadDim + c_out) * kHeadDim + (kHeadDim / 2) * kh);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) r[k] = R[k];
+  }
+  const int nv_raw = ws.nvalid()[b * hkv + h];
+  for (int e = t; e < ns; e += kHeadThreads) {
+    const float2 ml = *ws.ml(b, hq, jq, e);
+    s_w[e] = ml.x;
+    s_w[ns + e] = ml.y;
+  }
+  __syncthreads();
+  const int nv = min(max(nv_raw, 0), ns - 1);
+  float* wm = s_w;
+  const float* wl = s_w + ns;
+  float mloc = -INFINITY;
+  for (int e = t; e < ns; e += kHeadThreads)
+    if ((e < nv || e == ns - 1) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2));
+  if (lane == 0) s_red[0][wv] = mloc;
+  __syncthreads();
+  float M = s_red[0][0];
+#pragma unroll
+  for (int k = 1; k < kHeadThreads / 64; ++k) M = fmaxf(M, s_red[0][k]);
+  float lloc = 0.f;
+  for (int e = t; e < ns; e += kHeadThreads) {
+    const bool use = (e < nv || e == ns - 1) && wl[e] > 0.f;
+    const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
+    wm[e] = w;
+    lloc = fmaf(w, wl[e], lloc);
+  }
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2);
+  if (lane == 0) s_red[1][wv] = lloc;
+  __syncthreads();
+  float l = 0.f;
+#pragma unroll
+  for (int k = 0; k < kHeadThreads / 64; ++k) l += s_red[1][k];
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (t == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
+
+  // o' partial sums: slot lane sg over slots sg, sg + 16, ... (< nv), skipping empty slots.
+  const int sg = t >> 5, c4 = t & 31;
+  const float4* ob = reinterpret_cast<const float4*>(ws.o(b, hq, jq, 0)) + c4;
+  constexpr int kStride = kHeadDim / 4;  // float4 per slot
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float w, const float4& x) {
+    if (w > 0.f) {
+      acc.x = fmaf(w, x.x, acc.x);
+      acc.y = fmaf(w, x.y, acc.y);
+      acc.z = fmaf(w, x.z, acc.z);
+      acc.w = fmaf(w, x.w, acc.w);
+    }
+  };
+  int e = sg;
+  constexpr int kFlight = 8;
+  for (; e + (kFlight - 1) * kSlotLanes < nv; e += kFlight * kSlotLanes) {
+    float4 x[kFlight];
+#pragma unroll
+    for (int k = 0; k < kFlight; ++k) x[k] = ob[(size_t)(e + k * kSlotLanes) * kStride];
+#pragma unroll
+    for (int k = 0; k < kFlight; ++k) add(wm[e + k * kSlotLanes], x[k]);
+  }
+  for (; e < nv; e += kSlotLanes) add(wm[e], ob[(size_t)e * kStride]);
+  s_part[sg][c4] = acc;
+  __syncthreads();
+  if (t < 32) {
+    float4 sum = s_part[0][t];
+#pragma unroll
+    for (int k = 1; k < kSlotLanes; ++k) {
+      const float4 v = s_part[k][t];
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    const float ww = wm[ns - 1];
+    if (ww > 0.f) {
+      const float4 x = ob[(size_t)(ns - 1) * kStride];
+      sum.x = fmaf(ww, x.x, sum.x);
+      sum.y = fmaf(ww, x.y, sum.y);
+      sum.z = fmaf(ww, x.z, sum.z);
+      sum.w = fmaf(ww, x.w, sum.w);
+    }
+    s_o[4 * t + 0] = sum.x * inv;
+    s_o[4 * t + 1] = sum.y * inv;
+    s_o[4 * t + 2] = sum.z * inv;
+    s_o[4 * t + 3] = sum.w * inv;
+  }
+  __syncthreads();
+  float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
+  if (rot_v == nullptr) {
+    if (t < kHeadDim) orow[t] = s_o[t];
+    return;
+  }
+  if (t >= 2 * kHeadDim) return;
+  // out[c] = sum_k o'[k] * R_V[h][c][k]: the two halves of k, then their sum (low half first)
+  float part = 0.f;
+#pragma unroll
+  for (int k4 = 0; k4 < 16; ++k4) {
+    const int k = (kHeadDim / 2) * kh + 4 * k4;
+    part = fmaf(s_o[k + 0], r[k4].x, part);
+    part = fmaf(s_o[k + 1], r[k4].y, part);
+    part = fmaf(s_o[k + 2], r[k4].z, part);
+    part = fmaf(s_o[k + 3], r[k4].w, part);
+  }
+  const float other = __shfl_xor(part, 1);
+  if (kh == 0) orow[c_out] = part + other;
+}
+
 }  // namespace
 
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
+  // One workgroup per query head when one per KV head would cover less than half of the
+  // compute units and the heads have many splits to merge.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidValue;
+  if ((long long)batch * hkv * 2 < cus && ws.nslots > 32) {
+    const size_t lds1 = (size_t)2 * ws.nslots * sizeof(float);
+    hipLaunchKernelGGL(combine_head_kernel, dim3(hq, batch), dim3(kHeadThreads), lds1, stream, hq,
+                       hkv, ws, rot_v, out, lse);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)2 * (hq / hkv) * ws.nslots * sizeof(float);
   if (lds > 48 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(combine_kernel, dim3(hkv, batch), dim3(128 * (hq / hkv)), lds, stream, hq, hkv,

@@ -593,6 +593,7 @@ __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* 
                                             const int32_t* __restrict__ seq_lens, float sm_log2,
                                             const Workspace& ws, int b, int h, uint8_t* smem) {
   constexpr int kJ = 4 * NCB;  // head rows kept (G <= kJ)
+  static_assert(kWaves == 2, "the P.V partials of the two waves are added pairwise");
   static_assert((kMaxSinkWindow * kJ + 2 * kJ + kJ * kHeadDim) * sizeof(float) <= kSmemBytes<NCB>,
                 "window scratch exceeds the workgroup's shared memory");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -632,30 +633,55 @@ __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* 
       qlo[s] = __builtin_bit_cast(v4s, make_uint2(l01, l23));
     }
   }
+  // Two tiles per wave per round, both tiles' K rows loaded before either is used.
   const int ntiles = (n + kPage - 1) / kPage;
-  for (int tl = wave; tl < ntiles; tl += kWaves) {
-    const int i = tl * kPage + m;
-    uint4 kr[4] = {};
-    if (i < n) {
-      const uint4* kp = reinterpret_cast<const uint4*>(row_ptr(i) + 32 * kq);
+  for (int tl0 = wave; tl0 < ntiles; tl0 += 2 * kWaves) {
+    uint4 kr[2][4] = {};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kr[u] = kp[u];
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int i = (tl0 + h2 * kWaves) * kPage + m;
+      if (i < n) {
+        const uint4* kp = reinterpret_cast<const uint4*>(row_ptr(i) + 32 * kq);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kr[h2][u] = kp[u];
+      }
     }
-    v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4& u = kr[s >> 1];
-      const v4s kb = __builtin_bit_cast(v4s, (s & 1) ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y));
-      d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qhi[s], kb, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qlo[s], kb, d, 0, 0, 0);
-    }
-    // D: this lane holds token i (column lane % 16) for heads 4*kq + e
-    if (i < n) {
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int i = (tl0 + h2 * kWaves) * kPage + m;
+      v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * kq + e < kJ) s_p[i * kJ + 4 * kq + e] = d[e] * sm_log2;
+      for (int s = 0; s < 8; ++s) {
+        const uint4& u = kr[h2][s >> 1];
+        const v4s kb = __builtin_bit_cast(v4s, (s & 1) ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y));
+        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qhi[s], kb, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qlo[s], kb, d, 0, 0, 0);
+      }
+      // D: this lane holds token i (column lane % 16) for heads 4*kq + e
+      if (i < n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * kq + e < kJ) s_p[i * kJ + 4 * kq + e] = d[e] * sm_log2;
+      }
     }
   }
+
+  // P.V operands: lane -> channels 8*cq .. 8*cq + 7 (one 16-byte load) of token 4*k + tq of
+  // the wave's token quads wave, wave + kWaves, ...; kVB loads per lane per round, the first
+  // round issued before the softmax.
+  const int cq = lane & 15, tq = lane >> 4;
+  constexpr int kVB = 8;
+  constexpr int kRound = 4 * kWaves * kVB;  // tokens per round of the workgroup
+  auto load_v = [&](int i0, uint4 (&vv)[kVB]) {
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int i = i0 + 4 * kWaves * u + tq;
+      vv[u] = i < n ? *reinterpret_cast<const uint4*>(row_ptr(i) + kHeadDim + 8 * cq)
+                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 vv[kVB];
+  load_v(4 * wave, vv);
   __syncthreads();
 
   // Softmax per head over the n tokens: 16 threads per head.
@@ -678,79 +704,91 @@ __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* 
   }
   __syncthreads();
 
-  // P.V: lane -> channels 2*lane, 2*lane + 1; wave w takes tokens w, w + kWaves, ...
-  float acc[kJ][2];
+  float acc[kJ][8];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) acc[j][0] = acc[j][1] = 0.f;
-  constexpr int kBatch = 8;
-  for (int i0 = wave; i0 < n; i0 += kWaves * kBatch) {
-    uint32_t vv[kBatch];
+  for (int j = 0; j < kJ; ++j)
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + kWaves * u;
-      vv[u] = i < n ? reinterpret_cast<const uint32_t*>(row_ptr(i) + kHeadDim)[lane] : 0u;
-    }
+    for (int c = 0; c < 8; ++c) acc[j][c] = 0.f;
+  for (int i0 = 4 * wave; i0 < n; i0 += kRound) {
+    if (i0 > 4 * wave) load_v(i0, vv);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + kWaves * u;
+    for (int u = 0; u < kVB; ++u) {
+      const int i = i0 + 4 * kWaves * u + tq;
       if (i < n) {
-        const float v0 = __uint_as_float(vv[u] << 16), v1 = __uint_as_float(vv[u] & 0xFFFF0000u);
+        const uint32_t w4[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
           const float p = s_p[i * kJ + j];
-          acc[j][0] = fmaf(p, v0, acc[j][0]);
-          acc[j][1] = fmaf(p, v1, acc[j][1]);
+#pragma unroll
+          for (int c2 = 0; c2 < 4; ++c2) {
+            acc[j][2 * c2] = fmaf(p, __uint_as_float(w4[c2] << 16), acc[j][2 * c2]);
+            acc[j][2 * c2 + 1] = fmaf(p, __uint_as_float(w4[c2] & 0xFFFF0000u), acc[j][2 * c2 + 1]);
+          }
         }
       }
     }
   }
-  if (wave == 1) {
+  // sum over the four token lanes of each channel group (fixed order), then over the waves
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      s_o[j * kHeadDim + 2 * lane] = acc[j][0];
-      s_o[j * kHeadDim + 2 * lane + 1] = acc[j][1];
+  for (int j = 0; j < kJ; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      acc[j][c] += __shfl_xor(acc[j][c], 16);
+      acc[j][c] += __shfl_xor(acc[j][c], 32);
     }
+  if (wave == 1 && tq == 0) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s_o[j * kHeadDim + 8 * cq + c] = acc[j][c];
   }
   __syncthreads();
   if (wave == 0) {
     const int out_slot = ws.nslots - 1;
+    if (tq == 0) {
 #pragma unroll
-    for (int j = 0; j < kJ; ++j)
-      if (j < G) {
-        float* o = ws.o(b, hq, h * G + j, out_slot);
-        o[2 * lane] = acc[j][0] + s_o[j * kHeadDim + 2 * lane];
-        o[2 * lane + 1] = acc[j][1] + s_o[j * kHeadDim + 2 * lane + 1];
-      }
+      for (int j = 0; j < kJ; ++j)
+        if (j < G) {
+          float4* o = reinterpret_cast<float4*>(ws.o(b, hq, h * G + j, out_slot) + 8 * cq);
+          const float* so = s_o + j * kHeadDim + 8 * cq;
+          o[0] = make_float4(acc[j][0] + so[0], acc[j][1] + so[1], acc[j][2] + so[2], acc[j][3] + so[3]);
+          o[1] = make_float4(acc[j][4] + so[4], acc[j][5] + so[5], acc[j][6] + so[6], acc[j][7] + so[7]);
+        }
+    }
     if (lane < G)
       *ws.ml(b, hq, h * G + lane, out_slot) =
           n > 0 ? make_float2(s_red[lane], s_red[kJ + lane]) : make_float2(kNegBig, 0.f);
   }
 }
 
+
 // NCB = number of 16-row blocks of (query head, group) pairs = ceil(G / 4).
-// Workgroups [0, worker_groups) are INT2 workers, kWaves per workgroup.  Persistent part:
+// worker_groups workgroups are INT2 workers, kWaves per workgroup.  Persistent part:
 // worker w (one wavefront) takes run w of C pages of the concatenation of all (sequence, KV
 // head) pairs' INT2 pages (the plan in the workspace, built by prep_q_kernel), and writes one
 // partial for each pair its run touches, into that pair's slot w - (first run of the pair).
-// Every worker therefore streams about the same number of pages.  The workgroups after them
-// compute the BF16 sink + window partial of one pair each; they are dispatched last and so
-// mostly run in the tail of the INT2 workers.
+// Every worker therefore streams about the same number of pages.  batch * Hkv more workgroups
+// compute the BF16 sink + window partial of one pair each: after the workers, so that they
+// mostly run in the workers' tail, or (window_first, for launches with few pairs) before them.
 template <int NCB>
 __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
     CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ plan, float sm_scale,
-    int worker_groups, Workspace ws) {
+    int worker_groups, int window_first, Workspace ws) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes<NCB>];
-  if ((int)blockIdx.x >= worker_groups) {
-    const int pair = blockIdx.x - worker_groups;
+  int bid = blockIdx.x;
+  const int nwin = ws.batch * g.hkv;
+  if (window_first ? bid < nwin : bid >= worker_groups) {
+    const int pair = window_first ? bid : bid - worker_groups;
     window_pair<NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
                      pair % g.hkv, smem);
     return;
   }
+  if (window_first) bid -= nwin;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
-  const int worker = blockIdx.x * kWaves + wave;
+  const int worker = bid * kWaves + wave;
   const int t = lane & 15, r = lane >> 4;
   WTile<NCB>& tile = *reinterpret_cast<WTile<NCB>*>(smem + (size_t)kWaves * kRingBytes +
                                                     wave * sizeof(WTile<NCB>));
@@ -1013,15 +1051,22 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
                      rot_k, hq, seq_lens, workers, ws);
   const int worker_groups = (workers + kWaves - 1) / kWaves;
   const dim3 grid(worker_groups + batch * g.hkv);
+  // Few pairs: their sink/window workgroups go first, so that they start at once instead of
+  // after the INT2 workers that fill the device.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int window_first = (long long)batch * g.hkv * 2 < cus ? 1 : 0;
   const int32_t* plan = ws.plan();
   if (G <= 4)
     hipLaunchKernelGGL(int2_decode_kernel<1>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
-                       worker_groups, ws);
+                       worker_groups, window_first, ws);
   else
     hipLaunchKernelGGL(int2_decode_kernel<2>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
-                       worker_groups, ws);
+                       worker_groups, window_first, ws);
   return hipGetLastError();
 }
 

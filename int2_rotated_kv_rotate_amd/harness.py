@@ -135,18 +135,35 @@ class GpuCache:
 # Partial slots per (sequence, KV head): enough that the run length is set by the worker count
 # for the contexts used here (a pair of P pages needs about P / run + 1 slots).
 DEFAULT_MAX_SPLITS = 64
+MAX_SPLITS_CAP = 512
+SMALL_LAUNCH_PAIRS = 128   # (sequence, KV head) pairs below which runs are cut short
+SHORT_RUN_PAGES = 24      # run length aimed at for such launches
+
+
+def default_max_splits(batch: int, num_kv_heads: int, max_context: int) -> int:
+    """Slots per (sequence, KV head) for a decode launch.  With many pairs the worker count
+    sets the run length and DEFAULT_MAX_SPLITS is ample; with few pairs (batch 1) the runs are
+    cut to about SHORT_RUN_PAGES pages so that a long context spreads over the device, at most
+    MAX_SPLITS_CAP slots."""
+    if batch * num_kv_heads >= SMALL_LAUNCH_PAIRS:
+        return DEFAULT_MAX_SPLITS
+    pages = -(-max(1, max_context) // 16)
+    want = -(-pages // SHORT_RUN_PAGES) + 2
+    return int(min(MAX_SPLITS_CAP, max(DEFAULT_MAX_SPLITS, want)))
 
 
 class DecodeStep:
     """Buffers and launches of one decode step: append the new token, attend, combine."""
 
-    def __init__(self, cache: GpuCache, num_workers: int = 0, max_splits: int = DEFAULT_MAX_SPLITS):
+    def __init__(self, cache: GpuCache, num_workers: int = 0, max_splits: Optional[int] = None):
         """num_workers 0: one worker per resident wavefront slot; max_splits bounds the INT2
-        partials per (sequence, KV head) (a small value lengthens the workers' runs)."""
+        partials per (sequence, KV head) (a small value lengthens the workers' runs); None
+        takes default_max_splits."""
         p = cache.p
         self.cache = cache
         self.num_workers = num_workers
-        self.max_splits = max_splits
+        self.max_splits = (max_splits if max_splits is not None
+                           else default_max_splits(p.batch, p.w.num_kv_heads, int(p.lens.max())))
         dev = cache.device
         self.ws = torch.empty(ops.decode_workspace_bytes(p.batch, p.w.num_q_heads, self.max_splits),
                               dtype=torch.uint8, device=dev)

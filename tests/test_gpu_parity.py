@@ -145,20 +145,25 @@ def test_distinct_k_and_v_rotations_are_not_conflated():
     assert row_errors(step.out.cpu().numpy(), wrong).max() > 0.1
 
 
-def test_combine_with_synthetic_partials():
+@pytest.mark.parametrize("max_splits,nvalid_rows", [
+    (5, [[5, 3], [2, 0], [4, 5]]),            # one workgroup per KV head
+    (100, [[100, 37], [2, 0], [99, 64]]),     # few pairs, many splits: one per query head
+])
+def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
     """oscar_combine on seeded partials (not produced by the library) vs the oracle merge.
 
     Each (sequence, KV head) pair declares how many INT2 slots it filled (the plan's nvalid);
     slots past that hold NaN outputs and large (m, l) and must not be read."""
-    B, hq, hkv, max_splits = 3, 8, 2, 5
+    B, hq, hkv = 3, 8, 2
     nslots = max_splits + 1
     G = hq // hkv
     valid = np.ones((B, nslots), bool)
     valid[0, 2] = False
+    valid[0, 3:max_splits:7] = False
     valid[1, 1:] = False
     valid[2, :] = False                      # a row with no positions at all
     m, l, o = W.synthetic_partials(42, B, hq, nslots, valid)
-    nvalid = np.array([[5, 3], [2, 0], [4, 5]], np.int32)       # [B][hkv]
+    nvalid = np.array(nvalid_rows, np.int32)       # [B][hkv]
     for b in range(B):
         for j in range(hq):
             stale = np.arange(nvalid[b, j // G], max_splits)
