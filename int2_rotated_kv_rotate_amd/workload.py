@@ -153,6 +153,16 @@ def outlier_channels(w: Workload) -> np.ndarray:
                      for _ in range(w.num_kv_heads)]).astype(np.int64)
 
 
+def key_channel_means(w: Workload) -> np.ndarray:
+    """fp32 [Hkv][128]: the mean of the generated keys per (KV head, channel), i.e. the channel
+    offset, times 15 on the outlier channels (the keys are (N(0,1) + offset) * scale)."""
+    mu = key_offsets(w).astype(np.float32).copy()
+    out = outlier_channels(w)
+    for h in range(w.num_kv_heads):
+        mu[h, out[h]] *= np.float32(15.0)
+    return mu
+
+
 def needle_site(w: Workload, lens: np.ndarray):
     """(b, position, kv_head, query_head) of the planted needle, or None."""
     if not w.needle:

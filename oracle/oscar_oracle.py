@@ -30,7 +30,9 @@ for bit.  bf16 rounding is round to nearest even.
 Parity pins: every function here is checked in the CPU tests against closed forms,
 invariants, special cases and brute force (orthogonality, rotation invariance of attention,
 level membership, exhaustive code enumeration, hand-derived record bytes, partition
-invariance of the split merge).  No function is "parity unpinned".
+invariance of the split merge; for the key-mean form, one rounded subtraction under identity
+and signed-permutation rotations, exact rational sums, and softmax invariance).  No function
+is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -82,6 +84,38 @@ def rotate_rows(x_bits: np.ndarray, rot32: np.ndarray) -> np.ndarray:
     for i in range(D):
         acc = acc + x[:, i:i + 1] * r[i:i + 1, :]
     return acc.astype(np.float32)
+
+
+def mean_shift(mean32: np.ndarray, rot32: np.ndarray) -> np.ndarray:
+    """C = mu . R for a per-channel key mean mu (fp32 [128]): fp64, ascending input channel,
+    from +0.0 (each product of two fp32 values is exact in fp64).  Returns fp64 [128]."""
+    mu = np.asarray(mean32, dtype=np.float32).astype(np.float64)
+    r = np.asarray(rot32, dtype=np.float32).astype(np.float64)
+    acc = np.zeros(D, dtype=np.float64)
+    for i in range(D):
+        acc = acc + mu[i] * r[i]
+    return acc
+
+
+def rotate_rows_centered(x_bits: np.ndarray, rot32: np.ndarray, mean32) -> np.ndarray:
+    """y = (x - mu) . R for bf16 key rows, with a fixed per-channel mean mu subtracted.
+
+    The OptR abstract on the OSCAR paper's page ("OSCAR: Offline Spectral Covariance-Aware
+    Rotation for 2-bit KV Cache Quantization") adds an attention-equivalent reparameterisation
+    of the keys that removes large per-channel offsets: q . (k - mu) differs from q . k by
+    q . mu, the same for every position of a query, so the softmax does not change.  Reading
+    taken here: mu is a fixed fp32 vector per KV head, removed in the rotated frame as
+        y_j = fp32( fp64(S_j - C_j) ),  S_j = the sum of rotate_rows, C_j = mean_shift(mu, R)_j,
+    one fp64 subtraction then one rounding to fp32.  mean32 None gives rotate_rows exactly.
+    """
+    if mean32 is None:
+        return rotate_rows(x_bits, rot32)
+    x = bf16_bits_to_f64(x_bits)
+    r = np.asarray(rot32, dtype=np.float32).astype(np.float64)
+    acc = np.zeros((x.shape[0], D), dtype=np.float64)
+    for i in range(D):
+        acc = acc + x[:, i:i + 1] * r[i:i + 1, :]
+    return (acc - mean_shift(mean32, rot32)[None, :]).astype(np.float32)
 
 
 def rotate_query(q_bits: np.ndarray, rot_k32: np.ndarray, group: int) -> np.ndarray:
@@ -152,9 +186,10 @@ def dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
     return v.reshape(-1, D)
 
 
-def quantize_rows(x_bits: np.ndarray, rot32: np.ndarray, clip: float):
-    """Rotate, clip and quantise rows: returns (y fp32, codes u8, s16, z16)."""
-    y = rotate_rows(x_bits, rot32)
+def quantize_rows(x_bits: np.ndarray, rot32: np.ndarray, clip: float, mean32=None):
+    """Rotate (after removing mean32, if given), clip and quantise rows: returns (y fp32,
+    codes u8, s16, z16)."""
+    y = rotate_rows_centered(x_bits, rot32, mean32)
     s16, z16 = group_params(y, clip)
     return y, group_codes(y, s16, z16), s16, z16
 
@@ -303,19 +338,22 @@ class Cache:
         pages = np.asarray(table_row)[np.asarray(positions) // PAGE].astype(np.int64)
         return (pages * self.hkv + h) * RECORD, np.asarray(positions) % PAGE
 
-    def append(self, table_row, slot, start_pos, k_bits, v_bits, rot_k32, rot_v32, clip_k, clip_v):
+    def append(self, table_row, slot, start_pos, k_bits, v_bits, rot_k32, rot_v32, clip_k, clip_v,
+               k_mean32=None):
         """Append n new tokens of one sequence at positions start_pos .. start_pos+n-1.
 
         k_bits, v_bits: uint16 [n][Hkv][128] unrotated bf16 rows.  Every new position gets its
         INT2 encoding in its page record; sink positions and the last W positions of the new
-        length also get bf16(y) in the BF16 store.
+        length also get bf16(y) in the BF16 store.  k_mean32 (fp32 [Hkv][128] or None): a key
+        mean removed before the rotation (rotate_rows_centered).
         """
         n = k_bits.shape[0]
         new_len = start_pos + n
         positions = np.arange(start_pos, new_len)
         flat = self.pages.reshape(-1)
         for h in range(self.hkv):
-            yk, kc, ks, kz = quantize_rows(k_bits[:, h], rot_k32[h], clip_k)
+            yk, kc, ks, kz = quantize_rows(k_bits[:, h], rot_k32[h], clip_k,
+                                           None if k_mean32 is None else k_mean32[h])
             yv, vc, vs, vz = quantize_rows(v_bits[:, h], rot_v32[h], clip_v)
             base, r = self._bases(table_row, h, positions)
             write_slots(flat, base, r, kc, ks, kz, vc, vs, vz)
