@@ -122,7 +122,7 @@ int32_t oscar_rotate_quantize_append(
     const float* rot_k, const float* rot_v, float clip_k, float clip_v,
     void* stream);
 
-/* Kernel choices for oscar_rotate_quantize_append_method. */
+/* Kernel choices for oscar_rotate_quantize_append_ex. */
 enum {
   OSCAR_APPEND_AUTO = 0,    /* the matrix cores from 256 new rows, else the vector ALUs */
   OSCAR_APPEND_VECTOR = 1,  /* the rotation in fp64 on the vector ALUs, as defined above */
@@ -133,18 +133,33 @@ enum {
 };
 
 /*
- * oscar_rotate_quantize_append with the kernel chosen by `method` (one of OSCAR_APPEND_*;
- * anything else is OSCAR_ERR_INVALID_ARGUMENT).  Every method writes the same bytes; they differ
- * in speed only (the matrix cores win for prefill-sized appends, the vector ALUs for a few
- * rows).  oscar_rotate_quantize_append is this call with OSCAR_APPEND_AUTO.
+ * oscar_rotate_quantize_append with two more arguments.
+ *
+ * k_mean (NULLABLE, fp32 [Hkv][128], 4-byte aligned): a fixed per-(KV head, channel) key mean
+ * removed before the key rotation, the attention-equivalent key reparameterisation of the
+ * OptR abstract on the OSCAR paper's page ("OSCAR: Offline Spectral Covariance-Aware Rotation
+ * for 2-bit KV Cache Quantization"): q . (k - mu) differs from q . k by q . mu for every
+ * position, so attention outputs are unchanged while the keys lose their channel offsets.
+ * For K rows the rotated value becomes
+ *   y_j = fp32( S_j - C_j ),  S_j = the fp64 ascending sum above,
+ *                             C_j = sum_i mu_i R_ij in fp64, i ascending from +0.0,
+ * with the subtraction in fp64; V rows are unchanged.  NULL is the plain rotation, byte for
+ * byte.  The same mean must be used for every append of a cache.  The decode entry points do
+ * not take it: their outputs are unchanged, and the log-sum-exp oscar_combine reports is the
+ * one of the centered logits (lower by sm_scale * (q . mu) for each query head).
+ *
+ * method: one of OSCAR_APPEND_* (anything else is OSCAR_ERR_INVALID_ARGUMENT).  Every method
+ * writes the same bytes; they differ in speed only (the matrix cores win for prefill-sized
+ * appends, the vector ALUs for a few rows).  oscar_rotate_quantize_append is this call with
+ * k_mean NULL and OSCAR_APPEND_AUTO.
  */
-int32_t oscar_rotate_quantize_append_method(
+int32_t oscar_rotate_quantize_append_ex(
     const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
     const int32_t* block_table, const int32_t* slot_ids,
     int32_t batch, int32_t total_new,
     const uint16_t* k_new, const uint16_t* v_new,
     const int32_t* new_offsets, const int32_t* start_pos,
-    const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+    const float* rot_k, const float* rot_v, const float* k_mean, float clip_k, float clip_v,
     int32_t method, void* stream);
 
 /*

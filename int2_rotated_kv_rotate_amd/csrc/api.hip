@@ -60,13 +60,13 @@ const char* oscar_status_string(int32_t status) {
   }
 }
 
-int32_t oscar_rotate_quantize_append_method(
+int32_t oscar_rotate_quantize_append_ex(
     const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
     const int32_t* block_table, const int32_t* slot_ids,
     int32_t batch, int32_t total_new,
     const uint16_t* k_new, const uint16_t* v_new,
     const int32_t* new_offsets, const int32_t* start_pos,
-    const float* rot_k, const float* rot_v, float clip_k, float clip_v,
+    const float* rot_k, const float* rot_v, const float* k_mean, float clip_k, float clip_v,
     int32_t method, void* stream) {
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
@@ -80,13 +80,13 @@ int32_t oscar_rotate_quantize_append_method(
     return OSCAR_ERR_INVALID_ARGUMENT;
   if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
   if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rot_k) ||
-      !aligned16(rot_v) || (sinkwin && !aligned16(sinkwin)))
+      !aligned16(rot_v) || (sinkwin && !aligned16(sinkwin)) || ((uintptr_t)k_mean & 3u) != 0)
     return OSCAR_ERR_INVALID_ARGUMENT;
   static_assert(OSCAR_APPEND_AUTO == kAppendAuto && OSCAR_APPEND_VECTOR == kAppendVector &&
                 OSCAR_APPEND_MATRIX == kAppendMatrix, "append method numbering");
   return hip_status(launch_append(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
                                   total_new, k_new, v_new, new_offsets, start_pos, rot_k, rot_v,
-                                  clip_k, clip_v, method, (hipStream_t)stream));
+                                  k_mean, clip_k, clip_v, method, (hipStream_t)stream));
 }
 
 int32_t oscar_rotate_quantize_append(
@@ -97,9 +97,9 @@ int32_t oscar_rotate_quantize_append(
     const int32_t* new_offsets, const int32_t* start_pos,
     const float* rot_k, const float* rot_v, float clip_k, float clip_v,
     void* stream) {
-  return oscar_rotate_quantize_append_method(lay, pages, sinkwin, block_table, slot_ids, batch,
-                                             total_new, k_new, v_new, new_offsets, start_pos, rot_k,
-                                             rot_v, clip_k, clip_v, OSCAR_APPEND_AUTO, stream);
+  return oscar_rotate_quantize_append_ex(lay, pages, sinkwin, block_table, slot_ids, batch,
+                                         total_new, k_new, v_new, new_offsets, start_pos, rot_k,
+                                         rot_v, nullptr, clip_k, clip_v, OSCAR_APPEND_AUTO, stream);
 }
 
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits) {

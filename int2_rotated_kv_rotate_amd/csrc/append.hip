@@ -140,12 +140,14 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
     int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ new_offsets, const int32_t* __restrict__ start_pos,
-    const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
-    float clip_v) {
+    const float* __restrict__ rot_k, const float* __restrict__ rot_v,
+    const float* __restrict__ k_mean, float clip_k, float clip_v) {
 #pragma clang fp contract(off)
   static_assert(ROWS == 4 || ROWS == 16, "row blocking");
   __shared__ float4 s_rot[kHeadDim * kHeadDim / 4];   // R[i][j], row-major, 64 KiB
   __shared__ float s_x[ROWS][kHeadDim];               // input rows (bf16 widened)
+  __shared__ float s_mu[kHeadDim];                    // key mean (centered K only)
+  __shared__ double s_c[kHeadDim];                    // C = mu . R, fp64
   __shared__ float s_y[ROWS][kHeadDim + 1];           // rotated rows (fp32)
   __shared__ uint8_t s_code[ROWS][kHeadDim];
   __shared__ RowInfo s_info[ROWS];
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
   const uint16_t* src = is_v ? v_new : k_new;
   const float clip = is_v ? clip_v : clip_k;
   const int nrows = min(ROWS, total_new - row0);
+  const bool centered = !is_v && k_mean != nullptr;
 
   // Stage R (fp32) and the rows: all 16 loads of a thread are issued before the first LDS
   // store, so staging costs one memory latency.
@@ -181,7 +184,19 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
                       row0 + t, h, is_v);
     s_info[t] = info;
   }
+  if (centered && t < kHeadDim) s_mu[t] = k_mean[(size_t)h * kHeadDim + t];
   __syncthreads();
+  // Key mean: C_j = sum_i mu_i R_ij in fp64, i ascending (exact products), removed from the
+  // rotated key as one fp64 subtraction before the rounding to fp32.
+  if (centered) {
+    if (t < kHeadDim) {
+      const float* rf = reinterpret_cast<const float*>(s_rot);
+      double c = 0.0;
+      for (int i = 0; i < kHeadDim; ++i) c = __fma_rn((double)s_mu[i], (double)rf[i * kHeadDim + t], c);
+      s_c[t] = c;
+    }
+    __syncthreads();
+  }
 
   // y = x . R in fp64, i ascending (products are exact in fp64: fma == mul then add).
   if constexpr (ROWS == 16) {
@@ -202,8 +217,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      s_y[r0][4 * jq + k] = (float)a0[k];
-      s_y[r1][4 * jq + k] = (float)a1[k];
+      const double c = centered ? s_c[4 * jq + k] : 0.0;
+      s_y[r0][4 * jq + k] = (float)(a0[k] - c);
+      s_y[r1][4 * jq + k] = (float)(a1[k] - c);
     }
   } else {
     // thread -> row t / 64, channels 2*jp, 2*jp + 1
@@ -217,8 +233,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
       a[0] = __fma_rn(x, (double)rv.x, a[0]);
       a[1] = __fma_rn(x, (double)rv.y, a[1]);
     }
-    s_y[rr][2 * jp] = (float)a[0];
-    s_y[rr][2 * jp + 1] = (float)a[1];
+    const double c0 = centered ? s_c[2 * jp] : 0.0, c1 = centered ? s_c[2 * jp + 1] : 0.0;
+    s_y[rr][2 * jp] = (float)(a[0] - c0);
+    s_y[rr][2 * jp + 1] = (float)(a[1] - c1);
   }
   __syncthreads();
 
@@ -325,15 +342,17 @@ constexpr int kListCap = kPTile * kHeadDim;
 // Recompute the listed (row, channel) values as defined, four lanes per value: lane q sums the
 // products of inputs 32q .. 32q+31 in fp64, and the four partial sums are combined.  That sum
 // differs from the defined ascending one by at most 2 * 127 * 2^-53 sum|terms| <= 2^-45 ||x||
-// ||R_.c||; unless it lies that close to a midpoint between fp32 values both round to the same
-// fp32 value, and the rare value that close is summed again in ascending order.  `pass2` also
-// recodes the values (the defined formula); otherwise they are marked exact.
+// ||R_.c||, and after the fp64 subtraction of the key-mean term C_c (0 without a mean) by at
+// most that plus two fp64 ulps.  Unless it lies that close to a midpoint between fp32 values or
+// to zero (where the sign of a zero result is decided), both round to the same fp32 value, and
+// the rare value that close is summed again in ascending order.  `pass2` also recodes the
+// values (the defined formula); otherwise they are marked exact.
 // Called by all threads of the workgroup.
 __device__ void recompute_listed(const uint16_t* __restrict__ list, int n,
                                  const float (*s_rot)[kRStride], const uint16_t (*s_x)[kXStride],
-                                 const float* s_nrm, const float* s_cng, float (*s_y)[kYStride],
-                                 uint8_t (*s_code)[kHeadDim], const float2 (*s_sz)[kGroups],
-                                 bool pass2) {
+                                 const double* s_cd, const float* s_nrm, const float* s_cng,
+                                 float (*s_y)[kYStride], uint8_t (*s_code)[kHeadDim],
+                                 const float2 (*s_sz)[kGroups], bool pass2) {
   const int t = threadIdx.x, q = t & 3;
   for (int k0 = 0; k0 < n; k0 += kPThreads / 4) {
     const int k = k0 + (t >> 2);
@@ -356,15 +375,16 @@ __device__ void recompute_listed(const uint16_t* __restrict__ list, int n,
     part += __shfl_xor(part, 1);
     part += __shfl_xor(part, 2);
     if (act && q == 0) {
-      float f = (float)part + 0.0f;   // the defined sum is never -0
-      const double tol = (double)s_nrm[r] * (double)s_cng[c / kGroup] * 0x1p-44;
+      const double v = part - s_cd[c];
+      float f = (float)v;
+      const double tol = (double)s_nrm[r] * (double)s_cng[c / kGroup] * 0x1p-44 + fabs(v) * 0x1p-50;
       const double m_lo = ((double)f + (double)down(f)) * 0.5;
       const double m_hi = ((double)f + (double)up(f)) * 0.5;
-      if (fabs(part - m_lo) <= tol || fabs(part - m_hi) <= tol) {
+      if (fabs(v - m_lo) <= tol || fabs(v - m_hi) <= tol || fabs(v) <= tol) {
         double acc = 0.0;
         for (int i = 0; i < kHeadDim; ++i)
           acc = __fma_rn((double)bf16_to_f32(s_x[r][i]), (double)s_rot[i][c], acc);
-        f = (float)acc;
+        f = (float)(acc - s_cd[c]);
       }
       s_y[r][c] = f;
       const float2 sz = s_sz[r][c / kGroup];
@@ -398,8 +418,8 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
     int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ new_offsets, const int32_t* __restrict__ start_pos,
-    const float* __restrict__ rot_k, const float* __restrict__ rot_v, float clip_k,
-    float clip_v) {
+    const float* __restrict__ rot_k, const float* __restrict__ rot_v,
+    const float* __restrict__ k_mean, float clip_k, float clip_v) {
 #pragma clang fp contract(off)
   __shared__ float s_rot[kHeadDim][kRStride];  // R (fp32), for the A operands and recomputation
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kPTile][kXStride];
@@ -411,6 +431,10 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
   __shared__ float s_err[kPTile];              // 64 u ||x|| per row, 5% high
   __shared__ float s_nrm[kPTile];              // ||x|| per row (rounded up)
   __shared__ float s_cng[kGroups];             // the largest ||R_.j|| of each group (rounded up)
+  __shared__ float s_mu[kHeadDim];             // key mean (centered K only)
+  __shared__ double s_cd[kHeadDim];            // C = mu . R (fp64; 0 without a mean)
+  __shared__ __attribute__((aligned(16))) float s_cf[kHeadDim];  // fp32(C)
+  __shared__ float s_cmax[kGroups];            // the largest |fp32(C_j)| of each group
   __shared__ int s_n[2];                       // list lengths of the two passes
 
   const int t = threadIdx.x, lane = t & 63;
@@ -421,6 +445,8 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
   const uint16_t* src = is_v ? v_new : k_new;
   const float clip = is_v ? clip_v : clip_k;
   const int m = lane & 15, kq = lane >> 4;
+  const bool centered = !is_v && k_mean != nullptr;
+  if (centered && t < kHeadDim) s_mu[t] = k_mean[(size_t)h * kHeadDim + t];
 
   // Stage R: all 8 float4 loads of a thread first, then the (unaligned-row) LDS stores.
   {
@@ -443,14 +469,27 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     float ss = 0.f;
     for (int i = 0; i < kHeadDim; ++i) ss = fmaf(s_rot[i][t], s_rot[i][t], ss);
     s_y[0][t] = ss;
+    // key mean: C_t = sum_i mu_i R_it, fp64, i ascending (exact products)
+    double cd = 0.0;
+    if (centered)
+      for (int i = 0; i < kHeadDim; ++i) cd = __fma_rn((double)s_mu[i], (double)s_rot[i][t], cd);
+    s_cd[t] = cd;
+    s_cf[t] = (float)cd;
   }
   __syncthreads();
   if (t < kGroups) {   // the largest per group, rounded up
-    float cm = 0.f;
-    for (int c = kGroup * t; c < kGroup * (t + 1); ++c) cm = fmaxf(cm, s_y[0][c]);
+    float cm = 0.f, cc = 0.f;
+    for (int c = kGroup * t; c < kGroup * (t + 1); ++c) {
+      cm = fmaxf(cm, s_y[0][c]);
+      cc = fmaxf(cc, fabsf(s_cf[c]));
+    }
     s_cng[t] = __builtin_sqrtf(cm) * 1.001f;
+    s_cmax[t] = cc;
   }
   __syncthreads();
+  // fp32(C) of this lane's four output channels (16w + 4kq + i), subtracted from the matrix-core
+  // sums; 0 without a mean
+  const float4 cfl = *reinterpret_cast<const float4*>(&s_cf[16 * wave + 4 * kq]);
 
   // A operands: lane (m, kq), slice s holds R[32s + 8kq + e][16w + m], e = 0..7, as 3 pieces.
   v8bf ra[4][3];
@@ -551,10 +590,10 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
         acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s][0], xb, acc[s], 0, 0, 0);
       }
       float4 y;
-      y.x = (acc[0][0] + acc[1][0]) + (acc[2][0] + acc[3][0]);
-      y.y = (acc[0][1] + acc[1][1]) + (acc[2][1] + acc[3][1]);
-      y.z = (acc[0][2] + acc[1][2]) + (acc[2][2] + acc[3][2]);
-      y.w = (acc[0][3] + acc[1][3]) + (acc[2][3] + acc[3][3]);
+      y.x = ((acc[0][0] + acc[1][0]) + (acc[2][0] + acc[3][0])) - cfl.x;
+      y.y = ((acc[0][1] + acc[1][1]) + (acc[2][1] + acc[3][1])) - cfl.y;
+      y.z = ((acc[0][2] + acc[1][2]) + (acc[2][2] + acc[3][2])) - cfl.z;
+      y.w = ((acc[0][3] + acc[1][3]) + (acc[2][3] + acc[3][3])) - cfl.w;
       // D row = channel 16w + 4kq + i, column = token 16tt + m
       *reinterpret_cast<float4*>(&s_y[16 * tt + m][16 * wave + 4 * kq]) = y;
     }
@@ -592,7 +631,8 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
       }
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mn = fminf(mn, __shfl_xor(mn, 1));
-      const float E = er * s_cng[gi] + kErrAbs;
+      const float E = er * s_cng[gi] + kErrAbs +
+                      (centered ? (s_cmax[gi] + 2.0f * fmaxf(fabsf(mx), fabsf(mn))) * 0x1p-22f : 0.0f);
       _Float16 s_hi, z_hi, s_lo, z_lo;
       group_params(mx + E, mn - E, clip, s_hi, z_lo);
       group_params(mx - E, mn + E, clip, s_lo, z_hi);
@@ -607,7 +647,7 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
       }
     }
     __syncthreads();
-    recompute_listed(s_list, s_n[0], s_rot, s_x, s_nrm, s_cng, s_y, s_code, s_sz, false);
+    recompute_listed(s_list, s_n[0], s_rot, s_x, s_cd, s_nrm, s_cng, s_y, s_code, s_sz, false);
     __syncthreads();
 
     // placement stage 3: page of the successor row
@@ -645,7 +685,8 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
         if (r < nrows && info.rec >= 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
       }
       const bool bf = info.sw >= 0;
-      const float Eg = er * s_cng[gi] + kErrAbs;
+      const float Eg = er * s_cng[gi] + kErrAbs +
+                       (centered ? (s_cmax[gi] + 2.0f * fmaxf(fabsf(mx), fabsf(mn))) * 0x1p-22f : 0.0f);
       const uint4 mk = *reinterpret_cast<const uint4*>(&s_code[r][c0]);
       const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
       uint32_t cw[4] = {0, 0, 0, 0};
@@ -679,7 +720,7 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
         }
     }
     __syncthreads();
-    recompute_listed(s_list, s_n[1], s_rot, s_x, s_nrm, s_cng, s_y, s_code, s_sz, true);
+    recompute_listed(s_list, s_n[1], s_rot, s_x, s_cd, s_nrm, s_cng, s_y, s_code, s_sz, true);
     __syncthreads();
 
     // placement stage 4: the successor row's record and sink/window row
@@ -749,8 +790,8 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int total_new, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* new_offsets, const int32_t* start_pos,
-                         const float* rot_k, const float* rot_v, float clip_k, float clip_v,
-                         int method, hipStream_t stream) {
+                         const float* rot_k, const float* rot_v, const float* k_mean,
+                         float clip_k, float clip_v, int method, hipStream_t stream) {
   if (batch == 0 || total_new == 0) return hipSuccess;
   if (method == kAppendAuto) method = total_new >= kMatrixAppendRows ? kAppendMatrix : kAppendVector;
   if (method == kAppendMatrix) {
@@ -765,7 +806,7 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
     const int per_pair = max(1, min(tiles, (cus + 2 * g.hkv - 1) / (2 * g.hkv)));
     hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_pair, g.hkv, 2), dim3(kPThreads), 0,
                        stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
-                       v_new, new_offsets, start_pos, rot_k, rot_v, clip_k, clip_v);
+                       v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v);
     return hipGetLastError();
   }
   // few rows: 4 per workgroup, so that the launch covers more CUs
@@ -773,12 +814,12 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
     dim3 grid((total_new + 3) / 4, g.hkv, 2);
     hipLaunchKernelGGL(rotate_quantize_append_kernel<4>, grid, dim3(kThreads), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
-                       start_pos, rot_k, rot_v, clip_k, clip_v);
+                       start_pos, rot_k, rot_v, k_mean, clip_k, clip_v);
   } else {
     dim3 grid((total_new + 15) / 16, g.hkv, 2);
     hipLaunchKernelGGL(rotate_quantize_append_kernel<16>, grid, dim3(kThreads), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
-                       start_pos, rot_k, rot_v, clip_k, clip_v);
+                       start_pos, rot_k, rot_v, k_mean, clip_k, clip_v);
   }
   return hipGetLastError();
 }

@@ -90,8 +90,8 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int total_new, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* new_offsets, const int32_t* start_pos,
-                         const float* rot_k, const float* rot_v, float clip_k, float clip_v,
-                         int method, hipStream_t stream);
+                         const float* rot_k, const float* rot_v, const float* k_mean,
+                         float clip_k, float clip_v, int method, hipStream_t stream);
 
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,

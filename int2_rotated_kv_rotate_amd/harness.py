@@ -52,7 +52,10 @@ def as_i16(a: np.ndarray) -> torch.Tensor:
 class GpuCache:
     """INT2 page pool + BF16 sink/window store + block table on the GPU."""
 
-    def __init__(self, p: Problem, device="cuda", fill: Optional[int] = None):
+    def __init__(self, p: Problem, device="cuda", fill: Optional[int] = None,
+                 k_mean: Optional[np.ndarray] = None):
+        """k_mean: None or fp32 [Hkv][128], a key mean removed before the key rotation on every
+        append into this cache."""
         w = p.w
         self.p = p
         self.device = device
@@ -70,6 +73,8 @@ class GpuCache:
         self.slots = torch.arange(w.batch, dtype=torch.int32, device=device)
         self.rot_k = torch.from_numpy(p.rot_k).to(device)
         self.rot_v = torch.from_numpy(p.rot_v).to(device)
+        self.k_mean = (None if k_mean is None else
+                       torch.from_numpy(np.ascontiguousarray(k_mean, dtype=np.float32)).to(device))
 
     def append(self, k_rows: Sequence[np.ndarray], v_rows: Sequence[np.ndarray],
                start: Sequence[int], method: int = ops.APPEND_AUTO):
@@ -86,7 +91,8 @@ class GpuCache:
             self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
             torch.from_numpy(offs).to(self.device),
             torch.from_numpy(np.asarray(start, dtype=np.int32)).to(self.device),
-            self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip, method=method)
+            self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip, method=method,
+            k_mean=self.k_mean)
 
     def fill_context(self, chunk_tokens: int = 1 << 20, keep_tail: int = 0):
         """Append positions [0, L_b - 1) of every sequence (everything but the decoded token),
@@ -184,7 +190,7 @@ class DecodeStep:
         c = self.cache
         ops.rotate_quantize_append(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.k_last,
                                    self.v_last, self.new_off, self.start, c.rot_k, c.rot_v,
-                                   c.p.w.clip, c.p.w.clip, stream)
+                                   c.p.w.clip, c.p.w.clip, stream, k_mean=c.k_mean)
 
     def decode_only(self, stream=None):
         c = self.cache

@@ -23,7 +23,7 @@ BF16_PAGE_ELEMS = 2 * PAGE_SIZE * HEAD_DIM
 EXPORTED = (
     "oscar_status_string",
     "oscar_rotate_quantize_append",
-    "oscar_rotate_quantize_append_method",
+    "oscar_rotate_quantize_append_ex",
     "oscar_decode_workspace_bytes",
     "oscar_decode_attention",
     "oscar_combine",
@@ -76,9 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_status_string.restype = ctypes.c_char_p
     lib.oscar_rotate_quantize_append.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P, F32, F32, P]
     lib.oscar_rotate_quantize_append.restype = I32
-    lib.oscar_rotate_quantize_append_method.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P,
-                                                        F32, F32, I32, P]
-    lib.oscar_rotate_quantize_append_method.restype = I32
+    lib.oscar_rotate_quantize_append_ex.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P, P,
+                                                    F32, F32, I32, P]
+    lib.oscar_rotate_quantize_append_ex.restype = I32
     lib.oscar_decode_workspace_bytes.argtypes = [I32, I32, I32]
     lib.oscar_decode_workspace_bytes.restype = SZ
     lib.oscar_decode_attention.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, F32, I32, I32, P, SZ, P]
@@ -123,19 +123,21 @@ APPEND_AUTO, APPEND_VECTOR, APPEND_MATRIX = 0, 1, 2
 
 def rotate_quantize_append(lay: Layout, pages, sinkwin, block_table, slot_ids, k_new, v_new,
                            new_offsets, start_pos, rot_k, rot_v, clip_k: float, clip_v: float,
-                           stream=None, method: int = APPEND_AUTO) -> None:
+                           stream=None, method: int = APPEND_AUTO, k_mean=None) -> None:
     """pages uint8 [P][Hkv][1536]; sinkwin int16 bf16 bits [slots][Hkv][S+W][2][128];
     k_new/v_new int16 bf16 bits [N][Hkv][128]; new_offsets int32 [B+1]; start_pos int32 [B];
-    rot_k/rot_v float32 [Hkv][128][128].  method: APPEND_AUTO, APPEND_VECTOR or APPEND_MATRIX."""
+    rot_k/rot_v float32 [Hkv][128][128].  method: APPEND_AUTO, APPEND_VECTOR or APPEND_MATRIX.
+    k_mean: None or float32 [Hkv][128], a key mean removed before the key rotation."""
     lib = load_library()
     batch = start_pos.numel()
-    _check("oscar_rotate_quantize_append_method", lib.oscar_rotate_quantize_append_method(
+    _check("oscar_rotate_quantize_append_ex", lib.oscar_rotate_quantize_append_ex(
         ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
         _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
         batch, k_new.shape[0], _ptr(k_new, torch.int16, "k_new"), _ptr(v_new, torch.int16, "v_new"),
         _ptr(new_offsets, torch.int32, "new_offsets"), _ptr(start_pos, torch.int32, "start_pos"),
         _ptr(rot_k, torch.float32, "rot_k"), _ptr(rot_v, torch.float32, "rot_v"),
-        float(clip_k), float(clip_v), int(method), _stream(stream)))
+        _ptr(k_mean, torch.float32, "k_mean"), float(clip_k), float(clip_v), int(method),
+        _stream(stream)))
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, max_splits: int) -> int:

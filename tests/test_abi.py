@@ -86,18 +86,19 @@ def test_append_validation(lib):
     assert _append(lib, _layout(), total=0) == 0
 
 
-def test_append_method_validation(lib):
+def test_append_ex_validation(lib):
     lay = _layout()
 
     def call(method, **kw):
         a = dict(pages=FAKE, batch=1)
         a.update(kw)
-        return lib.oscar_rotate_quantize_append_method(
+        return lib.oscar_rotate_quantize_append_ex(
             ctypes.byref(lay), a["pages"], FAKE, FAKE, None, a["batch"], 1, FAKE, FAKE, FAKE, FAKE,
-            FAKE, FAKE, 0.95, 0.95, method, None)
+            FAKE, FAKE, a.get("k_mean"), 0.95, 0.95, method, None)
 
     assert call(3) == 1
     assert call(-1) == 1
+    assert call(0, k_mean=ctypes.c_void_p(18)) == 1   # a misaligned key mean
     for m in (0, 1, 2):
         assert call(m, pages=None) == 1       # every method validates before launching
         assert call(m, batch=0) == 0          # nothing to do

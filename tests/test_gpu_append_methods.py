@@ -14,6 +14,8 @@ Cases:
     rotated value is tiny next to ||x||, so scales, zeros, codes and BF16 copies are uncertain
     and recomputed), zero rows, subnormal rows, a huge dynamic range within a row;
   * groups with max == -min (a code threshold exactly at zero), one-signed and constant groups;
+  * keys with a mean removed before the rotation (workload means, a large random mean, zero,
+    and the special rows with a mean);
   * the full prefill shape: 64 sequences x 2048 new tokens at the end of 16K-32K contexts
     (GPU against GPU: 2.1 million rows are beyond the oracle's seconds).
 """
@@ -37,29 +39,29 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def _append_both(p, k_rows, v_rows, start):
+def _append_both(p, k_rows, v_rows, start, k_mean=None):
     """GPU caches after appending with each method (one call each)."""
     out = {}
     for method in (ops.APPEND_VECTOR, ops.APPEND_MATRIX):
-        c = H.GpuCache(p, fill=SENTINEL)
+        c = H.GpuCache(p, fill=SENTINEL, k_mean=k_mean)
         c.append(k_rows, v_rows, start, method=method)
         torch.cuda.synchronize()
         out[method] = (c.pages.cpu().numpy(), c.sinkwin.cpu().numpy().view(np.uint16))
     return out
 
 
-def _oracle(p, k_rows, v_rows, start):
+def _oracle(p, k_rows, v_rows, start, k_mean=None):
     w = p.w
     oc = O.Cache(p.num_pages, w.num_kv_heads, w.batch, w.num_sink, w.window, fill=SENTINEL)
     for b in range(w.batch):
         if k_rows[b].shape[0]:
             oc.append(p.table[b], b, int(start[b]), k_rows[b], v_rows[b], p.rot_k, p.rot_v,
-                      w.clip, w.clip)
+                      w.clip, w.clip, k_mean)
     return oc
 
 
-def _check(name, p, k_rows, v_rows, start, with_oracle=True):
-    res = _append_both(p, k_rows, v_rows, start)
+def _check(name, p, k_rows, v_rows, start, with_oracle=True, k_mean=None):
+    res = _append_both(p, k_rows, v_rows, start, k_mean)
     (pv, sv), (pm, sm) = res[ops.APPEND_VECTOR], res[ops.APPEND_MATRIX]
     nd = int((pv != pm).sum())
     _log(f"[append] {name}: {sum(r.shape[0] for r in k_rows)} rows; vector vs matrix: "
@@ -67,7 +69,7 @@ def _check(name, p, k_rows, v_rows, start, with_oracle=True):
     assert nd == 0
     assert np.array_equal(sv, sm)
     if with_oracle:
-        oc = _oracle(p, k_rows, v_rows, start)
+        oc = _oracle(p, k_rows, v_rows, start, k_mean)
         assert np.array_equal(pm, oc.pages), f"{int((pm != oc.pages).sum())} bytes differ from the oracle"
         assert np.array_equal(sm, oc.sinkwin)
 
@@ -142,6 +144,40 @@ def test_special_rows():
     ks = [_special_rows(rng, p.rot_k, int(L)) for L in p.lens]
     vs = [_special_rows(rng, p.rot_v, int(L)) for L in p.lens]
     _check("special_rows", p, ks, vs, [0] * w.batch)
+
+
+@pytest.mark.parametrize("kind", ["workload_means", "large_random", "zero"])
+def test_key_mean(kind):
+    """Keys with a mean removed before the rotation: the workload's channel means, a large
+    random mean (|mu| ~ 30, so the centered values are small next to both terms), and a zero
+    mean (which must give exactly the bytes of no mean)."""
+    w = W.scaled(W.WORKLOADS["qwen3_8b_b64"], name="append_kmean", batch=2, ctx=900, ctx_min=500)
+    p = H.make_problem(w)
+    ks, vs = _workload_rows(w, p.lens)
+    if kind == "workload_means":
+        mu = W.key_channel_means(w)
+    elif kind == "large_random":
+        mu = (np.random.default_rng(21).standard_normal((w.num_kv_heads, 128)) * 30).astype(np.float32)
+    else:
+        mu = np.zeros((w.num_kv_heads, 128), np.float32)
+    _check("key_mean_" + kind, p, ks, vs, [0] * w.batch, k_mean=mu)
+    if kind == "zero":
+        plain = _oracle(p, ks, vs, [0] * w.batch)
+        centered = _oracle(p, ks, vs, [0] * w.batch, mu)
+        assert np.array_equal(plain.pages, centered.pages)
+
+
+def test_key_mean_special_rows():
+    """The special rows (see _special_rows) with a seeded mean: the certification of scales,
+    zeros, codes and BF16 copies with the mean's rounding in the error bound."""
+    w = W.scaled(W.WORKLOADS["qwen3_4b"], name="append_kmean_special", batch=2, ctx=600, ctx_min=500)
+    p = H.make_problem(w)
+    rng = np.random.default_rng(22)
+    ks = [_special_rows(rng, p.rot_k, int(L)) for L in p.lens]
+    vs = [_special_rows(rng, p.rot_v, int(L)) for L in p.lens]
+    mu = (rng.standard_normal((w.num_kv_heads, 128)) * 3).astype(np.float32)
+    mu[0, :64] = 0.0                     # some channels without a mean
+    _check("key_mean_special_rows", p, ks, vs, [0] * w.batch, k_mean=mu)
 
 
 def test_symmetric_groups():

@@ -32,20 +32,22 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def oracle_cache(p: H.Problem):
+def oracle_cache(p: H.Problem, k_mean=None):
     w = p.w
     cache = O.Cache(p.num_pages, w.num_kv_heads, w.batch, w.num_sink, w.window, fill=SENTINEL)
     needle = W.needle_site(w, p.lens)
     for b in range(w.batch):
         L = int(p.lens[b])
         kb, vb = W.sequence_kv(w, b, L, needle=needle, q_bits=p.q)
-        cache.append(p.table[b], b, 0, kb[:L - 1], vb[:L - 1], p.rot_k, p.rot_v, w.clip, w.clip)
-        cache.append(p.table[b], b, L - 1, kb[L - 1:], vb[L - 1:], p.rot_k, p.rot_v, w.clip, w.clip)
+        cache.append(p.table[b], b, 0, kb[:L - 1], vb[:L - 1], p.rot_k, p.rot_v, w.clip, w.clip,
+                     k_mean)
+        cache.append(p.table[b], b, L - 1, kb[L - 1:], vb[L - 1:], p.rot_k, p.rot_v, w.clip,
+                     w.clip, k_mean)
     return cache
 
 
-def run_gpu(p: H.Problem, num_workers=0, max_splits=H.DEFAULT_MAX_SPLITS):
-    cache = H.GpuCache(p, fill=SENTINEL)
+def run_gpu(p: H.Problem, num_workers=0, max_splits=H.DEFAULT_MAX_SPLITS, k_mean=None):
+    cache = H.GpuCache(p, fill=SENTINEL, k_mean=k_mean)
     last_k, last_v = cache.fill_context()
     step = H.DecodeStep(cache, num_workers=num_workers, max_splits=max_splits)
     step.set_new_token(last_k, last_v)
@@ -102,6 +104,45 @@ def test_append_and_decode_parity(name):
     assert np.all(np.isfinite(out))
     assert rel.max() <= TOL
     assert np.abs(lse - ref_lse).max() <= TOL
+
+
+def test_key_mean_decode():
+    """A cache whose keys had the workload's channel means removed before the rotation: pages
+    equal to the oracle's, out within 2e-3 of the oracle's decode of that cache, lse of the
+    centered logits; and the INT2 output is closer to the exact attention over the unquantised
+    keys than without the mean (the point of removing it)."""
+    w = W.scaled(W.WORKLOADS["qwen3_8b_b64"], name="kmean_decode", batch=3, ctx=1500, ctx_min=800)
+    p = H.make_problem(w)
+    mu = W.key_channel_means(w)
+    cache, step = run_gpu(p, 0, H.DEFAULT_MAX_SPLITS, k_mean=mu)
+    oc = oracle_cache(p, mu)
+    assert np.array_equal(cache.pages.cpu().numpy(), oc.pages)
+    assert np.array_equal(cache.sinkwin.cpu().numpy().view(np.uint16), oc.sinkwin)
+    ref, ref_lse = O.decode_attention(oc, p.table, np.arange(w.batch), p.lens, p.q, p.rot_k,
+                                      p.rot_v, H.SM_SCALE)
+    out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
+    rel = row_errors(out, ref)
+    _log(f"[parity] key mean: max row rel err {rel.max():.3e}, "
+         f"max |dlse| {np.abs(lse - ref_lse).max():.3e}")
+    assert rel.max() <= TOL
+    assert np.abs(lse - ref_lse).max() <= TOL
+    # against the exact attention over the unquantised, unrotated keys and values
+    _, plain = run_gpu(p, 0, H.DEFAULT_MAX_SPLITS)
+    err_c, err_p = [], []
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        L = int(p.lens[b])
+        kb, vb = W.sequence_kv(w, b, L)
+        for j in range(w.num_q_heads):
+            h = j // G
+            q = O.bf16_bits_to_f64(p.q[b, j])
+            o_ex, _, _ = O.softmax_attention(q, O.bf16_bits_to_f64(kb[:, h]),
+                                             O.bf16_bits_to_f64(vb[:, h]), H.SM_SCALE)
+            err_c.append(np.abs(out[b, j] - o_ex).max() / np.abs(o_ex).max())
+            err_p.append(np.abs(plain.out.cpu().numpy()[b, j] - o_ex).max() / np.abs(o_ex).max())
+    _log(f"[parity] key mean: error vs exact attention {np.mean(err_c):.4f} (centered) vs "
+         f"{np.mean(err_p):.4f} (plain)")
+    assert np.mean(err_c) < np.mean(err_p)
 
 
 def test_split_size_and_permutation_invariance():
