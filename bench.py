@@ -294,10 +294,12 @@ def main():
         offs_d = torch.from_numpy(offs).cuda()
         start_d = torch.from_numpy((p.lens - 1 - tail).astype(np.int32)).cuda()
 
-        def do_prefill(method=ops.APPEND_AUTO):
+        kmean_d = torch.from_numpy(W.key_channel_means(w)).cuda()
+
+        def do_prefill(method=ops.APPEND_AUTO, k_mean=None):
             ops.rotate_quantize_append(cache.layout, cache.pages, cache.sinkwin, cache.table,
                                        cache.slots, kt, vt, offs_d, start_d, cache.rot_k,
-                                       cache.rot_v, w.clip, w.clip, method=method)
+                                       cache.rot_v, w.clip, w.clip, method=method, k_mean=k_mean)
         do_prefill()
         torch.cuda.synchronize()
 
@@ -365,12 +367,14 @@ def main():
         # matrix-core one, and the fp64 vector kernel is timed beside it.
         reps = 3
         pf = {}
-        for name, method in (("matrix", ops.APPEND_MATRIX), ("vector", ops.APPEND_VECTOR)):
-            do_prefill(method)
+        for name, method, mean in (("matrix", ops.APPEND_MATRIX, None),
+                                   ("vector", ops.APPEND_VECTOR, None),
+                                   ("matrix_key_mean", ops.APPEND_MATRIX, kmean_d)):
+            do_prefill(method, mean)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(reps):
-                do_prefill(method)
+                do_prefill(method, mean)
             b.record(stream)
             torch.cuda.synchronize()
             pf[name] = a.elapsed_time(b) / reps
@@ -382,9 +386,11 @@ def main():
                    "tokens_per_s": round(n_new / (pf_ms / 1e3), 1),
                    "effective_gbps": round(pf_bytes / (pf_ms / 1e3) / 1e9, 1),
                    "rotation": "bf16 matrix cores, certified, uncertain values recomputed in fp64",
-                   "fp64_vector_kernel_ms": round(pf["vector"], 4)}
+                   "fp64_vector_kernel_ms": round(pf["vector"], 4),
+                   "with_key_mean_ms": round(pf["matrix_key_mean"], 4)}
         log(f"prefill append {n_new} tokens: matrix cores {pf_ms:.3f} ms, fp64 vector "
-            f"{pf['vector']:.3f} ms")
+            f"{pf['vector']:.3f} ms, matrix cores with a key mean {pf['matrix_key_mean']:.3f} ms")
+        do_prefill(ops.APPEND_MATRIX)  # the cache without the key mean again
         step.run()  # restore the window rows the prefill re-append rewrote
         torch.cuda.synchronize()
 

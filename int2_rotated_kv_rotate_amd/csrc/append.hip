@@ -541,10 +541,16 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
                          blockIdx.x * kPTile + t, h, is_v);
   }
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // Round k takes tile k * G + (x + k) mod G (G workgroups per pair, x this one), one tile of
+  // each block of G; the rotation spreads tiles that cost more (e.g. the last rows of every
+  // sequence, whose BF16 copies are certified too) over all workgroups.  Successive tiles of a
+  // workgroup increase, as the placement look-ahead needs.
+  const int G = gridDim.x, x0 = blockIdx.x;
+  auto tile_of = [&](int k) { return k * G + (x0 + k) % G; };   // tile_of(0) == blockIdx.x
+  for (int k = 0, tile = x0; tile < ntiles; ++k, tile = tile_of(k)) {
     const int row0 = tile * kPTile;
     const int nrows = min(kPTile, total_new - row0);
-    const int nt = tile + gridDim.x;   // the successor tile
+    const int nt = tile_of(k + 1);     // the successor tile
     const int n_next = nt * kPTile + t;
     const bool look = t < kPTile && nt < ntiles && n_next < total_new;
 

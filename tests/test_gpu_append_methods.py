@@ -8,8 +8,9 @@ byte, and (except at the full prefill size) equal to the oracle's.
 Cases:
   * the Qwen3-8B layer workload (per-channel offsets, x15 outlier key channels), ragged
     lengths, one call per batch;
-  * special rotations: identity and a signed permutation (rotation exact in any order), and an
-    orthogonal matrix scaled by 2.5 (column norms far from 1);
+  * special rotations: identity and a signed permutation (rotation exact in any order), an
+    orthogonal matrix scaled by 2.5 (column norms far from 1), and the offline spectral
+    rotation (eigenbasis of a calibration covariance) with the calibrated key mean;
   * special rows with a seeded orthogonal rotation: rows along a column of R (every other
     rotated value is tiny next to ||x||, so scales, zeros, codes and BF16 copies are uncertain
     and recomputed), zero rows, subnormal rows, a huge dynamic range within a row;
@@ -27,6 +28,7 @@ import torch
 
 from oracle import oscar_oracle as O
 from int2_rotated_kv_rotate_amd import harness as H
+from int2_rotated_kv_rotate_amd import offline as OF
 from int2_rotated_kv_rotate_amd import ops
 from int2_rotated_kv_rotate_amd import workload as W
 
@@ -99,11 +101,16 @@ def _signed_permutation(rng, hkv):
     return out
 
 
-@pytest.mark.parametrize("kind", ["identity", "signed_permutation", "scaled"])
+@pytest.mark.parametrize("kind", ["identity", "signed_permutation", "scaled", "spectral"])
 def test_special_rotations(kind):
     w = W.scaled(W.WORKLOADS["qwen3_4b"], name="append_rot_" + kind, batch=2, ctx=700, ctx_min=300)
     rng = np.random.default_rng(11)
-    if kind == "identity":
+    k_mean = None
+    if kind == "spectral":   # offline calibration on another sequence's rows, keys centered
+        wc = W.scaled(W.WORKLOADS["qwen3_4b"], name="calib", batch=3, ctx=1024)
+        kc, vc = W.sequence_kv(wc, 2, 1024)
+        rk, rv, k_mean = OF.calibrate(kc, vc)
+    elif kind == "identity":
         rk = np.broadcast_to(np.eye(128), (w.num_kv_heads, 128, 128)).copy()
         rv = rk.copy()
     elif kind == "signed_permutation":
@@ -112,7 +119,7 @@ def test_special_rotations(kind):
         rk, rv = 2.5 * W.rotations(w, "k"), 2.5 * W.rotations(w, "v")
     p = H.make_problem(w, rot_k=rk, rot_v=rv)
     ks, vs = _workload_rows(w, p.lens)
-    _check(kind, p, ks, vs, [0] * w.batch)
+    _check(kind, p, ks, vs, [0] * w.batch, k_mean=k_mean)
 
 
 def _special_rows(rng, rot32, n):
