@@ -118,6 +118,50 @@ def rotate_rows_centered(x_bits: np.ndarray, rot32: np.ndarray, mean32) -> np.nd
     return (acc - mean_shift(mean32, rot32)[None, :]).astype(np.float32)
 
 
+# Hadamard rotation: R = diag(s) . H / sqrt(128), H the Sylvester-Hadamard matrix of order 128
+# (H_ij = (-1)^popcount(i & j)) and s a fixed sign per input channel.  The paper's page ("OSCAR:
+# Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization", the OSCAR and
+# INT4 abstracts) names Hadamard transforms as the simple rotation that reduces outliers
+# (block-diagonal in the INT4 work).  Reading taken here for its arithmetic: the signed row goes
+# through the fast Walsh-Hadamard transform in fp64 (stages h = 1, 2, 4, ..., 64; the pair
+# (a, b) = (u_i, u_{i+h}) becomes (a + b, a - b)), each result is multiplied in fp64 by the
+# double nearest to 1/sqrt(128), and rounded once more to fp32.
+
+HADAMARD_SCALE = float(np.sqrt(np.float64(2.0)) / 16.0)   # nearest double to 2^-3.5
+
+
+def fwht(u: np.ndarray) -> np.ndarray:
+    """Unnormalised fast Walsh-Hadamard transform of fp64 rows [N][128], stage by stage."""
+    v = np.array(u, dtype=np.float64, copy=True)
+    h = 1
+    while h < D:
+        for start in range(0, D, 2 * h):
+            a = v[:, start:start + h].copy()
+            b = v[:, start + h:start + 2 * h].copy()
+            v[:, start:start + h] = a + b
+            v[:, start + h:start + 2 * h] = a - b
+        h *= 2
+    return v
+
+
+def rotate_rows_hadamard(x_bits: np.ndarray, signs) -> np.ndarray:
+    """y = x . diag(s) H / sqrt(128) for bf16 rows: fp64 FWHT of the signed row, times
+    HADAMARD_SCALE in fp64, rounded to fp32.  signs: [128] of +-1 (a negative entry flips the
+    channel) or None for all +1.  Returns float32 [N][128]."""
+    x = bf16_bits_to_f64(x_bits)
+    if signs is not None:
+        x = x * np.where(np.asarray(signs) < 0, -1.0, 1.0)[None, :]
+    return (fwht(x) * HADAMARD_SCALE).astype(np.float32)
+
+
+def hadamard_rotation32(signs) -> np.ndarray:
+    """The dense fp32 matrix of the same rotation, fp32(s_i H_ij / sqrt(128)), for the parts of
+    the path that take a dense R (q rotation, R_V^T)."""
+    s = np.ones(D) if signs is None else np.where(np.asarray(signs) < 0, -1.0, 1.0)
+    h = fwht(np.eye(D))          # row i = H e_i = row i of H (H is symmetric)
+    return (s[:, None] * h * HADAMARD_SCALE).astype(np.float32)
+
+
 def rotate_query(q_bits: np.ndarray, rot_k32: np.ndarray, group: int) -> np.ndarray:
     """q' = q . R_K(h) in fp64 for each query head; query head j reads KV head j // group.
 
@@ -186,10 +230,14 @@ def dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
     return v.reshape(-1, D)
 
 
-def quantize_rows(x_bits: np.ndarray, rot32: np.ndarray, clip: float, mean32=None):
+def quantize_rows(x_bits: np.ndarray, rot32, clip: float, mean32=None, hadamard_signs=None):
     """Rotate (after removing mean32, if given), clip and quantise rows: returns (y fp32,
-    codes u8, s16, z16)."""
-    y = rotate_rows_centered(x_bits, rot32, mean32)
+    codes u8, s16, z16).  With rot32 None the rotation is the Hadamard one with the given
+    signs (rotate_rows_hadamard)."""
+    if rot32 is None:
+        y = rotate_rows_hadamard(x_bits, hadamard_signs)
+    else:
+        y = rotate_rows_centered(x_bits, rot32, mean32)
     s16, z16 = group_params(y, clip)
     return y, group_codes(y, s16, z16), s16, z16
 
@@ -339,22 +387,31 @@ class Cache:
         return (pages * self.hkv + h) * RECORD, np.asarray(positions) % PAGE
 
     def append(self, table_row, slot, start_pos, k_bits, v_bits, rot_k32, rot_v32, clip_k, clip_v,
-               k_mean32=None):
+               k_mean32=None, hadamard_signs=None):
         """Append n new tokens of one sequence at positions start_pos .. start_pos+n-1.
 
         k_bits, v_bits: uint16 [n][Hkv][128] unrotated bf16 rows.  Every new position gets its
         INT2 encoding in its page record; sink positions and the last W positions of the new
         length also get bf16(y) in the BF16 store.  k_mean32 (fp32 [Hkv][128] or None): a key
-        mean removed before the rotation (rotate_rows_centered).
+        mean removed before the rotation (rotate_rows_centered).  With rot_k32 and rot_v32 None
+        the rotation is the Hadamard one; hadamard_signs is then None or a pair (signs_k,
+        signs_v), each None or [Hkv][128].
         """
         n = k_bits.shape[0]
         new_len = start_pos + n
         positions = np.arange(start_pos, new_len)
         flat = self.pages.reshape(-1)
         for h in range(self.hkv):
-            yk, kc, ks, kz = quantize_rows(k_bits[:, h], rot_k32[h], clip_k,
-                                           None if k_mean32 is None else k_mean32[h])
-            yv, vc, vs, vz = quantize_rows(v_bits[:, h], rot_v32[h], clip_v)
+            if rot_k32 is None:
+                sk, sv = hadamard_signs if hadamard_signs is not None else (None, None)
+                yk, kc, ks, kz = quantize_rows(k_bits[:, h], None, clip_k, None,
+                                               None if sk is None else sk[h])
+                yv, vc, vs, vz = quantize_rows(v_bits[:, h], None, clip_v, None,
+                                               None if sv is None else sv[h])
+            else:
+                yk, kc, ks, kz = quantize_rows(k_bits[:, h], rot_k32[h], clip_k,
+                                               None if k_mean32 is None else k_mean32[h])
+                yv, vc, vs, vz = quantize_rows(v_bits[:, h], rot_v32[h], clip_v)
             base, r = self._bases(table_row, h, positions)
             write_slots(flat, base, r, kc, ks, kz, vc, vs, vz)
             kb = f32_to_bf16_bits(yk)
