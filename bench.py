@@ -295,6 +295,13 @@ def main():
         start_d = torch.from_numpy((p.lens - 1 - tail).astype(np.int32)).cuda()
 
         kmean_d = torch.from_numpy(W.key_channel_means(w)).cuda()
+        from int2_rotated_kv_rotate_amd import offline as OF
+        signs_d = [torch.from_numpy(OF.hadamard_signs(seed, w.num_kv_heads)).cuda() for seed in (1, 2)]
+
+        def do_prefill_hadamard():
+            ops.rotate_quantize_append_hadamard(cache.layout, cache.pages, cache.sinkwin,
+                                                cache.table, cache.slots, kt, vt, offs_d, start_d,
+                                                signs_d[0], signs_d[1], w.clip, w.clip)
 
         def do_prefill(method=ops.APPEND_AUTO, k_mean=None):
             ops.rotate_quantize_append(cache.layout, cache.pages, cache.sinkwin, cache.table,
@@ -367,14 +374,16 @@ def main():
         # matrix-core one, and the fp64 vector kernel is timed beside it.
         reps = 3
         pf = {}
-        for name, method, mean in (("matrix", ops.APPEND_MATRIX, None),
-                                   ("vector", ops.APPEND_VECTOR, None),
-                                   ("matrix_key_mean", ops.APPEND_MATRIX, kmean_d)):
-            do_prefill(method, mean)
+        cases = (("matrix", lambda: do_prefill(ops.APPEND_MATRIX)),
+                 ("vector", lambda: do_prefill(ops.APPEND_VECTOR)),
+                 ("matrix_key_mean", lambda: do_prefill(ops.APPEND_MATRIX, kmean_d)),
+                 ("hadamard", do_prefill_hadamard))
+        for name, fn in cases:
+            fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(reps):
-                do_prefill(method, mean)
+                fn()
             b.record(stream)
             torch.cuda.synchronize()
             pf[name] = a.elapsed_time(b) / reps
@@ -387,9 +396,12 @@ def main():
                    "effective_gbps": round(pf_bytes / (pf_ms / 1e3) / 1e9, 1),
                    "rotation": "bf16 matrix cores, certified, uncertain values recomputed in fp64",
                    "fp64_vector_kernel_ms": round(pf["vector"], 4),
-                   "with_key_mean_ms": round(pf["matrix_key_mean"], 4)}
+                   "with_key_mean_ms": round(pf["matrix_key_mean"], 4),
+                   "hadamard_rotation_ms": round(pf["hadamard"], 4),
+                   "hadamard_effective_gbps": round(pf_bytes / (pf["hadamard"] / 1e3) / 1e9, 1)}
         log(f"prefill append {n_new} tokens: matrix cores {pf_ms:.3f} ms, fp64 vector "
-            f"{pf['vector']:.3f} ms, matrix cores with a key mean {pf['matrix_key_mean']:.3f} ms")
+            f"{pf['vector']:.3f} ms, matrix cores with a key mean {pf['matrix_key_mean']:.3f} ms, "
+            f"Hadamard rotation {pf['hadamard']:.3f} ms")
         do_prefill(ops.APPEND_MATRIX)  # the cache without the key mean again
         step.run()  # restore the window rows the prefill re-append rewrote
         torch.cuda.synchronize()

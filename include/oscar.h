@@ -163,6 +163,32 @@ int32_t oscar_rotate_quantize_append_ex(
     int32_t method, void* stream);
 
 /*
+ * oscar_rotate_quantize_append with the Hadamard rotation R = diag(s) . H / sqrt(128) (H the
+ * Sylvester-Hadamard matrix of order 128, H_ij = (-1)^popcount(i & j), s a fixed sign per input
+ * channel) for both K and V: the rotation the OSCAR paper's page ("OSCAR: Offline Spectral
+ * Covariance-Aware Rotation for 2-bit KV Cache Quantization", OSCAR and INT4 abstracts) names as
+ * the simple outlier-reducing baseline.  For every new row x:
+ *   u_i = -x_i where signs[h][i] < 0, else x_i;
+ *   T = fast Walsh-Hadamard transform of u in fp64, stages h = 1, 2, 4, ..., 64, the pair
+ *       (u_i, u_{i+h}) (i in the lower half of its block) becoming (u_i + u_{i+h}, u_i - u_{i+h});
+ *   y_j = fp32( fp64(T_j * r) ), r = the double nearest to 1/sqrt(128);
+ * then the same groups, scales, zeros, codes, records and BF16 copies as
+ * oscar_rotate_quantize_append.  No matrix is read.  Attention over such a cache takes the dense
+ * fp32 form R_ij = fp32(s_i H_ij r) as rot_k (oscar_decode_attention) and rot_v (oscar_combine).
+ *
+ *   signs_k, signs_v  NULLABLE int8 [Hkv][128] (device); NULL means every sign +1.
+ * Other arguments, validation and errors as oscar_rotate_quantize_append.
+ */
+int32_t oscar_rotate_quantize_append_hadamard(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const int8_t* signs_k, const int8_t* signs_v, float clip_k, float clip_v,
+    void* stream);
+
+/*
  * Bytes of workspace oscar_decode_attention / oscar_bf16_decode_attention need for `batch`
  * sequences of `num_q_heads` query heads split at most `max_splits` ways.  Returns 0 for
  * invalid arguments.

@@ -102,6 +102,30 @@ int32_t oscar_rotate_quantize_append(
                                          rot_v, nullptr, clip_k, clip_v, OSCAR_APPEND_AUTO, stream);
 }
 
+int32_t oscar_rotate_quantize_append_hadamard(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const int8_t* signs_k, const int8_t* signs_v, float clip_k, float clip_v,
+    void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || total_new == 0) return OSCAR_OK;
+  if (!pages || !block_table || !k_new || !v_new || !new_offsets || !start_pos)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new) || (sinkwin && !aligned16(sinkwin)))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_append_hadamard(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                           total_new, k_new, v_new, new_offsets, start_pos,
+                                           signs_k, signs_v, clip_k, clip_v, (hipStream_t)stream));
+}
+
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits) {
   if (batch < 0 || num_q_heads < 1 || max_splits < 1) return 0;
   return workspace_bytes(batch, num_q_heads, max_splits);

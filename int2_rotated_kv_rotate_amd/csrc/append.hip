@@ -790,7 +790,197 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
   }
 }
 
+// ------------------------------------------------------------------ Hadamard rotation
+//
+// R = diag(s) . H / sqrt(128) with H the Sylvester-Hadamard matrix of order 128: the signed row
+// goes through the fast Walsh-Hadamard transform in fp64 (stages h = 1, 2, ..., 64, the pair
+// (u_i, u_{i+h}) becoming (u_i + u_{i+h}, u_i - u_{i+h})), each result is multiplied in fp64 by
+// the double nearest to 1/sqrt(128) and rounded to fp32.  896 additions per row instead of
+// 16,384 multiply-adds, so no matrix and no certification.
+//
+// One wavefront per row at a time: lane l holds channels 2l and 2l + 1; stage h = 1 is inside
+// the lane and stage h = 2m pairs lane l with lane l ^ m.  Each wave takes a contiguous range
+// of rows (the row's sequence, page and slot advance incrementally, the next page id is read
+// ahead) and loads the next kHadBatch rows while it computes the current ones.  Group g
+// (channels 32g .. 32g + 31) is lanes 16g .. 16g + 15.
+
+constexpr double kHadScale = 0x1.6a09e667f3bcdp-4;   // the double nearest to 2^-3.5 (sqrt(2)/16)
+constexpr int kHadWaves = 4;
+constexpr int kHadBatch = 8;
+
+__global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kernel(
+    CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
+    int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ new_offsets, const int32_t* __restrict__ start_pos,
+    const int8_t* __restrict__ signs_k, const int8_t* __restrict__ signs_v, float clip_k,
+    float clip_v) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const uint16_t* src = is_v ? v_new : k_new;
+  const int8_t* sg = is_v ? signs_v : signs_k;
+  const float clip = is_v ? clip_v : clip_k;
+  const bool neg0 = sg != nullptr && sg[h * kHeadDim + 2 * lane] < 0;
+  const bool neg1 = sg != nullptr && sg[h * kHeadDim + 2 * lane + 1] < 0;
+  const int nwaves = gridDim.x * kHadWaves;
+  const int per = (total_new + nwaves - 1) / nwaves;
+  const int n0 = min(total_new, (int)(blockIdx.x * kHadWaves + wave) * per);
+  const int n1 = min(total_new, n0 + per);
+  if (n0 >= n1) return;
+  const int gi = lane >> 4;
+
+  auto load_row = [&](int n) -> uint32_t {
+    return *reinterpret_cast<const uint32_t*>(src + ((size_t)n * g.hkv + h) * kHeadDim + 2 * lane);
+  };
+  int seq = row_to_seq(new_offsets, batch, n0);
+  int first = new_offsets[seq], next_first = new_offsets[seq + 1];
+  int sp = start_pos[seq];
+  int slot = slot_ids ? slot_ids[seq] : seq;
+  int lp_cached = -1, page = -1, page_ahead = -1;
+  uint32_t cur[kHadBatch], nxt[kHadBatch];
+#pragma unroll
+  for (int u = 0; u < kHadBatch; ++u) cur[u] = n0 + u < n1 ? load_row(n0 + u) : 0u;
+  for (int nb = n0; nb < n1; nb += kHadBatch) {
+#pragma unroll
+    for (int u = 0; u < kHadBatch; ++u) nxt[u] = nb + kHadBatch + u < n1 ? load_row(nb + kHadBatch + u) : 0u;
+#pragma unroll 1
+    for (int u = 0; u < kHadBatch; ++u) {
+      const int n = nb + u;
+      if (n >= n1) break;
+      uint32_t xw = 0u;
+#pragma unroll
+      for (int k = 0; k < kHadBatch; ++k)
+        if (k == u) xw = cur[k];
+      if (n >= next_first) {   // the row starts a later sequence (rows are consecutive)
+        seq = advance_seq(new_offsets, batch, seq + 1, n);
+        first = new_offsets[seq];
+        next_first = new_offsets[seq + 1];
+        sp = start_pos[seq];
+        slot = slot_ids ? slot_ids[seq] : seq;
+        lp_cached = -1;
+        page_ahead = -1;
+      }
+      // fp64 transform of the signed row
+      double a = (double)bf16_lo(xw), b = (double)bf16_hi(xw);
+      if (neg0) a = -a;
+      if (neg1) b = -b;
+      {
+        const double s0 = a + b, d0 = a - b;
+        a = s0;
+        b = d0;
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const double pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
+        const bool upper = (lane & m) != 0;   // lower: a + partner; upper: partner - a
+        a = pa + (upper ? -a : a);
+        b = pb + (upper ? -b : b);
+      }
+      const float y0 = (float)(a * kHadScale), y1 = (float)(b * kHadScale);
+
+      // group extremes over the 16 lanes of the group, scale/zero, codes
+      float mx = fmaxf(y0, y1), mn = fminf(y0, y1);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+        mn = fminf(mn, __shfl_xor(mn, o));
+      }
+      _Float16 s16, z16;
+      group_params(mx, mn, clip, s16, z16);
+      const float sc = (float)s16, z = (float)z16;
+      const uint32_t c0 = (uint32_t)code_of(y0, sc, z), c1 = (uint32_t)code_of(y1, sc, z);
+
+      // placement
+      const int pos = sp + (n - first);
+      const int new_len = sp + (next_first - first);
+      const int lp = pos / kPage;
+      if (lp != lp_cached) {
+        page = (lp == lp_cached + 1 && lp_cached >= 0) ? page_ahead
+               : ((pos >= 0 && lp < g.max_pages) ? block_table[(size_t)seq * g.max_pages + lp] : -1);
+        lp_cached = lp;
+        page_ahead = (pos >= 0 && lp + 1 < g.max_pages) ? block_table[(size_t)seq * g.max_pages + lp + 1]
+                                                       : -1;
+      }
+      RowInfo info{-1, 0, -1};
+      if (pos >= 0 && page >= 0 && page < g.num_pages && lp < g.max_pages) {
+        info.rec = ((long long)page * g.hkv + h) * kRecord;
+        info.slot_in_page = pos % kPage;
+      }
+      int row = -1;
+      if (pos >= 0 && pos < g.num_sink) row = pos;
+      else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
+        row = g.num_sink + pos % g.window;
+      if (row >= 0 && sinkwin != nullptr && slot >= 0 && slot < g.num_slots)
+        info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
+                  (is_v ? kHeadDim : 0);
+
+      if (info.rec >= 0) {
+        if ((lane & 15) == 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
+        const int sl = info.slot_in_page;
+        if (!is_v) {
+          // K word d = lane / 8 (channels 16d .. 16d + 15); channel 2l + e sits at byte
+          // (l % 8) / 2, bits 2 * (2 * (l % 2) + e)
+          const int sh = 8 * ((lane & 7) >> 1) + 4 * (lane & 1);
+          uint32_t w = (c0 << sh) | (c1 << (sh + 2));
+          w |= __shfl_xor(w, 1);
+          w |= __shfl_xor(w, 2);
+          w |= __shfl_xor(w, 4);
+          if ((lane & 7) == 0) {
+            const int d = lane >> 3;
+            *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes + 8 * (16 * (d % 4) + sl) +
+                                         4 * (d / 4)) = w;
+          }
+        } else {
+          // V half of channel residue k = (2l + e) % 16 holds channel k + 16 nb at bits 2 nb,
+          // nb = l / 8: lanes l % 8 == k / 2 combine
+          uint32_t v0 = c0 << (2 * (lane >> 3)), v1 = c1 << (2 * (lane >> 3));
+          v0 |= __shfl_xor(v0, 8);
+          v1 |= __shfl_xor(v1, 8);
+          v0 |= __shfl_xor(v0, 16);
+          v1 |= __shfl_xor(v1, 16);
+          v0 |= __shfl_xor(v0, 32);
+          v1 |= __shfl_xor(v1, 32);
+          if (lane < 8) {
+            uint8_t* base = pages + info.rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
+            *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + 2 * lane)) = (uint16_t)v0;
+            *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + 2 * lane + 1)) = (uint16_t)v1;
+          }
+        }
+      }
+      if (info.sw >= 0)
+        *reinterpret_cast<uint32_t*>(sinkwin + info.sw + 2 * lane) =
+            (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kHadBatch; ++u) cur[u] = nxt[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_hadamard(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                                  const int32_t* block_table, const int32_t* slot_ids, int batch,
+                                  int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                                  const int32_t* new_offsets, const int32_t* start_pos,
+                                  const int8_t* signs_k, const int8_t* signs_v, float clip_k,
+                                  float clip_v, hipStream_t stream) {
+  if (batch == 0 || total_new == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  // about 8 waves per SIMD over the 2 * Hkv (head, K|V) pairs; at least one row per wave
+  const int want = max(1, 32 * cus / (2 * g.hkv * kHadWaves));
+  const int blocks = max(1, min(want, (total_new + kHadWaves - 1) / kHadWaves));
+  hipLaunchKernelGGL(rotate_quantize_hadamard_kernel, dim3(blocks, g.hkv, 2), dim3(64 * kHadWaves),
+                     0, stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
+                     v_new, new_offsets, start_pos, signs_k, signs_v, clip_k, clip_v);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,

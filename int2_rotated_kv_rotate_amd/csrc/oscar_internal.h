@@ -93,6 +93,15 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                          const float* rot_k, const float* rot_v, const float* k_mean,
                          float clip_k, float clip_v, int method, hipStream_t stream);
 
+// Append with the Hadamard rotation diag(s) . H / sqrt(128) (fp64 fast transform); signs
+// int8 [Hkv][128] (negative flips the input channel) or NULL for all +1.
+hipError_t launch_append_hadamard(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                                  const int32_t* block_table, const int32_t* slot_ids, int batch,
+                                  int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                                  const int32_t* new_offsets, const int32_t* start_pos,
+                                  const int8_t* signs_k, const int8_t* signs_v, float clip_k,
+                                  float clip_v, hipStream_t stream);
+
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,

@@ -53,9 +53,11 @@ class GpuCache:
     """INT2 page pool + BF16 sink/window store + block table on the GPU."""
 
     def __init__(self, p: Problem, device="cuda", fill: Optional[int] = None,
-                 k_mean: Optional[np.ndarray] = None):
+                 k_mean: Optional[np.ndarray] = None, hadamard_signs=None):
         """k_mean: None or fp32 [Hkv][128], a key mean removed before the key rotation on every
-        append into this cache."""
+        append into this cache.  hadamard_signs: None for the dense rotations p.rot_k / p.rot_v,
+        else a pair (signs_k, signs_v) (each None or int8 [Hkv][128]) for appends with the
+        Hadamard rotation; p.rot_k / p.rot_v must then be its dense form (attention reads them)."""
         w = p.w
         self.p = p
         self.device = device
@@ -75,6 +77,10 @@ class GpuCache:
         self.rot_v = torch.from_numpy(p.rot_v).to(device)
         self.k_mean = (None if k_mean is None else
                        torch.from_numpy(np.ascontiguousarray(k_mean, dtype=np.float32)).to(device))
+        self.hadamard = hadamard_signs is not None
+        self.signs = tuple(None if sg is None else
+                           torch.from_numpy(np.ascontiguousarray(sg, dtype=np.int8)).to(device)
+                           for sg in (hadamard_signs or (None, None)))
 
     def append(self, k_rows: Sequence[np.ndarray], v_rows: Sequence[np.ndarray],
                start: Sequence[int], method: int = ops.APPEND_AUTO):
@@ -87,6 +93,13 @@ class GpuCache:
         offs[1:] = np.cumsum(counts)
         k = as_i16(np.concatenate(k_rows)).to(self.device)
         v = as_i16(np.concatenate(v_rows)).to(self.device)
+        if self.hadamard:
+            ops.rotate_quantize_append_hadamard(
+                self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
+                torch.from_numpy(offs).to(self.device),
+                torch.from_numpy(np.asarray(start, dtype=np.int32)).to(self.device),
+                self.signs[0], self.signs[1], self.p.w.clip, self.p.w.clip)
+            return
         ops.rotate_quantize_append(
             self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
             torch.from_numpy(offs).to(self.device),
@@ -188,6 +201,12 @@ class DecodeStep:
 
     def append_new(self, stream=None):
         c = self.cache
+        if c.hadamard:
+            ops.rotate_quantize_append_hadamard(c.layout, c.pages, c.sinkwin, c.table, c.slots,
+                                                self.k_last, self.v_last, self.new_off, self.start,
+                                                c.signs[0], c.signs[1], c.p.w.clip, c.p.w.clip,
+                                                stream)
+            return
         ops.rotate_quantize_append(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.k_last,
                                    self.v_last, self.new_off, self.start, c.rot_k, c.rot_v,
                                    c.p.w.clip, c.p.w.clip, stream, k_mean=c.k_mean)

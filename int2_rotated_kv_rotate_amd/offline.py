@@ -74,3 +74,30 @@ def calibrate(k_rows, v_rows, center_keys: bool = True):
     rot_k = spectral_rotation(covariance(k_rows, center=center_keys)).astype(np.float32)
     rot_v = spectral_rotation(covariance(v_rows, center=False)).astype(np.float32)
     return rot_k, rot_v, k_mean
+
+
+HADAMARD_SCALE = float(np.sqrt(2.0) / 16.0)   # the double nearest to 1/sqrt(128)
+
+
+def hadamard_signs(seed: int, num_kv_heads: int) -> np.ndarray:
+    """Seeded random signs int8 [Hkv][128] for oscar_rotate_quantize_append_hadamard."""
+    rng = np.random.default_rng(seed)
+    return rng.choice(np.array([-1, 1], dtype=np.int8), size=(num_kv_heads, HEAD_DIM))
+
+
+def hadamard_rotation(signs) -> np.ndarray:
+    """Dense fp32 form of diag(s) . H / sqrt(128), H_ij = (-1)^popcount(i & j), for the parts of
+    the path that take a matrix (rot_k of oscar_decode_attention, rot_v of oscar_combine).
+    signs: None, [128] or [Hkv][128] (negative entries flip).  Returns fp32 [128][128] or
+    [Hkv][128][128]: fp32(s_i H_ij r) with r the double nearest to 1/sqrt(128)."""
+    i = np.arange(HEAD_DIM)
+    par = np.bitwise_and(i[:, None], i[None, :])
+    bits = np.zeros_like(par)
+    for k in range(7):
+        bits += (par >> k) & 1
+    h = np.where(bits % 2 == 0, 1.0, -1.0)
+    if signs is None:
+        return (h * HADAMARD_SCALE).astype(np.float32)
+    s = np.where(np.asarray(signs) < 0, -1.0, 1.0)
+    return (s[..., :, None] * h * HADAMARD_SCALE).astype(np.float32)
+

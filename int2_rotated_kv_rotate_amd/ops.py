@@ -24,6 +24,7 @@ EXPORTED = (
     "oscar_status_string",
     "oscar_rotate_quantize_append",
     "oscar_rotate_quantize_append_ex",
+    "oscar_rotate_quantize_append_hadamard",
     "oscar_decode_workspace_bytes",
     "oscar_decode_attention",
     "oscar_combine",
@@ -79,6 +80,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_rotate_quantize_append_ex.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P, P,
                                                     F32, F32, I32, P]
     lib.oscar_rotate_quantize_append_ex.restype = I32
+    lib.oscar_rotate_quantize_append_hadamard.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P,
+                                                          F32, F32, P]
+    lib.oscar_rotate_quantize_append_hadamard.restype = I32
     lib.oscar_decode_workspace_bytes.argtypes = [I32, I32, I32]
     lib.oscar_decode_workspace_bytes.restype = SZ
     lib.oscar_decode_attention.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, F32, I32, I32, P, SZ, P]
@@ -138,6 +142,22 @@ def rotate_quantize_append(lay: Layout, pages, sinkwin, block_table, slot_ids, k
         _ptr(rot_k, torch.float32, "rot_k"), _ptr(rot_v, torch.float32, "rot_v"),
         _ptr(k_mean, torch.float32, "k_mean"), float(clip_k), float(clip_v), int(method),
         _stream(stream)))
+
+
+def rotate_quantize_append_hadamard(lay: Layout, pages, sinkwin, block_table, slot_ids, k_new,
+                                    v_new, new_offsets, start_pos, signs_k, signs_v,
+                                    clip_k: float, clip_v: float, stream=None) -> None:
+    """As rotate_quantize_append with the Hadamard rotation diag(s) H / sqrt(128) for K and V;
+    signs_k / signs_v: None or int8 [Hkv][128]."""
+    lib = load_library()
+    batch = start_pos.numel()
+    _check("oscar_rotate_quantize_append_hadamard", lib.oscar_rotate_quantize_append_hadamard(
+        ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
+        batch, k_new.shape[0], _ptr(k_new, torch.int16, "k_new"), _ptr(v_new, torch.int16, "v_new"),
+        _ptr(new_offsets, torch.int32, "new_offsets"), _ptr(start_pos, torch.int32, "start_pos"),
+        _ptr(signs_k, torch.int8, "signs_k"), _ptr(signs_v, torch.int8, "signs_v"),
+        float(clip_k), float(clip_v), _stream(stream)))
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, max_splits: int) -> int:

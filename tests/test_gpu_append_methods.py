@@ -17,6 +17,7 @@ Cases:
   * groups with max == -min (a code threshold exactly at zero), one-signed and constant groups;
   * keys with a mean removed before the rotation (workload means, a large random mean, zero,
     and the special rows with a mean);
+  * the Hadamard-rotation append (its own kernel) against the oracle;
   * the full prefill shape: 64 sequences x 2048 new tokens at the end of 16K-32K contexts
     (GPU against GPU: 2.1 million rows are beyond the oracle's seconds).
 """
@@ -185,6 +186,44 @@ def test_key_mean_special_rows():
     mu = (rng.standard_normal((w.num_kv_heads, 128)) * 3).astype(np.float32)
     mu[0, :64] = 0.0                     # some channels without a mean
     _check("key_mean_special_rows", p, ks, vs, [0] * w.batch, k_mean=mu)
+
+
+def _dense_hadamard(signs, hkv):
+    """[Hkv][128][128] dense form (what attention reads) of the Hadamard rotation."""
+    if signs is None:
+        return np.broadcast_to(OF.hadamard_rotation(None), (hkv, 128, 128)).copy()
+    return OF.hadamard_rotation(signs)
+
+
+@pytest.mark.parametrize("kind", ["workload", "special_rows", "no_signs"])
+def test_hadamard_append(kind):
+    """The Hadamard-rotation append (fp64 fast transform) against the oracle, byte for byte:
+    workload rows with seeded signs, the special rows (zero, subnormal, high dynamic range), and
+    all signs +1.  Whole contexts, so every call writes sink, window and bulk rows."""
+    w = W.scaled(W.WORKLOADS["qwen3_8b_b64"], name="append_hadamard_" + kind, batch=3, ctx=1100,
+                 ctx_min=300)
+    sk, sv = (None, None) if kind == "no_signs" else (OF.hadamard_signs(60, w.num_kv_heads),
+                                                      OF.hadamard_signs(61, w.num_kv_heads))
+    p = H.make_problem(w, rot_k=_dense_hadamard(sk, w.num_kv_heads),
+                       rot_v=_dense_hadamard(sv, w.num_kv_heads))
+    if kind == "special_rows":
+        rng = np.random.default_rng(62)
+        ks = [_special_rows(rng, p.rot_k, int(L)) for L in p.lens]
+        vs = [_special_rows(rng, p.rot_v, int(L)) for L in p.lens]
+    else:
+        ks, vs = _workload_rows(w, p.lens)
+    c = H.GpuCache(p, fill=SENTINEL, hadamard_signs=(sk, sv))
+    c.append(ks, vs, [0] * w.batch)
+    torch.cuda.synchronize()
+    oc = O.Cache(p.num_pages, w.num_kv_heads, w.batch, w.num_sink, w.window, fill=SENTINEL)
+    for b in range(w.batch):
+        oc.append(p.table[b], b, 0, ks[b], vs[b], None, None, w.clip, w.clip,
+                  hadamard_signs=(sk, sv))
+    pages = c.pages.cpu().numpy()
+    nd = int((pages != oc.pages).sum())
+    _log(f"[append] hadamard {kind}: {sum(k.shape[0] for k in ks)} rows, {nd} page bytes differ")
+    assert nd == 0
+    assert np.array_equal(c.sinkwin.cpu().numpy().view(np.uint16), oc.sinkwin)
 
 
 def test_symmetric_groups():

@@ -32,22 +32,24 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def oracle_cache(p: H.Problem, k_mean=None):
+def oracle_cache(p: H.Problem, k_mean=None, hadamard_signs=None):
     w = p.w
     cache = O.Cache(p.num_pages, w.num_kv_heads, w.batch, w.num_sink, w.window, fill=SENTINEL)
     needle = W.needle_site(w, p.lens)
     for b in range(w.batch):
         L = int(p.lens[b])
         kb, vb = W.sequence_kv(w, b, L, needle=needle, q_bits=p.q)
-        cache.append(p.table[b], b, 0, kb[:L - 1], vb[:L - 1], p.rot_k, p.rot_v, w.clip, w.clip,
-                     k_mean)
-        cache.append(p.table[b], b, L - 1, kb[L - 1:], vb[L - 1:], p.rot_k, p.rot_v, w.clip,
-                     w.clip, k_mean)
+        rk, rv = (None, None) if hadamard_signs is not None else (p.rot_k, p.rot_v)
+        cache.append(p.table[b], b, 0, kb[:L - 1], vb[:L - 1], rk, rv, w.clip, w.clip,
+                     k_mean, hadamard_signs)
+        cache.append(p.table[b], b, L - 1, kb[L - 1:], vb[L - 1:], rk, rv, w.clip,
+                     w.clip, k_mean, hadamard_signs)
     return cache
 
 
-def run_gpu(p: H.Problem, num_workers=0, max_splits=H.DEFAULT_MAX_SPLITS, k_mean=None):
-    cache = H.GpuCache(p, fill=SENTINEL, k_mean=k_mean)
+def run_gpu(p: H.Problem, num_workers=0, max_splits=H.DEFAULT_MAX_SPLITS, k_mean=None,
+            hadamard_signs=None):
+    cache = H.GpuCache(p, fill=SENTINEL, k_mean=k_mean, hadamard_signs=hadamard_signs)
     last_k, last_v = cache.fill_context()
     step = H.DecodeStep(cache, num_workers=num_workers, max_splits=max_splits)
     step.set_new_token(last_k, last_v)
@@ -143,6 +145,28 @@ def test_key_mean_decode():
     _log(f"[parity] key mean: error vs exact attention {np.mean(err_c):.4f} (centered) vs "
          f"{np.mean(err_p):.4f} (plain)")
     assert np.mean(err_c) < np.mean(err_p)
+
+
+def test_hadamard_decode():
+    """A cache written with the Hadamard-rotation append (fp64 fast transform, seeded signs),
+    attended with its dense fp32 form as R_K and R_V: pages equal to the oracle's, outputs and
+    lse within 2e-3 of the oracle's decode of that cache."""
+    from int2_rotated_kv_rotate_amd import offline as OF
+    w = W.scaled(W.WORKLOADS["qwen3_4b"], name="hadamard_decode", batch=2, ctx=1300, ctx_min=700)
+    sk, sv = OF.hadamard_signs(70, w.num_kv_heads), OF.hadamard_signs(71, w.num_kv_heads)
+    p = H.make_problem(w, rot_k=OF.hadamard_rotation(sk), rot_v=OF.hadamard_rotation(sv))
+    cache, step = run_gpu(p, 0, H.DEFAULT_MAX_SPLITS, hadamard_signs=(sk, sv))
+    oc = oracle_cache(p, hadamard_signs=(sk, sv))
+    assert np.array_equal(cache.pages.cpu().numpy(), oc.pages)
+    assert np.array_equal(cache.sinkwin.cpu().numpy().view(np.uint16), oc.sinkwin)
+    ref, ref_lse = O.decode_attention(oc, p.table, np.arange(w.batch), p.lens, p.q, p.rot_k,
+                                      p.rot_v, H.SM_SCALE)
+    out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
+    rel = row_errors(out, ref)
+    _log(f"[parity] hadamard: max row rel err {rel.max():.3e}, "
+         f"max |dlse| {np.abs(lse - ref_lse).max():.3e}")
+    assert rel.max() <= TOL
+    assert np.abs(lse - ref_lse).max() <= TOL
 
 
 def test_split_size_and_permutation_invariance():

@@ -78,3 +78,15 @@ def test_calibrated_parameters_shapes_and_quantisation_error():
         errs[name] = float(np.mean(e))
     print("key INT2 mse on held-out rows:", errs)
     assert all(np.isfinite(v) for v in errs.values())
+
+
+def test_dense_hadamard_matrix_matches_the_oracle():
+    """The library-side dense Hadamard matrix (popcount formula) is bit-identical to the
+    oracle's (built from its fast transform of the identity)."""
+    s = OF.hadamard_signs(50, 3)
+    assert s.dtype == np.int8 and set(np.unique(s)) == {-1, 1}
+    dense = OF.hadamard_rotation(s)
+    for h in range(3):
+        assert np.array_equal(dense[h].view(np.uint32), O.hadamard_rotation32(s[h]).view(np.uint32))
+    assert np.array_equal(OF.hadamard_rotation(None).view(np.uint32),
+                          O.hadamard_rotation32(None).view(np.uint32))
