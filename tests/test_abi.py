@@ -104,6 +104,26 @@ def test_append_ex_validation(lib):
         assert call(m, batch=0) == 0          # nothing to do
 
 
+def test_append_hadamard_validation(lib):
+    lay = _layout()
+
+    def call(**kw):
+        a = dict(pages=FAKE, batch=1, k_new=FAKE, clip_k=0.95, sinkwin=FAKE)
+        a.update(kw)
+        return lib.oscar_rotate_quantize_append_hadamard(
+            ctypes.byref(lay), a["pages"], a["sinkwin"], FAKE, None, a["batch"], 1, a["k_new"], FAKE,
+            FAKE, FAKE, None, None, a["clip_k"], 0.95, None)
+
+    assert call(pages=None) == 1
+    assert call(k_new=None) == 1
+    assert call(k_new=ctypes.c_void_p(24)) == 1    # rows must be 16-byte aligned
+    assert call(clip_k=0.0) == 1
+    assert call(clip_k=1.5) == 1
+    assert call(sinkwin=None) == 1                 # the layout has sink/window rows
+    assert call(batch=0) == 0
+    assert call(batch=-1) == 1
+
+
 def _decode(lib, lay, **kw):
     a = dict(pages=FAKE, sinkwin=FAKE, bt=FAKE, slots=None, batch=1, hq=32, q=FAKE, lens=FAKE,
              rk=FAKE, sm=0.088, nw=0, ms=4, ws=FAKE, wsb=1 << 30)
