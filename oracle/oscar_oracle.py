@@ -178,7 +178,7 @@ def rotate_query(q_bits: np.ndarray, rot_k32: np.ndarray, group: int) -> np.ndar
 # Quantiser: per-token groups of 32 rotated channels, clipped min/max, 4 affine levels.
 # ----------------------------------------------------------------------------------------
 
-def group_params(y: np.ndarray, clip: float):
+def group_params(y: np.ndarray, clip: float, levels: int = LEVELS):
     """fp16 scale and zero of every 32-channel group of every rotated row.
 
     For each group: mx = max, mn = min of the fp32 values (a -0.0 extreme counts as +0.0);
@@ -199,11 +199,11 @@ def group_params(y: np.ndarray, clip: float):
     mx_c = (c * mx).astype(np.float32)
     mn_c = (c * mn).astype(np.float32)
     width = (mx_c - mn_c).astype(np.float32)
-    s32 = (width / np.float32(LEVELS - 1)).astype(np.float32)
+    s32 = (width / np.float32(levels - 1)).astype(np.float32)
     return s32.astype(np.float16), mn_c.astype(np.float16)
 
 
-def group_codes(y: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+def group_codes(y: np.ndarray, s16: np.ndarray, z16: np.ndarray, levels: int = LEVELS) -> np.ndarray:
     """2-bit code of every channel: round((y - z) / s) to nearest even, clamped to [0, 3].
 
     The quotient uses the stored fp16 scale and zero (widened to fp32) in fp32 arithmetic, so
@@ -218,7 +218,7 @@ def group_codes(y: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
     diff = (y - z).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         t = (diff / np.where(s == 0, np.float32(1), s)).astype(np.float32)
-    code = np.clip(np.rint(t), 0, LEVELS - 1)
+    code = np.clip(np.rint(t), 0, levels - 1)
     code = np.where(s == 0, 0, code)
     return code.astype(np.uint8).reshape(-1, D)
 
@@ -230,16 +230,17 @@ def dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
     return v.reshape(-1, D)
 
 
-def quantize_rows(x_bits: np.ndarray, rot32, clip: float, mean32=None, hadamard_signs=None):
-    """Rotate (after removing mean32, if given), clip and quantise rows: returns (y fp32,
-    codes u8, s16, z16).  With rot32 None the rotation is the Hadamard one with the given
-    signs (rotate_rows_hadamard)."""
+def quantize_rows(x_bits: np.ndarray, rot32, clip: float, mean32=None, hadamard_signs=None,
+                  levels: int = LEVELS):
+    """Rotate (after removing mean32, if given), clip and quantise rows to `levels` levels (4:
+    INT2, 16: INT4): returns (y fp32, codes u8, s16, z16).  With rot32 None the rotation is the
+    Hadamard one with the given signs (rotate_rows_hadamard)."""
     if rot32 is None:
         y = rotate_rows_hadamard(x_bits, hadamard_signs)
     else:
         y = rotate_rows_centered(x_bits, rot32, mean32)
-    s16, z16 = group_params(y, clip)
-    return y, group_codes(y, s16, z16), s16, z16
+    s16, z16 = group_params(y, clip, levels)
+    return y, group_codes(y, s16, z16, levels), s16, z16
 
 
 # ----------------------------------------------------------------------------------------
@@ -279,34 +280,59 @@ def meta_location(kind: str, r, g):
     return (K_META if kind == "k" else V_META) + 16 * r + 4 * g
 
 
+# INT4 records (the INT4 abstract on the OSCAR paper's page: token-wise INT4 in a paged
+# layout).  2560 bytes per (page, KV head); 16 levels, two codes per byte, low nibble first:
+#   [   0, 1024)  K codes, token-major: channel c of slot r at byte 64*r + c/2, bits 4*(c % 2);
+#   [1024, 2048)  V codes, channel-pair-major: channel c of slot r at byte 1024 + 16*(c/2) + r,
+#                 bits 4*(c % 2);
+#   [2048, 2304)  K scale/zero: fp16 pair of group g of slot r at 2048 + 16*r + 4*g;
+#   [2304, 2560)  V scale/zero, the same arrangement at 2304.
+LEVELS4 = 16
+RECORD4 = 2560
+K4_CODES, V4_CODES, K4_META, V4_META = 0, 1024, 2048, 2304
+
+
+def k4_code_location(r, c):
+    return K4_CODES + 64 * r + c // 2, 4 * (c % 2)
+
+
+def v4_code_location(r, c):
+    return V4_CODES + 16 * (c // 2) + r, 4 * (c % 2)
+
+
+def meta4_location(kind: str, r, g):
+    return (K4_META if kind == "k" else V4_META) + 16 * r + 4 * g
+
+
 _CH = np.arange(D)
 _GR = np.arange(NGROUPS)
 
 
-def _put_codes(flat, base, r, codes, loc):
+def _put_codes(flat, base, r, codes, loc, width=2):
     byte, bit = loc(r[:, None], _CH[None, :])
     idx = (base[:, None] + byte).ravel()
     bit = np.broadcast_to(bit, codes.shape).ravel().astype(np.uint8)
-    np.bitwise_and.at(flat, idx, (~(np.uint8(3) << bit)).astype(np.uint8))
+    mask = np.uint8((1 << width) - 1)
+    np.bitwise_and.at(flat, idx, (~(mask << bit)).astype(np.uint8))
     np.bitwise_or.at(flat, idx, (codes.astype(np.uint8).ravel() << bit).astype(np.uint8))
 
 
-def _get_codes(flat, base, r, loc):
+def _get_codes(flat, base, r, loc, width=2):
     byte, bit = loc(r[:, None], _CH[None, :])
-    return ((flat[base[:, None] + byte] >> np.broadcast_to(bit, byte.shape).astype(np.uint8)) & 3
-            ).astype(np.uint8)
+    return ((flat[base[:, None] + byte] >> np.broadcast_to(bit, byte.shape).astype(np.uint8))
+            & np.uint8((1 << width) - 1)).astype(np.uint8)
 
 
-def _put_meta(flat, base, r, kind, s16, z16):
-    off = base[:, None] + meta_location(kind, r[:, None], _GR[None, :])
+def _put_meta(flat, base, r, kind, s16, z16, mloc=None):
+    off = base[:, None] + (mloc or meta_location)(kind, r[:, None], _GR[None, :])
     for field, vals in ((0, s16), (2, z16)):
         u = np.asarray(vals, dtype=np.float16).view(np.uint16)
         flat[off + field] = (u & 0xFF).astype(np.uint8)
         flat[off + field + 1] = (u >> 8).astype(np.uint8)
 
 
-def _get_meta(flat, base, r, kind):
-    off = base[:, None] + meta_location(kind, r[:, None], _GR[None, :])
+def _get_meta(flat, base, r, kind, mloc=None):
+    off = base[:, None] + (mloc or meta_location)(kind, r[:, None], _GR[None, :])
     out = []
     for field in (0, 2):
         u = flat[off + field].astype(np.uint16) | (flat[off + field + 1].astype(np.uint16) << 8)
@@ -314,24 +340,37 @@ def _get_meta(flat, base, r, kind):
     return out[0], out[1]
 
 
-def write_slots(flat, base, r, kcodes, ks16, kz16, vcodes, vs16, vz16) -> None:
+def write_slots(flat, base, r, kcodes, ks16, kz16, vcodes, vs16, vz16, bits: int = 2) -> None:
     """Store n tokens' K and V encodings (in place) into a flat byte pool.
 
     base: int [n] byte offset of each token's record; r: int [n] page slot of each token;
     codes [n][128]; scales/zeros [n][4].  Only the bits belonging to each token's slot change.
+    bits: 2 (the 1536-byte INT2 record) or 4 (the 2560-byte INT4 record).
     """
     base = np.asarray(base, dtype=np.int64)
     r = np.asarray(r, dtype=np.int64)
+    if bits == 4:
+        _put_codes(flat, base, r, kcodes, k4_code_location, 4)
+        _put_codes(flat, base, r, vcodes, v4_code_location, 4)
+        _put_meta(flat, base, r, "k", ks16, kz16, meta4_location)
+        _put_meta(flat, base, r, "v", vs16, vz16, meta4_location)
+        return
     _put_codes(flat, base, r, kcodes, k_code_location)
     _put_codes(flat, base, r, vcodes, v_code_location)
     _put_meta(flat, base, r, "k", ks16, kz16)
     _put_meta(flat, base, r, "v", vs16, vz16)
 
 
-def read_slots(flat, base, r):
+def read_slots(flat, base, r, bits: int = 2):
     """Decode n tokens: (kcodes, ks16, kz16, vcodes, vs16, vz16), codes [n][128], meta [n][4]."""
     base = np.asarray(base, dtype=np.int64)
     r = np.asarray(r, dtype=np.int64)
+    if bits == 4:
+        kc = _get_codes(flat, base, r, k4_code_location, 4)
+        vc = _get_codes(flat, base, r, v4_code_location, 4)
+        ks, kz = _get_meta(flat, base, r, "k", meta4_location)
+        vs, vz = _get_meta(flat, base, r, "v", meta4_location)
+        return kc, ks, kz, vc, vs, vz
     kc = _get_codes(flat, base, r, k_code_location)
     vc = _get_codes(flat, base, r, v_code_location)
     ks, kz = _get_meta(flat, base, r, "k")
@@ -369,13 +408,16 @@ def sink_window_index(pos: int, num_sink: int, window: int, new_len: int):
 class Cache:
     """Oracle model of the cache a sequence batch writes.
 
-    pages:   uint8 [num_pages][Hkv][1536]  INT2 records.
+    pages:   uint8 [num_pages][Hkv][1536]  INT2 records (bits = 4: [2560] INT4 records).
     sinkwin: uint16 [num_slots][Hkv][S+W][2][128] bf16 bits of the rotated K (index 0) and
              V (index 1) rows of sink and window positions.
     """
 
-    def __init__(self, num_pages, num_kv_heads, num_slots, num_sink, window, fill=0):
-        self.pages = np.full((num_pages, num_kv_heads, RECORD), fill, dtype=np.uint8)
+    def __init__(self, num_pages, num_kv_heads, num_slots, num_sink, window, fill=0, bits=2):
+        self.bits = bits
+        self.record = RECORD4 if bits == 4 else RECORD
+        self.levels = LEVELS4 if bits == 4 else LEVELS
+        self.pages = np.full((num_pages, num_kv_heads, self.record), fill, dtype=np.uint8)
         self.sinkwin = np.full((num_slots, num_kv_heads, num_sink + window, 2, D),
                                fill | (fill << 8), dtype=np.uint16)
         self.num_sink = num_sink
@@ -384,7 +426,7 @@ class Cache:
 
     def _bases(self, table_row, h, positions):
         pages = np.asarray(table_row)[np.asarray(positions) // PAGE].astype(np.int64)
-        return (pages * self.hkv + h) * RECORD, np.asarray(positions) % PAGE
+        return (pages * self.hkv + h) * self.record, np.asarray(positions) % PAGE
 
     def append(self, table_row, slot, start_pos, k_bits, v_bits, rot_k32, rot_v32, clip_k, clip_v,
                k_mean32=None, hadamard_signs=None):
@@ -402,18 +444,19 @@ class Cache:
         positions = np.arange(start_pos, new_len)
         flat = self.pages.reshape(-1)
         for h in range(self.hkv):
+            lv = self.levels
             if rot_k32 is None:
                 sk, sv = hadamard_signs if hadamard_signs is not None else (None, None)
                 yk, kc, ks, kz = quantize_rows(k_bits[:, h], None, clip_k, None,
-                                               None if sk is None else sk[h])
+                                               None if sk is None else sk[h], lv)
                 yv, vc, vs, vz = quantize_rows(v_bits[:, h], None, clip_v, None,
-                                               None if sv is None else sv[h])
+                                               None if sv is None else sv[h], lv)
             else:
                 yk, kc, ks, kz = quantize_rows(k_bits[:, h], rot_k32[h], clip_k,
-                                               None if k_mean32 is None else k_mean32[h])
-                yv, vc, vs, vz = quantize_rows(v_bits[:, h], rot_v32[h], clip_v)
+                                               None if k_mean32 is None else k_mean32[h], None, lv)
+                yv, vc, vs, vz = quantize_rows(v_bits[:, h], rot_v32[h], clip_v, None, None, lv)
             base, r = self._bases(table_row, h, positions)
-            write_slots(flat, base, r, kc, ks, kz, vc, vs, vz)
+            write_slots(flat, base, r, kc, ks, kz, vc, vs, vz, self.bits)
             kb = f32_to_bf16_bits(yk)
             vb = f32_to_bf16_bits(yv)
             for i, pos in enumerate(positions):
@@ -456,7 +499,7 @@ class Cache:
 
     def decode_positions(self, table_row, h, positions):
         base, r = self._bases(table_row, h, positions)
-        return read_slots(self.pages.reshape(-1), base, r)
+        return read_slots(self.pages.reshape(-1), base, r, self.bits)
 
 
 # ----------------------------------------------------------------------------------------
