@@ -23,6 +23,7 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 INT2_TOKEN_HEAD_BYTES = 96      # 32 B K codes + 32 B V codes + 16 B K meta + 16 B V meta
 BF16_TOKEN_HEAD_BYTES = 512     # bf16 K + V rows
+INT4_TOKEN_HEAD_BYTES = 160     # INT4 K + V codes (64 + 64) + K/V scale-zero (16 + 16)
 METRIC = "decode attn tokens/s + effective HBM GB/s (% of peak), Qwen3-8B shape B=64 ctx=32k"
 
 
@@ -154,7 +155,8 @@ def int2_vs_bf16(n_iter: int):
       * Qwen3-32B layer shape, context 32768: INT2 at batch 16 vs BF16 at batch 2 (about 1/8
         of the batch) and batch 3 (the equal-memory batch for 3 bits per element);
       * Qwen3-4B layer shape, batch 1, context 32768: latency of each;
-      * long-context layer (32 query / 8 KV heads), batch 1, context 131072: latency of each."""
+      * long-context layer (32 query / 8 KV heads), batch 1, context 131072: latency of each;
+      * the INT4 variant at the Qwen3-8B batch-64 shape."""
     import torch
     from int2_rotated_kv_rotate_amd import harness as H
     from int2_rotated_kv_rotate_amd import workload as W
@@ -234,6 +236,28 @@ def int2_vs_bf16(n_iter: int):
                                  "int2_effective_gbps": gbps(w4, p4, ms_i, False),
                                  "bf16_effective_gbps": gbps(w4, p4, ms_b, True)}
     log(f"qwen3_4b B=1: INT2 {ms_i:.4f} ms, BF16 {ms_b:.4f} ms")
+
+    # The INT4 variant (2560-byte records, vector-ALU decode) at the Qwen3-8B batch-64 shape
+    w8 = W.WORKLOADS["qwen3_8b_b64"]
+    p8 = H.make_problem(w8)
+    c4 = H.GpuCache(p8, bits=4)
+    lk, lv = c4.fill_context()
+    st4 = H.DecodeStep(c4)
+    st4.set_new_token(lk, lv)
+    st4.run()
+    torch.cuda.synchronize()
+    ms4, _, _ = time_scrubbed(st4.attend, n_iter, scrub)
+    lens = np.asarray(p8.lens, np.int64)
+    n_sink = np.minimum(lens, w8.num_sink)
+    n_win = np.minimum(w8.window, lens - n_sink)
+    b4 = (w8.num_kv_heads * (INT4_TOKEN_HEAD_BYTES * int((lens - n_sink - n_win).sum()) +
+                             BF16_TOKEN_HEAD_BYTES * int((n_sink + n_win).sum())) +
+          w8.batch * w8.num_q_heads * 128 * (2 + 4) + 4 * int(((lens + 15) // 16).sum()))
+    res["int4_qwen3_8b_b64"] = {"ms": round(ms4, 4), "tokens_per_s": round(w8.batch / ms4 * 1e3, 1),
+                                "bytes": int(b4), "effective_gbps": round(b4 / (ms4 * 1e-3) / 1e9, 1),
+                                "decode": "vector ALUs, one workgroup per (split, KV head, sequence)"}
+    log(f"INT4 qwen3_8b B=64: {ms4:.4f} ms ({b4 / (ms4 * 1e-3) / 1e9:.0f} GB/s)")
+    del st4, c4
     del scrub
     return res
 

@@ -189,6 +189,47 @@ int32_t oscar_rotate_quantize_append_hadamard(
     void* stream);
 
 /*
+ * INT4 variant of the cache: the same rotation (with the optional key mean of
+ * oscar_rotate_quantize_append_ex), clip, 32-channel groups, fp16 scale/zero and BF16
+ * sink/window store, with 16-level codes: s = fp16(fp32(c*mx - c*mn) / 15), z = fp16(c*mn),
+ * code = clamp(rint((y - z) / s), 0, 15) (0 when s == 0).  Token-wise INT4 with a rotation is the
+ * serving-compatible 4-bit design of the INT4 abstract on the OSCAR paper's page ("OSCAR:
+ * Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization").
+ * The pool is uint8 [num_pages][Hkv][2560]; within a record (slot r, channel c, group g; two
+ * codes per byte, the even channel in the low nibble):
+ *   [   0, 1024)  K codes at byte 64*r + c/2;
+ *   [1024, 2048)  V codes at byte 1024 + 16*(c/2) + r;
+ *   [2048, 2304)  K (fp16 scale, fp16 zero) at 2048 + 16*r + 4*g;
+ *   [2304, 2560)  V (scale, zero) at 2304 + 16*r + 4*g.
+ * Arguments, validation and errors as oscar_rotate_quantize_append_ex (no method choice: the
+ * rotation runs in fp64 on the vector ALUs).
+ */
+int32_t oscar_int4_rotate_quantize_append(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, const float* k_mean, float clip_k, float clip_v,
+    void* stream);
+
+/*
+ * Decode attention over an INT4 cache, written in the workspace format of
+ * oscar_decode_attention and finished by oscar_combine with the same rot_v.  Sequence b's pages
+ * are cut into splits of max(split_pages, ceil(P_b / max_splits)) pages (P_b = ceil(L_b / 16));
+ * each split attends over all of its positions (INT4 records and BF16 sink/window rows) on the
+ * vector ALUs.  Arguments, validation and errors as oscar_decode_attention, with split_pages
+ * (>= 1) in place of num_workers.
+ */
+int32_t oscar_int4_decode_attention(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k, float sm_scale,
+    int32_t split_pages, int32_t max_splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace oscar_decode_attention / oscar_bf16_decode_attention need for `batch`
  * sequences of `num_q_heads` query heads split at most `max_splits` ways.  Returns 0 for
  * invalid arguments.

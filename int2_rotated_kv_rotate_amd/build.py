@@ -27,6 +27,8 @@ SOURCES = {
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "combine.hip": [],
     "bf16_baseline.hip": [],
+    # the INT4 quantiser is the same kind of fp32 formula
+    "int4.hip": ["-ffp-contract=off"],
 }
 COMMON = [
     "-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

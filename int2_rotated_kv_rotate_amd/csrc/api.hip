@@ -126,6 +126,62 @@ int32_t oscar_rotate_quantize_append_hadamard(
                                            signs_k, signs_v, clip_k, clip_v, (hipStream_t)stream));
 }
 
+int32_t oscar_int4_rotate_quantize_append(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, const float* k_mean, float clip_k, float clip_v,
+    void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || total_new == 0) return OSCAR_OK;
+  if (!pages || !block_table || !k_new || !v_new || !new_offsets || !start_pos || !rot_k || !rot_v)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rot_k) ||
+      !aligned16(rot_v) || (sinkwin && !aligned16(sinkwin)) || ((uintptr_t)k_mean & 3u) != 0)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_int4_append(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                       total_new, k_new, v_new, new_offsets, start_pos, rot_k,
+                                       rot_v, k_mean, clip_k, clip_v, (hipStream_t)stream));
+}
+
+int32_t oscar_int4_decode_attention(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k, float sm_scale,
+    int32_t split_pages, int32_t max_splits,
+    void* workspace, size_t workspace_bytes_given, void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || split_pages < 1 || max_splits < 1 || max_splits > 65535)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
+  if (st != OSCAR_OK) return st;
+  if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return OSCAR_OK;
+  if (!pages || !block_table || !q || !seq_lens || !rot_k || !workspace)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(q) || !aligned16(workspace) || !aligned16(rot_k) ||
+      (sinkwin && !aligned16(sinkwin)))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
+  return hip_status(launch_int4_decode(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                       num_q_heads, q, seq_lens, rot_k, sm_scale, split_pages, ws,
+                                       (hipStream_t)stream));
+}
+
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits) {
   if (batch < 0 || num_q_heads < 1 || max_splits < 1) return 0;
   return workspace_bytes(batch, num_q_heads, max_splits);

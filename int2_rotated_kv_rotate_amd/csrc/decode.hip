@@ -1038,6 +1038,14 @@ int resident_workers() {
 
 }  // namespace
 
+hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot_k, int batch,
+                         int hq, const int32_t* seq_lens, const Workspace& ws, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv, batch + 1), dim3(kPrepThreads), 0, stream, g, q,
+                     rot_k, hq, seq_lens, 1, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,

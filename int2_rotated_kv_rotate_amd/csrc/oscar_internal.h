@@ -108,6 +108,24 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
                          float sm_scale, int num_workers, const Workspace& ws,
                          hipStream_t stream);
 
+// q' = q . R_K (fp32 and int8 forms) into the workspace Q blocks, as oscar_decode_attention's
+// first kernel does (its work plan is built for a single worker).
+hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot_k, int batch,
+                         int hq, const int32_t* seq_lens, const Workspace& ws, hipStream_t stream);
+
+// INT4 cache (2560-byte records): append and decode (partials for launch_combine).
+hipError_t launch_int4_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                              const int32_t* block_table, const int32_t* slot_ids, int batch,
+                              int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                              const int32_t* new_offsets, const int32_t* start_pos,
+                              const float* rot_k, const float* rot_v, const float* k_mean,
+                              float clip_k, float clip_v, hipStream_t stream);
+hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
+                              const int32_t* block_table, const int32_t* slot_ids, int batch,
+                              int hq, const uint16_t* q, const int32_t* seq_lens,
+                              const float* rot_k, float sm_scale, int split_pages,
+                              const Workspace& ws, hipStream_t stream);
+
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream);
 

@@ -53,17 +53,20 @@ class GpuCache:
     """INT2 page pool + BF16 sink/window store + block table on the GPU."""
 
     def __init__(self, p: Problem, device="cuda", fill: Optional[int] = None,
-                 k_mean: Optional[np.ndarray] = None, hadamard_signs=None):
+                 k_mean: Optional[np.ndarray] = None, hadamard_signs=None, bits: int = 2):
         """k_mean: None or fp32 [Hkv][128], a key mean removed before the key rotation on every
         append into this cache.  hadamard_signs: None for the dense rotations p.rot_k / p.rot_v,
         else a pair (signs_k, signs_v) (each None or int8 [Hkv][128]) for appends with the
-        Hadamard rotation; p.rot_k / p.rot_v must then be its dense form (attention reads them)."""
+        Hadamard rotation; p.rot_k / p.rot_v must then be its dense form (attention reads them).
+        bits: 2 (INT2 records) or 4 (the INT4 variant, 2560-byte records)."""
         w = p.w
         self.p = p
         self.device = device
         self.layout = ops.make_layout(w.num_kv_heads, w.num_sink, w.window, p.num_pages,
                                       p.table.shape[1], w.batch)
-        self.pages = torch.empty((p.num_pages, w.num_kv_heads, ops.RECORD_BYTES), dtype=torch.uint8,
+        self.bits = bits
+        rec = ops.INT4_RECORD_BYTES if bits == 4 else ops.RECORD_BYTES
+        self.pages = torch.empty((p.num_pages, w.num_kv_heads, rec), dtype=torch.uint8,
                                  device=device)
         self.sinkwin = torch.empty((w.batch, w.num_kv_heads, max(w.num_sink + w.window, 1), 2, 128),
                                    dtype=torch.int16, device=device)
@@ -93,6 +96,13 @@ class GpuCache:
         offs[1:] = np.cumsum(counts)
         k = as_i16(np.concatenate(k_rows)).to(self.device)
         v = as_i16(np.concatenate(v_rows)).to(self.device)
+        if self.bits == 4:
+            ops.int4_rotate_quantize_append(
+                self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
+                torch.from_numpy(offs).to(self.device),
+                torch.from_numpy(np.asarray(start, dtype=np.int32)).to(self.device),
+                self.rot_k, self.rot_v, self.p.w.clip, self.p.w.clip, k_mean=self.k_mean)
+            return
         if self.hadamard:
             ops.rotate_quantize_append_hadamard(
                 self.layout, self.pages, self.sinkwin, self.table, self.slots, k, v,
@@ -183,6 +193,11 @@ class DecodeStep:
         self.num_workers = num_workers
         self.max_splits = (max_splits if max_splits is not None
                            else default_max_splits(p.batch, p.w.num_kv_heads, int(p.lens.max())))
+        if cache.bits == 4:   # INT4: fixed page splits, about 2048 workgroups over the batch
+            pages_max = -(-int(p.lens.max()) // 16)
+            self.split_pages = max(1, -(-pages_max * p.batch * p.w.num_kv_heads // 2048))
+            if max_splits is None:
+                self.max_splits = max(1, -(-pages_max // self.split_pages))
         dev = cache.device
         self.ws = torch.empty(ops.decode_workspace_bytes(p.batch, p.w.num_q_heads, self.max_splits),
                               dtype=torch.uint8, device=dev)
@@ -201,6 +216,12 @@ class DecodeStep:
 
     def append_new(self, stream=None):
         c = self.cache
+        if c.bits == 4:
+            ops.int4_rotate_quantize_append(c.layout, c.pages, c.sinkwin, c.table, c.slots,
+                                            self.k_last, self.v_last, self.new_off, self.start,
+                                            c.rot_k, c.rot_v, c.p.w.clip, c.p.w.clip, stream,
+                                            k_mean=c.k_mean)
+            return
         if c.hadamard:
             ops.rotate_quantize_append_hadamard(c.layout, c.pages, c.sinkwin, c.table, c.slots,
                                                 self.k_last, self.v_last, self.new_off, self.start,
@@ -213,6 +234,11 @@ class DecodeStep:
 
     def decode_only(self, stream=None):
         c = self.cache
+        if c.bits == 4:
+            ops.int4_decode_attention(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.q,
+                                      self.seq_lens, c.rot_k, SM_SCALE, self.split_pages,
+                                      self.max_splits, self.ws, stream)
+            return
         ops.decode_attention(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.q, self.seq_lens,
                              c.rot_k, SM_SCALE, self.num_workers, self.max_splits, self.ws, stream)
 

@@ -25,6 +25,8 @@ EXPORTED = (
     "oscar_rotate_quantize_append",
     "oscar_rotate_quantize_append_ex",
     "oscar_rotate_quantize_append_hadamard",
+    "oscar_int4_rotate_quantize_append",
+    "oscar_int4_decode_attention",
     "oscar_decode_workspace_bytes",
     "oscar_decode_attention",
     "oscar_combine",
@@ -83,6 +85,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_rotate_quantize_append_hadamard.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P,
                                                           F32, F32, P]
     lib.oscar_rotate_quantize_append_hadamard.restype = I32
+    lib.oscar_int4_rotate_quantize_append.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P, P,
+                                                      F32, F32, P]
+    lib.oscar_int4_rotate_quantize_append.restype = I32
+    lib.oscar_int4_decode_attention.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, F32, I32, I32,
+                                                P, SZ, P]
+    lib.oscar_int4_decode_attention.restype = I32
     lib.oscar_decode_workspace_bytes.argtypes = [I32, I32, I32]
     lib.oscar_decode_workspace_bytes.restype = SZ
     lib.oscar_decode_attention.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, F32, I32, I32, P, SZ, P]
@@ -158,6 +166,38 @@ def rotate_quantize_append_hadamard(lay: Layout, pages, sinkwin, block_table, sl
         _ptr(new_offsets, torch.int32, "new_offsets"), _ptr(start_pos, torch.int32, "start_pos"),
         _ptr(signs_k, torch.int8, "signs_k"), _ptr(signs_v, torch.int8, "signs_v"),
         float(clip_k), float(clip_v), _stream(stream)))
+
+
+INT4_RECORD_BYTES = 2560
+
+
+def int4_rotate_quantize_append(lay: Layout, pages, sinkwin, block_table, slot_ids, k_new, v_new,
+                                new_offsets, start_pos, rot_k, rot_v, clip_k: float,
+                                clip_v: float, stream=None, k_mean=None) -> None:
+    """As rotate_quantize_append into an INT4 pool uint8 [P][Hkv][2560]."""
+    lib = load_library()
+    batch = start_pos.numel()
+    _check("oscar_int4_rotate_quantize_append", lib.oscar_int4_rotate_quantize_append(
+        ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
+        batch, k_new.shape[0], _ptr(k_new, torch.int16, "k_new"), _ptr(v_new, torch.int16, "v_new"),
+        _ptr(new_offsets, torch.int32, "new_offsets"), _ptr(start_pos, torch.int32, "start_pos"),
+        _ptr(rot_k, torch.float32, "rot_k"), _ptr(rot_v, torch.float32, "rot_v"),
+        _ptr(k_mean, torch.float32, "k_mean"), float(clip_k), float(clip_v), _stream(stream)))
+
+
+def int4_decode_attention(lay: Layout, pages, sinkwin, block_table, slot_ids, q, seq_lens, rot_k,
+                          sm_scale: float, split_pages: int, max_splits: int, workspace,
+                          stream=None) -> None:
+    """Decode attention over an INT4 pool; finish with combine()."""
+    lib = load_library()
+    batch, hq = q.shape[0], q.shape[1]
+    _check("oscar_int4_decode_attention", lib.oscar_int4_decode_attention(
+        ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
+        batch, hq, _ptr(q, torch.int16, "q"), _ptr(seq_lens, torch.int32, "seq_lens"),
+        _ptr(rot_k, torch.float32, "rot_k"), float(sm_scale), int(split_pages), int(max_splits),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, max_splits: int) -> int:
