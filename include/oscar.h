@@ -198,7 +198,7 @@ int32_t oscar_rotate_quantize_append_hadamard(
  * The pool is uint8 [num_pages][Hkv][2560]; within a record (slot r, channel c, group g; two
  * codes per byte, the even channel in the low nibble):
  *   [   0, 1024)  K codes at byte 64*r + c/2;
- *   [1024, 2048)  V codes at byte 1024 + 16*(c/2) + r;
+ *   [1024, 2048)  V codes at byte 1024 + 64*r + c/2;
  *   [2048, 2304)  K (fp16 scale, fp16 zero) at 2048 + 16*r + 4*g;
  *   [2304, 2560)  V (scale, zero) at 2304 + 16*r + 4*g.
  * Arguments, validation and errors as oscar_rotate_quantize_append_ex (no method choice: the

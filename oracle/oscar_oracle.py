@@ -283,7 +283,7 @@ def meta_location(kind: str, r, g):
 # INT4 records (the INT4 abstract on the OSCAR paper's page: token-wise INT4 in a paged
 # layout).  2560 bytes per (page, KV head); 16 levels, two codes per byte, low nibble first:
 #   [   0, 1024)  K codes, token-major: channel c of slot r at byte 64*r + c/2, bits 4*(c % 2);
-#   [1024, 2048)  V codes, channel-pair-major: channel c of slot r at byte 1024 + 16*(c/2) + r,
+#   [1024, 2048)  V codes, token-major as K: channel c of slot r at byte 1024 + 64*r + c/2,
 #                 bits 4*(c % 2);
 #   [2048, 2304)  K scale/zero: fp16 pair of group g of slot r at 2048 + 16*r + 4*g;
 #   [2304, 2560)  V scale/zero, the same arrangement at 2304.
@@ -297,7 +297,7 @@ def k4_code_location(r, c):
 
 
 def v4_code_location(r, c):
-    return V4_CODES + 16 * (c // 2) + r, 4 * (c % 2)
+    return V4_CODES + 64 * r + c // 2, 4 * (c % 2)
 
 
 def meta4_location(kind: str, r, g):

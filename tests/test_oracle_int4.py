@@ -66,7 +66,7 @@ def test_int4_record_layout_is_a_bijection():
 
 def test_int4_hand_derived_bytes():
     """K codes 3 and 12 for channels 0 and 1 of slot 0 make K byte 0 = 0xC3; V codes 7 and 9
-    for channels 0 and 1 of slot 5 make byte 1024 + 5 = 0x97; K scale 1.0 / zero -2.0 of
+    for channels 0 and 1 of slot 5 make byte 1024 + 64 * 5 = 0x97; K scale 1.0 / zero -2.0 of
     group 1 of slot 2 are the fp16 bytes 00 3C 00 C0 at 2048 + 32 + 4."""
     rec = np.zeros(O.RECORD4, np.uint8)
     kc = np.zeros((3, 128), np.uint8)
@@ -80,7 +80,7 @@ def test_int4_hand_derived_bytes():
     O.write_slots(rec, np.zeros(6, np.int64), np.arange(6), np.vstack([kc, np.zeros((3, 128), np.uint8)]),
                   ks, kz, vc, ones, zeros, bits=4)
     assert rec[0] == 0xC3
-    assert rec[1024 + 5] == 0x97
+    assert rec[1024 + 64 * 5] == 0x97
     assert list(rec[2048 + 32 + 4:2048 + 32 + 8]) == [0x00, 0x3C, 0x00, 0xC0]
 
 
