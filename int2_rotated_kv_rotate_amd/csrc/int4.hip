@@ -6,7 +6,7 @@
 //
 // Record (2560 bytes; codes two per byte, the even channel in the low nibble):
 //   [   0, 1024)  K codes, token-major: channel c of slot r at byte 64 r + c / 2;
-//   [1024, 2048)  V codes, channel-pair-major: channel c of slot r at byte 1024 + 16 (c / 2) + r;
+//   [1024, 2048)  V codes, token-major as K: channel c of slot r at byte 1024 + 64 r + c / 2;
 //   [2048, 2304)  K (fp16 scale, fp16 zero) of group g of slot r at 2048 + 16 r + 4 g;
 //   [2304, 2560)  V (scale, zero), the same arrangement.
 // Quantiser: s = fp16(fp32(c mx - c mn) / 15), z = fp16(c mn), code = clamp(rint((y - z) / s),
@@ -18,9 +18,10 @@
 //                       vector ALUs (R staged in LDS), quantisation, packing, BF16 copies;
 //   int4_decode_kernel  one workgroup per (split, KV head, sequence): every position of the
 //                       split, INT4 or BF16 sink/window, on the vector ALUs; each of the 16
-//                       token lanes keeps its own running softmax and the 16 are merged at the
-//                       end; writes a partial in the INT2 workspace format, so oscar_combine
-//                       finishes it (R_V^T, fixed merge order).
+//                       token lanes keeps its own running softmax (rescaled only when its max
+//                       grows) and the 16 are merged at the end; the next page's words are
+//                       loaded while a page is computed; writes a partial in the INT2 workspace
+//                       format, so oscar_combine finishes it (R_V^T, fixed merge order).
 #include "oscar_internal.h"
 
 namespace oscar {
@@ -209,26 +210,16 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
   }
   __syncthreads();
 
-  // packing: K words (thread -> row t / 16, word t % 16: channels 8w .. 8w + 7), V bytes
-  // (thread -> row t / 16, channel pairs 4 (t % 16) .. + 3), BF16 copies
+  // packing: code words (thread -> row t / 16, word t % 16: channels 8w .. 8w + 7), BF16 copies
   {
     const int r = t / 16, w = t % 16;
     const Row4 info = s_info[r];
     if (r < nrows && info.rec >= 0) {
-      const int sl = info.slot_in_page;
-      if (!is_v) {
-        uint32_t word = 0;
+      uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) word |= (uint32_t)s_code[r][8 * w + i] << (4 * i);
-        *reinterpret_cast<uint32_t*>(pages + info.rec + kK4Codes + 64 * sl + 4 * w) = word;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int cp = 4 * w + k;
-          pages[info.rec + kV4Codes + 16 * cp + sl] =
-              (uint8_t)(s_code[r][2 * cp] | (s_code[r][2 * cp + 1] << 4));
-        }
-      }
+      for (int i = 0; i < 8; ++i) word |= (uint32_t)s_code[r][8 * w + i] << (4 * i);
+      *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kV4Codes : kK4Codes) +
+                                   64 * info.slot_in_page + 4 * w) = word;
     }
     if (r < nrows && info.sw >= 0) {
       const float* yr = &s_y[r][8 * w];
@@ -247,7 +238,7 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
 // k = t % 16: channels 8k .. 8k + 7, group k / 4).  Split s of sequence b covers pages
 // [s * sp, (s + 1) * sp) with sp = max(split_pages, ceil(P_b / max_splits)), P_b = ceil(L_b / 16).
 template <int GMAX>
-__global__ __launch_bounds__(kT4) void int4_decode_kernel(
+__global__ __launch_bounds__(kT4, GMAX <= 4 ? 4 : 2) void int4_decode_kernel(
     CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
     const int32_t* __restrict__ seq_lens, float sm_scale, int split_pages, Workspace ws) {
@@ -296,64 +287,88 @@ __global__ __launch_bounds__(kT4) void int4_decode_kernel(
     for (int c = 0; c < 8; ++c) acc[j][c] = 0.f;
   }
   const int pg0 = s * sp, pg1 = min(P, pg0 + sp);
-  for (int pg = pg0; pg < pg1; ++pg) {
+  // One position's words: kind 0 none, 1 BF16 store row (K, V octets), 2 INT4 record (codes and
+  // (scale, zero) words).  Fetched one page ahead of its use.
+  struct Words {
+    int kind;
+    uint4 ku, vu;
+    uint32_t km, vm;
+  };
+  const int32_t* bt = block_table + (size_t)b * g.max_pages;
+  auto fetch = [&](int pg) {
+    Words f{0, make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), 0u, 0u};
     const int pos = pg * kPage + r;
-    if (pos >= L) continue;   // the 16 lanes of a token agree
-    float kx[8], vx[8];
-    const bool in_store = pos < n_sink || pos >= L - n_win;
-    if (in_store) {
-      if (!have_store) continue;
+    if (pg >= pg1 || pos >= L) return f;
+    if (pos < n_sink || pos >= L - n_win) {
+      if (!have_store) return f;
       const int row = pos < n_sink ? pos : g.num_sink + pos % g.window;
       const uint16_t* kr = sinkwin + (sw_base + row) * 2 * kHeadDim;
-      const uint4 ku = *reinterpret_cast<const uint4*>(kr + 8 * k);
-      const uint4 vu = *reinterpret_cast<const uint4*>(kr + kHeadDim + 8 * k);
-      const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w}, vw[4] = {vu.x, vu.y, vu.z, vu.w};
+      f.ku = *reinterpret_cast<const uint4*>(kr + 8 * k);
+      f.vu = *reinterpret_cast<const uint4*>(kr + kHeadDim + 8 * k);
+      f.kind = 1;
+      return f;
+    }
+    const int id = pg < g.max_pages ? bt[pg] : -1;
+    if (id < 0 || id >= g.num_pages) return f;
+    const uint8_t* rec = pages + ((size_t)id * g.hkv + h) * kRecord4;
+    f.ku.x = *reinterpret_cast<const uint32_t*>(rec + kK4Codes + 64 * r + 4 * k);
+    f.vu.x = *reinterpret_cast<const uint32_t*>(rec + kV4Codes + 64 * r + 4 * k);
+    f.km = *reinterpret_cast<const uint32_t*>(rec + kK4Meta + 16 * r + 4 * gi);
+    f.vm = *reinterpret_cast<const uint32_t*>(rec + kV4Meta + 16 * r + 4 * gi);
+    f.kind = 2;
+    return f;
+  };
+  Words cur = fetch(pg0);
+  for (int pg = pg0; pg < pg1; ++pg) {
+    const Words nxt = fetch(pg + 1);
+    if (cur.kind != 0) {   // the 16 lanes of a token agree
+      float kx[8], vx[8];
+      if (cur.kind == 1) {
+        const uint32_t kw[4] = {cur.ku.x, cur.ku.y, cur.ku.z, cur.ku.w};
+        const uint32_t vw[4] = {cur.vu.x, cur.vu.y, cur.vu.z, cur.vu.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kx[2 * i] = __uint_as_float(kw[i] << 16);
-        kx[2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
-        vx[2 * i] = __uint_as_float(vw[i] << 16);
-        vx[2 * i + 1] = __uint_as_float(vw[i] & 0xFFFF0000u);
+        for (int i = 0; i < 4; ++i) {
+          kx[2 * i] = __uint_as_float(kw[i] << 16);
+          kx[2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
+          vx[2 * i] = __uint_as_float(vw[i] << 16);
+          vx[2 * i + 1] = __uint_as_float(vw[i] & 0xFFFF0000u);
+        }
+      } else {
+        const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.km & 0xFFFFu));
+        const float kz = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.km >> 16));
+        const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.vm & 0xFFFFu));
+        const float vz = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.vm >> 16));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          kx[c] = fmaf(ks, (float)((cur.ku.x >> (4 * c)) & 15u), kz);
+          vx[c] = fmaf(vs, (float)((cur.vu.x >> (4 * c)) & 15u), vz);
+        }
       }
-    } else {
-      const int id = pg < g.max_pages ? block_table[(size_t)b * g.max_pages + pg] : -1;
-      if (id < 0 || id >= g.num_pages) continue;
-      const uint8_t* rec = pages + ((size_t)id * g.hkv + h) * kRecord4;
-      const uint32_t kc = *reinterpret_cast<const uint32_t*>(rec + kK4Codes + 64 * r + 4 * k);
-      const uint32_t km = *reinterpret_cast<const uint32_t*>(rec + kK4Meta + 16 * r + 4 * gi);
-      const uint32_t vm = *reinterpret_cast<const uint32_t*>(rec + kV4Meta + 16 * r + 4 * gi);
-      uint32_t vc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vc[i] = rec[kV4Codes + 16 * (4 * k + i) + r];
-      const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)(km & 0xFFFFu));
-      const float kz = (float)__builtin_bit_cast(_Float16, (uint16_t)(km >> 16));
-      const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(vm & 0xFFFFu));
-      const float vz = (float)__builtin_bit_cast(_Float16, (uint16_t)(vm >> 16));
+      for (int j = 0; j < GMAX; ++j) {
+        if (j >= G) break;
+        float d = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        kx[c] = fmaf(ks, (float)((kc >> (4 * c)) & 15u), kz);
-        vx[c] = fmaf(vs, (float)((vc[c >> 1] >> (4 * (c & 1))) & 15u), vz);
+        for (int c = 0; c < 8; ++c) d = fmaf(qv[j][c], kx[c], d);
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 4);
+        d += __shfl_xor(d, 8);
+        const float z = d * sm_log2;
+        if (z > m[j]) {   // a new running max for this token lane: rescale its sums
+          const float sc = __builtin_amdgcn_exp2f(m[j] - z);
+          l[j] *= sc;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[j][c] *= sc;
+          m[j] = z;
+        }
+        const float p = __builtin_amdgcn_exp2f(z - m[j]);
+        l[j] += p;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[j][c] = fmaf(p, vx[c], acc[j][c]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < GMAX; ++j) {
-      if (j >= G) break;
-      float d = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) d = fmaf(qv[j][c], kx[c], d);
-      d += __shfl_xor(d, 1);
-      d += __shfl_xor(d, 2);
-      d += __shfl_xor(d, 4);
-      d += __shfl_xor(d, 8);
-      const float z = d * sm_log2;
-      const float mn = fmaxf(m[j], z);
-      const float sc = __builtin_amdgcn_exp2f(m[j] - mn);
-      const float p = __builtin_amdgcn_exp2f(z - mn);
-      m[j] = mn;
-      l[j] = fmaf(l[j], sc, p);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[j][c] = fmaf(acc[j][c], sc, p * vx[c]);
-    }
+    cur = nxt;
   }
 
   // merge the 16 token lanes: max of m over r, rescale, sum over the lanes of a wave (4 token

@@ -193,9 +193,9 @@ class DecodeStep:
         self.num_workers = num_workers
         self.max_splits = (max_splits if max_splits is not None
                            else default_max_splits(p.batch, p.w.num_kv_heads, int(p.lens.max())))
-        if cache.bits == 4:   # INT4: fixed page splits, about 2048 workgroups over the batch
+        if cache.bits == 4:   # INT4: fixed page splits, about 8192 workgroups over the batch
             pages_max = -(-int(p.lens.max()) // 16)
-            self.split_pages = max(1, -(-pages_max * p.batch * p.w.num_kv_heads // 2048))
+            self.split_pages = max(1, -(-pages_max * p.batch * p.w.num_kv_heads // 8192))
             if max_splits is None:
                 self.max_splits = max(1, -(-pages_max // self.split_pages))
         dev = cache.device
