@@ -9,6 +9,7 @@
 * The INT4 output is closer to exact attention over the unquantised keys and values than the
   INT2 output of the same inputs.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -62,6 +63,8 @@ CASES = {
     "all_bf16": (W.WORKLOADS["tiny"], dict(ctx=60), None),
     "one_token": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=1), None),
     "few_splits": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=2, ctx=1200, ctx_min=900), 2),
+    "g2_no_sink_window16": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_q_heads=16, num_sink=0,
+                                                window=16), dict(batch=2, ctx=800, ctx_min=500), None),
 }
 
 

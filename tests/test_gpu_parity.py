@@ -10,6 +10,7 @@ from one worker for the whole batch (runs crossing many (sequence, head) pairs) 
 workers than pages; edge cases cover a context entirely in BF16, a single token, and a
 partial-slot budget small enough to lengthen the runs.
 """
+import dataclasses
 import math
 import sys
 
@@ -77,6 +78,11 @@ CASES = {
     "just_past_window": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=4 + 128 + 1), 1, 64),
     "page_multiple": (W.WORKLOADS["qwen3_4b"], dict(batch=2, ctx=16 * 20), 5, 64),
     "one_worker_many_pairs": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=4, ctx=500, ctx_min=140), 1, 64),
+    # other head groupings and sink/window geometries
+    "g2": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_q_heads=16), dict(batch=2, ctx=800, ctx_min=500), 0, 64),
+    "g1_two_heads": (dataclasses.replace(W.WORKLOADS["tiny"], num_q_heads=2, num_kv_heads=2), dict(ctx=700), 0, 64),
+    "no_sink_window16": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_sink=0, window=16), dict(batch=2, ctx=900, ctx_min=600), 0, 64),
+    "sink8_window1": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_sink=8, window=1), dict(batch=2, ctx=640, ctx_min=400), 3, 64),
 }
 
 
