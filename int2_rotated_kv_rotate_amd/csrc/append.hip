@@ -805,6 +805,36 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
 // (channels 32g .. 32g + 31) is lanes 16g .. 16g + 15.
 
 constexpr double kHadScale = 0x1.6a09e667f3bcdp-4;   // the double nearest to 2^-3.5 (sqrt(2)/16)
+
+// The 32-bit value of lane (this lane ^ M): DPP within quads and rows where a pattern exists
+// (M = 1, 2: quad permutes; M = 8: rotate a 16-lane row by 8), a swizzle within 32 lanes for
+// M = 4, 16, and a lane permute for M = 32.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, true);
+  else if constexpr (M == 4 || M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));
+  else return (uint32_t)__shfl_xor((int)v, M);
+}
+template <int M>
+__device__ __forceinline__ double lane_xor_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = lane_xor<M>((uint32_t)u), hi = lane_xor<M>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int M>
+__device__ __forceinline__ float lane_xor_f32(float v) {
+  return __uint_as_float(lane_xor<M>(__float_as_uint(v)));
+}
+// One cross-lane FWHT stage h = 2M on the lane's two values.
+template <int M>
+__device__ __forceinline__ void fwht_stage(double& a, double& b, int lane) {
+  const double pa = lane_xor_f64<M>(a), pb = lane_xor_f64<M>(b);
+  const bool upper = (lane & M) != 0;   // lower: a + partner; upper: partner - a
+  a = pa + (upper ? -a : a);
+  b = pb + (upper ? -b : b);
+}
 constexpr int kHadWaves = 4;
 constexpr int kHadBatch = 8;
 
@@ -872,22 +902,24 @@ __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kerne
         a = s0;
         b = d0;
       }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const double pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
-        const bool upper = (lane & m) != 0;   // lower: a + partner; upper: partner - a
-        a = pa + (upper ? -a : a);
-        b = pb + (upper ? -b : b);
-      }
+      fwht_stage<1>(a, b, lane);
+      fwht_stage<2>(a, b, lane);
+      fwht_stage<4>(a, b, lane);
+      fwht_stage<8>(a, b, lane);
+      fwht_stage<16>(a, b, lane);
+      fwht_stage<32>(a, b, lane);
       const float y0 = (float)(a * kHadScale), y1 = (float)(b * kHadScale);
 
       // group extremes over the 16 lanes of the group, scale/zero, codes
       float mx = fmaxf(y0, y1), mn = fminf(y0, y1);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-        mn = fminf(mn, __shfl_xor(mn, o));
-      }
+      mx = fmaxf(mx, lane_xor_f32<1>(mx));
+      mn = fminf(mn, lane_xor_f32<1>(mn));
+      mx = fmaxf(mx, lane_xor_f32<2>(mx));
+      mn = fminf(mn, lane_xor_f32<2>(mn));
+      mx = fmaxf(mx, lane_xor_f32<4>(mx));
+      mn = fminf(mn, lane_xor_f32<4>(mn));
+      mx = fmaxf(mx, lane_xor_f32<8>(mx));
+      mn = fminf(mn, lane_xor_f32<8>(mn));
       _Float16 s16, z16;
       group_params(mx, mn, clip, s16, z16);
       const float sc = (float)s16, z = (float)z16;
@@ -925,9 +957,9 @@ __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kerne
           // (l % 8) / 2, bits 2 * (2 * (l % 2) + e)
           const int sh = 8 * ((lane & 7) >> 1) + 4 * (lane & 1);
           uint32_t w = (c0 << sh) | (c1 << (sh + 2));
-          w |= __shfl_xor(w, 1);
-          w |= __shfl_xor(w, 2);
-          w |= __shfl_xor(w, 4);
+          w |= lane_xor<1>(w);
+          w |= lane_xor<2>(w);
+          w |= lane_xor<4>(w);
           if ((lane & 7) == 0) {
             const int d = lane >> 3;
             *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes + 8 * (16 * (d % 4) + sl) +
@@ -937,12 +969,12 @@ __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kerne
           // V half of channel residue k = (2l + e) % 16 holds channel k + 16 nb at bits 2 nb,
           // nb = l / 8: lanes l % 8 == k / 2 combine
           uint32_t v0 = c0 << (2 * (lane >> 3)), v1 = c1 << (2 * (lane >> 3));
-          v0 |= __shfl_xor(v0, 8);
-          v1 |= __shfl_xor(v1, 8);
-          v0 |= __shfl_xor(v0, 16);
-          v1 |= __shfl_xor(v1, 16);
-          v0 |= __shfl_xor(v0, 32);
-          v1 |= __shfl_xor(v1, 32);
+          v0 |= lane_xor<8>(v0);
+          v1 |= lane_xor<8>(v1);
+          v0 |= lane_xor<16>(v0);
+          v1 |= lane_xor<16>(v1);
+          v0 |= lane_xor<32>(v0);
+          v1 |= lane_xor<32>(v1);
           if (lane < 8) {
             uint8_t* base = pages + info.rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
             *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + 2 * lane)) = (uint16_t)v0;
