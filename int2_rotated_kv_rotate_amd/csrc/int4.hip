@@ -350,10 +350,10 @@ __global__ __launch_bounds__(kT4, GMAX <= 4 ? 4 : 2) void int4_decode_kernel(
         float d = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) d = fmaf(qv[j][c], kx[c], d);
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        d += __shfl_xor(d, 4);
-        d += __shfl_xor(d, 8);
+        d += lane_xor_f32<1>(d);
+        d += lane_xor_f32<2>(d);
+        d += lane_xor_f32<4>(d);
+        d += lane_xor_f32<8>(d);
         const float z = d * sm_log2;
         if (z > m[j]) {   // a new running max for this token lane: rescale its sums
           const float sc = __builtin_amdgcn_exp2f(m[j] - z);

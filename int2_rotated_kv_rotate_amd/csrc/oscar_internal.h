@@ -152,6 +152,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The 32-bit value of lane (this lane ^ M): DPP within quads and rows where a pattern exists
+// (M = 1, 2: quad permutes; M = 8: rotate a 16-lane row by 8), a swizzle within 32 lanes for
+// M = 4, 16, and a lane permute for M = 32.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, true);
+  else if constexpr (M == 4 || M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));
+  else return (uint32_t)__shfl_xor((int)v, M);
+}
+template <int M>
+__device__ __forceinline__ double lane_xor_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = lane_xor<M>((uint32_t)u), hi = lane_xor<M>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int M>
+__device__ __forceinline__ float lane_xor_f32(float v) {
+  return __uint_as_float(lane_xor<M>(__float_as_uint(v)));
+}
 // Sequence index of flattened row n, given prefix offsets off[0..batch] (binary search).
 __device__ __forceinline__ int row_to_seq(const int32_t* off, int batch, int n) {
   // find the largest b < batch with off[b] <= n.  First guess b = n (one new row per sequence,
