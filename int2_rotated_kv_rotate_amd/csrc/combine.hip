@@ -129,9 +129,11 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
 // Small-grid form: grid (Hq, batch), block 512, one workgroup per query head, for launches
 // where one workgroup per KV head would leave most of the chip idle and each head has many
 // splits.  Thread t = (slot lane sg = t / 32 of 16, channel quad c4 = t % 32): slot lane sg
-// sums slots sg, sg + 16, ... in ascending order with 16-byte loads, eight slots in flight; the
-// 16 lanes' partial sums are added in lane order.  For R_V^T, thread t computes half (kh = t % 2)
-// of output channel t / 2 (only threads < 256) from its R_V row, loaded first.
+// sums slots sg, sg + 16, ... in ascending order with 16-byte loads; its first eight slots and
+// the BF16 slot are loaded with everything else at the start (slots past the pair's count are
+// read but never used), the rest eight at a time.  The 16 lanes' partial sums are added in lane
+// order.  For R_V^T, thread t computes half (kh = t % 2) of output channel t / 2 (only threads
+// < 256) from its R_V row, loaded first.
 constexpr int kHeadThreads = 512, kSlotLanes = kHeadThreads / 32;
 
 __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int hkv, Workspace ws,
@@ -155,6 +157,17 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
     for (int k = 0; k < 16; ++k) r[k] = R[k];
   }
   const int nv_raw = ws.nvalid()[b * hkv + h];
+  const int sg = t >> 5, c4 = t & 31;
+  const float4* ob = reinterpret_cast<const float4*>(ws.o(b, hq, jq, 0)) + c4;
+  constexpr int kStride = kHeadDim / 4;  // float4 per slot
+  constexpr int kFlight = 8;
+  float4 pre[kFlight];
+#pragma unroll
+  for (int k = 0; k < kFlight; ++k) {
+    const int e = sg + k * kSlotLanes;
+    pre[k] = e < ns - 1 ? ob[(size_t)e * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float4 owin = t < 32 ? ob[(size_t)(ns - 1) * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int e = t; e < ns; e += kHeadThreads) {
     const float2 ml = *ws.ml(b, hq, jq, e);
     s_w[e] = ml.x;
@@ -190,9 +203,6 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
   if (t == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
 
   // o' partial sums: slot lane sg over slots sg, sg + 16, ... (< nv), skipping empty slots.
-  const int sg = t >> 5, c4 = t & 31;
-  const float4* ob = reinterpret_cast<const float4*>(ws.o(b, hq, jq, 0)) + c4;
-  constexpr int kStride = kHeadDim / 4;  // float4 per slot
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   auto add = [&](float w, const float4& x) {
     if (w > 0.f) {
@@ -202,8 +212,12 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
       acc.w = fmaf(w, x.w, acc.w);
     }
   };
-  int e = sg;
-  constexpr int kFlight = 8;
+#pragma unroll
+  for (int k = 0; k < kFlight; ++k) {
+    const int e = sg + k * kSlotLanes;
+    if (e < nv) add(wm[e], pre[k]);
+  }
+  int e = sg + kFlight * kSlotLanes;
   for (; e + (kFlight - 1) * kSlotLanes < nv; e += kFlight * kSlotLanes) {
     float4 x[kFlight];
 #pragma unroll
@@ -226,7 +240,7 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
     }
     const float ww = wm[ns - 1];
     if (ww > 0.f) {
-      const float4 x = ob[(size_t)(ns - 1) * kStride];
+      const float4 x = owin;
       sum.x = fmaf(ww, x.x, sum.x);
       sum.y = fmaf(ww, x.y, sum.y);
       sum.z = fmaf(ww, x.z, sum.z);

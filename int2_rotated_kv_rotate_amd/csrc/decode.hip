@@ -170,16 +170,19 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
   }
 }
 
+// hpw: query heads per workgroup, G (one workgroup per KV head) or 1 (one per query head, for
+// small batches: more workgroups, each with a quarter or less of the work).
 __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
     CacheGeom g, const uint16_t* __restrict__ q, const float* __restrict__ rot_k, int hq,
-    const int32_t* __restrict__ seq_lens, int workers, Workspace ws) {
-  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int32_t* __restrict__ seq_lens, int workers, int hpw, Workspace ws) {
+  const int b = blockIdx.y, t = threadIdx.x;
   if (b == ws.batch) {  // the extra row of workgroups: (0, batch) builds the plan
-    if (h == 0) build_plan(g, seq_lens, workers, ws);
+    if (blockIdx.x == 0) build_plan(g, seq_lens, workers, ws);
     return;
   }
   const int lane = t & 63, wv = t >> 6;
   const int G = hq / g.hkv;
+  const int h = blockIdx.x / (G / hpw), j0 = (blockIdx.x % (G / hpw)) * hpw;
   __shared__ float s_q[8][kHeadDim];                   // q (bf16 widened)
   __shared__ float s_qr[8][kHeadDim];                  // q' = q . R_K
   __shared__ float4 s_part[8][8][kHeadDim / 4];        // [input block][head][channel quad]
@@ -190,8 +193,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
   float4 r[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) r[k] = R4[(16 * ib + k) * (kHeadDim / 4) + c4];
-  for (int i = t; i < G * kHeadDim; i += kPrepThreads)
-    s_q[i / kHeadDim][i % kHeadDim] = bf16_to_f32(q[((size_t)b * hq + h * G) * kHeadDim + i]);
+  for (int i = t; i < hpw * kHeadDim; i += kPrepThreads)
+    s_q[i / kHeadDim][i % kHeadDim] = bf16_to_f32(q[((size_t)b * hq + h * G + j0) * kHeadDim + i]);
   __syncthreads();
 
   // q' partial sums over this thread's 16 input rows, then reduce the 8 blocks in order.
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
       const int i = 16 * ib + k;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (j < G) {
+        if (j < hpw) {
           const float qi = s_q[j][i];
           acc[j].x = fmaf(qi, r[k].x, acc[j].x);
           acc[j].y = fmaf(qi, r[k].y, acc[j].y);
@@ -214,10 +217,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < G) s_part[ib][j][c4] = acc[j];
+      if (j < hpw) s_part[ib][j][c4] = acc[j];
   }
   __syncthreads();
-  for (int e = t; e < G * kHeadDim; e += kPrepThreads) {
+  for (int e = t; e < hpw * kHeadDim; e += kPrepThreads) {
     const int j = e / kHeadDim, c = e % kHeadDim;
     float s = 0.f;
 #pragma unroll
@@ -227,12 +230,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
   __syncthreads();
 
   // int8 form: wave wv handles heads wv, wv + 4; lane -> channels 2*lane, 2*lane + 1.
-  for (int j = wv; j < G; j += 4) {
+  for (int j = wv; j < hpw; j += 4) {
     const float v0 = s_qr[j][2 * lane], v1 = s_qr[j][2 * lane + 1];
     float a = fmaxf(fabsf(v0), fabsf(v1));
     for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
     const float qsc = a / 127.0f;
-    char* blk = ws.qblock(b, hq, h * G + j);
+    char* blk = ws.qblock(b, hq, h * G + j0 + j);
     int esum = 0;  // sum of the encoded values 254*hi + lo over this lane's two channels
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -1042,7 +1045,7 @@ hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot
                          int hq, const int32_t* seq_lens, const Workspace& ws, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv, batch + 1), dim3(kPrepThreads), 0, stream, g, q,
-                     rot_k, hq, seq_lens, 1, ws);
+                     rot_k, hq, seq_lens, 1, hq / g.hkv, ws);
   return hipGetLastError();
 }
 
@@ -1055,17 +1058,20 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
   const int G = hq / g.hkv;
   const int workers = num_workers > 0 ? num_workers
                                       : (G <= 4 ? resident_workers<1>() : resident_workers<2>());
-  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv, batch + 1), dim3(kPrepThreads), 0, stream, g, q,
-                     rot_k, hq, seq_lens, workers, ws);
-  const int worker_groups = (workers + kWaves - 1) / kWaves;
-  const dim3 grid(worker_groups + batch * g.hkv);
   // Few pairs: their sink/window workgroups go first, so that they start at once instead of
-  // after the INT2 workers that fill the device.
+  // after the INT2 workers that fill the device, and the q rotation takes one workgroup per
+  // query head.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 0;
-  const int window_first = (long long)batch * g.hkv * 2 < cus ? 1 : 0;
+  const bool small = (long long)batch * g.hkv * 2 < cus;
+  const int window_first = small ? 1 : 0;
+  const int hpw = small ? 1 : G;
+  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (G / hpw), batch + 1), dim3(kPrepThreads), 0,
+                     stream, g, q, rot_k, hq, seq_lens, workers, hpw, ws);
+  const int worker_groups = (workers + kWaves - 1) / kWaves;
+  const dim3 grid(worker_groups + batch * g.hkv);
   const int32_t* plan = ws.plan();
   if (G <= 4)
     hipLaunchKernelGGL(int2_decode_kernel<1>, grid, dim3(64 * kWaves), 0, stream, g, pages,
