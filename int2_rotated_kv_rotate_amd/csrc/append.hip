@@ -25,73 +25,20 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Keeps the compiler from fusing an fp32 result into a following conversion (it would
-// otherwise turn fp16(c * mn) into one single-rounding mixed-precision FMA).
-__device__ __forceinline__ float materialize(float x) {
-  asm volatile("" : "+v"(x));
-  return x;
+// The INT2 forms of the shared helpers: 1536-byte records, 4 levels.
+__device__ __forceinline__ RowInfo row_info(const CacheGeom& g, const int32_t* __restrict__ block_table,
+                                            const int32_t* __restrict__ slot_ids, int batch,
+                                            const int32_t* __restrict__ new_offsets,
+                                            const int32_t* __restrict__ start_pos, bool has_store,
+                                            int n, int h, bool is_v) {
+  return row_info_t<kRecord>(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store, n,
+                             h, is_v);
 }
-
-struct RowInfo {
-  long long rec;     // byte offset of the row's page record in the pool, -1 = skip
-  int slot_in_page;  // 0..15
-  long long sw;      // element offset of the row's bf16 K/V row in the store, -1 = none
-};
-
-// Where new row n (flattened over the batch) of KV head h goes.
-__device__ RowInfo row_info(const CacheGeom& g, const int32_t* __restrict__ block_table,
-                            const int32_t* __restrict__ slot_ids, int batch,
-                            const int32_t* __restrict__ new_offsets,
-                            const int32_t* __restrict__ start_pos, bool has_store, int n, int h,
-                            bool is_v) {
-  RowInfo info{-1, 0, -1};
-  const int b = row_to_seq(new_offsets, batch, n);
-  const int first = new_offsets[b];
-  const int nnew = new_offsets[b + 1] - first;
-  const int pos = start_pos[b] + (n - first);
-  const int new_len = start_pos[b] + nnew;
-  const int lp = pos / kPage;
-  if (pos >= 0 && lp < g.max_pages) {
-    const int page = block_table[(size_t)b * g.max_pages + lp];
-    if (page >= 0 && page < g.num_pages) {
-      info.rec = ((long long)page * g.hkv + h) * kRecord;
-      info.slot_in_page = pos % kPage;
-    }
-  }
-  const int slot = slot_ids ? slot_ids[b] : b;
-  int row = -1;
-  if (pos >= 0 && pos < g.num_sink) row = pos;
-  else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
-    row = g.num_sink + pos % g.window;
-  if (row >= 0 && has_store && slot >= 0 && slot < g.num_slots)
-    info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
-              (is_v ? kHeadDim : 0);
-  return info;
-}
-
-// fp16 scale and zero of a group from its extremes: s = (c*mx - c*mn) / 3, z = c*mn, every
-// step in fp32, a signed-zero extreme counting as +0.  Monotone: s never decreases with mx nor
-// increases with mn, z never decreases with mn.
 __device__ __forceinline__ void group_params(float mx, float mn, float clip, _Float16& s16,
                                              _Float16& z16) {
-  mx = mx + 0.0f;
-  mn = mn + 0.0f;
-  const float mx_c = clip * mx;
-  const float mn_c = clip * mn;
-  const float width = mx_c - mn_c;
-  const float s32 = width / 3.0f;
-  s16 = (_Float16)materialize(s32);
-  z16 = (_Float16)materialize(mn_c);
+  group_params_t<3>(mx, mn, clip, s16, z16);
 }
-
-// clamp(rint((y - z) / s), 0, 3), 0 for a zero scale.  Monotone in y for s > 0.
-__device__ __forceinline__ int code_of(float y, float s, float z) {
-  if (s == 0.0f) return 0;
-  float q = (y - z) / s;
-  q = __builtin_rintf(q);
-  q = fminf(fmaxf(q, 0.0f), 3.0f);
-  return (int)q;
-}
+__device__ __forceinline__ int code_of(float y, float s, float z) { return code_of_t<3>(y, s, z); }
 
 __device__ __forceinline__ uint32_t meta_word(_Float16 s16, _Float16 z16) {
   return (uint32_t)__builtin_bit_cast(uint16_t, s16) |

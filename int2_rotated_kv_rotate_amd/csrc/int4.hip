@@ -33,68 +33,6 @@ constexpr int kT4 = 256;
 constexpr float kLog2e4 = 1.4426950408889634f;
 constexpr float kNegBig4 = -1.0e30f;
 
-__device__ __forceinline__ float materialize4(float x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-// 16-level scale and zero from a group's extremes (fp32 steps, no contraction).
-__device__ __forceinline__ void group_params4(float mx, float mn, float clip, _Float16& s16,
-                                              _Float16& z16) {
-  mx = mx + 0.0f;
-  mn = mn + 0.0f;
-  const float mx_c = clip * mx;
-  const float mn_c = clip * mn;
-  const float width = mx_c - mn_c;
-  const float s32 = width / 15.0f;
-  s16 = (_Float16)materialize4(s32);
-  z16 = (_Float16)materialize4(mn_c);
-}
-
-__device__ __forceinline__ uint32_t code4_of(float y, float s, float z) {
-  if (s == 0.0f) return 0u;
-  float q = (y - z) / s;
-  q = __builtin_rintf(q);
-  q = fminf(fmaxf(q, 0.0f), 15.0f);
-  return (uint32_t)q;
-}
-
-struct Row4 {
-  long long rec;     // byte offset of the record, -1 = skip
-  int slot_in_page;
-  long long sw;      // element offset of the bf16 row in the sink/window store, -1 = none
-};
-
-__device__ Row4 row4_info(const CacheGeom& g, const int32_t* __restrict__ block_table,
-                          const int32_t* __restrict__ slot_ids, int batch,
-                          const int32_t* __restrict__ new_offsets,
-                          const int32_t* __restrict__ start_pos, bool has_store, int n, int h,
-                          bool is_v) {
-  Row4 info{-1, 0, -1};
-  const int b = row_to_seq(new_offsets, batch, n);
-  const int first = new_offsets[b];
-  const int nnew = new_offsets[b + 1] - first;
-  const int pos = start_pos[b] + (n - first);
-  const int new_len = start_pos[b] + nnew;
-  const int lp = pos / kPage;
-  if (pos >= 0 && lp < g.max_pages) {
-    const int page = block_table[(size_t)b * g.max_pages + lp];
-    if (page >= 0 && page < g.num_pages) {
-      info.rec = ((long long)page * g.hkv + h) * kRecord4;
-      info.slot_in_page = pos % kPage;
-    }
-  }
-  const int slot = slot_ids ? slot_ids[b] : b;
-  int row = -1;
-  if (pos >= 0 && pos < g.num_sink) row = pos;
-  else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
-    row = g.num_sink + pos % g.window;
-  if (row >= 0 && has_store && slot >= 0 && slot < g.num_slots)
-    info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
-              (is_v ? kHeadDim : 0);
-  return info;
-}
-
 // grid (ceil(N / 16), Hkv, K|V), 256 threads.
 __global__ __launch_bounds__(kT4) void int4_append_kernel(
     CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
@@ -111,7 +49,7 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
   __shared__ uint8_t s_code[ROWS][kHeadDim];
   __shared__ float s_mu[kHeadDim];
   __shared__ double s_c[kHeadDim];
-  __shared__ Row4 s_info[ROWS];
+  __shared__ RowInfo s_info[ROWS];
 
   const int t = threadIdx.x;
   const int row0 = blockIdx.x * ROWS;
@@ -137,10 +75,10 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
     s_x[r][c] = r < nrows ? bf16_to_f32(src[((size_t)(row0 + r) * g.hkv + h) * kHeadDim + c]) : 0.f;
   }
   if (t < ROWS) {
-    Row4 info{-1, 0, -1};
+    RowInfo info{-1, 0, -1};
     if (t < nrows)
-      info = row4_info(g, block_table, slot_ids, batch, new_offsets, start_pos, sinkwin != nullptr,
-                       row0 + t, h, is_v);
+      info = row_info_t<kRecord4>(g, block_table, slot_ids, batch, new_offsets, start_pos,
+                                  sinkwin != nullptr, row0 + t, h, is_v);
     s_info[t] = info;
   }
   if (centered && t < kHeadDim) s_mu[t] = k_mean[(size_t)h * kHeadDim + t];
@@ -197,11 +135,11 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
       mn = fminf(mn, __shfl_xor(mn, o));
     }
     _Float16 s16, z16;
-    group_params4(mx, mn, clip, s16, z16);
+    group_params_t<15>(mx, mn, clip, s16, z16);
     const float sc = (float)s16, z = (float)z16;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_code[r][c0 + c] = (uint8_t)code4_of(s_y[r][c0 + c], sc, z);
-    const Row4 info = s_info[r];
+    for (int c = 0; c < 8; ++c) s_code[r][c0 + c] = (uint8_t)code_of_t<15>(s_y[r][c0 + c], sc, z);
+    const RowInfo info = s_info[r];
     if (sub == 0 && r < nrows && info.rec >= 0)
       *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kV4Meta : kK4Meta) +
                                    16 * info.slot_in_page + 4 * gi) =
@@ -213,7 +151,7 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
   // packing: code words (thread -> row t / 16, word t % 16: channels 8w .. 8w + 7), BF16 copies
   {
     const int r = t / 16, w = t % 16;
-    const Row4 info = s_info[r];
+    const RowInfo info = s_info[r];
     if (r < nrows && info.rec >= 0) {
       uint32_t word = 0;
 #pragma unroll
