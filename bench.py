@@ -149,6 +149,46 @@ def time_scrubbed(fn, n: int, scrub):
     return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
 
+def record_read_probe(w, p, cache, stream, attn_ms: float):
+    """The practical HBM ceiling of the decode launch's INT2 stream: the same records (every
+    INT2 page of every (sequence, KV head) pair, in the decode kernel's order) read by
+    oscar_read_records with the same number of wavefronts and none of the arithmetic."""
+    import torch
+    from int2_rotated_kv_rotate_amd import ops
+    lens = np.asarray(p.lens, dtype=np.int64)
+    ids = []
+    for b, L in enumerate(lens):
+        n_sink = min(L, w.num_sink)
+        hi = L - min(w.window, L - n_sink)
+        first, last = n_sink // 16, -(-hi // 16)
+        if hi <= n_sink:
+            continue
+        pages = p.table[b, first:last].astype(np.int64)
+        for h in range(w.num_kv_heads):
+            ids.append(pages * w.num_kv_heads + h)
+    ids = torch.from_numpy(np.concatenate(ids).astype(np.int32)).to(cache.device)
+    workers = torch.cuda.get_device_properties(cache.device).multi_processor_count * 16
+    out = torch.empty(64 * workers, dtype=torch.int32, device=cache.device)
+    for _ in range(3):
+        ops.read_records(cache.pages, ids, workers, out, stream)
+    reps = 10
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        ops.read_records(cache.pages, ids, workers, out, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = ids.numel() * INT2_TOKEN_HEAD_BYTES * 16
+    gbps = nbytes / (ms / 1e3) / 1e9
+    log(f"record-read probe: {ids.numel()} records, {ms:.4f} ms, {gbps:.0f} GB/s")
+    return {"records": int(ids.numel()), "bytes": int(nbytes), "ms": round(ms, 5),
+            "gbps": round(gbps, 1), "workers": workers,
+            "what": "oscar_read_records over the decode launch's INT2 records in its order, "
+                    "two 1536-byte records per step per wavefront, no arithmetic"}
+
+
 def int2_vs_bf16(n_iter: int):
     """Attention (decode launch + combine) of the INT2 path against the BF16 paged baseline of
     the same library, with a 1 GiB cache scrub before every timed launch:
@@ -387,6 +427,7 @@ def main():
     copy_gbps = 2 * (1 << 30) / (ca.elapsed_time(cb) / 5 / 1e3) / 1e9
     del scrub, csrc, cdst
     log(f"step with cache scrub {ms_scrub:.4f} ms; device copy {copy_gbps:.0f} GB/s")
+    record_read = record_read_probe(w, p, cache, stream, attn_avg)
 
     tokens_per_s = w.batch / (ms_step / 1e3)
     step_gbps = bm["step"] / (ms_step / 1e3) / 1e9
@@ -488,7 +529,9 @@ def main():
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": bm["decode_attention"], "launch_ms": round(attn_avg, 5),
                      "traffic": measured_traffic(w.name),
-                     "frac_of_copy": round(attn_gbps / copy_gbps, 4)},
+                     "frac_of_copy": round(attn_gbps / copy_gbps, 4),
+                     "frac_of_record_read": round(attn_gbps / record_read["gbps"], 4)},
+        "record_read": record_read,
         "bytes": bm,
         "prefill_append": prefill,
         "cpu_baseline": cpu,

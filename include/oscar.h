@@ -326,6 +326,23 @@ int32_t oscar_bf16_decode_attention(
     float sm_scale, int32_t split_pages, int32_t max_splits,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Read-bandwidth probe (a measurement aid, not part of the method): reads the INT2 records
+ * pool + 1536 * record_ids[i], i = 0..n-1, with the decode kernel's access pattern and none of
+ * its arithmetic, so that the HBM rate it reaches is the practical ceiling of the decode
+ * kernel's INT2 stream on the device.  A record index is page * num_kv_heads + head.
+ * Wavefront w of num_workers reads the w-th of num_workers equal runs of the list, two
+ * records per step, and writes the XOR of all 32-bit words it read, folded per lane, to
+ * out[64*w + lane].
+ *   pool        uint8 INT2 pool (16-byte aligned); every record_ids[i] must lie in the pool
+ *               (not checked: the kernel reads pool + 1536 * record_ids[i])
+ *   record_ids  int32 [n]
+ *   out         uint32 [64 * num_workers], written
+ * Returns OSCAR_ERR_INVALID_ARGUMENT for n < 0, num_workers < 1 or a null/misaligned pointer.
+ */
+int32_t oscar_read_records(const uint8_t* pool, const int32_t* record_ids, int32_t n,
+                           int32_t num_workers, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,7 @@ SOURCES = {
     "bf16_baseline.hip": [],
     # the INT4 quantiser is the same kind of fp32 formula
     "int4.hip": ["-ffp-contract=off"],
+    "probe.hip": [],
 }
 COMMON = [
     "-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

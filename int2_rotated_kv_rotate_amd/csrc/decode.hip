@@ -552,9 +552,12 @@ __device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16
     const v8bf alo = __builtin_bit_cast(v8bf, make_uint4(l0.x, l0.y, l1.x, l1.y));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint32_t y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = q == 0 ? (vsw[i] << 3) : (vsw[i] >> (4 * q - 3));
+      // words shifted in 64-bit pairs: bits crossing between the two words of a pair land
+      // outside both masks (bits 3-6 and 19-22 of each word)
+      const uint64_t v01 = ((uint64_t)vsw[1] << 32) | vsw[0], v23 = ((uint64_t)vsw[3] << 32) | vsw[2];
+      const uint64_t s01 = q == 0 ? (v01 << 3) : (v01 >> (4 * q - 3));
+      const uint64_t s23 = q == 0 ? (v23 << 3) : (v23 >> (4 * q - 3));
+      const uint32_t y[4] = {(uint32_t)s01, (uint32_t)(s01 >> 32), (uint32_t)s23, (uint32_t)(s23 >> 32)};
       const v8bf ve = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_e, magic), and_or(y[1], mask_e, magic),
                                                           and_or(y[2], mask_e, magic), and_or(y[3], mask_e, magic)));
       const v8bf vo = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_o, magic), and_or(y[1], mask_o, magic),

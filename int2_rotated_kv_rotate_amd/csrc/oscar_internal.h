@@ -129,6 +129,10 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream);
 
+// Read-bandwidth probe over INT2 records (no arithmetic): see oscar_read_records.
+hipError_t launch_read_records(const uint8_t* pool, const int32_t* record_ids, int n, int workers,
+                               uint32_t* out, hipStream_t stream);
+
 hipError_t launch_bf16_append(const CacheGeom& g, uint16_t* pages, const int32_t* block_table,
                               int batch, int total_new, const uint16_t* k_new,
                               const uint16_t* v_new, const int32_t* new_offsets,

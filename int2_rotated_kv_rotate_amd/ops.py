@@ -32,6 +32,7 @@ EXPORTED = (
     "oscar_combine",
     "oscar_bf16_append",
     "oscar_bf16_decode_attention",
+    "oscar_read_records",
 )
 
 
@@ -101,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_bf16_append.restype = I32
     lib.oscar_bf16_decode_attention.argtypes = [LP, P, P, I32, I32, P, P, F32, I32, I32, P, SZ, P]
     lib.oscar_bf16_decode_attention.restype = I32
+    lib.oscar_read_records.argtypes = [P, P, I32, I32, P, P]
+    lib.oscar_read_records.restype = I32
     _lib = lib
     return lib
 
@@ -247,3 +250,15 @@ def bf16_decode_attention(lay: Layout, pages, block_table, q, seq_lens, sm_scale
         _ptr(block_table, torch.int32, "block_table"), batch, hq, _ptr(q, torch.int16, "q"),
         _ptr(seq_lens, torch.int32, "seq_lens"), float(sm_scale), split_pages, max_splits,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def read_records(pages, record_ids, num_workers: int, out, stream=None) -> None:
+    """Read-bandwidth probe: reads the INT2 records record_ids (page * Hkv + head) of the pool
+    with the decode kernel's access pattern and writes per-lane XORs to out (uint32 / int32
+    [64 * num_workers])."""
+    lib = load_library()
+    if out.numel() < 64 * num_workers:
+        raise ValueError("out: needs 64 * num_workers entries")
+    _check("oscar_read_records", lib.oscar_read_records(
+        _ptr(pages, torch.uint8, "pages"), _ptr(record_ids, torch.int32, "record_ids"),
+        record_ids.numel(), num_workers, _ptr(out, torch.int32, "out"), _stream(stream)))
