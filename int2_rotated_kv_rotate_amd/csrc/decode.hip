@@ -541,36 +541,44 @@ __device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16
   page_weights<NCB, MASKED>(aB, V.vmB, liveB, qo, st, tile, t, r, kPage);
 
   const uint32_t vsw[4] = {V.vs.x, V.vs.y, V.vs.z, V.vs.w};
+  // A operands of every column block: row (j,g) = l % 16 (= t as an index), tokens 8r .. 8r+7
+  // of the pair (rows are 8-byte aligned only: two 8-byte reads each)
+  v8bf ahi[NCB], alo[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    // A operands: row (j,g) = l % 16 (= t as an index), tokens 8r .. 8r+7 of the pair
-    // (rows are 8-byte aligned only: two 8-byte reads each)
     const uint2* ph = reinterpret_cast<const uint2*>(&tile.w[cb][0][t][8 * r]);
     const uint2* pl = reinterpret_cast<const uint2*>(&tile.w[cb][1][t][8 * r]);
     const uint2 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
-    const v8bf ahi = __builtin_bit_cast(v8bf, make_uint4(h0.x, h0.y, h1.x, h1.y));
-    const v8bf alo = __builtin_bit_cast(v8bf, make_uint4(l0.x, l0.y, l1.x, l1.y));
+    ahi[cb] = __builtin_bit_cast(v8bf, make_uint4(h0.x, h0.y, h1.x, h1.y));
+    alo[cb] = __builtin_bit_cast(v8bf, make_uint4(l0.x, l0.y, l1.x, l1.y));
+  }
+  // B operands built once per pair and shared by the column blocks
+  const uint64_t v01 = ((uint64_t)vsw[1] << 32) | vsw[0], v23 = ((uint64_t)vsw[3] << 32) | vsw[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // words shifted in 64-bit pairs: bits crossing between the two words of a pair land
-      // outside both masks (bits 3-6 and 19-22 of each word)
-      const uint64_t v01 = ((uint64_t)vsw[1] << 32) | vsw[0], v23 = ((uint64_t)vsw[3] << 32) | vsw[2];
-      const uint64_t s01 = q == 0 ? (v01 << 3) : (v01 >> (4 * q - 3));
-      const uint64_t s23 = q == 0 ? (v23 << 3) : (v23 >> (4 * q - 3));
-      const uint32_t y[4] = {(uint32_t)s01, (uint32_t)(s01 >> 32), (uint32_t)s23, (uint32_t)(s23 >> 32)};
-      const v8bf ve = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_e, magic), and_or(y[1], mask_e, magic),
-                                                          and_or(y[2], mask_e, magic), and_or(y[3], mask_e, magic)));
-      const v8bf vo = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_o, magic), and_or(y[1], mask_o, magic),
-                                                          and_or(y[2], mask_o, magic), and_or(y[3], mask_o, magic)));
-      st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, ve, st.acc[cb][2 * q], 0, 0, 0);
-      st.acc[cb][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vo, st.acc[cb][2 * q + 1], 0, 0, 0);
-      st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ve, st.acc[cb][2 * q], 0, 0, 0);
-      st.acc[cb][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vo, st.acc[cb][2 * q + 1], 0, 0, 0);
+  for (int q = 0; q < 4; ++q) {
+    // words shifted in 64-bit pairs: bits crossing between the two words of a pair land
+    // outside both masks (bits 3-6 and 19-22 of each word)
+    const uint64_t s01 = q == 0 ? (v01 << 3) : (v01 >> (4 * q - 3));
+    const uint64_t s23 = q == 0 ? (v23 << 3) : (v23 >> (4 * q - 3));
+    const uint32_t y[4] = {(uint32_t)s01, (uint32_t)(s01 >> 32), (uint32_t)s23, (uint32_t)(s23 >> 32)};
+    const v8bf ve = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_e, magic), and_or(y[1], mask_e, magic),
+                                                        and_or(y[2], mask_e, magic), and_or(y[3], mask_e, magic)));
+    const v8bf vo = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_o, magic), and_or(y[1], mask_o, magic),
+                                                        and_or(y[2], mask_o, magic), and_or(y[3], mask_o, magic)));
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cb], ve, st.acc[cb][2 * q], 0, 0, 0);
+      st.acc[cb][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cb], vo, st.acc[cb][2 * q + 1], 0, 0, 0);
+      st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cb], ve, st.acc[cb][2 * q], 0, 0, 0);
+      st.acc[cb][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cb], vo, st.acc[cb][2 * q + 1], 0, 0, 0);
     }
-    // the same weights against a column of ones: the exact bf16 weight sums that the code
-    // accumulators carry in their "1 +" part
-    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, ones, st.wsum[cb], 0, 0, 0);
-    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ones, st.wsum[cb], 0, 0, 0);
+  }
+  // the same weights against a column of ones: the exact bf16 weight sums that the code
+  // accumulators carry in their "1 +" part
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cb], ones, st.wsum[cb], 0, 0, 0);
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cb], ones, st.wsum[cb], 0, 0, 0);
   }
 }
 
