@@ -132,11 +132,16 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
   long long C = max(1LL, ((long long)total + workers - 1) / workers);
   if (max_splits > 1) C = max(C, ((long long)pmax + max_splits - 2) / (max_splits - 1));
   else C = max(C, (long long)total);
-  // pass 2: prefix sums in chunks of kPrepThreads sequences
+  // pass 2: prefix sums in chunks of kPrepThreads sequences; then the partial count of every
+  // (sequence, KV head) pair of the chunk, spread over all threads.  Page counts fit in 31
+  // bits (the plan stores them as int32), so the run arithmetic is unsigned 32-bit.
+  __shared__ int s_start[kPrepThreads];
+  __shared__ int s_np[kPrepThreads];
   int32_t* pstart = ws.pstart();
   int32_t* npg = ws.npg();
   int32_t* pglo = ws.pglo();
   int32_t* nvalid = ws.nvalid();
+  const uint32_t Cu = (uint32_t)C;
   int carry = 0;
   for (int base = 0; base < B; base += kPrepThreads) {
     const int b = base + t;
@@ -151,15 +156,21 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
       s_scan[t] += y;
       __syncthreads();
     }
+    const int start = carry + s_scan[t] - x;
     if (b < B) {
-      const int start = carry + s_scan[t] - x;
       pstart[b] = start;
       npg[b] = P;
       pglo[b] = first;
-      for (int h = 0; h < g.hkv; ++h) {
-        const long long s0 = (long long)start + (long long)h * P;
-        nvalid[b * g.hkv + h] = P == 0 ? 0 : (int)((s0 + P - 1) / C - s0 / C + 1);
-      }
+    }
+    s_start[t] = start;
+    s_np[t] = P;
+    __syncthreads();
+    const int nb = min(kPrepThreads, B - base);
+    for (int i = t; i < nb * g.hkv; i += kPrepThreads) {
+      const int bl = i / g.hkv, h = i - bl * g.hkv;
+      const uint32_t Pp = (uint32_t)s_np[bl];
+      const uint32_t s0 = (uint32_t)s_start[bl] + (uint32_t)h * Pp;
+      nvalid[(base + bl) * g.hkv + h] = Pp == 0 ? 0 : (int)((s0 + Pp - 1) / Cu - s0 / Cu + 1);
     }
     carry += s_scan[kPrepThreads - 1];
     __syncthreads();
