@@ -78,7 +78,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
     const bool use = (e < nv || e == ns - 1) && wl[e] > 0.f;
     const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
     wm[e] = w;
-    lloc = fmaf(w, wl[e], lloc);
+    if (use) lloc = fmaf(w, wl[e], lloc);  // an unused slot's stale l may be NaN
   }
   for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2);
   if ((c & 63) == 0) s_red[j][2 + (c >> 6)] = lloc;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
     const bool use = (e < nv || e == ns - 1) && wl[e] > 0.f;
     const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
     wm[e] = w;
-    lloc = fmaf(w, wl[e], lloc);
+    if (use) lloc = fmaf(w, wl[e], lloc);  // an unused slot's stale l may be NaN
   }
   for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2);
   if (lane == 0) s_red[1][wv] = lloc;

@@ -184,10 +184,12 @@ def default_max_splits(batch: int, num_kv_heads: int, max_context: int) -> int:
 class DecodeStep:
     """Buffers and launches of one decode step: append the new token, attend, combine."""
 
-    def __init__(self, cache: GpuCache, num_workers: int = 0, max_splits: Optional[int] = None):
+    def __init__(self, cache: GpuCache, num_workers: int = 0, max_splits: Optional[int] = None,
+                 ws_fill: Optional[int] = None):
         """num_workers 0: one worker per resident wavefront slot; max_splits bounds the INT2
         partials per (sequence, KV head) (a small value lengthens the workers' runs); None
-        takes default_max_splits."""
+        takes default_max_splits.  ws_fill: a byte written over the whole workspace first
+        (0xFF makes every float in it a NaN; the kernels must not depend on its contents)."""
         p = cache.p
         self.cache = cache
         self.num_workers = num_workers
@@ -201,6 +203,8 @@ class DecodeStep:
         dev = cache.device
         self.ws = torch.empty(ops.decode_workspace_bytes(p.batch, p.w.num_q_heads, self.max_splits),
                               dtype=torch.uint8, device=dev)
+        if ws_fill is not None:
+            self.ws.fill_(ws_fill)
         self.q = as_i16(p.q).to(dev)
         self.seq_lens = torch.from_numpy(p.lens.astype(np.int32)).to(dev)
         self.out = torch.empty((p.batch, p.w.num_q_heads, 128), dtype=torch.float32, device=dev)

@@ -38,7 +38,7 @@ def full_run():
     p = H.make_problem(w)
     cache = H.GpuCache(p, fill=SENTINEL)
     last_k, last_v = cache.fill_context()
-    step = H.DecodeStep(cache)          # bench.py's configuration: auto workers, 64 slots
+    step = H.DecodeStep(cache, ws_fill=0xFF)          # bench.py's configuration: auto workers, 64 slots
     step.set_new_token(last_k, last_v)
     step.run()
     torch.cuda.synchronize()

@@ -45,7 +45,7 @@ def _oracle_cache(p, k_mean=None):
 def _run(p, max_splits=None, k_mean=None, bits=4):
     cache = H.GpuCache(p, fill=SENTINEL, k_mean=k_mean, bits=bits)
     lk, lv = cache.fill_context()
-    step = H.DecodeStep(cache, max_splits=max_splits)
+    step = H.DecodeStep(cache, ws_fill=0xFF, max_splits=max_splits)
     step.set_new_token(lk, lv)
     step.run()
     torch.cuda.synchronize()

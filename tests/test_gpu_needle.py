@@ -40,7 +40,7 @@ def test_needle_weight_128k():
 
     cache = H.GpuCache(p, fill=SENTINEL)
     last_k, last_v = cache.fill_context()
-    step = H.DecodeStep(cache)
+    step = H.DecodeStep(cache, ws_fill=0xFF)
     step.set_new_token(last_k, last_v)
     step.run()
     torch.cuda.synchronize()
