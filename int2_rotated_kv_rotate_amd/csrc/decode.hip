@@ -97,9 +97,10 @@ constexpr int kPrepThreads = 256;
 // `workers` runs and leaves no pair more than max_splits runs.
 __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_lens, int workers,
                            const Workspace& ws) {
-  __shared__ int s_scan[kPrepThreads];
-  __shared__ int s_max[kPrepThreads];
-  const int t = threadIdx.x, B = ws.batch, max_splits = ws.nslots - 1;
+  constexpr int kPlanWaves = kPrepThreads / 64;
+  __shared__ int s_w[2][kPlanWaves];  // per-wave sums / maxima, then per-wave scan totals
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int B = ws.batch, max_splits = ws.nslots - 1;
   auto int2_pages = [&](int b, int& first) -> int {  // INT2 pages of sequence b, first page
     const int L = max(seq_lens[b], 0);
     const int n_sink = min(L, g.num_sink);
@@ -108,7 +109,7 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
     if (hi <= lo || g.num_pages < 1) return 0;
     return max(min((hi + kPage - 1) / kPage, g.max_pages) - first, 0);
   };
-  // pass 1: total pages and the largest pair
+  // pass 1: total pages and the largest pair (wave reductions, then the waves in order)
   int tot = 0, pmax = 0;
   for (int b = t; b < B; b += kPrepThreads) {
     int first;
@@ -116,27 +117,28 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
     tot += P * g.hkv;
     pmax = max(pmax, P);
   }
-  s_scan[t] = tot;
-  s_max[t] = pmax;
-  __syncthreads();
-  for (int o = kPrepThreads / 2; o > 0; o >>= 1) {
-    if (t < o) {
-      s_scan[t] += s_scan[t + o];
-      s_max[t] = max(s_max[t], s_max[t + o]);
-    }
-    __syncthreads();
+  for (int o = 32; o >= 1; o >>= 1) {
+    tot += __shfl_xor(tot, o);
+    pmax = max(pmax, __shfl_xor(pmax, o));
   }
-  const int total = s_scan[0];
-  pmax = s_max[0];
+  if (lane == 0) {
+    s_w[0][wv] = tot;
+    s_w[1][wv] = pmax;
+  }
+  __syncthreads();
+  int total = 0;
+  pmax = 0;
+  for (int k = 0; k < kPlanWaves; ++k) {
+    total += s_w[0][k];
+    pmax = max(pmax, s_w[1][k]);
+  }
   __syncthreads();
   long long C = max(1LL, ((long long)total + workers - 1) / workers);
   if (max_splits > 1) C = max(C, ((long long)pmax + max_splits - 2) / (max_splits - 1));
   else C = max(C, (long long)total);
-  // pass 2: prefix sums in chunks of kPrepThreads sequences; then the partial count of every
-  // (sequence, KV head) pair of the chunk, spread over all threads.  Page counts fit in 31
-  // bits (the plan stores them as int32), so the run arithmetic is unsigned 32-bit.
-  __shared__ int s_start[kPrepThreads];
-  __shared__ int s_np[kPrepThreads];
+  // pass 2: prefix sums in chunks of kPrepThreads sequences (a wave scan, then the waves'
+  // totals in order), and the partial count of each (sequence, KV head) pair.  Page counts fit
+  // in 31 bits (the plan stores them as int32), so the run arithmetic is unsigned 32-bit.
   int32_t* pstart = ws.pstart();
   int32_t* npg = ws.npg();
   int32_t* pglo = ws.pglo();
@@ -148,31 +150,30 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
     int first = 0;
     const int P = b < B ? int2_pages(b, first) : 0;
     const int x = P * g.hkv;
-    s_scan[t] = x;
-    __syncthreads();
-    for (int o = 1; o < kPrepThreads; o <<= 1) {  // inclusive scan
-      const int y = t >= o ? s_scan[t - o] : 0;
-      __syncthreads();
-      s_scan[t] += y;
-      __syncthreads();
+    int incl = x;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
     }
-    const int start = carry + s_scan[t] - x;
+    if (lane == 63) s_w[0][wv] = incl;
+    __syncthreads();
+    int before = 0, chunk = 0;
+    for (int k = 0; k < kPlanWaves; ++k) {
+      before += k < wv ? s_w[0][k] : 0;
+      chunk += s_w[0][k];
+    }
+    const int start = carry + before + incl - x;
     if (b < B) {
       pstart[b] = start;
       npg[b] = P;
       pglo[b] = first;
+      const uint32_t Pp = (uint32_t)P;
+      for (int h = 0; h < g.hkv; ++h) {
+        const uint32_t s0 = (uint32_t)start + (uint32_t)h * Pp;
+        nvalid[b * g.hkv + h] = Pp == 0 ? 0 : (int)((s0 + Pp - 1) / Cu - s0 / Cu + 1);
+      }
     }
-    s_start[t] = start;
-    s_np[t] = P;
-    __syncthreads();
-    const int nb = min(kPrepThreads, B - base);
-    for (int i = t; i < nb * g.hkv; i += kPrepThreads) {
-      const int bl = i / g.hkv, h = i - bl * g.hkv;
-      const uint32_t Pp = (uint32_t)s_np[bl];
-      const uint32_t s0 = (uint32_t)s_start[bl] + (uint32_t)h * Pp;
-      nvalid[(base + bl) * g.hkv + h] = Pp == 0 ? 0 : (int)((s0 + Pp - 1) / Cu - s0 / Cu + 1);
-    }
-    carry += s_scan[kPrepThreads - 1];
+    carry += chunk;
     __syncthreads();
   }
   if (t == 0) {
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
   const int lane = t & 63, wv = t >> 6;
   const int G = hq / g.hkv;
   const int h = blockIdx.x / (G / hpw), j0 = (blockIdx.x % (G / hpw)) * hpw;
-  __shared__ float s_q[8][kHeadDim];                   // q (bf16 widened)
+  __shared__ __attribute__((aligned(16))) float s_q[8][kHeadDim];  // q (bf16 widened)
   __shared__ float s_qr[8][kHeadDim];                  // q' = q . R_K
   __shared__ float4 s_part[8][8][kHeadDim / 4];        // [input block][head][channel quad]
 
@@ -208,27 +209,22 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
     s_q[i / kHeadDim][i % kHeadDim] = bf16_to_f32(q[((size_t)b * hq + h * G + j0) * kHeadDim + i]);
   __syncthreads();
 
-  // q' partial sums over this thread's 16 input rows, then reduce the 8 blocks in order.
-  {
-    float4 acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // q' partial sums over this thread's 16 input rows (ascending), one query head at a time,
+  // its 16 q values read as four 16-byte loads; then reduce the 8 blocks in order.
+  for (int j = 0; j < hpw; ++j) {
+    const float4* qp = reinterpret_cast<const float4*>(&s_q[j][16 * ib]);
+    const float4 qv[4] = {qp[0], qp[1], qp[2], qp[3]};
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int i = 16 * ib + k;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < hpw) {
-          const float qi = s_q[j][i];
-          acc[j].x = fmaf(qi, r[k].x, acc[j].x);
-          acc[j].y = fmaf(qi, r[k].y, acc[j].y);
-          acc[j].z = fmaf(qi, r[k].z, acc[j].z);
-          acc[j].w = fmaf(qi, r[k].w, acc[j].w);
-        }
+      const float4& q4 = qv[k >> 2];
+      const float qi = (k & 3) == 0 ? q4.x : (k & 3) == 1 ? q4.y : (k & 3) == 2 ? q4.z : q4.w;
+      a.x = fmaf(qi, r[k].x, a.x);
+      a.y = fmaf(qi, r[k].y, a.y);
+      a.z = fmaf(qi, r[k].z, a.z);
+      a.w = fmaf(qi, r[k].w, a.w);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < hpw) s_part[ib][j][c4] = acc[j];
+    s_part[ib][j][c4] = a;
   }
   __syncthreads();
   for (int e = t; e < hpw * kHeadDim; e += kPrepThreads) {

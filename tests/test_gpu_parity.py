@@ -27,6 +27,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
 SENTINEL = 0xA5
+WS_FILL = 0xFF   # every float of a fresh workspace reads as NaN: nothing may depend on it
 
 
 def _log(msg):
@@ -52,7 +53,7 @@ def run_gpu(p: H.Problem, num_workers=0, max_splits=H.DEFAULT_MAX_SPLITS, k_mean
             hadamard_signs=None):
     cache = H.GpuCache(p, fill=SENTINEL, k_mean=k_mean, hadamard_signs=hadamard_signs)
     last_k, last_v = cache.fill_context()
-    step = H.DecodeStep(cache, num_workers=num_workers, max_splits=max_splits)
+    step = H.DecodeStep(cache, num_workers=num_workers, max_splits=max_splits, ws_fill=WS_FILL)
     step.set_new_token(last_k, last_v)
     step.run()
     torch.cuda.synchronize()
@@ -83,6 +84,9 @@ CASES = {
     "g1_two_heads": (dataclasses.replace(W.WORKLOADS["tiny"], num_q_heads=2, num_kv_heads=2), dict(ctx=700), 0, 64),
     "no_sink_window16": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_sink=0, window=16), dict(batch=2, ctx=900, ctx_min=600), 0, 64),
     "sink8_window1": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_sink=8, window=1), dict(batch=2, ctx=640, ctx_min=400), 3, 64),
+    # more sequences than one chunk of the work plan's prefix sums (256), short and ragged:
+    # many have no INT2 page at all
+    "batch_300_short": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_q_heads=4, num_kv_heads=1), dict(batch=300, ctx=220, ctx_min=1), 0, 64),
 }
 
 
@@ -224,7 +228,7 @@ def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
     """oscar_combine on seeded partials (not produced by the library) vs the oracle merge.
 
     Each (sequence, KV head) pair declares how many INT2 slots it filled (the plan's nvalid);
-    slots past that hold NaN outputs and large (m, l) and must not be read."""
+    slots past that hold NaN outputs, a large m and an l of 7 or NaN, and must not be read."""
     B, hq, hkv = 3, 8, 2
     nslots = max_splits + 1
     G = hq // hkv
@@ -240,7 +244,7 @@ def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
             stale = np.arange(nvalid[b, j // G], max_splits)
             o[b, j, stale] = np.nan
             m[b, j, stale] = 1e30
-            l[b, j, stale] = 7.0
+            l[b, j, stale] = 7.0 if j % 2 == 0 else np.nan
     rot_v = W.rotations(W.scaled(W.WORKLOADS["qwen3_4b"], name="rv"), "v")[:hkv].astype(np.float32)
     nbytes = ops.decode_workspace_bytes(B, hq, max_splits)
     ws = np.zeros(nbytes, np.uint8)
@@ -299,8 +303,8 @@ def test_bf16_baseline_parity(name, over, split_pages):
     torch.cuda.synchronize()
     assert np.array_equal(pages.cpu().numpy().view(np.uint16), opages)
     max_splits = int(math.ceil(p.table.shape[1] / split_pages))
-    ws = torch.empty(ops.decode_workspace_bytes(w.batch, w.num_q_heads, max_splits), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.full((ops.decode_workspace_bytes(w.batch, w.num_q_heads, max_splits),), WS_FILL,
+                    dtype=torch.uint8, device="cuda")
     q = H.as_i16(p.q).cuda()
     lens = torch.from_numpy(p.lens.astype(np.int32)).cuda()
     ops.bf16_decode_attention(lay, pages, table, q, lens, H.SM_SCALE, split_pages, max_splits, ws)
