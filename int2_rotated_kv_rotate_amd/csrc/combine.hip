@@ -29,19 +29,22 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
 
   // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of the slots.
-  // Loads are issued 4 at a time before their LDS stores (4096 quads = a multiple of
-  // 4 * blockDim.x for every group size), so staging costs 1 to 8 memory latencies.
+  // Loads are issued 8 at a time before their LDS stores, so staging costs one memory latency
+  // for G >= 4 (4096 quads over 512 or 1024 threads) and 2 or 4 for G = 2, 1.
   if (rot_v != nullptr) {
     const float4* R = reinterpret_cast<const float4*>(rot_v + (size_t)h * kHeadDim * kHeadDim);
-    constexpr int kQuads = kHeadDim * kHeadDim / 4, kChunk = 4;
+    constexpr int kQuads = kHeadDim * kHeadDim / 4, kChunk = 8;
     for (int e0 = threadIdx.x; e0 < kQuads; e0 += kChunk * blockDim.x) {
       float4 rr[kChunk];
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) rr[k] = R[e0 + k * blockDim.x];
+      for (int k = 0; k < kChunk; ++k) {
+        const int e = e0 + k * blockDim.x;
+        rr[k] = e < kQuads ? R[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
       for (int k = 0; k < kChunk; ++k) {
         const int e = e0 + k * blockDim.x;
-        s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = rr[k];
+        if (e < kQuads) s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = rr[k];
       }
     }
   }
