@@ -306,7 +306,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # after an idle gap the shader clock ramps up over the first ~100 back-to-back steps
+    # (~0.32 ms per step at first, ~0.26 ms once it has settled): warm up past the ramp
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qwen3_8b_b64")
     ap.add_argument("--workers", type=int, default=0,
                     help="INT2 worker wavefronts (0: one per resident slot of the device)")
