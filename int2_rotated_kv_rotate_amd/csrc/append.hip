@@ -258,8 +258,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_append_kernel(
 //     which the extremes are the defined ones;
 //   * a code: with t = (y - z) * (1/s) (fp32), the defined t lies within
 //     mt = (E + (|y| + |z| + E) 2^-23) / s * 1.01 + 2^-19 of it (E, the rounding of y - z, the
-//     rounding of the defined division, of 1/s and of the product, for |t| < 4); the code is
-//     clamp(rint(t), 0, 3) when no boundary 1/2, 3/2, 5/2 lies within mt of t, else recomputed;
+//     rounding of the defined division, of 1/s and of the product, for |t| < 4); the kernel
+//     takes |y| as the group's largest; the code is clamp(rint(t), 0, 3) when no half-integer
+//     lies within mt of t (which includes the boundaries 1/2, 3/2, 5/2), else recomputed;
 //   * a BF16 copy (sink/window row): certified when bf16(y - E) == bf16(y + E), else recomputed.
 //
 // Recomputation reads R (fp32) from LDS, where the workgroup stages it once; four lanes share a
@@ -640,6 +641,11 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
       const bool bf = info.sw >= 0;
       const float Eg = er * s_cng[gi] + kErrAbs +
                        (centered ? (s_cmax[gi] + 2.0f * fmaxf(fabsf(mx), fabsf(mn))) * 0x1p-22f : 0.0f);
+      // code margins of the group (see above), taken at its largest |y| (>= every |y| in it):
+      // one for values recomputed in pass 1 (E = 0), one for the others
+      const float gabs = fmaxf(fabsf(mx), fabsf(mn)) + fabsf(z);
+      const float mt_exact = (gabs * 0x1p-23f) * inv * 1.01f + 0x1p-19f;
+      const float mt_bound = (Eg + (gabs + Eg) * 0x1p-23f) * inv * 1.01f + 0x1p-19f;
       const uint4 mk = *reinterpret_cast<const uint4*>(&s_code[r][c0]);
       const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
       uint32_t cw[4] = {0, 0, 0, 0};
@@ -651,14 +657,17 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float y = yk[i];
-          const float E = ((mw[k] >> (8 * i)) & 0xFF) == kExact ? 0.0f : Eg;
+          const bool exact = ((mw[k] >> (8 * i)) & 0xFF) == kExact;
           // t within mt of the defined t (see above); the code is certain when no boundary
-          // k + 1/2 lies within mt of t
+          // 1/2, 3/2, 5/2 lies within mt of t.  The distance to the nearest half-integer is at
+          // most the distance to those three, so comparing it is conservative.
           const float tq = (y - z) * inv;
-          const float mt = (E + (fabsf(y) + fabsf(z) + E) * 0x1p-23f) * inv * 1.01f + 0x1p-19f;
-          const float dist = fminf(fminf(fabsf(tq - 0.5f), fabsf(tq - 1.5f)), fabsf(tq - 2.5f));
-          bool ok = dist > mt;
-          if (bf) ok = ok && f32_to_bf16_rne(y - E) == f32_to_bf16_rne(y + E);
+          const float dist = fabsf(__builtin_amdgcn_fractf(tq) - 0.5f);
+          bool ok = dist > (exact ? mt_exact : mt_bound);
+          if (bf) {
+            const float E = exact ? 0.0f : Eg;
+            ok = ok && f32_to_bf16_rne(y - E) == f32_to_bf16_rne(y + E);
+          }
           const int code = (int)fminf(fmaxf(__builtin_rintf(tq), 0.0f), 3.0f);
           cw[k] |= (uint32_t)code << (8 * i);
           flagged |= (ok ? 0u : 1u) << (4 * k + i);
