@@ -418,14 +418,25 @@ __device__ __forceinline__ void read_pair_v(uint32_t ps, uint32_t a16, uint32_t 
       : "memory");
 }
 
+// Layouts of the 16 MFMA rows: NCB = 1 or 2 blocks of (query head, group) rows, 4 heads x 4
+// groups each (G <= 4: one block; a lane owns one head per block); NCB = 8 (G = 8): rows
+// (head, group pair), 8 heads x 2 groups, one block for groups {0, 1} and one for {2, 3}, so a
+// QK product needs only the half of the channels that its groups cover and a P.V product uses
+// 8 of its 16 rows; a lane owns two heads.
+template <int NCB>
+constexpr int kLaneHeads = NCB == 8 ? 2 : NCB;   // heads whose softmax state a lane keeps
+template <int NCB>
+constexpr int kAccSets = NCB == 8 ? 1 : NCB;     // sets of 8 column-block accumulators
+
 template <int NCB>
 struct SplitState {
-  v4f acc[NCB][8];     // P.V accumulators
-  float mref[NCB];     // reference (log2 units) of this lane's head; p = 2^(z - mref)
-  float mlane[NCB];    // running max of this lane's unscaled logits
-  float lsum[NCB];     // sum of p over this lane's token positions
-  float zp[NCB][4];    // sum of p * zero_v per group
-  v4f wsum[NCB];       // sum of the bf16 weights W = p * scale_v per group (rows 4r + g)
+  v4f acc[kAccSets<NCB>][8];  // P.V accumulators
+  float mref[kLaneHeads<NCB>];    // reference (log2 units) of a lane head; p = 2^(z - mref)
+  float mlane[kLaneHeads<NCB>];   // running max of a lane head's unscaled logits
+  float lsum[kLaneHeads<NCB>];    // sum of p over this lane's token positions
+  float zp[kLaneHeads<NCB>][4];   // sum of p * zero_v per group
+  v4f wsum[kLaneHeads<NCB>];      // sums of the bf16 weights W = p * scale_v of each row of a
+                                  // block (against a column of ones)
 };
 
 template <int NCB>
@@ -434,6 +445,13 @@ struct QOperands {
   float qs[NCB][4];             // sum over group g of the encoded q' (254*hi + lo), this lane's head
   float cscale[NCB];            // qsc / 254 * sm_scale * log2(e), > 0
 };
+template <>
+struct QOperands<8> {
+  v4i hi[2], lo[2];             // A operands of the two blocks (groups {0,1} on channel half 0,
+                                // {2,3} on half 1), masked to the row's group
+  float qs[2][4];               // group sums of the encoded q' of the lane's two heads
+  float cscale[2];
+};
 
 // Per-wave LDS tile for the W transpose: [cb][hi/lo][row (j,g)][token of the pair] bf16, page A
 // tokens in columns 0..15, page B in 16..31.  Rows hold 36 entries (72 bytes): the 16-lane
@@ -441,7 +459,7 @@ struct QOperands {
 constexpr int kTileRow = 36;
 template <int NCB>
 struct WTile {
-  uint16_t w[NCB][2][16][kTileRow];
+  uint16_t w[kLaneHeads<NCB>][2][16][kTileRow];   // [block][hi/lo][row][token of the pair]
 };
 
 // A run keeps the first page's max as its reference: later logits may exceed it, and
@@ -459,12 +477,36 @@ constexpr float kVScale[2] = {16.0f, 4.0f};  // code = scale * (bf16 value - 1),
 // on the stale values).
 template <int NCB, bool MASKED>
 __device__ __forceinline__ void page_logits(const PageK& d, bool live, const QOperands<NCB>& qo,
-                                            float a[NCB]) {
+                                            float a[kLaneHeads<NCB>]) {
   const v4i ka0 = (v4i){(int)(d.kc.x & 0x03030303u), (int)((d.kc.x >> 2) & 0x03030303u),
                         (int)((d.kc.x >> 4) & 0x03030303u), (int)((d.kc.x >> 6) & 0x03030303u)};
   const v4i ka1 = (v4i){(int)(d.kc.y & 0x03030303u), (int)((d.kc.y >> 2) & 0x03030303u),
                         (int)((d.kc.y >> 4) & 0x03030303u), (int)((d.kc.y >> 6) & 0x03030303u)};
   const uint32_t kmw[4] = {d.km.x, d.km.y, d.km.z, d.km.w};
+  if constexpr (NCB == 8) {
+    // D element i of a lane: head 2r + i/2, group i%2 (block A) or 2 + i%2 (block B)
+    const v4i zero = {0, 0, 0, 0};
+    const v4i dhA = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0], ka0, zero, 0, 0, 0);
+    const v4i dlA = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0], ka0, zero, 0, 0, 0);
+    const v4i dhB = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[1], ka1, zero, 0, 0, 0);
+    const v4i dlB = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[1], ka1, zero, 0, 0, 0);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float x = 0.f;
+#pragma unroll
+      for (int gl = 0; gl < 2; ++gl) {
+        const int i = 2 * hh + gl;
+        const int dA = __mul24(dhA[i], 254) + dlA[i], dB = __mul24(dhB[i], 254) + dlB[i];
+        x = fmaf(f16lo(kmw[gl]), (float)dA, x);
+        x = fmaf(f16hi(kmw[gl]), qo.qs[hh][gl], x);
+        x = fmaf(f16lo(kmw[2 + gl]), (float)dB, x);
+        x = fmaf(f16hi(kmw[2 + gl]), qo.qs[hh][2 + gl], x);
+      }
+      if (MASKED) x = live ? x : -INFINITY;
+      a[hh] = x;
+    }
+    return;
+  } else {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
@@ -482,6 +524,7 @@ __device__ __forceinline__ void page_logits(const PageK& d, bool live, const QOp
     if (MASKED) x = live ? x : -INFINITY;
     a[cb] = x;
   }
+  }
 }
 
 // Softmax weights of one page and their transpose into the W tile (columns col0 + t):
@@ -489,7 +532,7 @@ __device__ __forceinline__ void page_logits(const PageK& d, bool live, const QOp
 // rounded to nearest even; relative error <= 2^-17, unbiased).  A dead token has p = 0 and its
 // V scale/zero replaced by 0.
 template <int NCB, bool MASKED>
-__device__ __forceinline__ void page_weights(const float a[NCB], uint4 vm, bool live,
+__device__ __forceinline__ void page_weights(const float a[kLaneHeads<NCB>], uint4 vm, bool live,
                                              const QOperands<NCB>& qo, SplitState<NCB>& st,
                                              WTile<NCB>& tile, int t, int r, int col0) {
   uint32_t vmw[4] = {vm.x, vm.y, vm.z, vm.w};
@@ -498,7 +541,7 @@ __device__ __forceinline__ void page_weights(const float a[NCB], uint4 vm, bool 
     for (int g = 0; g < 4; ++g) vmw[g] = live ? vmw[g] : 0u;
   }
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
     const float p = __builtin_amdgcn_exp2f(fmaf(a[cb], qo.cscale[cb], -st.mref[cb]));
     st.lsum[cb] += p;
     float w[4], lo[4];
@@ -510,8 +553,20 @@ __device__ __forceinline__ void page_weights(const float a[NCB], uint4 vm, bool 
       lo[g] = w[g] - __uint_as_float(__float_as_uint(w[g]) & 0xFFFF0000u);
     }
     const uint32_t l01 = pack_bf16(lo[0], lo[1]), l23 = pack_bf16(lo[2], lo[3]);
+    const int col = col0 + t;
+    if constexpr (NCB == 8) {
+      // lane head cb = head 2r + cb: group g -> block g/2, row 2 (2r + cb) + g%2
+      const int row = 4 * r + 2 * cb;
+      const uint16_t lp[4] = {(uint16_t)l01, (uint16_t)(l01 >> 16), (uint16_t)l23, (uint16_t)(l23 >> 16)};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        tile.w[g >> 1][0][row + (g & 1)][col] = (uint16_t)(__float_as_uint(w[g]) >> 16);
+        tile.w[g >> 1][1][row + (g & 1)][col] = lp[g];
+      }
+      continue;
+    }
     // transpose: this lane's (head r, token t, groups 0..3) -> rows 4r + g, column col0 + t
-    const int row = 4 * r, col = col0 + t;
+    const int row = 4 * r;
 #pragma unroll
     for (int g = 0; g < 4; ++g) tile.w[cb][0][row + g][col] = (uint16_t)(__float_as_uint(w[g]) >> 16);
     tile.w[cb][1][row + 0][col] = (uint16_t)l01;
@@ -533,11 +588,11 @@ __device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16
                                           v8bf ones, bool fixed_ref, AfterReads&& after_reads) {
   PageK kA, kB;
   read_pair_k(ps, a8, a16, kA, kB);
-  float aA[NCB], aB[NCB];
+  float aA[kLaneHeads<NCB>], aB[kLaneHeads<NCB>];
   page_logits<NCB, MASKED>(kA, liveA, qo, aA);
   page_logits<NCB, MASKED>(kB, liveB, qo, aB);
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
     st.mlane[cb] = fmaxf(st.mlane[cb], fmaxf(aA[cb], aB[cb]));
     if (FIRST && !fixed_ref) st.mref[cb] = fmaxf(row_max16(aA[cb]) * qo.cscale[cb], kNegBig);
   }
@@ -550,9 +605,9 @@ __device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16
   const uint32_t vsw[4] = {V.vs.x, V.vs.y, V.vs.z, V.vs.w};
   // A operands of every column block: row (j,g) = l % 16 (= t as an index), tokens 8r .. 8r+7
   // of the pair (rows are 8-byte aligned only: two 8-byte reads each)
-  v8bf ahi[NCB], alo[NCB];
+  v8bf ahi[kLaneHeads<NCB>], alo[kLaneHeads<NCB>];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
     const uint2* ph = reinterpret_cast<const uint2*>(&tile.w[cb][0][t][8 * r]);
     const uint2* pl = reinterpret_cast<const uint2*>(&tile.w[cb][1][t][8 * r]);
     const uint2 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
@@ -572,6 +627,14 @@ __device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16
                                                         and_or(y[2], mask_e, magic), and_or(y[3], mask_e, magic)));
     const v8bf vo = __builtin_bit_cast(v8bf, make_uint4(and_or(y[0], mask_o, magic), and_or(y[1], mask_o, magic),
                                                         and_or(y[2], mask_o, magic), and_or(y[3], mask_o, magic)));
+    if constexpr (NCB == 8) {  // one accumulator set; the group's block supplies the rows
+      const int bk = q >> 1;
+      st.acc[0][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[bk], ve, st.acc[0][2 * q], 0, 0, 0);
+      st.acc[0][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[bk], vo, st.acc[0][2 * q + 1], 0, 0, 0);
+      st.acc[0][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[bk], ve, st.acc[0][2 * q], 0, 0, 0);
+      st.acc[0][2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[bk], vo, st.acc[0][2 * q + 1], 0, 0, 0);
+      continue;
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       st.acc[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cb], ve, st.acc[cb][2 * q], 0, 0, 0);
@@ -583,7 +646,7 @@ __device__ __forceinline__ void int2_pair(uint32_t ps, uint32_t a8, uint32_t a16
   // the same weights against a column of ones: the exact bf16 weight sums that the code
   // accumulators carry in their "1 +" part
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
     st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cb], ones, st.wsum[cb], 0, 0, 0);
     st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cb], ones, st.wsum[cb], 0, 0, 0);
   }
@@ -802,7 +865,7 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   const int nwin = ws.batch * g.hkv;
   if (window_first ? bid < nwin : bid >= worker_groups) {
     const int pair = window_first ? bid : bid - worker_groups;
-    window_pair<NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
+    window_pair<NCB == 8 ? 2 : NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
                      pair % g.hkv, smem);
     return;
   }
@@ -879,44 +942,70 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
     const int lo = n_sink, hi = L - min(g.window, L - n_sink);
 
     QOperands<NCB> qo;
+    if constexpr (NCB == 8) {
+      // A-operand row of this lane: head t/2 with group t%2 (block 0, channel words 0..3) or
+      // 2 + t%2 (block 1, words 4..7); quarter r holds word r of the block's half
+      const char* blka = ws.qblock(b, hq, h * G + (t >> 1));
+      const bool use = (r >> 1) == (t & 1);
+      const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      // A-operand row of this lane: head 4*cb + t/4, group t%4
-      const int ja = 4 * cb + (t >> 2), ga = t & 3;
-      const char* blka = ws.qblock(b, hq, h * G + (ja < G ? ja : 0));
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int dw = 4 * m + r;  // 16-channel word of this lane's K quarter
-        const bool use = ja < G && (dw >> 1) == ga;
-        const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * dw);
-        const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * dw);
-        const v4i zero = {0, 0, 0, 0};
-        qo.hi[cb][m] = use ? zh : zero;
-        qo.lo[cb][m] = use ? zl : zero;
+      for (int bk = 0; bk < 2; ++bk) {
+        const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * (4 * bk + r));
+        const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * (4 * bk + r));
+        qo.hi[bk] = use ? zh : zero;
+        qo.lo[bk] = use ? zl : zero;
       }
-      // D rows of this lane: head 4*cb + r
-      const int jd = 4 * cb + r;
-      const char* blkd = ws.qblock(b, hq, h * G + (jd < G ? jd : 0));
-      const float qsc = jd < G ? *reinterpret_cast<const float*>(blkd + kQScOff) : 0.f;
+      // D rows of this lane: heads 2r and 2r + 1
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        qo.qs[cb][gg] = jd < G ? reinterpret_cast<const float*>(blkd + kQSumOff)[gg] : 0.f;
-      // strictly positive so that a masked -inf logit never becomes 0 * inf
-      qo.cscale[cb] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* blkd = ws.qblock(b, hq, h * G + 2 * r + hh);
+        const float qsc = *reinterpret_cast<const float*>(blkd + kQScOff);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) qo.qs[hh][gg] = reinterpret_cast<const float*>(blkd + kQSumOff)[gg];
+        qo.cscale[hh] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
+      }
+    } else {
+  #pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        // A-operand row of this lane: head 4*cb + t/4, group t%4
+        const int ja = 4 * cb + (t >> 2), ga = t & 3;
+        const char* blka = ws.qblock(b, hq, h * G + (ja < G ? ja : 0));
+  #pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int dw = 4 * m + r;  // 16-channel word of this lane's K quarter
+          const bool use = ja < G && (dw >> 1) == ga;
+          const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * dw);
+          const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * dw);
+          const v4i zero = {0, 0, 0, 0};
+          qo.hi[cb][m] = use ? zh : zero;
+          qo.lo[cb][m] = use ? zl : zero;
+        }
+        // D rows of this lane: head 4*cb + r
+        const int jd = 4 * cb + r;
+        const char* blkd = ws.qblock(b, hq, h * G + (jd < G ? jd : 0));
+        const float qsc = jd < G ? *reinterpret_cast<const float*>(blkd + kQScOff) : 0.f;
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          qo.qs[cb][gg] = jd < G ? reinterpret_cast<const float*>(blkd + kQSumOff)[gg] : 0.f;
+        // strictly positive so that a masked -inf logit never becomes 0 * inf
+        qo.cscale[cb] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
+      }
     }
 
     const int32_t* bt = block_table + (size_t)b * g.max_pages;
     const uint8_t* pages_h = pages + (size_t)h * kRecord;  // record of (page 0, head h)
     SplitState<NCB> st;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) st.mref[cb] = kNegBig;
+    for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) st.mref[cb] = kNegBig;
 #pragma nounroll
     for (int pass = 0; pass < 2; ++pass) {
       const bool fixed_ref = pass > 0;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int cs = 0; cs < kAccSets<NCB>; ++cs)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) st.acc[cb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 8; ++nb) st.acc[cs][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
         st.lsum[cb] = 0.f;
         st.mlane[cb] = -INFINITY;
 #pragma unroll
@@ -994,21 +1083,41 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
 
       // A logit beyond the reference margin: recompute once with the exact max (rare path).
       bool redo = false;
-      float mexact[NCB];
+      float mexact[kLaneHeads<NCB>];
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
         mexact[cb] = row_max16(st.mlane[cb]) * qo.cscale[cb];
         redo |= mexact[cb] > st.mref[cb] + kRefMargin;
       }
       if (pass > 0 || !__any(redo)) break;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) st.mref[cb] = mexact[cb];
+      for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) st.mref[cb] = mexact[cb];
     }
 
     // Finish: l and the per-group sums reduced over the row's 16 tokens; the accumulator row
     // of a lane (head 4*cb + r) matches its own row, so no exchange is needed.
     //   o'[c] = sum_t p_t (s_t code_t(c) + z_t) = f (acc - sum_t W_t) + sum_t p_t z_t
     // with f = 16 or 4 for the block's code scale and W_t the bf16 weight pair.
+    if constexpr (NCB == 8) {
+      // lane head hh = head 2r + hh; its row in block g/2 for group g is element 2hh + g%2
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float lt = row_sum16(st.lsum[hh]);
+        float zt[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) zt[gg] = row_sum16(st.zp[hh][gg]);
+        const int j = 2 * r + hh;
+        if ((unsigned)slot < (unsigned)max_splits) {
+          float* o = ws.o(b, hq, h * G + j, slot);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int gg = nb >> 1, i = 2 * hh + (gg & 1);
+            o[16 * nb + t] = fmaf(kVScale[nb & 1], st.acc[0][nb][i] - st.wsum[gg >> 1][i], zt[gg]);
+          }
+          if (t == 0) *ws.ml(b, hq, h * G + j, slot) = make_float2(st.mref[hh], lt);
+        }
+      }
+    } else {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const float lt = row_sum16(st.lsum[cb]);
@@ -1028,6 +1137,7 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
         }
         if (t == 0) *ws.ml(b, hq, h * G + j, slot) = make_float2(st.mref[cb], lt);
       }
+    }
     }
 
     pos = seg_end;
@@ -1075,7 +1185,7 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
   if (batch == 0) return hipSuccess;
   const int G = hq / g.hkv;
   const int workers = num_workers > 0 ? num_workers
-                                      : (G <= 4 ? resident_workers<1>() : resident_workers<2>());
+                                      : (G <= 4 ? resident_workers<1>() : resident_workers<8>());
   // Few pairs: their sink/window workgroups go first, so that they start at once instead of
   // after the INT2 workers that fill the device, and the q rotation takes one workgroup per
   // query head.
@@ -1096,7 +1206,7 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
                        worker_groups, window_first, ws);
   else
-    hipLaunchKernelGGL(int2_decode_kernel<2>, grid, dim3(64 * kWaves), 0, stream, g, pages,
+    hipLaunchKernelGGL(int2_decode_kernel<8>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
                        worker_groups, window_first, ws);
   return hipGetLastError();
