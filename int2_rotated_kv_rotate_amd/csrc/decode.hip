@@ -846,7 +846,7 @@ __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* 
 }
 
 
-// NCB = number of 16-row blocks of (query head, group) pairs = ceil(G / 4).
+// NCB: the row layout (1 for G <= 4, 8 for G = 8; see kLaneHeads).
 // worker_groups workgroups are INT2 workers, kWaves per workgroup.  Persistent part:
 // worker w (one wavefront) takes run w of C pages of the concatenation of all (sequence, KV
 // head) pairs' INT2 pages (the plan in the workspace, built by prep_q_kernel), and writes one
