@@ -1,8 +1,11 @@
-"""GPU parity at the full benchmark workload, in the launch configuration bench.py times.
+"""GPU parity at full workload sizes, in the launch configuration bench.py times.
 
-Qwen3-8B layer shape, batch 64, context lengths uniform in [16384, 32768], sink 4 + window 128
-in BF16, INT2 bulk, one worker wavefront per resident slot (num_workers = 0) and 64 partial
-slots per (sequence, KV head).  Both sides start from pools filled with a 0xA5 sentinel.
+Qwen3-8B layer shape, batch 64, context lengths uniform in [16384, 32768] (the benchmark
+workload, 4 query heads per KV head), and Qwen3-32B layer shape, batch 16, context 32768 (8
+query heads per KV head, the other row layout of the decode kernel); sink 4 + window 128 in
+BF16, INT2 bulk, one worker wavefront per resident slot (num_workers = 0) and 64 partial slots
+per (sequence, KV head).  Both sides start from pools filled with a 0xA5 sentinel; the decode
+workspace starts filled with 0xFF bytes.
 
 The whole batch runs on the GPU; the oracle recomputes sampled (sequence, KV head) pairs one by
 one (the shortest and the longest sequence and one in between, on different KV heads):
@@ -32,9 +35,10 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-@pytest.fixture(scope="module")
-def full_run():
-    w = W.WORKLOADS["qwen3_8b_b64"]
+@pytest.fixture(scope="module", params=["qwen3_8b_b64", "qwen3_32b"])
+def full_run(request):
+    w = W.WORKLOADS[request.param]
+    _log(f"[full] workload {w.name}: batch {w.batch}, {w.num_q_heads}/{w.num_kv_heads} heads")
     p = H.make_problem(w)
     cache = H.GpuCache(p, fill=SENTINEL)
     last_k, last_v = cache.fill_context()
