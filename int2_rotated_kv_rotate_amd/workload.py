@@ -52,6 +52,7 @@ class Workload:
     seed: int
     prefill_new: int = 0          # tokens appended per sequence by the prefill-append step
     needle: bool = False
+    needle_scale: float = 8.0     # the planted key is needle_scale * q / |q| of its query head
     bf16_batches: tuple = ()      # batches of the BF16 paged baseline at equal KV memory
 
     @property
@@ -200,7 +201,7 @@ def sequence_kv(w: Workload, b: int, length: int, *, offsets=None, outliers=None
     if needle is not None and needle[0] == b and needle[1] < length:
         _, p, h, j = needle
         qv = bf16_bits_to_f32(q_bits[b, j]).astype(np.float64)
-        kb[p, h] = to_bf16_bits((8.0 * qv / np.linalg.norm(qv)).astype(np.float32))
+        kb[p, h] = to_bf16_bits((w.needle_scale * qv / np.linalg.norm(qv)).astype(np.float32))
     return kb, vb
 
 

@@ -72,6 +72,11 @@ CASES = {
     "q4b_ragged": (W.WORKLOADS["qwen3_4b"], dict(batch=2, ctx=1500, ctx_min=700), 7, 64),
     "q32b_g8": (W.WORKLOADS["qwen3_32b"], dict(batch=2, ctx=1000), 3, 64),
     "q32b_g8_ragged": (W.WORKLOADS["qwen3_32b"], dict(batch=5, ctx=900, ctx_min=100), 0, 64),
+    # a key of 128 q/|q| mid-sequence: its logit (about 117 nats) exceeds the first page of its
+    # run by more than the decode kernel's reference margin (and by more than fp32's range), so
+    # that run is recomputed against its exact max; 3 workers keep the key away from the start
+    # of a run
+    "spike_recompute": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], needle=True, needle_scale=128.0), dict(batch=2, ctx=1200, ctx_min=900), 3, 64),
     "q8b_more_workers_than_pages": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=5, ctx=900, ctx_min=100), 5000, 64),
     "q8b_few_slots": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=1200, ctx_min=600), 0, 3),
     "q8b_one_slot": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=700, ctx_min=300), 0, 1),
