@@ -33,9 +33,10 @@ def _log(msg):
 def _oracle_cache(p, k_mean=None):
     w = p.w
     oc = O.Cache(p.num_pages, w.num_kv_heads, w.batch, w.num_sink, w.window, fill=SENTINEL, bits=4)
+    needle = W.needle_site(w, p.lens)
     for b in range(w.batch):
         L = int(p.lens[b])
-        kb, vb = W.sequence_kv(w, b, L)
+        kb, vb = W.sequence_kv(w, b, L, needle=needle, q_bits=p.q)
         oc.append(p.table[b], b, 0, kb[:L - 1], vb[:L - 1], p.rot_k, p.rot_v, w.clip, w.clip, k_mean)
         oc.append(p.table[b], b, L - 1, kb[L - 1:], vb[L - 1:], p.rot_k, p.rot_v, w.clip, w.clip,
                   k_mean)
@@ -65,6 +66,9 @@ CASES = {
     "few_splits": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=2, ctx=1200, ctx_min=900), 2),
     "g2_no_sink_window16": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], num_q_heads=16, num_sink=0,
                                                 window=16), dict(batch=2, ctx=800, ctx_min=500), None),
+    # a key of 128 q/|q| mid-sequence: one token lane's running max jumps by ~170 binades
+    "spike": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], needle=True, needle_scale=128.0),
+              dict(batch=2, ctx=1200, ctx_min=900), None),
 }
 
 

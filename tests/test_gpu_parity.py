@@ -77,6 +77,7 @@ CASES = {
     # that run is recomputed against its exact max; 3 workers keep the key away from the start
     # of a run
     "spike_recompute": (dataclasses.replace(W.WORKLOADS["qwen3_4b"], needle=True, needle_scale=128.0), dict(batch=2, ctx=1200, ctx_min=900), 3, 64),
+    "spike_recompute_g8": (dataclasses.replace(W.WORKLOADS["qwen3_32b"], needle=True, needle_scale=128.0), dict(batch=2, ctx=1100, ctx_min=900), 3, 64),
     "q8b_more_workers_than_pages": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=5, ctx=900, ctx_min=100), 5000, 64),
     "q8b_few_slots": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=1200, ctx_min=600), 0, 3),
     "q8b_one_slot": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=3, ctx=700, ctx_min=300), 0, 1),
