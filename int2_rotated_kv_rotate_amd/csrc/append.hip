@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ new_offsets, const int32_t* __restrict__ start_pos,
     const float* __restrict__ rot_k, const float* __restrict__ rot_v,
-    const float* __restrict__ k_mean, float clip_k, float clip_v) {
+    const float* __restrict__ k_mean, float clip_k, float clip_v, int k_groups) {
 #pragma clang fp contract(off)
   __shared__ float s_rot[kHeadDim][kRStride];  // R (fp32), for the A operands and recomputation
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kPTile][kXStride];
@@ -388,7 +388,11 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h = blockIdx.y;
-  const bool is_v = blockIdx.z != 0;
+  // workgroups [0, k_groups) of a KV head serve its K rows, the rest its V rows; x0 is this
+  // workgroup's index among the G of its (head, K|V) pair
+  const bool is_v = (int)blockIdx.x >= k_groups;
+  const int G = is_v ? (int)gridDim.x - k_groups : k_groups;
+  const int x0 = is_v ? (int)blockIdx.x - k_groups : (int)blockIdx.x;
   const float* rot = (is_v ? rot_v : rot_k) + (size_t)h * kHeadDim * kHeadDim;
   const uint16_t* src = is_v ? v_new : k_new;
   const float clip = is_v ? clip_v : clip_k;
@@ -480,21 +484,20 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     }
   };
   uint4 u0, u1;
-  load_rows(blockIdx.x, u0, u1);
+  load_rows(x0, u0, u1);
   int seq = 0;                         // sequence of this thread's row (t < 64)
   RowInfo info_next{-1, 0, -1};
-  if (t < kPTile && blockIdx.x < ntiles && (int)blockIdx.x * kPTile + t < total_new) {
-    seq = row_to_seq(new_offsets, batch, blockIdx.x * kPTile + t);
+  if (t < kPTile && x0 < ntiles && x0 * kPTile + t < total_new) {
+    seq = row_to_seq(new_offsets, batch, x0 * kPTile + t);
     info_next = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store,
-                         blockIdx.x * kPTile + t, h, is_v);
+                         x0 * kPTile + t, h, is_v);
   }
 
   // Round k takes tile k * G + (x + k) mod G (G workgroups per pair, x this one), one tile of
   // each block of G; the rotation spreads tiles that cost more (e.g. the last rows of every
   // sequence, whose BF16 copies are certified too) over all workgroups.  Successive tiles of a
   // workgroup increase, as the placement look-ahead needs.
-  const int G = gridDim.x, x0 = blockIdx.x;
-  auto tile_of = [&](int k) { return k * G + (x0 + k) % G; };   // tile_of(0) == blockIdx.x
+  auto tile_of = [&](int k) { return k * G + (x0 + k) % G; };   // tile_of(0) == x0
   for (int k = 0, tile = x0; tile < ntiles; ++k, tile = tile_of(k)) {
     const int row0 = tile * kPTile;
     const int nrows = min(kPTile, total_new - row0);
@@ -964,12 +967,16 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
         cus <= 0)
       cus = 256;
     // one resident workgroup per CU (R and the tile take most of the LDS) over the 2 * Hkv
-    // (KV head, K|V) pairs
+    // (KV head, K|V) pairs.  Centered keys leave more values uncertain (about 1.8% against
+    // 1.2% recomputed), so with a key mean K gets 19 of every 32 workgroups of a head.
     const int tiles = (total_new + kPTile - 1) / kPTile;
-    const int per_pair = max(1, min(tiles, (cus + 2 * g.hkv - 1) / (2 * g.hkv)));
-    hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_pair, g.hkv, 2), dim3(kPThreads), 0,
+    const int per_head = 2 * max(1, min(tiles, (cus + 2 * g.hkv - 1) / (2 * g.hkv)));
+    const int k_groups = k_mean != nullptr ? max(1, min(per_head - 1, (per_head * 19 + 16) / 32))
+                                           : per_head / 2;
+    hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_head, g.hkv), dim3(kPThreads), 0,
                        stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
-                       v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v);
+                       v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v,
+                       k_groups);
     return hipGetLastError();
   }
   // few rows: 4 per workgroup, so that the launch covers more CUs
