@@ -157,3 +157,14 @@ def test_combine_and_bf16_validation(lib):
     assert lib.oscar_bf16_append(ctypes.byref(lay), None, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.oscar_bf16_decode_attention(ctypes.byref(lay), FAKE, FAKE, 1, 32, FAKE, FAKE, 0.1,
                                            128, 4, FAKE, 10, None) == 3
+
+
+def test_read_records_validation(lib):
+    # n < 0, no workers, null or misaligned pointers: rejected before any launch; n = 0 is a no-op
+    assert lib.oscar_read_records(FAKE, FAKE, -1, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, FAKE, 8, 0, FAKE, None) == 1
+    assert lib.oscar_read_records(None, FAKE, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, None, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, FAKE, 8, 4, None, None) == 1
+    assert lib.oscar_read_records(ctypes.c_void_p(20), FAKE, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(None, None, 0, 4, None, None) == 0
