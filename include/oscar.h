@@ -338,7 +338,8 @@ int32_t oscar_bf16_decode_attention(
  *               (not checked: the kernel reads pool + 1536 * record_ids[i])
  *   record_ids  int32 [n]
  *   out         uint32 [64 * num_workers], written
- * Returns OSCAR_ERR_INVALID_ARGUMENT for n < 0, num_workers < 1 or a null/misaligned pointer.
+ * Returns OSCAR_ERR_INVALID_ARGUMENT for n < 0, num_workers outside [1, 1048576] or a
+ * null/misaligned pointer.
  */
 int32_t oscar_read_records(const uint8_t* pool, const int32_t* record_ids, int32_t n,
                            int32_t num_workers, uint32_t* out, void* stream);

@@ -283,7 +283,7 @@ int32_t oscar_bf16_decode_attention(
 
 int32_t oscar_read_records(const uint8_t* pool, const int32_t* record_ids, int32_t n,
                            int32_t num_workers, uint32_t* out, void* stream) {
-  if (n < 0 || num_workers < 1) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (n < 0 || num_workers < 1 || num_workers > kMaxWorkers) return OSCAR_ERR_INVALID_ARGUMENT;
   if (n == 0) return OSCAR_OK;
   if (!pool || !record_ids || !out || !aligned16(pool)) return OSCAR_ERR_INVALID_ARGUMENT;
   return hip_status(launch_read_records(pool, record_ids, n, num_workers, out,

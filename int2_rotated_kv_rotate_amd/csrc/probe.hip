@@ -41,7 +41,7 @@ __global__ __launch_bounds__(64 * kProbeWaves) void read_records_kernel(
 
 hipError_t launch_read_records(const uint8_t* pool, const int32_t* record_ids, int n, int workers,
                                uint32_t* out, hipStream_t stream) {
-  const int C = ((n + workers - 1) / workers + 1) & ~1;
+  const int C = (int)((((long long)n + workers - 1) / workers + 1) & ~1LL);
   const dim3 grid((workers + kProbeWaves - 1) / kProbeWaves);
   hipLaunchKernelGGL(read_records_kernel, grid, dim3(64 * kProbeWaves), 0, stream, pool,
                      record_ids, n, C, workers, out);

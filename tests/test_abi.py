@@ -163,6 +163,7 @@ def test_read_records_validation(lib):
     # n < 0, no workers, null or misaligned pointers: rejected before any launch; n = 0 is a no-op
     assert lib.oscar_read_records(FAKE, FAKE, -1, 4, FAKE, None) == 1
     assert lib.oscar_read_records(FAKE, FAKE, 8, 0, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, FAKE, 8, (1 << 20) + 1, FAKE, None) == 1
     assert lib.oscar_read_records(None, FAKE, 8, 4, FAKE, None) == 1
     assert lib.oscar_read_records(FAKE, None, 8, 4, FAKE, None) == 1
     assert lib.oscar_read_records(FAKE, FAKE, 8, 4, None, None) == 1
