@@ -24,7 +24,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   const int ns = ws.nslots;
   const int jq = h * G + j;
   extern __shared__ float s_w[];        // [2][G][ns]: merge weights 2^(m - M) (0 for empty), l
-  __shared__ float s_o[8][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_o[8][kHeadDim];
   __shared__ float s_red[8][4];         // per head: max, then l, of each of its two waves
   __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
 
@@ -121,10 +121,11 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
 #pragma unroll 8
   for (int k4 = 0; k4 < kHeadDim / 4; ++k4) {
     const float4 r = s_r[c][k4];
-    acc2 = fmaf(s_o[j][4 * k4 + 0], r.x, acc2);
-    acc2 = fmaf(s_o[j][4 * k4 + 1], r.y, acc2);
-    acc2 = fmaf(s_o[j][4 * k4 + 2], r.z, acc2);
-    acc2 = fmaf(s_o[j][4 * k4 + 3], r.w, acc2);
+    const float4 ov = *reinterpret_cast<const float4*>(&s_o[j][4 * k4]);
+    acc2 = fmaf(ov.x, r.x, acc2);
+    acc2 = fmaf(ov.y, r.y, acc2);
+    acc2 = fmaf(ov.z, r.z, acc2);
+    acc2 = fmaf(ov.w, r.w, acc2);
   }
   orow[c] = acc2;
 }
