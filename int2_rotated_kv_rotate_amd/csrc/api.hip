@@ -45,6 +45,10 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? OSCAR_OK : OSCAR_ERR
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A softmax scale must be finite and positive: the INT2 workers fold it into a strictly
+// positive logit scale, while the BF16 sink/window logits use it as given.
+bool valid_scale(float s) { return s > 0.f && s <= 3.402823466e38f; }
+
 }  // namespace
 
 extern "C" {
@@ -166,7 +170,7 @@ int32_t oscar_int4_decode_attention(
   if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
-  if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0) return OSCAR_OK;
   if (!pages || !block_table || !q || !seq_lens || !rot_k || !workspace)
     return OSCAR_ERR_INVALID_ARGUMENT;
@@ -206,7 +210,7 @@ int32_t oscar_decode_attention(
   if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
-  if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0) return OSCAR_OK;
   if (!pages || !block_table || !q || !seq_lens || !rot_k || !workspace)
     return OSCAR_ERR_INVALID_ARGUMENT;
@@ -270,7 +274,7 @@ int32_t oscar_bf16_decode_attention(
   if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
-  if (!(sm_scale == sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0) return OSCAR_OK;
   if (!pages || !block_table || !q || !seq_lens || !workspace) return OSCAR_ERR_INVALID_ARGUMENT;
   if (!aligned16(pages) || !aligned16(q) || !aligned16(workspace)) return OSCAR_ERR_INVALID_ARGUMENT;
@@ -281,12 +285,21 @@ int32_t oscar_bf16_decode_attention(
                                        seq_lens, sm_scale, split_pages, ws, (hipStream_t)stream));
 }
 
-int32_t oscar_read_records(const uint8_t* pool, const int32_t* record_ids, int32_t n,
-                           int32_t num_workers, uint32_t* out, void* stream) {
-  if (n < 0 || num_workers < 1 || num_workers > kMaxWorkers) return OSCAR_ERR_INVALID_ARGUMENT;
+int32_t oscar_mfma_bf16_tiles(const uint16_t* a, const uint16_t* b, const float* c, float* d,
+                              int32_t tiles, void* stream) {
+  if (tiles < 0 || tiles > (1 << 20)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (tiles == 0) return OSCAR_OK;
+  if (!a || !b || !c || !d) return OSCAR_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_mfma_bf16_tiles(a, b, c, d, tiles, (hipStream_t)stream));
+}
+
+int32_t oscar_read_records(const uint8_t* pool, int32_t num_records, const int32_t* record_ids,
+                           int32_t n, int32_t num_workers, uint32_t* out, void* stream) {
+  if (n < 0 || num_records < 1 || num_workers < 1 || num_workers > kMaxWorkers)
+    return OSCAR_ERR_INVALID_ARGUMENT;
   if (n == 0) return OSCAR_OK;
   if (!pool || !record_ids || !out || !aligned16(pool)) return OSCAR_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_read_records(pool, record_ids, n, num_workers, out,
+  return hip_status(launch_read_records(pool, num_records, record_ids, n, num_workers, out,
                                         (hipStream_t)stream));
 }
 

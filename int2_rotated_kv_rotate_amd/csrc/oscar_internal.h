@@ -129,9 +129,13 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream);
 
+// One bf16 matrix-core instruction per tile (D = A . B + C): see oscar_mfma_bf16_tiles.
+hipError_t launch_mfma_bf16_tiles(const uint16_t* a, const uint16_t* b, const float* c, float* d,
+                                  int tiles, hipStream_t stream);
+
 // Read-bandwidth probe over INT2 records (no arithmetic): see oscar_read_records.
-hipError_t launch_read_records(const uint8_t* pool, const int32_t* record_ids, int n, int workers,
-                               uint32_t* out, hipStream_t stream);
+hipError_t launch_read_records(const uint8_t* pool, int num_records, const int32_t* record_ids,
+                               int n, int workers, uint32_t* out, hipStream_t stream);
 
 hipError_t launch_bf16_append(const CacheGeom& g, uint16_t* pages, const int32_t* block_table,
                               int batch, int total_new, const uint16_t* k_new,

@@ -33,6 +33,7 @@ EXPORTED = (
     "oscar_bf16_append",
     "oscar_bf16_decode_attention",
     "oscar_read_records",
+    "oscar_mfma_bf16_tiles",
 )
 
 
@@ -102,7 +103,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_bf16_append.restype = I32
     lib.oscar_bf16_decode_attention.argtypes = [LP, P, P, I32, I32, P, P, F32, I32, I32, P, SZ, P]
     lib.oscar_bf16_decode_attention.restype = I32
-    lib.oscar_read_records.argtypes = [P, P, I32, I32, P, P]
+    lib.oscar_read_records.argtypes = [P, I32, P, I32, I32, P, P]
+    lib.oscar_mfma_bf16_tiles.argtypes = [P, P, P, P, I32, P]
+    lib.oscar_mfma_bf16_tiles.restype = I32
     lib.oscar_read_records.restype = I32
     _lib = lib
     return lib
@@ -260,5 +263,19 @@ def read_records(pages, record_ids, num_workers: int, out, stream=None) -> None:
     if out.numel() < 64 * num_workers:
         raise ValueError("out: needs 64 * num_workers entries")
     _check("oscar_read_records", lib.oscar_read_records(
-        _ptr(pages, torch.uint8, "pages"), _ptr(record_ids, torch.int32, "record_ids"),
+        _ptr(pages, torch.uint8, "pages"), pages.numel() // RECORD_BYTES,
+        _ptr(record_ids, torch.int32, "record_ids"),
         record_ids.numel(), num_workers, _ptr(out, torch.int32, "out"), _stream(stream)))
+
+
+def mfma_bf16_tiles(a, b, c, d, stream=None) -> None:
+    """D = A . B + C per 16x16x32 tile with one bf16 matrix-core instruction: a int16 (bf16 bits)
+    [tiles][16][32], b [tiles][32][16], c and d float32 [tiles][16][16]."""
+    lib = load_library()
+    tiles = a.shape[0]
+    if a.shape != (tiles, 16, 32) or b.shape != (tiles, 32, 16) or c.shape != (tiles, 16, 16) \
+            or d.shape != (tiles, 16, 16):
+        raise ValueError("mfma_bf16_tiles: shapes [T][16][32], [T][32][16], [T][16][16] x 2")
+    _check("oscar_mfma_bf16_tiles", lib.oscar_mfma_bf16_tiles(
+        _ptr(a, torch.int16, "a"), _ptr(b, torch.int16, "b"), _ptr(c, torch.float32, "c"),
+        _ptr(d, torch.float32, "d"), tiles, _stream(stream)))

@@ -141,7 +141,8 @@ def test_decode_validation(lib):
     assert _decode(lib, _layout(), nw=(1 << 20) + 1) == 1
     assert _decode(lib, _layout(max_pages_per_seq=1 << 20), batch=1 << 10) == 2  # plan > int32
     assert _decode(lib, _layout(), ms=0) == 1
-    assert _decode(lib, _layout(), sm=float("nan")) == 1
+    for bad in (float("nan"), float("inf"), -float("inf"), 0.0, -0.0, -0.088):
+        assert _decode(lib, _layout(), sm=bad) == 1     # the scale must be finite and > 0
     assert _decode(lib, _layout(), wsb=100) == 3
     assert _decode(lib, _layout(), q=None) == 1
     assert _decode(lib, _layout(head_dim=256)) == 2
@@ -157,15 +158,24 @@ def test_combine_and_bf16_validation(lib):
     assert lib.oscar_bf16_append(ctypes.byref(lay), None, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.oscar_bf16_decode_attention(ctypes.byref(lay), FAKE, FAKE, 1, 32, FAKE, FAKE, 0.1,
                                            128, 4, FAKE, 10, None) == 3
+    for bad in (float("nan"), float("inf"), 0.0, -1.0):
+        assert lib.oscar_bf16_decode_attention(ctypes.byref(lay), FAKE, FAKE, 1, 32, FAKE, FAKE,
+                                               bad, 128, 4, FAKE, 1 << 30, None) == 1
+        assert lib.oscar_int4_decode_attention(ctypes.byref(lay), FAKE, FAKE, FAKE, None, 1, 32,
+                                               FAKE, FAKE, FAKE, bad, 16, 4, FAKE, 1 << 30,
+                                               None) == 1
 
 
 def test_read_records_validation(lib):
-    # n < 0, no workers, null or misaligned pointers: rejected before any launch; n = 0 is a no-op
-    assert lib.oscar_read_records(FAKE, FAKE, -1, 4, FAKE, None) == 1
-    assert lib.oscar_read_records(FAKE, FAKE, 8, 0, FAKE, None) == 1
-    assert lib.oscar_read_records(FAKE, FAKE, 8, (1 << 20) + 1, FAKE, None) == 1
-    assert lib.oscar_read_records(None, FAKE, 8, 4, FAKE, None) == 1
-    assert lib.oscar_read_records(FAKE, None, 8, 4, FAKE, None) == 1
-    assert lib.oscar_read_records(FAKE, FAKE, 8, 4, None, None) == 1
-    assert lib.oscar_read_records(ctypes.c_void_p(20), FAKE, 8, 4, FAKE, None) == 1
-    assert lib.oscar_read_records(None, None, 0, 4, None, None) == 0
+    # n < 0, an empty pool, no workers, null or misaligned pointers: rejected before any
+    # launch; n = 0 is a no-op
+    assert lib.oscar_read_records(FAKE, 8, FAKE, -1, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, 0, FAKE, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, 8, FAKE, 8, 0, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, 8, FAKE, 8, (1 << 20) + 1, FAKE, None) == 1
+    assert lib.oscar_read_records(None, 8, FAKE, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, 8, None, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(FAKE, 8, FAKE, 8, 4, None, None) == 1
+    assert lib.oscar_read_records(ctypes.c_void_p(20), 8, FAKE, 8, 4, FAKE, None) == 1
+    assert lib.oscar_read_records(None, 8, None, 0, 4, None, None) == 0
+

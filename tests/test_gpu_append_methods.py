@@ -18,8 +18,9 @@ Cases:
   * keys with a mean removed before the rotation (workload means, a large random mean, zero,
     and the special rows with a mean);
   * the Hadamard-rotation append (its own kernel) against the oracle;
-  * the full prefill shape: 64 sequences x 2048 new tokens at the end of 16K-32K contexts
-    (GPU against GPU: 2.1 million rows are beyond the oracle's seconds).
+  * the full prefill shape: 64 sequences x 2048 new tokens at the end of 16K-32K contexts,
+    the two kernels against each other over all 2.1 million rows, and sampled (sequence, KV
+    head) pairs against the oracle (their rows copied to the host).
 """
 import sys
 
@@ -316,3 +317,21 @@ def test_full_prefill_shape():
     b = 0
     last_page = int(p.table[b, (int(p.lens[b]) - 1) // 16])
     assert not bool((pm[last_page, 0, :1024] == SENTINEL).all().item())
+    # sampled (sequence, KV head) pairs against the oracle: the pair's 2048 rows appended at
+    # the same positions into a sentinel-filled one-head oracle cache; every record its pages
+    # hold and its sink/window rows must be byte-identical
+    offs_h = offs.cpu().numpy()
+    for b, h in ((0, 1), (37, 6), (63, 0)):
+        L = int(p.lens[b])
+        kb = k16[offs_h[b]:offs_h[b + 1], h:h + 1].cpu().numpy().view(np.uint16)
+        vb = v16[offs_h[b]:offs_h[b + 1], h:h + 1].cpu().numpy().view(np.uint16)
+        oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window, fill=SENTINEL)
+        oc.append(p.table[b], b, L - n_new, kb, vb, p.rot_k[h:h + 1], p.rot_v[h:h + 1],
+                  w.clip, w.clip)
+        pg = p.table[b, (L - n_new) // 16:(L + 15) // 16]
+        gpu_rec = pm[torch.from_numpy(pg.astype(np.int64)).cuda(), h].cpu().numpy()
+        nd_o = int((gpu_rec != oc.pages[pg, 0]).sum())
+        _log(f"[append] full prefill, sequence {b} KV head {h}: {len(pg)} records, "
+             f"{nd_o} bytes differ from the oracle")
+        assert nd_o == 0
+        assert np.array_equal(sm[b, h].cpu().numpy().view(np.uint16), oc.sinkwin[b, 0])

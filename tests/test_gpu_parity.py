@@ -66,6 +66,16 @@ def row_errors(gpu, ref):
     return err / scale
 
 
+def elem_errors(gpu, ref, floor=0.25):
+    """Elementwise relative error with a floor: |gpu - ref| / max(|ref|, floor * max_row |ref|).
+    For outputs of at least a quarter of their row's largest magnitude this is the plain
+    relative error; below that (where relative error is unbounded near zero) it falls back to a
+    quarter of the row scale."""
+    ref = np.asarray(ref, np.float64)
+    row = np.abs(ref).max(axis=-1, keepdims=True)
+    return np.abs(gpu.astype(np.float64) - ref) / np.maximum(np.abs(ref), floor * row)
+
+
 CASES = {
     # name: (workload, overrides, num_workers (0 = one per resident slot), max_splits)
     "tiny": (W.WORKLOADS["tiny"], {}, 0, 64),
@@ -118,10 +128,12 @@ def test_append_and_decode_parity(name):
     out = step.out.cpu().numpy()
     lse = step.lse.cpu().numpy()
     rel = row_errors(out, ref)
-    _log(f"[parity] {name}: max row rel err {rel.max():.3e}, max |dlse| "
-         f"{np.abs(lse - ref_lse).max():.3e}")
+    el = elem_errors(out, ref)
+    _log(f"[parity] {name}: max row rel err {rel.max():.3e}, max elementwise {el.max():.3e}, "
+         f"max |dlse| {np.abs(lse - ref_lse).max():.3e}")
     assert np.all(np.isfinite(out))
     assert rel.max() <= TOL
+    assert el.max() <= TOL
     assert np.abs(lse - ref_lse).max() <= TOL
 
 
@@ -144,6 +156,7 @@ def test_key_mean_decode():
     _log(f"[parity] key mean: max row rel err {rel.max():.3e}, "
          f"max |dlse| {np.abs(lse - ref_lse).max():.3e}")
     assert rel.max() <= TOL
+    assert elem_errors(out, ref).max() <= TOL
     assert np.abs(lse - ref_lse).max() <= TOL
     # against the exact attention over the unquantised, unrotated keys and values
     _, plain = run_gpu(p, 0, H.DEFAULT_MAX_SPLITS)
@@ -183,6 +196,7 @@ def test_hadamard_decode():
     _log(f"[parity] hadamard: max row rel err {rel.max():.3e}, "
          f"max |dlse| {np.abs(lse - ref_lse).max():.3e}")
     assert rel.max() <= TOL
+    assert elem_errors(out, ref).max() <= TOL
     assert np.abs(lse - ref_lse).max() <= TOL
 
 
@@ -323,4 +337,5 @@ def test_bf16_baseline_parity(name, over, split_pages):
     rel = row_errors(out.cpu().numpy(), ref)
     _log(f"[parity] {name}: max row rel err {rel.max():.3e}")
     assert rel.max() <= TOL
+    assert elem_errors(out.cpu().numpy(), ref).max() <= TOL
     assert np.abs(lse.cpu().numpy() - ref_lse).max() <= TOL
