@@ -329,6 +329,33 @@ int32_t oscar_bf16_decode_attention(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention and combine in one call with no allocation anywhere: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It computes exactly what oscar_decode_attention followed by oscar_combine
+ * compute (same kernels, same work plan for the same num_workers and max_splits, so the same
+ * bits), with the decode workspace in a buffer that the library holds in device memory on each
+ * GPU it runs on, OSCAR_STATIC_WORKSPACE_BYTES in size, for the life of the process.
+ *   Arguments as for oscar_decode_attention and oscar_combine (rot_v, out, lse); there is no
+ *   workspace argument.
+ * Returns OSCAR_ERR_WORKSPACE_TOO_SMALL when oscar_decode_workspace_bytes(batch, num_q_heads,
+ * max_splits) exceeds OSCAR_STATIC_WORKSPACE_BYTES (a smaller max_splits lengthens the worker
+ * runs and needs less), and OSCAR_ERR_HIP if the buffer's device address cannot be looked up;
+ * nothing is launched in either case.  The buffer's address is looked up once per device, on
+ * the first call with that device current.  The buffer keeps the last call's contents, and the
+ * kernels read nothing in it that the same call has not written.  All calls on one GPU share
+ * its buffer: calls whose executions overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give undefined results.
+ */
+#define OSCAR_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+int32_t oscar_decode_attention_static(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k, const float* rot_v,
+    float sm_scale, int32_t num_workers, int32_t max_splits,
+    float* out, float* lse, void* stream);
+
+/*
  * Accumulation check of the matrix-core instruction (not part of the method): for each of
  * `tiles` independent tiles, one v_mfma_f32_16x16x32_bf16 computes D = A . B + C.  The
  * matrix-core prefill append (oscar_rotate_quantize_append from 256 rows on) certifies its

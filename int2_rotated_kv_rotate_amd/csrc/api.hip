@@ -1,5 +1,7 @@
 // C ABI entry points: validate host-visible arguments, then enqueue the kernels on the caller's
 // stream.  No allocation, no synchronisation, no state.
+#include <mutex>
+
 #include "../../include/oscar.h"
 #include "oscar_internal.h"
 
@@ -48,6 +50,35 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // A softmax scale must be finite and positive: the INT2 workers fold it into a strictly
 // positive logit scale, while the BF16 sink/window logits use it as given.
 bool valid_scale(float s) { return s > 0.f && s <= 3.402823466e38f; }
+
+// Decode workspace for oscar_decode_attention_static: one copy per GPU, in device memory for
+// the life of the process.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol): it looks up the device address of this device's copy
+// once and uses that address everywhere.
+constexpr size_t kStaticWorkspaceBytes = OSCAR_STATIC_WORKSPACE_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, set once
+
+// Device address of the current device's `scratch` (looked up on the first call per device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -224,6 +255,44 @@ int32_t oscar_decode_attention(
   return hip_status(launch_decode(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
                                   num_q_heads, q, seq_lens, rot_k, sm_scale, num_workers, ws,
                                   (hipStream_t)stream));
+}
+
+int32_t oscar_decode_attention_static(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k, const float* rot_v,
+    float sm_scale, int32_t num_workers, int32_t max_splits,
+    float* out, float* lse, void* stream) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || num_workers < 0 || num_workers > kMaxWorkers || max_splits < 1 ||
+      max_splits > 65535)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if ((long long)batch * lay->num_kv_heads * lay->max_pages_per_seq > 0x7FFFFFFFLL)
+    return OSCAR_ERR_UNSUPPORTED;
+  st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
+  if (st != OSCAR_OK) return st;
+  if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return OSCAR_OK;
+  if (!pages || !block_table || !q || !seq_lens || !rot_k || !out)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(q) || !aligned16(rot_k) || (rot_v && !aligned16(rot_v)) ||
+      (sinkwin && !aligned16(sinkwin)))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes(batch, num_q_heads, max_splits) > kStaticWorkspaceBytes)
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  void* base = nullptr;
+  if (scratch_address(&base) != hipSuccess) return OSCAR_ERR_HIP;
+  Workspace ws = make_workspace(base, batch, num_q_heads, max_splits);
+  const hipStream_t s = (hipStream_t)stream;
+  st = hip_status(launch_decode(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                num_q_heads, q, seq_lens, rot_k, sm_scale, num_workers, ws, s));
+  if (st != OSCAR_OK) return st;
+  return hip_status(launch_combine(batch, num_q_heads, lay->num_kv_heads, ws, rot_v, out, lse, s));
 }
 
 int32_t oscar_combine(

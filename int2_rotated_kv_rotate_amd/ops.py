@@ -34,7 +34,10 @@ EXPORTED = (
     "oscar_bf16_decode_attention",
     "oscar_read_records",
     "oscar_mfma_bf16_tiles",
+    "oscar_decode_attention_static",
 )
+
+STATIC_WORKSPACE_BYTES = 32 << 20   # OSCAR_STATIC_WORKSPACE_BYTES
 
 
 class OscarError(RuntimeError):
@@ -103,6 +106,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_bf16_append.restype = I32
     lib.oscar_bf16_decode_attention.argtypes = [LP, P, P, I32, I32, P, P, F32, I32, I32, P, SZ, P]
     lib.oscar_bf16_decode_attention.restype = I32
+    lib.oscar_decode_attention_static.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, F32, I32,
+                                                  I32, P, P, P]
+    lib.oscar_decode_attention_static.restype = I32
     lib.oscar_read_records.argtypes = [P, I32, P, I32, I32, P, P]
     lib.oscar_mfma_bf16_tiles.argtypes = [P, P, P, P, I32, P]
     lib.oscar_mfma_bf16_tiles.restype = I32
@@ -222,6 +228,21 @@ def decode_attention(lay: Layout, pages, sinkwin, block_table, slot_ids, q, seq_
         batch, hq, _ptr(q, torch.int16, "q"), _ptr(seq_lens, torch.int32, "seq_lens"),
         _ptr(rot_k, torch.float32, "rot_k"), float(sm_scale), num_workers, max_splits,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def decode_attention_static(lay: Layout, pages, sinkwin, block_table, slot_ids, q, seq_lens,
+                            rot_k, rot_v, sm_scale: float, num_workers: int, max_splits: int,
+                            out, lse=None, stream=None) -> None:
+    """Decode attention + combine with the library's own workspace (no allocation)."""
+    lib = load_library()
+    batch, hq = q.shape[0], q.shape[1]
+    _check("oscar_decode_attention_static", lib.oscar_decode_attention_static(
+        ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
+        batch, hq, _ptr(q, torch.int16, "q"), _ptr(seq_lens, torch.int32, "seq_lens"),
+        _ptr(rot_k, torch.float32, "rot_k"), _ptr(rot_v, torch.float32, "rot_v"),
+        float(sm_scale), num_workers, max_splits, _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)))
 
 
 def combine(batch: int, num_q_heads: int, num_kv_heads: int, max_splits: int, workspace,

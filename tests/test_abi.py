@@ -179,3 +179,23 @@ def test_read_records_validation(lib):
     assert lib.oscar_read_records(ctypes.c_void_p(20), 8, FAKE, 8, 4, FAKE, None) == 1
     assert lib.oscar_read_records(None, 8, None, 0, 4, None, None) == 0
 
+
+def test_decode_static_validation(lib):
+    lay = _layout()
+
+    def call(**kw):
+        a = dict(pages=FAKE, batch=1, hq=32, out=FAKE, sm=0.088, ms=4, rv=FAKE)
+        a.update(kw)
+        return lib.oscar_decode_attention_static(
+            ctypes.byref(lay), a["pages"], FAKE, FAKE, None, a["batch"], a["hq"], FAKE, FAKE,
+            FAKE, a["rv"], a["sm"], 0, a["ms"], a["out"], None, None)
+
+    assert call(out=None) == 1
+    assert call(pages=None) == 1
+    assert call(hq=24) == 2
+    assert call(sm=float("inf")) == 1
+    assert call(ms=0) == 1
+    assert call(rv=ctypes.c_void_p(20)) == 1     # misaligned R_V
+    # 64 sequences x 32 query heads x 65 slots need ~71 MB: more than the library's buffer
+    assert call(batch=64, ms=64) == 3
+    assert call(batch=0) == 0
