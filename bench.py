@@ -8,7 +8,16 @@ BF16, INT2 bulk, 16-token pages, all inputs synthetic and already resident in HB
 
 Prints ONE JSON line.  Extra fields: effective GB/s of the step, the decode-attention roofline
 (bytes from the method's byte model / the launch's HIP-event duration), the prefill append of
-2048 tokens per sequence, and the CPU oracle timed on a bounded sample of the same workload.
+2048 tokens per sequence, and the CPU oracle timed on a bounded sample of the same workload,
+whose outputs are also compared with the GPU's for one (sequence, KV head) pair of every timed
+INT2 workload.
+
+Order of a run: cache fill; 20 decode steps after 1 s of idle (the cold-start figures: the
+power management cuts the shader clock for the first ~10 ms of load); a step with a cache
+scrub, a device copy and max(50, K) single steps with their own events (the spread: median,
+p10, p90), which keep the load on; then, without an idle gap, the W warm-up steps and the K timed steps (the headline:
+back-to-back decode steps as a serving loop runs them); the record-read probe; the prefill
+timings; the INT2/BF16 comparisons; the CPU leg.
 """
 from __future__ import annotations
 
@@ -119,7 +128,14 @@ def cpu_baseline(p, target_s: float):
                                             p.rot_k[h:h + 1], p.rot_v[h:h + 1], sm)
                 per_step.append(time.perf_counter() - t0)
     t_head = float(np.mean(per_step))
+    # bytes of one single-head decode step of this sequence by the method's byte model: its
+    # INT2 records and BF16 sink/window rows, the G query rows and outputs, its table row
+    n_sink = min(L, w.num_sink)
+    n_win = min(w.window, L - n_sink)
+    head_bytes = (INT2_TOKEN_HEAD_BYTES * (L - n_sink - n_win) + BF16_TOKEN_HEAD_BYTES *
+                  (n_sink + n_win) + G * 128 * (2 + 4) + 4 * ((L + 15) // 16))
     return ref, {"value": 1.0 / (t_head * w.num_kv_heads), "unit": "tokens/s", "cores": 1,
+            "effective_gbps": round(head_bytes / t_head / 1e9, 4),
             "kind": "oracle",
             "sample": (f"sequence 0 (L={L}), KV heads {heads} x {G} query heads: "
                        f"{len(per_step)} timed single-head decode steps (append of the new "
@@ -127,6 +143,40 @@ def cpu_baseline(p, target_s: float):
                        f"all {w.num_kv_heads} KV heads of one decode step; one BLAS thread"),
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "blas_threads": 1}
+
+
+def oracle_pair(p, b: int, h: int):
+    """The CPU oracle's decode of one (sequence, KV head) pair of a problem: its cache built by
+    the same appends as the GPU run (the context, then the decoded token) and decode attention
+    for the pair's query heads.  Returns (out [G][128], lse [G])."""
+    from oracle import oscar_oracle as O
+    from int2_rotated_kv_rotate_amd import harness as H
+    from int2_rotated_kv_rotate_amd import workload as W
+    w = p.w
+    L = int(p.lens[b])
+    G = w.group
+    kb, vb = W.sequence_kv(w, b, L, offsets=W.key_offsets(w), outliers=W.outlier_channels(w),
+                           needle=W.needle_site(w, p.lens), q_bits=p.q)
+    oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window)
+    args = (p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
+    oc.append(p.table[b], b, 0, kb[:L - 1, h:h + 1], vb[:L - 1, h:h + 1], *args)
+    oc.append(p.table[b], b, L - 1, kb[L - 1:, h:h + 1], vb[L - 1:, h:h + 1], *args)
+    ref, ref_lse = O.decode_attention(oc, p.table[b:b + 1], np.array([b]), p.lens[b:b + 1],
+                                      p.q[b:b + 1, h * G:(h + 1) * G], p.rot_k[h:h + 1],
+                                      p.rot_v[h:h + 1], H.SM_SCALE)
+    return ref[0], ref_lse[0]
+
+
+def parity_record(out, lse, ref, ref_lse, **extra):
+    """Per-row normwise error, elementwise error (floor: a quarter of the row's largest |ref|)
+    and |dlse| of GPU rows against the oracle's, with the 2e-3 tolerance."""
+    out = np.asarray(out, np.float64)
+    row = float((np.abs(out - ref).max(-1) / np.abs(ref).max(-1)).max())
+    el = float((np.abs(out - ref) / np.maximum(np.abs(ref),
+                                               0.25 * np.abs(ref).max(-1, keepdims=True))).max())
+    dl = float(np.abs(np.asarray(lse, np.float64) - ref_lse).max())
+    return dict(extra, max_row_rel_err=row, max_elementwise_rel_err=el, max_abs_dlse=dl,
+                tolerance=2e-3, ok=bool(row <= 2e-3 and el <= 2e-3 and dl <= 2e-3))
 
 
 def time_scrubbed(fn, n: int, scrub):
@@ -149,7 +199,7 @@ def time_scrubbed(fn, n: int, scrub):
     return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
 
-def record_read_probe(w, p, cache, stream, attn_ms: float):
+def record_read_probe(w, p, cache, stream):
     """The practical HBM ceiling of the decode launch's INT2 stream: the same records (every
     INT2 page of every (sequence, KV head) pair, in the decode kernel's order) read by
     oscar_read_records with the same number of wavefronts and none of the arithmetic."""
@@ -189,14 +239,16 @@ def record_read_probe(w, p, cache, stream, attn_ms: float):
                     "two 1536-byte records per step per wavefront, no arithmetic"}
 
 
-def int2_vs_bf16(n_iter: int):
+def int2_vs_bf16(n_iter: int, samples: dict):
     """Attention (decode launch + combine) of the INT2 path against the BF16 paged baseline of
     the same library, with a 1 GiB cache scrub before every timed launch:
       * Qwen3-32B layer shape, context 32768: INT2 at batch 16 vs BF16 at batch 2 (about 1/8
         of the batch) and batch 3 (the equal-memory batch for 3 bits per element);
       * Qwen3-4B layer shape, batch 1, context 32768: latency of each;
       * long-context layer (32 query / 8 KV heads), batch 1, context 131072: latency of each;
-      * the INT4 variant at the Qwen3-8B batch-64 shape."""
+      * the INT4 variant at the Qwen3-8B batch-64 shape.
+    samples receives, per INT2 workload, the GPU outputs of one (sequence, KV head) pair for the
+    oracle comparison of the CPU-baseline leg."""
     import torch
     from int2_rotated_kv_rotate_amd import harness as H
     from int2_rotated_kv_rotate_amd import workload as W
@@ -227,6 +279,13 @@ def int2_vs_bf16(n_iter: int):
         torch.cuda.synchronize()
         ms = time_scrubbed(step.attend, n_iter, scrub)
         pool = p.num_pages * w.num_kv_heads * 1536
+        # the outputs of one (sequence, KV head) pair, kept for the oracle comparison: the
+        # longest sequence, the last KV head
+        b = int(np.argmax(p.lens))
+        h = w.num_kv_heads - 1
+        G = w.group
+        samples[w.name] = (p, b, h, step.out[b, h * G:(h + 1) * G].cpu().numpy(),
+                           step.lse[b, h * G:(h + 1) * G].cpu().numpy())
         del step, cache
         return p, ms, pool
 
@@ -306,9 +365,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # after an idle gap the shader clock ramps up over the first ~100 back-to-back steps
-    # (~0.32 ms per step at first, ~0.26 ms once it has settled): warm up past the ramp
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_b64")
     ap.add_argument("--workers", type=int, default=0,
                     help="INT2 worker wavefronts (0: one per resident slot of the device)")
@@ -380,6 +437,67 @@ def main():
     step.set_new_token(last_k, last_v)
     stream = torch.cuda.current_stream()
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # Cold start, for the record: after 1 s of idle the power management cuts the shader clock
+    # for the first ~10 ms of load (measured with s_memtime against s_memrealtime: 2.4 GHz
+    # idle, 1.3-1.6 GHz a few milliseconds into the load, ~2.1 GHz settled).  20 steps, the
+    # decode launch of each bracketed by events.
+    step.run()
+    torch.cuda.synchronize()
+    time.sleep(1.0)
+    ca, cb = ev(), ev()
+    cold_ev = []
+    ca.record(stream)
+    for _ in range(20):
+        a, b = ev(), ev()
+        step.append_new()
+        a.record(stream)
+        step.decode_only()
+        b.record(stream)
+        step.combine_only()
+        cold_ev.append((a, b))
+    cb.record(stream)
+    torch.cuda.synchronize()
+    cold_dec = np.array([a.elapsed_time(b) for a, b in cold_ev])
+    cold = {"after_idle_s": 1.0, "steps": 20, "ms_per_step": round(ca.elapsed_time(cb) / 20, 5),
+            "decode_launch_ms_mean": round(float(cold_dec.mean()), 5),
+            "decode_launch_ms_max": round(float(cold_dec.max()), 5)}
+    log(f"cold start (after 1 s idle): {cold}")
+
+    # Before the timed region: the step with a cache scrub, the device copy and the spread of
+    # single steps (memory-bound or decode work, which keeps the load on and lets the clock
+    # settle); then, without an idle gap, the W warm-up steps and the K timed steps (the
+    # headline: back-to-back decode steps as a serving loop runs them).  The record-read probe
+    # and the prefill timings come after the timed region.
+    scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    ms_scrub, _, _ = time_scrubbed(step.run, max(5, args.steps // 2), scrub)
+    # Achievable device-copy bandwidth in the same run: 1 GiB copied (2 GiB moved).
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    c0, c1 = ev(), ev()
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) / (c0.elapsed_time(c1) / 5 / 1e3) / 1e9
+    del scrub, csrc, cdst
+    log(f"step with cache scrub {ms_scrub:.4f} ms; device copy {copy_gbps:.0f} GB/s")
+    # The spread of single steps: max(50, K) steps each bracketed by its own events (median,
+    # p10, p90 over at least 50 iterations), run before the timed region so that their markers
+    # do not touch the headline.
+    n_spread = max(50, args.steps)
+    sev = [ev() for _ in range(n_spread + 1)]
+    sev[0].record(stream)
+    for k in range(n_spread):
+        step.run()
+        sev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([sev[k].elapsed_time(sev[k + 1]) for k in range(n_spread)])
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -387,67 +505,42 @@ def main():
     # Timed region: exactly K whole steps back to back, bracketed by synchronisation.  The
     # decode-attention launch (the dominant part) is timed inside the same region, on its
     # stream: an event pair around the decode launch of every 4th step (steps 1, 5, 9, ...), so
-    # that the samples see the same clock and power state as the steps they belong to (the
-    # launch takes 225-250 us early in a run of back-to-back steps and up to ~300 us after a
-    # few milliseconds more of them) while only a quarter of the steps carry the two markers.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    ev = []
-    torch.cuda.synchronize()
+    # that the samples see the same clock and power state as the steps they belong to, while
+    # only a quarter of the steps carry the two markers.
+    start, end = ev(), ev()
+    dec_ev = []
     start.record(stream)
     for k in range(args.steps):
         if k % 4 == 1:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a, b = ev(), ev()
             step.append_new()
             a.record(stream)
             step.decode_only()
             b.record(stream)
             step.combine_only()
-            ev.append((a, b))
+            dec_ev.append((a, b))
         else:
             step.run()
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    if not ev:  # fewer than 2 steps: one more step, timed on its own
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+    if not dec_ev:  # fewer than 2 steps: one more step, timed on its own
+        a, b = ev(), ev()
         step.append_new()
         a.record(stream)
         step.decode_only()
         b.record(stream)
         step.combine_only()
         torch.cuda.synchronize()
-        ev.append((a, b))
-    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        dec_ev.append((a, b))
+    attn_ms = np.array([a.elapsed_time(b) for a, b in dec_ev])
     attn_avg = float(attn_ms.mean())
-    log(f"step {ms_step:.4f} ms; decode attention avg {attn_avg:.4f} ms over {len(ev)} timed "
-        f"steps (min {attn_ms.min():.4f}, max {attn_ms.max():.4f})")
+    log(f"step {ms_step:.4f} ms; decode attention avg {attn_avg:.4f} ms over {len(dec_ev)} timed "
+        f"steps (min {attn_ms.min():.4f}, max {attn_ms.max():.4f}); single steps p10/p50/p90 "
+        f"{np.percentile(step_ms, 10):.4f}/{np.percentile(step_ms, 50):.4f}/"
+        f"{np.percentile(step_ms, 90):.4f} ms")
 
-    # The same step with the last-level cache evicted (a 1 GiB read) before each one.
-    scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
-    ms_scrub, _, _ = time_scrubbed(step.run, max(5, args.steps // 2), scrub)
-    # Achievable device-copy bandwidth in the same run: 1 GiB copied (2 GiB moved).
-    csrc = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cdst = torch.empty_like(csrc)
-    cdst.copy_(csrc)
-    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ca.record(stream)
-    for _ in range(5):
-        cdst.copy_(csrc)
-    cb.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * (1 << 30) / (ca.elapsed_time(cb) / 5 / 1e3) / 1e9
-    del scrub, csrc, cdst
-    log(f"step with cache scrub {ms_scrub:.4f} ms; device copy {copy_gbps:.0f} GB/s")
-    record_read = record_read_probe(w, p, cache, stream, attn_avg)
-
-    tokens_per_s = w.batch / (ms_step / 1e3)
-    step_gbps = bm["step"] / (ms_step / 1e3) / 1e9
-    attn_gbps = bm["decode_attention"] / (attn_avg / 1e3) / 1e9
-
+    record_read = record_read_probe(w, p, cache, stream)
     prefill = None
     if tail:
         # Both append kernels write the same bytes; the automatic choice for this size is the
@@ -460,7 +553,7 @@ def main():
                  ("hadamard", do_prefill_hadamard))
         for name, fn in cases:
             fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = ev(), ev()
             a.record(stream)
             for _ in range(reps):
                 fn()
@@ -486,6 +579,10 @@ def main():
         step.run()  # restore the window rows the prefill re-append rewrote
         torch.cuda.synchronize()
 
+    tokens_per_s = w.batch / (ms_step / 1e3)
+    step_gbps = bm["step"] / (ms_step / 1e3) / 1e9
+    attn_gbps = bm["decode_attention"] / (attn_avg / 1e3) / 1e9
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -493,28 +590,36 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 1 GiB device copy done")
 
+    gpu_out = step.out.cpu().numpy()
+    gpu_lse = step.lse.cpu().numpy()
+    samples = {}
+    compare = None
+    if not args.no_compare:
+        compare = int2_vs_bf16(20, samples)
+
+    # CPU leg: the oracle timed on a bounded sample of the headline workload (the CPU
+    # baseline), and the oracle's outputs of one (sequence, KV head) pair of every timed INT2
+    # workload compared with the GPU's.
     cpu = None
     parity = None
     if not args.no_cpu:
         t0 = time.time()
         ref, cpu = cpu_baseline(p, args.cpu_seconds)
         log(f"cpu oracle baseline: {cpu['value']:.4f} tokens/s ({time.time() - t0:.1f} s)")
-        # the oracle's outputs of the same cache state against the GPU's last decode step
         G = w.group
-        out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
-        errs, dl = [], []
-        for h, (o_ref, l_ref) in ref.items():
-            o_gpu = out[0, h * G:(h + 1) * G].astype(np.float64)
-            errs.append(np.abs(o_gpu - o_ref[0]).max(axis=-1) / np.abs(o_ref[0]).max(axis=-1))
-            dl.append(np.abs(lse[0, h * G:(h + 1) * G] - l_ref[0]))
-        parity = {"rows": int(sum(e.size for e in errs)), "sequence": 0,
-                  "kv_heads": sorted(ref), "max_row_rel_err": float(np.max(errs)),
-                  "max_abs_dlse": float(np.max(dl)), "tolerance": 2e-3}
-        log(f"parity sample: {parity}")
-
-    compare = None
-    if not args.no_compare:
-        compare = int2_vs_bf16(20)
+        outs = [gpu_out[0, h * G:(h + 1) * G] for h in sorted(ref)]
+        lses = [gpu_lse[0, h * G:(h + 1) * G] for h in sorted(ref)]
+        parity = {w.name: parity_record(np.stack(outs), np.stack(lses),
+                                        np.stack([ref[h][0][0] for h in sorted(ref)]),
+                                        np.stack([ref[h][1][0] for h in sorted(ref)]),
+                                        sequence=0, kv_heads=sorted(ref))}
+        for name, (pp, b, h, o, l) in samples.items():
+            t1 = time.time()
+            r, rl = oracle_pair(pp, b, h)
+            parity[name] = parity_record(o, l, r, rl, sequence=b, kv_heads=[h],
+                                         context=int(pp.lens[b]))
+            log(f"parity {name}: {parity[name]} ({time.time() - t1:.1f} s)")
+        log(f"parity {w.name}: {parity[w.name]}")
 
     line = {
         "metric": METRIC,
@@ -537,13 +642,18 @@ def main():
                    "max_splits": step.max_splits},
         "effective_gbps": round(step_gbps, 1),
         "pct_of_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
+        "kv_positions_per_s": round(float(np.asarray(p.lens, np.int64).sum()) / (ms_step / 1e3), 1),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
+        "step_spread_samples": int(len(step_ms)),
+        "cold_start": cold,
         "ms_per_step_cache_scrubbed": round(ms_scrub, 5),
         "copy_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "oscar_decode_attention (q prep + INT2 runs + "
                      "BF16 window)", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": bm["decode_attention"], "launch_ms": round(attn_avg, 5),
-                     "launch_samples": len(ev),
+                     "launch_samples": len(dec_ev),
+                     "launch_ms_p10_p90": [round(float(np.percentile(attn_ms, q)), 5) for q in (10, 90)],
                      "traffic": measured_traffic(w.name),
                      "frac_of_copy": round(attn_gbps / copy_gbps, 4),
                      "frac_of_record_read": round(attn_gbps / record_read["gbps"], 4)},
@@ -551,7 +661,7 @@ def main():
         "bytes": bm,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
-        "parity_sample": parity,
+        "parity": parity,
         "int2_vs_bf16": compare,
     }
     print(json.dumps(line), flush=True)

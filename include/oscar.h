@@ -383,7 +383,7 @@ int32_t oscar_mfma_bf16_tiles(const uint16_t* a, const uint16_t* b, const float*
  *               [0, num_records) reads the last record instead, so memory stays in bounds
  *   record_ids  int32 [n]
  *   out         uint32 [64 * num_workers], written
- * A run of odd length reads its last record once (the step's second record is skipped).
+ * A run of odd length folds its last record once (the step's second record contributes zero).
  * Returns OSCAR_ERR_INVALID_ARGUMENT for n < 0, num_records < 1, num_workers outside
  * [1, 1048576] or a null/misaligned pointer.
  */

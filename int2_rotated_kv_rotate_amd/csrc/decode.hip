@@ -41,29 +41,6 @@ constexpr float kNegBig = -1.0e30f;
 
 // ---------------------------------------------------------------------- small wave helpers
 
-__device__ __forceinline__ float dpp_quad_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_quad_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float max_across_rows(float x) {  // lanes l, l^16, l^32, l^48
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float sum_across_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-// bf16 "1 + code/4" for two 2-bit codes at bits (2*nb) and (16 + 2*nb) of x.
-__device__ __forceinline__ uint32_t vcode_pair(uint32_t x, int nb) {
-  const uint32_t y = (nb <= 2) ? (x << (5 - 2 * nb)) : (x >> (2 * nb - 5));
-  return (y & 0x00600060u) | 0x3F803F80u;
-}
-
 typedef float v2f_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
 
@@ -335,7 +312,7 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 constexpr int kPairBytes = 3 * 1024;
 constexpr int kPairSlots = 2;  // the pair being computed + the next one in flight
 constexpr int kRingBytes = kPairSlots * kPairBytes;
-constexpr int kPairHeadB = 1024, kPairTailA = 2048, kPairTailB = 2560;
+constexpr int kPairHeadB = 1024;   // record B head; the tails follow at 2048 and 2560
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

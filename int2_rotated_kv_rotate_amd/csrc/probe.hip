@@ -14,7 +14,7 @@ constexpr int kProbeWaves = 2;
 // the first 1024 bytes of each record, lanes 0..31 the last 512), and writes the XOR of
 // everything it read to out[w*64 + lane].  A record id outside [0, num_records) reads the
 // pool's last record instead (as the decode kernel does with page ids outside the pool); the
-// second record of a step past the end of the run is not read (it contributes zero).
+// second record of a step past the end of the run contributes zero.
 __global__ __launch_bounds__(64 * kProbeWaves) void read_records_kernel(
     const uint8_t* __restrict__ pool, int num_records, const int32_t* __restrict__ record_ids,
     int n, int C, int workers, uint32_t* __restrict__ out) {
@@ -27,15 +27,21 @@ __global__ __launch_bounds__(64 * kProbeWaves) void read_records_kernel(
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   uint4 acc = zero;
   for (int i = (int)min(r0, (long long)n); i < r1; i += 2) {
+    // both records are always loaded (the second is record i again past the end of the run)
+    // so that the four loads issue together; the dummy's words are then replaced by zeros
     const bool has_b = i + 1 < r1;
     const uint32_t ida = min((uint32_t)record_ids[i], last);
-    const uint32_t idb = has_b ? min((uint32_t)record_ids[i + 1], last) : ida;
+    const uint32_t idb = min((uint32_t)record_ids[has_b ? i + 1 : i], last);
     const uint4* ra = reinterpret_cast<const uint4*>(pool + (size_t)ida * kRecord);
     const uint4* rb = reinterpret_cast<const uint4*>(pool + (size_t)idb * kRecord);
     const uint4 a0 = ra[lane];
-    const uint4 b0 = has_b ? rb[lane] : zero;
+    uint4 b0 = rb[lane];
     const uint4 a1 = lane < 32 ? ra[64 + lane] : zero;
-    const uint4 b1 = has_b && lane < 32 ? rb[64 + lane] : zero;
+    uint4 b1 = lane < 32 ? rb[64 + lane] : zero;
+    if (!has_b) {
+      b0 = zero;
+      b1 = zero;
+    }
     acc.x ^= a0.x ^ b0.x ^ a1.x ^ b1.x;
     acc.y ^= a0.y ^ b0.y ^ a1.y ^ b1.y;
     acc.z ^= a0.z ^ b0.z ^ a1.z ^ b1.z;
