@@ -278,6 +278,9 @@ def int2_vs_bf16(n_iter: int, samples: dict):
         step.run()
         torch.cuda.synchronize()
         ms = time_scrubbed(step.attend, n_iter, scrub)
+        g = H.capture_graph(step.attend)
+        graph_ms = time_scrubbed(g.replay, n_iter, scrub)
+        del g
         pool = p.num_pages * w.num_kv_heads * 1536
         # the outputs of one (sequence, KV head) pair, kept for the oracle comparison: the
         # longest sequence, the last KV head
@@ -287,7 +290,7 @@ def int2_vs_bf16(n_iter: int, samples: dict):
         samples[w.name] = (p, b, h, step.out[b, h * G:(h + 1) * G].cpu().numpy(),
                            step.lse[b, h * G:(h + 1) * G].cpu().numpy())
         del step, cache
-        return p, ms, pool
+        return p, ms, pool, graph_ms
 
     def bf16_case(w):
         p = H.make_problem(w)
@@ -295,30 +298,42 @@ def int2_vs_bf16(n_iter: int, samples: dict):
         bc.attend()
         torch.cuda.synchronize()
         ms = time_scrubbed(bc.attend, n_iter, scrub)
+        g = H.capture_graph(bc.attend)
+        graph_ms = time_scrubbed(g.replay, n_iter, scrub)
+        del g, bc
         pool = p.num_pages * w.num_kv_heads * 8192
-        del bc
-        return p, ms, pool
+        return p, ms, pool, graph_ms
 
     def gbps(w, p, ms, bf16):
         return round(attn_bytes(w, p, bf16) / (ms * 1e-3) / 1e9, 1)
 
     # Long context, batch 1 (131072 positions, the needle workload's cache): INT2 latency
+    def graph_pair(gi, gb):
+        """Latency of INT2 and BF16 attention replayed from HIP graphs (median, p10, p90)."""
+        return {"int2_ms": round(gi[0], 4), "bf16_ms": round(gb[0], 4),
+                "int2_ms_p10_p90": [round(gi[1], 4), round(gi[2], 4)],
+                "bf16_ms_p10_p90": [round(gb[1], 4), round(gb[2], 4)],
+                "latency_ratio": round(gb[0] / gi[0], 3)}
+
     wl = W.WORKLOADS["long_128k"]
-    pl, (msl, _, _), _ = int2_case(wl)
-    _, (msl_b, _, _), _ = bf16_case(wl)
+    pl, (msl, _, _), _, gl = int2_case(wl)
+    _, (msl_b, _, _), _, gl_b = bf16_case(wl)
     res["long_128k_b1"] = {"int2_ms": round(msl, 4), "bf16_ms": round(msl_b, 4),
                            "latency_ratio": round(msl_b / msl, 3),
                            "int2_effective_gbps": gbps(wl, pl, msl, False),
-                           "bf16_effective_gbps": gbps(wl, pl, msl_b, True)}
-    log(f"long_128k B=1: INT2 {msl:.4f} ms, BF16 {msl_b:.4f} ms")
+                           "bf16_effective_gbps": gbps(wl, pl, msl_b, True),
+                           "graph": graph_pair(gl, gl_b)}
+    log(f"long_128k B=1: INT2 {msl:.4f} ms, BF16 {msl_b:.4f} ms; from graphs INT2 "
+        f"{gl[0]:.4f} ms, BF16 {gl_b[0]:.4f} ms")
 
     w32 = W.WORKLOADS["qwen3_32b"]
-    p, (ms, p10, p90), pool = int2_case(w32)
+    p, (ms, p10, p90), pool, g32 = int2_case(w32)
     r32 = {"int2": {"batch": w32.batch, "ms": round(ms, 4), "tokens_per_s": round(w32.batch / ms * 1e3, 1),
-                    "pool_bytes": pool, "effective_gbps": gbps(w32, p, ms, False)}}
+                    "pool_bytes": pool, "effective_gbps": gbps(w32, p, ms, False),
+                    "graph_ms": round(g32[0], 4)}}
     for bb in w32.bf16_batches:
         wb = W.scaled(w32, batch=bb, name=f"qwen3_32b_bf16_b{bb}")
-        pb, (msb, _, _), poolb = bf16_case(wb)
+        pb, (msb, _, _), poolb, _ = bf16_case(wb)
         r32[f"bf16_b{bb}"] = {"batch": bb, "ms": round(msb, 4),
                               "tokens_per_s": round(bb / msb * 1e3, 1), "pool_bytes": poolb,
                               "effective_gbps": gbps(wb, pb, msb, True)}
@@ -328,13 +343,15 @@ def int2_vs_bf16(n_iter: int, samples: dict):
         f"BF16 B={r32[k]['batch']} {r32[k]['ms']:.4f} ms" for k in r32 if k.startswith("bf16")))
 
     w4 = W.WORKLOADS["qwen3_4b"]
-    p4, (ms_i, _, _), _ = int2_case(w4)
-    _, (ms_b, _, _), _ = bf16_case(w4)
+    p4, (ms_i, _, _), _, g4 = int2_case(w4)
+    _, (ms_b, _, _), _, g4_b = bf16_case(w4)
     res["qwen3_4b_b1_ctx32k"] = {"int2_ms": round(ms_i, 4), "bf16_ms": round(ms_b, 4),
                                  "latency_ratio": round(ms_b / ms_i, 3),
                                  "int2_effective_gbps": gbps(w4, p4, ms_i, False),
-                                 "bf16_effective_gbps": gbps(w4, p4, ms_b, True)}
-    log(f"qwen3_4b B=1: INT2 {ms_i:.4f} ms, BF16 {ms_b:.4f} ms")
+                                 "bf16_effective_gbps": gbps(w4, p4, ms_b, True),
+                                 "graph": graph_pair(g4, g4_b)}
+    log(f"qwen3_4b B=1: INT2 {ms_i:.4f} ms, BF16 {ms_b:.4f} ms; from graphs INT2 "
+        f"{g4[0]:.4f} ms, BF16 {g4_b[0]:.4f} ms")
 
     # The INT4 variant (2560-byte records, vector-ALU decode) at the Qwen3-8B batch-64 shape
     w8 = W.WORKLOADS["qwen3_8b_b64"]
@@ -541,6 +558,31 @@ def main():
         f"{np.percentile(step_ms, 90):.4f} ms")
 
     record_read = record_read_probe(w, p, cache, stream)
+
+    # The same step replayed from a HIP graph, the way a serving loop issues it when the
+    # kernels are shorter than the host's work per launch (batch 1): K replays of the whole
+    # step back to back, then K replays of the decode launch alone (q preparation + decode
+    # kernel), each bracketed by events.  After the timed region: not part of the headline.
+    g_step = H.capture_graph(step.run)
+    g_dec = H.capture_graph(step.decode_only)
+    n_rep = max(args.steps, 5)
+    ga, gb = ev(), ev()
+    ga.record(stream)
+    for _ in range(n_rep):
+        g_step.replay()
+    gb.record(stream)
+    dev_ev = [ev() for _ in range(n_rep + 1)]
+    dev_ev[0].record(stream)
+    for k in range(n_rep):
+        g_dec.replay()
+        dev_ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    graph = {"replays": n_rep, "ms_per_step": round(ga.elapsed_time(gb) / n_rep, 5),
+             "decode_launch_ms": round(float(np.mean(
+                 [dev_ev[k].elapsed_time(dev_ev[k + 1]) for k in range(n_rep)])), 5)}
+    del g_step, g_dec
+    log(f"graph replay: step {graph['ms_per_step']:.4f} ms, decode launch "
+        f"{graph['decode_launch_ms']:.4f} ms")
     prefill = None
     if tail:
         # Both append kernels write the same bytes; the automatic choice for this size is the
@@ -658,6 +700,7 @@ def main():
                      "frac_of_copy": round(attn_gbps / copy_gbps, 4),
                      "frac_of_record_read": round(attn_gbps / record_read["gbps"], 4)},
         "record_read": record_read,
+        "graph_replay": graph,
         "bytes": bm,
         "prefill_append": prefill,
         "cpu_baseline": cpu,

@@ -231,8 +231,10 @@ int32_t oscar_int4_decode_attention(
 
 /*
  * Bytes of workspace oscar_decode_attention / oscar_bf16_decode_attention need for `batch`
- * sequences of `num_q_heads` query heads split at most `max_splits` ways.  Returns 0 for
- * invalid arguments.
+ * sequences of `num_q_heads` query heads split at most `max_splits` ways: per (sequence, query
+ * head) a 1024-byte query block and max_splits + 8 partial slots of 520 bytes (128 fp32
+ * outputs, then (m, l) in a region of its own), plus a plan of 4 * (4 + 3 * batch +
+ * batch * num_q_heads) bytes rounded up to 256.  Returns 0 for invalid arguments.
  */
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits);
 
@@ -255,7 +257,11 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  * streams the same number of pages however the lengths are mixed.  A run yields one partial
  * for each pair it touches; a pair's partials fill its slots 0, 1, ... in page order.  C is the
  * smallest run length that needs at most num_workers runs and gives no pair more than
- * max_splits partials.  The BF16 positions of each pair form one more partial.
+ * max_splits partials.  The BF16 positions of each pair (sink first, then window, in position
+ * order) form up to 8 more partials, the pair's window slots: one for all of them when the
+ * launch has at least half as many (sequence, KV head) pairs as the device has compute units,
+ * else one per 32 positions (each on its own workgroup, so that a short launch is not held up
+ * by the window's dependent loads); unused window slots are marked empty.
  *
  *   q            bf16 bits [batch][num_q_heads][128] (after RoPE, unrotated).
  *   seq_lens     int32 [batch], >= 1.
@@ -265,7 +271,7 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *   num_workers  worker wavefronts, 0 for one per resident wavefront slot of the device
  *                (the fastest choice); at most 2^20.
  *   max_splits   INT2 partials per (sequence, KV head), >= 1, with
- *                8 * (num_q_heads / Hkv) * (max_splits + 1) <= 49152 (else
+ *                8 * (num_q_heads / Hkv) * (max_splits + 8) <= 49152 (else
  *                OSCAR_ERR_UNSUPPORTED).  Too small a value lengthens the runs.
  *   workspace    device buffer of at least oscar_decode_workspace_bytes(batch, num_q_heads,
  *                max_splits) bytes; contents on entry do not matter.

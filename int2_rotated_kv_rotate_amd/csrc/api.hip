@@ -1,5 +1,7 @@
 // C ABI entry points: validate host-visible arguments, then enqueue the kernels on the caller's
-// stream.  No allocation, no synchronisation, no state.
+// stream.  No allocation and no synchronisation; the only state is a per-device cache of the
+// compute-unit count and of the static workspace address.
+#include <atomic>
 #include <mutex>
 
 #include "../../include/oscar.h"
@@ -36,7 +38,7 @@ int32_t check_heads(int32_t hq, int32_t hkv) {
 // The combine keeps (m, l) of every split of a KV head's G query heads in 48 KiB of LDS.
 int32_t check_splits(int32_t hq, int32_t hkv, int32_t max_splits) {
   if (max_splits < 1) return OSCAR_ERR_INVALID_ARGUMENT;
-  if ((size_t)2 * (hq / hkv) * ((size_t)max_splits + 1) * sizeof(float) > 48 * 1024)
+  if ((size_t)2 * (hq / hkv) * ((size_t)max_splits + kWinSlots) * sizeof(float) > 48 * 1024)
     return OSCAR_ERR_UNSUPPORTED;
   return OSCAR_OK;
 }
@@ -81,6 +83,18 @@ hipError_t scratch_address(void** out) {
 }
 
 }  // namespace
+
+int oscar::current_device_cus() {
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 0;
+  cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 extern "C" {
 

@@ -938,11 +938,8 @@ hipError_t launch_append_hadamard(const CacheGeom& g, uint8_t* pages, uint16_t* 
                                   const int8_t* signs_k, const int8_t* signs_v, float clip_k,
                                   float clip_v, hipStream_t stream) {
   if (batch == 0 || total_new == 0) return hipSuccess;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
+  int cus = current_device_cus();
+  if (cus <= 0) cus = 256;
   // about 8 waves per SIMD over the 2 * Hkv (head, K|V) pairs; at least one row per wave
   const int want = max(1, 32 * cus / (2 * g.hkv * kHadWaves));
   const int blocks = max(1, min(want, (total_new + kHadWaves - 1) / kHadWaves));
@@ -961,11 +958,8 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
   if (batch == 0 || total_new == 0) return hipSuccess;
   if (method == kAppendAuto) method = total_new >= kMatrixAppendRows ? kAppendMatrix : kAppendVector;
   if (method == kAppendMatrix) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
+    int cus = current_device_cus();
+    if (cus <= 0) cus = 256;
     // one resident workgroup per CU (R and the tile take most of the LDS) over the 2 * Hkv
     // (KV head, K|V) pairs.  Centered keys leave more values uncertain (about 1.8% against
     // 1.2% recomputed), so with a key mean K gets 19 of every 32 workgroups of a head.

@@ -62,8 +62,16 @@ __global__ __launch_bounds__(64) void bf16_decode_kernel(
     int split_pages, Workspace ws) {
   const int lane = threadIdx.x, kq = lane >> 4, c16 = lane & 15;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int max_splits = ws.nslots - 1;
+  const int max_splits = ws.max_splits();
   const int G = hq / g.hkv;
+  if (split == 0) {  // no sink/window split here: the pair's window slots are empty, and every
+                     // split slot is written (each split writes its own, empty or not)
+    static_assert(8 * kWinSlots <= 64, "one lane per window slot of the pair's heads");
+    if (lane < G * kWinSlots)
+      *ws.ml(b, hq, h * G + lane / kWinSlots, ws.win_slot() + lane % kWinSlots) =
+          make_float2(kNegBig, 0.f);
+    if (lane == 0) ws.nvalid()[b * g.hkv + h] = max_splits;
+  }
   const int L = max(seq_lens[b], 0);
   const float sm_log2 = sm_scale * kLog2e;
   int pg0 = split * split_pages;
@@ -188,15 +196,6 @@ __global__ __launch_bounds__(64) void bf16_decode_kernel(
   if (kq == 0 && c16 < G) *ws.ml(b, hq, h * G + c16, split) = make_float2(mrun, lt);
 }
 
-// The BF16 baseline has no sink/window split: mark the last slot empty, and every split slot
-// of every (sequence, KV head) as written (each split writes its slot, empty or not).
-__global__ void empty_slot_kernel(int hq, int hkv, Workspace ws) {
-  const int b = blockIdx.x;
-  for (int j = threadIdx.x; j < hq; j += blockDim.x)
-    *ws.ml(b, hq, j, ws.nslots - 1) = make_float2(kNegBig, 0.f);
-  for (int h = threadIdx.x; h < hkv; h += blockDim.x) ws.nvalid()[b * hkv + h] = ws.nslots - 1;
-}
-
 }  // namespace
 
 hipError_t launch_bf16_append(const CacheGeom& g, uint16_t* pages, const int32_t* block_table,
@@ -214,9 +213,8 @@ hipError_t launch_bf16_decode(const CacheGeom& g, const uint16_t* pages,
                               const int32_t* seq_lens, float sm_scale, int split_pages,
                               const Workspace& ws, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(bf16_decode_kernel, dim3(ws.nslots - 1, g.hkv, batch), dim3(64), 0, stream,
+  hipLaunchKernelGGL(bf16_decode_kernel, dim3(ws.max_splits(), g.hkv, batch), dim3(64), 0, stream,
                      g, pages, block_table, hq, q, seq_lens, sm_scale, split_pages, ws);
-  hipLaunchKernelGGL(empty_slot_kernel, dim3(batch), dim3(64), 0, stream, hq, g.hkv, ws);
   return hipGetLastError();
 }
 

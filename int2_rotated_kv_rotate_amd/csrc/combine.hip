@@ -48,37 +48,40 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
       }
     }
   }
-  // INT2 partials in slots [0, nvalid), the BF16 sink/window partial in the last slot.  All
-  // loads are issued before nvalid is known (slots past it hold stale but readable values that
-  // never enter the sums), so the kernel pays one memory latency, not two.
+  // INT2 partials in slots [0, nvalid), the BF16 sink/window partials in the last kWinSlots
+  // slots.  All loads are issued before nvalid is known (slots past it hold stale but readable
+  // values that never enter the sums), so the kernel pays one memory latency, not two.
   const int nv_raw = ws.nvalid()[b * hkv + h];
+  const int ms = ws.max_splits();
   const float* o = ws.o(b, hq, jq, 0) + c;
   constexpr int kBatch = 16;
   float ov[kBatch];
 #pragma unroll
-  for (int e = 0; e < kBatch; ++e) ov[e] = e < ns - 1 ? o[(size_t)e * kHeadDim] : 0.f;
-  const float ow = o[(size_t)(ns - 1) * kHeadDim];
+  for (int e = 0; e < kBatch; ++e) ov[e] = e < ms ? o[(size_t)e * kHeadDim] : 0.f;
+  float ow[kWinSlots];
+#pragma unroll
+  for (int k = 0; k < kWinSlots; ++k) ow[k] = o[(size_t)(ms + k) * kHeadDim];
   for (int e = c; e < ns; e += 128) {  // raw (m, l) of every slot of head j
     const float2 ml = *ws.ml(b, hq, jq, e);
     s_w[j * ns + e] = ml.x;
     s_w[G * ns + j * ns + e] = ml.y;
   }
   __syncthreads();
-  const int nv = min(max(nv_raw, 0), ns - 1);
+  const int nv = min(max(nv_raw, 0), ms);
   // Merge weights, computed by the head's 128 threads (entry e by thread e % 128): the INT2
-  // slots 0 .. nv-1 and the window slot; M and l reduced in a fixed order.
+  // slots 0 .. nv-1 and the window slots; M and l reduced in a fixed order.
   float* wm = s_w + j * ns;
   const float* wl = s_w + G * ns + j * ns;
   float mloc = -INFINITY;
   for (int e = c; e < ns; e += 128)
-    if ((e < nv || e == ns - 1) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
+    if ((e < nv || e >= ms) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
   for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2));
   if ((c & 63) == 0) s_red[j][c >> 6] = mloc;
   __syncthreads();
   const float M = fmaxf(s_red[j][0], s_red[j][1]);
   float lloc = 0.f;
   for (int e = c; e < ns; e += 128) {
-    const bool use = (e < nv || e == ns - 1) && wl[e] > 0.f;
+    const bool use = (e < nv || e >= ms) && wl[e] > 0.f;
     const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
     wm[e] = w;
     if (use) lloc = fmaf(w, wl[e], lloc);  // an unused slot's stale l may be NaN
@@ -89,9 +92,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
   const float l = s_red[j][2] + s_red[j][3];
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   if (c == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
-  // o'[j][c] = sum_e w_e o'_e[c] / l over the INT2 slots in order, then the window slot; an
-  // empty entry (w = 0) is skipped, so its partial output is never read into the sum.  Slots
-  // past the first 16 are loaded 16 at a time.
+  // o'[j][c] = sum_e w_e o'_e[c] / l over the INT2 slots in order, then the window slots in
+  // order; an empty entry (w = 0) is skipped, so its partial output is never read into the
+  // sum.  Slots past the first 16 are loaded 16 at a time.
   const float* wj = wm;
   float acc = 0.f;
 #pragma unroll
@@ -108,7 +111,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
       if (w > 0.f) acc = fmaf(w, ob[e], acc);
     }
   }
-  if (wj[ns - 1] > 0.f) acc = fmaf(wj[ns - 1], ow, acc);
+#pragma unroll
+  for (int k = 0; k < kWinSlots; ++k)
+    if (wj[ms + k] > 0.f) acc = fmaf(wj[ms + k], ow[k], acc);
   s_o[j][c] = acc * inv;
   __syncthreads();
   float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspac
 // order.  For R_V^T, thread t computes half (kh = t % 2) of output channel t / 2 (only threads
 // < 256) from its R_V row, loaded first.
 constexpr int kHeadThreads = 512, kSlotLanes = kHeadThreads / 32;
+static_assert(kWinSlots <= kSlotLanes, "one slot lane per window slot");
 
 __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int hkv, Workspace ws,
                                                                   const float* __restrict__ rot_v,
@@ -149,6 +155,7 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
   const int ns = ws.nslots;
   extern __shared__ float s_w[];  // [2][ns]: m of each slot (then its merge weight), l
   __shared__ float4 s_part[kSlotLanes][32];
+  __shared__ float4 s_win[kWinSlots][32];  // the window slots' outputs
   __shared__ float s_o[kHeadDim];
   __shared__ float s_red[2][kHeadThreads / 64];
 
@@ -165,25 +172,27 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
   const float4* ob = reinterpret_cast<const float4*>(ws.o(b, hq, jq, 0)) + c4;
   constexpr int kStride = kHeadDim / 4;  // float4 per slot
   constexpr int kFlight = 8;
+  const int ms = ws.max_splits();
   float4 pre[kFlight];
 #pragma unroll
   for (int k = 0; k < kFlight; ++k) {
     const int e = sg + k * kSlotLanes;
-    pre[k] = e < ns - 1 ? ob[(size_t)e * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
+    pre[k] = e < ms ? ob[(size_t)e * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float4 owin = t < 32 ? ob[(size_t)(ns - 1) * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
+  // window slot sg (< kWinSlots) of this thread's channel quad, added after the INT2 sums
+  const float4 owin = sg < kWinSlots ? ob[(size_t)(ms + sg) * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int e = t; e < ns; e += kHeadThreads) {
     const float2 ml = *ws.ml(b, hq, jq, e);
     s_w[e] = ml.x;
     s_w[ns + e] = ml.y;
   }
   __syncthreads();
-  const int nv = min(max(nv_raw, 0), ns - 1);
+  const int nv = min(max(nv_raw, 0), ms);
   float* wm = s_w;
   const float* wl = s_w + ns;
   float mloc = -INFINITY;
   for (int e = t; e < ns; e += kHeadThreads)
-    if ((e < nv || e == ns - 1) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
+    if ((e < nv || e >= ms) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
   for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2));
   if (lane == 0) s_red[0][wv] = mloc;
   __syncthreads();
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
   for (int k = 1; k < kHeadThreads / 64; ++k) M = fmaxf(M, s_red[0][k]);
   float lloc = 0.f;
   for (int e = t; e < ns; e += kHeadThreads) {
-    const bool use = (e < nv || e == ns - 1) && wl[e] > 0.f;
+    const bool use = (e < nv || e >= ms) && wl[e] > 0.f;
     const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
     wm[e] = w;
     if (use) lloc = fmaf(w, wl[e], lloc);  // an unused slot's stale l may be NaN
@@ -231,6 +240,7 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
   }
   for (; e < nv; e += kSlotLanes) add(wm[e], ob[(size_t)e * kStride]);
   s_part[sg][c4] = acc;
+  if (sg < kWinSlots) s_win[sg][c4] = owin;
   __syncthreads();
   if (t < 32) {
     float4 sum = s_part[0][t];
@@ -242,13 +252,16 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
       sum.z += v.z;
       sum.w += v.w;
     }
-    const float ww = wm[ns - 1];
-    if (ww > 0.f) {
-      const float4 x = owin;
-      sum.x = fmaf(ww, x.x, sum.x);
-      sum.y = fmaf(ww, x.y, sum.y);
-      sum.z = fmaf(ww, x.z, sum.z);
-      sum.w = fmaf(ww, x.w, sum.w);
+#pragma unroll
+    for (int k = 0; k < kWinSlots; ++k) {
+      const float ww = wm[ms + k];
+      if (ww > 0.f) {
+        const float4 x = s_win[k][t];
+        sum.x = fmaf(ww, x.x, sum.x);
+        sum.y = fmaf(ww, x.y, sum.y);
+        sum.z = fmaf(ww, x.z, sum.z);
+        sum.w = fmaf(ww, x.w, sum.w);
+      }
     }
     s_o[4 * t + 0] = sum.x * inv;
     s_o[4 * t + 1] = sum.y * inv;
@@ -283,11 +296,9 @@ hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const
   if (batch == 0) return hipSuccess;
   // One workgroup per query head when one per KV head would cover less than half of the
   // compute units and the heads have many splits to merge.
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipErrorInvalidValue;
-  if ((long long)batch * hkv * 2 < cus && ws.nslots > 32) {
+  const int cus = current_device_cus();
+  if (cus <= 0) return hipErrorInvalidValue;
+  if ((long long)batch * hkv * 2 < cus && ws.max_splits() > 32) {
     const size_t lds1 = (size_t)2 * ws.nslots * sizeof(float);
     hipLaunchKernelGGL(combine_head_kernel, dim3(hq, batch), dim3(kHeadThreads), lds1, stream, hq,
                        hkv, ws, rot_v, out, lse);

@@ -77,7 +77,7 @@ __device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_l
   constexpr int kPlanWaves = kPrepThreads / 64;
   __shared__ int s_w[2][kPlanWaves];  // per-wave sums / maxima, then per-wave scan totals
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int B = ws.batch, max_splits = ws.nslots - 1;
+  const int B = ws.batch, max_splits = ws.max_splits();
   auto int2_pages = [&](int b, int& first) -> int {  // INT2 pages of sequence b, first page
     const int L = max(seq_lens[b], 0);
     const int n_sink = min(L, g.num_sink);
@@ -647,12 +647,16 @@ constexpr size_t kSmemBytes = (size_t)kWaves * kRingBytes + (size_t)kWaves * siz
 
 // BF16 sink + window positions of one (sequence, KV head), computed by the kWaves waves of one
 // workgroup: logits on the bf16 MFMA (q' as a hi/lo bf16 pair, K rows exact), softmax in fp32,
-// P.V on the VALU with one channel pair per lane.  Written as the pair's last partial slot.
+// P.V on the VALU with one channel pair per lane.  With nparts > 1 the pair's positions (sink
+// first, then window, in position order) are cut into parts of kWinPartTokens and this
+// workgroup takes part `part`; with nparts == 1 it takes them all.  Written as window slot
+// `part` of the pair; part 0 also marks window slots nparts .. kWinSlots-1 empty.
 template <int NCB>
 __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* __restrict__ sinkwin,
                                             const int32_t* __restrict__ slot_ids, int hq,
                                             const int32_t* __restrict__ seq_lens, float sm_log2,
-                                            const Workspace& ws, int b, int h, uint8_t* smem) {
+                                            const Workspace& ws, int b, int h, int part,
+                                            int nparts, uint8_t* smem) {
   constexpr int kJ = 4 * NCB;  // head rows kept (G <= kJ)
   static_assert(kWaves == 2, "the P.V partials of the two waves are added pairwise");
   static_assert((kMaxSinkWindow * kJ + 2 * kJ + kJ * kHeadDim) * sizeof(float) <= kSmemBytes<NCB>,
@@ -665,12 +669,15 @@ __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* 
   const int n_sink = min(L, g.num_sink);
   const int n_win = min(g.window, L - n_sink);
   const bool live = sinkwin != nullptr && slot >= 0 && slot < g.num_slots && n_sink + n_win > 0;
-  const int n = live ? n_sink + n_win : 0;
+  const int n_all = live ? n_sink + n_win : 0;
+  const int t0 = nparts == 1 ? 0 : part * kWinPartTokens;  // first position index of the part
+  const int n = nparts == 1 ? n_all : min(max(n_all - t0, 0), kWinPartTokens);
   float* s_p = reinterpret_cast<float*>(smem);   // [kMaxSinkWindow][kJ] logits, then p
   float* s_red = s_p + kMaxSinkWindow * kJ;      // [kJ] max, then [kJ] sum
   float* s_o = s_red + 2 * kJ;                   // [kJ][128] P.V of the second wave
   const size_t base = ((size_t)slot * g.hkv + h) * (size_t)(g.num_sink + g.window);
-  auto row_ptr = [&](int i) -> const uint16_t* {  // K row of window index i; the V row follows
+  auto row_ptr = [&](int il) -> const uint16_t* {  // K row of part index il; the V row follows
+    const int i = t0 + il;
     const int p = i < n_sink ? i : L - n_win + (i - n_sink);
     const int row = p < g.num_sink ? p : g.num_sink + p % g.window;
     return sinkwin + (base + row) * 2 * kHeadDim;
@@ -805,7 +812,11 @@ __device__ __forceinline__ void window_pair(const CacheGeom& g, const uint16_t* 
   }
   __syncthreads();
   if (wave == 0) {
-    const int out_slot = ws.nslots - 1;
+    const int out_slot = ws.win_slot() + part;
+    if (part == 0) {  // the window slots no part of this launch writes
+      for (int e = lane; e < G * (kWinSlots - nparts); e += 64)
+        *ws.ml(b, hq, h * G + e % G, ws.win_slot() + nparts + e / G) = make_float2(kNegBig, 0.f);
+    }
     if (tq == 0) {
 #pragma unroll
       for (int j = 0; j < kJ; ++j)
@@ -836,14 +847,15 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
     CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ plan, float sm_scale,
-    int worker_groups, int window_first, Workspace ws) {
+    int worker_groups, int window_first, int wparts, Workspace ws) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes<NCB>];
   int bid = blockIdx.x;
-  const int nwin = ws.batch * g.hkv;
+  const int nwin = ws.batch * g.hkv * wparts;
   if (window_first ? bid < nwin : bid >= worker_groups) {
-    const int pair = window_first ? bid : bid - worker_groups;
-    window_pair<NCB == 8 ? 2 : NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
-                     pair % g.hkv, smem);
+    const int widx = window_first ? bid : bid - worker_groups;
+    const int pair = widx / wparts;
+    window_pair<NCB == 8 ? 2 : NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws,
+                                    pair / g.hkv, pair % g.hkv, widx % wparts, wparts, smem);
     return;
   }
   if (window_first) bid -= nwin;
@@ -870,7 +882,7 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   const int run0 = worker * C;
   const int run1 = (int)min((long long)total, (long long)run0 + C);
   const int B = ws.batch;
-  const int max_splits = ws.nslots - 1;
+  const int max_splits = ws.max_splits();
   const int32_t* pstart = plan + kPlanHeader;
   const int32_t* npg = pstart + B;
   const int32_t* pglo = npg + B;
@@ -1134,8 +1146,8 @@ int resident_workers() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n > 0) return n;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  const int cus = current_device_cus();
+  int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)int2_decode_kernel<NCB>,
                                                    64 * kWaves, 0) != hipSuccess)
     per_cu = 0;
@@ -1164,28 +1176,30 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
   const int workers = num_workers > 0 ? num_workers
                                       : (G <= 4 ? resident_workers<1>() : resident_workers<8>());
   // Few pairs: their sink/window workgroups go first, so that they start at once instead of
-  // after the INT2 workers that fill the device, and the q rotation takes one workgroup per
-  // query head.
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 0;
+  // after the INT2 workers that fill the device, each pair's positions are cut into parts of
+  // kWinPartTokens (one workgroup each: a part's loads all go out in one round, where a whole
+  // window takes several dependent rounds), and the q rotation takes one workgroup per query
+  // head.  Many pairs: one window workgroup per pair, in the workers' tail.
+  const int cus = current_device_cus();
   const bool small = (long long)batch * g.hkv * 2 < cus;
   const int window_first = small ? 1 : 0;
+  const int wparts =
+      small ? max(1, min(kWinSlots, (g.num_sink + g.window + kWinPartTokens - 1) / kWinPartTokens))
+            : 1;
   const int hpw = small ? 1 : G;
   hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (G / hpw), batch + 1), dim3(kPrepThreads), 0,
                      stream, g, q, rot_k, hq, seq_lens, workers, hpw, ws);
   const int worker_groups = (workers + kWaves - 1) / kWaves;
-  const dim3 grid(worker_groups + batch * g.hkv);
+  const dim3 grid(worker_groups + batch * g.hkv * wparts);
   const int32_t* plan = ws.plan();
   if (G <= 4)
     hipLaunchKernelGGL(int2_decode_kernel<1>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
-                       worker_groups, window_first, ws);
+                       worker_groups, window_first, wparts, ws);
   else
     hipLaunchKernelGGL(int2_decode_kernel<8>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
-                       worker_groups, window_first, ws);
+                       worker_groups, window_first, wparts, ws);
   return hipGetLastError();
 }
 

@@ -184,14 +184,16 @@ __global__ __launch_bounds__(kT4, GMAX <= 4 ? 4 : 2) void int4_decode_kernel(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = t >> 4, k = t & 15, gi = k >> 2;
   const int G = hq / g.hkv;
-  const int max_splits = ws.nslots - 1;
+  const int max_splits = ws.max_splits();
   const int L = max(seq_lens[b], 0);
   const int P = (L + kPage - 1) / kPage;
   const int sp = max(split_pages, (P + max_splits - 1) / max_splits);
   const int nsplit = P == 0 ? 0 : (P + sp - 1) / sp;
-  if (s == 0) {  // the split count of this pair, and an empty BF16 slot (positions are here)
+  if (s == 0) {  // the split count of this pair, and empty window slots (positions are here)
     if (t == 0) ws.nvalid()[b * g.hkv + h] = nsplit;
-    if (t < G) *ws.ml(b, hq, h * G + t, ws.nslots - 1) = make_float2(kNegBig4, 0.f);
+    static_assert(GMAX * kWinSlots <= kT4, "one thread per empty window slot");
+    if (t < G * kWinSlots)
+      *ws.ml(b, hq, h * G + t / kWinSlots, ws.win_slot() + t % kWinSlots) = make_float2(kNegBig4, 0.f);
   }
   if (s >= nsplit) return;
 
@@ -377,7 +379,7 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
   if (batch == 0) return hipSuccess;
   hipError_t e = launch_prep_q(g, q, rot_k, batch, hq, seq_lens, ws, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid(ws.nslots - 1, g.hkv, batch);
+  const dim3 grid(ws.max_splits(), g.hkv, batch);
   if (hq / g.hkv <= 4)
     hipLaunchKernelGGL(int4_decode_kernel<4>, grid, dim3(kT4), 0, stream, g, pages, sinkwin,
                        block_table, slot_ids, hq, seq_lens, sm_scale, split_pages, ws);

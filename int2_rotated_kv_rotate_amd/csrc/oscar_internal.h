@@ -15,6 +15,10 @@ constexpr int kRecord = 1536;                 // bytes per (page, KV head) INT2 
 constexpr int kKCodes = 0, kVCodes = 512, kKMeta = 1024, kVMeta = 1280;
 constexpr int kBf16PageElems = 2 * kPage * kHeadDim;  // 4096 bf16 per (page, KV head)
 constexpr int kMaxSinkWindow = 256;   // S + W
+// The BF16 sink + window positions of a (sequence, KV head) pair are split into at most
+// kWinSlots parts of kWinPartTokens positions (or kept whole), each with its own partial slot.
+constexpr int kWinPartTokens = 32;
+constexpr int kWinSlots = kMaxSinkWindow / kWinPartTokens;
 
 // Workspace layout (all offsets in bytes from the workspace base).
 //   Q region:  per (b, j) a 1024-byte block
@@ -31,7 +35,8 @@ constexpr int kMaxSinkWindow = 256;   // S + W
 //     pages pstart[b] + h*npg[b] .. + npg[b] of the concatenation), npg[B] (INT2 pages per
 //     KV head of sequence b), pglo[B] (first logical INT2 page of sequence b), and
 //     nvalid[B][Hkv] (partial slots 0 .. nvalid-1 of the pair hold INT2 partials).
-//   Slot nslots - 1 of every (b, j) holds the BF16 sink/window partial.
+//   Slots 0 .. max_splits-1 of every (b, j) hold INT2 partials, the last kWinSlots slots
+//   (max_splits .. nslots-1) the BF16 sink/window partials; a slot with l = 0 is empty.
 constexpr int kQBlock = 1024;
 constexpr int kQHiOff = 512, kQLoOff = 640, kQScOff = 768, kQSumOff = 772;
 constexpr int kPlanHeader = 4;
@@ -39,7 +44,9 @@ constexpr int kPlanHeader = 4;
 struct Workspace {
   char* base;
   int batch;
-  int nslots;  // max_splits + 1 (the last slot holds the BF16 sink/window split)
+  int nslots;  // max_splits + kWinSlots
+  __host__ __device__ int max_splits() const { return nslots - kWinSlots; }
+  __host__ __device__ int win_slot() const { return nslots - kWinSlots; }  // first window slot
   size_t q_bytes, o_bytes, ml_bytes, plan_bytes;
   __host__ __device__ char* qblock(int b, int hq, int j) const {
     return base + ((size_t)b * hq + j) * kQBlock;
@@ -64,7 +71,7 @@ inline Workspace make_workspace(void* base, int batch, int hq, int max_splits) {
   Workspace w;
   w.base = (char*)base;
   w.batch = batch;
-  w.nslots = max_splits + 1;
+  w.nslots = max_splits + kWinSlots;
   w.q_bytes = (size_t)batch * hq * kQBlock;
   w.o_bytes = (size_t)batch * hq * w.nslots * kHeadDim * sizeof(float);
   w.ml_bytes = (size_t)batch * hq * w.nslots * sizeof(float2);
@@ -128,6 +135,10 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
 
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream);
+
+// Compute units of the current device, queried once per device and then read from a cache
+// (launch paths call it on every launch); 0 when the query fails.
+int current_device_cus();
 
 // One bf16 matrix-core instruction per tile (D = A . B + C): see oscar_mfma_bf16_tiles.
 hipError_t launch_mfma_bf16_tiles(const uint16_t* a, const uint16_t* b, const float* c, float* d,

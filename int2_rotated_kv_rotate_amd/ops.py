@@ -38,6 +38,9 @@ EXPORTED = (
 )
 
 STATIC_WORKSPACE_BYTES = 32 << 20   # OSCAR_STATIC_WORKSPACE_BYTES
+# Partial slots per (sequence, query head) that follow the max_splits INT2 slots in a decode
+# workspace: the BF16 sink/window parts (include/oscar.h, oscar_decode_workspace_bytes).
+WINDOW_SLOTS = 8
 
 
 class OscarError(RuntimeError):

@@ -43,7 +43,11 @@ def test_workspace_size(lib):
     # Q blocks, partial outputs and (m, l) per slot, then the work plan (4 header words,
     # three words per sequence, one per (sequence, head)) rounded up to 256 bytes
     plan = (4 * (4 + 3 * 64 + 64 * 32) + 255) // 256 * 256
-    assert ops.decode_workspace_bytes(64, 32, 12) == 64 * 32 * 1024 + 64 * 32 * 13 * (512 + 8) + plan
+    # per (sequence, query head): the query block, then max_splits INT2 slots and the window
+    # slots of 512 + 8 bytes each
+    assert ops.WINDOW_SLOTS == 8
+    assert ops.decode_workspace_bytes(64, 32, 12) == \
+        64 * 32 * 1024 + 64 * 32 * (12 + ops.WINDOW_SLOTS) * (512 + 8) + plan
     assert lib.oscar_decode_workspace_bytes(-1, 32, 12) == 0
     assert lib.oscar_decode_workspace_bytes(1, 32, 0) == 0
 

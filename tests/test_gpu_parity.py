@@ -249,13 +249,16 @@ def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
     """oscar_combine on seeded partials (not produced by the library) vs the oracle merge.
 
     Each (sequence, KV head) pair declares how many INT2 slots it filled (the plan's nvalid);
-    slots past that hold NaN outputs, a large m and an l of 7 or NaN, and must not be read."""
+    slots past that hold NaN outputs, a large m and an l of 7 or NaN, and must not be read.
+    The window slots that follow are all merged, some of them empty."""
     B, hq, hkv = 3, 8, 2
-    nslots = max_splits + 1
+    nslots = max_splits + ops.WINDOW_SLOTS
     G = hq // hkv
     valid = np.ones((B, nslots), bool)
     valid[0, 2] = False
     valid[0, 3:max_splits:7] = False
+    valid[0, max_splits + 1] = False         # an empty window part between two full ones
+    valid[0, max_splits + 5:] = False        # window parts the launch did not use
     valid[1, 1:] = False
     valid[2, :] = False                      # a row with no positions at all
     m, l, o = W.synthetic_partials(42, B, hq, nslots, valid)
@@ -285,7 +288,7 @@ def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     for b in range(B):
         for j in range(hq):
-            used = list(range(nvalid[b, j // G])) + [nslots - 1]
+            used = list(range(nvalid[b, j // G])) + list(range(max_splits, nslots))
             if not valid[b, used].any():
                 assert np.all(out[b, j] == 0) and lse[b, j] == -np.inf
                 continue

@@ -79,7 +79,7 @@ def test_static_workspace_refuses_oversized_requests():
     p = H.make_problem(w)
     cache = H.GpuCache(p)
     step = H.DecodeStep(cache, max_splits=8)
-    too_many = 1500   # 2 x 32 query heads x 1501 slots x 520 bytes > 32 MiB
+    too_many = 1500   # 2 x 32 query heads x 1508 slots x 520 bytes > 32 MiB
     assert ops.decode_workspace_bytes(2, w.num_q_heads, too_many) > ops.STATIC_WORKSPACE_BYTES
     sentinel = torch.full_like(step.out, 7.0)
     with pytest.raises(ops.OscarError) as e:
