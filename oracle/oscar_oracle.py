@@ -281,10 +281,21 @@ def meta_location(kind: str, r, g):
 
 
 # INT4 records (the INT4 abstract on the OSCAR paper's page: token-wise INT4 in a paged
-# layout).  2560 bytes per (page, KV head); 16 levels, two codes per byte, low nibble first:
-#   [   0, 1024)  K codes, token-major: channel c of slot r at byte 64*r + c/2, bits 4*(c % 2);
-#   [1024, 2048)  V codes, token-major as K: channel c of slot r at byte 1024 + 64*r + c/2,
-#                 bits 4*(c % 2);
+# layout).  2560 bytes per (page, KV head); 16 levels, 4 bits per code.  The arrangement of the
+# codes is this implementation's own (the pages fix none), chosen for matrix-core operands:
+#   [   0, 1024)  K codes in 16-byte lane chunks: chunk 16*q + r holds token slot r's channels
+#                 16q .. 16q+15 (bytes 0..7) and 64+16q .. 64+16q+15 (bytes 8..15).  Channel c
+#                 (h = c // 64, q = (c % 64) // 16, j = c % 16, i = j % 4) sits at byte
+#                 16*(16q + r) + 8h + 4*(i // 2) + j // 4, bits 4*(i % 2): masking the chunk's
+#                 dwords with 0x0F0F0F0F (shifted by 0 and 4) gives int8 vectors whose byte b of
+#                 vector i is channel 16q + 4b + i, the INT2 record's operand order.
+#   [1024, 2048)  V codes in 16-byte lane chunks: chunk 16*(r // 4) + (c % 16) holds channel
+#                 residue c % 16 of the four token slots 4*(r // 4) .. +3.  With nb = c // 16,
+#                 k = nb // 2, u = r % 4: byte 1024 + 16*chunk + 4k + 2*(u % 2) + u // 2, bits
+#                 4*(nb % 2).  Each token slot owns whole bytes; a dword shifted left by 3 or
+#                 right by 5 (right by 1 or 9) and masked with 0x00780078 holds column block
+#                 2k's (2k + 1's) codes of tokens 0, 1 (2, 3) of the quad at the mantissa bits of
+#                 two bf16 values 1 + code/16.
 #   [2048, 2304)  K scale/zero: fp16 pair of group g of slot r at 2048 + 16*r + 4*g;
 #   [2304, 2560)  V scale/zero, the same arrangement at 2304.
 LEVELS4 = 16
@@ -293,11 +304,17 @@ K4_CODES, V4_CODES, K4_META, V4_META = 0, 1024, 2048, 2304
 
 
 def k4_code_location(r, c):
-    return K4_CODES + 64 * r + c // 2, 4 * (c % 2)
+    """(byte offset, bit offset) of K channel c of slot r in an INT4 record; elementwise."""
+    h, q, j = c // 64, (c % 64) // 16, c % 16
+    i = j % 4
+    return K4_CODES + 16 * (16 * q + r) + 8 * h + 4 * (i // 2) + j // 4, 4 * (i % 2)
 
 
 def v4_code_location(r, c):
-    return V4_CODES + 64 * r + c // 2, 4 * (c % 2)
+    """(byte offset, bit offset) of V channel c of slot r in an INT4 record; elementwise."""
+    nb, u = c // 16, r % 4
+    chunk = 16 * (r // 4) + c % 16
+    return V4_CODES + 16 * chunk + 4 * (nb // 2) + 2 * (u % 2) + u // 2, 4 * (nb % 2)
 
 
 def meta4_location(kind: str, r, g):
