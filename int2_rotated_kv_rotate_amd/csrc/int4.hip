@@ -4,9 +4,17 @@
 // Cache Quantization") finds token-wise INT4 with a rotation the serving-compatible choice at 4
 // bits; this file carries that codec through the same paged path.
 //
-// Record (2560 bytes; codes two per byte, the even channel in the low nibble):
-//   [   0, 1024)  K codes, token-major: channel c of slot r at byte 64 r + c / 2;
-//   [1024, 2048)  V codes, token-major as K: channel c of slot r at byte 1024 + 64 r + c / 2;
+// Record (2560 bytes, 4-bit codes; the arrangement is this implementation's own, made for the
+// matrix-core operands):
+//   [   0, 1024)  K codes in 16-byte lane chunks: chunk 16 q + r holds slot r's channels
+//                 16q .. 16q+15 (bytes 0..7) and 64+16q .. (bytes 8..15); channel c (h = c/64,
+//                 q = (c%64)/16, j = c%16, i = j%4) at byte 16 (16q + r) + 8h + 4 (i/2) + j/4,
+//                 bits 4 (i%2), so the 0x0F0F0F0F masks of a chunk give the INT2 record's int8
+//                 operand order (byte b of vector i = channel 16q + 4b + i);
+//   [1024, 2048)  V codes in 16-byte lane chunks: chunk 16 (r/4) + c%16, dword nb/2 (nb = c/16),
+//                 byte 2 (u%2) + u/2 of it (u = r%4: each slot owns whole bytes), nibble nb%2;
+//                 shifts of a dword by +3 / -5 (-1 / -9) masked with 0x00780078 give column
+//                 block 2k's (2k+1's) codes of tokens 0,1 / 2,3 as bf16 1 + code/16 mantissas;
 //   [2048, 2304)  K (fp16 scale, fp16 zero) of group g of slot r at 2048 + 16 r + 4 g;
 //   [2304, 2560)  V (scale, zero), the same arrangement.
 // Quantiser: s = fp16(fp32(c mx - c mn) / 15), z = fp16(c mn), code = clamp(rint((y - z) / s),
@@ -148,16 +156,31 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
   }
   __syncthreads();
 
-  // packing: code words (thread -> row t / 16, word t % 16: channels 8w .. 8w + 7), BF16 copies
+  // packing (thread -> row t / 16, w = t % 16), BF16 copies.  K: w = 4 q + d is dword d of the
+  // row's chunk q, byte b = channels 64 (d/2) + 16 q + 4 b + 2 (d%2) and + 1 (low, high nibble).
+  // V: w is the channel residue; the row owns byte 2 (u%2) + u/2 of each dword k of chunk
+  // 16 (slot/4) + w, the codes of channels 32 k + w (low nibble) and 32 k + 16 + w (high).
   {
     const int r = t / 16, w = t % 16;
     const RowInfo info = s_info[r];
     if (r < nrows && info.rec >= 0) {
-      uint32_t word = 0;
+      const int sl = info.slot_in_page;
+      if (!is_v) {
+        const int q = w >> 2, d = w & 3;
+        const int cb = 64 * (d >> 1) + 16 * q + 2 * (d & 1);
+        uint32_t word = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) word |= (uint32_t)s_code[r][8 * w + i] << (4 * i);
-      *reinterpret_cast<uint32_t*>(pages + info.rec + (is_v ? kV4Codes : kK4Codes) +
-                                   64 * info.slot_in_page + 4 * w) = word;
+        for (int b = 0; b < 4; ++b)
+          word |= ((uint32_t)s_code[r][cb + 4 * b] | ((uint32_t)s_code[r][cb + 4 * b + 1] << 4))
+                  << (8 * b);
+        *reinterpret_cast<uint32_t*>(pages + info.rec + kK4Codes + 16 * (16 * q + sl) + 4 * d) = word;
+      } else {
+        const int u = sl & 3;
+        uint8_t* chunk = pages + info.rec + kV4Codes + 16 * (16 * (sl >> 2) + w) + 2 * (u & 1) + (u >> 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          chunk[4 * k] = (uint8_t)(s_code[r][32 * k + w] | (s_code[r][32 * k + 16 + w] << 4));
+      }
     }
     if (r < nrows && info.sw >= 0) {
       const float* yr = &s_y[r][8 * w];
@@ -251,8 +274,25 @@ __global__ __launch_bounds__(kT4, GMAX <= 4 ? 4 : 2) void int4_decode_kernel(
     const int id = pg < g.max_pages ? bt[pg] : -1;
     if (id < 0 || id >= g.num_pages) return f;
     const uint8_t* rec = pages + ((size_t)id * g.hkv + h) * kRecord4;
-    f.ku.x = *reinterpret_cast<const uint32_t*>(rec + kK4Codes + 64 * r + 4 * k);
-    f.vu.x = *reinterpret_cast<const uint32_t*>(rec + kV4Codes + 64 * r + 4 * k);
+    // this lane's 8 channels 8k .. 8k+7 of slot r as one word, channel 8k + m at bits 4m.
+    // K: bytes 2 (k%2) and 2 (k%2) + 1 of the two dwords of chunk 16 ((k%8)/2) + r, half k/8
+    // (channels m = 0, 1, 4, 5 in the first dword, 2, 3, 6, 7 in the second).
+    {
+      const uint2 d = *reinterpret_cast<const uint2*>(rec + kK4Codes + 16 * (16 * ((k & 7) >> 1) + r) +
+                                                      8 * (k >> 3));
+      const uint32_t x = (d.x >> (16 * (k & 1))) & 0xFFFFu, y = (d.y >> (16 * (k & 1))) & 0xFFFFu;
+      f.ku.x = (x & 0xFFu) | ((y & 0xFFu) << 8) | ((x >> 8) << 16) | ((y >> 8) << 24);
+    }
+    // V: channel 8k + m is residue 8 (k%2) + m of column block k/2: one byte per channel.
+    {
+      const int u = r & 3, e = (k >> 1) & 1;
+      const uint8_t* vb = rec + kV4Codes + 16 * (16 * (r >> 2) + 8 * (k & 1)) + 4 * (k >> 2) +
+                          2 * (u & 1) + (u >> 1);
+      uint32_t word = 0;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) word |= (((uint32_t)vb[16 * m] >> (4 * e)) & 15u) << (4 * m);
+      f.vu.x = word;
+    }
     f.km = *reinterpret_cast<const uint32_t*>(rec + kK4Meta + 16 * r + 4 * gi);
     f.vm = *reinterpret_cast<const uint32_t*>(rec + kV4Meta + 16 * r + 4 * gi);
     f.kind = 2;
