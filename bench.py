@@ -353,7 +353,7 @@ def int2_vs_bf16(n_iter: int, samples: dict):
     log(f"qwen3_4b B=1: INT2 {ms_i:.4f} ms, BF16 {ms_b:.4f} ms; from graphs INT2 "
         f"{g4[0]:.4f} ms, BF16 {g4_b[0]:.4f} ms")
 
-    # The INT4 variant (2560-byte records, vector-ALU decode) at the Qwen3-8B batch-64 shape
+    # The INT4 variant (2560-byte records, matrix-core decode) at the Qwen3-8B batch-64 shape
     w8 = W.WORKLOADS["qwen3_8b_b64"]
     p8 = H.make_problem(w8)
     c4 = H.GpuCache(p8, bits=4)
@@ -371,7 +371,8 @@ def int2_vs_bf16(n_iter: int, samples: dict):
           w8.batch * w8.num_q_heads * 128 * (2 + 4) + 4 * int(((lens + 15) // 16).sum()))
     res["int4_qwen3_8b_b64"] = {"ms": round(ms4, 4), "tokens_per_s": round(w8.batch / ms4 * 1e3, 1),
                                 "bytes": int(b4), "effective_gbps": round(b4 / (ms4 * 1e-3) / 1e9, 1),
-                                "decode": "vector ALUs, one workgroup per (split, KV head, sequence)"}
+                                "decode": "matrix cores: int8 logits, bf16 P.V, stream-K workers over "
+                                          "2560-byte pages in a two-page LDS ring"}
     log(f"INT4 qwen3_8b B=64: {ms4:.4f} ms ({b4 / (ms4 * 1e-3) / 1e9:.0f} GB/s)")
     del st4, c4
     del scrub

@@ -195,10 +195,14 @@ int32_t oscar_rotate_quantize_append_hadamard(
  * code = clamp(rint((y - z) / s), 0, 15) (0 when s == 0).  Token-wise INT4 with a rotation is the
  * serving-compatible 4-bit design of the INT4 abstract on the OSCAR paper's page ("OSCAR:
  * Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache Quantization").
- * The pool is uint8 [num_pages][Hkv][2560]; within a record (slot r, channel c, group g; two
- * codes per byte, the even channel in the low nibble):
- *   [   0, 1024)  K codes at byte 64*r + c/2;
- *   [1024, 2048)  V codes at byte 1024 + 64*r + c/2;
+ * The pool is uint8 [num_pages][Hkv][2560]; within a record (slot r, channel c, group g; 4-bit
+ * codes, an arrangement made for matrix-core operands):
+ *   [   0, 1024)  K codes in 16-byte chunks: chunk 16*q + r holds slot r's channels 16q..16q+15
+ *                 and 64+16q..64+16q+15; with h = c/64, q = (c%64)/16, j = c%16, i = j%4,
+ *                 channel c is at byte 16*(16q + r) + 8h + 4*(i/2) + j/4, bits 4*(i%2);
+ *   [1024, 2048)  V codes in 16-byte chunks: chunk 16*(r/4) + c%16; with nb = c/16, u = r%4,
+ *                 channel c is at byte 1024 + 16*chunk + 4*(nb/2) + 2*(u%2) + u/2, bits
+ *                 4*(nb%2) (each slot owns whole bytes);
  *   [2048, 2304)  K (fp16 scale, fp16 zero) at 2048 + 16*r + 4*g;
  *   [2304, 2560)  V (scale, zero) at 2304 + 16*r + 4*g.
  * Arguments, validation and errors as oscar_rotate_quantize_append_ex (no method choice: the
@@ -215,11 +219,16 @@ int32_t oscar_int4_rotate_quantize_append(
 
 /*
  * Decode attention over an INT4 cache, written in the workspace format of
- * oscar_decode_attention and finished by oscar_combine with the same rot_v.  Sequence b's pages
- * are cut into splits of max(split_pages, ceil(P_b / max_splits)) pages (P_b = ceil(L_b / 16));
- * each split attends over all of its positions (INT4 records and BF16 sink/window rows) on the
- * vector ALUs.  Arguments, validation and errors as oscar_decode_attention, with split_pages
- * (>= 1) in place of num_workers.
+ * oscar_decode_attention and finished by oscar_combine with the same rot_v.
+ * G = num_q_heads / Hkv <= 4: the work split of oscar_decode_attention (equal runs of INT4
+ * pages per worker wavefront, one per resident slot; at most max_splits partials per (sequence,
+ * KV head); the BF16 sink/window positions as extra partials) on the matrix cores; split_pages
+ * is not used.
+ * G = 8: sequence b's pages are cut into splits of max(split_pages, ceil(P_b / max_splits))
+ * pages (P_b = ceil(L_b / 16)); each split attends over all of its positions (INT4 records and
+ * BF16 sink/window rows) on the vector ALUs.
+ * Arguments, validation and errors as oscar_decode_attention, with split_pages (>= 1) in place
+ * of num_workers.
  */
 int32_t oscar_int4_decode_attention(
     const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,

@@ -1137,6 +1137,336 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
   }
 }
 
+// ------------------------------------------------------------------ INT4 pages, matrix cores
+//
+// The INT4 variant's decode for G <= 4 (the INT4 abstract on the OSCAR paper's page: token-wise
+// INT4 through the same paged path).  The same workers, plan, q' encoding, sink/window role and
+// partial format as int2_decode_kernel<1>; what changes is the page: 2560-byte records copied
+// one page at a time into a two-page LDS ring (three direct-to-LDS loads per page, the next page
+// in flight while one is computed), K codes read as int8 operands with two nibble masks (the
+// record keeps the INT2 operand order, so q' is encoded once for both), and P.V per page on
+// v_mfma_f32_16x16x16_bf16 with V codes as bf16 1 + code/16 built from one shift and one AND-OR
+// per two tokens (every column block scales by 16).
+
+constexpr int kPage4Bytes = 2560;
+constexpr int kRing4Bytes = 2 * kPage4Bytes;
+constexpr size_t kSmem4Bytes = (size_t)kWaves * kRing4Bytes + (size_t)kWaves * sizeof(WTile<1>);
+static_assert((kMaxSinkWindow * 4 + 2 * 4 + 4 * kHeadDim) * sizeof(float) <= kSmem4Bytes,
+              "window scratch exceeds the INT4 workgroup's shared memory");
+
+// Copy the record at rec (uniform) into the page slot at LDS offset ps: bytes [0, 1024) and
+// [1024, 2048) by full-wave loads, [2048, 2560) by lanes 0..31 (exec restricted inside the
+// statement and restored before it ends).  Lane l's 16 bytes land at M0 + 16 l; v0 = 16 l.
+__device__ __forceinline__ void dma_page4(const uint8_t* rec, uint32_t ps, uint32_t v0) {
+  uint64_t saved;
+  const uint32_t ps1 = __builtin_amdgcn_readfirstlane(ps + 0x400u);
+  const uint32_t ps2 = __builtin_amdgcn_readfirstlane(ps + 0x800u);
+  asm volatile(
+      "s_mov_b32 m0, %[ps]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v0], %[a]\n\t"
+      "s_mov_b32 m0, %[ps1]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v1], %[a]\n\t"
+      "s_mov_b32 m0, %[ps2]\n\t"
+      "s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b32 exec_hi, 0\n\t"
+      "global_load_lds_dwordx4 %[v2], %[a]\n\t"
+      "s_mov_b64 exec, %[sv]"
+      : [sv] "=&s"(saved)
+      : [ps] "s"(ps), [ps1] "s"(ps1), [ps2] "s"(ps2), [v0] "v"(v0), [v1] "v"(v0 + 1024u),
+        [v2] "v"(v0 + 2048u), [a] "s"(rec)
+      : "memory", "m0");
+}
+
+// Wait until at most N pages' copies (3 loads each) are still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_pages4() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * N) : "memory");
+}
+
+// This lane's view of a page slot: its K chunk (quarter r, token t) and the K (scale, zero) of
+// token t; then the V (scale, zero) of token t and its V chunk (token quad r, channel residue
+// t).  a16l = 16 lane, a16t = 16 t.
+__device__ __forceinline__ void read_page4_k(uint32_t ps, uint32_t a16l, uint32_t a16t,
+                                             uint4& kc, uint4& km) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kc), "=&v"(km)
+      : "v"(ps + a16l), "v"(ps + a16t)
+      : "memory");
+}
+__device__ __forceinline__ void read_page4_v(uint32_t ps, uint32_t a16l, uint32_t a16t,
+                                             uint4& vm, uint4& vc) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:2304\n\t"
+      "ds_read_b128 %1, %2 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vm), "=&v"(vc)
+      : "v"(ps + a16l), "v"(ps + a16t)
+      : "memory");
+}
+
+// Logit of head r, token t in units of cscale (as page_logits<1>): the chunk's dwords masked
+// with 0x0F0F0F0F at shifts 0 and 4 are the two int8 K operands.
+template <bool MASKED>
+__device__ __forceinline__ float page4_logit(uint4 kc, uint4 km, bool live, const QOperands<1>& qo,
+                                             uint32_t m4) {
+  const v4i ka0 = (v4i){(int)(kc.x & m4), (int)((kc.x >> 4) & m4), (int)(kc.y & m4),
+                        (int)((kc.y >> 4) & m4)};
+  const v4i ka1 = (v4i){(int)(kc.z & m4), (int)((kc.z >> 4) & m4), (int)(kc.w & m4),
+                        (int)((kc.w >> 4) & m4)};
+  v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
+  dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0][0], ka0, dh, 0, 0, 0);
+  dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0][1], ka1, dh, 0, 0, 0);
+  dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0][0], ka0, dl, 0, 0, 0);
+  dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0][1], ka1, dl, 0, 0, 0);
+  const uint32_t kmw[4] = {km.x, km.y, km.z, km.w};
+  float x = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    // |dh| <= 127 * 15 * 32 per group: 254 dh + dl stays below 2^24, exact in fp32
+    const int dint = __mul24(dh[g], 254) + dl[g];
+    x = fmaf(f16lo(kmw[g]), (float)dint, x);
+    x = fmaf(f16hi(kmw[g]), qo.qs[0][g], x);
+  }
+  if (MASKED) x = live ? x : -INFINITY;
+  return x;
+}
+
+// One page in the slot at ps: logits, weights into the tile (columns 0..15), P.V and the weight
+// sums.  after_reads() runs once the slot's LDS reads have completed (the copy of a later page
+// into the slot goes there).
+template <bool MASKED, bool FIRST, class AfterReads>
+__device__ __forceinline__ void int4_page(uint32_t ps, uint32_t a16l, uint32_t a16t, bool live,
+                                          const QOperands<1>& qo, SplitState<1>& st,
+                                          WTile<1>& tile, int t, int r, uint32_t m4,
+                                          uint32_t mask_v, uint32_t magic, v4s ones,
+                                          bool fixed_ref, AfterReads&& after_reads) {
+  uint4 kc, km;
+  read_page4_k(ps, a16l, a16t, kc, km);
+  float a[1];
+  a[0] = page4_logit<MASKED>(kc, km, live, qo, m4);
+  st.mlane[0] = fmaxf(st.mlane[0], a[0]);
+  if (FIRST && !fixed_ref) st.mref[0] = fmaxf(row_max16(a[0]) * qo.cscale[0], kNegBig);
+  uint4 vm, vc;
+  read_page4_v(ps, a16l, a16t, vm, vc);
+  after_reads();
+  page_weights<1, MASKED>(a, vm, live, qo, st, tile, t, r, 0);
+  // A operands: row t of the tile, tokens 4r .. 4r + 3
+  const uint2 h2 = *reinterpret_cast<const uint2*>(&tile.w[0][0][t][4 * r]);
+  const uint2 l2 = *reinterpret_cast<const uint2*>(&tile.w[0][1][t][4 * r]);
+  const v4s ahi = __builtin_bit_cast(v4s, h2), alo = __builtin_bit_cast(v4s, l2);
+  const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = vw[k];
+    // column block 2k: tokens (0, 1) from w << 3, (2, 3) from w >> 5; block 2k + 1: w >> 1, w >> 9
+    const v4s b0 = __builtin_bit_cast(v4s, make_uint2(and_or(w << 3, mask_v, magic),
+                                                      and_or(w >> 5, mask_v, magic)));
+    const v4s b1 = __builtin_bit_cast(v4s, make_uint2(and_or(w >> 1, mask_v, magic),
+                                                      and_or(w >> 9, mask_v, magic)));
+    st.acc[0][2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b0, st.acc[0][2 * k], 0, 0, 0);
+    st.acc[0][2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b0, st.acc[0][2 * k], 0, 0, 0);
+    st.acc[0][2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b1, st.acc[0][2 * k + 1], 0, 0, 0);
+    st.acc[0][2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b1, st.acc[0][2 * k + 1], 0, 0, 0);
+  }
+  st.wsum[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, ones, st.wsum[0], 0, 0, 0);
+  st.wsum[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, ones, st.wsum[0], 0, 0, 0);
+}
+
+// grid: worker_groups INT2-style worker workgroups (kWaves workers each) and batch * Hkv *
+// wparts sink/window workgroups, ordered as in int2_decode_kernel.
+__global__ __launch_bounds__(64 * kWaves) void int4_decode_mfma_kernel(
+    CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ plan, float sm_scale,
+    int worker_groups, int window_first, int wparts, Workspace ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem4Bytes];
+  int bid = blockIdx.x;
+  const int nwin = ws.batch * g.hkv * wparts;
+  if (window_first ? bid < nwin : bid >= worker_groups) {
+    const int widx = window_first ? bid : bid - worker_groups;
+    const int pair = widx / wparts;
+    window_pair<1>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
+                   pair % g.hkv, widx % wparts, wparts, smem);
+    return;
+  }
+  if (window_first) bid -= nwin;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = bid * kWaves + wave;
+  const int t = lane & 15, r = lane >> 4;
+  WTile<1>& tile = *reinterpret_cast<WTile<1>*>(smem + (size_t)kWaves * kRing4Bytes +
+                                                wave * sizeof(WTile<1>));
+  const uint32_t ring0 = lds_offset(smem + (size_t)wave * kRing4Bytes);
+  const uint32_t a16l = 16 * lane, a16t = 16 * t;
+
+  const int total = plan[0], C = plan[1];
+  if ((long long)worker * C >= total) return;
+  __builtin_amdgcn_s_setprio(3);
+  const int band_len = max(C / 4, 1);
+  int band_left = band_len, band = 0;
+  const int run0 = worker * C;
+  const int run1 = (int)min((long long)total, (long long)run0 + C);
+  const int B = ws.batch;
+  const int max_splits = ws.max_splits();
+  const int32_t* pstart = plan + kPlanHeader;
+  const int32_t* npg = pstart + B;
+  const int32_t* pglo = npg + B;
+  int b = 0;
+  {
+    int len = B;
+    while (len > 1) {
+      const int step = (len + 63) / 64;
+      const bool probe = lane * step < len;
+      const int v = pstart[probe ? b + lane * step : b];
+      const bool ok = probe && v <= run0;
+      const int last = 63 - __clzll(__ballot(ok));
+      b += last * step;
+      len = min(step, len - last * step);
+    }
+  }
+  const int G = hq / g.hkv;
+  const float sm_log2 = sm_scale * kLog2e;
+  const size_t rec_stride = (size_t)g.hkv * kPage4Bytes;
+  const uint32_t last_page = (uint32_t)(g.num_pages - 1);
+  uint32_t m4 = 0x0F0F0F0Fu, mask_v = 0x00780078u, magic = 0x3F803F80u;
+  asm volatile("" : "+s"(m4));
+  asm volatile("" : "+s"(mask_v));
+  asm volatile("" : "+v"(magic));
+  const v4s ones = __builtin_bit_cast(v4s, make_uint2(0x3F803F80u, 0x3F803F80u));  // bf16 1.0
+
+  int pos = run0;
+  while (true) {
+    const int P = npg[b];
+    const int rel = pos - pstart[b];
+    const int h = rel / P;
+    const int pair0 = pstart[b] + h * P;
+    const int seg_end = min(run1, pair0 + P);
+    const int slot = worker - pair0 / C;
+    const int pgA = pglo[b] + (pos - pair0), pgB = pgA + (seg_end - pos);
+
+    const int L = max(seq_lens[b], 0);
+    const int n_sink = min(L, g.num_sink);
+    const int lo = n_sink, hi = L - min(g.window, L - n_sink);
+
+    QOperands<1> qo;
+    {
+      const int ja = t >> 2, ga = t & 3;
+      const char* blka = ws.qblock(b, hq, h * G + (ja < G ? ja : 0));
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int dw = 4 * m + r;
+        const bool use = ja < G && (dw >> 1) == ga;
+        const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * dw);
+        const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * dw);
+        const v4i zero = {0, 0, 0, 0};
+        qo.hi[0][m] = use ? zh : zero;
+        qo.lo[0][m] = use ? zl : zero;
+      }
+      const int jd = r;
+      const char* blkd = ws.qblock(b, hq, h * G + (jd < G ? jd : 0));
+      const float qsc = jd < G ? *reinterpret_cast<const float*>(blkd + kQScOff) : 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        qo.qs[0][gg] = jd < G ? reinterpret_cast<const float*>(blkd + kQSumOff)[gg] : 0.f;
+      qo.cscale[0] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
+    }
+
+    const int32_t* bt = block_table + (size_t)b * g.max_pages;
+    const uint8_t* pages_h = pages + (size_t)h * kPage4Bytes;
+    SplitState<1> st;
+    st.mref[0] = kNegBig;
+#pragma nounroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool fixed_ref = pass > 0;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) st.acc[0][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+      st.lsum[0] = 0.f;
+      st.mlane[0] = -INFINITY;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) st.zp[0][gg] = 0.f;
+      st.wsum[0] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+      // Pages pgA .. pgB-1, two in flight; page ids from uniform (scalar) loads one page ahead
+      // of their copy.  An id outside the pool reads the pool's last page (memory safety).
+      const int np = pgB - pgA;
+      auto pslot = [&](int k) { return ring0 + (uint32_t)(k & 1) * kPage4Bytes; };
+      auto rec_of = [&](int id) {
+        return pages_h + (size_t)min((uint32_t)id, last_page) * rec_stride;
+      };
+      auto live_at = [&](int q) {
+        const int p = q * kPage + t;
+        return q < pgB && p >= lo && p < hi;
+      };
+      int pf = bt[pgA];
+      dma_page4(rec_of(pf), pslot(0), a16l);
+      if (np > 1) {
+        pf = bt[pgA + 1];
+        dma_page4(rec_of(pf), pslot(1), a16l);
+      }
+      pf = np > 2 ? bt[pgA + 2] : 0;
+      for (int k = 0; k < np; ++k) {
+        if (k + 1 < np) wait_pages4<1>();
+        else wait_pages4<0>();
+        auto next = [&] {  // the slot just read takes page k + 2
+          if (k + 2 < np) {
+            dma_page4(rec_of(pf), pslot(k), a16l);
+            pf = k + 3 < np ? bt[pgA + k + 3] : 0;
+          }
+        };
+        if (--band_left <= 0) {
+          band_left += band_len;
+          lower_priority(++band);
+        }
+        const int q = pgA + k;
+        if (k == 0)
+          int4_page<true, true>(pslot(k), a16l, a16t, live_at(q), qo, st, tile, t, r, m4, mask_v,
+                                magic, ones, fixed_ref, next);
+        else if (k == np - 1)
+          int4_page<true, false>(pslot(k), a16l, a16t, live_at(q), qo, st, tile, t, r, m4, mask_v,
+                                 magic, ones, fixed_ref, next);
+        else
+          int4_page<false, false>(pslot(k), a16l, a16t, true, qo, st, tile, t, r, m4, mask_v,
+                                  magic, ones, fixed_ref, next);
+      }
+
+      // A logit beyond the reference margin: recompute once with the exact max (rare path).
+      const float mexact = row_max16(st.mlane[0]) * qo.cscale[0];
+      const bool redo = mexact > st.mref[0] + kRefMargin;
+      if (pass > 0 || !__any(redo)) break;
+      st.mref[0] = mexact;
+    }
+
+    // Finish (as int2_decode_kernel<1>): o'[c] = 16 (acc - sum_t W_t) + sum_t p_t z_t.
+    {
+      const float lt = row_sum16(st.lsum[0]);
+      float zt[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) zt[gg] = row_sum16(st.zp[0][gg]);
+      const int j = r;
+      if (j < G && (unsigned)slot < (unsigned)max_splits) {
+        float* o = ws.o(b, hq, h * G + j, slot);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int gg = nb >> 1;
+          o[16 * nb + t] = fmaf(16.0f, st.acc[0][nb][gg] - st.wsum[0][gg], zt[gg]);
+        }
+        if (t == 0) *ws.ml(b, hq, h * G + j, slot) = make_float2(st.mref[0], lt);
+      }
+    }
+
+    pos = seg_end;
+    if (pos >= run1) break;
+    if (h == g.hkv - 1) {
+      do { ++b; } while (b < B - 1 && npg[b] == 0);
+    }
+  }
+}
+
 // Resident worker waves of int2_decode_kernel<NCB> on the current device (cached per device).
 template <int NCB>
 int resident_workers() {
@@ -1149,6 +1479,24 @@ int resident_workers() {
   const int cus = current_device_cus();
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)int2_decode_kernel<NCB>,
+                                                   64 * kWaves, 0) != hipSuccess)
+    per_cu = 0;
+  n = max(cus, 1) * max(per_cu, 1) * kWaves;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Resident worker waves of int4_decode_mfma_kernel on the current device (cached per device).
+int int4_resident_workers() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  const int cus = current_device_cus();
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)int4_decode_mfma_kernel,
                                                    64 * kWaves, 0) != hipSuccess)
     per_cu = 0;
   n = max(cus, 1) * max(per_cu, 1) * kWaves;
@@ -1200,6 +1548,33 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
     hipLaunchKernelGGL(int2_decode_kernel<8>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
                        worker_groups, window_first, wparts, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_int4_mfma_decode(const CacheGeom& g, const uint8_t* pages,
+                                  const uint16_t* sinkwin, const int32_t* block_table,
+                                  const int32_t* slot_ids, int batch, int hq, const uint16_t* q,
+                                  const int32_t* seq_lens, const float* rot_k, float sm_scale,
+                                  const Workspace& ws, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const int G = hq / g.hkv;
+  if (G > 4) return hipErrorInvalidValue;
+  const int workers = int4_resident_workers();
+  // Launch shape as for the INT2 pages (launch_decode).
+  const int cus = current_device_cus();
+  const bool small = (long long)batch * g.hkv * 2 < cus;
+  const int window_first = small ? 1 : 0;
+  const int wparts =
+      small ? max(1, min(kWinSlots, (g.num_sink + g.window + kWinPartTokens - 1) / kWinPartTokens))
+            : 1;
+  const int hpw = small ? 1 : G;
+  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (G / hpw), batch + 1), dim3(kPrepThreads), 0,
+                     stream, g, q, rot_k, hq, seq_lens, workers, hpw, ws);
+  const int worker_groups = (workers + kWaves - 1) / kWaves;
+  const dim3 grid(worker_groups + batch * g.hkv * wparts);
+  hipLaunchKernelGGL(int4_decode_mfma_kernel, grid, dim3(64 * kWaves), 0, stream, g, pages,
+                     sinkwin, block_table, slot_ids, hq, seq_lens, ws.plan(), sm_scale,
+                     worker_groups, window_first, wparts, ws);
   return hipGetLastError();
 }
 

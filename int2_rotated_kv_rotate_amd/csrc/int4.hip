@@ -24,7 +24,8 @@
 // Kernels:
 //   int4_append_kernel  16 new rows of one (KV head, K|V) per workgroup, fp64 rotation on the
 //                       vector ALUs (R staged in LDS), quantisation, packing, BF16 copies;
-//   int4_decode_kernel  one workgroup per (split, KV head, sequence): every position of the
+//   int4_decode_kernel  (G = 8; G <= 4 runs int4_decode_mfma_kernel on the matrix cores, in
+//                       decode.hip) one workgroup per (split, KV head, sequence): every position of the
 //                       split, INT4 or BF16 sink/window, on the vector ALUs; each of the 16
 //                       token lanes keeps its own running softmax (rescaled only when its max
 //                       grows) and the 16 are merged at the end; the next page's words are
@@ -417,6 +418,9 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
                               const float* rot_k, float sm_scale, int split_pages,
                               const Workspace& ws, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
+  if (hq / g.hkv <= 4)   // the matrix-core kernel (stream-K workers; split_pages unused)
+    return launch_int4_mfma_decode(g, pages, sinkwin, block_table, slot_ids, batch, hq, q,
+                                   seq_lens, rot_k, sm_scale, ws, stream);
   hipError_t e = launch_prep_q(g, q, rot_k, batch, hq, seq_lens, ws, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(ws.max_splits(), g.hkv, batch);

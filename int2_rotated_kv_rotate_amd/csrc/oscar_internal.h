@@ -136,6 +136,13 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream);
 
+// INT4 pages on the matrix cores (G <= 4): the INT2 launch shape with 2560-byte pages.
+hipError_t launch_int4_mfma_decode(const CacheGeom& g, const uint8_t* pages,
+                                  const uint16_t* sinkwin, const int32_t* block_table,
+                                  const int32_t* slot_ids, int batch, int hq, const uint16_t* q,
+                                  const int32_t* seq_lens, const float* rot_k, float sm_scale,
+                                  const Workspace& ws, hipStream_t stream);
+
 // Compute units of the current device, queried once per device and then read from a cache
 // (launch paths call it on every launch); 0 when the query fails.
 int current_device_cus();
