@@ -145,10 +145,11 @@ def cpu_baseline(p, target_s: float):
             "blas_threads": 1}
 
 
-def oracle_pair(p, b: int, h: int):
+def oracle_pair(p, b: int, h: int, bits: int = 2):
     """The CPU oracle's decode of one (sequence, KV head) pair of a problem: its cache built by
     the same appends as the GPU run (the context, then the decoded token) and decode attention
-    for the pair's query heads.  Returns (out [G][128], lse [G])."""
+    for the pair's query heads; bits 2 (INT2 records) or 4 (INT4).  Returns (out [G][128],
+    lse [G])."""
     from oracle import oscar_oracle as O
     from int2_rotated_kv_rotate_amd import harness as H
     from int2_rotated_kv_rotate_amd import workload as W
@@ -157,7 +158,7 @@ def oracle_pair(p, b: int, h: int):
     G = w.group
     kb, vb = W.sequence_kv(w, b, L, offsets=W.key_offsets(w), outliers=W.outlier_channels(w),
                            needle=W.needle_site(w, p.lens), q_bits=p.q)
-    oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window)
+    oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window, bits=bits)
     args = (p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
     oc.append(p.table[b], b, 0, kb[:L - 1, h:h + 1], vb[:L - 1, h:h + 1], *args)
     oc.append(p.table[b], b, L - 1, kb[L - 1:, h:h + 1], vb[L - 1:, h:h + 1], *args)
@@ -247,8 +248,8 @@ def int2_vs_bf16(n_iter: int, samples: dict):
       * Qwen3-4B layer shape, batch 1, context 32768: latency of each;
       * long-context layer (32 query / 8 KV heads), batch 1, context 131072: latency of each;
       * the INT4 variant at the Qwen3-8B batch-64 shape.
-    samples receives, per INT2 workload, the GPU outputs of one (sequence, KV head) pair for the
-    oracle comparison of the CPU-baseline leg."""
+    samples receives, per INT2 workload and for the INT4 one, the GPU outputs of one (sequence,
+    KV head) pair for the oracle comparison of the CPU-baseline leg."""
     import torch
     from int2_rotated_kv_rotate_amd import harness as H
     from int2_rotated_kv_rotate_amd import workload as W
@@ -288,7 +289,7 @@ def int2_vs_bf16(n_iter: int, samples: dict):
         h = w.num_kv_heads - 1
         G = w.group
         samples[w.name] = (p, b, h, step.out[b, h * G:(h + 1) * G].cpu().numpy(),
-                           step.lse[b, h * G:(h + 1) * G].cpu().numpy())
+                           step.lse[b, h * G:(h + 1) * G].cpu().numpy(), 2)
         del step, cache
         return p, ms, pool, graph_ms
 
@@ -363,6 +364,10 @@ def int2_vs_bf16(n_iter: int, samples: dict):
     st4.run()
     torch.cuda.synchronize()
     ms4, _, _ = time_scrubbed(st4.attend, n_iter, scrub)
+    # one (sequence, KV head) pair of the timed INT4 cache for the oracle comparison
+    b4i, h4i, G8 = int(np.argmax(p8.lens)), w8.num_kv_heads - 1, w8.group
+    samples["int4_" + w8.name] = (p8, b4i, h4i, st4.out[b4i, h4i * G8:(h4i + 1) * G8].cpu().numpy(),
+                                  st4.lse[b4i, h4i * G8:(h4i + 1) * G8].cpu().numpy(), 4)
     lens = np.asarray(p8.lens, np.int64)
     n_sink = np.minimum(lens, w8.num_sink)
     n_win = np.minimum(w8.window, lens - n_sink)
@@ -642,7 +647,7 @@ def main():
 
     # CPU leg: the oracle timed on a bounded sample of the headline workload (the CPU
     # baseline), and the oracle's outputs of one (sequence, KV head) pair of every timed INT2
-    # workload compared with the GPU's.
+    # and INT4 workload compared with the GPU's.
     cpu = None
     parity = None
     if not args.no_cpu:
@@ -656,9 +661,9 @@ def main():
                                         np.stack([ref[h][0][0] for h in sorted(ref)]),
                                         np.stack([ref[h][1][0] for h in sorted(ref)]),
                                         sequence=0, kv_heads=sorted(ref))}
-        for name, (pp, b, h, o, l) in samples.items():
+        for name, (pp, b, h, o, l, bits) in samples.items():
             t1 = time.time()
-            r, rl = oracle_pair(pp, b, h)
+            r, rl = oracle_pair(pp, b, h, bits)
             parity[name] = parity_record(o, l, r, rl, sequence=b, kv_heads=[h],
                                          context=int(pp.lens[b]))
             log(f"parity {name}: {parity[name]} ({time.time() - t1:.1f} s)")

@@ -4,8 +4,9 @@ Qwen3-8B layer shape, batch 64, context lengths uniform in [16384, 32768] (the b
 workload, 4 query heads per KV head); Qwen3-32B layer shape, batch 16, context 32768 (8 query
 heads per KV head, the other row layout of the decode kernel); and Qwen3-4B layer shape, batch
 1, context 32768 (the small-launch path: sink/window workgroups first, one q-rotation workgroup
-per query head, short worker runs, the per-query-head combine); sink 4 + window 128 in BF16,
-INT2 bulk, one worker wavefront per resident slot (num_workers = 0) and the harness's default
+per query head, short worker runs, the per-query-head combine); and the Qwen3-8B batch-64
+workload with INT4 records (the matrix-core INT4 decode); sink 4 + window 128 in BF16,
+INT2 (or INT4) bulk, one worker wavefront per resident slot (num_workers = 0) and the harness's default
 partial-slot count (64 at large batch, enough for ~24-page runs at batch 1).  Both sides start from pools filled with a 0xA5 sentinel; the decode
 workspace starts filled with 0xFF bytes.
 
@@ -37,28 +38,30 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-@pytest.fixture(scope="module", params=["qwen3_8b_b64", "qwen3_32b", "qwen3_4b"])
+@pytest.fixture(scope="module", params=["qwen3_8b_b64", "qwen3_32b", "qwen3_4b", "qwen3_8b_b64_int4"])
 def full_run(request):
-    w = W.WORKLOADS[request.param]
-    _log(f"[full] workload {w.name}: batch {w.batch}, {w.num_q_heads}/{w.num_kv_heads} heads")
+    bits = 4 if request.param.endswith("_int4") else 2
+    w = W.WORKLOADS[request.param.removesuffix("_int4")]
+    _log(f"[full] workload {w.name}: batch {w.batch}, {w.num_q_heads}/{w.num_kv_heads} heads, "
+         f"INT{bits}")
     p = H.make_problem(w)
-    cache = H.GpuCache(p, fill=SENTINEL)
+    cache = H.GpuCache(p, fill=SENTINEL, bits=bits)
     last_k, last_v = cache.fill_context()
     step = H.DecodeStep(cache, ws_fill=0xFF)          # bench.py's configuration: auto workers, 64 slots
     step.set_new_token(last_k, last_v)
     step.run()
     torch.cuda.synchronize()
-    return w, p, cache, step
+    return w, p, cache, step, bits
 
 
-def _oracle_pair(w, p, b, h):
+def _oracle_pair(w, p, b, h, bits):
     """Oracle cache of one (sequence, KV head) built by the same appends as the GPU run
     (context, then the decoded token), and its decode attention for the G query heads."""
     L = int(p.lens[b])
     G = w.group
     kb, vb = W.sequence_kv(w, b, L, offsets=W.key_offsets(w), outliers=W.outlier_channels(w),
                            needle=W.needle_site(w, p.lens), q_bits=p.q)
-    oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window, fill=SENTINEL)
+    oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window, fill=SENTINEL, bits=bits)
     args = (p.rot_k[h:h + 1], p.rot_v[h:h + 1], w.clip, w.clip)
     oc.append(p.table[b], b, 0, kb[:L - 1, h:h + 1], vb[:L - 1, h:h + 1], *args)
     oc.append(p.table[b], b, L - 1, kb[L - 1:, h:h + 1], vb[L - 1:, h:h + 1], *args)
@@ -69,20 +72,20 @@ def _oracle_pair(w, p, b, h):
 
 
 def test_full_size_outputs_finite(full_run):
-    _, _, _, step = full_run
+    _, _, _, step, _ = full_run
     assert torch.isfinite(step.out).all()
     assert torch.isfinite(step.lse).all()
 
 
 @pytest.mark.parametrize("which,h", [("shortest", 0), ("middle", 3), ("longest", 7)])
 def test_full_size_sampled_pairs(full_run, which, h):
-    w, p, cache, step = full_run
+    w, p, cache, step, bits = full_run
     order = np.argsort(p.lens, kind="stable")
     b = int({"shortest": order[0], "middle": order[len(order) // 2], "longest": order[-1]}[which])
     L = int(p.lens[b])
     G = w.group
     _log(f"[full] {which}: sequence {b} L={L} KV head {h}")
-    oc, ref, ref_lse = _oracle_pair(w, p, b, h)
+    oc, ref, ref_lse = _oracle_pair(w, p, b, h, bits)
 
     pages_b = p.table[b, :math.ceil(L / 16)]
     gpu_rec = cache.pages[torch.from_numpy(pages_b.astype(np.int64)).to(cache.pages.device), h]
