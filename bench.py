@@ -89,6 +89,7 @@ def byte_model(w, lens):
     rot = 2 * hkv * 128 * 128 * 4
     return dict(int2=int2, bf16=bf16, q=q, table=table, out=out, append=append, rot=rot,
                 decode_attention=int2 + bf16 + q + table,
+                decode_kernel=int2 + bf16 + table,
                 step=int2 + bf16 + q + table + out + append + rot)
 
 
@@ -463,24 +464,30 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # The step on one stream: the new token's append, the query preparation
+    # (oscar_prepare_queries), the decode kernel (oscar_decode_attention_prepared) and the combine
+    # (the kernels of append + oscar_decode_attention + oscar_combine).  The decode kernel, the
+    # dominant part, is bracketed by events where it is timed.  (Running the append on a second
+    # stream beside the query preparation was slower: each cross-stream join left the device
+    # idle for 7-18 us.)
+    def timed_step(marks):
+        a, b = ev(), ev()
+        step.run_split(before_decode=lambda: a.record(stream),
+                       after_decode=lambda: b.record(stream))
+        marks.append((a, b))
+
     # Cold start, for the record: after 1 s of idle the power management cuts the shader clock
     # for the first ~10 ms of load (measured with s_memtime against s_memrealtime: 2.4 GHz
     # idle, 1.3-1.6 GHz a few milliseconds into the load, ~2.1 GHz settled).  20 steps, the
-    # decode launch of each bracketed by events.
-    step.run()
+    # decode kernel of each bracketed by events.
+    step.run_split()
     torch.cuda.synchronize()
     time.sleep(1.0)
     ca, cb = ev(), ev()
     cold_ev = []
     ca.record(stream)
     for _ in range(20):
-        a, b = ev(), ev()
-        step.append_new()
-        a.record(stream)
-        step.decode_only()
-        b.record(stream)
-        step.combine_only()
-        cold_ev.append((a, b))
+        timed_step(cold_ev)
     cb.record(stream)
     torch.cuda.synchronize()
     cold_dec = np.array([a.elapsed_time(b) for a, b in cold_ev])
@@ -495,7 +502,7 @@ def main():
     # headline: back-to-back decode steps as a serving loop runs them).  The record-read probe
     # and the prefill timings come after the timed region.
     scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
-    ms_scrub, _, _ = time_scrubbed(step.run, max(5, args.steps // 2), scrub)
+    ms_scrub, _, _ = time_scrubbed(step.run_split, max(5, args.steps // 2), scrub)
     # Achievable device-copy bandwidth in the same run: 1 GiB copied (2 GiB moved).
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     cdst = torch.empty_like(csrc)
@@ -517,48 +524,36 @@ def main():
     sev = [ev() for _ in range(n_spread + 1)]
     sev[0].record(stream)
     for k in range(n_spread):
-        step.run()
+        step.run_split()
         sev[k + 1].record(stream)
     torch.cuda.synchronize()
     step_ms = np.array([sev[k].elapsed_time(sev[k + 1]) for k in range(n_spread)])
     for _ in range(args.warmup):
-        step.run()
+        step.run_split()
     torch.cuda.synchronize()
 
     # Timed region: exactly K whole steps back to back, bracketed by synchronisation.  The
-    # decode-attention launch (the dominant part) is timed inside the same region, on its
-    # stream: an event pair around the decode launch of every 4th step (steps 1, 5, 9, ...), so
-    # that the samples see the same clock and power state as the steps they belong to, while
-    # only a quarter of the steps carry the two markers.
+    # decode kernel (the dominant part) is timed inside the same region, on its stream: an event
+    # pair around the decode kernel of every 4th step (steps 1, 5, 9, ...), so that the samples
+    # see the same clock and power state as the steps they belong to, while only a quarter of
+    # the steps carry the two markers.
     start, end = ev(), ev()
     dec_ev = []
     start.record(stream)
     for k in range(args.steps):
         if k % 4 == 1:
-            a, b = ev(), ev()
-            step.append_new()
-            a.record(stream)
-            step.decode_only()
-            b.record(stream)
-            step.combine_only()
-            dec_ev.append((a, b))
+            timed_step(dec_ev)
         else:
-            step.run()
+            step.run_split()
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
     if not dec_ev:  # fewer than 2 steps: one more step, timed on its own
-        a, b = ev(), ev()
-        step.append_new()
-        a.record(stream)
-        step.decode_only()
-        b.record(stream)
-        step.combine_only()
+        timed_step(dec_ev)
         torch.cuda.synchronize()
-        dec_ev.append((a, b))
     attn_ms = np.array([a.elapsed_time(b) for a, b in dec_ev])
     attn_avg = float(attn_ms.mean())
-    log(f"step {ms_step:.4f} ms; decode attention avg {attn_avg:.4f} ms over {len(dec_ev)} timed "
+    log(f"step {ms_step:.4f} ms; decode kernel avg {attn_avg:.4f} ms over {len(dec_ev)} timed "
         f"steps (min {attn_ms.min():.4f}, max {attn_ms.max():.4f}); single steps p10/p50/p90 "
         f"{np.percentile(step_ms, 10):.4f}/{np.percentile(step_ms, 50):.4f}/"
         f"{np.percentile(step_ms, 90):.4f} ms")
@@ -629,7 +624,7 @@ def main():
 
     tokens_per_s = w.batch / (ms_step / 1e3)
     step_gbps = bm["step"] / (ms_step / 1e3) / 1e9
-    attn_gbps = bm["decode_attention"] / (attn_avg / 1e3) / 1e9
+    attn_gbps = bm["decode_kernel"] / (attn_avg / 1e3) / 1e9
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -696,10 +691,11 @@ def main():
         "cold_start": cold,
         "ms_per_step_cache_scrubbed": round(ms_scrub, 5),
         "copy_gbps": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": "oscar_decode_attention (q prep + INT2 runs + "
-                     "BF16 window)", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "int2_decode_kernel (INT2 runs + BF16 sink/window, "
+                     "oscar_decode_attention_prepared; q prepared before it)",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "bytes_per_launch": bm["decode_attention"], "launch_ms": round(attn_avg, 5),
+                     "bytes_per_launch": bm["decode_kernel"], "launch_ms": round(attn_avg, 5),
                      "launch_samples": len(dec_ev),
                      "launch_ms_p10_p90": [round(float(np.percentile(attn_ms, q)), 5) for q in (10, 90)],
                      "traffic": measured_traffic(w.name),

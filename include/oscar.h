@@ -299,6 +299,33 @@ int32_t oscar_decode_attention(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two halves of oscar_decode_attention, for callers that overlap the query preparation
+ * with other work, such as the new token's append on a second stream (the two are independent;
+ * the decode needs both).  oscar_prepare_queries computes q' = q . rot_k with its int8 encoding
+ * and the work plan into `workspace`; oscar_decode_attention_prepared then runs the attention
+ * over the cache from them.  The pair, called in this order, computes exactly what
+ * oscar_decode_attention computes (the same kernels: results are identical).  The second call
+ * must get the same layout, batch, num_q_heads, seq_lens contents, num_workers, max_splits and
+ * workspace as the first and be ordered after it, and after every append it should see; the
+ * workspace must not be reused in between.  Arguments, validation and errors as
+ * oscar_decode_attention (each call checks the arguments it takes).
+ * (OSCAR project card, "How it works": rotated queries against the rotated cache; OSCAR paper,
+ *  "Abstract": paged INT2 attention kernel.)
+ */
+int32_t oscar_prepare_queries(
+    const oscar_layout* lay, int32_t batch, int32_t num_q_heads,
+    const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
+    int32_t num_workers, int32_t max_splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t oscar_decode_attention_prepared(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t num_q_heads, const int32_t* seq_lens, float sm_scale,
+    int32_t num_workers, int32_t max_splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Second stage: merge the splits of every (sequence, query head) in ascending split order,
  * normalise, and rotate back with the transpose of the value rotation:
  *   M = max_s m_s, l = sum_s 2^(m_s - M) l_s, o' = sum_s 2^(m_s - M) o'_s / l,

@@ -271,6 +271,59 @@ int32_t oscar_decode_attention(
                                   (hipStream_t)stream));
 }
 
+// Checks shared by the two halves of oscar_decode_attention (everything that does not concern
+// one half's own pointers).
+int32_t check_decode_common(const oscar_layout* lay, int32_t batch, int32_t num_q_heads,
+                            int32_t num_workers, int32_t max_splits) {
+  int32_t st = check_layout(lay);
+  if (st != OSCAR_OK) return st;
+  if (batch < 0 || num_workers < 0 || num_workers > kMaxWorkers || max_splits < 1 ||
+      max_splits > 65535)
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if ((long long)batch * lay->num_kv_heads * lay->max_pages_per_seq > 0x7FFFFFFFLL)
+    return OSCAR_ERR_UNSUPPORTED;
+  st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  return check_splits(num_q_heads, lay->num_kv_heads, max_splits);
+}
+
+int32_t oscar_prepare_queries(const oscar_layout* lay, int32_t batch, int32_t num_q_heads,
+                              const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
+                              int32_t num_workers, int32_t max_splits, void* workspace,
+                              size_t workspace_bytes_given, void* stream) {
+  const int32_t st = check_decode_common(lay, batch, num_q_heads, num_workers, max_splits);
+  if (st != OSCAR_OK) return st;
+  if (batch == 0) return OSCAR_OK;
+  if (!q || !seq_lens || !rot_k || !workspace) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(workspace) || !aligned16(rot_k)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
+  return hip_status(launch_decode_prep(geom(lay), q, rot_k, batch, num_q_heads, seq_lens,
+                                       num_workers, ws, (hipStream_t)stream));
+}
+
+int32_t oscar_decode_attention_prepared(
+    const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids, int32_t batch, int32_t num_q_heads,
+    const int32_t* seq_lens, float sm_scale, int32_t num_workers, int32_t max_splits,
+    void* workspace, size_t workspace_bytes_given, void* stream) {
+  const int32_t st = check_decode_common(lay, batch, num_q_heads, num_workers, max_splits);
+  if (st != OSCAR_OK) return st;
+  if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return OSCAR_OK;
+  if (!pages || !block_table || !seq_lens || !workspace) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pages) || !aligned16(workspace) || (sinkwin && !aligned16(sinkwin)))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
+  return hip_status(launch_decode_main(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                       num_q_heads, seq_lens, sm_scale, num_workers, ws,
+                                       (hipStream_t)stream));
+}
+
 int32_t oscar_decode_attention_static(
     const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
     const int32_t* block_table, const int32_t* slot_ids,

@@ -1514,15 +1514,19 @@ hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
-                         const int32_t* block_table, const int32_t* slot_ids, int batch,
-                         int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
-                         float sm_scale, int num_workers, const Workspace& ws,
-                         hipStream_t stream) {
-  if (batch == 0) return hipSuccess;
-  const int G = hq / g.hkv;
-  const int workers = num_workers > 0 ? num_workers
-                                      : (G <= 4 ? resident_workers<1>() : resident_workers<8>());
+namespace {
+
+// Launch shape of the INT2 decode (shared by its q preparation and the decode kernel, which must
+// agree on the worker count the plan is built for).
+struct DecodeShape {
+  int G, workers, worker_groups, window_first, wparts, hpw;
+};
+
+DecodeShape decode_shape(const CacheGeom& g, int batch, int hq, int num_workers) {
+  DecodeShape s;
+  s.G = hq / g.hkv;
+  s.workers = num_workers > 0 ? num_workers
+                              : (s.G <= 4 ? resident_workers<1>() : resident_workers<8>());
   // Few pairs: their sink/window workgroups go first, so that they start at once instead of
   // after the INT2 workers that fill the device, each pair's positions are cut into parts of
   // kWinPartTokens (one workgroup each: a part's loads all go out in one round, where a whole
@@ -1530,25 +1534,55 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
   // head.  Many pairs: one window workgroup per pair, in the workers' tail.
   const int cus = current_device_cus();
   const bool small = (long long)batch * g.hkv * 2 < cus;
-  const int window_first = small ? 1 : 0;
-  const int wparts =
+  s.window_first = small ? 1 : 0;
+  s.wparts =
       small ? max(1, min(kWinSlots, (g.num_sink + g.window + kWinPartTokens - 1) / kWinPartTokens))
             : 1;
-  const int hpw = small ? 1 : G;
-  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (G / hpw), batch + 1), dim3(kPrepThreads), 0,
-                     stream, g, q, rot_k, hq, seq_lens, workers, hpw, ws);
-  const int worker_groups = (workers + kWaves - 1) / kWaves;
-  const dim3 grid(worker_groups + batch * g.hkv * wparts);
+  s.hpw = small ? 1 : s.G;
+  s.worker_groups = (s.workers + kWaves - 1) / kWaves;
+  return s;
+}
+
+}  // namespace
+
+hipError_t launch_decode_prep(const CacheGeom& g, const uint16_t* q, const float* rot_k, int batch,
+                              int hq, const int32_t* seq_lens, int num_workers,
+                              const Workspace& ws, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const DecodeShape s = decode_shape(g, batch, hq, num_workers);
+  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (s.G / s.hpw), batch + 1), dim3(kPrepThreads), 0,
+                     stream, g, q, rot_k, hq, seq_lens, s.workers, s.hpw, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_main(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
+                              const int32_t* block_table, const int32_t* slot_ids, int batch,
+                              int hq, const int32_t* seq_lens, float sm_scale, int num_workers,
+                              const Workspace& ws, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const DecodeShape s = decode_shape(g, batch, hq, num_workers);
+  const dim3 grid(s.worker_groups + batch * g.hkv * s.wparts);
   const int32_t* plan = ws.plan();
-  if (G <= 4)
+  if (s.G <= 4)
     hipLaunchKernelGGL(int2_decode_kernel<1>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
-                       worker_groups, window_first, wparts, ws);
+                       s.worker_groups, s.window_first, s.wparts, ws);
   else
     hipLaunchKernelGGL(int2_decode_kernel<8>, grid, dim3(64 * kWaves), 0, stream, g, pages,
                        sinkwin, block_table, slot_ids, hq, seq_lens, plan, sm_scale,
-                       worker_groups, window_first, wparts, ws);
+                       s.worker_groups, s.window_first, s.wparts, ws);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
+                         const int32_t* block_table, const int32_t* slot_ids, int batch,
+                         int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,
+                         float sm_scale, int num_workers, const Workspace& ws,
+                         hipStream_t stream) {
+  const hipError_t e = launch_decode_prep(g, q, rot_k, batch, hq, seq_lens, num_workers, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_decode_main(g, pages, sinkwin, block_table, slot_ids, batch, hq, seq_lens,
+                            sm_scale, num_workers, ws, stream);
 }
 
 hipError_t launch_int4_mfma_decode(const CacheGeom& g, const uint8_t* pages,

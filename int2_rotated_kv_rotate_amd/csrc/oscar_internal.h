@@ -117,6 +117,16 @@ hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_
 
 // q' = q . R_K (fp32 and int8 forms) into the workspace Q blocks, as oscar_decode_attention's
 // first kernel does (its work plan is built for a single worker).
+// The two halves of launch_decode: the q rotation and work plan, then the decode kernel (same
+// batch, heads, lengths and num_workers; the workspace carries the q blocks and the plan).
+hipError_t launch_decode_prep(const CacheGeom& g, const uint16_t* q, const float* rot_k, int batch,
+                              int hq, const int32_t* seq_lens, int num_workers,
+                              const Workspace& ws, hipStream_t stream);
+hipError_t launch_decode_main(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
+                              const int32_t* block_table, const int32_t* slot_ids, int batch,
+                              int hq, const int32_t* seq_lens, float sm_scale, int num_workers,
+                              const Workspace& ws, hipStream_t stream);
+
 hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot_k, int batch,
                          int hq, const int32_t* seq_lens, const Workspace& ws, hipStream_t stream);
 

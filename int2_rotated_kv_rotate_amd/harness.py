@@ -214,6 +214,7 @@ class DecodeStep:
         self.start = torch.from_numpy((p.lens - 1).astype(np.int32)).to(dev)
         self.k_last = None
         self.v_last = None
+        self.side = None            # second stream of run_overlapped, made on first use
 
     def set_new_token(self, last_k, last_v):
         self.k_last = as_i16(np.concatenate(last_k)).to(self.cache.device)
@@ -260,6 +261,54 @@ class DecodeStep:
     def run(self, stream=None):
         self.append_new(stream)
         self.attend(stream)
+
+    # The step with the decode split in two, on one stream (run_split) or with the new token's
+    # append on a second stream overlapped with the query preparation (run_overlapped: the two
+    # are independent; the decode waits for both).  INT2 caches only.
+    def prepare(self, stream=None):
+        c = self.cache
+        ops.prepare_queries(c.layout, self.q, self.seq_lens, c.rot_k, self.num_workers,
+                            self.max_splits, self.ws, stream)
+
+    def decode_prepared(self, stream=None):
+        c = self.cache
+        p = c.p
+        ops.decode_attention_prepared(c.layout, c.pages, c.sinkwin, c.table, c.slots, p.batch,
+                                      p.w.num_q_heads, self.seq_lens, SM_SCALE, self.num_workers,
+                                      self.max_splits, self.ws, stream)
+
+    def run_split(self, before_decode=None, after_decode=None):
+        """The step through the two halves of the decode on the current stream: append,
+        prepare, decode, combine (the same kernels as run()).  before_decode() and
+        after_decode(), if given, run right before and after the decode kernel's launch."""
+        self.append_new()
+        self.prepare()
+        if before_decode is not None:
+            before_decode()
+        self.decode_prepared()
+        if after_decode is not None:
+            after_decode()
+        self.combine_only()
+
+    def run_overlapped(self, before_decode=None, after_decode=None):
+        """append || prepare, then decode and combine on the current stream.  before_decode()
+        and after_decode(), if given, run on the current stream right before and after the
+        decode kernel's launch (event markers)."""
+        main = torch.cuda.current_stream()
+        if self.side is None:
+            self.side = torch.cuda.Stream()      # default priority
+        side = self.side
+        side.wait_stream(main)      # the previous step's decode has read the pool
+        with torch.cuda.stream(side):
+            self.append_new(side)
+        self.prepare(main)
+        main.wait_stream(side)
+        if before_decode is not None:
+            before_decode()
+        self.decode_prepared(main)
+        if after_decode is not None:
+            after_decode()
+        self.combine_only(main)
 
 
 def capture_graph(fn) -> "torch.cuda.CUDAGraph":

@@ -35,6 +35,8 @@ EXPORTED = (
     "oscar_read_records",
     "oscar_mfma_bf16_tiles",
     "oscar_decode_attention_static",
+    "oscar_prepare_queries",
+    "oscar_decode_attention_prepared",
 )
 
 STATIC_WORKSPACE_BYTES = 32 << 20   # OSCAR_STATIC_WORKSPACE_BYTES
@@ -103,6 +105,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_decode_workspace_bytes.restype = SZ
     lib.oscar_decode_attention.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, F32, I32, I32, P, SZ, P]
     lib.oscar_decode_attention.restype = I32
+    lib.oscar_prepare_queries.argtypes = [LP, I32, I32, P, P, P, I32, I32, P, SZ, P]
+    lib.oscar_prepare_queries.restype = I32
+    lib.oscar_decode_attention_prepared.argtypes = [LP, P, P, P, P, I32, I32, P, F32, I32, I32, P,
+                                                    SZ, P]
+    lib.oscar_decode_attention_prepared.restype = I32
     lib.oscar_combine.argtypes = [I32, I32, I32, I32, P, SZ, P, P, P, P]
     lib.oscar_combine.restype = I32
     lib.oscar_bf16_append.argtypes = [LP, P, P, I32, I32, P, P, P, P, P]
@@ -231,6 +238,30 @@ def decode_attention(lay: Layout, pages, sinkwin, block_table, slot_ids, q, seq_
         batch, hq, _ptr(q, torch.int16, "q"), _ptr(seq_lens, torch.int32, "seq_lens"),
         _ptr(rot_k, torch.float32, "rot_k"), float(sm_scale), num_workers, max_splits,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def prepare_queries(lay: Layout, q, seq_lens, rot_k, num_workers: int, max_splits: int,
+                    workspace, stream=None) -> None:
+    """First half of decode_attention: q' and the work plan into the workspace."""
+    lib = load_library()
+    batch, hq = q.shape[0], q.shape[1]
+    _check("oscar_prepare_queries", lib.oscar_prepare_queries(
+        ctypes.byref(lay), batch, hq, _ptr(q, torch.int16, "q"),
+        _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(rot_k, torch.float32, "rot_k"),
+        num_workers, max_splits, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))
+
+
+def decode_attention_prepared(lay: Layout, pages, sinkwin, block_table, slot_ids, batch: int,
+                              num_q_heads: int, seq_lens, sm_scale: float, num_workers: int,
+                              max_splits: int, workspace, stream=None) -> None:
+    """Second half of decode_attention, from a workspace filled by prepare_queries."""
+    lib = load_library()
+    _check("oscar_decode_attention_prepared", lib.oscar_decode_attention_prepared(
+        ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
+        batch, num_q_heads, _ptr(seq_lens, torch.int32, "seq_lens"), float(sm_scale), num_workers,
+        max_splits, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def decode_attention_static(lay: Layout, pages, sinkwin, block_table, slot_ids, q, seq_lens,

@@ -203,3 +203,39 @@ def test_decode_static_validation(lib):
     # 64 sequences x 32 query heads x 65 slots need ~71 MB: more than the library's buffer
     assert call(batch=64, ms=64) == 3
     assert call(batch=0) == 0
+
+
+def test_prepare_and_prepared_decode_validation(lib):
+    lay = _layout()
+
+    def prep(**kw):
+        a = dict(batch=1, hq=32, q=FAKE, lens=FAKE, rk=FAKE, nw=0, ms=4, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.oscar_prepare_queries(ctypes.byref(lay), a["batch"], a["hq"], a["q"], a["lens"],
+                                         a["rk"], a["nw"], a["ms"], a["ws"], a["wsb"], None)
+
+    def dec(**kw):
+        a = dict(pages=FAKE, sw=FAKE, bt=FAKE, batch=1, hq=32, lens=FAKE, sm=0.088, nw=0, ms=4,
+                 ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.oscar_decode_attention_prepared(
+            ctypes.byref(lay), a["pages"], a["sw"], a["bt"], None, a["batch"], a["hq"], a["lens"],
+            a["sm"], a["nw"], a["ms"], a["ws"], a["wsb"], None)
+
+    for f in (prep, dec):
+        assert f(hq=30) == 1               # not a multiple of Hkv
+        assert f(hq=24) == 2               # group 3 unsupported
+        assert f(nw=-1) == 1
+        assert f(ms=0) == 1
+        assert f(ws=None) == 1
+        assert f(wsb=100) == 3
+        assert f(ws=ctypes.c_void_p(20)) == 1   # misaligned workspace
+        assert f(batch=0) == 0
+    assert prep(q=None) == 1
+    assert prep(rk=None) == 1
+    assert prep(lens=None) == 1
+    assert dec(pages=None) == 1
+    assert dec(bt=None) == 1
+    assert dec(sw=None) == 1               # the layout has sink/window rows
+    for bad in (float("nan"), float("inf"), 0.0, -1.0):
+        assert dec(sm=bad) == 1
