@@ -15,7 +15,8 @@
  *   - Array arguments are DEVICE pointers (memory on the GPU that is current when the call is
  *     made), except `lay`, which is a host pointer read during the call only.
  *   - The caller owns all memory.  The library never allocates, frees or keeps a pointer past
- *     the call.  It keeps no state between calls.
+ *     the call.  Its only state between calls is a per-device cache of the compute-unit count
+ *     and of the device address of oscar_decode_attention_static's workspace.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the default stream)
  *     and returns without synchronising.  Calls on one stream run in order; calls that write
  *     the same cache from two streams at once race.
@@ -28,6 +29,9 @@
  *   - Inputs must be finite, and every rotated value must stay below 65504 in magnitude so the
  *     fp16 scales and zeros stay finite.
  *   - Pointers to pages, stores, q, k_new, v_new and workspace must be 16-byte aligned.
+ *   - Size limits (else OSCAR_ERR_UNSUPPORTED): batch * num_q_heads at most 2^27 for the decode,
+ *     combine and workspace calls; total_new at most 2^30 for the appends.  Every size the
+ *     library derives from them then fits its int32 grids and indices.
  *
  * Fixed geometry: head_dim 128, page_size 16 tokens, quantisation group 32 channels.
  *
@@ -243,7 +247,8 @@ int32_t oscar_int4_decode_attention(
  * sequences of `num_q_heads` query heads split at most `max_splits` ways: per (sequence, query
  * head) a 1024-byte query block and max_splits + 8 partial slots of 520 bytes (128 fp32
  * outputs, then (m, l) in a region of its own), plus a plan of 4 * (4 + 3 * batch +
- * batch * num_q_heads) bytes rounded up to 256.  Returns 0 for invalid arguments.
+ * batch * num_q_heads) bytes rounded up to 256.  Returns 0 for invalid arguments, for
+ * max_splits above 65535 and for batch * num_q_heads above 2^27.
  */
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits);
 

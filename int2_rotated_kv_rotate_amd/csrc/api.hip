@@ -17,7 +17,7 @@ int32_t check_layout(const oscar_layout* lay) {
     return OSCAR_ERR_UNSUPPORTED;
   if (lay->num_kv_heads < 1 || lay->num_kv_heads > 65535) return OSCAR_ERR_INVALID_ARGUMENT;
   if (lay->num_sink < 0 || lay->window < 0) return OSCAR_ERR_INVALID_ARGUMENT;
-  if (lay->num_sink + lay->window > kMaxSinkWindow) return OSCAR_ERR_UNSUPPORTED;
+  if ((long long)lay->num_sink + lay->window > kMaxSinkWindow) return OSCAR_ERR_UNSUPPORTED;
   if (lay->num_pages < 0 || lay->max_pages_per_seq < 1 || lay->num_slots < 0)
     return OSCAR_ERR_INVALID_ARGUMENT;
   return OSCAR_OK;
@@ -44,6 +44,17 @@ int32_t check_splits(int32_t hq, int32_t hkv, int32_t max_splits) {
 }
 
 constexpr int32_t kMaxWorkers = 1 << 20;
+
+// batch * num_q_heads rows of queries, partials and outputs: at most 2^27, so that every grid
+// size and index the launchers derive from them fits in int32 and the workspace size cannot
+// wrap in size_t.
+constexpr long long kMaxQueryRows = 1LL << 27;
+int32_t check_rows(int32_t batch, int32_t hq) {
+  return (long long)batch * hq > kMaxQueryRows ? OSCAR_ERR_UNSUPPORTED : OSCAR_OK;
+}
+
+// New rows of one append call: at most 2^30 (the launchers round the count up to tiles in int32).
+constexpr int32_t kMaxNewRows = 1 << 30;
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? OSCAR_OK : OSCAR_ERR_HIP; }
 
@@ -120,6 +131,7 @@ int32_t oscar_rotate_quantize_append_ex(
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (total_new > kMaxNewRows) return OSCAR_ERR_UNSUPPORTED;
   if (method != OSCAR_APPEND_AUTO && method != OSCAR_APPEND_VECTOR && method != OSCAR_APPEND_MATRIX)
     return OSCAR_ERR_INVALID_ARGUMENT;
   if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
@@ -162,6 +174,7 @@ int32_t oscar_rotate_quantize_append_hadamard(
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (total_new > kMaxNewRows) return OSCAR_ERR_UNSUPPORTED;
   if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
     return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0 || total_new == 0) return OSCAR_OK;
@@ -186,6 +199,7 @@ int32_t oscar_int4_rotate_quantize_append(
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (total_new > kMaxNewRows) return OSCAR_ERR_UNSUPPORTED;
   if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
     return OSCAR_ERR_INVALID_ARGUMENT;
   if (batch == 0 || total_new == 0) return OSCAR_OK;
@@ -213,6 +227,8 @@ int32_t oscar_int4_decode_attention(
     return OSCAR_ERR_INVALID_ARGUMENT;
   st = check_heads(num_q_heads, lay->num_kv_heads);
   if (st != OSCAR_OK) return st;
+  st = check_rows(batch, num_q_heads);
+  if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
   if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
@@ -232,7 +248,8 @@ int32_t oscar_int4_decode_attention(
 }
 
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_splits) {
-  if (batch < 0 || num_q_heads < 1 || max_splits < 1) return 0;
+  if (batch < 0 || num_q_heads < 1 || max_splits < 1 || max_splits > 65535) return 0;
+  if (check_rows(batch, num_q_heads) != OSCAR_OK) return 0;
   return workspace_bytes(batch, num_q_heads, max_splits);
 }
 
@@ -252,6 +269,8 @@ int32_t oscar_decode_attention(
   if ((long long)batch * lay->num_kv_heads * lay->max_pages_per_seq > 0x7FFFFFFFLL)
     return OSCAR_ERR_UNSUPPORTED;
   st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_rows(batch, num_q_heads);
   if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
@@ -283,6 +302,8 @@ int32_t check_decode_common(const oscar_layout* lay, int32_t batch, int32_t num_
   if ((long long)batch * lay->num_kv_heads * lay->max_pages_per_seq > 0x7FFFFFFFLL)
     return OSCAR_ERR_UNSUPPORTED;
   st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_rows(batch, num_q_heads);
   if (st != OSCAR_OK) return st;
   return check_splits(num_q_heads, lay->num_kv_heads, max_splits);
 }
@@ -340,6 +361,8 @@ int32_t oscar_decode_attention_static(
     return OSCAR_ERR_UNSUPPORTED;
   st = check_heads(num_q_heads, lay->num_kv_heads);
   if (st != OSCAR_OK) return st;
+  st = check_rows(batch, num_q_heads);
+  if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
   if (!valid_scale(sm_scale)) return OSCAR_ERR_INVALID_ARGUMENT;
@@ -370,6 +393,8 @@ int32_t oscar_combine(
     return OSCAR_ERR_INVALID_ARGUMENT;
   int32_t st = check_heads(num_q_heads, num_kv_heads);
   if (st != OSCAR_OK) return st;
+  st = check_rows(batch, num_q_heads);
+  if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;
   if (batch == 0) return OSCAR_OK;
@@ -389,6 +414,7 @@ int32_t oscar_bf16_append(
   int32_t st = check_layout(lay);
   if (st != OSCAR_OK) return st;
   if (batch < 0 || total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (total_new > kMaxNewRows) return OSCAR_ERR_UNSUPPORTED;
   if (batch == 0 || total_new == 0) return OSCAR_OK;
   if (!pages || !block_table || !k_new || !v_new || !new_offsets || !start_pos)
     return OSCAR_ERR_INVALID_ARGUMENT;
@@ -407,6 +433,8 @@ int32_t oscar_bf16_decode_attention(
   if (batch < 0 || split_pages < 1 || max_splits < 1 || max_splits > 65535)
     return OSCAR_ERR_INVALID_ARGUMENT;
   st = check_heads(num_q_heads, lay->num_kv_heads);
+  if (st != OSCAR_OK) return st;
+  st = check_rows(batch, num_q_heads);
   if (st != OSCAR_OK) return st;
   st = check_splits(num_q_heads, lay->num_kv_heads, max_splits);
   if (st != OSCAR_OK) return st;

@@ -75,7 +75,8 @@ inline Workspace make_workspace(void* base, int batch, int hq, int max_splits) {
   w.q_bytes = (size_t)batch * hq * kQBlock;
   w.o_bytes = (size_t)batch * hq * w.nslots * kHeadDim * sizeof(float);
   w.ml_bytes = (size_t)batch * hq * w.nslots * sizeof(float2);
-  w.plan_bytes = ((size_t)(kPlanHeader + 3 * batch + batch * hq) * sizeof(int32_t) + 255) & ~(size_t)255;
+  w.plan_bytes = (((size_t)kPlanHeader + 3 * (size_t)batch + (size_t)batch * hq) * sizeof(int32_t) +
+                  255) & ~(size_t)255;
   return w;
 }
 
