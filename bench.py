@@ -1,10 +1,11 @@
 """Benchmark: one decode step of the rotated-INT2 mixed-precision paged attention on one GPU.
 
 A step is one pass of the whole hot path over the batch: rotate-quantize-append of each
-sequence's new token, decode attention (q rotation, INT2 pages in equal per-worker runs, BF16
-sink + window) and the combine of the partials with R_V^T.  Default workload: Qwen3-8B-shaped layer, batch 64, 32 query /
-8 KV heads, head_dim 128, context lengths uniform in [16384, 32768], sink 4 + window 128 in
-BF16, INT2 bulk, 16-token pages, all inputs synthetic and already resident in HBM.
+sequence's new token with the q rotation in the same launch (oscar_append_and_prepare), decode
+attention (INT2 pages in equal per-worker runs, BF16 sink + window) and the combine of the
+partials with R_V^T.  Default workload: Qwen3-8B-shaped layer, batch 64, 32 query / 8 KV heads,
+head_dim 128, context lengths uniform in [16384, 32768], sink 4 + window 128 in BF16, INT2 bulk,
+16-token pages, all inputs synthetic and already resident in HBM.
 
 Prints ONE JSON line.  Extra fields: effective GB/s of the step, the decode-attention roofline
 (bytes from the method's byte model / the launch's HIP-event duration), the prefill append of
@@ -464,15 +465,15 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    # The step on one stream: the new token's append, the query preparation
-    # (oscar_prepare_queries), the decode kernel (oscar_decode_attention_prepared) and the combine
-    # (the kernels of append + oscar_decode_attention + oscar_combine).  The decode kernel, the
-    # dominant part, is bracketed by events where it is timed.  (Running the append on a second
-    # stream beside the query preparation was slower: each cross-stream join left the device
-    # idle for 7-18 us.)
+    # The step on one stream: the new token's append and the query preparation in one launch
+    # (oscar_append_and_prepare), the decode kernel (oscar_decode_attention_prepared) and the
+    # combine; the same bytes and results as append + oscar_decode_attention + oscar_combine
+    # (tests/test_gpu_fused_step.py).  The decode kernel, the dominant part, is bracketed by
+    # events where it is timed.  (The append on a second stream beside the query preparation
+    # was slower: each cross-stream join left the device idle for 7-18 us.)
     def timed_step(marks):
         a, b = ev(), ev()
-        step.run_split(before_decode=lambda: a.record(stream),
+        step.run_fused(before_decode=lambda: a.record(stream),
                        after_decode=lambda: b.record(stream))
         marks.append((a, b))
 
@@ -480,7 +481,7 @@ def main():
     # for the first ~10 ms of load (measured with s_memtime against s_memrealtime: 2.4 GHz
     # idle, 1.3-1.6 GHz a few milliseconds into the load, ~2.1 GHz settled).  20 steps, the
     # decode kernel of each bracketed by events.
-    step.run_split()
+    step.run_fused()
     torch.cuda.synchronize()
     time.sleep(1.0)
     ca, cb = ev(), ev()
@@ -502,7 +503,7 @@ def main():
     # headline: back-to-back decode steps as a serving loop runs them).  The record-read probe
     # and the prefill timings come after the timed region.
     scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
-    ms_scrub, _, _ = time_scrubbed(step.run_split, max(5, args.steps // 2), scrub)
+    ms_scrub, _, _ = time_scrubbed(step.run_fused, max(5, args.steps // 2), scrub)
     # Achievable device-copy bandwidth in the same run: 1 GiB copied (2 GiB moved).
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     cdst = torch.empty_like(csrc)
@@ -524,12 +525,12 @@ def main():
     sev = [ev() for _ in range(n_spread + 1)]
     sev[0].record(stream)
     for k in range(n_spread):
-        step.run_split()
+        step.run_fused()
         sev[k + 1].record(stream)
     torch.cuda.synchronize()
     step_ms = np.array([sev[k].elapsed_time(sev[k + 1]) for k in range(n_spread)])
     for _ in range(args.warmup):
-        step.run_split()
+        step.run_fused()
     torch.cuda.synchronize()
 
     # Timed region: exactly K whole steps back to back, bracketed by synchronisation.  The
@@ -544,7 +545,7 @@ def main():
         if k % 4 == 1:
             timed_step(dec_ev)
         else:
-            step.run_split()
+            step.run_fused()
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
@@ -564,7 +565,7 @@ def main():
     # kernels are shorter than the host's work per launch (batch 1): K replays of the whole
     # step back to back, then K replays of the decode launch alone (q preparation + decode
     # kernel), each bracketed by events.  After the timed region: not part of the headline.
-    g_step = H.capture_graph(step.run)
+    g_step = H.capture_graph(step.run_fused)
     g_dec = H.capture_graph(step.decode_only)
     n_rep = max(args.steps, 5)
     ga, gb = ev(), ev()
@@ -692,7 +693,7 @@ def main():
         "ms_per_step_cache_scrubbed": round(ms_scrub, 5),
         "copy_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "int2_decode_kernel (INT2 runs + BF16 sink/window, "
-                     "oscar_decode_attention_prepared; q prepared before it)",
+                     "oscar_decode_attention_prepared; q prepared by oscar_append_and_prepare)",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": bm["decode_kernel"], "launch_ms": round(attn_avg, 5),

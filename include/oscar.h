@@ -331,6 +331,32 @@ int32_t oscar_decode_attention_prepared(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The front half of a decode step in one launch: this step's new K/V rows appended as
+ * oscar_rotate_quantize_append_ex does with OSCAR_APPEND_AUTO (the arguments lay ... clip_v,
+ * k_mean optional), and the queries prepared as oscar_prepare_queries does (num_q_heads, q,
+ * seq_lens, rot_k, num_workers, max_splits, workspace).  One `batch` serves both: the step's
+ * sequences, whose new_offsets / start_pos place the new rows and whose seq_lens are the lengths
+ * after the append.  The two parts are independent and each alone leaves most of the device
+ * idle, so with fewer than 256 new rows (the append's 4-row vector kernel) their workgroups
+ * run in one launch; from 256 rows on they are two launches.  Either way the call writes
+ * exactly the bytes of oscar_rotate_quantize_append_ex followed by oscar_prepare_queries, and
+ * oscar_decode_attention_prepared continues it.  total_new = 0 prepares the queries only.
+ * Validation and errors: the union of those two calls' (the append's pointers only when
+ * total_new > 0).  (OSCAR project card, "How it works": K/V rows rotated, clipped and stored in
+ * INT2 beside the BF16 sink and window, queries rotated by the same R_K.)
+ */
+int32_t oscar_append_and_prepare(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
+    const int32_t* block_table, const int32_t* slot_ids,
+    int32_t batch, int32_t total_new,
+    const uint16_t* k_new, const uint16_t* v_new,
+    const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, const float* k_mean, float clip_k, float clip_v,
+    int32_t num_q_heads, const uint16_t* q, const int32_t* seq_lens,
+    int32_t num_workers, int32_t max_splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Second stage: merge the splits of every (sequence, query head) in ascending split order,
  * normalise, and rotate back with the transpose of the value rotation:
  *   M = max_s m_s, l = sum_s 2^(m_s - M) l_s, o' = sum_s 2^(m_s - M) o'_s / l,

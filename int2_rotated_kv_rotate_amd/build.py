@@ -30,6 +30,9 @@ SOURCES = {
     # the INT4 quantiser is the same kind of fp32 formula
     "int4.hip": ["-ffp-contract=off"],
     "probe.hip": [],
+    # the q preparation and the decode-step launch that holds it beside the append: built like
+    # the append (no contraction), so both launches run the same code
+    "step.hip": ["-ffp-contract=off"],
 }
 COMMON = [
     "-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

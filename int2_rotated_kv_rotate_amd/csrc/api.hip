@@ -324,6 +324,41 @@ int32_t oscar_prepare_queries(const oscar_layout* lay, int32_t batch, int32_t nu
                                        num_workers, ws, (hipStream_t)stream));
 }
 
+int32_t oscar_append_and_prepare(
+    const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin, const int32_t* block_table,
+    const int32_t* slot_ids, int32_t batch, int32_t total_new, const uint16_t* k_new,
+    const uint16_t* v_new, const int32_t* new_offsets, const int32_t* start_pos,
+    const float* rot_k, const float* rot_v, const float* k_mean, float clip_k, float clip_v,
+    int32_t num_q_heads, const uint16_t* q, const int32_t* seq_lens, int32_t num_workers,
+    int32_t max_splits, void* workspace, size_t workspace_bytes_given, void* stream) {
+  int32_t st = check_decode_common(lay, batch, num_q_heads, num_workers, max_splits);
+  if (st != OSCAR_OK) return st;
+  if (total_new < 0) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (total_new > kMaxNewRows) return OSCAR_ERR_UNSUPPORTED;
+  if (!(clip_k > 0.f && clip_k <= 1.f) || !(clip_v > 0.f && clip_v <= 1.f))
+    return OSCAR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return OSCAR_OK;
+  // the query preparation's arguments
+  if (!q || !seq_lens || !rot_k || !workspace) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(workspace) || !aligned16(rot_k)) return OSCAR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(batch, num_q_heads, max_splits))
+    return OSCAR_ERR_WORKSPACE_TOO_SMALL;
+  // the append's (none when there are no new rows)
+  if (total_new > 0) {
+    if (!pages || !block_table || !k_new || !v_new || !new_offsets || !start_pos || !rot_v)
+      return OSCAR_ERR_INVALID_ARGUMENT;
+    if (lay->num_sink + lay->window > 0 && sinkwin == nullptr) return OSCAR_ERR_INVALID_ARGUMENT;
+    if (!aligned16(pages) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rot_v) ||
+        (sinkwin && !aligned16(sinkwin)) || ((uintptr_t)k_mean & 3u) != 0)
+      return OSCAR_ERR_INVALID_ARGUMENT;
+  }
+  Workspace ws = make_workspace(workspace, batch, num_q_heads, max_splits);
+  return hip_status(launch_append_prepare(geom(lay), pages, sinkwin, block_table, slot_ids, batch,
+                                          total_new, k_new, v_new, new_offsets, start_pos, rot_k,
+                                          rot_v, k_mean, clip_k, clip_v, num_q_heads, q, seq_lens,
+                                          num_workers, ws, (hipStream_t)stream));
+}
+
 int32_t oscar_decode_attention_prepared(
     const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,
     const int32_t* block_table, const int32_t* slot_ids, int32_t batch, int32_t num_q_heads,

@@ -7,9 +7,9 @@
 // orthogonal R_K, and the rotated output is rotated back with R_V^T by the combine kernel.
 //
 // Kernels
-//   prep_q_kernel      per (KV head, sequence): q' = q . R_K for the G query heads of the group
-//                      plus an integer form of q' for the int8 matrix cores; one extra
-//                      workgroup writes the work plan of the INT2 workers.
+//   prep_q_kernel      (step.hip) per (KV head, sequence): q' = q . R_K for the G query heads of
+//                      the group plus an integer form of q' for the int8 matrix cores; one
+//                      extra workgroup writes the work plan of the INT2 workers.
 //   int2_decode_kernel persistent INT2 workers, one wavefront each: a worker walks an equal
 //                      share of all pages of all (sequence, KV head) pairs through the block
 //                      tables.  Per page it copies one 1536-byte record into an LDS ring with
@@ -56,194 +56,6 @@ __device__ __forceinline__ void split_bf16(const float w[4], uint32_t& h01, uint
   h23 = pack_bf16(w[2], w[3]);
   l01 = pack_bf16(w[0] - __uint_as_float(h01 << 16), w[1] - __uint_as_float(h01 & 0xFFFF0000u));
   l23 = pack_bf16(w[2] - __uint_as_float(h23 << 16), w[3] - __uint_as_float(h23 & 0xFFFF0000u));
-}
-
-// ------------------------------------------------------------------------ q rotation + plan
-
-// One workgroup (256 threads) per (KV head, sequence): q' = q . R_K for the G query heads of
-// the group (fp32), written to the workspace with its int8 form for the matrix cores:
-// q' ~= qsc * (hi + lo / 254), hi/lo in [-127, 127], stored in MFMA slot order, plus the
-// per-group sums of the encoded values.  Every global load is issued before its first use:
-// R_K as 16 independent float4 loads per thread (partial sums over 16 input rows, reduced
-// through LDS).  One more workgroup, (0, batch), builds the work plan of the INT2 kernel.
-constexpr int kPrepThreads = 256;
-
-// Work plan for int2_decode_kernel, built by one workgroup (kPrepThreads threads).  The INT2
-// pages of every (sequence, KV head) pair, laid end to end in (sequence, head) order, are cut
-// into runs of C pages, one run per worker; C is the smallest length that needs at most
-// `workers` runs and leaves no pair more than max_splits runs.
-__device__ void build_plan(const CacheGeom& g, const int32_t* __restrict__ seq_lens, int workers,
-                           const Workspace& ws) {
-  constexpr int kPlanWaves = kPrepThreads / 64;
-  __shared__ int s_w[2][kPlanWaves];  // per-wave sums / maxima, then per-wave scan totals
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int B = ws.batch, max_splits = ws.max_splits();
-  auto int2_pages = [&](int b, int& first) -> int {  // INT2 pages of sequence b, first page
-    const int L = max(seq_lens[b], 0);
-    const int n_sink = min(L, g.num_sink);
-    const int lo = n_sink, hi = L - min(g.window, L - n_sink);
-    first = lo / kPage;
-    if (hi <= lo || g.num_pages < 1) return 0;
-    return max(min((hi + kPage - 1) / kPage, g.max_pages) - first, 0);
-  };
-  // pass 1: total pages and the largest pair (wave reductions, then the waves in order)
-  int tot = 0, pmax = 0;
-  for (int b = t; b < B; b += kPrepThreads) {
-    int first;
-    const int P = int2_pages(b, first);
-    tot += P * g.hkv;
-    pmax = max(pmax, P);
-  }
-  for (int o = 32; o >= 1; o >>= 1) {
-    tot += __shfl_xor(tot, o);
-    pmax = max(pmax, __shfl_xor(pmax, o));
-  }
-  if (lane == 0) {
-    s_w[0][wv] = tot;
-    s_w[1][wv] = pmax;
-  }
-  __syncthreads();
-  int total = 0;
-  pmax = 0;
-  for (int k = 0; k < kPlanWaves; ++k) {
-    total += s_w[0][k];
-    pmax = max(pmax, s_w[1][k]);
-  }
-  __syncthreads();
-  long long C = max(1LL, ((long long)total + workers - 1) / workers);
-  if (max_splits > 1) C = max(C, ((long long)pmax + max_splits - 2) / (max_splits - 1));
-  else C = max(C, (long long)total);
-  // pass 2: prefix sums in chunks of kPrepThreads sequences (a wave scan, then the waves'
-  // totals in order), and the partial count of each (sequence, KV head) pair.  Page counts fit
-  // in 31 bits (the plan stores them as int32), so the run arithmetic is unsigned 32-bit.
-  int32_t* pstart = ws.pstart();
-  int32_t* npg = ws.npg();
-  int32_t* pglo = ws.pglo();
-  int32_t* nvalid = ws.nvalid();
-  const uint32_t Cu = (uint32_t)C;
-  int carry = 0;
-  for (int base = 0; base < B; base += kPrepThreads) {
-    const int b = base + t;
-    int first = 0;
-    const int P = b < B ? int2_pages(b, first) : 0;
-    const int x = P * g.hkv;
-    int incl = x;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) s_w[0][wv] = incl;
-    __syncthreads();
-    int before = 0, chunk = 0;
-    for (int k = 0; k < kPlanWaves; ++k) {
-      before += k < wv ? s_w[0][k] : 0;
-      chunk += s_w[0][k];
-    }
-    const int start = carry + before + incl - x;
-    if (b < B) {
-      pstart[b] = start;
-      npg[b] = P;
-      pglo[b] = first;
-      const uint32_t Pp = (uint32_t)P;
-      for (int h = 0; h < g.hkv; ++h) {
-        const uint32_t s0 = (uint32_t)start + (uint32_t)h * Pp;
-        nvalid[b * g.hkv + h] = Pp == 0 ? 0 : (int)((s0 + Pp - 1) / Cu - s0 / Cu + 1);
-      }
-    }
-    carry += chunk;
-    __syncthreads();
-  }
-  if (t == 0) {
-    ws.plan()[0] = total;
-    ws.plan()[1] = (int)C;
-  }
-}
-
-// hpw: query heads per workgroup, G (one workgroup per KV head) or 1 (one per query head, for
-// small batches: more workgroups, each with a quarter or less of the work).
-__global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
-    CacheGeom g, const uint16_t* __restrict__ q, const float* __restrict__ rot_k, int hq,
-    const int32_t* __restrict__ seq_lens, int workers, int hpw, Workspace ws) {
-  const int b = blockIdx.y, t = threadIdx.x;
-  if (b == ws.batch) {  // the extra row of workgroups: (0, batch) builds the plan
-    if (blockIdx.x == 0) build_plan(g, seq_lens, workers, ws);
-    return;
-  }
-  const int lane = t & 63, wv = t >> 6;
-  const int G = hq / g.hkv;
-  const int h = blockIdx.x / (G / hpw), j0 = (blockIdx.x % (G / hpw)) * hpw;
-  __shared__ __attribute__((aligned(16))) float s_q[8][kHeadDim];  // q (bf16 widened)
-  __shared__ float s_qr[8][kHeadDim];                  // q' = q . R_K
-  __shared__ float4 s_part[8][8][kHeadDim / 4];        // [input block][head][channel quad]
-
-  // Issue the R_K loads: thread -> channel quad c4 = t % 32, input block ib = t / 32 (16 rows).
-  const int c4 = t & 31, ib = t >> 5;
-  const float4* R4 = reinterpret_cast<const float4*>(rot_k + (size_t)h * kHeadDim * kHeadDim);
-  float4 r[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) r[k] = R4[(16 * ib + k) * (kHeadDim / 4) + c4];
-  for (int i = t; i < hpw * kHeadDim; i += kPrepThreads)
-    s_q[i / kHeadDim][i % kHeadDim] = bf16_to_f32(q[((size_t)b * hq + h * G + j0) * kHeadDim + i]);
-  __syncthreads();
-
-  // q' partial sums over this thread's 16 input rows (ascending), one query head at a time,
-  // its 16 q values read as four 16-byte loads; then reduce the 8 blocks in order.
-  for (int j = 0; j < hpw; ++j) {
-    const float4* qp = reinterpret_cast<const float4*>(&s_q[j][16 * ib]);
-    const float4 qv[4] = {qp[0], qp[1], qp[2], qp[3]};
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float4& q4 = qv[k >> 2];
-      const float qi = (k & 3) == 0 ? q4.x : (k & 3) == 1 ? q4.y : (k & 3) == 2 ? q4.z : q4.w;
-      a.x = fmaf(qi, r[k].x, a.x);
-      a.y = fmaf(qi, r[k].y, a.y);
-      a.z = fmaf(qi, r[k].z, a.z);
-      a.w = fmaf(qi, r[k].w, a.w);
-    }
-    s_part[ib][j][c4] = a;
-  }
-  __syncthreads();
-  for (int e = t; e < hpw * kHeadDim; e += kPrepThreads) {
-    const int j = e / kHeadDim, c = e % kHeadDim;
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s += reinterpret_cast<const float*>(&s_part[k][j][0])[c];
-    s_qr[j][c] = s;
-  }
-  __syncthreads();
-
-  // int8 form: wave wv handles heads wv, wv + 4; lane -> channels 2*lane, 2*lane + 1.
-  for (int j = wv; j < hpw; j += 4) {
-    const float v0 = s_qr[j][2 * lane], v1 = s_qr[j][2 * lane + 1];
-    float a = fmaxf(fabsf(v0), fabsf(v1));
-    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-    const float qsc = a / 127.0f;
-    char* blk = ws.qblock(b, hq, h * G + j0 + j);
-    int esum = 0;  // sum of the encoded values 254*hi + lo over this lane's two channels
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int c = 2 * lane + e;
-      const float v = e ? v1 : v0;
-      int hi = 0, lo = 0;
-      if (qsc > 0.f) {
-        hi = max(-127, min(127, (int)__builtin_rintf(v / qsc)));
-        lo = max(-127, min(127, (int)__builtin_rintf((v - (float)hi * qsc) * 254.0f / qsc)));
-      }
-      esum += 254 * hi + lo;
-      // slot order inside each 16-channel word: slot 4*i + b holds channel 4*b + i
-      const int pos = 16 * (c / 16) + 4 * (c % 4) + (c % 16) / 4;
-      blk[kQHiOff + pos] = (char)hi;
-      blk[kQLoOff + pos] = (char)lo;
-    }
-    // The zero-point term of a logit uses these sums of the encoded q' (exact integers), so
-    // that a key's code and zero parts see the same query: z*sum(q') and s*q'.codes then
-    // carry one encoding error that cancels as in q'.k, instead of two that do not.
-    for (int o = 8; o >= 1; o >>= 1) esum += __shfl_xor(esum, o);  // 16 lanes = 32 channels
-    reinterpret_cast<float2*>(blk)[lane] = make_float2(v0, v1);
-    if (lane == 0) *reinterpret_cast<float*>(blk + kQScOff) = qsc;
-    if ((lane & 15) == 0) reinterpret_cast<float*>(blk + kQSumOff)[lane >> 4] = (float)esum;
-  }
 }
 
 // ------------------------------------------------------------------------ INT2 page splits
@@ -1509,9 +1321,8 @@ int int4_resident_workers() {
 hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot_k, int batch,
                          int hq, const int32_t* seq_lens, const Workspace& ws, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv, batch + 1), dim3(kPrepThreads), 0, stream, g, q,
-                     rot_k, hq, seq_lens, 1, hq / g.hkv, ws);
-  return hipGetLastError();
+  return launch_prep_q_grid(dim3(g.hkv, batch + 1), stream, g, q, rot_k, hq, seq_lens, 1,
+                            hq / g.hkv, ws);
 }
 
 namespace {
@@ -1550,9 +1361,15 @@ hipError_t launch_decode_prep(const CacheGeom& g, const uint16_t* q, const float
                               const Workspace& ws, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   const DecodeShape s = decode_shape(g, batch, hq, num_workers);
-  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (s.G / s.hpw), batch + 1), dim3(kPrepThreads), 0,
-                     stream, g, q, rot_k, hq, seq_lens, s.workers, s.hpw, ws);
-  return hipGetLastError();
+  return launch_prep_q_grid(dim3(g.hkv * (s.G / s.hpw), batch + 1), stream, g, q, rot_k, hq,
+                            seq_lens, s.workers, s.hpw, ws);
+}
+
+void decode_prep_config(const CacheGeom& g, int batch, int hq, int num_workers, int* workers,
+                        int* hpw) {
+  const DecodeShape s = decode_shape(g, batch, hq, num_workers);
+  *workers = s.workers;
+  *hpw = s.hpw;
 }
 
 hipError_t launch_decode_main(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
@@ -1602,8 +1419,9 @@ hipError_t launch_int4_mfma_decode(const CacheGeom& g, const uint8_t* pages,
       small ? max(1, min(kWinSlots, (g.num_sink + g.window + kWinPartTokens - 1) / kWinPartTokens))
             : 1;
   const int hpw = small ? 1 : G;
-  hipLaunchKernelGGL(prep_q_kernel, dim3(g.hkv * (G / hpw), batch + 1), dim3(kPrepThreads), 0,
-                     stream, g, q, rot_k, hq, seq_lens, workers, hpw, ws);
+  const hipError_t e = launch_prep_q_grid(dim3(g.hkv * (G / hpw), batch + 1), stream, g, q, rot_k,
+                                          hq, seq_lens, workers, hpw, ws);
+  if (e != hipSuccess) return e;
   const int worker_groups = (workers + kWaves - 1) / kWaves;
   const dim3 grid(worker_groups + batch * g.hkv * wparts);
   hipLaunchKernelGGL(int4_decode_mfma_kernel, grid, dim3(64 * kWaves), 0, stream, g, pages,

@@ -110,6 +110,29 @@ hipError_t launch_append_hadamard(const CacheGeom& g, uint8_t* pages, uint16_t* 
                                   const int8_t* signs_k, const int8_t* signs_v, float clip_k,
                                   float clip_v, hipStream_t stream);
 
+// The q rotation and work plan (prep_q_kernel, step.hip) over `grid`: (Hkv * G / hpw, batch + 1)
+// workgroups, hpw query heads each; the plan is built for `workers` INT2 workers.
+hipError_t launch_prep_q_grid(dim3 grid, hipStream_t stream, const CacheGeom& g,
+                              const uint16_t* q, const float* rot_k, int hq,
+                              const int32_t* seq_lens, int workers, int hpw, const Workspace& ws);
+
+// Worker count and query heads per preparation workgroup of the INT2 decode for this launch
+// (decode.hip; the plan must be built for the decode kernel's own worker count).
+void decode_prep_config(const CacheGeom& g, int batch, int hq, int num_workers, int* workers,
+                        int* hpw);
+
+// The new rows' append (as launch_append with kAppendAuto) and the INT2 decode's query
+// preparation (as launch_decode_prep) in one launch when the append would take the 4-row vector
+// kernel, else as the two launches (step.hip).  Same bytes as the two calls.
+hipError_t launch_append_prepare(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                                 const int32_t* block_table, const int32_t* slot_ids, int batch,
+                                 int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                                 const int32_t* new_offsets, const int32_t* start_pos,
+                                 const float* rot_k, const float* rot_v, const float* k_mean,
+                                 float clip_k, float clip_v, int hq, const uint16_t* q,
+                                 const int32_t* seq_lens, int num_workers, const Workspace& ws,
+                                 hipStream_t stream);
+
 hipError_t launch_decode(const CacheGeom& g, const uint8_t* pages, const uint16_t* sinkwin,
                          const int32_t* block_table, const int32_t* slot_ids, int batch,
                          int hq, const uint16_t* q, const int32_t* seq_lens, const float* rot_k,

@@ -290,6 +290,28 @@ class DecodeStep:
             after_decode()
         self.combine_only()
 
+    def append_and_prepare(self, stream=None):
+        c = self.cache
+        ops.append_and_prepare(c.layout, c.pages, c.sinkwin, c.table, c.slots, self.k_last,
+                               self.v_last, self.new_off, self.start, c.rot_k, c.rot_v,
+                               c.p.w.clip, c.p.w.clip, self.q, self.seq_lens, self.num_workers,
+                               self.max_splits, self.ws, k_mean=c.k_mean, stream=stream)
+
+    def run_fused(self, before_decode=None, after_decode=None):
+        """The step with the append and the query preparation in one call
+        (oscar_append_and_prepare), then decode and combine, on the current stream; the same
+        bytes as run_split().  INT2 caches with a dense rotation only."""
+        c = self.cache
+        if c.bits != 2 or c.hadamard:
+            raise ValueError("run_fused: INT2 caches with a dense rotation only")
+        self.append_and_prepare()
+        if before_decode is not None:
+            before_decode()
+        self.decode_prepared()
+        if after_decode is not None:
+            after_decode()
+        self.combine_only()
+
     def run_overlapped(self, before_decode=None, after_decode=None):
         """append || prepare, then decode and combine on the current stream.  before_decode()
         and after_decode(), if given, run on the current stream right before and after the

@@ -37,6 +37,7 @@ EXPORTED = (
     "oscar_decode_attention_static",
     "oscar_prepare_queries",
     "oscar_decode_attention_prepared",
+    "oscar_append_and_prepare",
 )
 
 STATIC_WORKSPACE_BYTES = 32 << 20   # OSCAR_STATIC_WORKSPACE_BYTES
@@ -107,6 +108,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oscar_decode_attention.restype = I32
     lib.oscar_prepare_queries.argtypes = [LP, I32, I32, P, P, P, I32, I32, P, SZ, P]
     lib.oscar_prepare_queries.restype = I32
+    lib.oscar_append_and_prepare.argtypes = [LP, P, P, P, P, I32, I32, P, P, P, P, P, P, P, F32,
+                                             F32, I32, P, P, I32, I32, P, SZ, P]
+    lib.oscar_append_and_prepare.restype = I32
     lib.oscar_decode_attention_prepared.argtypes = [LP, P, P, P, P, I32, I32, P, F32, I32, I32, P,
                                                     SZ, P]
     lib.oscar_decode_attention_prepared.restype = I32
@@ -250,6 +254,28 @@ def prepare_queries(lay: Layout, q, seq_lens, rot_k, num_workers: int, max_split
         _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(rot_k, torch.float32, "rot_k"),
         num_workers, max_splits, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream)))
+
+
+def append_and_prepare(lay: Layout, pages, sinkwin, block_table, slot_ids, k_new, v_new,
+                       new_offsets, start_pos, rot_k, rot_v, clip_k: float, clip_v: float, q,
+                       seq_lens, num_workers: int, max_splits: int, workspace, k_mean=None,
+                       stream=None) -> None:
+    """rotate_quantize_append (APPEND_AUTO) of this step's new rows and prepare_queries of the
+    same batch in one call (one launch below 256 new rows); batch = start_pos.numel() =
+    q.shape[0]."""
+    lib = load_library()
+    batch, hq = q.shape[0], q.shape[1]
+    if start_pos.numel() != batch:
+        raise ValueError("append_and_prepare: start_pos and q disagree on the batch")
+    _check("oscar_append_and_prepare", lib.oscar_append_and_prepare(
+        ctypes.byref(lay), _ptr(pages, torch.uint8, "pages"), _ptr(sinkwin, torch.int16, "sinkwin"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(slot_ids, torch.int32, "slot_ids"),
+        batch, k_new.shape[0], _ptr(k_new, torch.int16, "k_new"), _ptr(v_new, torch.int16, "v_new"),
+        _ptr(new_offsets, torch.int32, "new_offsets"), _ptr(start_pos, torch.int32, "start_pos"),
+        _ptr(rot_k, torch.float32, "rot_k"), _ptr(rot_v, torch.float32, "rot_v"),
+        _ptr(k_mean, torch.float32, "k_mean"), float(clip_k), float(clip_v), hq,
+        _ptr(q, torch.int16, "q"), _ptr(seq_lens, torch.int32, "seq_lens"), num_workers,
+        max_splits, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def decode_attention_prepared(lay: Layout, pages, sinkwin, block_table, slot_ids, batch: int,

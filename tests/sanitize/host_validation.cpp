@@ -356,6 +356,41 @@ void decode_cases() {
   }
 }
 
+void append_prepare_cases() {
+  const oscar_layout lay = layout();
+  auto call = [&](int32_t batch, int32_t total, int32_t hq, void* pages, void* k, void* km,
+                  float ck, void* q, void* ws, size_t wsb, int32_t nw, int32_t ms) {
+    return oscar_append_and_prepare(&lay, p<uint8_t>(pages), p<uint16_t>(A), p<int32_t>(A),
+                                    nullptr, batch, total, p<uint16_t>(k), p<uint16_t>(A),
+                                    p<int32_t>(A), p<int32_t>(A), p<float>(A), p<float>(A),
+                                    p<float>(km), ck, 0.9f, hq, p<uint16_t>(q), p<int32_t>(A), nw,
+                                    ms, ws, wsb, nullptr);
+  };
+  expect("append_prepare: valid, one launch", call(64, 64, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), HIP);
+  expect("append_prepare: valid, 255 rows", call(64, 255, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), HIP);
+  expect("append_prepare: valid, two launches", call(64, 256, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), HIP);
+  expect("append_prepare: valid, key mean", call(4, 4, 32, A, A, A, 1.0f, A, A, kBig, 0, 4), HIP);
+  expect("append_prepare: no new rows", call(4, 0, 32, nullptr, nullptr, nullptr, 1.0f, A, A, kBig, 0, 4), HIP);
+  expect("append_prepare: G 8", call(4, 4, 64, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), HIP);
+  expect("append_prepare: 2^27 rows", call(1 << 22, 64, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), UNS);
+  expect("append_prepare: batch 0", call(0, 64, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), OK);
+  expect("append_prepare: batch -1", call(-1, 64, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: total -1", call(4, -1, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: total INT_MAX", call(4, INT_MAX, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), UNS);
+  expect("append_prepare: hq 30", call(4, 4, 30, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: hq 24", call(4, 4, 24, A, A, nullptr, 1.0f, A, A, kBig, 0, 4), UNS);
+  expect("append_prepare: clip 0", call(4, 4, 32, A, A, nullptr, 0.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: clip NaN", call(4, 4, 32, A, A, nullptr, NAN, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: pages null", call(4, 4, 32, nullptr, A, nullptr, 1.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: k misaligned", call(4, 4, 32, A, MIS, nullptr, 1.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: key mean misaligned", call(4, 4, 32, A, A, MIS2, 1.0f, A, A, kBig, 0, 4), INV);
+  expect("append_prepare: q null", call(4, 4, 32, A, A, nullptr, 1.0f, nullptr, A, kBig, 0, 4), INV);
+  expect("append_prepare: workspace small", call(4, 4, 32, A, A, nullptr, 1.0f, A, A, 100, 0, 4), SMALL);
+  expect("append_prepare: workspace misaligned", call(4, 4, 32, A, A, nullptr, 1.0f, A, MIS, kBig, 0, 4), INV);
+  expect("append_prepare: workers -1", call(4, 4, 32, A, A, nullptr, 1.0f, A, A, kBig, -1, 4), INV);
+  expect("append_prepare: max_splits 65536", call(4, 4, 32, A, A, nullptr, 1.0f, A, A, kBig, 0, 65536), INV);
+}
+
 void combine_cases() {
   auto comb = [](int32_t batch, int32_t hq, int32_t hkv, int32_t ms, void* ws, size_t wsb,
                  void* rv, void* out) {
@@ -449,6 +484,7 @@ int main() {
   layout_cases();
   append_cases();
   decode_cases();
+  append_prepare_cases();
   combine_cases();
   workspace_cases();
   probe_cases();

@@ -239,3 +239,47 @@ def test_prepare_and_prepared_decode_validation(lib):
     assert dec(sw=None) == 1               # the layout has sink/window rows
     for bad in (float("nan"), float("inf"), 0.0, -1.0):
         assert dec(sm=bad) == 1
+
+
+def test_append_and_prepare_validation(lib):
+    lay = _layout()
+
+    def call(**kw):
+        a = dict(pages=FAKE, sw=FAKE, bt=FAKE, batch=1, total=1, k=FAKE, v=FAKE, off=FAKE,
+                 start=FAKE, rk=FAKE, rv=FAKE, km=None, ck=0.95, cv=0.95, hq=32, q=FAKE,
+                 lens=FAKE, nw=0, ms=4, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.oscar_append_and_prepare(
+            ctypes.byref(lay), a["pages"], a["sw"], a["bt"], None, a["batch"], a["total"], a["k"],
+            a["v"], a["off"], a["start"], a["rk"], a["rv"], a["km"], a["ck"], a["cv"], a["hq"],
+            a["q"], a["lens"], a["nw"], a["ms"], a["ws"], a["wsb"], None)
+
+    # the query preparation's checks
+    assert call(hq=30) == 1
+    assert call(hq=24) == 2
+    assert call(nw=-1) == 1
+    assert call(ms=0) == 1
+    assert call(q=None) == 1
+    assert call(lens=None) == 1
+    assert call(rk=None) == 1
+    assert call(ws=None) == 1
+    assert call(ws=ctypes.c_void_p(20)) == 1
+    assert call(wsb=100) == 3
+    assert call(batch=(1 << 22) + 1) == 2          # more than 2^27 query rows
+    # the append's checks
+    assert call(total=-1) == 1
+    assert call(total=(1 << 30) + 1) == 2
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert call(ck=bad) == 1
+        assert call(cv=bad) == 1
+    assert call(pages=None) == 1
+    assert call(bt=None) == 1
+    assert call(k=None) == 1
+    assert call(v=None) == 1
+    assert call(off=None) == 1
+    assert call(start=None) == 1
+    assert call(rv=None) == 1
+    assert call(sw=None) == 1                      # the layout has sink/window rows
+    assert call(k=ctypes.c_void_p(20)) == 1        # misaligned
+    assert call(km=ctypes.c_void_p(18)) == 1       # misaligned key mean
+    assert call(batch=0) == 0
