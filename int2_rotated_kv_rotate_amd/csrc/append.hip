@@ -47,21 +47,30 @@ __global__ __launch_bounds__(kAppendThreads) void rotate_quantize_append_kernel(
 
 // ------------------------------------------------------------ matrix cores (many rows)
 //
-// A workgroup of 8 waves serves one (KV head, K|V) and loops over 64-row tiles.  Wave w owns
-// output channels 16w .. 16w+15: its A operands are the rows of R^T for those channels, split
-// exactly into three bf16 pieces (R = p0 + p1 + p2: 24 significand bits in three 8-bit pieces)
-// and held in registers for the whole loop.  The B operand is the bf16 input rows (exact) from
-// LDS.  For each 32-channel slice s of the input, three v_mfma_f32_16x16x32_bf16 accumulate
-// p2, p1 and p0 (small pieces first) into a slice accumulator, and y = (a0 + a1) + (a2 + a3).
+// A workgroup of four waves serves one (KV head, K|V) and loops over blocks of 32 rows.  Wave g
+// owns group g (output channels 32g .. 32g+31) of every row of the block, so a group's
+// extremes, scale, zero and codes, and the values it must recompute, stay inside one wave.  The
+// wave's A operands are the rows of R^T for its channels, split exactly into three bf16 pieces
+// (R = p0 + p1 + p2: 24 significand bits in three 8-bit pieces) and held in registers for the
+// whole loop; the B operand is the bf16 input rows (exact), loaded from memory a block ahead.
+// Twelve v_mfma_f32_16x16x32_bf16 accumulate one 16 x 16 tile into one fp32 accumulator: the p2
+// pieces of the four 32-channel input slices first, then p1, then p0.  The same instruction with
+// the input rows as both operands gives the diagonal of their Gram matrix, i.e. the rows'
+// squared norms.
 //
 // Error bound.  The products are exact.  Measured on gfx950, one such instruction runs four
 // passes over its 8-product blocks; a pass adds its products, aligned to the largest of them
-// (bits below 2^-24 of it dropped), to the accumulator with one fp32 round-to-nearest.  Per
-// slice that is at most 7u sum|terms| of dropped bits (u = 2^-24) and, since the small pieces
-// come first, about 4.1u sum|terms| of rounding; the two levels of fp32 additions and the
-// defined value's own rounding to fp32 add 3u.  So |y_mc - y| <= 14.1 u sum_i |x_i R_ij| <=
-// 14.1 u ||x|| ||R_.j||.  The kernel takes E = 64 u ||x|| ||R_.j|| plus 2^-100 for flushed
+// (bits below 2^-24 of it dropped), to the accumulator with one fp32 round-to-nearest.  Every
+// product is in one block, so the dropped bits total at most 7u sum|terms| (u = 2^-24; the
+// terms are the products of all three pieces, sum|terms| <= (1 + 2^-7) sum_i |x_i R_ij|).  Of
+// the accumulator's 48 roundings, the 16 of the p0 passes are each at most u/2 of a partial sum
+// <= sum|terms| (8u), the 32 before them act on partial sums below 2^-7 sum|terms| (0.13u), and
+// the defined value's own rounding to fp32 adds u/2.  So |y_mc - y| <= 16 u sum_i |x_i R_ij| <=
+// 16 u ||x|| ||R_.j||.  The kernel takes E = 64 u ||x|| ||R_.j|| plus 2^-100 for flushed
 // subnormals, computed 5% high so that y -+ E rounded to nearest still encloses [y - E, y + E].
+// ||x|| is bounded from the Gram diagonal: its terms are positive, so by the same model it is
+// within 15u of the sum of squares, less at most 2^-122 of flushed subnormal partial sums; the
+// bound takes it 1e-4 high plus 2^-121.
 //
 // Certification (each output is a monotone function of the values it reads):
 //   * s16, z16 of a group: equal at the ends of the extremes' intervals [m - E, m + E], else
@@ -74,13 +83,20 @@ __global__ __launch_bounds__(kAppendThreads) void rotate_quantize_append_kernel(
 //     lies within mt of t (which includes the boundaries 1/2, 3/2, 5/2), else recomputed;
 //   * a BF16 copy (sink/window row): certified when bf16(y - E) == bf16(y + E), else recomputed.
 //
-// Recomputation reads R (fp32) from LDS, where the workgroup stages it once; four lanes share a
-// value and the midpoint argument below keeps the result the defined one.
-constexpr int kPTile = 64;
-constexpr int kPThreads = 512;
-constexpr int kXStride = kHeadDim + 8;   // bf16 per LDS row of x: 16-byte rows, skewed banks
-constexpr int kYStride = kHeadDim + 4;   // floats per LDS row of y
-constexpr int kExact = 0x80;             // s_code mark: s_y holds the defined value
+// Recomputation: a wave lists the values it cannot certify in LDS and recomputes them itself,
+// 4 to 16 lanes per value, with R from the workgroup's copy of R^T in LDS (the midpoint argument
+// at recompute_wave keeps the result the defined one).
+//
+// A V record holds every group's codes in each 16-bit half, so the four waves of a V workgroup
+// hand their code pairs to each other through LDS once per block (one barrier); K words,
+// scale/zero words and BF16 copies are written by the wave that owns the group.  With 79 KB of
+// LDS (R^T in fp32 for the recomputation) two workgroups fit on a CU.
+constexpr int kMWaves = kGroups;          // one wave per 32-channel group
+constexpr int kMThreads = 64 * kMWaves;
+constexpr int kMBlock = 32;               // rows per block: two 16-row tiles of MFMA columns
+constexpr int kRtStride = kHeadDim + 4;   // floats per LDS row of R^T: the 16-byte reads of
+                                          // different rows start on different banks
+constexpr int kMListCap = 256;            // values a wave recomputes per round
 constexpr float kErrScale = 64.0f * 0x1p-24f * 1.05f;
 constexpr float kErrAbs = 0x1p-100f * 1.05f;
 
@@ -95,60 +111,182 @@ __device__ __forceinline__ float down(float x) { return -up(-x); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-constexpr int kRStride = kHeadDim + 1;   // floats per LDS row of R: column reads spread banks
-constexpr int kListCap = kPTile * kHeadDim;
+// The ||x|| bound from the Gram diagonal d2 (see above); +inf when d2 overflowed.
+__device__ __forceinline__ float norm_bound(float d2) {
+  return __builtin_sqrtf(d2 * 1.0001f + 0x1p-121f) * 1.0001f;
+}
 
-// Recompute the listed (row, channel) values as defined, four lanes per value: lane q sums the
-// products of inputs 32q .. 32q+31 in fp64, and the four partial sums are combined.  That sum
-// differs from the defined ascending one by at most 2 * 127 * 2^-53 sum|terms| <= 2^-45 ||x||
-// ||R_.c||, and after the fp64 subtraction of the key-mean term C_c (0 without a mean) by at
-// most that plus two fp64 ulps.  Unless it lies that close to a midpoint between fp32 values or
-// to zero (where the sign of a zero result is decided), both round to the same fp32 value, and
-// the rare value that close is summed again in ascending order.  `pass2` also recodes the
-// values (the defined formula); otherwise they are marked exact.
-// Called by all threads of the workgroup.
-__device__ void recompute_listed(const uint16_t* __restrict__ list, int n,
-                                 const float (*s_rot)[kRStride], const uint16_t (*s_x)[kXStride],
-                                 const double* s_cd, const float* s_nrm, const float* s_cng,
-                                 float (*s_y)[kYStride], uint8_t (*s_code)[kHeadDim],
-                                 const float2 (*s_sz)[kGroups], bool pass2) {
-  const int t = threadIdx.x, q = t & 3;
-  for (int k0 = 0; k0 < n; k0 += kPThreads / 4) {
-    const int k = k0 + (t >> 2);
+// Orders this wave's LDS accesses: the stores before it are complete and visible to its loads
+// after it (every lane of the wave; no other wave reads these arrays).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+struct alignas(16) MatrixShared {
+  float rt[kHeadDim][kRtStride];          // R^T (fp32): rt[c][i] = R[i][c]
+  double cd[kHeadDim];                    // C = mu . R (fp64, i ascending), 0 without a key mean
+  float cf[kHeadDim];                     // fp32(C)
+  float nrm[kMWaves][kMBlock];            // per wave: the ||x|| bound of each row of the block
+  uint16_t list[kMWaves][kMListCap];      // per wave: values to recompute, 32 row + channel
+  float res[kMWaves][kMListCap];          // their defined values
+  uint32_t vn[2][kMWaves][kMBlock][4];    // V code pairs [buffer][group g][row]: byte c % 4 of
+                                          // word c / 4 = code(32g + c) | code(32g + 16 + c) << 2
+};
+
+// Recompute n listed values of one wave as defined, L lanes per value: lane q sums the products
+// of inputs (128/L) q .. (128/L)(q+1) - 1 in fp64 (exact products), and the L partial sums are
+// combined.  That sum differs from the defined ascending one by at most
+// 2 * 127 * 2^-53 sum|terms| <= 2^-45 ||x|| ||R_.c||, and after the fp64 subtraction of the
+// key-mean term C_c (0 without a mean) by at most that plus two fp64 ulps.  Unless it lies that
+// close to a midpoint between fp32 values or to zero (where the sign of a zero result is
+// decided), both round to the same fp32 value, and the rare value that close is summed again in
+// ascending order.  Entry k = 32 r + c (row r of the block at n0, channel c of group gq) gets its
+// value in res[k].
+template <int L>
+__device__ __forceinline__ void recompute_wave(const uint16_t* list, float* res, int n,
+                               const uint16_t* __restrict__ src, int hkv, int h, int n0, int gq,
+                               const float (*rt)[kRtStride], const double* cd, const float* nrm,
+                               float cng, int lane) {
+  constexpr int kIn = kHeadDim / L;   // inputs per lane: 8, 16 or 32
+  const int q = lane & (L - 1);
+  for (int k0 = 0; k0 < n; k0 += 64 / L) {
+    const int k = k0 + lane / L;
     const bool act = k < n;
-    const int it = act ? list[k] : 0;
-    const int r = it / kHeadDim, c = it % kHeadDim;
-    double part = 0.0;
+    const int e = act ? list[k] : 0;
+    const int r = e >> 5, c = kGroup * gq + (e & 31);
+    const uint16_t* xrow = src + ((size_t)(n0 + r) * hkv + h) * kHeadDim;
+    double part = 0.0, part2 = 0.0;
     if (act) {
+      uint4 xv[kIn / 8];   // all of the lane's inputs in flight at once
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(&s_x[r][32 * q + 8 * j]);
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      for (int j = 0; j < kIn / 8; ++j) xv[j] = *reinterpret_cast<const uint4*>(xrow + kIn * q + 8 * j);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = e & 1 ? bf16_hi(xw[e / 2]) : bf16_lo(xw[e / 2]);
-          part = __fma_rn((double)x, (double)s_rot[32 * q + 8 * j + e][c], part);
+      for (int j = 0; j < kIn / 8; ++j) {   // inputs kIn q + 8j .. + 7
+        __builtin_amdgcn_sched_barrier(0);   // eight products at a time: few registers live
+        const uint32_t xw[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+        const float4* rp = reinterpret_cast<const float4*>(&rt[c][kIn * q + 8 * j]);
+        const float4 r0 = rp[0], r1 = rp[1];
+        const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {   // two chains: even and odd inputs
+          part = __fma_rn((double)bf16_lo(xw[u / 2]), (double)rr[u], part);
+          part2 = __fma_rn((double)bf16_hi(xw[u / 2]), (double)rr[u + 1], part2);
         }
       }
     }
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
+    part += part2;
+    part += lane_xor_f64<1>(part);
+    part += lane_xor_f64<2>(part);
+    if constexpr (L >= 8) part += lane_xor_f64<4>(part);
+    if constexpr (L >= 16) part += lane_xor_f64<8>(part);
     if (act && q == 0) {
-      const double v = part - s_cd[c];
+      const double v = part - cd[c];
       float f = (float)v;
-      const double tol = (double)s_nrm[r] * (double)s_cng[c / kGroup] * 0x1p-44 + fabs(v) * 0x1p-50;
+      const double tol = (double)nrm[r] * (double)cng * 0x1p-44 + fabs(v) * 0x1p-50;
       const double m_lo = ((double)f + (double)down(f)) * 0.5;
       const double m_hi = ((double)f + (double)up(f)) * 0.5;
       if (fabs(v - m_lo) <= tol || fabs(v - m_hi) <= tol || fabs(v) <= tol) {
         double acc = 0.0;
         for (int i = 0; i < kHeadDim; ++i)
-          acc = __fma_rn((double)bf16_to_f32(s_x[r][i]), (double)s_rot[i][c], acc);
-        f = (float)(acc - s_cd[c]);
+          acc = __fma_rn((double)bf16_to_f32(xrow[i]), (double)rt[c][i], acc);
+        f = (float)(acc - cd[c]);
       }
-      s_y[r][c] = f;
-      const float2 sz = s_sz[r][c / kGroup];
-      s_code[r][c] = pass2 ? (uint8_t)code_of(f, sz.x, sz.y) : (uint8_t)kExact;
+      res[k] = f;
     }
+  }
+}
+
+// Inclusive prefix sum over the wave's lanes (row shifts within 16-lane rows, then the row
+// broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Replace this wave's flagged values by the defined ones.  Bit v = 8 tb + 4 cb + i of fl: the
+// lane's value y[v], row 16 tb + m of the block, channel 16 cb + 4 kq + i of the group.  The
+// wave's flagged values are numbered lane first, then value index, and recomputed in rounds of
+// up to kMListCap.  RECODE: also replace their codes (bits 2v of cw) by the defined ones, with
+// the rows' scale sc and zero zz.
+template <bool RECODE>
+__device__ __forceinline__ void recompute_flagged(uint32_t fl, float (&y)[16], uint32_t& cw,
+                                                  const float sc[2], const float zz[2],
+                                                  uint16_t* list, float* res,
+                                                  const uint16_t* __restrict__ src, int hkv, int h,
+                                                  int n0, int gq, const float (*rt)[kRtStride],
+                                                  const double* cd, const float* nrm, float cng,
+                                                  int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  const int cnt = __builtin_popcount(fl);
+  const int incl = wave_scan(cnt);
+  const int excl = incl - cnt;
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  uint32_t wor = fl;   // the value indices flagged in any lane
+  wor |= lane_xor<1>(wor);
+  wor |= lane_xor<2>(wor);
+  wor |= lane_xor<4>(wor);
+  wor |= lane_xor<8>(wor);
+  wor |= lane_xor<16>(wor);
+  wor |= lane_xor<32>(wor);
+  wor = __builtin_amdgcn_readfirstlane(wor);
+  for (int r0 = 0; r0 < total; r0 += kMListCap) {
+    {
+      uint32_t f = fl;
+      int p = excl - r0;
+      while (f != 0u) {
+        const int v = __builtin_ctz(f);
+        f &= f - 1u;
+        if (p >= 0 && p < kMListCap)
+          list[p] = (uint16_t)(kGroup * (16 * (v >> 3) + m) + 16 * ((v >> 2) & 1) + 4 * kq + (v & 3));
+        ++p;
+      }
+    }
+    wave_lds_sync();
+    // as many lanes per value as fill the wave in one step (at least 4)
+    const int nr = min(kMListCap, total - r0);
+    if (nr <= 4)
+      recompute_wave<16>(list, res, nr, src, hkv, h, n0, gq, rt, cd, nrm, cng, lane);
+    else if (nr <= 8)
+      recompute_wave<8>(list, res, nr, src, hkv, h, n0, gq, rt, cd, nrm, cng, lane);
+    else
+      recompute_wave<4>(list, res, nr, src, hkv, h, n0, gq, rt, cd, nrm, cng, lane);
+    wave_lds_sync();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if ((wor >> v) & 1u) {
+        const int p = excl + __builtin_popcount(fl & ((1u << v) - 1u)) - r0;
+        if (((fl >> v) & 1u) && p >= 0 && p < kMListCap) {
+          y[v] = res[p];
+          if (RECODE) {
+            const int code = code_of(y[v], v >> 3 ? sc[1] : sc[0], v >> 3 ? zz[1] : zz[0]);
+            cw = (cw & ~(3u << (2 * v))) | ((uint32_t)code << (2 * v));
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+}
+
+// Group extremes of the lane's rows (tb = 0, 1) over the four lanes kq of each row.
+__device__ __forceinline__ void group_extremes(const float (&y)[16], float mx[2], float mn[2]) {
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    float a = y[8 * tb], b = y[8 * tb];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      a = fmaxf(a, y[8 * tb + j]);
+      b = fminf(b, y[8 * tb + j]);
+    }
+    a = fmaxf(a, lane_xor_f32<16>(a));
+    b = fminf(b, lane_xor_f32<16>(b));
+    a = fmaxf(a, lane_xor_f32<32>(a));
+    b = fminf(b, lane_xor_f32<32>(b));
+    mx[tb] = a;
+    mn[tb] = b;
   }
 }
 
@@ -172,7 +310,7 @@ __device__ int advance_seq(const int32_t* __restrict__ off, int batch, int seq, 
   return lo;
 }
 
-__global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
+__global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
     CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
     int total_new, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -180,24 +318,9 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     const float* __restrict__ rot_k, const float* __restrict__ rot_v,
     const float* __restrict__ k_mean, float clip_k, float clip_v, int k_groups) {
 #pragma clang fp contract(off)
-  __shared__ float s_rot[kHeadDim][kRStride];  // R (fp32), for the A operands and recomputation
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[kPTile][kXStride];
-  __shared__ __attribute__((aligned(16))) float s_y[kPTile][kYStride];
-  __shared__ __attribute__((aligned(16))) uint8_t s_code[kPTile][kHeadDim];
-  __shared__ float2 s_sz[kPTile][kGroups];     // (scale, zero) of each group, fp32
-  __shared__ uint16_t s_list[kListCap];        // (row, channel) to recompute: 128 r + c
-  __shared__ RowInfo s_info[kPTile];
-  __shared__ float s_err[kPTile];              // 64 u ||x|| per row, 5% high
-  __shared__ float s_nrm[kPTile];              // ||x|| per row (rounded up)
-  __shared__ float s_cng[kGroups];             // the largest ||R_.j|| of each group (rounded up)
-  __shared__ float s_mu[kHeadDim];             // key mean (centered K only)
-  __shared__ double s_cd[kHeadDim];            // C = mu . R (fp64; 0 without a mean)
-  __shared__ __attribute__((aligned(16))) float s_cf[kHeadDim];  // fp32(C)
-  __shared__ float s_cmax[kGroups];            // the largest |fp32(C_j)| of each group
-  __shared__ int s_n[2];                       // list lengths of the two passes
-
+  __shared__ MatrixShared sm;
   const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int gq = __builtin_amdgcn_readfirstlane(t >> 6);   // this wave's group
   const int h = blockIdx.y;
   // workgroups [0, k_groups) of a KV head serve its K rows, the rest its V rows; x0 is this
   // workgroup's index among the G of its (head, K|V) pair
@@ -207,165 +330,196 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
   const float* rot = (is_v ? rot_v : rot_k) + (size_t)h * kHeadDim * kHeadDim;
   const uint16_t* src = is_v ? v_new : k_new;
   const float clip = is_v ? clip_v : clip_k;
-  const int m = lane & 15, kq = lane >> 4;
   const bool centered = !is_v && k_mean != nullptr;
-  if (centered && t < kHeadDim) s_mu[t] = k_mean[(size_t)h * kHeadDim + t];
+  const bool has_store = sinkwin != nullptr;
+  const int m = lane & 15, kq = lane >> 4;
 
-  // Stage R: all 8 float4 loads of a thread first, then the (unaligned-row) LDS stores.
+  // Stage R^T: all 16 float4 loads of a thread first, then the transposed LDS stores.
   {
-    constexpr int kPer = kHeadDim * kHeadDim / 4 / kPThreads;  // 8
+    constexpr int kPer = kHeadDim * kHeadDim / 4 / kMThreads;  // 16
     const float4* rot4 = reinterpret_cast<const float4*>(rot);
     float4 rr[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) rr[k] = rot4[t + kPThreads * k];
+    for (int k = 0; k < kPer; ++k) rr[k] = rot4[t + kMThreads * k];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const int e = 4 * (t + kPThreads * k), i = e / kHeadDim, j = e % kHeadDim;
-      s_rot[i][j] = rr[k].x;
-      s_rot[i][j + 1] = rr[k].y;
-      s_rot[i][j + 2] = rr[k].z;
-      s_rot[i][j + 3] = rr[k].w;
+      const int e = 4 * (t + kMThreads * k), i = e / kHeadDim, j = e % kHeadDim;
+      sm.rt[j][i] = rr[k].x;
+      sm.rt[j + 1][i] = rr[k].y;
+      sm.rt[j + 2][i] = rr[k].z;
+      sm.rt[j + 3][i] = rr[k].w;
     }
   }
   __syncthreads();
-  if (t < kHeadDim) {  // column norms (squared), parked in s_y before its first use
+
+  // The group's largest column norm (rounded up) and key-mean terms: lane l takes column
+  // 32g + l % 32 (the upper half of the wave repeats the lower).
+  float cng, cmax;
+  {
+    const int c = kGroup * gq + (lane & 31);
     float ss = 0.f;
-    for (int i = 0; i < kHeadDim; ++i) ss = fmaf(s_rot[i][t], s_rot[i][t], ss);
-    s_y[0][t] = ss;
-    // key mean: C_t = sum_i mu_i R_it, fp64, i ascending (exact products)
-    double cd = 0.0;
-    if (centered)
-      for (int i = 0; i < kHeadDim; ++i) cd = __fma_rn((double)s_mu[i], (double)s_rot[i][t], cd);
-    s_cd[t] = cd;
-    s_cf[t] = (float)cd;
+    double cdv = 0.0;
+    for (int i = 0; i < kHeadDim; ++i) ss = fmaf(sm.rt[c][i], sm.rt[c][i], ss);
+    if (centered)   // C_c = sum_i mu_i R_ic, fp64, i ascending (exact products)
+      for (int i = 0; i < kHeadDim; ++i)
+        cdv = __fma_rn((double)k_mean[(size_t)h * kHeadDim + i], (double)sm.rt[c][i], cdv);
+    if (lane < 32) {
+      sm.cd[c] = cdv;
+      sm.cf[c] = (float)cdv;
+    }
+    float cm = fabsf((float)cdv);
+    ss = fmaxf(ss, lane_xor_f32<1>(ss));
+    cm = fmaxf(cm, lane_xor_f32<1>(cm));
+    ss = fmaxf(ss, lane_xor_f32<2>(ss));
+    cm = fmaxf(cm, lane_xor_f32<2>(cm));
+    ss = fmaxf(ss, lane_xor_f32<4>(ss));
+    cm = fmaxf(cm, lane_xor_f32<4>(cm));
+    ss = fmaxf(ss, lane_xor_f32<8>(ss));
+    cm = fmaxf(cm, lane_xor_f32<8>(cm));
+    ss = fmaxf(ss, lane_xor_f32<16>(ss));
+    cm = fmaxf(cm, lane_xor_f32<16>(cm));
+    cng = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__builtin_sqrtf(ss) * 1.001f)));
+    cmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cm)));
   }
   __syncthreads();
-  if (t < kGroups) {   // the largest per group, rounded up
-    float cm = 0.f, cc = 0.f;
-    for (int c = kGroup * t; c < kGroup * (t + 1); ++c) {
-      cm = fmaxf(cm, s_y[0][c]);
-      cc = fmaxf(cc, fabsf(s_cf[c]));
-    }
-    s_cng[t] = __builtin_sqrtf(cm) * 1.001f;
-    s_cmax[t] = cc;
-  }
-  __syncthreads();
-  // fp32(C) of this lane's four output channels (16w + 4kq + i), subtracted from the matrix-core
-  // sums; 0 without a mean
-  const float4 cfl = *reinterpret_cast<const float4*>(&s_cf[16 * wave + 4 * kq]);
-
-  // A operands: lane (m, kq), slice s holds R[32s + 8kq + e][16w + m], e = 0..7, as 3 pieces.
-  v8bf ra[4][3];
+  // A operands: lane (m, kq), channel block cb, slice s holds R[32s + 8kq + e][32g + 16cb + m],
+  // e = 0..7, as 3 pieces.
+  v8bf ra[2][4][3];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint16_t pc[3][8];
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float r0 = s_rot[32 * s + 8 * kq + e][16 * wave + m];
-      pc[0][e] = f32_to_bf16_rne(r0);
-      const float r1 = r0 - bf16_to_f32(pc[0][e]);
-      pc[1][e] = f32_to_bf16_rne(r1);
-      pc[2][e] = f32_to_bf16_rne(r1 - bf16_to_f32(pc[1][e]));
-    }
+    for (int s = 0; s < 4; ++s) {
+      const float* rp = &sm.rt[kGroup * gq + 16 * cb + m][32 * s + 8 * kq];
+      const float4 r0 = *reinterpret_cast<const float4*>(rp);
+      const float4 r1 = *reinterpret_cast<const float4*>(rp + 4);
+      const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      uint16_t pc[3][8];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      uint4 w;
-      w.x = pc[q][0] | ((uint32_t)pc[q][1] << 16);
-      w.y = pc[q][2] | ((uint32_t)pc[q][3] << 16);
-      w.z = pc[q][4] | ((uint32_t)pc[q][5] << 16);
-      w.w = pc[q][6] | ((uint32_t)pc[q][7] << 16);
-      ra[s][q] = __builtin_bit_cast(v8bf, w);
+      for (int e = 0; e < 8; ++e) {
+        pc[0][e] = f32_to_bf16_rne(rv[e]);
+        const float d1 = rv[e] - bf16_to_f32(pc[0][e]);
+        pc[1][e] = f32_to_bf16_rne(d1);
+        pc[2][e] = f32_to_bf16_rne(d1 - bf16_to_f32(pc[1][e]));
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        uint4 w;
+        w.x = pc[p][0] | ((uint32_t)pc[p][1] << 16);
+        w.y = pc[p][2] | ((uint32_t)pc[p][3] << 16);
+        w.z = pc[p][4] | ((uint32_t)pc[p][5] << 16);
+        w.w = pc[p][6] | ((uint32_t)pc[p][7] << 16);
+        ra[cb][s][p] = __builtin_bit_cast(v8bf, w);
+      }
     }
-  }
 
-  const int ntiles = (total_new + kPTile - 1) / kPTile;
-  const bool has_store = sinkwin != nullptr;
+  const int ntiles = (total_new + kMBlock - 1) / kMBlock;
+  // Block order: round k takes tile k * G + (x + k) mod G (G workgroups per pair, x this one),
+  // one tile of each span of G; the rotation spreads tiles that cost more (the last rows of
+  // every sequence, whose BF16 copies are certified too) over all workgroups.  Successive tiles
+  // of a workgroup increase, as the placement look-ahead needs.
+  auto tile_of = [&](int k) { return k * G + (x0 + k) % G; };   // tile_of(0) == x0
 
-  // Software pipeline over the tiles: while tile k is processed, its successor's input rows are
-  // in flight into registers, and threads t < 64 look up the successor's row placements in
-  // stages (one dependent load per stage, each consumed a phase later).
-  auto load_rows = [&](int tl, uint4& a0, uint4& a1) {
-    const int r = t >> 3, q = t & 7, n = tl * kPTile + r;
-    a0 = uint4{0, 0, 0, 0};
-    a1 = uint4{0, 0, 0, 0};
-    if (tl < ntiles && n < total_new) {
-      const uint4* rp = reinterpret_cast<const uint4*>(src + ((size_t)n * g.hkv + h) * kHeadDim);
-      a0 = rp[q];
-      a1 = rp[q + 8];
+  // B operands of a block: lane (m, kq), row 16 tb + m, slice s holds inputs 32s + 8kq .. +7.
+  uint4 xs[2][4];
+  auto load_x = [&](int tile) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int n = tile * kMBlock + 16 * tb + m;
+      if (tile < ntiles && n < total_new) {
+        const uint4* rp = reinterpret_cast<const uint4*>(src + ((size_t)n * g.hkv + h) * kHeadDim + 8 * kq);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xs[tb][s] = rp[4 * s];
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xs[tb][s] = uint4{0u, 0u, 0u, 0u};
+      }
     }
   };
-  uint4 u0, u1;
-  load_rows(x0, u0, u1);
-  int seq = 0;                         // sequence of this thread's row (t < 64)
+
+  // This lane looks up the placement of block row tp; the other row it holds comes from lane
+  // kq ^ 1.  The lookups of the next block run a stage per phase (one dependent load each).
+  const int tp = 16 * (kq & 1) + m;
+  int seq = 0;
   RowInfo info_next{-1, 0, -1};
-  if (t < kPTile && x0 < ntiles && x0 * kPTile + t < total_new) {
-    seq = row_to_seq(new_offsets, batch, x0 * kPTile + t);
-    info_next = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store,
-                         x0 * kPTile + t, h, is_v);
+  if (x0 < ntiles && x0 * kMBlock + tp < total_new) {
+    const int n = x0 * kMBlock + tp;
+    seq = row_to_seq(new_offsets, batch, n);
+    info_next = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store, n, h,
+                         is_v);
   }
+  load_x(x0);
+  uint16_t* list = sm.list[gq];
+  float* res = sm.res[gq];
+  const float* nrm_w = sm.nrm[gq];
 
-  // Round k takes tile k * G + (x + k) mod G (G workgroups per pair, x this one), one tile of
-  // each block of G; the rotation spreads tiles that cost more (e.g. the last rows of every
-  // sequence, whose BF16 copies are certified too) over all workgroups.  Successive tiles of a
-  // workgroup increase, as the placement look-ahead needs.
-  auto tile_of = [&](int k) { return k * G + (x0 + k) % G; };   // tile_of(0) == x0
   for (int k = 0, tile = x0; tile < ntiles; ++k, tile = tile_of(k)) {
-    const int row0 = tile * kPTile;
-    const int nrows = min(kPTile, total_new - row0);
-    const int nt = tile_of(k + 1);     // the successor tile
-    const int n_next = nt * kPTile + t;
-    const bool look = t < kPTile && nt < ntiles && n_next < total_new;
-
-    // Input rows into LDS (8 threads per row, 2 x 16 bytes each), their norms, placements.
+    const int n0 = tile * kMBlock;
+    const int nt = tile_of(k + 1);     // the successor block
+    const int n_next = nt * kMBlock + tp;
+    const bool look = nt < ntiles && n_next < total_new;
+    // placement of row tp (this lane's row of block tile tp / 16), and the BF16-copy offsets of
+    // both its rows (tb = 0, 1)
+    const RowInfo own = info_next;
+    long long sw[2];
     {
-      const int r = t >> 3, q = t & 7;
-      *reinterpret_cast<uint4*>(&s_x[r][8 * q]) = u0;
-      *reinterpret_cast<uint4*>(&s_x[r][8 * q + 64]) = u1;
-      const uint32_t xw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-      double ss = 0.0;   // fp64: no underflow for rows of subnormal values
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        ss = __fma_rn((double)bf16_lo(xw[k]), (double)bf16_lo(xw[k]), ss);
-        ss = __fma_rn((double)bf16_hi(xw[k]), (double)bf16_hi(xw[k]), ss);
-      }
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      ss += __shfl_xor(ss, 4);
-      if (q == 0) {
-        const float nrm = (float)__builtin_sqrt(ss) * (1.0f + 0x1p-20f);
-        s_nrm[r] = nrm;
-        s_err[r] = kErrScale * nrm;
-      }
-      if (t < kPTile) s_info[t] = info_next;
-      if (t == 0) s_n[0] = s_n[1] = 0;
+      const long long so = (long long)(((uint64_t)lane_xor<16>((uint32_t)((uint64_t)own.sw >> 32)) << 32) |
+                                       lane_xor<16>((uint32_t)own.sw));
+      sw[0] = (kq & 1) ? so : own.sw;
+      sw[1] = (kq & 1) ? own.sw : so;
     }
-    load_rows(nt, u0, u1);
+    bool valid[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) valid[tb] = n0 + 16 * tb + m < total_new;
+
     // placement stage 1: is the successor's row still in the same sequence?
     int off_up = 0;
     if (look && seq + 1 < batch) off_up = new_offsets[seq + 1];
-    __syncthreads();
 
-    // y on the matrix cores: channels 16w .. 16w+15 of the tile's 64 rows.
-#pragma unroll 1
-    for (int tt = 0; tt < kPTile / 16; ++tt) {
-      const uint16_t* xr = &s_x[16 * tt + m][8 * kq];
-      v4f acc[4];
+    // y and the rows' norm bounds on the matrix cores
+    float y[16], nrm[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8bf xb = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(xr + 32 * s));
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s][2], xb, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s][1], xb, acc[s], 0, 0, 0);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[s][0], xb, acc[s], 0, 0, 0);
+    for (int tb = 0; tb < 2; ++tb) {
+      __builtin_amdgcn_sched_barrier(0);   // one 16-row tile's chains at a time
+      v8bf xb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xb[s] = __builtin_bit_cast(v8bf, xs[tb][s]);
+      v4f gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[s], xb[s], gm, 0, 0, 0);
+      // lane (m, kq) holds Gram rows 4kq .. 4kq+3 of column m: the diagonal entry of row m is in
+      // lane (m, m / 4), element m % 4
+      const int mi = m & 3;
+      const float d = mi == 0 ? gm[0] : mi == 1 ? gm[1] : mi == 2 ? gm[2] : gm[3];
+      nrm[tb] = norm_bound(__shfl(d, m + 16 * (m >> 2)));
+      v4f a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int pc = 2; pc >= 0; --pc)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            a[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[cb][s][pc], xb[s], a[cb], 0, 0, 0);
+      // D row = channel 16cb + 4kq + i of the group, column = row 16tb + m of the block
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[8 * tb + 4 * cb + i] = a[cb][i];
+      if (centered) {   // minus fp32(C) of the lane's channels 32g + 16cb + 4kq + i
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const float4 cf = *reinterpret_cast<const float4*>(&sm.cf[kGroup * gq + 16 * cb + 4 * kq]);
+          y[8 * tb + 4 * cb] -= cf.x;
+          y[8 * tb + 4 * cb + 1] -= cf.y;
+          y[8 * tb + 4 * cb + 2] -= cf.z;
+          y[8 * tb + 4 * cb + 3] -= cf.w;
+        }
       }
-      float4 y;
-      y.x = ((acc[0][0] + acc[1][0]) + (acc[2][0] + acc[3][0])) - cfl.x;
-      y.y = ((acc[0][1] + acc[1][1]) + (acc[2][1] + acc[3][1])) - cfl.y;
-      y.z = ((acc[0][2] + acc[1][2]) + (acc[2][2] + acc[3][2])) - cfl.z;
-      y.w = ((acc[0][3] + acc[1][3]) + (acc[2][3] + acc[3][3])) - cfl.w;
-      // D row = channel 16w + 4kq + i, column = token 16tt + m
-      *reinterpret_cast<float4*>(&s_y[16 * tt + m][16 * wave + 4 * kq]) = y;
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kq == 0) {
+      sm.nrm[gq][m] = nrm[0];
+      sm.nrm[gq][16 + m] = nrm[1];
+    }
 
     // placement stage 2: the successor row's sequence, then its per-sequence values
     int first = 0, next_first = 0, sp = 0, slot = 0;
@@ -377,46 +531,46 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
       slot = slot_ids ? slot_ids[seq] : seq;
     }
 
-    // Thread -> (row r, group gi, half of the group's 32 channels) for the group passes.
-    const int r = t >> 3, gi = (t >> 1) & 3, half = t & 1;
-    const int c0 = gi * kGroup + 16 * half;
-    const float er = s_err[r];
-
-    // Pass 1: certify each group's scale and zero; if they are not certain, flag every channel
-    // that can hold the group's maximum or minimum.
+    // Pass 1: certify each group's scale and zero; where they are not certain, flag every
+    // channel that can hold the group's maximum or minimum.  Lane kq evaluates one end of one
+    // row's interval: row tb = kq / 2, upper ends for even kq.
+    float mx[2], mn[2], E[2];
+    group_extremes(y, mx, mn);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+      E[tb] = kErrScale * nrm[tb] * cng + kErrAbs +
+              (centered ? (cmax + 2.0f * fmaxf(fabsf(mx[tb]), fabsf(mn[tb]))) * 0x1p-22f : 0.0f);
+    uint32_t unsure;
     {
-      float yv[16];
+      const int vt = kq >> 1;
+      const bool lo_end = (kq & 1) != 0;
+      const float a = vt ? mx[1] : mx[0], b = vt ? mn[1] : mn[0], e = vt ? E[1] : E[0];
+      _Float16 s16, z16;
+      group_params(lo_end ? a - e : a + e, lo_end ? b + e : b - e, clip, s16, z16);
+      const uint32_t key = meta_word(s16, z16);
+      const uint32_t diff = key != lane_xor<16>(key) ? 1u : 0u;   // kq ^ 1: the other end
+      const uint32_t other = lane_xor<32>(diff);                    // kq ^ 2: the other row
+      unsure = (diff << vt) | (other << (vt ^ 1));
+    }
+    uint32_t fl = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0 + 4 * k]);
-        yv[4 * k] = a.x; yv[4 * k + 1] = a.y; yv[4 * k + 2] = a.z; yv[4 * k + 3] = a.w;
-      }
-      float mx = yv[0], mn = yv[0];
+    for (int tb = 0; tb < 2; ++tb) {
+      if (((unsure >> tb) & 1u) && valid[tb]) {
+        const float top = mx[tb] - 2.0f * E[tb], bot = mn[tb] + 2.0f * E[tb];
 #pragma unroll
-      for (int c = 1; c < 16; ++c) {
-        mx = fmaxf(mx, yv[c]);
-        mn = fminf(mn, yv[c]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mn = fminf(mn, __shfl_xor(mn, 1));
-      const float E = er * s_cng[gi] + kErrAbs +
-                      (centered ? (s_cmax[gi] + 2.0f * fmaxf(fabsf(mx), fabsf(mn))) * 0x1p-22f : 0.0f);
-      _Float16 s_hi, z_hi, s_lo, z_lo;
-      group_params(mx + E, mn - E, clip, s_hi, z_lo);
-      group_params(mx - E, mn + E, clip, s_lo, z_hi);
-      const bool sure = __builtin_bit_cast(uint16_t, s_hi) == __builtin_bit_cast(uint16_t, s_lo) &&
-                        __builtin_bit_cast(uint16_t, z_hi) == __builtin_bit_cast(uint16_t, z_lo);
-      *reinterpret_cast<uint4*>(&s_code[r][c0]) = uint4{0, 0, 0, 0};
-      if (!sure && r < nrows) {
-        const float top = mx - 2.0f * E, bot = mn + 2.0f * E;
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (yv[c] >= top || yv[c] <= bot) s_list[atomicAdd(&s_n[0], 1)] = (uint16_t)(kHeadDim * r + c0 + c);
+        for (int j = 0; j < 8; ++j)
+          if (y[8 * tb + j] >= top || y[8 * tb + j] <= bot) fl |= 1u << (8 * tb + j);
       }
     }
-    __syncthreads();
-    recompute_listed(s_list, s_n[0], s_rot, s_x, s_cd, s_nrm, s_cng, s_y, s_code, s_sz, false);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t cw = 0;   // 2-bit codes at bits 2v
+    const bool redo = __ballot(fl != 0u) != 0;
+    if (redo) {
+      const float none[2] = {0.f, 0.f};
+      recompute_flagged<false>(fl, y, cw, none, none, list, res, src, g.hkv, h, n0, gq, sm.rt,
+                               sm.cd, nrm_w, cng, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // placement stage 3: page of the successor row
     int pos = 0, page = -1;
@@ -427,84 +581,78 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
     }
 
     // Pass 2: the group's scale and zero (now the defined ones), every code and BF16 copy; flag
-    // what the bound cannot certify (E taken for the group's largest column norm).
+    // what the bound cannot certify (E taken for the group's largest column norm).  Lane kq
+    // evaluates row kq % 2's scale and zero.  (Values recomputed in pass 1 are certified with
+    // the same margins as the others: looser than they need, never wrong.)
+    if (redo) group_extremes(y, mx, mn);
+    uint32_t meta[2];
+    float sc[2], zz[2], inv[2];
     {
-      float mx, mn;
-      {
-        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0]);
-        mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
-        mn = fminf(fminf(a.x, a.y), fminf(a.z, a.w));
-      }
-#pragma unroll
-      for (int k = 1; k < 4; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0 + 4 * k]);
-        mx = fmaxf(mx, fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)));
-        mn = fminf(mn, fminf(fminf(a.x, a.y), fminf(a.z, a.w)));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mn = fminf(mn, __shfl_xor(mn, 1));
+      const int pt = kq & 1;
       _Float16 s16, z16;
-      group_params(mx, mn, clip, s16, z16);
-      const float sc = (float)s16, z = (float)z16;
-      const float inv = sc != 0.0f ? 1.0f / sc : 0.0f;
-      const RowInfo info = s_info[r];
-      if (half == 0) {
-        s_sz[r][gi] = make_float2(sc, z);
-        if (r < nrows && info.rec >= 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
-      }
-      const bool bf = info.sw >= 0;
-      const float Eg = er * s_cng[gi] + kErrAbs +
-                       (centered ? (s_cmax[gi] + 2.0f * fmaxf(fabsf(mx), fabsf(mn))) * 0x1p-22f : 0.0f);
-      // code margins of the group (see above), taken at its largest |y| (>= every |y| in it):
-      // one for values recomputed in pass 1 (E = 0), one for the others
-      const float gabs = fmaxf(fabsf(mx), fabsf(mn)) + fabsf(z);
-      const float mt_exact = (gabs * 0x1p-23f) * inv * 1.01f + 0x1p-19f;
-      const float mt_bound = (Eg + (gabs + Eg) * 0x1p-23f) * inv * 1.01f + 0x1p-19f;
-      const uint4 mk = *reinterpret_cast<const uint4*>(&s_code[r][c0]);
-      const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
-      uint32_t cw[4] = {0, 0, 0, 0};
-      unsigned flagged = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_y[r][c0 + 4 * k]);
-        const float yk[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = yk[i];
-          const bool exact = ((mw[k] >> (8 * i)) & 0xFF) == kExact;
-          // t within mt of the defined t (see above); the code is certain when no boundary
-          // 1/2, 3/2, 5/2 lies within mt of t.  The distance to the nearest half-integer is at
-          // most the distance to those three, so comparing it is conservative.
-          const float tq = (y - z) * inv;
-          const float dist = fabsf(__builtin_amdgcn_fractf(tq) - 0.5f);
-          bool ok = dist > (exact ? mt_exact : mt_bound);
-          if (bf) {
-            const float E = exact ? 0.0f : Eg;
-            ok = ok && f32_to_bf16_rne(y - E) == f32_to_bf16_rne(y + E);
-          }
-          const int code = (int)fminf(fmaxf(__builtin_rintf(tq), 0.0f), 3.0f);
-          cw[k] |= (uint32_t)code << (8 * i);
-          flagged |= (ok ? 0u : 1u) << (4 * k + i);
-        }
-      }
-      *reinterpret_cast<uint4*>(&s_code[r][c0]) = uint4{cw[0], cw[1], cw[2], cw[3]};
-      if (r < nrows)
-        while (flagged) {
-          const int c = __builtin_ctz(flagged);
-          flagged &= flagged - 1u;
-          s_list[atomicAdd(&s_n[1], 1)] = (uint16_t)(kHeadDim * r + c0 + c);
-        }
+      group_params(pt ? mx[1] : mx[0], pt ? mn[1] : mn[0], clip, s16, z16);
+      const uint32_t mw = meta_word(s16, z16);
+      const float s = (float)s16;
+      const float iv = s != 0.0f ? 1.0f / s : 0.0f;
+      const uint32_t mo = lane_xor<16>(mw);
+      const float io = lane_xor_f32<16>(iv);
+      meta[0] = pt ? mo : mw;
+      meta[1] = pt ? mw : mo;
+      inv[0] = pt ? io : iv;
+      inv[1] = pt ? iv : io;
     }
-    __syncthreads();
-    recompute_listed(s_list, s_n[1], s_rot, s_x, s_cd, s_nrm, s_cng, s_y, s_code, s_sz, true);
-    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sc[tb] = (float)__builtin_bit_cast(_Float16, (uint16_t)meta[tb]);
+      zz[tb] = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta[tb] >> 16));
+    }
+    if (kq < 2) {   // lane kq stores row kq's scale/zero word of the group
+      if ((kq ? valid[1] : valid[0]) && own.rec >= 0) store_meta(pages, own, is_v, gq, kq ? meta[1] : meta[0]);
+    }
+    uint32_t fl2 = 0;   // values to recompute
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const float Eg = kErrScale * nrm[tb] * cng + kErrAbs +
+                       (centered ? (cmax + 2.0f * fmaxf(fabsf(mx[tb]), fabsf(mn[tb]))) * 0x1p-22f : 0.0f);
+      // the code margin of the group, taken at its largest |y| (>= every |y| in it)
+      const float gabs = fmaxf(fabsf(mx[tb]), fabsf(mn[tb])) + fabsf(zz[tb]);
+      const float mt = (Eg + (gabs + Eg) * 0x1p-23f) * inv[tb] * 1.01f + 0x1p-19f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int v = 8 * tb + j;
+        const float yv = y[v];
+        // t within mt of the defined t; the code is certain when no boundary 1/2, 3/2, 5/2
+        // lies within mt of t.  The distance to the nearest half-integer is at most the
+        // distance to those three, so comparing it is conservative.
+        const float tq = (yv - zz[tb]) * inv[tb];
+        const float dist = fabsf(__builtin_amdgcn_fractf(tq) - 0.5f);
+        const bool ok = dist > mt;
+        const int code = (int)fminf(fmaxf(__builtin_rintf(tq), 0.0f), 3.0f);
+        cw |= (uint32_t)code << (2 * v);
+        fl2 |= (ok ? 0u : 1u) << v;
+      }
+      // BF16 copies of sink/window rows: certain when y -+ E round to the same bf16
+      if (__ballot(sw[tb] >= 0) != 0 && sw[tb] >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = 8 * tb + j;
+          if (f32_to_bf16_rne(y[v] - Eg) != f32_to_bf16_rne(y[v] + Eg)) fl2 |= 1u << v;
+        }
+      }
+      if (!valid[tb]) fl2 &= ~(0xFFu << (8 * tb));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__ballot(fl2 != 0u) != 0)
+      recompute_flagged<true>(fl2, y, cw, sc, zz, list, res, src, g.hkv, h, n0, gq, sm.rt, sm.cd,
+                              nrm_w, cng, lane);
 
+    load_x(nt);   // the successor's rows, in flight from here to the next block's matrix cores
     // placement stage 4: the successor row's record and sink/window row
     if (look) {
-      RowInfo info{-1, 0, -1};
+      RowInfo nx{-1, 0, -1};
       if (pos >= 0 && page >= 0 && page < g.num_pages && pos / kPage < g.max_pages) {
-        info.rec = ((long long)page * g.hkv + h) * kRecord;
-        info.slot_in_page = pos % kPage;
+        nx.rec = ((long long)page * g.hkv + h) * kRecord;
+        nx.slot_in_page = pos % kPage;
       }
       const int new_len = sp + (next_first - first);
       int row = -1;
@@ -512,51 +660,81 @@ __global__ __launch_bounds__(kPThreads, 2) void rotate_quantize_prefill_kernel(
       else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
         row = g.num_sink + pos % g.window;
       if (row >= 0 && has_store && slot >= 0 && slot < g.num_slots)
-        info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
-                  (is_v ? kHeadDim : 0);
-      info_next = info;
+        nx.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
+                (is_v ? kHeadDim : 0);
+      info_next = nx;
     } else {
       info_next = RowInfo{-1, 0, -1};
     }
 
-    // Pack the codes into the records; BF16 copies of sink/window rows.
-    {
-      const int q = t & 7;
-      const RowInfo info = s_info[r];
-      if (r < nrows && info.rec >= 0 && !is_v) {
-        const uint4 cv = *reinterpret_cast<const uint4*>(&s_code[r][16 * q]);
-        const uint32_t cwd[4] = {cv.x, cv.y, cv.z, cv.w};
-        uint32_t w = 0;
+    // BF16 copies of sink/window rows: lane (m, kq) holds 4 consecutive channels per block cb
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t b = cwd[k];  // four codes, one per byte
-          const uint32_t packed = (b & 3u) | ((b >> 6) & 0xCu) | ((b >> 12) & 0x30u) | ((b >> 18) & 0xC0u);
-          w |= packed << (8 * k);
-        }
-        *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes +
-                                     8 * (16 * (q % 4) + info.slot_in_page) + 4 * (q / 4)) = w;
-      }
-      if (r < nrows && info.sw >= 0) {
-        uint32_t o[8];
+    for (int tb = 0; tb < 2; ++tb) {
+      if (valid[tb] && sw[tb] >= 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 a = *reinterpret_cast<const float4*>(&s_y[r][16 * q + 4 * k]);
-          o[2 * k] = f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
-          o[2 * k + 1] = f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
+        for (int cb = 0; cb < 2; ++cb) {
+          const int v = 8 * tb + 4 * cb;
+          const uint2 o = {(uint32_t)f32_to_bf16_rne(y[v]) | ((uint32_t)f32_to_bf16_rne(y[v + 1]) << 16),
+                           (uint32_t)f32_to_bf16_rne(y[v + 2]) | ((uint32_t)f32_to_bf16_rne(y[v + 3]) << 16)};
+          *reinterpret_cast<uint2*>(sinkwin + sw[tb] + kGroup * gq + 16 * cb + 4 * kq) = o;
         }
-        uint4* dst = reinterpret_cast<uint4*>(sinkwin + info.sw + 16 * q);
-        dst[0] = uint4{o[0], o[1], o[2], o[3]};
-        dst[1] = uint4{o[4], o[5], o[6], o[7]};
       }
     }
-    if (is_v) {
-      for (int e = t; e < kPTile * 16; e += kPThreads) {
-        const int rr = e >> 4, c16 = e & 15;
-        const RowInfo info = s_info[rr];
-        if (rr < nrows && info.rec >= 0) store_v_half(pages, info, s_code[rr], c16);
+
+    if (!is_v) {
+      // K word d = 2g + cb of row 16 tb + m: channel 4kq + i of the word at bits 8kq + 2i, so
+      // the four lanes of a row contribute a byte each; lane kq stores word cb = kq / 2 of its
+      // own row (tb = kq % 2)
+      uint32_t wsel = 0;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          uint32_t w = ((cw >> (16 * tb + 8 * cb)) & 0xFFu) << (8 * kq);
+          w |= lane_xor<16>(w);
+          w |= lane_xor<32>(w);
+          if (kq == 2 * cb + tb) wsel = w;
+        }
+      if (((kq & 1) ? valid[1] : valid[0]) && own.rec >= 0) {
+        const int d = 2 * gq + (kq >> 1);
+        *reinterpret_cast<uint32_t*>(pages + own.rec + kKCodes + 8 * (16 * (d % 4) + own.slot_in_page) +
+                                     4 * (d / 4)) = wsel;
+      }
+    } else {
+      // V: the group's code pairs of channel residues c16 = 4kq + i, to LDS, then each thread
+      // assembles two 16-bit halves of one row from the four groups' pairs
+      const int buf = k & 1;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t nib = ((cw >> (16 * tb + 2 * i)) & 3u) | (((cw >> (16 * tb + 8 + 2 * i)) & 3u) << 2);
+          wv |= nib << (8 * i);
+        }
+        sm.vn[buf][gq][16 * tb + m][kq] = wv;
+      }
+      __syncthreads();
+      const int tl = t >> 3, c2 = 2 * (t & 7);
+      // row tl's placement is held by lane (tl % 16, tl / 16) of every wave
+      const int srcl = (tl & 15) + 16 * (tl >> 4);
+      const uint32_t rlo = (uint32_t)__shfl((int)(uint32_t)own.rec, srcl);
+      const uint32_t rhi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)own.rec >> 32), srcl);
+      const int sl = __shfl(own.slot_in_page, srcl);
+      const long long rec = (long long)(((uint64_t)rhi << 32) | rlo);
+      if (n0 + tl < total_new && rec >= 0) {
+        uint32_t hw0 = 0, hw1 = 0;
+#pragma unroll
+        for (int gg = 0; gg < kMWaves; ++gg) {
+          const uint32_t wv = sm.vn[buf][gg][tl][c2 >> 2];
+          hw0 |= ((wv >> (8 * (c2 & 3))) & 0xFu) << (4 * gg);
+          hw1 |= ((wv >> (8 * ((c2 + 1) & 3))) & 0xFu) << (4 * gg);
+        }
+        uint8_t* base = pages + rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
+        *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + c2)) = (uint16_t)hw0;
+        *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + c2 + 1)) = (uint16_t)hw1;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -771,14 +949,14 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
   if (method == kAppendMatrix) {
     int cus = current_device_cus();
     if (cus <= 0) cus = 256;
-    // one resident workgroup per CU (R and the tile take most of the LDS) over the 2 * Hkv
-    // (KV head, K|V) pairs.  Centered keys leave more values uncertain (about 1.8% against
-    // 1.2% recomputed), so with a key mean K gets 19 of every 32 workgroups of a head.
-    const int tiles = (total_new + kPTile - 1) / kPTile;
-    const int per_head = 2 * max(1, min(tiles, (cus + 2 * g.hkv - 1) / (2 * g.hkv)));
+    // two resident workgroups per CU (R^T takes most of their LDS) over the 2 * Hkv (KV head,
+    // K|V) pairs.  Centered keys leave more values uncertain (about 1.8% against 1.2%
+    // recomputed), so with a key mean K gets 19 of every 32 workgroups of a head.
+    const int tiles = (total_new + kMBlock - 1) / kMBlock;
+    const int per_head = 2 * max(1, min(tiles, (2 * cus + 2 * g.hkv - 1) / (2 * g.hkv)));
     const int k_groups = k_mean != nullptr ? max(1, min(per_head - 1, (per_head * 19 + 16) / 32))
                                            : per_head / 2;
-    hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_head, g.hkv), dim3(kPThreads), 0,
+    hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_head, g.hkv), dim3(kMThreads), 0,
                        stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
                        v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v,
                        k_groups);
