@@ -66,7 +66,10 @@ __global__ __launch_bounds__(kAppendThreads) void rotate_quantize_append_kernel(
 // the accumulator's 48 roundings, the 16 of the p0 passes are each at most u/2 of a partial sum
 // <= sum|terms| (8u), the 32 before them act on partial sums below 2^-7 sum|terms| (0.13u), and
 // the defined value's own rounding to fp32 adds u/2.  So |y_mc - y| <= 16 u sum_i |x_i R_ij| <=
-// 16 u ||x|| ||R_.j||.  The kernel takes E = 64 u ||x|| ||R_.j|| plus 2^-100 for flushed
+// 16 u ||x|| ||R_.j||.  The coarser per-instruction bound that tests/test_gpu_mfma_model.py
+// holds the device to (11u sum|products| + 4u |C| + 2^-124, C the accumulator input) gives at
+// most 28u sum_i |x_i R_ij| + 12 * 2^-124 over the chain (the p0 instructions' inputs sum to at
+// most 3 sum|terms|).  The kernel takes E = 64 u ||x|| ||R_.j|| plus 2^-100 for flushed
 // subnormals, computed 5% high so that y -+ E rounded to nearest still encloses [y - E, y + E].
 // ||x|| is bounded from the Gram diagonal: its terms are positive, so by the same model it is
 // within 15u of the sum of squares, less at most 2^-122 of flushed subnormal partial sums; the
