@@ -423,19 +423,17 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
   auto tile_of = [&](int k) { return k * G + (x0 + k) % G; };   // tile_of(0) == x0
 
   // B operands of a block: lane (m, kq), row 16 tb + m, slice s holds inputs 32s + 8kq .. +7.
+  // A row past the end (or past the last block) loads the last row instead: its values are
+  // never stored and no flag is raised for it, and the loads stay unconditional, so a later
+  // wait for an earlier load can count them exactly instead of waiting for all.
   uint4 xs[2][4];
   auto load_x = [&](int tile) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int n = tile * kMBlock + 16 * tb + m;
-      if (tile < ntiles && n < total_new) {
-        const uint4* rp = reinterpret_cast<const uint4*>(src + ((size_t)n * g.hkv + h) * kHeadDim + 8 * kq);
+      const int n = min(tile * kMBlock + 16 * tb + m, total_new - 1);
+      const uint4* rp = reinterpret_cast<const uint4*>(src + ((size_t)n * g.hkv + h) * kHeadDim + 8 * kq);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xs[tb][s] = rp[4 * s];
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) xs[tb][s] = uint4{0u, 0u, 0u, 0u};
-      }
+      for (int s = 0; s < 4; ++s) xs[tb][s] = rp[4 * s];
     }
   };
 
