@@ -951,12 +951,13 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
     int cus = current_device_cus();
     if (cus <= 0) cus = 256;
     // two resident workgroups per CU (R^T takes most of their LDS) over the 2 * Hkv (KV head,
-    // K|V) pairs.  Centered keys leave more values uncertain (about 1.8% against 1.2%
-    // recomputed), so with a key mean K gets 19 of every 32 workgroups of a head.
+    // K|V) pairs.  A V block costs ~15% more than a K block (its waves exchange code pairs
+    // behind a barrier), so K gets 15 of every 32 workgroups of a head; centered keys leave
+    // more values uncertain (about 1.8% against 1.2% recomputed), so with a key mean K gets 19.
     const int tiles = (total_new + kMBlock - 1) / kMBlock;
     const int per_head = 2 * max(1, min(tiles, (2 * cus + 2 * g.hkv - 1) / (2 * g.hkv)));
-    const int k_groups = k_mean != nullptr ? max(1, min(per_head - 1, (per_head * 19 + 16) / 32))
-                                           : per_head / 2;
+    const int k_share = k_mean != nullptr ? 19 : 15;
+    const int k_groups = max(1, min(per_head - 1, (per_head * k_share + 16) / 32));
     hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_head, g.hkv), dim3(kMThreads), 0,
                        stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
                        v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v,
