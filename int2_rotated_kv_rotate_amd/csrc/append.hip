@@ -123,6 +123,48 @@ __device__ __forceinline__ float norm_bound(float d2) {
 // after it (every lane of the wave; no other wave reads these arrays).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// A lane's value and that of lane ^ 16 (or lane ^ 32) from one lane-swap instruction (a vector
+// ALU operation, no LDS round trip).  Called with both operands equal, v_permlane16_swap leaves
+// each lane its own value and its partner's as the two results, own first in rows 0 and 2 of the
+// wave and partner first in rows 1 and 3 (v_permlane32_swap: own first in lanes 0..31), so a
+// symmetric combination (max, min, or, equality) needs no select.
+struct LanePair { uint32_t a, b; };
+__device__ __forceinline__ LanePair pair16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {(uint32_t)r[0], (uint32_t)r[1]};
+}
+__device__ __forceinline__ LanePair pair32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {(uint32_t)r[0], (uint32_t)r[1]};
+}
+// The partner's value alone.
+__device__ __forceinline__ uint32_t partner16(uint32_t v, int lane) {
+  const LanePair p = pair16(v);
+  return (lane & 16) ? p.a : p.b;
+}
+__device__ __forceinline__ uint32_t partner32(uint32_t v, int lane) {
+  const LanePair p = pair32(v);
+  return (lane & 32) ? p.a : p.b;
+}
+__device__ __forceinline__ float max16(float x) {
+  const LanePair p = pair16(__float_as_uint(x));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+__device__ __forceinline__ float min16(float x) {
+  const LanePair p = pair16(__float_as_uint(x));
+  return fminf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+__device__ __forceinline__ float max32(float x) {
+  const LanePair p = pair32(__float_as_uint(x));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+__device__ __forceinline__ float min32(float x) {
+  const LanePair p = pair32(__float_as_uint(x));
+  return fminf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+__device__ __forceinline__ uint32_t or16(uint32_t v) { const LanePair p = pair16(v); return p.a | p.b; }
+__device__ __forceinline__ uint32_t or32(uint32_t v) { const LanePair p = pair32(v); return p.a | p.b; }
+
 struct alignas(16) MatrixShared {
   float rt[kHeadDim][kRtStride];          // R^T (fp32): rt[c][i] = R[i][c]
   double cd[kHeadDim];                    // C = mu . R (fp64, i ascending), 0 without a key mean
@@ -178,7 +220,12 @@ __device__ __forceinline__ void recompute_wave(const uint16_t* list, float* res,
     part += part2;
     part += lane_xor_f64<1>(part);
     part += lane_xor_f64<2>(part);
-    if constexpr (L >= 8) part += lane_xor_f64<4>(part);
+    if constexpr (L >= 8) {   // the other quad of the lane's eight: row_half_mirror (DPP)
+      const uint64_t u = __builtin_bit_cast(uint64_t, part);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x141, 0xF, 0xF, true);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x141, 0xF, 0xF, true);
+      part += __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    }
     if constexpr (L >= 16) part += lane_xor_f64<8>(part);
     if (act && q == 0) {
       const double v = part - cd[c];
@@ -232,8 +279,8 @@ __device__ __forceinline__ void recompute_flagged(uint32_t fl, float (&y)[16], u
   wor |= lane_xor<2>(wor);
   wor |= lane_xor<4>(wor);
   wor |= lane_xor<8>(wor);
-  wor |= lane_xor<16>(wor);
-  wor |= lane_xor<32>(wor);
+  wor = or16(wor);
+  wor = or32(wor);
   wor = __builtin_amdgcn_readfirstlane(wor);
   for (int r0 = 0; r0 < total; r0 += kMListCap) {
     {
@@ -284,10 +331,8 @@ __device__ __forceinline__ void group_extremes(const float (&y)[16], float mx[2]
       a = fmaxf(a, y[8 * tb + j]);
       b = fminf(b, y[8 * tb + j]);
     }
-    a = fmaxf(a, lane_xor_f32<16>(a));
-    b = fminf(b, lane_xor_f32<16>(b));
-    a = fmaxf(a, lane_xor_f32<32>(a));
-    b = fminf(b, lane_xor_f32<32>(b));
+    a = max32(max16(a));
+    b = min32(min16(b));
     mx[tb] = a;
     mn[tb] = b;
   }
@@ -463,8 +508,8 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
     const RowInfo own = info_next;
     long long sw[2];
     {
-      const long long so = (long long)(((uint64_t)lane_xor<16>((uint32_t)((uint64_t)own.sw >> 32)) << 32) |
-                                       lane_xor<16>((uint32_t)own.sw));
+      const long long so = (long long)(((uint64_t)partner16((uint32_t)((uint64_t)own.sw >> 32), lane) << 32) |
+                                       partner16((uint32_t)own.sw, lane));
       sw[0] = (kq & 1) ? so : own.sw;
       sw[1] = (kq & 1) ? own.sw : so;
     }
@@ -549,8 +594,9 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
       _Float16 s16, z16;
       group_params(lo_end ? a - e : a + e, lo_end ? b + e : b - e, clip, s16, z16);
       const uint32_t key = meta_word(s16, z16);
-      const uint32_t diff = key != lane_xor<16>(key) ? 1u : 0u;   // kq ^ 1: the other end
-      const uint32_t other = lane_xor<32>(diff);                    // kq ^ 2: the other row
+      const LanePair ends = pair16(key);                            // kq ^ 1: the other end
+      const uint32_t diff = ends.a != ends.b ? 1u : 0u;
+      const uint32_t other = partner32(diff, lane);                 // kq ^ 2: the other row
       unsure = (diff << vt) | (other << (vt ^ 1));
     }
     uint32_t fl = 0;
@@ -595,8 +641,8 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
       const uint32_t mw = meta_word(s16, z16);
       const float s = (float)s16;
       const float iv = s != 0.0f ? 1.0f / s : 0.0f;
-      const uint32_t mo = lane_xor<16>(mw);
-      const float io = lane_xor_f32<16>(iv);
+      const uint32_t mo = partner16(mw, lane);
+      const float io = __uint_as_float(partner16(__float_as_uint(iv), lane));
       meta[0] = pt ? mo : mw;
       meta[1] = pt ? mw : mo;
       inv[0] = pt ? io : iv;
@@ -692,8 +738,7 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           uint32_t w = ((cw >> (16 * tb + 8 * cb)) & 0xFFu) << (8 * kq);
-          w |= lane_xor<16>(w);
-          w |= lane_xor<32>(w);
+          w = or32(or16(w));
           if (kq == 2 * cb + tb) wsel = w;
         }
       if (((kq & 1) ? valid[1] : valid[0]) && own.rec >= 0) {
