@@ -223,16 +223,12 @@ int32_t oscar_int4_rotate_quantize_append(
 
 /*
  * Decode attention over an INT4 cache, written in the workspace format of
- * oscar_decode_attention and finished by oscar_combine with the same rot_v.
- * G = num_q_heads / Hkv <= 4: the work split of oscar_decode_attention (equal runs of INT4
- * pages per worker wavefront, one per resident slot; at most max_splits partials per (sequence,
- * KV head); the BF16 sink/window positions as extra partials) on the matrix cores; split_pages
- * is not used.
- * G = 8: sequence b's pages are cut into splits of max(split_pages, ceil(P_b / max_splits))
- * pages (P_b = ceil(L_b / 16)); each split attends over all of its positions (INT4 records and
- * BF16 sink/window rows) on the vector ALUs.
- * Arguments, validation and errors as oscar_decode_attention, with split_pages (>= 1) in place
- * of num_workers.
+ * oscar_decode_attention and finished by oscar_combine with the same rot_v.  The work split of
+ * oscar_decode_attention (equal runs of INT4 pages per worker wavefront, one per resident slot;
+ * at most max_splits partials per (sequence, KV head); the BF16 sink/window positions as extra
+ * partials), on the matrix cores for every G = num_q_heads / Hkv (1, 2, 4 or 8).
+ * Arguments, validation and errors as oscar_decode_attention, with split_pages (>= 1, kept for
+ * compatibility and not used) in place of num_workers.
  */
 int32_t oscar_int4_decode_attention(
     const oscar_layout* lay, const uint8_t* pages, const uint16_t* sinkwin,

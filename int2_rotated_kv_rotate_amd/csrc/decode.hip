@@ -962,8 +962,10 @@ __global__ __launch_bounds__(64 * kWaves) void int2_decode_kernel(
 
 constexpr int kPage4Bytes = 2560;
 constexpr int kRing4Bytes = 2 * kPage4Bytes;
-constexpr size_t kSmem4Bytes = (size_t)kWaves * kRing4Bytes + (size_t)kWaves * sizeof(WTile<1>);
-static_assert((kMaxSinkWindow * 4 + 2 * 4 + 4 * kHeadDim) * sizeof(float) <= kSmem4Bytes,
+template <int NCB>
+constexpr size_t kSmem4Bytes = (size_t)kWaves * kRing4Bytes + (size_t)kWaves * sizeof(WTile<NCB>);
+static_assert((kMaxSinkWindow * 4 + 2 * 4 + 4 * kHeadDim) * sizeof(float) <= kSmem4Bytes<1> &&
+                  (kMaxSinkWindow * 8 + 2 * 8 + 8 * kHeadDim) * sizeof(float) <= kSmem4Bytes<8>,
               "window scratch exceeds the INT4 workgroup's shared memory");
 
 // Copy the record at rec (uniform) into the page slot at LDS offset ps: bytes [0, 1024) and
@@ -1023,54 +1025,87 @@ __device__ __forceinline__ void read_page4_v(uint32_t ps, uint32_t a16l, uint32_
 
 // Logit of head r, token t in units of cscale (as page_logits<1>): the chunk's dwords masked
 // with 0x0F0F0F0F at shifts 0 and 4 are the two int8 K operands.
-template <bool MASKED>
-__device__ __forceinline__ float page4_logit(uint4 kc, uint4 km, bool live, const QOperands<1>& qo,
-                                             uint32_t m4) {
+template <int NCB, bool MASKED>
+__device__ __forceinline__ void page4_logits(uint4 kc, uint4 km, bool live, const QOperands<NCB>& qo,
+                                             uint32_t m4, float a[kLaneHeads<NCB>]) {
   const v4i ka0 = (v4i){(int)(kc.x & m4), (int)((kc.x >> 4) & m4), (int)(kc.y & m4),
                         (int)((kc.y >> 4) & m4)};
   const v4i ka1 = (v4i){(int)(kc.z & m4), (int)((kc.z >> 4) & m4), (int)(kc.w & m4),
                         (int)((kc.w >> 4) & m4)};
-  v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
-  dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0][0], ka0, dh, 0, 0, 0);
-  dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0][1], ka1, dh, 0, 0, 0);
-  dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0][0], ka0, dl, 0, 0, 0);
-  dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0][1], ka1, dl, 0, 0, 0);
   const uint32_t kmw[4] = {km.x, km.y, km.z, km.w};
-  float x = 0.f;
+  // |dh| <= 127 * 15 * 32 per group: 254 dh + dl stays below 2^24, exact in fp32
+  if constexpr (NCB == 8) {
+    // the INT2 G = 8 row layout: D element i of a lane is head 2r + i/2, group i%2 (block A,
+    // channels 0..63) or 2 + i%2 (block B, channels 64..127)
+    const v4i zero = {0, 0, 0, 0};
+    const v4i dhA = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0], ka0, zero, 0, 0, 0);
+    const v4i dlA = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0], ka0, zero, 0, 0, 0);
+    const v4i dhB = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[1], ka1, zero, 0, 0, 0);
+    const v4i dlB = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[1], ka1, zero, 0, 0, 0);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    // |dh| <= 127 * 15 * 32 per group: 254 dh + dl stays below 2^24, exact in fp32
-    const int dint = __mul24(dh[g], 254) + dl[g];
-    x = fmaf(f16lo(kmw[g]), (float)dint, x);
-    x = fmaf(f16hi(kmw[g]), qo.qs[0][g], x);
+    for (int hh = 0; hh < 2; ++hh) {
+      float x = 0.f;
+#pragma unroll
+      for (int gl = 0; gl < 2; ++gl) {
+        const int i = 2 * hh + gl;
+        const int dA = __mul24(dhA[i], 254) + dlA[i], dB = __mul24(dhB[i], 254) + dlB[i];
+        x = fmaf(f16lo(kmw[gl]), (float)dA, x);
+        x = fmaf(f16hi(kmw[gl]), qo.qs[hh][gl], x);
+        x = fmaf(f16lo(kmw[2 + gl]), (float)dB, x);
+        x = fmaf(f16hi(kmw[2 + gl]), qo.qs[hh][2 + gl], x);
+      }
+      if (MASKED) x = live ? x : -INFINITY;
+      a[hh] = x;
+    }
+  } else {
+    v4i dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0][0], ka0, dh, 0, 0, 0);
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.hi[0][1], ka1, dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0][0], ka0, dl, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qo.lo[0][1], ka1, dl, 0, 0, 0);
+    float x = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dint = __mul24(dh[g], 254) + dl[g];
+      x = fmaf(f16lo(kmw[g]), (float)dint, x);
+      x = fmaf(f16hi(kmw[g]), qo.qs[0][g], x);
+    }
+    if (MASKED) x = live ? x : -INFINITY;
+    a[0] = x;
   }
-  if (MASKED) x = live ? x : -INFINITY;
-  return x;
 }
 
 // One page in the slot at ps: logits, weights into the tile (columns 0..15), P.V and the weight
 // sums.  after_reads() runs once the slot's LDS reads have completed (the copy of a later page
 // into the slot goes there).
-template <bool MASKED, bool FIRST, class AfterReads>
+template <int NCB, bool MASKED, bool FIRST, class AfterReads>
 __device__ __forceinline__ void int4_page(uint32_t ps, uint32_t a16l, uint32_t a16t, bool live,
-                                          const QOperands<1>& qo, SplitState<1>& st,
-                                          WTile<1>& tile, int t, int r, uint32_t m4,
+                                          const QOperands<NCB>& qo, SplitState<NCB>& st,
+                                          WTile<NCB>& tile, int t, int r, uint32_t m4,
                                           uint32_t mask_v, uint32_t magic, v4s ones,
                                           bool fixed_ref, AfterReads&& after_reads) {
   uint4 kc, km;
   read_page4_k(ps, a16l, a16t, kc, km);
-  float a[1];
-  a[0] = page4_logit<MASKED>(kc, km, live, qo, m4);
-  st.mlane[0] = fmaxf(st.mlane[0], a[0]);
-  if (FIRST && !fixed_ref) st.mref[0] = fmaxf(row_max16(a[0]) * qo.cscale[0], kNegBig);
+  float a[kLaneHeads<NCB>];
+  page4_logits<NCB, MASKED>(kc, km, live, qo, m4, a);
+#pragma unroll
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
+    st.mlane[cb] = fmaxf(st.mlane[cb], a[cb]);
+    if (FIRST && !fixed_ref) st.mref[cb] = fmaxf(row_max16(a[cb]) * qo.cscale[cb], kNegBig);
+  }
   uint4 vm, vc;
   read_page4_v(ps, a16l, a16t, vm, vc);
   after_reads();
-  page_weights<1, MASKED>(a, vm, live, qo, st, tile, t, r, 0);
-  // A operands: row t of the tile, tokens 4r .. 4r + 3
-  const uint2 h2 = *reinterpret_cast<const uint2*>(&tile.w[0][0][t][4 * r]);
-  const uint2 l2 = *reinterpret_cast<const uint2*>(&tile.w[0][1][t][4 * r]);
-  const v4s ahi = __builtin_bit_cast(v4s, h2), alo = __builtin_bit_cast(v4s, l2);
+  page_weights<NCB, MASKED>(a, vm, live, qo, st, tile, t, r, 0);
+  // A operands of each row block: row t of the tile, tokens 4r .. 4r + 3
+  v4s ahi[kLaneHeads<NCB>], alo[kLaneHeads<NCB>];
+#pragma unroll
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
+    const uint2 h2 = *reinterpret_cast<const uint2*>(&tile.w[cb][0][t][4 * r]);
+    const uint2 l2 = *reinterpret_cast<const uint2*>(&tile.w[cb][1][t][4 * r]);
+    ahi[cb] = __builtin_bit_cast(v4s, h2);
+    alo[cb] = __builtin_bit_cast(v4s, l2);
+  }
   const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -1080,30 +1115,37 @@ __device__ __forceinline__ void int4_page(uint32_t ps, uint32_t a16l, uint32_t a
                                                       and_or(w >> 5, mask_v, magic)));
     const v4s b1 = __builtin_bit_cast(v4s, make_uint2(and_or(w >> 1, mask_v, magic),
                                                       and_or(w >> 9, mask_v, magic)));
-    st.acc[0][2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b0, st.acc[0][2 * k], 0, 0, 0);
-    st.acc[0][2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b0, st.acc[0][2 * k], 0, 0, 0);
-    st.acc[0][2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b1, st.acc[0][2 * k + 1], 0, 0, 0);
-    st.acc[0][2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b1, st.acc[0][2 * k + 1], 0, 0, 0);
+    // column blocks 2k, 2k + 1 are group k: G = 8 takes the row block of its group pair
+    const int bk = NCB == 8 ? (k >> 1) : 0;
+    st.acc[0][2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi[bk], b0, st.acc[0][2 * k], 0, 0, 0);
+    st.acc[0][2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo[bk], b0, st.acc[0][2 * k], 0, 0, 0);
+    st.acc[0][2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi[bk], b1, st.acc[0][2 * k + 1], 0, 0, 0);
+    st.acc[0][2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo[bk], b1, st.acc[0][2 * k + 1], 0, 0, 0);
   }
-  st.wsum[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, ones, st.wsum[0], 0, 0, 0);
-  st.wsum[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, ones, st.wsum[0], 0, 0, 0);
+#pragma unroll
+  for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi[cb], ones, st.wsum[cb], 0, 0, 0);
+    st.wsum[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo[cb], ones, st.wsum[cb], 0, 0, 0);
+  }
 }
 
 // grid: worker_groups INT2-style worker workgroups (kWaves workers each) and batch * Hkv *
-// wparts sink/window workgroups, ordered as in int2_decode_kernel.
-__global__ __launch_bounds__(64 * kWaves) void int4_decode_mfma_kernel(
+// wparts sink/window workgroups, ordered as in int2_decode_kernel.  NCB: the row layout of
+// int2_decode_kernel (1 for G <= 4, 8 for G = 8).
+template <int NCB>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void int4_decode_mfma_kernel(
     CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ plan, float sm_scale,
     int worker_groups, int window_first, int wparts, Workspace ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem4Bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem4Bytes<NCB>];
   int bid = blockIdx.x;
   const int nwin = ws.batch * g.hkv * wparts;
   if (window_first ? bid < nwin : bid >= worker_groups) {
     const int widx = window_first ? bid : bid - worker_groups;
     const int pair = widx / wparts;
-    window_pair<1>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws, pair / g.hkv,
-                   pair % g.hkv, widx % wparts, wparts, smem);
+    window_pair<NCB == 8 ? 2 : NCB>(g, sinkwin, slot_ids, hq, seq_lens, sm_scale * kLog2e, ws,
+                                    pair / g.hkv, pair % g.hkv, widx % wparts, wparts, smem);
     return;
   }
   if (window_first) bid -= nwin;
@@ -1111,8 +1153,8 @@ __global__ __launch_bounds__(64 * kWaves) void int4_decode_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int worker = bid * kWaves + wave;
   const int t = lane & 15, r = lane >> 4;
-  WTile<1>& tile = *reinterpret_cast<WTile<1>*>(smem + (size_t)kWaves * kRing4Bytes +
-                                                wave * sizeof(WTile<1>));
+  WTile<NCB>& tile = *reinterpret_cast<WTile<NCB>*>(smem + (size_t)kWaves * kRing4Bytes +
+                                                    wave * sizeof(WTile<NCB>));
   const uint32_t ring0 = lds_offset(smem + (size_t)wave * kRing4Bytes);
   const uint32_t a16l = 16 * lane, a16t = 16 * t;
 
@@ -1165,8 +1207,30 @@ __global__ __launch_bounds__(64 * kWaves) void int4_decode_mfma_kernel(
     const int n_sink = min(L, g.num_sink);
     const int lo = n_sink, hi = L - min(g.window, L - n_sink);
 
-    QOperands<1> qo;
-    {
+    QOperands<NCB> qo;
+    if constexpr (NCB == 8) {
+      // A-operand row of this lane: head t/2 with group t%2 (block 0, channel words 0..3) or
+      // 2 + t%2 (block 1, words 4..7); quarter r holds word r of the block's half
+      const char* blka = ws.qblock(b, hq, h * G + (t >> 1));
+      const bool use = (r >> 1) == (t & 1);
+      const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        const v4i zh = *reinterpret_cast<const v4i*>(blka + kQHiOff + 16 * (4 * bk + r));
+        const v4i zl = *reinterpret_cast<const v4i*>(blka + kQLoOff + 16 * (4 * bk + r));
+        qo.hi[bk] = use ? zh : zero;
+        qo.lo[bk] = use ? zl : zero;
+      }
+      // D rows of this lane: heads 2r and 2r + 1
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* blkd = ws.qblock(b, hq, h * G + 2 * r + hh);
+        const float qsc = *reinterpret_cast<const float*>(blkd + kQScOff);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) qo.qs[hh][gg] = reinterpret_cast<const float*>(blkd + kQSumOff)[gg];
+        qo.cscale[hh] = fmaxf(qsc / 254.0f * sm_log2, 1e-30f);
+      }
+    } else {
       const int ja = t >> 2, ga = t & 3;
       const char* blka = ws.qblock(b, hq, h * G + (ja < G ? ja : 0));
 #pragma unroll
@@ -1190,18 +1254,22 @@ __global__ __launch_bounds__(64 * kWaves) void int4_decode_mfma_kernel(
 
     const int32_t* bt = block_table + (size_t)b * g.max_pages;
     const uint8_t* pages_h = pages + (size_t)h * kPage4Bytes;
-    SplitState<1> st;
-    st.mref[0] = kNegBig;
+    SplitState<NCB> st;
+#pragma unroll
+    for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) st.mref[cb] = kNegBig;
 #pragma nounroll
     for (int pass = 0; pass < 2; ++pass) {
       const bool fixed_ref = pass > 0;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) st.acc[0][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
-      st.lsum[0] = 0.f;
-      st.mlane[0] = -INFINITY;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) st.zp[0][gg] = 0.f;
-      st.wsum[0] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
+        st.lsum[cb] = 0.f;
+        st.mlane[cb] = -INFINITY;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) st.zp[cb][gg] = 0.f;
+        st.wsum[cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+      }
 
       // Pages pgA .. pgB-1, two in flight; page ids from uniform (scalar) loads one page ahead
       // of their copy.  An id outside the pool reads the pool's last page (memory safety).
@@ -1236,25 +1304,50 @@ __global__ __launch_bounds__(64 * kWaves) void int4_decode_mfma_kernel(
         }
         const int q = pgA + k;
         if (k == 0)
-          int4_page<true, true>(pslot(k), a16l, a16t, live_at(q), qo, st, tile, t, r, m4, mask_v,
-                                magic, ones, fixed_ref, next);
+          int4_page<NCB, true, true>(pslot(k), a16l, a16t, live_at(q), qo, st, tile, t, r, m4,
+                                     mask_v, magic, ones, fixed_ref, next);
         else if (k == np - 1)
-          int4_page<true, false>(pslot(k), a16l, a16t, live_at(q), qo, st, tile, t, r, m4, mask_v,
-                                 magic, ones, fixed_ref, next);
+          int4_page<NCB, true, false>(pslot(k), a16l, a16t, live_at(q), qo, st, tile, t, r, m4,
+                                      mask_v, magic, ones, fixed_ref, next);
         else
-          int4_page<false, false>(pslot(k), a16l, a16t, true, qo, st, tile, t, r, m4, mask_v,
-                                  magic, ones, fixed_ref, next);
+          int4_page<NCB, false, false>(pslot(k), a16l, a16t, true, qo, st, tile, t, r, m4, mask_v,
+                                       magic, ones, fixed_ref, next);
       }
 
       // A logit beyond the reference margin: recompute once with the exact max (rare path).
-      const float mexact = row_max16(st.mlane[0]) * qo.cscale[0];
-      const bool redo = mexact > st.mref[0] + kRefMargin;
+      bool redo = false;
+      float mexact[kLaneHeads<NCB>];
+#pragma unroll
+      for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) {
+        mexact[cb] = row_max16(st.mlane[cb]) * qo.cscale[cb];
+        redo |= mexact[cb] > st.mref[cb] + kRefMargin;
+      }
       if (pass > 0 || !__any(redo)) break;
-      st.mref[0] = mexact;
+#pragma unroll
+      for (int cb = 0; cb < kLaneHeads<NCB>; ++cb) st.mref[cb] = mexact[cb];
     }
 
-    // Finish (as int2_decode_kernel<1>): o'[c] = 16 (acc - sum_t W_t) + sum_t p_t z_t.
-    {
+    // Finish (as int2_decode_kernel<NCB>): o'[c] = 16 (acc - sum_t W_t) + sum_t p_t z_t.
+    if constexpr (NCB == 8) {
+      // lane head hh = head 2r + hh; its row in block g/2 for group g is element 2hh + g%2
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float lt = row_sum16(st.lsum[hh]);
+        float zt[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) zt[gg] = row_sum16(st.zp[hh][gg]);
+        const int j = 2 * r + hh;
+        if ((unsigned)slot < (unsigned)max_splits) {
+          float* o = ws.o(b, hq, h * G + j, slot);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int gg = nb >> 1, i = 2 * hh + (gg & 1);
+            o[16 * nb + t] = fmaf(16.0f, st.acc[0][nb][i] - st.wsum[gg >> 1][i], zt[gg]);
+          }
+          if (t == 0) *ws.ml(b, hq, h * G + j, slot) = make_float2(st.mref[hh], lt);
+        }
+      }
+    } else {
       const float lt = row_sum16(st.lsum[0]);
       float zt[4];
 #pragma unroll
@@ -1298,7 +1391,8 @@ int resident_workers() {
   return n;
 }
 
-// Resident worker waves of int4_decode_mfma_kernel on the current device (cached per device).
+// Resident worker waves of int4_decode_mfma_kernel<NCB> on the current device (cached per device).
+template <int NCB>
 int int4_resident_workers() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
@@ -1308,7 +1402,7 @@ int int4_resident_workers() {
   if (n > 0) return n;
   const int cus = current_device_cus();
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)int4_decode_mfma_kernel,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)int4_decode_mfma_kernel<NCB>,
                                                    64 * kWaves, 0) != hipSuccess)
     per_cu = 0;
   n = max(cus, 1) * max(per_cu, 1) * kWaves;
@@ -1409,8 +1503,8 @@ hipError_t launch_int4_mfma_decode(const CacheGeom& g, const uint8_t* pages,
                                   const Workspace& ws, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   const int G = hq / g.hkv;
-  if (G > 4) return hipErrorInvalidValue;
-  const int workers = int4_resident_workers();
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  const int workers = G <= 4 ? int4_resident_workers<1>() : int4_resident_workers<8>();
   // Launch shape as for the INT2 pages (launch_decode).
   const int cus = current_device_cus();
   const bool small = (long long)batch * g.hkv * 2 < cus;
@@ -1424,9 +1518,14 @@ hipError_t launch_int4_mfma_decode(const CacheGeom& g, const uint8_t* pages,
   if (e != hipSuccess) return e;
   const int worker_groups = (workers + kWaves - 1) / kWaves;
   const dim3 grid(worker_groups + batch * g.hkv * wparts);
-  hipLaunchKernelGGL(int4_decode_mfma_kernel, grid, dim3(64 * kWaves), 0, stream, g, pages,
-                     sinkwin, block_table, slot_ids, hq, seq_lens, ws.plan(), sm_scale,
-                     worker_groups, window_first, wparts, ws);
+  if (G <= 4)
+    hipLaunchKernelGGL(int4_decode_mfma_kernel<1>, grid, dim3(64 * kWaves), 0, stream, g, pages,
+                       sinkwin, block_table, slot_ids, hq, seq_lens, ws.plan(), sm_scale,
+                       worker_groups, window_first, wparts, ws);
+  else
+    hipLaunchKernelGGL(int4_decode_mfma_kernel<8>, grid, dim3(64 * kWaves), 0, stream, g, pages,
+                       sinkwin, block_table, slot_ids, hq, seq_lens, ws.plan(), sm_scale,
+                       worker_groups, window_first, wparts, ws);
   return hipGetLastError();
 }
 

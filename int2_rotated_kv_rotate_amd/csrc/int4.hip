@@ -24,13 +24,8 @@
 // Kernels:
 //   int4_append_kernel  16 new rows of one (KV head, K|V) per workgroup, fp64 rotation on the
 //                       vector ALUs (R staged in LDS), quantisation, packing, BF16 copies;
-//   int4_decode_kernel  (G = 8; G <= 4 runs int4_decode_mfma_kernel on the matrix cores, in
-//                       decode.hip) one workgroup per (split, KV head, sequence): every position of the
-//                       split, INT4 or BF16 sink/window, on the vector ALUs; each of the 16
-//                       token lanes keeps its own running softmax (rescaled only when its max
-//                       grows) and the 16 are merged at the end; the next page's words are
-//                       loaded while a page is computed; writes a partial in the INT2 workspace
-//                       format, so oscar_combine finishes it (R_V^T, fixed merge order).
+// The decode of these records runs on the matrix cores (int4_decode_mfma_kernel in decode.hip,
+// every G), in the INT2 workspace format, so oscar_combine finishes it.
 #include "oscar_internal.h"
 
 namespace oscar {
@@ -39,8 +34,6 @@ namespace {
 constexpr int kRecord4 = 2560;
 constexpr int kK4Codes = 0, kV4Codes = 1024, kK4Meta = 2048, kV4Meta = 2304;
 constexpr int kT4 = 256;
-constexpr float kLog2e4 = 1.4426950408889634f;
-constexpr float kNegBig4 = -1.0e30f;
 
 // grid (ceil(N / 16), Hkv, K|V), 256 threads.
 __global__ __launch_bounds__(kT4) void int4_append_kernel(
@@ -194,209 +187,6 @@ __global__ __launch_bounds__(kT4) void int4_append_kernel(
   }
 }
 
-// ------------------------------------------------------------------------------------ decode
-
-// grid (max_splits, Hkv, B), 256 threads: thread t = (token lane r = t / 16, channel octet
-// k = t % 16: channels 8k .. 8k + 7, group k / 4).  Split s of sequence b covers pages
-// [s * sp, (s + 1) * sp) with sp = max(split_pages, ceil(P_b / max_splits)), P_b = ceil(L_b / 16).
-template <int GMAX>
-__global__ __launch_bounds__(kT4, GMAX <= 4 ? 4 : 2) void int4_decode_kernel(
-    CacheGeom g, const uint8_t* __restrict__ pages, const uint16_t* __restrict__ sinkwin,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int hq,
-    const int32_t* __restrict__ seq_lens, float sm_scale, int split_pages, Workspace ws) {
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int r = t >> 4, k = t & 15, gi = k >> 2;
-  const int G = hq / g.hkv;
-  const int max_splits = ws.max_splits();
-  const int L = max(seq_lens[b], 0);
-  const int P = (L + kPage - 1) / kPage;
-  const int sp = max(split_pages, (P + max_splits - 1) / max_splits);
-  const int nsplit = P == 0 ? 0 : (P + sp - 1) / sp;
-  if (s == 0) {  // the split count of this pair, and empty window slots (positions are here)
-    if (t == 0) ws.nvalid()[b * g.hkv + h] = nsplit;
-    static_assert(GMAX * kWinSlots <= kT4, "one thread per empty window slot");
-    if (t < G * kWinSlots)
-      *ws.ml(b, hq, h * G + t / kWinSlots, ws.win_slot() + t % kWinSlots) = make_float2(kNegBig4, 0.f);
-  }
-  if (s >= nsplit) return;
-
-  __shared__ float s_q[GMAX][kHeadDim];
-  __shared__ float s_m[16][GMAX];
-  __shared__ float s_acc[4][GMAX][kHeadDim];
-  __shared__ float s_l[4][GMAX];
-  for (int i = t; i < G * kHeadDim; i += kT4) {
-    const float* qrow = reinterpret_cast<const float*>(ws.qblock(b, hq, h * G + i / kHeadDim));
-    s_q[i / kHeadDim][i % kHeadDim] = qrow[i % kHeadDim];
-  }
-  __syncthreads();
-  float qv[GMAX][8];
-#pragma unroll
-  for (int j = 0; j < GMAX; ++j)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qv[j][c] = j < G ? s_q[j][8 * k + c] : 0.f;
-
-  const float sm_log2 = sm_scale * kLog2e4;
-  const int n_sink = min(L, g.num_sink);
-  const int n_win = min(g.window, L - n_sink);
-  const int slot = slot_ids ? slot_ids[b] : b;
-  const bool have_store = sinkwin != nullptr && slot >= 0 && slot < g.num_slots;
-  const size_t sw_base = ((size_t)slot * g.hkv + h) * (size_t)(g.num_sink + g.window);
-  float m[GMAX], l[GMAX], acc[GMAX][8];
-#pragma unroll
-  for (int j = 0; j < GMAX; ++j) {
-    m[j] = kNegBig4;
-    l[j] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[j][c] = 0.f;
-  }
-  const int pg0 = s * sp, pg1 = min(P, pg0 + sp);
-  // One position's words: kind 0 none, 1 BF16 store row (K, V octets), 2 INT4 record (codes and
-  // (scale, zero) words).  Fetched one page ahead of its use.
-  struct Words {
-    int kind;
-    uint4 ku, vu;
-    uint32_t km, vm;
-  };
-  const int32_t* bt = block_table + (size_t)b * g.max_pages;
-  auto fetch = [&](int pg) {
-    Words f{0, make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), 0u, 0u};
-    const int pos = pg * kPage + r;
-    if (pg >= pg1 || pos >= L) return f;
-    if (pos < n_sink || pos >= L - n_win) {
-      if (!have_store) return f;
-      const int row = pos < n_sink ? pos : g.num_sink + pos % g.window;
-      const uint16_t* kr = sinkwin + (sw_base + row) * 2 * kHeadDim;
-      f.ku = *reinterpret_cast<const uint4*>(kr + 8 * k);
-      f.vu = *reinterpret_cast<const uint4*>(kr + kHeadDim + 8 * k);
-      f.kind = 1;
-      return f;
-    }
-    const int id = pg < g.max_pages ? bt[pg] : -1;
-    if (id < 0 || id >= g.num_pages) return f;
-    const uint8_t* rec = pages + ((size_t)id * g.hkv + h) * kRecord4;
-    // this lane's 8 channels 8k .. 8k+7 of slot r as one word, channel 8k + m at bits 4m.
-    // K: bytes 2 (k%2) and 2 (k%2) + 1 of the two dwords of chunk 16 ((k%8)/2) + r, half k/8
-    // (channels m = 0, 1, 4, 5 in the first dword, 2, 3, 6, 7 in the second).
-    {
-      const uint2 d = *reinterpret_cast<const uint2*>(rec + kK4Codes + 16 * (16 * ((k & 7) >> 1) + r) +
-                                                      8 * (k >> 3));
-      const uint32_t x = (d.x >> (16 * (k & 1))) & 0xFFFFu, y = (d.y >> (16 * (k & 1))) & 0xFFFFu;
-      f.ku.x = (x & 0xFFu) | ((y & 0xFFu) << 8) | ((x >> 8) << 16) | ((y >> 8) << 24);
-    }
-    // V: channel 8k + m is residue 8 (k%2) + m of column block k/2: one byte per channel.
-    {
-      const int u = r & 3, e = (k >> 1) & 1;
-      const uint8_t* vb = rec + kV4Codes + 16 * (16 * (r >> 2) + 8 * (k & 1)) + 4 * (k >> 2) +
-                          2 * (u & 1) + (u >> 1);
-      uint32_t word = 0;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) word |= (((uint32_t)vb[16 * m] >> (4 * e)) & 15u) << (4 * m);
-      f.vu.x = word;
-    }
-    f.km = *reinterpret_cast<const uint32_t*>(rec + kK4Meta + 16 * r + 4 * gi);
-    f.vm = *reinterpret_cast<const uint32_t*>(rec + kV4Meta + 16 * r + 4 * gi);
-    f.kind = 2;
-    return f;
-  };
-  Words cur = fetch(pg0);
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const Words nxt = fetch(pg + 1);
-    if (cur.kind != 0) {   // the 16 lanes of a token agree
-      float kx[8], vx[8];
-      if (cur.kind == 1) {
-        const uint32_t kw[4] = {cur.ku.x, cur.ku.y, cur.ku.z, cur.ku.w};
-        const uint32_t vw[4] = {cur.vu.x, cur.vu.y, cur.vu.z, cur.vu.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kx[2 * i] = __uint_as_float(kw[i] << 16);
-          kx[2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
-          vx[2 * i] = __uint_as_float(vw[i] << 16);
-          vx[2 * i + 1] = __uint_as_float(vw[i] & 0xFFFF0000u);
-        }
-      } else {
-        const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.km & 0xFFFFu));
-        const float kz = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.km >> 16));
-        const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.vm & 0xFFFFu));
-        const float vz = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.vm >> 16));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          kx[c] = fmaf(ks, (float)((cur.ku.x >> (4 * c)) & 15u), kz);
-          vx[c] = fmaf(vs, (float)((cur.vu.x >> (4 * c)) & 15u), vz);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < GMAX; ++j) {
-        if (j >= G) break;
-        float d = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) d = fmaf(qv[j][c], kx[c], d);
-        d += lane_xor_f32<1>(d);
-        d += lane_xor_f32<2>(d);
-        d += lane_xor_f32<4>(d);
-        d += lane_xor_f32<8>(d);
-        const float z = d * sm_log2;
-        if (z > m[j]) {   // a new running max for this token lane: rescale its sums
-          const float sc = __builtin_amdgcn_exp2f(m[j] - z);
-          l[j] *= sc;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[j][c] *= sc;
-          m[j] = z;
-        }
-        const float p = __builtin_amdgcn_exp2f(z - m[j]);
-        l[j] += p;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[j][c] = fmaf(p, vx[c], acc[j][c]);
-      }
-    }
-    cur = nxt;
-  }
-
-  // merge the 16 token lanes: max of m over r, rescale, sum over the lanes of a wave (4 token
-  // lanes), then over the 4 waves, in a fixed order
-  if (k == 0) {
-#pragma unroll
-    for (int j = 0; j < GMAX; ++j)
-      if (j < G) s_m[r][j] = m[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < GMAX; ++j) {
-    if (j >= G) break;
-    float M = s_m[0][j];
-    for (int rr = 1; rr < 16; ++rr) M = fmaxf(M, s_m[rr][j]);
-    const float e = l[j] > 0.f ? __builtin_amdgcn_exp2f(m[j] - M) : 0.f;
-    float lj = l[j] * e;
-    lj += __shfl_xor(lj, 16);
-    lj += __shfl_xor(lj, 32);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float a = acc[j][c] * e;
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      acc[j][c] = a;
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s_acc[wave][j][8 * k + c] = acc[j][c];
-      if (k == 0) s_l[wave][j] = lj;
-    }
-    m[j] = M;
-  }
-  __syncthreads();
-  for (int e = t; e < G * kHeadDim; e += kT4) {
-    const int j = e / kHeadDim, c = e % kHeadDim;
-    const float o = ((s_acc[0][j][c] + s_acc[1][j][c]) + s_acc[2][j][c]) + s_acc[3][j][c];
-    const float lsum = ((s_l[0][j] + s_l[1][j]) + s_l[2][j]) + s_l[3][j];
-    ws.o(b, hq, h * G + j, s)[c] = lsum > 0.f ? o : 0.f;
-    if (c == 0) {
-      float M = s_m[0][j];
-      for (int rr = 1; rr < 16; ++rr) M = fmaxf(M, s_m[rr][j]);
-      *ws.ml(b, hq, h * G + j, s) = make_float2(M, lsum);
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_int4_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
@@ -417,20 +207,10 @@ hipError_t launch_int4_decode(const CacheGeom& g, const uint8_t* pages, const ui
                               int hq, const uint16_t* q, const int32_t* seq_lens,
                               const float* rot_k, float sm_scale, int split_pages,
                               const Workspace& ws, hipStream_t stream) {
+  (void)split_pages;   // the matrix-core kernel's stream-K workers need no split size
   if (batch == 0) return hipSuccess;
-  if (hq / g.hkv <= 4)   // the matrix-core kernel (stream-K workers; split_pages unused)
-    return launch_int4_mfma_decode(g, pages, sinkwin, block_table, slot_ids, batch, hq, q,
-                                   seq_lens, rot_k, sm_scale, ws, stream);
-  hipError_t e = launch_prep_q(g, q, rot_k, batch, hq, seq_lens, ws, stream);
-  if (e != hipSuccess) return e;
-  const dim3 grid(ws.max_splits(), g.hkv, batch);
-  if (hq / g.hkv <= 4)
-    hipLaunchKernelGGL(int4_decode_kernel<4>, grid, dim3(kT4), 0, stream, g, pages, sinkwin,
-                       block_table, slot_ids, hq, seq_lens, sm_scale, split_pages, ws);
-  else
-    hipLaunchKernelGGL(int4_decode_kernel<8>, grid, dim3(kT4), 0, stream, g, pages, sinkwin,
-                       block_table, slot_ids, hq, seq_lens, sm_scale, split_pages, ws);
-  return hipGetLastError();
+  return launch_int4_mfma_decode(g, pages, sinkwin, block_table, slot_ids, batch, hq, q, seq_lens,
+                                 rot_k, sm_scale, ws, stream);
 }
 
 }  // namespace oscar

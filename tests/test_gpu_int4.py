@@ -4,8 +4,9 @@
   sentinel on both sides, equal byte for byte after the same appends (plain and with a key mean).
 * Decode: oscar_int4_decode_attention + oscar_combine within 2e-3 normwise per (sequence, query
   head) row of the oracle's decode of the same INT4 cache, lse within 2e-3; cases span G = 1,
-  4 and 8, ragged lengths, a context entirely in BF16, a single token, and a split budget small
-  enough that splits grow past split_pages.
+  2, 4 and 8 (the matrix-core kernel in both row layouts), ragged lengths, a context entirely in
+  BF16, a single token, a budget of two partials per (sequence, KV head), and a key whose logit
+  jumps ~170 binades past the run's reference (the exact-max recomputation).
 * The INT4 output is closer to exact attention over the unquantised keys and values than the
   INT2 output of the same inputs.
 """
@@ -61,6 +62,10 @@ CASES = {
     "tiny": (W.WORKLOADS["tiny"], {}, None),
     "q4b_ragged": (W.WORKLOADS["qwen3_4b"], dict(batch=3, ctx=1500, ctx_min=300), None),
     "q32b_g8": (W.WORKLOADS["qwen3_32b"], dict(batch=2, ctx=900), None),
+    "q32b_g8_ragged": (W.WORKLOADS["qwen3_32b"], dict(batch=3, ctx=1400, ctx_min=300), None),
+    "q32b_g8_few_splits": (W.WORKLOADS["qwen3_32b"], dict(batch=2, ctx=1200, ctx_min=900), 2),
+    "q32b_g8_spike": (dataclasses.replace(W.WORKLOADS["qwen3_32b"], needle=True, needle_scale=128.0),
+                      dict(batch=2, ctx=1200, ctx_min=900), None),
     "all_bf16": (W.WORKLOADS["tiny"], dict(ctx=60), None),
     "one_token": (W.WORKLOADS["qwen3_4b"], dict(batch=1, ctx=1), None),
     "few_splits": (W.WORKLOADS["qwen3_8b_b64"], dict(batch=2, ctx=1200, ctx_min=900), 2),
