@@ -382,6 +382,35 @@ def int2_vs_bf16(n_iter: int, samples: dict):
                                           "2560-byte pages in a two-page LDS ring"}
     log(f"INT4 qwen3_8b B=64: {ms4:.4f} ms ({b4 / (ms4 * 1e-3) / 1e9:.0f} GB/s)")
     del st4, c4
+
+    # The INT4 variant at G = 8 (Qwen3-32B layer, batch 16, 32k): the matrix-core decode with
+    # the (head, group pair) row layout
+    wg8 = W.WORKLOADS["qwen3_32b"]
+    pg8 = H.make_problem(wg8)
+    c4g8 = H.GpuCache(pg8, bits=4)
+    lk, lv = c4g8.fill_context()
+    st4g8 = H.DecodeStep(c4g8)
+    st4g8.set_new_token(lk, lv)
+    st4g8.run()
+    torch.cuda.synchronize()
+    ms4g8, _, _ = time_scrubbed(st4g8.attend, n_iter, scrub)
+    bg, hg, Gg = int(np.argmax(pg8.lens)), 0, wg8.group
+    samples["int4_" + wg8.name] = (pg8, bg, hg, st4g8.out[bg, hg * Gg:(hg + 1) * Gg].cpu().numpy(),
+                                   st4g8.lse[bg, hg * Gg:(hg + 1) * Gg].cpu().numpy(), 4)
+    lens = np.asarray(pg8.lens, np.int64)
+    n_sink = np.minimum(lens, wg8.num_sink)
+    n_win = np.minimum(wg8.window, lens - n_sink)
+    bg8 = (wg8.num_kv_heads * (INT4_TOKEN_HEAD_BYTES * int((lens - n_sink - n_win).sum()) +
+                               BF16_TOKEN_HEAD_BYTES * int((n_sink + n_win).sum())) +
+           wg8.batch * wg8.num_q_heads * 128 * (2 + 4) + 4 * int(((lens + 15) // 16).sum()))
+    res["int4_qwen3_32b_b16"] = {"ms": round(ms4g8, 4),
+                                 "tokens_per_s": round(wg8.batch / ms4g8 * 1e3, 1),
+                                 "bytes": int(bg8),
+                                 "effective_gbps": round(bg8 / (ms4g8 * 1e-3) / 1e9, 1),
+                                 "decode": "matrix cores, G = 8: (head, group pair) rows, int8 "
+                                           "logits, bf16 P.V"}
+    log(f"INT4 qwen3_32b B=16: {ms4g8:.4f} ms ({bg8 / (ms4g8 * 1e-3) / 1e9:.0f} GB/s)")
+    del st4g8, c4g8
     del scrub
     return res
 
