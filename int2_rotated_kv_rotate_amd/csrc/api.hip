@@ -35,7 +35,8 @@ int32_t check_heads(int32_t hq, int32_t hkv) {
   return OSCAR_OK;
 }
 
-// The combine keeps (m, l) of every split of a KV head's G query heads in 48 KiB of LDS.
+// Slots per (sequence, query head): 2 * G * (max_splits + kWinSlots) floats fit 48 KiB (a limit
+// of the C ABI; the per-query-head combine keeps one float per slot in LDS).
 int32_t check_splits(int32_t hq, int32_t hkv, int32_t max_splits) {
   if (max_splits < 1) return OSCAR_ERR_INVALID_ARGUMENT;
   if ((size_t)2 * (hq / hkv) * ((size_t)max_splits + kWinSlots) * sizeof(float) > 48 * 1024)

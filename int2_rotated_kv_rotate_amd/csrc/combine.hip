@@ -3,147 +3,242 @@
 // rotation (o = o' . R_V^T, exact for orthogonal R_V; OSCAR paper, "Abstract": fixed rotations
 // keep attention aligned with what it consumes).
 //
-// One workgroup serves the G query heads of a KV head; every thread issues all of its global
-// loads (its R_V row and its channel of every split) before the first use.
+// Both forms issue their first loads together (R_V rows into registers, the first partial
+// outputs, the (m, l) pairs), so a workgroup pays about one memory latency for most pairs, and
+// need one workgroup barrier before the R_V^T product (the per-query-head form two more).
+// R_V^T: thread (row c, part p) of 8 threads per row holds R_V[h][c][k] for the p-th slice of
+// 16 k in registers, sums o'[k] R_V[h][c][k] over its slice in ascending k, and the 8 slices
+// are added by a butterfly over the 8 adjacent lanes (a fixed order).  Lane reductions use DPP
+// row operations and lane reads, not LDS permutes.
 #include "oscar_internal.h"
 
 namespace oscar {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kRStride = kHeadDim + 4;  // floats per LDS row of R_V (16-byte aligned, skewed banks)
 
-// grid (Hkv, batch), block 128 * G: thread (j, c) = (query head of the group, channel).
-__global__ __launch_bounds__(1024) void combine_kernel(int hq, int hkv, Workspace ws,
-                                                      const float* __restrict__ rot_v,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int G = hq / hkv;
-  const int j = threadIdx.x >> 7, c = threadIdx.x & 127;
-  const int ns = ws.nslots;
-  const int jq = h * G + j;
-  extern __shared__ float s_w[];        // [2][G][ns]: merge weights 2^(m - M) (0 for empty), l
-  __shared__ __attribute__((aligned(16))) float s_o[8][kHeadDim];
-  __shared__ float s_red[8][4];         // per head: max, then l, of each of its two waves
-  __shared__ float4 s_r[kHeadDim][kRStride / 4];  // R_V[h], rows padded: conflict-free reads
-
-  // Issue the loads first: R_V[h] (coalesced, into LDS) and this thread's channel of the slots.
-  // Loads are issued 8 at a time before their LDS stores, so staging costs one memory latency
-  // for G >= 4 (4096 quads over 512 or 1024 threads) and 2 or 4 for G = 2, 1.
-  if (rot_v != nullptr) {
-    const float4* R = reinterpret_cast<const float4*>(rot_v + (size_t)h * kHeadDim * kHeadDim);
-    constexpr int kQuads = kHeadDim * kHeadDim / 4, kChunk = 8;
-    for (int e0 = threadIdx.x; e0 < kQuads; e0 += kChunk * blockDim.x) {
-      float4 rr[kChunk];
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const int e = e0 + k * blockDim.x;
-        rr[k] = e < kQuads ? R[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const int e = e0 + k * blockDim.x;
-        if (e < kQuads) s_r[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = rr[k];
-      }
-    }
-  }
-  // INT2 partials in slots [0, nvalid), the BF16 sink/window partials in the last kWinSlots
-  // slots.  All loads are issued before nvalid is known (slots past it hold stale but readable
-  // values that never enter the sums), so the kernel pays one memory latency, not two.
-  const int nv_raw = ws.nvalid()[b * hkv + h];
-  const int ms = ws.max_splits();
-  const float* o = ws.o(b, hq, jq, 0) + c;
-  constexpr int kBatch = 16;
-  float ov[kBatch];
-#pragma unroll
-  for (int e = 0; e < kBatch; ++e) ov[e] = e < ms ? o[(size_t)e * kHeadDim] : 0.f;
-  float ow[kWinSlots];
-#pragma unroll
-  for (int k = 0; k < kWinSlots; ++k) ow[k] = o[(size_t)(ms + k) * kHeadDim];
-  for (int e = c; e < ns; e += 128) {  // raw (m, l) of every slot of head j
-    const float2 ml = *ws.ml(b, hq, jq, e);
-    s_w[j * ns + e] = ml.x;
-    s_w[G * ns + j * ns + e] = ml.y;
-  }
-  __syncthreads();
-  const int nv = min(max(nv_raw, 0), ms);
-  // Merge weights, computed by the head's 128 threads (entry e by thread e % 128): the INT2
-  // slots 0 .. nv-1 and the window slots; M and l reduced in a fixed order.
-  float* wm = s_w + j * ns;
-  const float* wl = s_w + G * ns + j * ns;
-  float mloc = -INFINITY;
-  for (int e = c; e < ns; e += 128)
-    if ((e < nv || e >= ms) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2));
-  if ((c & 63) == 0) s_red[j][c >> 6] = mloc;
-  __syncthreads();
-  const float M = fmaxf(s_red[j][0], s_red[j][1]);
-  float lloc = 0.f;
-  for (int e = c; e < ns; e += 128) {
-    const bool use = (e < nv || e >= ms) && wl[e] > 0.f;
-    const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
-    wm[e] = w;
-    if (use) lloc = fmaf(w, wl[e], lloc);  // an unused slot's stale l may be NaN
-  }
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2);
-  if ((c & 63) == 0) s_red[j][2 + (c >> 6)] = lloc;
-  __syncthreads();
-  const float l = s_red[j][2] + s_red[j][3];
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  if (c == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
-  // o'[j][c] = sum_e w_e o'_e[c] / l over the INT2 slots in order, then the window slots in
-  // order; an empty entry (w = 0) is skipped, so its partial output is never read into the
-  // sum.  Slots past the first 16 are loaded 16 at a time.
-  const float* wj = wm;
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < kBatch; ++e) {
-    if (e < nv && wj[e] > 0.f) acc = fmaf(wj[e], ov[e], acc);
-  }
-  for (int e0 = kBatch; e0 < nv; e0 += kBatch) {
-    float ob[kBatch];
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e) ob[e] = e0 + e < nv ? o[(size_t)(e0 + e) * kHeadDim] : 0.f;
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e) {
-      const float w = e0 + e < nv ? wj[e0 + e] : 0.f;
-      if (w > 0.f) acc = fmaf(w, ob[e], acc);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kWinSlots; ++k)
-    if (wj[ms + k] > 0.f) acc = fmaf(wj[ms + k], ow[k], acc);
-  s_o[j][c] = acc * inv;
-  __syncthreads();
-  float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
-  if (rot_v == nullptr) {
-    orow[c] = s_o[j][c];
-    return;
-  }
-  // out[j][c] = sum_k o'[j][k] * R_V[h][c][k]
-  float acc2 = 0.f;
-#pragma unroll 8
-  for (int k4 = 0; k4 < kHeadDim / 4; ++k4) {
-    const float4 r = s_r[c][k4];
-    const float4 ov = *reinterpret_cast<const float4*>(&s_o[j][4 * k4]);
-    acc2 = fmaf(ov.x, r.x, acc2);
-    acc2 = fmaf(ov.y, r.y, acc2);
-    acc2 = fmaf(ov.z, r.z, acc2);
-    acc2 = fmaf(ov.w, r.w, acc2);
-  }
-  orow[c] = acc2;
+// DPP lane moves within rows of 16 lanes: quad_perm xor 1 and xor 2, row rotation by 8 (= xor
+// 8), and xor 4 from a left and a right row shift on alternate banks of 4 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kRor8 = 0x128;
+__device__ __forceinline__ float xor4(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int t = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+  t = __builtin_amdgcn_update_dpp(t, x, 0x114, 0xF, 0xA, false);      // row_shr:4, banks 1, 3
+  return __builtin_bit_cast(float, t);
+}
+// Sum / max over the 16 lanes of each row: every lane of a row gets the same value.
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<kXor1>(v);
+  v += dpp<kXor2>(v);
+  v += xor4(v);
+  return v + dpp<kRor8>(v);
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp<kXor1>(v));
+  v = fmaxf(v, dpp<kXor2>(v));
+  v = fmaxf(v, xor4(v));
+  return fmaxf(v, dpp<kRor8>(v));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
-// Small-grid form: grid (Hq, batch), block 512, one workgroup per query head, for launches
-// where one workgroup per KV head would leave most of the chip idle and each head has many
-// splits.  Thread t = (slot lane sg = t / 32 of 16, channel quad c4 = t % 32): slot lane sg
-// sums slots sg, sg + 16, ... in ascending order with 16-byte loads; its first eight slots and
-// the BF16 slot are loaded with everything else at the start (slots past the pair's count are
-// read but never used), the rest eight at a time.  The 16 lanes' partial sums are added in lane
-// order.  For R_V^T, thread t computes half (kh = t % 2) of output channel t / 2 (only threads
-// < 256) from its R_V row, loaded first.
-constexpr int kHeadThreads = 512, kSlotLanes = kHeadThreads / 32;
+// A slot enters the merge if it is one of the pair's INT2 slots (e < nv) or a window slot
+// (e >= ms) and holds positions (l > 0); the outputs of other slots are never read into a sum
+// (their stale values may be NaN).
+__device__ __forceinline__ bool slot_used(int e, int nv, int ms, float l) {
+  return (e < nv || e >= ms) && l > 0.f;
+}
+
+// R_V^T: 8 threads per output row.
+constexpr int kRotParts = 8, kRotQuads = kHeadDim / 4 / kRotParts;
+
+// R_V[h] row c, slice part: kRotQuads float4, loaded first and used last.
+__device__ __forceinline__ void load_rot(const float* rot_v, int h, int c, int part,
+                                         float4 (&r)[kRotQuads]) {
+  const float4* R =
+      reinterpret_cast<const float4*>(rot_v + ((size_t)h * kHeadDim + c) * kHeadDim) +
+      part * kRotQuads;
+#pragma unroll
+  for (int i = 0; i < kRotQuads; ++i) r[i] = R[i];
+}
+
+// o'[k] R_V[c][k] over the thread's slice (k ascending) for the o' row so, then the 8 slices of
+// the row added by a butterfly over the 8 adjacent lanes: every lane of the 8 gets the sum.
+__device__ __forceinline__ float rot_slice(const float* so, const float4 (&r)[kRotQuads], int part) {
+  const float4* s4 = reinterpret_cast<const float4*>(so) + part * kRotQuads;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRotQuads; ++i) {
+    const float4 x = s4[i];
+    acc = fmaf(x.x, r[i].x, acc);
+    acc = fmaf(x.y, r[i].y, acc);
+    acc = fmaf(x.z, r[i].z, acc);
+    acc = fmaf(x.w, r[i].w, acc);
+  }
+  acc += dpp<kXor1>(acc);
+  acc += dpp<kXor2>(acc);
+  return acc + xor4(acc);
+}
+
+// Query-head rows per workgroup of the per-KV-head form: 8 / G sequences x G heads, so R_V[h]
+// is read once for 8 rows whatever G is.
+constexpr int kRows = 8, kRowThreads = kRows * kHeadDim;
+
+// grid (Hkv, ceil(batch / (8 / G))), block 1024.
+// Merge role: thread (row j, channel c), row j = (sequence b0 + j / G, head j % G of the
+// group); each of a row's two wavefronts computes the row's merge weights itself (max and sum
+// in a fixed order, every lane holding the weights of slots lane, lane + 64) and reads a
+// slot's weight with a lane read, so the merge needs no barrier and no LDS.
+// R_V^T role: every thread, (output row u / 8, slice u % 8), for the 8 o' rows.
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(int batch, int hq, int hkv,
+                                                            Workspace ws,
+                                                            const float* __restrict__ rot_v,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+  const int h = blockIdx.x;
+  const int G = hq / hkv, nb = kRows / G;
+  const int u = threadIdx.x, lane = u & 63;
+  const int j = u >> 7, c = u & 127;
+  const int b = blockIdx.y * nb + j / G, jq = h * G + j % G;
+  const bool live = b < batch;  // uniform per wavefront
+  const int ns = ws.nslots, ms = ws.max_splits();
+  __shared__ __attribute__((aligned(16))) float s_o[kRows][kHeadDim];
+
+  float4 r[kRotQuads];
+  if (rot_v != nullptr) load_rot(rot_v, h, u / kRotParts, u % kRotParts, r);
+  // The first kFirst INT2 slots and window slot 0 are loaded with everything else; later INT2
+  // slots (past kFirst, up to nv) kBatch at a time, and window slots 1.. only where used.
+  constexpr int kFirst = 12, kBatch = 8;
+  constexpr int kMl = 2;  // (m, l) of slots lane and lane + 64, loaded up front
+  if (live) {
+    const int nv = min(max(ws.nvalid()[b * hkv + h], 0), ms);
+    const float* o = ws.o(b, hq, jq, 0) + c;
+    float ov[kFirst];
+#pragma unroll
+    for (int e = 0; e < kFirst; ++e) ov[e] = e < ms ? o[(size_t)e * kHeadDim] : 0.f;
+    const float ow0 = o[(size_t)ms * kHeadDim];
+    float2 mlr[kMl];
+#pragma unroll
+    for (int i = 0; i < kMl; ++i) {
+      const int e = lane + 64 * i;
+      mlr[i] = e < ns ? *ws.ml(b, hq, jq, e) : make_float2(-INFINITY, 0.f);
+    }
+    // M over the used slots, then w_e = 2^(m_e - M) and l = sum_e w_e l_e (lane sums in slot
+    // order, then the fixed reduction)
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMl; ++i) {
+      const int e = lane + 64 * i;
+      if (e < ns && slot_used(e, nv, ms, mlr[i].y)) mloc = fmaxf(mloc, mlr[i].x);
+    }
+    for (int e = lane + 64 * kMl; e < ns; e += 64) {
+      const float2 ml = *ws.ml(b, hq, jq, e);
+      if (slot_used(e, nv, ms, ml.y)) mloc = fmaxf(mloc, ml.x);
+    }
+    const float M = wave_max(mloc);
+    float wl[kMl];  // weights of slots lane, lane + 64
+    float lloc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMl; ++i) {
+      const int e = lane + 64 * i;
+      const bool use = e < ns && slot_used(e, nv, ms, mlr[i].y);
+      wl[i] = use ? __builtin_amdgcn_exp2f(mlr[i].x - M) : 0.f;
+      if (use) lloc = fmaf(wl[i], mlr[i].y, lloc);
+    }
+    for (int e = lane + 64 * kMl; e < ns; e += 64) {
+      const float2 ml = *ws.ml(b, hq, jq, e);
+      if (slot_used(e, nv, ms, ml.y)) lloc = fmaf(__builtin_amdgcn_exp2f(ml.x - M), ml.y, lloc);
+    }
+    const float l = wave_sum(lloc);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    if (c == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
+    // weight of slot e (uniform): from the lane that holds it, else from its (m, l)
+    auto weight = [&](int e) {
+      if (e < 64 * kMl) return lane_value(e < 64 ? wl[0] : wl[1], e & 63);
+      const float2 ml = *ws.ml(b, hq, jq, e);
+      return slot_used(e, nv, ms, ml.y) ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+    };
+    // used window slots past the first: their loads go out before the INT2 sums
+    float owk[kWinSlots - 1];
+#pragma unroll
+    for (int k = 1; k < kWinSlots; ++k)
+      owk[k - 1] = weight(ms + k) > 0.f ? o[(size_t)(ms + k) * kHeadDim] : 0.f;
+    // o'[j][c] = sum_e w_e o'_e[c] / l: INT2 slots in order, then the window slots in order
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < kFirst; ++e) {
+      if (e < nv) {
+        const float w = weight(e);
+        if (w > 0.f) acc = fmaf(w, ov[e], acc);
+      }
+    }
+    for (int e0 = kFirst; e0 < nv; e0 += kBatch) {
+      float ob[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) ob[e] = e0 + e < nv ? o[(size_t)(e0 + e) * kHeadDim] : 0.f;
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        if (e0 + e < nv) {
+          const float w = weight(e0 + e);
+          if (w > 0.f) acc = fmaf(w, ob[e], acc);
+        }
+      }
+    }
+    {
+      const float w = weight(ms);
+      if (w > 0.f) acc = fmaf(w, ow0, acc);
+    }
+#pragma unroll
+    for (int k = 1; k < kWinSlots; ++k) {
+      const float w = weight(ms + k);
+      if (w > 0.f) acc = fmaf(w, owk[k - 1], acc);
+    }
+    s_o[j][c] = acc * inv;
+  }
+  __syncthreads();
+  if (rot_v == nullptr) {
+    if (live) out[((size_t)b * hq + jq) * kHeadDim + c] = s_o[j][c];
+    return;
+  }
+  // out[row jr][c'] = sum_k o'[jr][k] R_V[h][c'][k]; lane slice p writes row p
+  const int crow = u / kRotParts, part = u % kRotParts;
+  const int b0 = blockIdx.y * nb;
+#pragma unroll
+  for (int jr = 0; jr < kRows; ++jr) {
+    const int br = b0 + jr / G;
+    if (br < batch) {  // uniform
+      const float v = rot_slice(s_o[jr], r, part);
+      if (part == jr) out[((size_t)br * hq + h * G + jr % G) * kHeadDim + crow] = v;
+    }
+  }
+}
+
+// Per-query-head form: grid (Hq, batch), block 1024, for launches where one workgroup per KV
+// head would leave most of the chip idle and each head has many splits.
+//   (m, l) role: thread u takes slots u, u + 1024, ... with a running (max, sum); the
+//     wavefronts' pairs are merged through LDS (one barrier) in wavefront order.
+//   slot lanes: thread (sg = u / 32 of 32, channel quad u % 32) sums slots sg, sg + 32, ... in
+//     ascending order with 16-byte loads, the first eight loaded at the start, the rest eight
+//     at a time; then (second barrier) thread ch < 128 adds the 32 lanes' sums in lane order,
+//     then the window slots in order.
+//   R_V^T: thread (row u / 8, slice u % 8), its 16 values of R_V[h][row] loaded at the start.
+// The (m, l) merges of a wavefront run over its rows of 16 lanes, then its four rows in order.
+constexpr int kHeadThreads = 1024, kSlotLanes = kHeadThreads / 32, kHeadWaves = kHeadThreads / 64;
 static_assert(kWinSlots <= kSlotLanes, "one slot lane per window slot");
 
 __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int hkv, Workspace ws,
@@ -151,74 +246,92 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
                                                                   float* __restrict__ out,
                                                                   float* __restrict__ lse) {
   const int jq = blockIdx.x, b = blockIdx.y, h = jq / (hq / hkv);
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int ns = ws.nslots;
-  extern __shared__ float s_w[];  // [2][ns]: m of each slot (then its merge weight), l
-  __shared__ float4 s_part[kSlotLanes][32];
-  __shared__ float4 s_win[kWinSlots][32];  // the window slots' outputs
-  __shared__ float s_o[kHeadDim];
-  __shared__ float s_red[2][kHeadThreads / 64];
+  const int u = threadIdx.x, lane = u & 63, wv = u >> 6;
+  const int ns = ws.nslots, ms = ws.max_splits();
+  extern __shared__ float s_m[];  // [ns]: m of each used slot, -inf for the others
+  __shared__ __attribute__((aligned(16))) float s_part[kSlotLanes][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_win[kWinSlots][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_o[kHeadDim];
+  __shared__ float2 s_red[kHeadWaves];
 
-  const int c_out = t >> 1, kh = t & 1;
-  float4 r[16];
-  if (rot_v != nullptr && t < 2 * kHeadDim) {
-    const float4* R = reinterpret_cast<const float4*>(
-        rot_v + ((size_t)h * kHeadDim + c_out) * kHeadDim + (kHeadDim / 2) * kh);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) r[k] = R[k];
-  }
-  const int nv_raw = ws.nvalid()[b * hkv + h];
-  const int sg = t >> 5, c4 = t & 31;
+  float4 r[kRotQuads];
+  if (rot_v != nullptr) load_rot(rot_v, h, u / kRotParts, u % kRotParts, r);
+  const int nv = min(max(ws.nvalid()[b * hkv + h], 0), ms);
+  const int sg = u >> 5, c4 = u & 31;
   const float4* ob = reinterpret_cast<const float4*>(ws.o(b, hq, jq, 0)) + c4;
   constexpr int kStride = kHeadDim / 4;  // float4 per slot
   constexpr int kFlight = 8;
-  const int ms = ws.max_splits();
   float4 pre[kFlight];
 #pragma unroll
   for (int k = 0; k < kFlight; ++k) {
     const int e = sg + k * kSlotLanes;
     pre[k] = e < ms ? ob[(size_t)e * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // window slot sg (< kWinSlots) of this thread's channel quad, added after the INT2 sums
+  // window slot sg (< kWinSlots) of this thread's channel quad
   const float4 owin = sg < kWinSlots ? ob[(size_t)(ms + sg) * kStride] : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int e = t; e < ns; e += kHeadThreads) {
-    const float2 ml = *ws.ml(b, hq, jq, e);
-    s_w[e] = ml.x;
-    s_w[ns + e] = ml.y;
+  const float2 ml0 = u < ns ? *ws.ml(b, hq, jq, u) : make_float2(-INFINITY, 0.f);
+
+  // running (max, sum of 2^(m - max) l) over this thread's slots, then the wavefront's
+  float mt = -INFINITY, lt = 0.f;
+  auto take = [&](int e, float2 ml) {
+    const bool use = slot_used(e, nv, ms, ml.y);
+    s_m[e] = use ? ml.x : -INFINITY;
+    if (use) {
+      if (ml.x > mt) {
+        lt = lt * __builtin_amdgcn_exp2f(mt - ml.x) + ml.y;
+        mt = ml.x;
+      } else {
+        lt = fmaf(__builtin_amdgcn_exp2f(ml.x - mt), ml.y, lt);
+      }
+    }
+  };
+  if (u < ns) take(u, ml0);
+  for (int e = u + kHeadThreads; e < ns; e += kHeadThreads) take(e, *ws.ml(b, hq, jq, e));
+  // (max, sum) pairs merged over each row of 16 lanes, then the four rows in order
+  auto merge_pair = [&](float m2, float l2) {
+    const float mm = fmaxf(mt, m2);
+    float ln = 0.f;
+    if (mt > -INFINITY) ln = lt * __builtin_amdgcn_exp2f(mt - mm);
+    if (m2 > -INFINITY) ln = fmaf(l2, __builtin_amdgcn_exp2f(m2 - mm), ln);
+    mt = mm;
+    lt = ln;
+  };
+  merge_pair(dpp<kXor1>(mt), dpp<kXor1>(lt));
+  merge_pair(dpp<kXor2>(mt), dpp<kXor2>(lt));
+  merge_pair(xor4(mt), xor4(lt));
+  merge_pair(dpp<kRor8>(mt), dpp<kRor8>(lt));
+  {
+    const float m0 = lane_value(mt, 0), l0 = lane_value(lt, 0);
+    const float m1 = lane_value(mt, 16), l1 = lane_value(lt, 16);
+    const float m2 = lane_value(mt, 32), l2 = lane_value(lt, 32);
+    const float m3 = lane_value(mt, 48), l3 = lane_value(lt, 48);
+    mt = m0;
+    lt = l0;
+    merge_pair(m1, l1);
+    merge_pair(m2, l2);
+    merge_pair(m3, l3);
   }
+  if (lane == 0) s_red[wv] = make_float2(mt, lt);
+  // slot lanes' channel quads and the window slots' outputs go to LDS after the barrier
   __syncthreads();
-  const int nv = min(max(nv_raw, 0), ms);
-  float* wm = s_w;
-  const float* wl = s_w + ns;
-  float mloc = -INFINITY;
-  for (int e = t; e < ns; e += kHeadThreads)
-    if ((e < nv || e >= ms) && wl[e] > 0.f) mloc = fmaxf(mloc, wm[e]);
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2));
-  if (lane == 0) s_red[0][wv] = mloc;
-  __syncthreads();
-  float M = s_red[0][0];
+  float M = -INFINITY;
 #pragma unroll
-  for (int k = 1; k < kHeadThreads / 64; ++k) M = fmaxf(M, s_red[0][k]);
-  float lloc = 0.f;
-  for (int e = t; e < ns; e += kHeadThreads) {
-    const bool use = (e < nv || e >= ms) && wl[e] > 0.f;
-    const float w = use ? __builtin_amdgcn_exp2f(wm[e] - M) : 0.f;
-    wm[e] = w;
-    if (use) lloc = fmaf(w, wl[e], lloc);  // an unused slot's stale l may be NaN
-  }
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2);
-  if (lane == 0) s_red[1][wv] = lloc;
-  __syncthreads();
+  for (int k = 0; k < kHeadWaves; ++k) M = fmaxf(M, s_red[k].x);
   float l = 0.f;
 #pragma unroll
-  for (int k = 0; k < kHeadThreads / 64; ++k) l += s_red[1][k];
+  for (int k = 0; k < kHeadWaves; ++k) {
+    const float2 p = s_red[k];
+    if (p.x > -INFINITY) l = fmaf(p.y, __builtin_amdgcn_exp2f(p.x - M), l);
+  }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  if (t == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
+  if (u == 0 && lse != nullptr) lse[(size_t)b * hq + jq] = l > 0.f ? M * kLn2 + logf(l) : -INFINITY;
 
-  // o' partial sums: slot lane sg over slots sg, sg + 16, ... (< nv), skipping empty slots.
+  // o' partial sums: slot lane sg over slots sg, sg + 32, ... (< nv), skipping unused slots
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](float w, const float4& x) {
-    if (w > 0.f) {
+  auto add = [&](int e, const float4& x) {
+    const float me = s_m[e];
+    if (me > -INFINITY) {
+      const float w = __builtin_amdgcn_exp2f(me - M);
       acc.x = fmaf(w, x.x, acc.x);
       acc.y = fmaf(w, x.y, acc.y);
       acc.z = fmaf(w, x.z, acc.z);
@@ -228,7 +341,7 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
 #pragma unroll
   for (int k = 0; k < kFlight; ++k) {
     const int e = sg + k * kSlotLanes;
-    if (e < nv) add(wm[e], pre[k]);
+    if (e < nv) add(e, pre[k]);
   }
   int e = sg + kFlight * kSlotLanes;
   for (; e + (kFlight - 1) * kSlotLanes < nv; e += kFlight * kSlotLanes) {
@@ -236,57 +349,31 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
 #pragma unroll
     for (int k = 0; k < kFlight; ++k) x[k] = ob[(size_t)(e + k * kSlotLanes) * kStride];
 #pragma unroll
-    for (int k = 0; k < kFlight; ++k) add(wm[e + k * kSlotLanes], x[k]);
+    for (int k = 0; k < kFlight; ++k) add(e + k * kSlotLanes, x[k]);
   }
-  for (; e < nv; e += kSlotLanes) add(wm[e], ob[(size_t)e * kStride]);
-  s_part[sg][c4] = acc;
-  if (sg < kWinSlots) s_win[sg][c4] = owin;
+  for (; e < nv; e += kSlotLanes) add(e, ob[(size_t)e * kStride]);
+  reinterpret_cast<float4*>(s_part[sg])[c4] = acc;
+  if (sg < kWinSlots) reinterpret_cast<float4*>(s_win[sg])[c4] = owin;
   __syncthreads();
-  if (t < 32) {
-    float4 sum = s_part[0][t];
+  if (u < kHeadDim) {
+    float sum = s_part[0][u];
 #pragma unroll
-    for (int k = 1; k < kSlotLanes; ++k) {
-      const float4 v = s_part[k][t];
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
-    }
+    for (int k = 1; k < kSlotLanes; ++k) sum += s_part[k][u];
 #pragma unroll
     for (int k = 0; k < kWinSlots; ++k) {
-      const float ww = wm[ms + k];
-      if (ww > 0.f) {
-        const float4 x = s_win[k][t];
-        sum.x = fmaf(ww, x.x, sum.x);
-        sum.y = fmaf(ww, x.y, sum.y);
-        sum.z = fmaf(ww, x.z, sum.z);
-        sum.w = fmaf(ww, x.w, sum.w);
-      }
+      const float me = s_m[ms + k];
+      if (me > -INFINITY) sum = fmaf(__builtin_amdgcn_exp2f(me - M), s_win[k][u], sum);
     }
-    s_o[4 * t + 0] = sum.x * inv;
-    s_o[4 * t + 1] = sum.y * inv;
-    s_o[4 * t + 2] = sum.z * inv;
-    s_o[4 * t + 3] = sum.w * inv;
+    s_o[u] = sum * inv;
   }
   __syncthreads();
   float* orow = out + ((size_t)b * hq + jq) * kHeadDim;
   if (rot_v == nullptr) {
-    if (t < kHeadDim) orow[t] = s_o[t];
+    if (u < kHeadDim) orow[u] = s_o[u];
     return;
   }
-  if (t >= 2 * kHeadDim) return;
-  // out[c] = sum_k o'[k] * R_V[h][c][k]: the two halves of k, then their sum (low half first)
-  float part = 0.f;
-#pragma unroll
-  for (int k4 = 0; k4 < 16; ++k4) {
-    const int k = (kHeadDim / 2) * kh + 4 * k4;
-    part = fmaf(s_o[k + 0], r[k4].x, part);
-    part = fmaf(s_o[k + 1], r[k4].y, part);
-    part = fmaf(s_o[k + 2], r[k4].z, part);
-    part = fmaf(s_o[k + 3], r[k4].w, part);
-  }
-  const float other = __shfl_xor(part, 1);
-  if (kh == 0) orow[c_out] = part + other;
+  const float v = rot_slice(s_o, r, u % kRotParts);
+  if (u % kRotParts == 0) orow[u / kRotParts] = v;
 }
 
 }  // namespace
@@ -294,20 +381,20 @@ __global__ __launch_bounds__(kHeadThreads) void combine_head_kernel(int hq, int 
 hipError_t launch_combine(int batch, int hq, int hkv, const Workspace& ws, const float* rot_v,
                           float* out, float* lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  // One workgroup per query head when one per KV head would cover less than half of the
-  // compute units and the heads have many splits to merge.
+  // One workgroup per query head when the (sequence, KV head) pairs would cover less than half
+  // of the compute units and the heads have many splits to merge; else 8 query-head rows of
+  // one KV head per workgroup.
   const int cus = current_device_cus();
   if (cus <= 0) return hipErrorInvalidValue;
   if ((long long)batch * hkv * 2 < cus && ws.max_splits() > 32) {
-    const size_t lds1 = (size_t)2 * ws.nslots * sizeof(float);
+    const size_t lds1 = (size_t)ws.nslots * sizeof(float);
     hipLaunchKernelGGL(combine_head_kernel, dim3(hq, batch), dim3(kHeadThreads), lds1, stream, hq,
                        hkv, ws, rot_v, out, lse);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)2 * (hq / hkv) * ws.nslots * sizeof(float);
-  if (lds > 48 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(hkv, batch), dim3(128 * (hq / hkv)), lds, stream, hq, hkv,
-                     ws, rot_v, out, lse);
+  const int nb = kRows / (hq / hkv);
+  hipLaunchKernelGGL(combine_kernel, dim3(hkv, (batch + nb - 1) / nb), dim3(kRowThreads), 0, stream,
+                     batch, hq, hkv, ws, rot_v, out, lse);
   return hipGetLastError();
 }
 
