@@ -112,27 +112,37 @@ __device__ __forceinline__ void append_rows(
   const int nrows = min(ROWS, total_new - row0);
   const bool centered = !is_v && k_mean != nullptr;
 
-  // Stage R (fp32) and the rows: all 16 loads of a thread are issued before the first LDS
-  // store, so staging costs one memory latency.
+  // Stage R (fp32) and the rows: the first round of the row placement lookups, all 16 R loads
+  // of a thread and its input values are issued before the first wait, so staging costs about
+  // two memory latencies (the lookups' second round overlaps the R loads).
+  const bool look = t < nrows;  // t < ROWS
+  RowLookup lk{};
+  if (look) lk = row_lookup(new_offsets, start_pos, slot_ids, batch, row0 + t);
   const float4* rot4 = reinterpret_cast<const float4*>(rot);
-  {
-    constexpr int kPer = kHeadDim * kHeadDim / 4 / kAppendThreads;  // 16
-    float4 rr[kPer];
+  constexpr int kPer = kHeadDim * kHeadDim / 4 / kAppendThreads;  // 16
+  float4 rr[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) rr[k] = rot4[t + kAppendThreads * k];
+  for (int k = 0; k < kPer; ++k) rr[k] = rot4[t + kAppendThreads * k];
+  constexpr int kXPer = ROWS * kHeadDim / kAppendThreads;  // 2 or 8
+  uint16_t xv[kXPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) s_rot[t + kAppendThreads * k] = rr[k];
-  }
-  for (int i = t; i < ROWS * kHeadDim; i += kAppendThreads) {
-    int r = i / kHeadDim, c = i % kHeadDim;
-    s_x[r][c] = r < nrows ? bf16_to_f32(src[((size_t)(row0 + r) * g.hkv + h) * kHeadDim + c]) : 0.f;
+  for (int k = 0; k < kXPer; ++k) {
+    const int i = t + kAppendThreads * k, r = i / kHeadDim, c = i % kHeadDim;
+    xv[k] = r < nrows ? src[((size_t)(row0 + r) * g.hkv + h) * kHeadDim + c] : (uint16_t)0;
   }
   if (t < ROWS) {
     RowInfo info{-1, 0, -1};
-    if (t < nrows)
-      info = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, sinkwin != nullptr,
-                      row0 + t, h, is_v);
+    if (look)
+      info = row_info_from<kRecord>(g, block_table, slot_ids, batch, new_offsets, start_pos,
+                                    sinkwin != nullptr, lk, h, is_v);
     s_info[t] = info;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) s_rot[t + kAppendThreads * k] = rr[k];
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) {
+    const int i = t + kAppendThreads * k;
+    s_x[i / kHeadDim][i % kHeadDim] = bf16_to_f32(xv[k]);
   }
   if (centered && t < kHeadDim) s_mu[t] = k_mean[(size_t)h * kHeadDim + t];
   __syncthreads();

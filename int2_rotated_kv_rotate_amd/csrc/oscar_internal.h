@@ -264,18 +264,51 @@ struct RowInfo {
 };
 
 // Where new row n (flattened over the batch) of KV head h goes, for records of REC bytes.
+// The lookups take two rounds of dependent loads: the offsets, start position and store slot of
+// the guessed sequence (b = n, one new row per sequence as in decode) together, then the block
+// table entry; a wrong guess bisects the offsets.  row_lookup issues the first round, so that a
+// caller can issue other loads before row_info_from waits for it.
+struct RowLookup {
+  int n, g, og, og1, sp, slot;
+};
+__device__ __forceinline__ RowLookup row_lookup(const int32_t* __restrict__ new_offsets,
+                                                const int32_t* __restrict__ start_pos,
+                                                const int32_t* __restrict__ slot_ids, int batch,
+                                                int n) {
+  RowLookup L;
+  L.n = n;
+  L.g = min(n, batch - 1);
+  L.og = new_offsets[L.g];
+  L.og1 = new_offsets[L.g + 1];
+  L.sp = start_pos[L.g];
+  L.slot = slot_ids ? slot_ids[L.g] : L.g;
+  return L;
+}
+
 template <int REC>
-__device__ RowInfo row_info_t(const CacheGeom& g, const int32_t* __restrict__ block_table,
-                              const int32_t* __restrict__ slot_ids, int batch,
-                              const int32_t* __restrict__ new_offsets,
-                              const int32_t* __restrict__ start_pos, bool has_store, int n, int h,
-                              bool is_v) {
+__device__ RowInfo row_info_from(const CacheGeom& g, const int32_t* __restrict__ block_table,
+                                 const int32_t* __restrict__ slot_ids, int batch,
+                                 const int32_t* __restrict__ new_offsets,
+                                 const int32_t* __restrict__ start_pos, bool has_store,
+                                 const RowLookup& L, int h, bool is_v) {
   RowInfo info{-1, 0, -1};
-  const int b = row_to_seq(new_offsets, batch, n);
-  const int first = new_offsets[b];
-  const int nnew = new_offsets[b + 1] - first;
-  const int pos = start_pos[b] + (n - first);
-  const int new_len = start_pos[b] + nnew;
+  const int n = L.n;
+  int b, first, nnew, sp, slot;
+  if (L.og <= n && (L.g == batch - 1 || L.og1 > n)) {
+    b = L.g;
+    first = L.og;
+    nnew = L.og1 - L.og;
+    sp = L.sp;
+    slot = L.slot;
+  } else {
+    b = row_to_seq(new_offsets, batch, n);
+    first = new_offsets[b];
+    nnew = new_offsets[b + 1] - first;
+    sp = start_pos[b];
+    slot = slot_ids ? slot_ids[b] : b;
+  }
+  const int pos = sp + (n - first);
+  const int new_len = sp + nnew;
   const int lp = pos / kPage;
   if (pos >= 0 && lp < g.max_pages) {
     const int page = block_table[(size_t)b * g.max_pages + lp];
@@ -284,7 +317,6 @@ __device__ RowInfo row_info_t(const CacheGeom& g, const int32_t* __restrict__ bl
       info.slot_in_page = pos % kPage;
     }
   }
-  const int slot = slot_ids ? slot_ids[b] : b;
   int row = -1;
   if (pos >= 0 && pos < g.num_sink) row = pos;
   else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
@@ -293,6 +325,16 @@ __device__ RowInfo row_info_t(const CacheGeom& g, const int32_t* __restrict__ bl
     info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
               (is_v ? kHeadDim : 0);
   return info;
+}
+
+template <int REC>
+__device__ RowInfo row_info_t(const CacheGeom& g, const int32_t* __restrict__ block_table,
+                              const int32_t* __restrict__ slot_ids, int batch,
+                              const int32_t* __restrict__ new_offsets,
+                              const int32_t* __restrict__ start_pos, bool has_store, int n, int h,
+                              bool is_v) {
+  return row_info_from<REC>(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store,
+                            row_lookup(new_offsets, start_pos, slot_ids, batch, n), h, is_v);
 }
 
 // fp16 scale and zero of a group from its extremes: s = (c*mx - c*mn) / STEPS, z = c*mn

@@ -234,10 +234,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_q_kernel(
   prep_q_block(g, q, rot_k, hq, seq_lens, workers, hpw, 1, ws, blockIdx.x, blockIdx.y, sm);
 }
 
-// Append (4 rows per workgroup) and query preparation in one grid: the first app_blocks
-// workgroups are the append's (app_gx x Hkv x 2, x fastest), then the preparation's
-// (prep_gx x ceil(batch / spb), x fastest) and last the one that builds the plan.  The two
-// roles share one block of LDS.
+// Append (4 rows per workgroup) and query preparation in one grid: workgroup 0 builds the
+// plan, the next app_blocks are the append's (app_gx x Hkv x 2, x fastest), then the
+// preparation's (prep_gx x ceil(batch / spb), x fastest).  The roles share one block of LDS.
 union StepShared {
   AppendShared<4> a;
   PrepShared p;
@@ -254,13 +253,16 @@ __global__ __launch_bounds__(kPrepThreads) void append_prepare_kernel(
     int app_blocks, int app_gx, int prep_gx) {
   __shared__ StepShared sm;
   const int id = blockIdx.x;
-  if (id < app_blocks) {
-    const int bx = id % app_gx, rest = id / app_gx;
+  if (id == 0) {  // the plan, first in the grid: its workgroup never waits for a free slot
+    prep_q_block(g, q, rot_k, hq, seq_lens, workers, hpw, spb, ws, 0, (ws.batch + spb - 1) / spb,
+                 sm.p);
+  } else if (id - 1 < app_blocks) {
+    const int a = id - 1, bx = a % app_gx, rest = a / app_gx;
     append_rows<4>(g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new,
                    new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v, bx,
                    rest % g.hkv, rest / g.hkv, sm.a);
   } else {
-    const int p = id - app_blocks;
+    const int p = id - 1 - app_blocks;
     prep_q_block(g, q, rot_k, hq, seq_lens, workers, hpw, spb, ws, p % prep_gx, p / prep_gx,
                  sm.p);
   }
