@@ -241,28 +241,13 @@ def test_distinct_k_and_v_rotations_are_not_conflated():
     assert row_errors(step.out.cpu().numpy(), wrong).max() > 0.1
 
 
-@pytest.mark.parametrize("max_splits,nvalid_rows", [
-    (5, [[5, 3], [2, 0], [4, 5]]),            # one workgroup per KV head
-    (100, [[100, 37], [2, 0], [99, 64]]),     # few pairs, many splits: one per query head
-])
-def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
-    """oscar_combine on seeded partials (not produced by the library) vs the oracle merge.
-
-    Each (sequence, KV head) pair declares how many INT2 slots it filled (the plan's nvalid);
-    slots past that hold NaN outputs, a large m and an l of 7 or NaN, and must not be read.
-    The window slots that follow are all merged, some of them empty."""
-    B, hq, hkv = 3, 8, 2
+def _combine_and_check(B, hq, hkv, max_splits, valid, nvalid, seed):
+    """Seeded partials in a fresh workspace (stale INT2 slots past each pair's nvalid hold NaN
+    outputs, a large m and an l of 7 or NaN), oscar_combine, and the oracle merge of the slots
+    each (sequence, query head) uses, rotated by R_V^T."""
     nslots = max_splits + ops.WINDOW_SLOTS
     G = hq // hkv
-    valid = np.ones((B, nslots), bool)
-    valid[0, 2] = False
-    valid[0, 3:max_splits:7] = False
-    valid[0, max_splits + 1] = False         # an empty window part between two full ones
-    valid[0, max_splits + 5:] = False        # window parts the launch did not use
-    valid[1, 1:] = False
-    valid[2, :] = False                      # a row with no positions at all
-    m, l, o = W.synthetic_partials(42, B, hq, nslots, valid)
-    nvalid = np.array(nvalid_rows, np.int32)       # [B][hkv]
+    m, l, o = W.synthetic_partials(seed, B, hq, nslots, valid)
     for b in range(B):
         for j in range(hq):
             stale = np.arange(nvalid[b, j // G], max_splits)
@@ -279,7 +264,7 @@ def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
     ws[qb + ob:qb + ob + ml.nbytes] = ml.reshape(-1).view(np.uint8)
     # plan region: 4 header words, pstart/npg/pglo [B] each, then nvalid [B][hkv]
     nv_off = qb + ob + ml.nbytes + 4 * (4 + 3 * B)
-    ws[nv_off:nv_off + nvalid.nbytes] = nvalid.reshape(-1).view(np.uint8)
+    ws[nv_off:nv_off + nvalid.nbytes] = nvalid.astype(np.int32).reshape(-1).view(np.uint8)
     dws = torch.from_numpy(ws).cuda()
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
@@ -294,8 +279,58 @@ def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
                 continue
             o_ref, lse_ref = O.merge_partials(m[b, j, used], l[b, j, used], o[b, j, used])
             o_ref = o_ref @ rot_v[j // G].astype(np.float64).T
-            assert np.abs(out[b, j] - o_ref).max() <= 1e-5 * max(1, np.abs(o_ref).max())
-            assert abs(lse[b, j] - lse_ref) <= 1e-5 * max(1, abs(lse_ref))
+            assert np.abs(out[b, j] - o_ref).max() <= 1e-5 * max(1, np.abs(o_ref).max()), (b, j)
+            assert abs(lse[b, j] - lse_ref) <= 1e-5 * max(1, abs(lse_ref)), (b, j)
+
+
+@pytest.mark.parametrize("max_splits,nvalid_rows", [
+    (5, [[5, 3], [2, 0], [4, 5]]),            # one workgroup per KV head
+    (100, [[100, 37], [2, 0], [99, 64]]),     # few pairs, many splits: one per query head
+])
+def test_combine_with_synthetic_partials(max_splits, nvalid_rows):
+    """oscar_combine on seeded partials (not produced by the library) vs the oracle merge.
+
+    Each (sequence, KV head) pair declares how many INT2 slots it filled (the plan's nvalid);
+    slots past that hold NaN outputs, a large m and an l of 7 or NaN, and must not be read.
+    The window slots that follow are all merged, some of them empty."""
+    B, hq, hkv = 3, 8, 2
+    nslots = max_splits + ops.WINDOW_SLOTS
+    valid = np.ones((B, nslots), bool)
+    valid[0, 2] = False
+    valid[0, 3:max_splits:7] = False
+    valid[0, max_splits + 1] = False         # an empty window part between two full ones
+    valid[0, max_splits + 5:] = False        # window parts the launch did not use
+    valid[1, 1:] = False
+    valid[2, :] = False                      # a row with no positions at all
+    _combine_and_check(B, hq, hkv, max_splits, valid, np.array(nvalid_rows, np.int32), 42)
+
+
+# (batch, query heads, KV heads, max_splits): the per-KV-head form for every group size with a
+# last workgroup of fewer than 8 / G sequences, with more slots than its lanes hold (past 128),
+# and the per-query-head form with more slots than its 1024 threads (past 1024).
+COMBINE_FORMS = {
+    "kv_g1": (3, 2, 2, 20),
+    "kv_g2": (5, 4, 2, 20),
+    "kv_g8": (3, 16, 2, 20),
+    "kv_g4_200_slots": (16, 32, 8, 200),
+    "head_g1_1100_slots": (1, 2, 2, 1100),
+}
+
+
+@pytest.mark.parametrize("name", list(COMBINE_FORMS))
+def test_combine_forms(name):
+    """oscar_combine against the oracle merge in each of its launch forms and slot-count
+    regimes: seeded nvalid per (sequence, KV head) (including 0 and max_splits), ~10% of the
+    used slots empty, a random subset of the window slots used."""
+    B, hq, hkv, max_splits = COMBINE_FORMS[name]
+    rng = np.random.default_rng(7)
+    nslots = max_splits + ops.WINDOW_SLOTS
+    valid = rng.random((B, nslots)) > 0.1
+    nvalid = rng.integers(0, max_splits + 1, (B, hkv)).astype(np.int32)
+    nvalid.reshape(-1)[0] = max_splits
+    if nvalid.size > 1:
+        nvalid.reshape(-1)[1] = 0
+    _combine_and_check(B, hq, hkv, max_splits, valid, nvalid, 43)
 
 
 @pytest.mark.parametrize("name,over,split_pages",
