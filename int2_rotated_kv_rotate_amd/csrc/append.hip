@@ -800,13 +800,35 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
 
 constexpr double kHadScale = 0x1.6a09e667f3bcdp-4;   // the double nearest to 2^-3.5 (sqrt(2)/16)
 
-// One cross-lane FWHT stage h = 2M on the lane's two values.
+// One cross-lane FWHT stage h = 2M on the lane's two values: the lower lane of a pair (bit M
+// clear) takes lower + upper, the upper lane lower - upper (the negation is a sign flip, exact).
+// M = 16, 32: one lane swap per dword gives the lower lane's value first on both lanes.
+__device__ __forceinline__ double with_sign(double x, uint32_t sign) {
+  uint64_t u = __builtin_bit_cast(uint64_t, x);
+  u ^= (uint64_t)sign << 32;
+  return __builtin_bit_cast(double, u);
+}
 template <int M>
 __device__ __forceinline__ void fwht_stage(double& a, double& b, int lane) {
-  const double pa = lane_xor_f64<M>(a), pb = lane_xor_f64<M>(b);
-  const bool upper = (lane & M) != 0;   // lower: a + partner; upper: partner - a
-  a = pa + (upper ? -a : a);
-  b = pb + (upper ? -b : b);
+  const uint32_t sign = (lane & M) ? 0x80000000u : 0u;
+  if constexpr (M == 16 || M == 32) {
+    auto lower_upper = [&](double x, double& lo_v, double& up_v) {
+      const uint64_t u = __builtin_bit_cast(uint64_t, x);
+      const LanePair pl = M == 16 ? pair16((uint32_t)u) : pair32((uint32_t)u);
+      const LanePair ph = M == 16 ? pair16((uint32_t)(u >> 32)) : pair32((uint32_t)(u >> 32));
+      lo_v = __builtin_bit_cast(double, ((uint64_t)ph.a << 32) | pl.a);
+      up_v = __builtin_bit_cast(double, ((uint64_t)ph.b << 32) | pl.b);
+    };
+    double la, ua, lb, ub;
+    lower_upper(a, la, ua);
+    lower_upper(b, lb, ub);
+    a = la + with_sign(ua, sign);
+    b = lb + with_sign(ub, sign);
+  } else {
+    const double pa = lane_xor_f64<M>(a), pb = lane_xor_f64<M>(b);
+    a = pa + with_sign(a, sign);   // lower: a + partner; upper: partner - a
+    b = pb + with_sign(b, sign);
+  }
 }
 constexpr int kHadWaves = 4;
 constexpr int kHadBatch = 8;
@@ -849,14 +871,11 @@ __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kerne
   for (int nb = n0; nb < n1; nb += kHadBatch) {
 #pragma unroll
     for (int u = 0; u < kHadBatch; ++u) nxt[u] = nb + kHadBatch + u < n1 ? load_row(nb + kHadBatch + u) : 0u;
-#pragma unroll 1
+#pragma unroll
     for (int u = 0; u < kHadBatch; ++u) {
       const int n = nb + u;
       if (n >= n1) break;
-      uint32_t xw = 0u;
-#pragma unroll
-      for (int k = 0; k < kHadBatch; ++k)
-        if (k == u) xw = cur[k];
+      const uint32_t xw = cur[u];
       if (n >= next_first) {   // the row starts a later sequence (rows are consecutive)
         seq = advance_seq(new_offsets, batch, seq + 1, n);
         first = new_offsets[seq];
@@ -944,10 +963,8 @@ __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kerne
           uint32_t v0 = c0 << (2 * (lane >> 3)), v1 = c1 << (2 * (lane >> 3));
           v0 |= lane_xor<8>(v0);
           v1 |= lane_xor<8>(v1);
-          v0 |= lane_xor<16>(v0);
-          v1 |= lane_xor<16>(v1);
-          v0 |= lane_xor<32>(v0);
-          v1 |= lane_xor<32>(v1);
+          v0 = or32(or16(v0));
+          v1 = or32(or16(v1));
           if (lane < 8) {
             uint8_t* base = pages + info.rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
             *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + 2 * lane)) = (uint16_t)v0;
