@@ -792,46 +792,39 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
 // the double nearest to 1/sqrt(128) and rounded to fp32.  896 additions per row instead of
 // 16,384 multiply-adds, so no matrix and no certification.
 //
-// One wavefront per row at a time: lane l holds channels 2l and 2l + 1; stage h = 1 is inside
-// the lane and stage h = 2m pairs lane l with lane l ^ m.  Each wave takes a contiguous range
-// of rows (the row's sequence, page and slot advance incrementally, the next page id is read
-// ahead) and loads the next kHadBatch rows while it computes the current ones.  Group g
-// (channels 32g .. 32g + 31) is lanes 16g .. 16g + 15.
+// Sixteen lanes per row, four rows per wavefront at a time: row slot q = lane / 16, lane
+// l = lane % 16 of the slot.  Layout A, lane l holding channels 8l .. 8l + 7, keeps stages
+// h = 1, 2, 4 inside the lane; an LDS transpose gives layout B, lane l holding channels
+// l + 16e (e = 0..7), where h = 16, 32, 64 are inside the lane and h = 8 pairs lane l with lane
+// l ^ 8 (a DPP row rotation).  The fp32 results go back to layout A through LDS, where the
+// four lanes 4g .. 4g + 3 hold quantisation group g.  Each row slot takes a contiguous quarter
+// of the wavefront's rows (sequence, page and slot advanced incrementally, the next page id
+// read ahead), and the next kHadAhead rows of every slot are loaded while the current ones are
+// computed.
 
 constexpr double kHadScale = 0x1.6a09e667f3bcdp-4;   // the double nearest to 2^-3.5 (sqrt(2)/16)
+constexpr int kHadWaves = 4;
+constexpr int kHadAhead = 4;
+constexpr int kHadStrideD = kHeadDim + 2;   // doubles per row slot in the transpose buffer
+constexpr int kHadStrideF = kHeadDim + 4;   // floats per row slot
 
-// One cross-lane FWHT stage h = 2M on the lane's two values: the lower lane of a pair (bit M
-// clear) takes lower + upper, the upper lane lower - upper (the negation is a sign flip, exact).
-// M = 16, 32: one lane swap per dword gives the lower lane's value first on both lanes.
+struct HadShared {
+  double d[kHadWaves][4][kHadStrideD];      // layout A -> B (fp64)
+  float f[kHadWaves][4][kHadStrideF];       // layout B -> A (fp32 results)
+};
+
+// x with its sign flipped where sign has bit 31 set (exact).
 __device__ __forceinline__ double with_sign(double x, uint32_t sign) {
   uint64_t u = __builtin_bit_cast(uint64_t, x);
   u ^= (uint64_t)sign << 32;
   return __builtin_bit_cast(double, u);
 }
-template <int M>
-__device__ __forceinline__ void fwht_stage(double& a, double& b, int lane) {
-  const uint32_t sign = (lane & M) ? 0x80000000u : 0u;
-  if constexpr (M == 16 || M == 32) {
-    auto lower_upper = [&](double x, double& lo_v, double& up_v) {
-      const uint64_t u = __builtin_bit_cast(uint64_t, x);
-      const LanePair pl = M == 16 ? pair16((uint32_t)u) : pair32((uint32_t)u);
-      const LanePair ph = M == 16 ? pair16((uint32_t)(u >> 32)) : pair32((uint32_t)(u >> 32));
-      lo_v = __builtin_bit_cast(double, ((uint64_t)ph.a << 32) | pl.a);
-      up_v = __builtin_bit_cast(double, ((uint64_t)ph.b << 32) | pl.b);
-    };
-    double la, ua, lb, ub;
-    lower_upper(a, la, ua);
-    lower_upper(b, lb, ub);
-    a = la + with_sign(ua, sign);
-    b = lb + with_sign(ub, sign);
-  } else {
-    const double pa = lane_xor_f64<M>(a), pb = lane_xor_f64<M>(b);
-    a = pa + with_sign(a, sign);   // lower: a + partner; upper: partner - a
-    b = pb + with_sign(b, sign);
-  }
+// In-lane FWHT pair: (a, b) -> (a + b, a - b).
+__device__ __forceinline__ void fwht_pair(double& a, double& b) {
+  const double s = a + b, d = a - b;
+  a = s;
+  b = d;
 }
-constexpr int kHadWaves = 4;
-constexpr int kHadBatch = 8;
 
 __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kernel(
     CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
@@ -841,143 +834,205 @@ __global__ __launch_bounds__(64 * kHadWaves) void rotate_quantize_hadamard_kerne
     const int8_t* __restrict__ signs_k, const int8_t* __restrict__ signs_v, float clip_k,
     float clip_v) {
 #pragma clang fp contract(off)
+  __shared__ HadShared sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4, l = lane & 15;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
   const uint16_t* src = is_v ? v_new : k_new;
   const int8_t* sg = is_v ? signs_v : signs_k;
   const float clip = is_v ? clip_v : clip_k;
-  const bool neg0 = sg != nullptr && sg[h * kHeadDim + 2 * lane] < 0;
-  const bool neg1 = sg != nullptr && sg[h * kHeadDim + 2 * lane + 1] < 0;
+  uint32_t neg = 0;  // bit e: channel 8l + e is negated
+  if (sg != nullptr) {
+    const uint2 s8 = *reinterpret_cast<const uint2*>(sg + h * kHeadDim + 8 * l);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t byte = ((e < 4 ? s8.x : s8.y) >> (8 * (e & 3))) & 0xFFu;
+      if (byte & 0x80u) neg |= 1u << e;
+    }
+  }
   const int nwaves = gridDim.x * kHadWaves;
   const int per = (total_new + nwaves - 1) / nwaves;
-  const int n0 = min(total_new, (int)(blockIdx.x * kHadWaves + wave) * per);
-  const int n1 = min(total_new, n0 + per);
-  if (n0 >= n1) return;
-  const int gi = lane >> 4;
+  const int w0 = min(total_new, (int)(blockIdx.x * kHadWaves + wave) * per);
+  const int w1 = min(total_new, w0 + per);
+  if (w0 >= w1) return;
+  // row slot q: rows [n0, n1), quarter q of [w0, w1)
+  const int qper = (w1 - w0 + 3) / 4;
+  const int n0 = min(w1, w0 + q * qper), n1 = min(w1, n0 + qper);
+  const int gi = l >> 2;
+  double* bd = sm.d[wave][q];
+  float* bf = sm.f[wave][q];
 
-  auto load_row = [&](int n) -> uint32_t {
-    return *reinterpret_cast<const uint32_t*>(src + ((size_t)n * g.hkv + h) * kHeadDim + 2 * lane);
+  // Loads are unconditional: a row past the slot's end (or of an empty slot) loads row w0,
+  // which is never stored.
+  auto load_row = [&](int n) -> uint4 {
+    const int nn = n < n1 ? n : w0;
+    return *reinterpret_cast<const uint4*>(src + ((size_t)nn * g.hkv + h) * kHeadDim + 8 * l);
   };
-  int seq = row_to_seq(new_offsets, batch, n0);
-  int first = new_offsets[seq], next_first = new_offsets[seq + 1];
-  int sp = start_pos[seq];
-  int slot = slot_ids ? slot_ids[seq] : seq;
+  int seq = 0, first = 0, next_first = 0, sp = 0, slot = 0;
+  if (n0 < n1) {
+    seq = row_to_seq(new_offsets, batch, n0);
+    first = new_offsets[seq];
+    next_first = new_offsets[seq + 1];
+    sp = start_pos[seq];
+    slot = slot_ids ? slot_ids[seq] : seq;
+  }
   int lp_cached = -1, page = -1, page_ahead = -1;
-  uint32_t cur[kHadBatch], nxt[kHadBatch];
+  uint4 cur[kHadAhead], nxt[kHadAhead];
 #pragma unroll
-  for (int u = 0; u < kHadBatch; ++u) cur[u] = n0 + u < n1 ? load_row(n0 + u) : 0u;
-  for (int nb = n0; nb < n1; nb += kHadBatch) {
+  for (int u = 0; u < kHadAhead; ++u) cur[u] = load_row(n0 + u);
+  for (int k = 0; k < qper; k += kHadAhead) {
 #pragma unroll
-    for (int u = 0; u < kHadBatch; ++u) nxt[u] = nb + kHadBatch + u < n1 ? load_row(nb + kHadBatch + u) : 0u;
+    for (int u = 0; u < kHadAhead; ++u) nxt[u] = load_row(n0 + k + kHadAhead + u);
 #pragma unroll
-    for (int u = 0; u < kHadBatch; ++u) {
-      const int n = nb + u;
-      if (n >= n1) break;
-      const uint32_t xw = cur[u];
-      if (n >= next_first) {   // the row starts a later sequence (rows are consecutive)
-        seq = advance_seq(new_offsets, batch, seq + 1, n);
-        first = new_offsets[seq];
-        next_first = new_offsets[seq + 1];
-        sp = start_pos[seq];
-        slot = slot_ids ? slot_ids[seq] : seq;
-        lp_cached = -1;
-        page_ahead = -1;
+    for (int u = 0; u < kHadAhead; ++u) {
+      const int n = n0 + k + u;
+      const bool act = n < n1;  // uniform over the row slot
+      // fp64 transform of the signed row; every lane computes (an inactive slot on row w0)
+      const uint32_t xs[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+      double v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double x = (double)((e & 1) ? bf16_hi(xs[e >> 1]) : bf16_lo(xs[e >> 1]));
+        v[e] = ((neg >> e) & 1u) ? -x : x;
       }
-      // fp64 transform of the signed row
-      double a = (double)bf16_lo(xw), b = (double)bf16_hi(xw);
-      if (neg0) a = -a;
-      if (neg1) b = -b;
+      // h = 1, 2, 4 in layout A
+      fwht_pair(v[0], v[1]); fwht_pair(v[2], v[3]); fwht_pair(v[4], v[5]); fwht_pair(v[6], v[7]);
+      fwht_pair(v[0], v[2]); fwht_pair(v[1], v[3]); fwht_pair(v[4], v[6]); fwht_pair(v[5], v[7]);
+      fwht_pair(v[0], v[4]); fwht_pair(v[1], v[5]); fwht_pair(v[2], v[6]); fwht_pair(v[3], v[7]);
+      // to layout B
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<double2*>(bd + 8 * l + 2 * j) = make_double2(v[2 * j], v[2 * j + 1]);
+      wave_lds_sync();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = bd[l + 16 * e];
+      wave_lds_sync();
+      // h = 8: the lower lane of (l, l ^ 8) takes lower + upper, the upper lower - upper
+      const uint32_t sign8 = (l & 8) ? 0x80000000u : 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = lane_xor_f64<8>(v[e]) + with_sign(v[e], sign8);
+      // h = 16, 32, 64 in layout B (channel l + 16e)
+      fwht_pair(v[0], v[1]); fwht_pair(v[2], v[3]); fwht_pair(v[4], v[5]); fwht_pair(v[6], v[7]);
+      fwht_pair(v[0], v[2]); fwht_pair(v[1], v[3]); fwht_pair(v[4], v[6]); fwht_pair(v[5], v[7]);
+      fwht_pair(v[0], v[4]); fwht_pair(v[1], v[5]); fwht_pair(v[2], v[6]); fwht_pair(v[3], v[7]);
+      // scale, round to fp32, back to layout A
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bf[l + 16 * e] = (float)(v[e] * kHadScale);
+      wave_lds_sync();
+      float y[8];
       {
-        const double s0 = a + b, d0 = a - b;
-        a = s0;
-        b = d0;
+        const float4 y0 = *reinterpret_cast<const float4*>(bf + 8 * l);
+        const float4 y1 = *reinterpret_cast<const float4*>(bf + 8 * l + 4);
+        y[0] = y0.x; y[1] = y0.y; y[2] = y0.z; y[3] = y0.w;
+        y[4] = y1.x; y[5] = y1.y; y[6] = y1.z; y[7] = y1.w;
       }
-      fwht_stage<1>(a, b, lane);
-      fwht_stage<2>(a, b, lane);
-      fwht_stage<4>(a, b, lane);
-      fwht_stage<8>(a, b, lane);
-      fwht_stage<16>(a, b, lane);
-      fwht_stage<32>(a, b, lane);
-      const float y0 = (float)(a * kHadScale), y1 = (float)(b * kHadScale);
+      wave_lds_sync();
 
-      // group extremes over the 16 lanes of the group, scale/zero, codes
-      float mx = fmaxf(y0, y1), mn = fminf(y0, y1);
+      // group extremes over the group's 4 lanes, scale/zero, codes
+      float mx = y[0], mn = y[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) {
+        mx = fmaxf(mx, y[e]);
+        mn = fminf(mn, y[e]);
+      }
       mx = fmaxf(mx, lane_xor_f32<1>(mx));
       mn = fminf(mn, lane_xor_f32<1>(mn));
       mx = fmaxf(mx, lane_xor_f32<2>(mx));
       mn = fminf(mn, lane_xor_f32<2>(mn));
-      mx = fmaxf(mx, lane_xor_f32<4>(mx));
-      mn = fminf(mn, lane_xor_f32<4>(mn));
-      mx = fmaxf(mx, lane_xor_f32<8>(mx));
-      mn = fminf(mn, lane_xor_f32<8>(mn));
       _Float16 s16, z16;
       group_params(mx, mn, clip, s16, z16);
       const float sc = (float)s16, z = (float)z16;
-      const uint32_t c0 = (uint32_t)code_of(y0, sc, z), c1 = (uint32_t)code_of(y1, sc, z);
-
-      // placement
-      const int pos = sp + (n - first);
-      const int new_len = sp + (next_first - first);
-      const int lp = pos / kPage;
-      if (lp != lp_cached) {
-        page = (lp == lp_cached + 1 && lp_cached >= 0) ? page_ahead
-               : ((pos >= 0 && lp < g.max_pages) ? block_table[(size_t)seq * g.max_pages + lp] : -1);
-        lp_cached = lp;
-        page_ahead = (pos >= 0 && lp + 1 < g.max_pages) ? block_table[(size_t)seq * g.max_pages + lp + 1]
-                                                       : -1;
-      }
-      RowInfo info{-1, 0, -1};
-      if (pos >= 0 && page >= 0 && page < g.num_pages && lp < g.max_pages) {
-        info.rec = ((long long)page * g.hkv + h) * kRecord;
-        info.slot_in_page = pos % kPage;
-      }
-      int row = -1;
-      if (pos >= 0 && pos < g.num_sink) row = pos;
-      else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
-        row = g.num_sink + pos % g.window;
-      if (row >= 0 && sinkwin != nullptr && slot >= 0 && slot < g.num_slots)
-        info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
-                  (is_v ? kHeadDim : 0);
-
-      if (info.rec >= 0) {
-        if ((lane & 15) == 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
-        const int sl = info.slot_in_page;
-        if (!is_v) {
-          // K word d = lane / 8 (channels 16d .. 16d + 15); channel 2l + e sits at byte
-          // (l % 8) / 2, bits 2 * (2 * (l % 2) + e)
-          const int sh = 8 * ((lane & 7) >> 1) + 4 * (lane & 1);
-          uint32_t w = (c0 << sh) | (c1 << (sh + 2));
-          w |= lane_xor<1>(w);
+      uint32_t code[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) code[e] = (uint32_t)code_of(y[e], sc, z);
+      // code words: K word d = l / 2 (lanes 2d, 2d + 1; channel 16d + c at bits
+      // 8 (c / 4) + 2 (c % 4)); V halves r16 = 8 (l % 2) + e of the lanes of one parity, channel
+      // r16 + 16 nb at bits 2 nb (nb = l / 2), two halves per word
+      uint32_t kw = 0;
+      uint32_t hv[4];
+      if (!is_v) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kw |= code[e] << (8 * (e >> 2) + 2 * (e & 3));
+        kw <<= 16 * (l & 1);
+        kw |= lane_xor<1>(kw);
+      } else {
+        const int nb = l >> 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t w = (code[2 * j] << (2 * nb)) | (code[2 * j + 1] << (16 + 2 * nb));
           w |= lane_xor<2>(w);
           w |= lane_xor<4>(w);
-          if ((lane & 7) == 0) {
-            const int d = lane >> 3;
-            *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes + 8 * (16 * (d % 4) + sl) +
-                                         4 * (d / 4)) = w;
-          }
-        } else {
-          // V half of channel residue k = (2l + e) % 16 holds channel k + 16 nb at bits 2 nb,
-          // nb = l / 8: lanes l % 8 == k / 2 combine
-          uint32_t v0 = c0 << (2 * (lane >> 3)), v1 = c1 << (2 * (lane >> 3));
-          v0 |= lane_xor<8>(v0);
-          v1 |= lane_xor<8>(v1);
-          v0 = or32(or16(v0));
-          v1 = or32(or16(v1));
-          if (lane < 8) {
-            uint8_t* base = pages + info.rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
-            *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + 2 * lane)) = (uint16_t)v0;
-            *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + 2 * lane + 1)) = (uint16_t)v1;
-          }
+          w |= lane_xor<8>(w);
+          hv[j] = w;
         }
       }
-      if (info.sw >= 0)
-        *reinterpret_cast<uint32_t*>(sinkwin + info.sw + 2 * lane) =
-            (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+
+      // placement of the slot's row
+      RowInfo info{-1, 0, -1};
+      if (act) {
+        if (n >= next_first) {   // the row starts a later sequence (rows are consecutive)
+          seq = advance_seq(new_offsets, batch, seq + 1, n);
+          first = new_offsets[seq];
+          next_first = new_offsets[seq + 1];
+          sp = start_pos[seq];
+          slot = slot_ids ? slot_ids[seq] : seq;
+          lp_cached = -1;
+          page_ahead = -1;
+        }
+        const int pos = sp + (n - first);
+        const int new_len = sp + (next_first - first);
+        const int lp = pos / kPage;
+        if (lp != lp_cached) {
+          page = (lp == lp_cached + 1 && lp_cached >= 0) ? page_ahead
+                 : ((pos >= 0 && lp < g.max_pages) ? block_table[(size_t)seq * g.max_pages + lp] : -1);
+          lp_cached = lp;
+          page_ahead = (pos >= 0 && lp + 1 < g.max_pages) ? block_table[(size_t)seq * g.max_pages + lp + 1]
+                                                         : -1;
+        }
+        if (pos >= 0 && page >= 0 && page < g.num_pages && lp < g.max_pages) {
+          info.rec = ((long long)page * g.hkv + h) * kRecord;
+          info.slot_in_page = pos % kPage;
+        }
+        int row = -1;
+        if (pos >= 0 && pos < g.num_sink) row = pos;
+        else if (g.window > 0 && pos >= g.num_sink && pos >= new_len - g.window)
+          row = g.num_sink + pos % g.window;
+        if (row >= 0 && sinkwin != nullptr && slot >= 0 && slot < g.num_slots)
+          info.sw = (((long long)slot * g.hkv + h) * (g.num_sink + g.window) + row) * 2 * kHeadDim +
+                    (is_v ? kHeadDim : 0);
+      }
+      if (info.rec >= 0) {
+        const int sl = info.slot_in_page;
+        if ((l & 3) == 0) store_meta(pages, info, is_v, gi, meta_word(s16, z16));
+        if (!is_v) {
+          if ((l & 1) == 0) {
+            const int d = l >> 1;
+            *reinterpret_cast<uint32_t*>(pages + info.rec + kKCodes + 8 * (16 * (d % 4) + sl) +
+                                         4 * (d / 4)) = kw;
+          }
+        } else {
+          // lane l stores half r16 = 8 (l % 2) + l / 2
+          const int idx = l >> 1, jj = idx >> 1;
+          const uint32_t w = jj == 0 ? hv[0] : jj == 1 ? hv[1] : jj == 2 ? hv[2] : hv[3];
+          const int r16 = 8 * (l & 1) + idx;
+          uint8_t* base = pages + info.rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
+          *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + r16)) =
+              (uint16_t)(w >> (16 * (idx & 1)));
+        }
+      }
+      if (info.sw >= 0) {
+        uint4 o;
+        o.x = (uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16);
+        o.z = (uint32_t)f32_to_bf16_rne(y[4]) | ((uint32_t)f32_to_bf16_rne(y[5]) << 16);
+        o.w = (uint32_t)f32_to_bf16_rne(y[6]) | ((uint32_t)f32_to_bf16_rne(y[7]) << 16);
+        *reinterpret_cast<uint4*>(sinkwin + info.sw + 8 * l) = o;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kHadBatch; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < kHadAhead; ++u) cur[u] = nxt[u];
   }
 }
 
