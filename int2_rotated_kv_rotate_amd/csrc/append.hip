@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
 
 constexpr double kHadScale = 0x1.6a09e667f3bcdp-4;   // the double nearest to 2^-3.5 (sqrt(2)/16)
 constexpr int kHadWaves = 4;
-constexpr int kHadAhead = 4;
+constexpr int kHadAhead = 2;
 constexpr int kHadStrideD = kHeadDim + 2;   // doubles per row slot in the transpose buffer
 constexpr int kHadStrideF = kHeadDim + 4;   // floats per row slot
 
@@ -1047,8 +1047,8 @@ hipError_t launch_append_hadamard(const CacheGeom& g, uint8_t* pages, uint16_t* 
   if (batch == 0 || total_new == 0) return hipSuccess;
   int cus = current_device_cus();
   if (cus <= 0) cus = 256;
-  // about 8 waves per SIMD over the 2 * Hkv (head, K|V) pairs; at least one row per wave
-  const int want = max(1, 32 * cus / (2 * g.hkv * kHadWaves));
+  // about 16 waves per SIMD over the 2 * Hkv (head, K|V) pairs; at least one row per wave
+  const int want = max(1, 64 * cus / (2 * g.hkv * kHadWaves));
   const int blocks = max(1, min(want, (total_new + kHadWaves - 1) / kHadWaves));
   hipLaunchKernelGGL(rotate_quantize_hadamard_kernel, dim3(blocks, g.hkv, 2), dim3(64 * kHadWaves),
                      0, stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
