@@ -280,10 +280,10 @@ def test_chunked_appends_with_window_rows():
         assert np.array_equal(c.sinkwin.cpu().numpy().view(np.uint16), oc.sinkwin), f"method {m}"
 
 
-def test_full_prefill_shape():
-    """64 sequences x 2048 new tokens at positions [L - 2048, L), L in [16384, 32768]: the
-    prefill append the benchmark times.  Rows follow the workload recipe (N(0,1) + per-channel
-    N(0,2) key offsets, x15 outlier key channels), drawn on the GPU from a seeded generator."""
+def _full_prefill_inputs():
+    """The benchmark's prefill: 64 sequences x 2048 new tokens at positions [L - 2048, L), L in
+    [16384, 32768].  Rows follow the workload recipe (N(0,1) + per-channel N(0,2) key offsets,
+    x15 outlier key channels), drawn on the GPU from a seeded generator."""
     w = W.WORKLOADS["qwen3_8b_b64"]
     p = H.make_problem(w)
     n_new = w.prefill_new
@@ -301,6 +301,13 @@ def test_full_prefill_shape():
     v16 = v.to(torch.bfloat16).view(torch.int16).contiguous()
     offs = torch.arange(0, total + 1, n_new, dtype=torch.int32, device="cuda")
     start = torch.from_numpy((p.lens - n_new).astype(np.int32)).cuda()
+    return w, p, n_new, total, k16, v16, offs, start
+
+
+def test_full_prefill_shape():
+    """The full prefill the benchmark times (see _full_prefill_inputs): both append methods byte
+    for byte, and sampled (sequence, KV head) pairs against the oracle."""
+    w, p, n_new, total, k16, v16, offs, start = _full_prefill_inputs()
     res = {}
     for m in (ops.APPEND_VECTOR, ops.APPEND_MATRIX):
         c = H.GpuCache(p, fill=SENTINEL)
@@ -335,3 +342,31 @@ def test_full_prefill_shape():
              f"{nd_o} bytes differ from the oracle")
         assert nd_o == 0
         assert np.array_equal(sm[b, h].cpu().numpy().view(np.uint16), oc.sinkwin[b, 0])
+
+
+def test_full_prefill_shape_hadamard():
+    """The Hadamard append at the full prefill shape, where each row slot of a wavefront takes
+    many consecutive rows (sequence and page changes inside a slot's range): sampled (sequence,
+    KV head) pairs against the oracle, every record and sink/window row byte for byte."""
+    w, p, n_new, total, k16, v16, offs, start = _full_prefill_inputs()
+    sk, sv = OF.hadamard_signs(70, w.num_kv_heads), OF.hadamard_signs(71, w.num_kv_heads)
+    c = H.GpuCache(p, fill=SENTINEL)
+    ops.rotate_quantize_append_hadamard(c.layout, c.pages, c.sinkwin, c.table, c.slots, k16, v16,
+                                        offs, start, torch.from_numpy(sk).cuda(),
+                                        torch.from_numpy(sv).cuda(), w.clip, w.clip)
+    torch.cuda.synchronize()
+    offs_h = offs.cpu().numpy()
+    for b, h in ((0, 1), (37, 6), (63, 0)):
+        L = int(p.lens[b])
+        kb = k16[offs_h[b]:offs_h[b + 1], h:h + 1].cpu().numpy().view(np.uint16)
+        vb = v16[offs_h[b]:offs_h[b + 1], h:h + 1].cpu().numpy().view(np.uint16)
+        oc = O.Cache(p.num_pages, 1, w.batch, w.num_sink, w.window, fill=SENTINEL)
+        oc.append(p.table[b], b, L - n_new, kb, vb, None, None, w.clip, w.clip,
+                  hadamard_signs=(sk[h:h + 1], sv[h:h + 1]))
+        pg = p.table[b, (L - n_new) // 16:(L + 15) // 16]
+        gpu_rec = c.pages[torch.from_numpy(pg.astype(np.int64)).cuda(), h].cpu().numpy()
+        nd_o = int((gpu_rec != oc.pages[pg, 0]).sum())
+        _log(f"[append] full prefill (Hadamard), sequence {b} KV head {h}: {len(pg)} records, "
+             f"{nd_o} bytes differ from the oracle")
+        assert nd_o == 0
+        assert np.array_equal(c.sinkwin[b, h].cpu().numpy().view(np.uint16), oc.sinkwin[b, 0])
