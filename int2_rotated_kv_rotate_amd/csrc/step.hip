@@ -167,7 +167,10 @@ __device__ __forceinline__ void prep_q_block(
 
   // q' partial sums over this thread's 16 input rows (ascending), one query head at a time,
   // its 16 q values read as four 16-byte loads; then reduce the 8 blocks in order.
-  for (int j = 0; j < nr; ++j) {
+  // (rows unrolled to the most a workgroup takes, so their independent chains interleave)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= nr) break;
     const float4* qp = reinterpret_cast<const float4*>(&s_q[j][16 * ib]);
     const float4 qv[4] = {qp[0], qp[1], qp[2], qp[3]};
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -197,8 +200,16 @@ __device__ __forceinline__ void prep_q_block(
     const int b = b0 + j / hpw;   // the same for the whole wave
     if (b >= ws.batch) continue;
     const float v0 = s_qr[j][2 * lane], v1 = s_qr[j][2 * lane + 1];
+    // max |q'| over the wave: DPP within each row of 16 lanes, then the four rows' values
     float a = fmaxf(fabsf(v0), fabsf(v1));
-    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    a = fmaxf(a, lane_xor_f32<1>(a));
+    a = fmaxf(a, lane_xor_f32<2>(a));
+    a = fmaxf(a, lane_xor_f32<4>(a));
+    a = fmaxf(a, lane_xor_f32<8>(a));
+    a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16))),
+              fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48))));
     const float qsc = a / 127.0f;
     char* blk = ws.qblock(b, hq, h * G + j0 + j % hpw);
     int esum = 0;  // sum of the encoded values 254*hi + lo over this lane's two channels
@@ -220,7 +231,10 @@ __device__ __forceinline__ void prep_q_block(
     // The zero-point term of a logit uses these sums of the encoded q' (exact integers), so
     // that a key's code and zero parts see the same query: z*sum(q') and s*q'.codes then
     // carry one encoding error that cancels as in q'.k, instead of two that do not.
-    for (int o = 8; o >= 1; o >>= 1) esum += __shfl_xor(esum, o);  // 16 lanes = 32 channels
+    esum += (int)lane_xor<1>((uint32_t)esum);   // the 16 lanes of a row = 32 channels
+    esum += (int)lane_xor<2>((uint32_t)esum);
+    esum += (int)lane_xor<4>((uint32_t)esum);
+    esum += (int)lane_xor<8>((uint32_t)esum);
     reinterpret_cast<float2*>(blk)[lane] = make_float2(v0, v1);
     if (lane == 0) *reinterpret_cast<float*>(blk + kQScOff) = qsc;
     if ((lane & 15) == 0) reinterpret_cast<float*>(blk + kQSumOff)[lane >> 4] = (float)esum;
