@@ -256,13 +256,25 @@ __device__ __forceinline__ int wave_scan(int x) {
   return x;
 }
 
+// The 16 values' codes of a lane: 2 bits each (INT2 records) or 4 (INT4 records), value v at
+// bits BITS * v.
+template <int BITS>
+struct CodeWord { using T = uint32_t; };
+template <>
+struct CodeWord<4> { using T = uint64_t; };
+
+// INT4 records (2560 bytes, the layout of the INT4 append): K codes [0, 1024), V codes
+// [1024, 2048), K (scale, zero) [2048, 2304), V [2304, 2560).
+constexpr int kRecord4 = 2560, kK4Codes = 0, kV4Codes = 1024, kK4Meta = 2048, kV4Meta = 2304;
+
 // Replace this wave's flagged values by the defined ones.  Bit v = 8 tb + 4 cb + i of fl: the
 // lane's value y[v], row 16 tb + m of the block, channel 16 cb + 4 kq + i of the group.  The
 // wave's flagged values are numbered lane first, then value index, and recomputed in rounds of
-// up to kMListCap.  RECODE: also replace their codes (bits 2v of cw) by the defined ones, with
-// the rows' scale sc and zero zz.
-template <bool RECODE>
-__device__ __forceinline__ void recompute_flagged(uint32_t fl, float (&y)[16], uint32_t& cw,
+// up to kMListCap.  RECODE: also replace their codes (bits BITS v of cw) by the defined ones,
+// with the rows' scale sc and zero zz.
+template <int BITS, bool RECODE>
+__device__ __forceinline__ void recompute_flagged(uint32_t fl, float (&y)[16],
+                                                  typename CodeWord<BITS>::T& cw,
                                                   const float sc[2], const float zz[2],
                                                   uint16_t* list, float* res,
                                                   const uint16_t* __restrict__ src, int hkv, int h,
@@ -311,8 +323,10 @@ __device__ __forceinline__ void recompute_flagged(uint32_t fl, float (&y)[16], u
         if (((fl >> v) & 1u) && p >= 0 && p < kMListCap) {
           y[v] = res[p];
           if (RECODE) {
-            const int code = code_of(y[v], v >> 3 ? sc[1] : sc[0], v >> 3 ? zz[1] : zz[0]);
-            cw = (cw & ~(3u << (2 * v))) | ((uint32_t)code << (2 * v));
+            using T = typename CodeWord<BITS>::T;
+            constexpr int kSteps = (1 << BITS) - 1;
+            const int code = code_of_t<kSteps>(y[v], v >> 3 ? sc[1] : sc[0], v >> 3 ? zz[1] : zz[0]);
+            cw = (cw & ~((T)kSteps << (BITS * v))) | ((T)code << (BITS * v));
           }
         }
       }
@@ -358,6 +372,8 @@ __device__ int advance_seq(const int32_t* __restrict__ off, int batch, int seq, 
   return lo;
 }
 
+// BITS = 2: INT2 records; BITS = 4: INT4 records (16 levels, the INT4 append's layout).
+template <int BITS>
 __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
     CacheGeom g, uint8_t* __restrict__ pages, uint16_t* __restrict__ sinkwin,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ slot_ids, int batch,
@@ -381,6 +397,9 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
   const bool centered = !is_v && k_mean != nullptr;
   const bool has_store = sinkwin != nullptr;
   const int m = lane & 15, kq = lane >> 4;
+  constexpr int kSteps = (1 << BITS) - 1;
+  constexpr int kRec = BITS == 2 ? kRecord : kRecord4;
+  using CW = typename CodeWord<BITS>::T;
 
   // Stage R^T: all 16 float4 loads of a thread first, then the transposed LDS stores.
   {
@@ -490,8 +509,8 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
   if (x0 < ntiles && x0 * kMBlock + tp < total_new) {
     const int n = x0 * kMBlock + tp;
     seq = row_to_seq(new_offsets, batch, n);
-    info_next = row_info(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store, n, h,
-                         is_v);
+    info_next = row_info_t<kRec>(g, block_table, slot_ids, batch, new_offsets, start_pos, has_store,
+                                 n, h, is_v);
   }
   load_x(x0);
   uint16_t* list = sm.list[gq];
@@ -592,7 +611,7 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
       const bool lo_end = (kq & 1) != 0;
       const float a = vt ? mx[1] : mx[0], b = vt ? mn[1] : mn[0], e = vt ? E[1] : E[0];
       _Float16 s16, z16;
-      group_params(lo_end ? a - e : a + e, lo_end ? b + e : b - e, clip, s16, z16);
+      group_params_t<kSteps>(lo_end ? a - e : a + e, lo_end ? b + e : b - e, clip, s16, z16);
       const uint32_t key = meta_word(s16, z16);
       const LanePair ends = pair16(key);                            // kq ^ 1: the other end
       const uint32_t diff = ends.a != ends.b ? 1u : 0u;
@@ -610,11 +629,11 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t cw = 0;   // 2-bit codes at bits 2v
+    CW cw = 0;   // codes at bits BITS v
     const bool redo = __ballot(fl != 0u) != 0;
     if (redo) {
       const float none[2] = {0.f, 0.f};
-      recompute_flagged<false>(fl, y, cw, none, none, list, res, src, g.hkv, h, n0, gq, sm.rt,
+      recompute_flagged<BITS, false>(fl, y, cw, none, none, list, res, src, g.hkv, h, n0, gq, sm.rt,
                                sm.cd, nrm_w, cng, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -637,7 +656,7 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
     {
       const int pt = kq & 1;
       _Float16 s16, z16;
-      group_params(pt ? mx[1] : mx[0], pt ? mn[1] : mn[0], clip, s16, z16);
+      group_params_t<kSteps>(pt ? mx[1] : mx[0], pt ? mn[1] : mn[0], clip, s16, z16);
       const uint32_t mw = meta_word(s16, z16);
       const float s = (float)s16;
       const float iv = s != 0.0f ? 1.0f / s : 0.0f;
@@ -654,16 +673,28 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
       zz[tb] = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta[tb] >> 16));
     }
     if (kq < 2) {   // lane kq stores row kq's scale/zero word of the group
-      if ((kq ? valid[1] : valid[0]) && own.rec >= 0) store_meta(pages, own, is_v, gq, kq ? meta[1] : meta[0]);
+      if ((kq ? valid[1] : valid[0]) && own.rec >= 0) {
+        if constexpr (BITS == 2) {
+          store_meta(pages, own, is_v, gq, kq ? meta[1] : meta[0]);
+        } else {
+          *reinterpret_cast<uint32_t*>(pages + own.rec + (is_v ? kV4Meta : kK4Meta) +
+                                       16 * own.slot_in_page + 4 * gq) = kq ? meta[1] : meta[0];
+        }
+      }
     }
     uint32_t fl2 = 0;   // values to recompute
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const float Eg = kErrScale * nrm[tb] * cng + kErrAbs +
                        (centered ? (cmax + 2.0f * fmaxf(fabsf(mx[tb]), fabsf(mn[tb]))) * 0x1p-22f : 0.0f);
-      // the code margin of the group, taken at its largest |y| (>= every |y| in it)
+      // the code margin of the group, taken at its largest |y| (>= every |y| in it).  The
+      // computed t carries three fp32 roundings (the difference, 1/s and the product) beyond the
+      // defined quotient's one: 4u |y - z| / s, with |y - z| <= gabs; with 4 levels the 2^-23
+      // term and the 2^-19 floor cover it (|t| that large needs gabs >> |y - z|), with 16 levels
+      // the relative term is 2^-22.
       const float gabs = fmaxf(fabsf(mx[tb]), fabsf(mn[tb])) + fabsf(zz[tb]);
-      const float mt = (Eg + (gabs + Eg) * 0x1p-23f) * inv[tb] * 1.01f + 0x1p-19f;
+      constexpr float kRel = BITS == 2 ? 0x1p-23f : 0x1p-22f;
+      const float mt = (Eg + (gabs + Eg) * kRel) * inv[tb] * 1.01f + 0x1p-19f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int v = 8 * tb + j;
@@ -674,8 +705,8 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
         const float tq = (yv - zz[tb]) * inv[tb];
         const float dist = fabsf(__builtin_amdgcn_fractf(tq) - 0.5f);
         const bool ok = dist > mt;
-        const int code = (int)fminf(fmaxf(__builtin_rintf(tq), 0.0f), 3.0f);
-        cw |= (uint32_t)code << (2 * v);
+        const int code = (int)fminf(fmaxf(__builtin_rintf(tq), 0.0f), (float)kSteps);
+        cw |= (CW)code << (BITS * v);
         fl2 |= (ok ? 0u : 1u) << v;
       }
       // BF16 copies of sink/window rows: certain when y -+ E round to the same bf16
@@ -690,7 +721,7 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     if (__ballot(fl2 != 0u) != 0)
-      recompute_flagged<true>(fl2, y, cw, sc, zz, list, res, src, g.hkv, h, n0, gq, sm.rt, sm.cd,
+      recompute_flagged<BITS, true>(fl2, y, cw, sc, zz, list, res, src, g.hkv, h, n0, gq, sm.rt, sm.cd,
                               nrm_w, cng, lane);
 
     load_x(nt);   // the successor's rows, in flight from here to the next block's matrix cores
@@ -698,7 +729,7 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
     if (look) {
       RowInfo nx{-1, 0, -1};
       if (pos >= 0 && page >= 0 && page < g.num_pages && pos / kPage < g.max_pages) {
-        nx.rec = ((long long)page * g.hkv + h) * kRecord;
+        nx.rec = ((long long)page * g.hkv + h) * kRec;
         nx.slot_in_page = pos % kPage;
       }
       const int new_len = sp + (next_first - first);
@@ -728,57 +759,110 @@ __global__ __launch_bounds__(kMThreads, 2) void rotate_quantize_prefill_kernel(
       }
     }
 
-    if (!is_v) {
-      // K word d = 2g + cb of row 16 tb + m: channel 4kq + i of the word at bits 8kq + 2i, so
-      // the four lanes of a row contribute a byte each; lane kq stores word cb = kq / 2 of its
-      // own row (tb = kq % 2)
-      uint32_t wsel = 0;
+    if constexpr (BITS == 2) {
+      if (!is_v) {
+        // K word d = 2g + cb of row 16 tb + m: channel 4kq + i of the word at bits 8kq + 2i, so
+        // the four lanes of a row contribute a byte each; lane kq stores word cb = kq / 2 of its
+        // own row (tb = kq % 2)
+        uint32_t wsel = 0;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            uint32_t w = ((cw >> (16 * tb + 8 * cb)) & 0xFFu) << (8 * kq);
+            w = or32(or16(w));
+            if (kq == 2 * cb + tb) wsel = w;
+          }
+        if (((kq & 1) ? valid[1] : valid[0]) && own.rec >= 0) {
+          const int d = 2 * gq + (kq >> 1);
+          *reinterpret_cast<uint32_t*>(pages + own.rec + kKCodes + 8 * (16 * (d % 4) + own.slot_in_page) +
+                                       4 * (d / 4)) = wsel;
+        }
+      } else {
+        // V: the group's code pairs of channel residues c16 = 4kq + i, to LDS, then each thread
+        // assembles two 16-bit halves of one row from the four groups' pairs
+        const int buf = k & 1;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          uint32_t wv = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t nib = ((cw >> (16 * tb + 2 * i)) & 3u) | (((cw >> (16 * tb + 8 + 2 * i)) & 3u) << 2);
+            wv |= nib << (8 * i);
+          }
+          sm.vn[buf][gq][16 * tb + m][kq] = wv;
+        }
+        __syncthreads();
+        const int tl = t >> 3, c2 = 2 * (t & 7);
+        // row tl's placement is held by lane (tl % 16, tl / 16) of every wave
+        const int srcl = (tl & 15) + 16 * (tl >> 4);
+        const uint32_t rlo = (uint32_t)__shfl((int)(uint32_t)own.rec, srcl);
+        const uint32_t rhi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)own.rec >> 32), srcl);
+        const int sl = __shfl(own.slot_in_page, srcl);
+        const long long rec = (long long)(((uint64_t)rhi << 32) | rlo);
+        if (n0 + tl < total_new && rec >= 0) {
+          uint32_t hw0 = 0, hw1 = 0;
+#pragma unroll
+          for (int gg = 0; gg < kMWaves; ++gg) {
+            const uint32_t wv = sm.vn[buf][gg][tl][c2 >> 2];
+            hw0 |= ((wv >> (8 * (c2 & 3))) & 0xFu) << (4 * gg);
+            hw1 |= ((wv >> (8 * ((c2 + 1) & 3))) & 0xFu) << (4 * gg);
+          }
+          uint8_t* base = pages + rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
+          *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + c2)) = (uint16_t)hw0;
+          *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + c2 + 1)) = (uint16_t)hw1;
+        }
+      }
+    } else if (!is_v) {
+      // INT4 K: channel 4kq + i of block cb goes to chunk 16 q + slot (q = 2 (g % 2) + cb), byte
+      // 8 (g / 2) + 4 (i / 2) + kq, nibble i % 2: the four lanes of a row contribute a byte of
+      // each of the two dwords; lane kq stores both dwords of (tb, cb) = (kq % 2, kq / 2) of its
+      // own row
+      uint2 wsel = {0u, 0u};
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-          uint32_t w = ((cw >> (16 * tb + 8 * cb)) & 0xFFu) << (8 * kq);
-          w = or32(or16(w));
-          if (kq == 2 * cb + tb) wsel = w;
+          const int vb = 8 * tb + 4 * cb;
+          uint32_t w0 = ((uint32_t)(cw >> (4 * vb)) & 0xFFu) << (8 * kq);
+          uint32_t w1 = ((uint32_t)(cw >> (4 * vb + 8)) & 0xFFu) << (8 * kq);
+          w0 = or32(or16(w0));
+          w1 = or32(or16(w1));
+          if (kq == 2 * cb + tb) wsel = make_uint2(w0, w1);
         }
       if (((kq & 1) ? valid[1] : valid[0]) && own.rec >= 0) {
-        const int d = 2 * gq + (kq >> 1);
-        *reinterpret_cast<uint32_t*>(pages + own.rec + kKCodes + 8 * (16 * (d % 4) + own.slot_in_page) +
-                                     4 * (d / 4)) = wsel;
+        const int q = 2 * (gq & 1) + (kq >> 1);
+        *reinterpret_cast<uint2*>(pages + own.rec + kK4Codes + 16 * (16 * q + own.slot_in_page) +
+                                  8 * (gq >> 1)) = wsel;
       }
     } else {
-      // V: the group's code pairs of channel residues c16 = 4kq + i, to LDS, then each thread
-      // assembles two 16-bit halves of one row from the four groups' pairs
-      const int buf = k & 1;
+      // INT4 V: channel 4kq + i of blocks cb = 0, 1 share a byte (cb in the nibble) of dword g in
+      // chunk 16 (slot / 4) + 4kq + i, byte 2 (u % 2) + u / 2 (u = slot % 4): each slot owns whole
+      // bytes, so no exchange between groups.  A lane stores its own row's bytes of its channels
+      // and, from lane kq ^ 1 (which holds the other row), those of that lane's channels.
+      uint32_t vb[2];   // [tb]: byte i of channel 4kq + i at bits 8i
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        uint32_t wv = 0;
+        uint32_t b = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t nib = ((cw >> (16 * tb + 2 * i)) & 3u) | (((cw >> (16 * tb + 8 + 2 * i)) & 3u) << 2);
-          wv |= nib << (8 * i);
+          const uint32_t lo = (uint32_t)(cw >> (4 * (8 * tb + i))) & 0xFu;
+          const uint32_t hi = (uint32_t)(cw >> (4 * (8 * tb + 4 + i))) & 0xFu;
+          b |= (lo | (hi << 4)) << (8 * i);
         }
-        sm.vn[buf][gq][16 * tb + m][kq] = wv;
+        vb[tb] = b;
       }
-      __syncthreads();
-      const int tl = t >> 3, c2 = 2 * (t & 7);
-      // row tl's placement is held by lane (tl % 16, tl / 16) of every wave
-      const int srcl = (tl & 15) + 16 * (tl >> 4);
-      const uint32_t rlo = (uint32_t)__shfl((int)(uint32_t)own.rec, srcl);
-      const uint32_t rhi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)own.rec >> 32), srcl);
-      const int sl = __shfl(own.slot_in_page, srcl);
-      const long long rec = (long long)(((uint64_t)rhi << 32) | rlo);
-      if (n0 + tl < total_new && rec >= 0) {
-        uint32_t hw0 = 0, hw1 = 0;
+      const uint32_t mine = (kq & 1) ? vb[1] : vb[0];
+      const uint32_t theirs = partner16((kq & 1) ? vb[0] : vb[1], lane);
+      if (((kq & 1) ? valid[1] : valid[0]) && own.rec >= 0) {
+        const int sl = own.slot_in_page, u = sl & 3;
+        uint8_t* base = pages + own.rec + kV4Codes + 16 * (16 * (sl >> 2)) + 4 * gq + 2 * (u & 1) +
+                        (u >> 1);
 #pragma unroll
-        for (int gg = 0; gg < kMWaves; ++gg) {
-          const uint32_t wv = sm.vn[buf][gg][tl][c2 >> 2];
-          hw0 |= ((wv >> (8 * (c2 & 3))) & 0xFu) << (4 * gg);
-          hw1 |= ((wv >> (8 * ((c2 + 1) & 3))) & 0xFu) << (4 * gg);
+        for (int i = 0; i < 4; ++i) {
+          base[16 * (4 * kq + i)] = (uint8_t)(mine >> (8 * i));
+          base[16 * (4 * (kq ^ 1) + i)] = (uint8_t)(theirs >> (8 * i));
         }
-        uint8_t* base = pages + rec + kVCodes + 4 * ((sl % 4) / 2) + 2 * (sl % 2);
-        *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + c2)) = (uint16_t)hw0;
-        *reinterpret_cast<uint16_t*>(base + 8 * (16 * (sl / 4) + c2 + 1)) = (uint16_t)hw1;
       }
     }
   }
@@ -1075,7 +1159,7 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
     const int per_head = 2 * max(1, min(tiles, (2 * cus + 2 * g.hkv - 1) / (2 * g.hkv)));
     const int k_share = k_mean != nullptr ? 19 : 15;
     const int k_groups = max(1, min(per_head - 1, (per_head * k_share + 16) / 32));
-    hipLaunchKernelGGL(rotate_quantize_prefill_kernel, dim3(per_head, g.hkv), dim3(kMThreads), 0,
+    hipLaunchKernelGGL(rotate_quantize_prefill_kernel<2>, dim3(per_head, g.hkv), dim3(kMThreads), 0,
                        stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
                        v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v,
                        k_groups);
@@ -1093,6 +1177,27 @@ hipError_t launch_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                        sinkwin, block_table, slot_ids, batch, total_new, k_new, v_new, new_offsets,
                        start_pos, rot_k, rot_v, k_mean, clip_k, clip_v);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_int4(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                               const int32_t* block_table, const int32_t* slot_ids, int batch,
+                               int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                               const int32_t* new_offsets, const int32_t* start_pos,
+                               const float* rot_k, const float* rot_v, const float* k_mean,
+                               float clip_k, float clip_v, hipStream_t stream) {
+  if (batch == 0 || total_new == 0) return hipSuccess;
+  int cus = current_device_cus();
+  if (cus <= 0) cus = 256;
+  // as the INT2 form; INT4 V blocks need no exchange between groups, so K and V blocks cost
+  // about the same: half of the workgroups each (19 of 32 for centered keys)
+  const int tiles = (total_new + kMBlock - 1) / kMBlock;
+  const int per_head = 2 * max(1, min(tiles, (2 * cus + 2 * g.hkv - 1) / (2 * g.hkv)));
+  const int k_share = k_mean != nullptr ? 19 : 16;
+  const int k_groups = max(1, min(per_head - 1, (per_head * k_share + 16) / 32));
+  hipLaunchKernelGGL(rotate_quantize_prefill_kernel<4>, dim3(per_head, g.hkv), dim3(kMThreads), 0,
+                     stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
+                     v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v, k_groups);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@
 // Kernels:
 //   int4_append_kernel  16 new rows of one (KV head, K|V) per workgroup, fp64 rotation on the
 //                       vector ALUs (R staged in LDS), quantisation, packing, BF16 copies;
+//                       appends of kMatrixAppendRows rows or more take the matrix-core prefill
+//                       kernel of append.hip in its 4-bit form instead (the same bytes);
 // The decode of these records runs on the matrix cores (int4_decode_mfma_kernel in decode.hip,
 // every G), in the INT2 workspace format, so oscar_combine finishes it.
 #include "oscar_internal.h"
@@ -196,6 +198,11 @@ hipError_t launch_int4_append(const CacheGeom& g, uint8_t* pages, uint16_t* sink
                               const float* rot_k, const float* rot_v, const float* k_mean,
                               float clip_k, float clip_v, hipStream_t stream) {
   if (batch == 0 || total_new == 0) return hipSuccess;
+  // prefill-sized appends on the matrix cores (certified, the same bytes: append.hip)
+  if (total_new >= kMatrixAppendRows)
+    return launch_prefill_int4(g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
+                               v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v,
+                               stream);
   hipLaunchKernelGGL(int4_append_kernel, dim3((total_new + 15) / 16, g.hkv, 2), dim3(kT4), 0,
                      stream, g, pages, sinkwin, block_table, slot_ids, batch, total_new, k_new,
                      v_new, new_offsets, start_pos, rot_k, rot_v, k_mean, clip_k, clip_v);

@@ -155,6 +155,14 @@ hipError_t launch_prep_q(const CacheGeom& g, const uint16_t* q, const float* rot
                          int hq, const int32_t* seq_lens, const Workspace& ws, hipStream_t stream);
 
 // INT4 cache (2560-byte records): append and decode (partials for launch_combine).
+// The matrix-core prefill kernel for INT4 records (append.hip); launch_int4_append takes it from
+// kMatrixAppendRows rows.
+hipError_t launch_prefill_int4(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
+                               const int32_t* block_table, const int32_t* slot_ids, int batch,
+                               int total_new, const uint16_t* k_new, const uint16_t* v_new,
+                               const int32_t* new_offsets, const int32_t* start_pos,
+                               const float* rot_k, const float* rot_v, const float* k_mean,
+                               float clip_k, float clip_v, hipStream_t stream);
 hipError_t launch_int4_append(const CacheGeom& g, uint8_t* pages, uint16_t* sinkwin,
                               const int32_t* block_table, const int32_t* slot_ids, int batch,
                               int total_new, const uint16_t* k_new, const uint16_t* v_new,

@@ -127,3 +127,105 @@ def test_int4_is_closer_to_exact_attention_than_int2():
             e2.append(np.abs(s2.out[b, j].cpu().numpy() - o_ex).max() / scale)
     _log(f"[int4] error vs exact attention: INT4 {np.mean(e4):.4f}, INT2 {np.mean(e2):.4f}")
     assert np.mean(e4) < 0.5 * np.mean(e2)
+
+
+@pytest.mark.parametrize("with_mean", [False, True])
+def test_int4_prefill_shape_matrix_vs_vector(with_mean):
+    """The INT4 append at the benchmark's prefill shape (64 sequences x 2048 new tokens at the end
+    of 16K-32K contexts, workload-recipe rows drawn on the GPU): one call (the matrix-core kernel,
+    from 256 rows on) against the same rows appended in calls of at most 255 rows (the fp64
+    vector kernel), every page and sink/window byte; plain and with the key mean."""
+    from int2_rotated_kv_rotate_amd import ops
+    w = W.WORKLOADS["qwen3_8b_b64"]
+    p = H.make_problem(w)
+    n_new = w.prefill_new
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4096)
+    hkv = w.num_kv_heads
+    total = n_new * w.batch
+    k = torch.randn((total, hkv, 128), generator=gen, device="cuda")
+    k += torch.from_numpy(W.key_offsets(w)).cuda()[None]
+    out_ch = torch.from_numpy(W.outlier_channels(w)).cuda()
+    for h in range(hkv):
+        k[:, h, out_ch[h]] *= 15.0
+    v = torch.randn((total, hkv, 128), generator=gen, device="cuda")
+    k16 = k.to(torch.bfloat16).view(torch.int16).contiguous()
+    v16 = v.to(torch.bfloat16).view(torch.int16).contiguous()
+    del k, v
+    offs = torch.arange(0, total + 1, n_new, dtype=torch.int32, device="cuda")
+    start = torch.from_numpy((p.lens - n_new).astype(np.int32)).cuda()
+    k_mean = torch.from_numpy(W.key_channel_means(w)).cuda() if with_mean else None
+    one = H.GpuCache(p, fill=SENTINEL, bits=4)
+    ops.int4_rotate_quantize_append(one.layout, one.pages, one.sinkwin, one.table, one.slots, k16,
+                                    v16, offs, start, one.rot_k, one.rot_v, w.clip, w.clip,
+                                    k_mean=k_mean)
+    torch.cuda.synchronize()
+    chunked = H.GpuCache(p, fill=SENTINEL, bits=4)
+    chunk = 255
+    B = w.batch
+    for b in range(B):
+        for c0 in range(0, n_new, chunk):
+            n = min(chunk, n_new - c0)
+            o = np.zeros(B + 1, np.int32)
+            o[b + 1:] = n
+            sp = (p.lens - n_new).astype(np.int32)
+            sp[b] += c0
+            r0 = b * n_new + c0
+            ops.int4_rotate_quantize_append(chunked.layout, chunked.pages, chunked.sinkwin,
+                                            chunked.table, chunked.slots,
+                                            k16[r0:r0 + n].contiguous(), v16[r0:r0 + n].contiguous(),
+                                            torch.from_numpy(o).cuda(), torch.from_numpy(sp).cuda(),
+                                            chunked.rot_k, chunked.rot_v, w.clip, w.clip,
+                                            k_mean=k_mean)
+    torch.cuda.synchronize()
+    nd = int((one.pages != chunked.pages).sum().item())
+    ns = int((one.sinkwin != chunked.sinkwin).sum().item())
+    _log(f"[int4] prefill shape {total} rows (key mean {with_mean}): {nd} page bytes, "
+         f"{ns} sink/window entries differ between the matrix-core and vector kernels")
+    assert nd == 0 and ns == 0
+    # and the new rows really were written (the sentinel replaced in a tail record)
+    last_page = int(p.table[0, (int(p.lens[0]) - 1) // 16])
+    assert not bool((one.pages[last_page, 0, :1024] == SENTINEL).all().item())
+
+
+@pytest.mark.parametrize("kind", ["special_rows", "symmetric_groups"])
+def test_int4_matrix_append_special_rows(kind):
+    """Rows that stress the matrix-core append's certification, in INT4 records (whole contexts,
+    so every call takes the matrix-core kernel and writes sink, window and bulk rows), against the
+    oracle byte for byte: rows along a column of R, zeros, subnormals and mixed 2^-20 / 2^8
+    magnitudes; or, under the identity rotation, groups with max = -min (a 16-level code
+    threshold exactly at a grid point), one-signed and constant groups."""
+    w = W.scaled(W.WORKLOADS["qwen3_4b"], name="int4_" + kind, batch=2, ctx=700, ctx_min=400)
+    rng = np.random.default_rng(77)
+    if kind == "special_rows":
+        from test_gpu_append_methods import _special_rows
+        p = H.make_problem(w)
+        ks = [_special_rows(rng, p.rot_k, int(L)) for L in p.lens]
+        vs = [_special_rows(rng, p.rot_v, int(L)) for L in p.lens]
+    else:
+        eye = np.broadcast_to(np.eye(128), (w.num_kv_heads, 128, 128)).copy()
+        p = H.make_problem(w, rot_k=eye, rot_v=eye)
+
+        def rows(n):
+            x = rng.uniform(-1.0, 1.0, size=(n, w.num_kv_heads, 4, 32)).astype(np.float32)
+            a = np.float32(2.0) ** rng.integers(-8, 8, size=(n, w.num_kv_heads, 4, 1)).astype(np.float32)
+            x *= a
+            kk = rng.integers(0, 4, size=(n, w.num_kv_heads, 4))
+            x[..., 0] = np.where(kk < 2, a[..., 0], x[..., 0])
+            x[..., 1] = np.where(kk < 2, -a[..., 0], x[..., 1])
+            x = np.where((kk == 2)[..., None], np.abs(x), x)
+            x = np.where((kk == 3)[..., None], a, x)
+            return W.to_bf16_bits(x.reshape(n, w.num_kv_heads, 128))
+
+        ks = [rows(int(L)) for L in p.lens]
+        vs = [rows(int(L)) for L in p.lens]
+    c = H.GpuCache(p, fill=SENTINEL, bits=4)
+    c.append(ks, vs, [0] * w.batch)
+    torch.cuda.synchronize()
+    oc = O.Cache(p.num_pages, w.num_kv_heads, w.batch, w.num_sink, w.window, fill=SENTINEL, bits=4)
+    for b in range(w.batch):
+        oc.append(p.table[b], b, 0, ks[b], vs[b], p.rot_k, p.rot_v, w.clip, w.clip)
+    nd = int((c.pages.cpu().numpy() != oc.pages).sum())
+    _log(f"[int4] matrix append {kind}: {sum(k.shape[0] for k in ks)} rows, {nd} page bytes differ")
+    assert nd == 0
+    assert np.array_equal(c.sinkwin.cpu().numpy().view(np.uint16), oc.sinkwin)
