@@ -249,11 +249,13 @@ def int2_vs_bf16(n_iter: int, samples: dict):
         of the batch) and batch 3 (the equal-memory batch for 3 bits per element);
       * Qwen3-4B layer shape, batch 1, context 32768: latency of each;
       * long-context layer (32 query / 8 KV heads), batch 1, context 131072: latency of each;
-      * the INT4 variant at the Qwen3-8B batch-64 shape.
+      * the INT4 variant at the Qwen3-8B batch-64 shape (decode, and the prefill append of each
+        sequence's last 2048 rows) and at the Qwen3-32B batch-16 shape.
     samples receives, per INT2 workload and for the INT4 one, the GPU outputs of one (sequence,
     KV head) pair for the oracle comparison of the CPU-baseline leg."""
     import torch
     from int2_rotated_kv_rotate_amd import harness as H
+    from int2_rotated_kv_rotate_amd import ops
     from int2_rotated_kv_rotate_amd import workload as W
 
     scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
@@ -360,7 +362,7 @@ def int2_vs_bf16(n_iter: int, samples: dict):
     w8 = W.WORKLOADS["qwen3_8b_b64"]
     p8 = H.make_problem(w8)
     c4 = H.GpuCache(p8, bits=4)
-    lk, lv = c4.fill_context()
+    lk, lv, tk4, tv4 = c4.fill_context(keep_tail=w8.prefill_new)
     st4 = H.DecodeStep(c4)
     st4.set_new_token(lk, lv)
     st4.run()
@@ -380,8 +382,36 @@ def int2_vs_bf16(n_iter: int, samples: dict):
                                 "bytes": int(b4), "effective_gbps": round(b4 / (ms4 * 1e-3) / 1e9, 1),
                                 "decode": "matrix cores: int8 logits, bf16 P.V, stream-K workers over "
                                           "2560-byte pages in a two-page LDS ring"}
-    log(f"INT4 qwen3_8b B=64: {ms4:.4f} ms ({b4 / (ms4 * 1e-3) / 1e9:.0f} GB/s)")
-    del st4, c4
+    # The INT4 prefill append: each sequence's last prefill_new rows again (the same bytes),
+    # one call, taken by the certified matrix-core kernel at this size
+    offs4 = np.zeros(w8.batch + 1, dtype=np.int32)
+    offs4[1:] = np.cumsum([t.shape[0] for t in tk4])
+    kt4 = H.as_i16(np.concatenate(tk4)).cuda()
+    vt4 = H.as_i16(np.concatenate(tv4)).cuda()
+    offs4_d = torch.from_numpy(offs4).cuda()
+    start4_d = torch.from_numpy(np.asarray([int(L) - 1 - t.shape[0] for L, t in zip(p8.lens, tk4)],
+                                           dtype=np.int32)).cuda()
+
+    def int4_prefill():
+        ops.int4_rotate_quantize_append(c4.layout, c4.pages, c4.sinkwin, c4.table, c4.slots, kt4,
+                                        vt4, offs4_d, start4_d, c4.rot_k, c4.rot_v, w8.clip,
+                                        w8.clip)
+    int4_prefill()
+    torch.cuda.synchronize()
+    a4, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a4.record()
+    for _ in range(3):
+        int4_prefill()
+    e4.record()
+    torch.cuda.synchronize()
+    pf4 = a4.elapsed_time(e4) / 3
+    n4 = int(offs4[-1])
+    res["int4_qwen3_8b_b64"]["prefill_append"] = {
+        "tokens": n4, "ms": round(pf4, 4), "tokens_per_s": round(n4 / (pf4 / 1e3), 1),
+        "rotation": "bf16 matrix cores, certified, uncertain values recomputed in fp64"}
+    log(f"INT4 qwen3_8b B=64: {ms4:.4f} ms ({b4 / (ms4 * 1e-3) / 1e9:.0f} GB/s); prefill append "
+        f"{n4} tokens {pf4:.3f} ms")
+    del st4, c4, kt4, vt4
 
     # The INT4 variant at G = 8 (Qwen3-32B layer, batch 16, 32k): the matrix-core decode with
     # the (head, group pair) row layout
