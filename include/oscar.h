@@ -209,8 +209,10 @@ int32_t oscar_rotate_quantize_append_hadamard(
  *                 4*(nb%2) (each slot owns whole bytes);
  *   [2048, 2304)  K (fp16 scale, fp16 zero) at 2048 + 16*r + 4*g;
  *   [2304, 2560)  V (scale, zero) at 2304 + 16*r + 4*g.
- * Arguments, validation and errors as oscar_rotate_quantize_append_ex (no method choice: the
- * rotation runs in fp64 on the vector ALUs).
+ * Arguments, validation and errors as oscar_rotate_quantize_append_ex, with no method argument:
+ * the choice is always that of OSCAR_APPEND_AUTO (the fp64 vector-ALU rotation below 256 new
+ * rows, from 256 the certified matrix-core one, which recomputes in fp64 every value whose code
+ * its bound cannot decide); both write the same bytes.
  */
 int32_t oscar_int4_rotate_quantize_append(
     const oscar_layout* lay, uint8_t* pages, uint16_t* sinkwin,
